@@ -1,0 +1,230 @@
+// C ABI of the binarized-QK attention library: argument validation,
+// workspace layout and kernel dispatch.  Every check runs before anything is
+// enqueued, so an error status means nothing was launched.
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "../../include/had.h"
+#include "had_internal.h"
+
+namespace had {
+
+int64_t dense_q8_max_n();
+
+static size_t align256(size_t x) { return (x + 255u) & ~(size_t)255u; }
+
+WorkspaceLayout workspace_layout(int64_t B, int64_t H, int64_t n, int64_t d) {
+  WorkspaceLayout w{};
+  const int64_t BH = B * H;
+  size_t off = 0;
+  w.pack_partial = off;
+  off = align256(off + sizeof(double) * (size_t)(BH * pack_chunks(n) * d));
+  w.vq = off;
+  off = align256(off + (size_t)(BH * n * d));
+  w.vscale = off;
+  off = align256(off + sizeof(float) * (size_t)(BH * d));
+  w.vmax_partial = off;
+  off = align256(off + sizeof(float) * (size_t)(BH * vq_chunks(n) * d));
+  w.total = off;
+  return w;
+}
+
+}  // namespace had
+
+using namespace had;
+
+namespace {
+
+bool debug_on() {
+  static const bool on = [] {
+    const char* e = getenv("HAD_DEBUG");
+    return e != nullptr && e[0] != '\0' && e[0] != '0';
+  }();
+  return on;
+}
+
+int fail(int status, const char* fn, const char* why) {
+  if (debug_on()) fprintf(stderr, "[had] %s: %s (%s)\n", fn, had_status_str(status), why);
+  return status;
+}
+
+// Total element count must stay addressable by the kernels' 32-bit row math.
+bool sizes_ok(int64_t B, int64_t H, int64_t n, int64_t d) {
+  if (B <= 0 || H <= 0 || n <= 0 || d <= 0) return false;
+  const double total = (double)B * (double)H * (double)n * (double)d;
+  return total < 2147483648.0;
+}
+
+int launch_status(hipError_t e, const char* fn) {
+  if (e == hipSuccess) return HAD_OK;
+  if (debug_on()) fprintf(stderr, "[had] %s: %s\n", fn, hipGetErrorString(e));
+  return HAD_ERR_HIP;
+}
+
+int check_workspace(const void* ws, size_t bytes, int64_t B, int64_t H, int64_t n, int64_t d, const char* fn) {
+  if (ws == nullptr) return fail(HAD_ERR_WORKSPACE, fn, "workspace is NULL");
+  if (bytes < workspace_layout(B, H, n, d).total) return fail(HAD_ERR_WORKSPACE, fn, "workspace too small");
+  if (((uintptr_t)ws & 255u) != 0) return fail(HAD_ERR_WORKSPACE, fn, "workspace not 256-byte aligned");
+  return HAD_OK;
+}
+
+// Checks shared by the two attention entry points.
+int check_attention(const uint32_t* qbits, const uint32_t* kbits, const void* v, int v_dtype, int64_t B,
+                    int64_t H, int64_t n, int64_t d, float* out, const char* fn) {
+  if (qbits == nullptr || kbits == nullptr || v == nullptr || out == nullptr)
+    return fail(HAD_ERR_INVALID_ARG, fn, "NULL tensor");
+  if (!sizes_ok(B, H, n, d)) return fail(HAD_ERR_INVALID_ARG, fn, "sizes must be positive and B*H*n*d < 2^31");
+  if (v_dtype != HAD_F32 && v_dtype != HAD_BF16) return fail(HAD_ERR_INVALID_ARG, fn, "unknown v_dtype");
+  if (d != 64) return fail(HAD_ERR_UNSUPPORTED, fn, "attention kernels take d = 64");
+  if (n > HAD_MAX_N) return fail(HAD_ERR_UNSUPPORTED, fn, "n above HAD_MAX_N");
+  return HAD_OK;
+}
+
+// Largest n the top-N kernel handles (V of one head staged in LDS).
+int64_t topn_max_n(int v_kind) { return v_kind == 0 ? 512 : 1024; }
+
+}  // namespace
+
+extern "C" {
+
+int had_abi_version(void) { return HAD_ABI_VERSION; }
+
+const char* had_status_str(int status) {
+  switch (status) {
+    case HAD_OK: return "HAD_OK";
+    case HAD_ERR_INVALID_ARG: return "HAD_ERR_INVALID_ARG";
+    case HAD_ERR_UNSUPPORTED: return "HAD_ERR_UNSUPPORTED";
+    case HAD_ERR_WORKSPACE: return "HAD_ERR_WORKSPACE";
+    case HAD_ERR_HIP: return "HAD_ERR_HIP";
+    default: return "HAD_ERR_UNKNOWN";
+  }
+}
+
+size_t had_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d) {
+  if (!sizes_ok(B, H, n, d)) return 0;
+  return workspace_layout(B, H, n, d).total;
+}
+
+int had_pack(const void* x, int x_dtype, int64_t B, int64_t H, int64_t n, int64_t d, int mode, uint32_t* bits,
+             float* alpha, float* mu, void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "had_pack";
+  if (x == nullptr || bits == nullptr) return fail(HAD_ERR_INVALID_ARG, fn, "NULL tensor");
+  if (!sizes_ok(B, H, n, d)) return fail(HAD_ERR_INVALID_ARG, fn, "sizes must be positive and B*H*n*d < 2^31");
+  if (x_dtype != HAD_F32 && x_dtype != HAD_BF16) return fail(HAD_ERR_INVALID_ARG, fn, "unknown x_dtype");
+  if (mode != HAD_SIGN && mode != HAD_MEAN_SIGN) return fail(HAD_ERR_INVALID_ARG, fn, "unknown mode");
+  if (d != 32 && d != 64 && d != 128) return fail(HAD_ERR_UNSUPPORTED, fn, "d must be 32, 64 or 128");
+  if (n > HAD_MAX_N) return fail(HAD_ERR_UNSUPPORTED, fn, "n above HAD_MAX_N");
+  PackParams p{};
+  p.x = x;
+  p.x_dtype = x_dtype;
+  p.BH = B * H;
+  p.n = n;
+  p.d = d;
+  p.mode = mode;
+  p.bits = bits;
+  p.alpha = alpha;
+  p.mu = mu;
+  if (mode == HAD_MEAN_SIGN) {
+    if (alpha == nullptr || mu == nullptr) return fail(HAD_ERR_INVALID_ARG, fn, "MEAN_SIGN needs alpha and mu");
+    const int st = check_workspace(workspace, workspace_bytes, B, H, n, d, fn);
+    if (st != HAD_OK) return st;
+    p.partial = reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + workspace_layout(B, H, n, d).pack_partial);
+  }
+  return launch_status(launch_pack(p, static_cast<hipStream_t>(stream)), fn);
+}
+
+int had_attention_topn(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q, const float* alpha_k,
+                       const float* bias_table, const void* v, int v_dtype, int64_t B, int64_t H, int64_t n,
+                       int64_t d, int64_t top_n, int av_mode, float* out, int32_t* idx_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  static const char* fn = "had_attention_topn";
+  int st = check_attention(qbits, kbits, v, v_dtype, B, H, n, d, out, fn);
+  if (st != HAD_OK) return st;
+  if (top_n < 1) return fail(HAD_ERR_INVALID_ARG, fn, "top_n must be >= 1");
+  if (av_mode != HAD_AV_F32 && av_mode != HAD_AV_Q8) return fail(HAD_ERR_INVALID_ARG, fn, "unknown av_mode");
+  const int64_t keep = top_n < n ? top_n : n;
+  if (keep > HAD_MAX_TOPN) return fail(HAD_ERR_UNSUPPORTED, fn, "min(top_n, n) above HAD_MAX_TOPN");
+  const int v_kind = av_mode == HAD_AV_Q8 ? 2 : (v_dtype == HAD_BF16 ? 1 : 0);
+  if (n > topn_max_n(v_kind)) return fail(HAD_ERR_UNSUPPORTED, fn, "n too large for the top-N kernel");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AttnParams p{};
+  p.qbits = qbits;
+  p.kbits = kbits;
+  p.alpha_q = alpha_q;
+  p.alpha_k = alpha_k;
+  p.bias = bias_table;
+  p.v = v;
+  p.v_kind = v_kind;
+  p.B = B;
+  p.H = H;
+  p.n = n;
+  p.d = d;
+  p.keep = keep;
+  p.out = out;
+  p.idx = idx_out;
+  if (av_mode == HAD_AV_Q8) {
+    st = check_workspace(workspace, workspace_bytes, B, H, n, d, fn);
+    if (st != HAD_OK) return st;
+    const WorkspaceLayout w = workspace_layout(B, H, n, d);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    VQuantParams q{};
+    q.v = v;
+    q.v_dtype = v_dtype;
+    q.BH = B * H;
+    q.n = n;
+    q.d = d;
+    q.vmax_partial = reinterpret_cast<float*>(ws + w.vmax_partial);
+    q.vscale = reinterpret_cast<float*>(ws + w.vscale);
+    q.vq = reinterpret_cast<int8_t*>(ws + w.vq);
+    hipError_t e = launch_vquant(q, s);
+    if (e != hipSuccess) return launch_status(e, fn);
+    p.v = q.vq;
+    p.vscale = q.vscale;
+  }
+  return launch_status(launch_topn(p, s), fn);
+}
+
+int binattn_dense_q8(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q, const float* alpha_k,
+                     const float* bias_table, const void* v, int v_dtype, int64_t B, int64_t H, int64_t n, int64_t d,
+                     float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "binattn_dense_q8";
+  int st = check_attention(qbits, kbits, v, v_dtype, B, H, n, d, out, fn);
+  if (st != HAD_OK) return st;
+  if (n > dense_q8_max_n()) return fail(HAD_ERR_UNSUPPORTED, fn, "n too large for the dense kernel");
+  st = check_workspace(workspace, workspace_bytes, B, H, n, d, fn);
+  if (st != HAD_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const WorkspaceLayout w = workspace_layout(B, H, n, d);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  VQuantParams q{};
+  q.v = v;
+  q.v_dtype = v_dtype;
+  q.BH = B * H;
+  q.n = n;
+  q.d = d;
+  q.vmax_partial = reinterpret_cast<float*>(ws + w.vmax_partial);
+  q.vscale = reinterpret_cast<float*>(ws + w.vscale);
+  q.vq = reinterpret_cast<int8_t*>(ws + w.vq);
+  hipError_t e = launch_vquant(q, s);
+  if (e != hipSuccess) return launch_status(e, fn);
+  AttnParams p{};
+  p.qbits = qbits;
+  p.kbits = kbits;
+  p.alpha_q = alpha_q;
+  p.alpha_k = alpha_k;
+  p.bias = bias_table;
+  p.v = q.vq;
+  p.v_kind = 2;
+  p.vscale = q.vscale;
+  p.B = B;
+  p.H = H;
+  p.n = n;
+  p.d = d;
+  p.keep = n;
+  p.out = out;
+  p.idx = nullptr;
+  return launch_status(launch_dense_q8(p, s), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,140 @@
+// Device-side helpers shared by the gfx950 kernels (wave64 primitives).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define HAD_DEVICE __device__ __forceinline__
+
+namespace had {
+
+constexpr int kWave = 64;
+
+HAD_DEVICE int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// Rank of this lane among the set lanes of `mask` below it.
+HAD_DEVICE uint32_t mask_rank(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+HAD_DEVICE uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+template <typename T>
+HAD_DEVICE T uniform(T v) {
+  return __builtin_bit_cast(T, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+// DPP controls (GFX9 encoding).
+constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+template <int CTRL>
+HAD_DEVICE int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+HAD_DEVICE float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xf, 0xf, false));
+}
+
+// Sum over all 64 lanes; the result is wave-uniform.
+HAD_DEVICE int wave_sum_i32(int v) {
+  v += dpp_i<kRowRor8>(v);
+  v += dpp_i<kRowRor4>(v);
+  v += dpp_i<kRowRor2>(v);
+  v += dpp_i<kRowRor1>(v);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
+HAD_DEVICE float wave_sum_f32(float v) {
+  v += dpp_f<kRowRor8>(v);
+  v += dpp_f<kRowRor4>(v);
+  v += dpp_f<kRowRor2>(v);
+  v += dpp_f<kRowRor1>(v);
+  float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (a + b) + (c + d);
+}
+
+HAD_DEVICE float wave_max_f32(float v) {
+  v = fmaxf(v, dpp_f<kRowRor8>(v));
+  v = fmaxf(v, dpp_f<kRowRor4>(v));
+  v = fmaxf(v, dpp_f<kRowRor2>(v));
+  v = fmaxf(v, dpp_f<kRowRor1>(v));
+  float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+HAD_DEVICE uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, (uint32_t)dpp_i<kRowRor8>((int)v));
+  v = min(v, (uint32_t)dpp_i<kRowRor4>((int)v));
+  v = min(v, (uint32_t)dpp_i<kRowRor2>((int)v));
+  v = min(v, (uint32_t)dpp_i<kRowRor1>((int)v));
+  uint32_t a = __builtin_amdgcn_readlane((int)v, 0), b = __builtin_amdgcn_readlane((int)v, 16);
+  uint32_t c = __builtin_amdgcn_readlane((int)v, 32), d = __builtin_amdgcn_readlane((int)v, 48);
+  return min(min(a, b), min(c, d));
+}
+
+HAD_DEVICE uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)dpp_i<kRowRor8>((int)v));
+  v = max(v, (uint32_t)dpp_i<kRowRor4>((int)v));
+  v = max(v, (uint32_t)dpp_i<kRowRor2>((int)v));
+  v = max(v, (uint32_t)dpp_i<kRowRor1>((int)v));
+  uint32_t a = __builtin_amdgcn_readlane((int)v, 0), b = __builtin_amdgcn_readlane((int)v, 16);
+  uint32_t c = __builtin_amdgcn_readlane((int)v, 32), d = __builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
+}
+
+// Exclusive prefix sum over lanes (lane 0 gets 0) and the wave total.
+HAD_DEVICE int wave_excl_scan_i32(int v, int* total) {
+  int x = v;
+  int lane = lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  *total = __builtin_amdgcn_readlane(x, 63);
+  return x - v;
+}
+
+// bf16 bits -> float (exact widening).
+HAD_DEVICE float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+HAD_DEVICE float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Order-preserving map float -> uint32 (a larger float maps to a larger key).
+HAD_DEVICE uint32_t ordered_key(float f) {
+  uint32_t b = __builtin_bit_cast(uint32_t, f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+HAD_DEVICE float from_ordered_key(uint32_t k) {
+  uint32_t b = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __builtin_bit_cast(float, b);
+}
+
+// Canonical float32 logit: each operation rounded as written, no contraction.
+HAD_DEVICE float canonical_logit(float aq, float ak, int dot, float inv_sqrt_d, float bias) {
+  float t = __fmul_rn(aq, ak);
+  float u = __fmul_rn(t, (float)dot);
+  float v = __fmul_rn(u, inv_sqrt_d);
+  return __fadd_rn(v, bias);
+}
+
+// XCD-aware remap of the linear workgroup id: consecutive logical ids land on
+// the same XCD (hardware dispatches workgroup w to XCD w % 8), so the blocks
+// that share a head's keys and values share one L2.
+HAD_DEVICE uint32_t xcd_remap(uint32_t w, uint32_t nwg) {
+  constexpr uint32_t kXcd = 8;
+  uint32_t per = nwg / kXcd;
+  uint32_t full = per * kXcd;
+  if (w >= full) return w;  // the remainder keeps its id
+  return (w % kXcd) * per + (w / kXcd);
+}
+
+}  // namespace had

@@ -1,0 +1,65 @@
+// Host-side declarations shared by the C-ABI layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace had {
+
+// ---- packing (pack.hip)
+struct PackParams {
+  const void* x;
+  int x_dtype;  // HAD_F32 / HAD_BF16
+  int64_t BH, n, d;
+  int mode;  // HAD_SIGN / HAD_MEAN_SIGN
+  uint32_t* bits;
+  float* alpha;
+  float* mu;
+  double* partial;  // MEAN_SIGN: [BH, chunks, d] float64 column sums
+};
+constexpr int kPackChunk = 256;  // tokens per column-sum chunk
+inline int64_t pack_chunks(int64_t n) { return (n + kPackChunk - 1) / kPackChunk; }
+hipError_t launch_pack(const PackParams& p, hipStream_t s);
+
+// ---- V quantization (vquant.hip)
+struct VQuantParams {
+  const void* v;
+  int v_dtype;
+  int64_t BH, n, d;
+  float* vmax_partial;  // [BH, chunks, d]
+  float* vscale;        // [BH, d]
+  int8_t* vq;           // [BH, n, d]
+};
+constexpr int kVqChunk = 256;
+inline int64_t vq_chunks(int64_t n) { return (n + kVqChunk - 1) / kVqChunk; }
+hipError_t launch_vquant(const VQuantParams& p, hipStream_t s);
+
+// ---- attention (topn.hip, dense_q8.hip)
+struct AttnParams {
+  const uint32_t* qbits;
+  const uint32_t* kbits;
+  const float* alpha_q;
+  const float* alpha_k;
+  const float* bias;
+  const void* v;  // f32 / bf16 V (AV_F32) or int8 Vq (AV_Q8)
+  int v_kind;     // 0 f32, 1 bf16, 2 int8 (quantized)
+  const float* vscale;
+  int64_t B, H, n, d;
+  int64_t keep;  // min(top_n, n)
+  float* out;
+  int32_t* idx;
+};
+hipError_t launch_topn(const AttnParams& p, hipStream_t s);
+hipError_t launch_dense_q8(const AttnParams& p, hipStream_t s);
+
+// Device scratch layout inside the caller's workspace.
+struct WorkspaceLayout {
+  size_t pack_partial;  // offset of double[BH, pack_chunks, d]
+  size_t vq;            // offset of int8[BH, n, d]
+  size_t vscale;        // offset of float[BH, d]
+  size_t vmax_partial;  // offset of float[BH, vq_chunks, d]
+  size_t total;
+};
+WorkspaceLayout workspace_layout(int64_t B, int64_t H, int64_t n, int64_t d);
+
+}  // namespace had

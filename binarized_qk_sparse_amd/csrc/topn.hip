@@ -1,0 +1,542 @@
+// Top-N binarized attention, one wavefront per query (gfx950, wave64).
+//
+// Method (Hamming Attention Distillation, summary "main points"/"method"; and
+// BinaryAttention sections 2.2-2.4):
+//   l_ij = alpha_q alpha_k (d - 2 popcount(q_i XOR k_j)) / sqrt(d) + B_ij
+//   S_i  = the N largest l_ij (ties to the lower j)
+//   O_i  = sum_{j in S_i} softmax_S(l)_j V_j           (fp32, or uint8 A x int8 V)
+//
+// Work decomposition.  A workgroup owns one (batch, head) and a tile of
+// consecutive queries; it stages that head's V rows in LDS once, and each of
+// its waves keeps every key's code bits in VGPRs (key j = 64 s + lane lives
+// in slot s of lane j % 64).  Per query the wave
+//   1. forms the logit of every key (VALU XOR + v_bcnt, two words for d = 64),
+//   2. finds the exact top-N threshold without sorting:
+//        integer keys (alpha = 1, no bias): the logit is a function of the
+//        Hamming distance h in [0, 64], so the threshold is the smallest level
+//        tau with #{h <= tau} >= N.  Counts are taken four keys per VALU op on
+//        byte-packed distances (SWAR add/and/popcount), starting from the
+//        previous query's tau.
+//        float keys: bisection on the logit value until at most 64 candidates
+//        straddle the threshold, then an exact radix search among them;
+//      ties at the threshold go to the lower key index;
+//   3. compacts the kept keys into a per-wave list in LDS (ascending j),
+//   4. softmax over the list (fp32), and
+//   5. A*V: eight lanes per kept key, eight channels per lane, V read from LDS
+//      (16-byte reads), fp32 FMA (or int32 multiply-add on int8 V), then a
+//      butterfly reduce-scatter leaves one output channel per lane.
+// The kernel is bound by VALU issue; the only HBM traffic is codes, V and O.
+#include <float.h>
+#include <limits.h>
+
+#include "had_device.hpp"
+#include "had_internal.h"
+#include "../../include/had.h"
+
+namespace had {
+namespace {
+
+constexpr int kD = 64;      // head_dim of these kernels
+constexpr int kQTile = 64;  // queries per workgroup tile
+constexpr int kMaxWaves = 16;
+constexpr uint32_t kLdsBytes = 160 * 1024;
+
+struct TopnKArgs {
+  const uint32_t* qbits;
+  const uint32_t* kbits;
+  const float* aq;
+  const float* ak;
+  const float* bias;
+  const void* v;
+  const float* vscale;
+  float* out;
+  int32_t* idx;
+  int H, n, keep, lcap, qt, tiles;
+  float isd;    // float(1/sqrt(d))
+  float exp_c;  // 2*isd*log2(e): integer-key exponent per Hamming step
+  uint32_t list_off, cand_off, bias_off;
+};
+
+template <int VK>
+constexpr int row_bytes() {
+  return VK == 0 ? kD * 4 : (VK == 1 ? kD * 2 : kD);
+}
+
+// Uniform: number of keys j (over all lanes and slots) with hv <= t, t in [0, 64].
+// Distances are byte-packed four to a register; a byte b satisfies b > t exactly
+// when bit 7 of b + (127 - t) is set (b <= 65, so no byte carries out).
+template <int NP>
+HAD_DEVICE int count_le(const uint32_t (&P)[NP], int t) {
+  const uint32_t add = (uint32_t)(127 - t) * 0x01010101u;
+  uint32_t c = 0;
+#pragma unroll
+  for (int m = 0; m < NP; ++m) c = __builtin_popcount((P[m] + add) & 0x80808080u) + c;
+  return NP * 256 - wave_sum_i32((int)c);
+}
+
+template <int NS>
+HAD_DEVICE int count_ge_f(const float (&l)[NS], float t) {
+  int c = 0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) c += __builtin_popcountll(ballot(l[s] >= t));
+  return c;
+}
+
+template <int NS, bool FK, int VK>
+__global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int ROWB = row_bytes<VK>();
+  constexpr int NP = (NS + 3) / 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / a.tiles, tile = wg % a.tiles, hh = bh % a.H;
+  const int n = a.n, keep = a.keep;
+  const int i0 = tile * a.qt, i1 = min(n, i0 + a.qt);
+
+  // ---- stage this head's V rows in LDS (16 bytes per thread and step)
+  {
+    const uint8_t* src = static_cast<const uint8_t*>(a.v) + (size_t)bh * n * ROWB;
+    const uint32_t total = (uint32_t)n * ROWB;
+    for (uint32_t o = threadIdx.x * 16u; o < total; o += blockDim.x * 16u)
+      *reinterpret_cast<uint4*>(smem + o) = *reinterpret_cast<const uint4*>(src + o);
+  }
+  // ---- stage the bias offsets this tile touches: o = j - i + n - 1 in [n - i1, 2n - 2 - i0]
+  const int ob = n - i1;
+  float* biasw = reinterpret_cast<float*>(smem + a.bias_off);
+  if (FK && a.bias != nullptr) {
+    const int cnt = n + (i1 - i0) - 1;
+    const float* src = a.bias + (size_t)hh * (2 * n - 1) + ob;
+    for (int o = threadIdx.x; o < cnt; o += blockDim.x) biasw[o] = src[o];
+  }
+  // ---- key codes: slot s of this lane is key 64 s + lane; slots from
+  // full_slots on may hold padding keys (j >= n)
+  uint32_t k0[NS], k1[NS];
+  float akv[NS];
+  const int full_slots = n / 64;
+  const uint2* kb = reinterpret_cast<const uint2*>(a.kbits) + (size_t)bh * n;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int j = 64 * s + lane;
+    const bool ok = j < n;
+    const uint2 kk = ok ? kb[j] : make_uint2(0u, 0u);
+    k0[s] = kk.x;
+    k1[s] = kk.y;
+    akv[s] = (FK && ok && a.ak != nullptr) ? a.ak[(size_t)bh * n + j] : 1.0f;
+  }
+  __syncthreads();
+
+  uint2* list = reinterpret_cast<uint2*>(smem + a.list_off) + wave * a.lcap;
+  uint2* cand = reinterpret_cast<uint2*>(smem + a.cand_off) + wave * 64;
+  const uint2* qb = reinterpret_cast<const uint2*>(a.qbits);
+  int tau_prev = 27;  // Hamming-level guess; each query starts from the last one's
+
+  for (int i = i0 + wave; i < i1; i += nwaves) {
+    const size_t row = (size_t)bh * n + i;
+    const uint2 qq = qb[row];
+    float lmax = 0.0f;  // float keys: largest logit of the row
+    int hmin = 0;       // integer keys: smallest distance of the row
+
+    if (!FK) {
+      // ------------------------------------------------ integer keys
+      uint32_t hv[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        hv[s] = __builtin_popcount(k1[s] ^ qq.y) + __builtin_popcount(k0[s] ^ qq.x);
+        if (s >= full_slots && 64 * s + lane >= n) hv[s] = 65u;  // padding: above every real distance
+      }
+      uint32_t P[NP];
+#pragma unroll
+      for (int m = 0; m < NP; ++m) {
+        uint32_t b[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) b[q] = (4 * m + q < NS) ? hv[4 * m + q] : 65u;
+        P[m] = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+      }
+      int tau, less;
+      if (keep >= n) {
+        tau = 65;  // every real key is below the padding level
+        less = keep;
+      } else {
+        int lo, hi, clo;
+        const int t = min(max(tau_prev, 0), 64);
+        const int c = count_le<NP>(P, t);
+        if (c >= keep) {
+          hi = t;
+          const int c1 = t > 0 ? count_le<NP>(P, t - 1) : 0;
+          if (c1 < keep) {
+            lo = t - 1;
+            clo = c1;
+          } else {
+            hi = t - 1;
+            lo = -1;
+            clo = 0;
+          }
+        } else {
+          lo = t;
+          clo = c;
+          const int c1 = count_le<NP>(P, t + 1);
+          if (c1 >= keep) {
+            hi = t + 1;
+          } else {
+            lo = t + 1;
+            clo = c1;
+            hi = 64;
+          }
+        }
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          const int cm = count_le<NP>(P, mid);
+          if (cm >= keep) {
+            hi = mid;
+          } else {
+            lo = mid;
+            clo = cm;
+          }
+        }
+        tau = hi;
+        less = clo;
+        tau_prev = tau;
+      }
+      // ---- compaction: all h < tau, then the first (keep - less) keys with h == tau
+      int r = keep - less;
+      int base = 0;
+      uint32_t hmin_l = 255u;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const uint64_t Lm = ballot(hv[s] < (uint32_t)tau);
+        uint64_t Sm = Lm;
+        if (r > 0) {
+          const uint64_t Em = ballot(hv[s] == (uint32_t)tau);
+          const int e = __builtin_popcountll(Em);
+          if (e <= r) {
+            Sm |= Em;
+            r -= e;
+          } else {
+            uint64_t x = Em;
+            for (int k = 0; k < r; ++k) x &= x - 1;  // drop the r lowest set bits
+            Sm |= Em ^ x;
+            r = 0;
+          }
+        }
+        if ((Sm >> lane) & 1u) {
+          const int pos = base + (int)mask_rank(Sm);
+          if (pos < a.lcap) list[pos] = make_uint2((uint32_t)(64 * s + lane), hv[s]);
+          hmin_l = min(hmin_l, hv[s]);
+        }
+        base += __builtin_popcountll(Sm);
+      }
+      hmin = (int)wave_min_u32(hmin_l);
+    } else {
+      // ------------------------------------------------ float keys
+      const float aqv = a.aq != nullptr ? a.aq[row] : 1.0f;
+      float lg[NS];
+      const int boff = n - 1 - ob - i;  // bias window index of key j is j + boff
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int j = 64 * s + lane;
+        const int hd = __builtin_popcount(k0[s] ^ qq.x) + __builtin_popcount(k1[s] ^ qq.y);
+        const float bias = (a.bias != nullptr && j < n) ? biasw[j + boff] : 0.0f;
+        const float l = canonical_logit(aqv, akv[s], kD - 2 * hd, a.isd, bias);
+        lg[s] = __fadd_rn(l, 0.0f);  // -0 and +0 compare equal
+        if (s >= full_slots && j >= n) lg[s] = -INFINITY;  // padding
+      }
+      float vstar;
+      int jstar;
+      lmax = -INFINITY;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) lmax = fmaxf(lmax, lg[s]);
+      lmax = wave_max_f32(lmax);
+      if (keep >= n) {
+        vstar = -INFINITY;  // everything real is kept
+        jstar = INT_MAX;
+      } else {
+        float lmin = INFINITY;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) lmin = fminf(lmin, lg[s] == -INFINITY ? INFINITY : lg[s]);
+        lmin = -wave_max_f32(-lmin);
+        int need;  // keys still to take at value vstar (lowest j first)
+        const int ctop = count_ge_f<NS>(lg, lmax);
+        if (ctop >= keep) {
+          vstar = lmax;
+          need = keep;
+        } else {
+          // invariant: cnt(>= lo) >= keep > cnt(>= hi)
+          float lo = lmin, hi = lmax;
+          int clo = n, chi = ctop;
+          bool split = true;
+          while (clo - chi > 64) {
+            const float mid = 0.5f * lo + 0.5f * hi;
+            if (!(mid > lo && mid < hi)) {
+              split = false;
+              break;
+            }
+            const int cm = count_ge_f<NS>(lg, mid);
+            if (cm >= keep) {
+              lo = mid;
+              clo = cm;
+            } else {
+              hi = mid;
+              chi = cm;
+            }
+          }
+          if (!split) {
+            vstar = lo;  // hi is the next float after lo: every candidate equals lo
+            need = keep - chi;
+          } else {
+            // compact the candidates lo <= l < hi (at most 64) into one per lane
+            int cb = 0;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+              const bool c = lg[s] >= lo && lg[s] < hi;
+              const uint64_t m = ballot(c);
+              const int pos = cb + (int)mask_rank(m);
+              if (c && pos < 64) cand[pos] = make_uint2(ordered_key(lg[s]), (uint32_t)(64 * s + lane));
+              cb += __builtin_popcountll(m);
+            }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            const uint32_t ck = lane < cb ? cand[lane].x : 0u;
+            const int rr = keep - chi;  // how many candidates to take
+            // largest T with #{ck >= T} >= rr: the rr-th largest candidate
+            uint32_t L = ordered_key(lo), R = ordered_key(hi);
+            while (R - L > 1u) {
+              const uint32_t M = L + ((R - L) >> 1);
+              if (__builtin_popcountll(ballot(ck >= M)) >= rr)
+                L = M;
+              else
+                R = M;
+            }
+            vstar = from_ordered_key(L);
+            need = keep - chi - __builtin_popcountll(ballot(ck > L));
+          }
+        }
+        // the need-th key (ascending j) with l == vstar
+        jstar = INT_MAX;
+        int seen = 0;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const uint64_t Em = ballot(lg[s] == vstar);
+          const int e = __builtin_popcountll(Em);
+          if (jstar == INT_MAX && seen + e >= need) {
+            uint64_t x = Em;
+            for (int k = 0; k < need - seen - 1; ++k) x &= x - 1;
+            jstar = 64 * s + (int)__builtin_ctzll(x);
+          }
+          seen += e;
+        }
+      }
+      // ---- compaction of l > vstar, or l == vstar with j <= jstar
+      int base = 0;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int j = 64 * s + lane;
+        const bool sel = j < n && (lg[s] > vstar || (lg[s] == vstar && j <= jstar));
+        const uint64_t Sm = ballot(sel);
+        const int pos = base + (int)mask_rank(Sm);
+        if (sel && pos < a.lcap) list[pos] = make_uint2((uint32_t)j, __builtin_bit_cast(uint32_t, lg[s]));
+        base += __builtin_popcountll(Sm);
+      }
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+
+    // ---------------------------------------------------- softmax over the kept list
+    float z = 0.0f;
+    for (int e = lane; e < keep; e += 64) {
+      const uint32_t sc = list[e].y;
+      const float x = FK ? __builtin_bit_cast(float, sc) - lmax : (float)(hmin - (int)sc) * a.exp_c;
+      const float ex = FK ? __expf(x) : exp2f(x);
+      z += ex;
+      list[e].y = __builtin_bit_cast(uint32_t, ex);
+    }
+    const float inv_z = 1.0f / wave_sum_f32(z);
+    for (int e = lane; e < a.lcap; e += 64) {
+      uint2 ent = e < keep ? list[e] : make_uint2(0u, 0u);
+      const float p = __builtin_bit_cast(float, ent.y) * inv_z;
+      if (VK == 2) {
+        const float qv = fminf(fmaxf(rintf(255.0f * p), 0.0f), 255.0f);
+        ent.y = e < keep ? (uint32_t)qv : 0u;
+      } else {
+        ent.y = e < keep ? __builtin_bit_cast(uint32_t, p) : 0u;
+      }
+      list[e] = ent;
+      if (a.idx != nullptr && e < keep) a.idx[row * keep + e] = (int32_t)ent.x;
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+
+    // ---------------------------------------------------- A*V
+    const int k = lane >> 3, g = lane & 7;
+    if (VK == 2) {
+      int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int t = 0; t < a.lcap; t += 8) {
+        const uint2 ent = list[t + k];
+        const uint2 raw = *reinterpret_cast<const uint2*>(smem + ent.x * ROWB + g * 8);
+        const int aq8 = (int)ent.y;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc[c] += aq8 * (int)(int8_t)(raw.x >> (8 * c));
+          acc[4 + c] += aq8 * (int)(int8_t)(raw.y >> (8 * c));
+        }
+      }
+      const bool u4 = k & 4, u2 = k & 2, u1 = k & 1;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int snd = u4 ? acc[c] : acc[c + 4];
+        const int kp = u4 ? acc[c + 4] : acc[c];
+        acc[c] = kp + __shfl_xor(snd, 32, 64);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int snd = u2 ? acc[c] : acc[c + 2];
+        const int kp = u2 ? acc[c + 2] : acc[c];
+        acc[c] = kp + __shfl_xor(snd, 16, 64);
+      }
+      {
+        const int snd = u1 ? acc[0] : acc[1];
+        const int kp = u1 ? acc[1] : acc[0];
+        acc[0] = kp + __shfl_xor(snd, 8, 64);
+      }
+      const int ch = 8 * g + k;
+      const float sc = a.vscale[(size_t)bh * kD + ch];
+      a.out[row * kD + ch] = __fdiv_rn(__fmul_rn((float)acc[0], sc), 255.0f);
+    } else {
+      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int t = 0; t < a.lcap; t += 8) {
+        const uint2 ent = list[t + k];
+        const float p = __builtin_bit_cast(float, ent.y);
+        if (VK == 1) {
+          const uint4 raw = *reinterpret_cast<const uint4*>(smem + ent.x * ROWB + g * 16);
+          acc[0] = __builtin_fmaf(p, bf16_lo(raw.x), acc[0]);
+          acc[1] = __builtin_fmaf(p, bf16_hi(raw.x), acc[1]);
+          acc[2] = __builtin_fmaf(p, bf16_lo(raw.y), acc[2]);
+          acc[3] = __builtin_fmaf(p, bf16_hi(raw.y), acc[3]);
+          acc[4] = __builtin_fmaf(p, bf16_lo(raw.z), acc[4]);
+          acc[5] = __builtin_fmaf(p, bf16_hi(raw.z), acc[5]);
+          acc[6] = __builtin_fmaf(p, bf16_lo(raw.w), acc[6]);
+          acc[7] = __builtin_fmaf(p, bf16_hi(raw.w), acc[7]);
+        } else {
+          const float4 r0 = *reinterpret_cast<const float4*>(smem + ent.x * ROWB + g * 32);
+          const float4 r1 = *reinterpret_cast<const float4*>(smem + ent.x * ROWB + g * 32 + 16);
+          acc[0] = __builtin_fmaf(p, r0.x, acc[0]);
+          acc[1] = __builtin_fmaf(p, r0.y, acc[1]);
+          acc[2] = __builtin_fmaf(p, r0.z, acc[2]);
+          acc[3] = __builtin_fmaf(p, r0.w, acc[3]);
+          acc[4] = __builtin_fmaf(p, r1.x, acc[4]);
+          acc[5] = __builtin_fmaf(p, r1.y, acc[5]);
+          acc[6] = __builtin_fmaf(p, r1.z, acc[6]);
+          acc[7] = __builtin_fmaf(p, r1.w, acc[7]);
+        }
+      }
+      const bool u4 = k & 4, u2 = k & 2, u1 = k & 1;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float snd = u4 ? acc[c] : acc[c + 4];
+        const float kp = u4 ? acc[c + 4] : acc[c];
+        acc[c] = kp + __shfl_xor(snd, 32, 64);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const float snd = u2 ? acc[c] : acc[c + 2];
+        const float kp = u2 ? acc[c + 2] : acc[c];
+        acc[c] = kp + __shfl_xor(snd, 16, 64);
+      }
+      {
+        const float snd = u1 ? acc[0] : acc[1];
+        const float kp = u1 ? acc[1] : acc[0];
+        acc[0] = kp + __shfl_xor(snd, 8, 64);
+      }
+      a.out[row * kD + 8 * g + k] = acc[0];
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  }
+}
+
+template <int NS, bool FK, int VK>
+hipError_t launch_one(const TopnKArgs& ka, dim3 grid, dim3 block, uint32_t lds, hipStream_t s) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&topn_resident_kernel<NS, FK, VK>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((topn_resident_kernel<NS, FK, VK>), grid, block, lds, s, ka);
+  return hipGetLastError();
+}
+
+template <int NS, bool FK>
+hipError_t launch_vk(const TopnKArgs& ka, int vk, dim3 grid, dim3 block, uint32_t lds, hipStream_t s) {
+  switch (vk) {
+    case 0: return launch_one<NS, FK, 0>(ka, grid, block, lds, s);
+    case 1: return launch_one<NS, FK, 1>(ka, grid, block, lds, s);
+    default: return launch_one<NS, FK, 2>(ka, grid, block, lds, s);
+  }
+}
+
+template <int NS>
+hipError_t launch_ns(const TopnKArgs& ka, bool fk, int vk, dim3 grid, dim3 block, uint32_t lds, hipStream_t s) {
+  return fk ? launch_vk<NS, true>(ka, vk, grid, block, lds, s) : launch_vk<NS, false>(ka, vk, grid, block, lds, s);
+}
+
+uint32_t align16(uint32_t x) { return (x + 15u) & ~15u; }
+
+}  // namespace
+
+// Slots per lane the resident kernel is instantiated for (n <= 64 * slots).
+static int resident_slots(int64_t n) {
+  const int64_t s = (n + 63) / 64;
+  if (s <= 1) return 1;
+  if (s <= 2) return 2;
+  if (s <= 4) return 4;
+  if (s <= 8) return 8;
+  if (s <= 12) return 12;
+  if (s <= 16) return 16;
+  return 0;
+}
+
+hipError_t launch_topn(const AttnParams& p, hipStream_t s) {
+  if (p.d != kD) return hipErrorInvalidValue;
+  const int NS = resident_slots(p.n);
+  if (NS == 0) return hipErrorInvalidValue;
+  const bool fk = p.alpha_q != nullptr || p.alpha_k != nullptr || p.bias != nullptr;
+  const int vk = p.v_kind;
+  const int rowb = vk == 0 ? kD * 4 : (vk == 1 ? kD * 2 : kD);
+  TopnKArgs ka{};
+  ka.qbits = p.qbits;
+  ka.kbits = p.kbits;
+  ka.aq = p.alpha_q;
+  ka.ak = p.alpha_k;
+  ka.bias = p.bias;
+  ka.v = p.v;
+  ka.vscale = p.vscale;
+  ka.out = p.out;
+  ka.idx = p.idx;
+  ka.H = (int)p.H;
+  ka.n = (int)p.n;
+  ka.keep = (int)p.keep;
+  ka.lcap = (int)((p.keep + 7) / 8 * 8);
+  ka.qt = kQTile;
+  ka.tiles = (int)((p.n + kQTile - 1) / kQTile);
+  ka.isd = (float)(1.0 / sqrt((double)p.d));
+  ka.exp_c = (float)(2.0 * (double)ka.isd * 1.4426950408889634);
+  const uint32_t vbytes = align16((uint32_t)p.n * rowb);
+  const uint32_t bias_bytes = fk ? align16((uint32_t)(p.n + kQTile - 1) * 4u) : 0u;
+  // as many waves as LDS allows (lists and candidate buffers are per wave)
+  const uint32_t per_wave = (uint32_t)ka.lcap * 8u + (fk ? 64u * 8u : 0u);
+  int nw = kMaxWaves;
+  while (nw > 1 && vbytes + bias_bytes + per_wave * nw > kLdsBytes) --nw;
+  if (vbytes + bias_bytes + per_wave * nw > kLdsBytes) return hipErrorInvalidValue;
+  ka.bias_off = vbytes;
+  ka.list_off = vbytes + bias_bytes;
+  ka.cand_off = ka.list_off + (uint32_t)ka.lcap * 8u * nw;
+  const uint32_t lds = ka.cand_off + (fk ? 64u * 8u * nw : 0u);
+  const dim3 grid((unsigned)(p.B * p.H * ka.tiles));
+  const dim3 block((unsigned)(64 * nw));
+  switch (NS) {
+    case 1: return launch_ns<1>(ka, fk, vk, grid, block, lds, s);
+    case 2: return launch_ns<2>(ka, fk, vk, grid, block, lds, s);
+    case 4: return launch_ns<4>(ka, fk, vk, grid, block, lds, s);
+    case 8: return launch_ns<8>(ka, fk, vk, grid, block, lds, s);
+    case 12: return launch_ns<12>(ka, fk, vk, grid, block, lds, s);
+    default: return launch_ns<16>(ka, fk, vk, grid, block, lds, s);
+  }
+}
+
+}  // namespace had

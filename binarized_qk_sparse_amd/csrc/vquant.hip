@@ -1,0 +1,131 @@
+// Per-channel int8 quantization of V (BinaryAttention, section 2.4: V is
+// quantized per channel to int8 because its channels can hold outliers).
+//   scale[c] = max_j |V[j][c]| / 127          (float32, correctly rounded)
+//   Vq[j][c] = clamp(rint(V[j][c] / scale[c]), -127, 127), 0 if scale is 0
+// A streaming pass bound by HBM bandwidth: a max pass over V, then a quantize
+// pass that reads V again and writes one byte per element.
+#include "had_device.hpp"
+#include "had_internal.h"
+#include "../../include/had.h"
+
+namespace had {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T>
+HAD_DEVICE void load8v(const T* p, float (&v)[8]);
+template <>
+HAD_DEVICE void load8v<float>(const float* p, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <>
+HAD_DEVICE void load8v<uint16_t>(const uint16_t* p, float (&v)[8]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x);
+  v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+  v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z);
+  v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void vmax_partial_kernel(const T* __restrict__ v, int64_t n,
+                                                                int64_t chunks, float* __restrict__ partial) {
+  constexpr int TPR = D / 8;
+  constexpr int RPP = kThreads / TPR;
+  __shared__ float red[RPP][D];
+  const int64_t bh = blockIdx.x / chunks;
+  const int64_t chunk = blockIdx.x % chunks;
+  const int t = threadIdx.x;
+  const int r_off = t / TPR, cg = t % TPR;
+  float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int64_t r0 = chunk * kVqChunk;
+  for (int k = 0; k < kVqChunk / RPP; ++k) {
+    const int64_t r = r0 + r_off + (int64_t)RPP * k;
+    if (r < n) {
+      float x[8];
+      load8v<T>(v + (bh * n + r) * D + 8 * cg, x);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) m[c] = fmaxf(m[c], fabsf(x[c]));
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) red[r_off][8 * cg + c] = m[c];
+  __syncthreads();
+  if (t < D) {
+    float acc = 0.0f;
+    for (int rp = 0; rp < RPP; ++rp) acc = fmaxf(acc, red[rp][t]);
+    partial[(bh * chunks + chunk) * D + t] = acc;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void vscale_kernel(const float* __restrict__ partial, int64_t BH,
+                                                          int64_t chunks, int D, float* __restrict__ scale) {
+  const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (id >= BH * D) return;
+  const int64_t bh = id / D, c = id % D;
+  float m = 0.0f;
+  for (int64_t k = 0; k < chunks; ++k) m = fmaxf(m, partial[(bh * chunks + k) * D + c]);
+  scale[id] = __fdiv_rn(m, 127.0f);
+}
+
+HAD_DEVICE uint32_t q8(float x, float s) {
+  if (!(s > 0.0f)) return 0u;
+  float r = rintf(__fdiv_rn(x, s));
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (uint32_t)((int32_t)r) & 0xffu;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void vq_kernel(const T* __restrict__ v, int64_t rows, int64_t n,
+                                                      const float* __restrict__ scale, int8_t* __restrict__ vq) {
+  constexpr int TPR = D / 8;
+  constexpr int RPP = kThreads / TPR;
+  const int t = threadIdx.x;
+  const int cg = t % TPR;
+  const int64_t r = (int64_t)blockIdx.x * RPP + t / TPR;
+  if (r >= rows) return;
+  float x[8];
+  load8v<T>(v + r * D + 8 * cg, x);
+  const float* s = scale + (r / n) * D + 8 * cg;
+  uint2 o;
+  o.x = q8(x[0], s[0]) | (q8(x[1], s[1]) << 8) | (q8(x[2], s[2]) << 16) | (q8(x[3], s[3]) << 24);
+  o.y = q8(x[4], s[4]) | (q8(x[5], s[5]) << 8) | (q8(x[6], s[6]) << 16) | (q8(x[7], s[7]) << 24);
+  *reinterpret_cast<uint2*>(vq + r * D + 8 * cg) = o;
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const VQuantParams& p, hipStream_t s) {
+  const T* v = static_cast<const T*>(p.v);
+  const int64_t chunks = vq_chunks(p.n);
+  hipLaunchKernelGGL((vmax_partial_kernel<T, D>), dim3((unsigned)(p.BH * chunks)), dim3(kThreads), 0, s, v,
+                     p.n, chunks, p.vmax_partial);
+  hipLaunchKernelGGL(vscale_kernel, dim3((unsigned)((p.BH * D + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     s, p.vmax_partial, p.BH, chunks, D, p.vscale);
+  const int64_t rows = p.BH * p.n;
+  constexpr int RPP = kThreads / (D / 8);
+  hipLaunchKernelGGL((vq_kernel<T, D>), dim3((unsigned)((rows + RPP - 1) / RPP)), dim3(kThreads), 0, s, v,
+                     rows, p.n, p.vscale, p.vq);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_dim(const VQuantParams& p, hipStream_t s) {
+  switch (p.d) {
+    case 32: return launch_typed<T, 32>(p, s);
+    case 64: return launch_typed<T, 64>(p, s);
+    case 128: return launch_typed<T, 128>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_vquant(const VQuantParams& p, hipStream_t s) {
+  return p.v_dtype == HAD_BF16 ? launch_dim<uint16_t>(p, s) : launch_dim<float>(p, s);
+}
+
+}  // namespace had

@@ -1,0 +1,122 @@
+"""Python binding of the C ABI: marshals torch device tensors into pointers.
+
+Every function here only checks shapes/dtypes, allocates outputs with torch
+and calls the same-named entry point of ``libhad.so`` on the current HIP
+stream.  All arithmetic runs in the library's gfx950 kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import (HAD_AV_F32, HAD_AV_Q8, HAD_BF16, HAD_F32, HAD_MEAN_SIGN,  # noqa: F401
+                   HAD_SIGN, HadError)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return HAD_F32
+    if t.dtype == torch.bfloat16:
+        return HAD_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def workspace_bytes(B: int, H: int, n: int, d: int) -> int:
+    return int(_lib.load().had_workspace_bytes(B, H, n, d))
+
+
+def workspace(B: int, H: int, n: int, d: int, device=None) -> torch.Tensor:
+    """A device byte buffer large enough for any entry point at these sizes."""
+    return torch.empty(max(workspace_bytes(B, H, n, d), 256), dtype=torch.uint8, device=device or "cuda")
+
+
+def had_pack(x: torch.Tensor, mode: int = HAD_SIGN, ws: Optional[torch.Tensor] = None
+             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """x [B,H,n,d] fp32/bf16 -> (bits int32 [B,H,n,d/32] holding uint32 words,
+    alpha f32 [B,H,n], mu f32 [B,H,d])."""
+    _dev(x, "x")
+    B, H, n, d = x.shape
+    bits = torch.empty((B, H, n, d // 32), dtype=torch.int32, device=x.device)
+    alpha = torch.empty((B, H, n), dtype=torch.float32, device=x.device)
+    mu = torch.empty((B, H, d), dtype=torch.float32, device=x.device)
+    if mode == HAD_MEAN_SIGN and ws is None:
+        ws = workspace(B, H, n, d, x.device)
+    wsz = 0 if ws is None else ws.numel()
+    st = _lib.load().had_pack(x.data_ptr(), _dtype_code(x), B, H, n, d, mode, bits.data_ptr(),
+                              alpha.data_ptr(), mu.data_ptr(), _ptr(ws), wsz, _stream())
+    _lib.check("had_pack", st)
+    return bits, alpha, mu
+
+
+def had_attention_topn(qbits: torch.Tensor, kbits: torch.Tensor, v: torch.Tensor, top_n: int, *,
+                       alpha_q: Optional[torch.Tensor] = None, alpha_k: Optional[torch.Tensor] = None,
+                       bias: Optional[torch.Tensor] = None, av_mode: int = HAD_AV_F32, want_idx: bool = False,
+                       ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """Top-N attention; returns out f32 [B,H,n,d] (and idx int32 [B,H,n,min(N,n)] if asked)."""
+    for t, nm in ((qbits, "qbits"), (kbits, "kbits"), (v, "v")):
+        _dev(t, nm)
+    B, H, n, d = v.shape
+    keep = min(int(top_n), n)
+    if out is None:
+        out = torch.empty((B, H, n, d), dtype=torch.float32, device=v.device)
+    idx = torch.empty((B, H, n, keep), dtype=torch.int32, device=v.device) if want_idx else None
+    if av_mode == HAD_AV_Q8 and ws is None:
+        ws = workspace(B, H, n, d, v.device)
+    wsz = 0 if ws is None else ws.numel()
+    st = _lib.load().had_attention_topn(qbits.data_ptr(), kbits.data_ptr(), _ptr(alpha_q), _ptr(alpha_k),
+                                        _ptr(bias), v.data_ptr(), _dtype_code(v), B, H, n, d, int(top_n),
+                                        av_mode, out.data_ptr(), _ptr(idx), _ptr(ws), wsz, _stream())
+    _lib.check("had_attention_topn", st)
+    return (out, idx) if want_idx else out
+
+
+def binattn_dense_q8(qbits: torch.Tensor, kbits: torch.Tensor, v: torch.Tensor, *,
+                     alpha_q: Optional[torch.Tensor] = None, alpha_k: Optional[torch.Tensor] = None,
+                     bias: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Dense softmax, uint8 A x per-channel int8 V; returns out f32 [B,H,n,d]."""
+    for t, nm in ((qbits, "qbits"), (kbits, "kbits"), (v, "v")):
+        _dev(t, nm)
+    B, H, n, d = v.shape
+    if out is None:
+        out = torch.empty((B, H, n, d), dtype=torch.float32, device=v.device)
+    if ws is None:
+        ws = workspace(B, H, n, d, v.device)
+    st = _lib.load().binattn_dense_q8(qbits.data_ptr(), kbits.data_ptr(), _ptr(alpha_q), _ptr(alpha_k),
+                                      _ptr(bias), v.data_ptr(), _dtype_code(v), B, H, n, d, out.data_ptr(),
+                                      ws.data_ptr(), ws.numel(), _stream())
+    _lib.check("binattn_dense_q8", st)
+    return out
+
+
+def workspace_view(ws: torch.Tensor, B: int, H: int, n: int, d: int):
+    """(vq int8 [B,H,n,d], vscale f32 [B,H,d]) views of a workspace after a quantized call."""
+    import math
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    chunks = math.ceil(n / 256)
+    off_vq = a256(8 * B * H * chunks * d)
+    off_sc = a256(off_vq + B * H * n * d)
+    vq = ws[off_vq:off_vq + B * H * n * d].view(torch.int8).view(B, H, n, d)
+    sc = ws[off_sc:off_sc + 4 * B * H * d].view(torch.float32).view(B, H, d)
+    return vq, sc

@@ -1,0 +1,159 @@
+/*
+ * had.h -- C ABI of the binarized-QK attention library (gfx950 / MI355X).
+ *
+ * The method (forward pass only):
+ *   1. Q and K become {-1,+1} codes, bit-packed along head_dim:
+ *      plain sign (Hamming Attention Distillation, abstract) or the
+ *      mean-centred scaled sign alpha*sign(x - mu) of BinaryAttention
+ *      (section 2.2, scaled binarized representation).  sign(0) = +1.
+ *   2. Logit of query i and key j (BinaryAttention section 2.3, attention with
+ *      bias; section 2.2, XNOR/popcount similarity):
+ *         l = alpha_q[i]*alpha_k[j]*(d - 2*popcount(q XOR k)) / sqrt(d) + B[i][j]
+ *   3. Optional per-query top-N (Hamming Attention Distillation, summary
+ *      "main points"/"method": keep the N largest attention scores of each
+ *      query), ties going to the lower key index.
+ *   4. Softmax over the kept keys only, then A*V either in fp32
+ *      (Hamming Attention Distillation keeps everything but K/Q full
+ *      precision) or with A as uint8 at scale 1/255 and V as per-channel int8
+ *      with integer accumulation (BinaryAttention section 2.4, mixed
+ *      quantization).
+ *
+ * Conventions for every entry point
+ *  - Tensors are contiguous, row-major, [B, H, n, .] (batch, head, token, .).
+ *  - All tensor pointers are DEVICE pointers on the current HIP device.  The
+ *    caller owns every buffer; the library never allocates or frees memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls only enqueue work and return; buffers must stay alive until the
+ *    stream has executed it.  The library keeps no state between calls and may
+ *    be called from several host threads.
+ *  - Arguments are validated on the host before anything is enqueued; on an
+ *    error status nothing is launched and no output is touched.  Faults that
+ *    happen on the device surface at the caller's next synchronisation.
+ *  - d must be 32, 64 or 128 (bits per token: d/32 uint32 words) for packing;
+ *    the attention entry points take d = 64.
+ *  - Relative-position bias: `bias_table` is float32 [H, 2n-1] and
+ *    B[i][j] = bias_table[h][j - i + n - 1]; NULL means B = 0.
+ *  - alpha pointers: float32 [B, H, n]; NULL means alpha = 1.
+ *  - Inputs must be finite (no NaN/Inf); a NaN input gets code +1.
+ */
+#ifndef HAD_H
+#define HAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HAD_ABI_VERSION 1
+
+/* status codes */
+#define HAD_OK 0
+#define HAD_ERR_INVALID_ARG 1 /* NULL required pointer, size <= 0, top_n < 1, unknown enum */
+#define HAD_ERR_UNSUPPORTED 2 /* a size outside what the kernels are built for */
+#define HAD_ERR_WORKSPACE 3   /* workspace NULL or smaller than had_workspace_bytes() */
+#define HAD_ERR_HIP 4         /* the HIP runtime reported an error at launch */
+
+/* element types of x / v */
+#define HAD_F32 0
+#define HAD_BF16 1
+
+/* binarization modes */
+#define HAD_SIGN 0      /* code = sign(x); alpha = 1 */
+#define HAD_MEAN_SIGN 1 /* code = sign(x - mu); alpha = mean_c |x - mu| */
+
+/* A*V modes */
+#define HAD_AV_F32 0 /* fp32 probabilities times V, fp32 accumulation */
+#define HAD_AV_Q8 1  /* uint8 A (scale 1/255) times per-channel int8 V, int32 accumulation */
+
+/* Largest sizes the kernels accept. */
+#define HAD_MAX_N 65536
+#define HAD_MAX_TOPN 1024
+
+int had_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* had_status_str(int status);
+
+/*
+ * Bytes of device workspace any entry point needs for these sizes (a single
+ * buffer of this size serves had_pack, had_attention_topn and
+ * binattn_dense_q8).  Multiple of 256.  Contents need not be initialised.
+ */
+size_t had_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d);
+
+/*
+ * had_pack -- binarize and bit-pack one of Q or K.
+ * (Hamming Attention Distillation, abstract: {-1,+1} keys and queries;
+ *  BinaryAttention section 2.2: x~ = alpha * sign(x - mu).)
+ *
+ *  x        [B,H,n,d] of x_dtype (HAD_F32 or HAD_BF16)
+ *  mode     HAD_SIGN or HAD_MEAN_SIGN
+ *  bits     out uint32 [B,H,n,d/32]: bit (c%32) of word c/32 is 1 iff the code
+ *           of channel c is -1, i.e. iff y < 0 where y = x (SIGN) or
+ *           y = float32(x - mu) (MEAN_SIGN).
+ *  alpha    out float32 [B,H,n]: MEAN_SIGN: float32(sum_c |y| / d) with the sum
+ *           in float64; SIGN: filled with 1.0f.  Required for MEAN_SIGN,
+ *           may be NULL for SIGN.
+ *  mu       out float32 [B,H,d]: MEAN_SIGN: float32(sum_i x / n), sum in
+ *           float64, mean over tokens per (batch, head, channel); SIGN: 0.
+ *           Required for MEAN_SIGN, may be NULL for SIGN.
+ *  workspace, workspace_bytes: device scratch of at least
+ *           had_workspace_bytes(B,H,n,d) bytes (MEAN_SIGN only; may be NULL for SIGN).
+ */
+int had_pack(const void* x, int x_dtype, int64_t B, int64_t H, int64_t n, int64_t d, int mode,
+             uint32_t* bits, float* alpha, float* mu, void* workspace, size_t workspace_bytes,
+             void* stream);
+
+/*
+ * had_attention_topn -- attention over each query's top-N keys.
+ * (Hamming Attention Distillation, summary "main points"/"method": per query
+ *  keep the top N attention scores, prune the rest before softmax and V
+ *  accumulation; BinaryAttention sections 2.3-2.4 for the bias and the
+ *  quantized A*V.)
+ *
+ *  qbits, kbits   uint32 [B,H,n,d/32] from had_pack
+ *  alpha_q, alpha_k  float32 [B,H,n] or NULL (alpha = 1)
+ *  bias_table     float32 [H,2n-1] or NULL (B = 0)
+ *  v              [B,H,n,d] of v_dtype (HAD_F32 or HAD_BF16)
+ *  top_n          N >= 1; N >= n keeps every key (dense softmax)
+ *  av_mode        HAD_AV_F32 or HAD_AV_Q8
+ *  out            out float32 [B,H,n,d]
+ *  idx_out        optional out int32 [B,H,n,min(N,n)]: kept key indices of
+ *                 each query in ascending order; NULL to skip
+ *  workspace      >= had_workspace_bytes(B,H,n,d) bytes (HAD_AV_Q8 only; may
+ *                 be NULL for HAD_AV_F32).  On return (after the stream has
+ *                 run) it holds the int8 V and its per-channel scales.
+ *
+ *  Logit, in float32 with each operation rounded as written:
+ *      t = alpha_q*alpha_k;  u = t*(d-2h);  v = u*float(1/sqrt(d));  l = v + B
+ *  The kept set is the N largest l, ties to the lower key index; it is exact.
+ *  Softmax in float32 over the kept set.  HAD_AV_Q8: scale_c = max_j|V[j][c]|/127
+ *  over all n tokens, Vq = clamp(rint(V/scale_c), -127, 127),
+ *  A_q = clamp(rint(255 p), 0, 255), O = float(sum A_q*Vq) * scale_c / 255.
+ */
+int had_attention_topn(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q,
+                       const float* alpha_k, const float* bias_table, const void* v, int v_dtype,
+                       int64_t B, int64_t H, int64_t n, int64_t d, int64_t top_n, int av_mode,
+                       float* out, int32_t* idx_out, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * binattn_dense_q8 -- BinaryAttention forward: dense softmax over all keys,
+ * uint8 A (scale 1/255) times per-channel int8 V with int32 accumulation
+ * (BinaryAttention section 2.4: O = dequant(matmul(quant_u8(A), quant_i8(V)))).
+ * Same arguments and arithmetic as had_attention_topn with top_n = n and
+ * av_mode = HAD_AV_Q8; the contraction runs on int8 matrix cores.
+ * workspace is required (>= had_workspace_bytes(B,H,n,d)).
+ */
+int binattn_dense_q8(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q,
+                     const float* alpha_k, const float* bias_table, const void* v, int v_dtype,
+                     int64_t B, int64_t H, int64_t n, int64_t d, float* out, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HAD_H */

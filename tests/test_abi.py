@@ -1,0 +1,118 @@
+"""The C-ABI library loads without a GPU, exports every declared entry point,
+and rejects bad arguments before touching the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from binarized_qk_sparse_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "had.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(had_\w+|binattn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = _declared_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_header_constants_match_binding():
+    with open(os.path.join(ROOT, "include", "had.h")) as f:
+        text = f.read()
+    defs = dict(re.findall(r"#define\s+(HAD_\w+)\s+(\d+)", text))
+    for k, v in defs.items():
+        if hasattr(_lib, k):
+            assert getattr(_lib, k) == int(v), k
+
+
+def test_status_strings_and_version():
+    assert _lib.load().had_abi_version() == _lib.HAD_ABI_VERSION
+    for code, name in [(0, "HAD_OK"), (1, "HAD_ERR_INVALID_ARG"), (2, "HAD_ERR_UNSUPPORTED"),
+                       (3, "HAD_ERR_WORKSPACE"), (4, "HAD_ERR_HIP"), (99, "HAD_ERR_UNKNOWN")]:
+        assert _lib.status_str(code) == name
+
+
+def test_workspace_bytes():
+    lib = _lib.load()
+    a = lib.had_workspace_bytes(1, 1, 100, 64)
+    b = lib.had_workspace_bytes(2, 1, 100, 64)
+    assert a > 0 and a % 256 == 0 and b > a
+    assert lib.had_workspace_bytes(0, 1, 100, 64) == 0
+    # c5 shape: int8 V plus scales and partials
+    assert lib.had_workspace_bytes(1, 16, 16384, 64) >= 16 * 16384 * 64
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(x=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(bits=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(B=0), _lib.HAD_ERR_INVALID_ARG),
+    (dict(n=-1), _lib.HAD_ERR_INVALID_ARG),
+    (dict(dtype=7), _lib.HAD_ERR_INVALID_ARG),
+    (dict(mode=5), _lib.HAD_ERR_INVALID_ARG),
+    (dict(d=48), _lib.HAD_ERR_UNSUPPORTED),
+    (dict(d=256), _lib.HAD_ERR_UNSUPPORTED),
+    (dict(n=70000), _lib.HAD_ERR_UNSUPPORTED),
+    (dict(mode=1, alpha=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(mode=1, ws=None), _lib.HAD_ERR_WORKSPACE),
+    (dict(mode=1, wsz=16), _lib.HAD_ERR_WORKSPACE),
+])
+def test_pack_validation(args, want):
+    a = dict(x=FAKE, dtype=_lib.HAD_BF16, B=1, H=1, n=64, d=64, mode=0, bits=FAKE, alpha=FAKE, mu=FAKE,
+             ws=FAKE, wsz=1 << 30)
+    a.update(args)
+    st = _lib.load().had_pack(a["x"], a["dtype"], a["B"], a["H"], a["n"], a["d"], a["mode"], a["bits"],
+                              a["alpha"], a["mu"], a["ws"], a["wsz"], None)
+    assert st == want
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(q=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(v=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(out=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(top_n=0), _lib.HAD_ERR_INVALID_ARG),
+    (dict(av=3), _lib.HAD_ERR_INVALID_ARG),
+    (dict(vdt=9), _lib.HAD_ERR_INVALID_ARG),
+    (dict(H=0), _lib.HAD_ERR_INVALID_ARG),
+    (dict(d=128), _lib.HAD_ERR_UNSUPPORTED),
+    (dict(n=1 << 20), _lib.HAD_ERR_UNSUPPORTED),
+    (dict(top_n=5000, n=8192), _lib.HAD_ERR_UNSUPPORTED),
+    (dict(av=1, ws=None), _lib.HAD_ERR_WORKSPACE),
+    (dict(av=1, wsz=100), _lib.HAD_ERR_WORKSPACE),
+    (dict(av=1, ws=ctypes.c_void_p(0x1001)), _lib.HAD_ERR_WORKSPACE),
+])
+def test_attention_validation(args, want):
+    a = dict(q=FAKE, k=FAKE, aq=None, ak=None, bias=None, v=FAKE, vdt=_lib.HAD_BF16, B=1, H=1, n=256, d=64,
+             top_n=30, av=0, out=FAKE, idx=None, ws=FAKE, wsz=1 << 30)
+    a.update(args)
+    st = _lib.load().had_attention_topn(a["q"], a["k"], a["aq"], a["ak"], a["bias"], a["v"], a["vdt"], a["B"],
+                                        a["H"], a["n"], a["d"], a["top_n"], a["av"], a["out"], a["idx"], a["ws"],
+                                        a["wsz"], None)
+    assert st == want
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(k=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(n=0), _lib.HAD_ERR_INVALID_ARG),
+    (dict(d=32), _lib.HAD_ERR_UNSUPPORTED),
+    (dict(ws=None), _lib.HAD_ERR_WORKSPACE),
+    (dict(wsz=0), _lib.HAD_ERR_WORKSPACE),
+])
+def test_dense_validation(args, want):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, B=2, H=3, n=197, d=64, out=FAKE, ws=FAKE, wsz=1 << 30)
+    a.update(args)
+    st = _lib.load().binattn_dense_q8(a["q"], a["k"], None, None, None, a["v"], _lib.HAD_BF16, a["B"], a["H"],
+                                      a["n"], a["d"], a["out"], a["ws"], a["wsz"], None)
+    assert st == want

@@ -1,0 +1,200 @@
+"""GPU parity: every entry point of libhad.so against the CPU oracle on the same seeded inputs.
+
+Bar: code bits, alpha, mu, Hamming-derived top-N index sets and int8 V are
+bit-exact; fp32 outputs within 1e-3 relative + 1e-4 absolute; the quantized
+path within one int8 LSB of V (the channel's scale) per output element.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from binarized_qk_sparse_amd import ops, synth
+from parity_util import assert_close, f32, packed_inputs, q8_tolerance, sample_rows, u32
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    ops._lib.load()
+
+
+# ------------------------------------------------------------------ packing
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_pack_full_size_configs(name):
+    w = synth.workload(name)
+    g = synth.generate(w)
+    for t in ("q", "k"):
+        x = g[t]
+        bits, alpha, mu = ops.had_pack(x.to(DEV), w.mode)
+        torch.cuda.synchronize()
+        ob, oa, om = oracle.pack(f32(x), w.mode)
+        assert np.array_equal(u32(bits), ob), f"{name} {t}: code bits differ"
+        assert np.array_equal(alpha.cpu().numpy(), oa), f"{name} {t}: alpha differs"
+        assert np.array_equal(mu.cpu().numpy(), om), f"{name} {t}: mu differs"
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("n", [1, 3, 255, 257, 700])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("mode", [synth.SIGN, synth.MEAN_SIGN])
+def test_pack_ragged_and_special_values(d, n, dtype, mode):
+    g = np.random.default_rng([3, d, n])
+    x = (g.standard_normal((2, 3, n, d)) + g.standard_normal((1, 3, 1, d))).astype(np.float32)
+    x[0, 0, 0, : d // 2] = 0.0
+    x[0, 1, 0, : d // 2] = -0.0
+    x[1, 2, :, 1] = 1.5  # a constant channel: x - mu is exactly 0 there
+    xt = torch.from_numpy(x).to(dtype)
+    bits, alpha, mu = ops.had_pack(xt.to(DEV), mode)
+    torch.cuda.synchronize()
+    ob, oa, om = oracle.pack(f32(xt), mode)
+    assert np.array_equal(u32(bits), ob)
+    assert np.array_equal(alpha.cpu().numpy(), oa)
+    assert np.array_equal(mu.cpu().numpy(), om)
+
+
+# ------------------------------------------------------------------ top-N, fp32 A*V
+def _topn_case(B, H, n, N, vdtype, mode, bias, seed, av=synth.AV_F32):
+    g = np.random.default_rng([11, B, H, n, N, seed])
+    xq = (g.standard_normal((B, H, n, 64)) + 0.3 * g.standard_normal((1, H, 1, 64))).astype(np.float32)
+    xk = (g.standard_normal((B, H, n, 64)) + 0.3 * g.standard_normal((1, H, 1, 64))).astype(np.float32)
+    v = torch.from_numpy(g.standard_normal((B, H, n, 64)).astype(np.float32)).to(vdtype)
+    T = (0.05 * g.standard_normal((H, 2 * n - 1))).astype(np.float32) if bias else None
+    qb, aq, _ = oracle.pack(xq, mode)
+    kb, ak, _ = oracle.pack(xk, mode)
+    if mode == synth.SIGN:
+        aq = ak = None
+    return qb, kb, aq, ak, T, v
+
+
+def _run_topn(qb, kb, aq, ak, T, v, N, av=synth.AV_F32):
+    dt = lambda a: None if a is None else torch.from_numpy(a).to(DEV)
+    out, idx = ops.had_attention_topn(dt(qb.view(np.int32)), dt(kb.view(np.int32)), v.to(DEV), N,
+                                      alpha_q=dt(aq), alpha_k=dt(ak), bias=dt(T), av_mode=av, want_idx=True)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), idx.cpu().numpy()
+
+
+@pytest.mark.parametrize("n", [1, 5, 63, 64, 65, 197, 256, 300, 513, 1024])
+@pytest.mark.parametrize("N", [1, 7, 30, 120, 5000])
+@pytest.mark.parametrize("keys", ["int", "bias", "alpha_bias"])
+def test_topn_fp32_matches_oracle(n, N, keys):
+    vdtype = torch.float32 if (n <= 512 and N == 7) else torch.bfloat16
+    mode = synth.MEAN_SIGN if keys == "alpha_bias" else synth.SIGN
+    qb, kb, aq, ak, T, v = _topn_case(1, 2, n, N, vdtype, mode, keys != "int", seed=1)
+    out, idx = _run_topn(qb, kb, aq, ak, T, v, N)
+    ref = oracle.attention(qb, kb, f32(v), alpha_q=aq, alpha_k=ak, bias=T, top_n=N, want_idx=True)
+    assert np.array_equal(idx, ref["idx"]), "kept index sets differ"
+    assert_close(out, ref["out"], f"n={n} N={N} {keys}")
+
+
+def test_topn_heavy_ties():
+    # only a handful of distinct codes: most logits tie and the lower index must win
+    g = np.random.default_rng(5)
+    B, H, n = 2, 3, 300
+    base = g.standard_normal((4, 64)).astype(np.float32)
+    xq = base[g.integers(0, 4, (B, H, n))]
+    xk = base[g.integers(0, 4, (B, H, n))]
+    v = torch.from_numpy(g.standard_normal((B, H, n, 64)).astype(np.float32))
+    qb, _, _ = oracle.pack(xq, oracle.SIGN)
+    kb, _, _ = oracle.pack(xk, oracle.SIGN)
+    T = np.zeros((H, 2 * n - 1), np.float32)  # float-key path with exact ties
+    for bias in (None, T):
+        for N in (1, 10, 77, 299):
+            out, idx = _run_topn(qb, kb, None, None, bias, v, N)
+            ref = oracle.attention(qb, kb, f32(v), bias=bias, top_n=N, want_idx=True)
+            assert np.array_equal(idx, ref["idx"])
+            assert_close(out, ref["out"], f"ties N={N}")
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_topn_configs_full(name):
+    w = synth.workload(name)
+    p = packed_inputs(w)
+    out, idx = ops.had_attention_topn(p["dq"], p["dk"], p["dv"], w.top_n, alpha_q=p["daq"], alpha_k=p["dak"],
+                                      bias=p["dbias"], want_idx=True)
+    torch.cuda.synchronize()
+    ref = oracle.attention(p["oq"], p["ok"], f32(p["v"]), alpha_q=p["oaq"], alpha_k=p["oak"], bias=p["obias"],
+                           top_n=w.top_n, want_idx=True)
+    assert np.array_equal(idx.cpu().numpy(), ref["idx"])
+    assert_close(out.cpu().numpy(), ref["out"], name)
+
+
+@pytest.mark.parametrize("n", synth.C3_SWEEP)
+def test_topn_c3_sweep_sampled(n):
+    w = synth.c3(n)
+    p = packed_inputs(w)
+    out, idx = ops.had_attention_topn(p["dq"], p["dk"], p["dv"], w.top_n, want_idx=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.B * w.H * n, 3000, n)
+    ref = oracle.attention(p["oq"], p["ok"], f32(p["v"]), top_n=w.top_n, rows=rows, want_idx=True)
+    keep = min(w.top_n, n)
+    assert np.array_equal(idx.cpu().numpy().reshape(-1, keep)[rows], ref["idx"])
+    assert_close(out.cpu().numpy().reshape(-1, 64)[rows], ref["out"], w.name)
+
+
+def test_topn_deterministic():
+    w = synth.c3(512)
+    p = packed_inputs(w)
+    a = ops.had_attention_topn(p["dq"], p["dk"], p["dv"], w.top_n)
+    b = ops.had_attention_topn(p["dq"], p["dk"], p["dv"], w.top_n)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ quantized paths
+def _check_q8(out, ws_vq, ws_sc, ref, rows, n, what):
+    assert np.array_equal(ws_vq, ref["vq"]), f"{what}: int8 V differs"
+    assert np.array_equal(ws_sc, ref["vscale"]), f"{what}: V scales differ"
+    tol = q8_tolerance(ref["vscale"], rows, n)
+    diff = np.abs(out - ref["out"])
+    assert np.all(diff <= tol + 1e-6), f"{what}: {int((diff > tol).sum())} elements beyond one int8 LSB"
+
+
+@pytest.mark.parametrize("n,N", [(5, 3), (197, 30), (256, 256), (700, 64), (1024, 120)])
+def test_topn_q8_matches_oracle(n, N):
+    qb, kb, aq, ak, T, v = _topn_case(2, 2, n, N, torch.bfloat16, synth.MEAN_SIGN, True, seed=2)
+    dt = lambda a: torch.from_numpy(a).to(DEV)
+    ws = ops.workspace(2, 2, n, 64)
+    out, idx = ops.had_attention_topn(dt(qb.view(np.int32)), dt(kb.view(np.int32)), v.to(DEV), N, alpha_q=dt(aq),
+                                      alpha_k=dt(ak), bias=dt(T), av_mode=ops.HAD_AV_Q8, want_idx=True, ws=ws)
+    torch.cuda.synchronize()
+    vq, sc = ops.workspace_view(ws, 2, 2, n, 64)
+    ref = oracle.attention(qb, kb, f32(v), alpha_q=aq, alpha_k=ak, bias=T, top_n=N, av_mode=oracle.AV_Q8,
+                           want_idx=True)
+    assert np.array_equal(idx.cpu().numpy(), ref["idx"])
+    rows = np.arange(2 * 2 * n)
+    _check_q8(out.cpu().numpy().reshape(-1, 64), vq.cpu().numpy(), sc.cpu().numpy(),
+              {**ref, "out": ref["out"].reshape(-1, 64)}, rows, n, f"q8 n={n}")
+
+
+@pytest.mark.parametrize("n", [1, 16, 33, 197, 256])
+def test_dense_q8_small(n):
+    qb, kb, aq, ak, T, v = _topn_case(2, 3, n, n, torch.bfloat16, synth.MEAN_SIGN, True, seed=3)
+    dt = lambda a: torch.from_numpy(a).to(DEV)
+    ws = ops.workspace(2, 3, n, 64)
+    out = ops.binattn_dense_q8(dt(qb.view(np.int32)), dt(kb.view(np.int32)), v.to(DEV), alpha_q=dt(aq),
+                               alpha_k=dt(ak), bias=dt(T), ws=ws)
+    torch.cuda.synchronize()
+    vq, sc = ops.workspace_view(ws, 2, 3, n, 64)
+    ref = oracle.attention(qb, kb, f32(v), alpha_q=aq, alpha_k=ak, bias=T, top_n=None, av_mode=oracle.AV_Q8)
+    _check_q8(out.cpu().numpy().reshape(-1, 64), vq.cpu().numpy(), sc.cpu().numpy(),
+              {**ref, "out": ref["out"].reshape(-1, 64)}, np.arange(2 * 3 * n), n, f"dense n={n}")
+
+
+def test_dense_q8_c4_full_size_sampled():
+    w = synth.workload("c4")
+    p = packed_inputs(w)
+    ws = ops.workspace(w.B, w.H, w.n, w.d)
+    out = ops.binattn_dense_q8(p["dq"], p["dk"], p["dv"], alpha_q=p["daq"], alpha_k=p["dak"], bias=p["dbias"],
+                               ws=ws)
+    torch.cuda.synchronize()
+    vq, sc = ops.workspace_view(ws, w.B, w.H, w.n, w.d)
+    rows = sample_rows(w.B * w.H * w.n, 6000, 4)
+    ref = oracle.attention(p["oq"], p["ok"], f32(p["v"]), alpha_q=p["oaq"], alpha_k=p["oak"], bias=p["obias"],
+                           top_n=None, av_mode=oracle.AV_Q8, rows=rows)
+    _check_q8(out.cpu().numpy().reshape(-1, 64)[rows], vq.cpu().numpy(), sc.cpu().numpy(), ref, rows, w.n, "c4")
