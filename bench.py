@@ -1,0 +1,277 @@
+"""Benchmark of the binarized-QK attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3@1024]
+
+A step is one pass of the whole path over one batch already resident in HBM:
+pack Q, pack K (and quantize V on the q8 paths), then attention.  The step is
+captured once into a HIP graph and replayed, so the timed region holds GPU
+work only.  The line printed on stdout is the only output on stdout:
+
+  value         query-key pairs per second of the whole step (B*H*n^2 / time)
+  roofline      the dominant kernel (attention) against the VALU issue roof:
+                algorithmic VALU lane-slots per launch / the kernel's average
+                duration (HIP events on the stream it runs on), against
+                256 CU * 64 lanes * 2.4 GHz
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "binarized-attention QK pairs/sec at n=1024,12 heads; % of roofline"
+VALU_PEAK = 256 * 64 * 2.4e9  # lane-slots per second: 256 CUs x 64 lanes x 2.4 GHz
+HBM_PEAK = 8.0e12
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_slots(w) -> float:
+    """VALU lane-slots the method needs per attention launch.
+
+    Per query row: n * (2W + 1 + F) for the logits (XOR and popcount per
+    32-bit word, one compare for the selection, F = 4 conversion/scale/bias
+    ops when alpha or a bias is present) plus, over the kept keys,
+    6 (exp at quarter rate + subtract + sum) + d/2 (fp32 FMA, two per slot on
+    packed hardware) for the fp32 A*V, or + d/4 (four 8-bit products per slot)
+    for the int8 A*V; the dense int8 path adds 9 per key (max, exp, sum,
+    quantize) and its contraction runs on the matrix cores.
+    """
+    W = w.d // 32
+    F = 4 if (w.bias or w.mode == 1) else 0
+    keep = w.kept
+    if w.top_n is None:
+        per_row = w.n * (2 * W + F + 9)
+    else:
+        per_row = w.n * (2 * W + 1 + F) + keep * (6 + (w.d / 2 if w.av_mode == 0 else w.d / 4))
+    return per_row * w.B * w.H * w.n
+
+
+def algorithmic_bytes(w) -> float:
+    """HBM bytes the attention launch must move: codes, scales, bias table, V (or int8 V), O."""
+    bh = w.B * w.H
+    b = 2 * w.n * w.d / 8
+    if w.mode == 1:
+        b += 2 * 4 * w.n
+    if w.bias:
+        b += 4 * (2 * w.n - 1) / w.B
+    vbytes = 2 if w.dtype == "bf16" else 4
+    b += w.n * w.d * (1 if w.av_mode == 1 else vbytes) + (4 * w.d if w.av_mode == 1 else 0)
+    b += 4 * w.n * w.d
+    return b * bh
+
+
+def traffic_from_profile(kernel_src: str):
+    """HBM bytes per launch from the committed rocprof counter summary, if it was
+    taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "topn_c3_n1024_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(kernel_src, "rb") as f:
+        h = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("kernel_sha256") != h:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, g, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of rows of the same workload."""
+    import numpy as np
+
+    import oracle
+
+    q = g["q"].float().numpy()
+    k = g["k"].float().numpy()
+    v = g["v"].float().numpy()
+    t0 = time.perf_counter()
+    qb, aq, _ = oracle.pack(q, w.mode)
+    kb, ak, _ = oracle.pack(k, w.mode)
+    t_pack = time.perf_counter() - t0
+    if w.mode == 0:
+        aq = ak = None
+    bias = None if g["bias"] is None else g["bias"].numpy()
+    total = w.B * w.H * w.n
+    rows_done, t_att, count = 0, 0.0, 256
+    rng = np.random.default_rng(12345)
+    # doubling seeded samples of query rows until the budget is spent or the
+    # sample covers as many rows as the workload holds
+    while t_att < budget_s and rows_done < total:
+        size = min(count, total - rows_done)
+        rows = np.sort(rng.choice(total, size=size, replace=False)).astype(np.int64)
+        t1 = time.perf_counter()
+        oracle.attention(qb, kb, v, alpha_q=aq, alpha_k=ak, bias=bias, top_n=w.top_n, av_mode=w.av_mode, rows=rows)
+        t_att += time.perf_counter() - t1
+        rows_done += len(rows)
+        count *= 2
+    per_row = t_att / rows_done + t_pack / total
+    value = w.n / per_row  # pairs per second
+    return {
+        "value": value,
+        "unit": "pairs/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": f"{rows_done} query rows of {w.name} (random, seeded) in {t_att:.1f} s plus the full Q/K pack "
+                  f"({t_pack:.2f} s) scaled per row",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c3@1024")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
+              f"(batch, head) with no communication, so the N-GPU figure is N times the one-GPU figure.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from binarized_qk_sparse_amd import ops, synth
+
+    w = synth.workload(args.config)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = synth.generate(w)
+    q, k, v = (g[t].to(dev) for t in ("q", "k", "v"))
+    bias = None if g["bias"] is None else g["bias"].to(dev)
+    ws = ops.workspace(w.B, w.H, w.n, w.d, dev)
+    out = torch.empty((w.B, w.H, w.n, w.d), dtype=torch.float32, device=dev)
+    lib = ops._lib.load()
+    dt = ops._dtype_code(q)
+    W = w.d // 32
+    qb = torch.empty((w.B, w.H, w.n, W), dtype=torch.int32, device=dev)
+    kb = torch.empty_like(qb)
+    aq = torch.empty((w.B, w.H, w.n), dtype=torch.float32, device=dev)
+    ak = torch.empty_like(aq)
+    mq = torch.empty((w.B, w.H, w.d), dtype=torch.float32, device=dev)
+    mk = torch.empty_like(mq)
+    pa = aq.data_ptr() if w.mode == 1 else None
+    pk = ak.data_ptr() if w.mode == 1 else None
+    pb = None if bias is None else bias.data_ptr()
+    def pack():
+        s = torch.cuda.current_stream().cuda_stream  # the capture stream while a graph records
+        ops._lib.check("had_pack", lib.had_pack(q.data_ptr(), dt, w.B, w.H, w.n, w.d, w.mode, qb.data_ptr(),
+                                                aq.data_ptr(), mq.data_ptr(), ws.data_ptr(), ws.numel(), s))
+        ops._lib.check("had_pack", lib.had_pack(k.data_ptr(), dt, w.B, w.H, w.n, w.d, w.mode, kb.data_ptr(),
+                                                ak.data_ptr(), mk.data_ptr(), ws.data_ptr(), ws.numel(), s))
+
+    def attend():
+        s = torch.cuda.current_stream().cuda_stream
+        if w.top_n is None:
+            st = lib.binattn_dense_q8(qb.data_ptr(), kb.data_ptr(), pa, pk, pb, v.data_ptr(), dt, w.B, w.H, w.n,
+                                      w.d, out.data_ptr(), ws.data_ptr(), ws.numel(), s)
+        else:
+            st = lib.had_attention_topn(qb.data_ptr(), kb.data_ptr(), pa, pk, pb, v.data_ptr(), dt, w.B, w.H, w.n,
+                                        w.d, w.top_n, w.av_mode, out.data_ptr(), None, ws.data_ptr(), ws.numel(), s)
+        ops._lib.check("attention", st)
+
+    def step():
+        pack()
+        attend()
+
+    # eager warm-up (also initialises the kernels' one-time launch attributes)
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    dt_s = (time.perf_counter() - t0) / args.steps
+    log(f"{w.name}: step {dt_s * 1e6:.1f} us over {args.steps} graph replays")
+
+    # the dominant kernel alone: HIP events on the stream it is launched on
+    att_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(att_graph):
+        attend()
+    for _ in range(5):
+        att_graph.replay()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = max(args.steps, 50)
+    stream = torch.cuda.current_stream()  # graph replays run on the replaying stream
+    e0.record(stream)
+    for _ in range(reps):
+        att_graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_att = e0.elapsed_time(e1) / 1e3 / reps
+    log(f"{w.name}: attention {t_att * 1e6:.2f} us per launch (HIP events, {reps} launches)")
+
+    slots = algorithmic_slots(w)
+    achieved = slots / t_att
+    src = os.path.join(ROOT, "binarized_qk_sparse_amd", "csrc", "dense_q8.hip" if w.top_n is None else "topn.hip")
+    traffic = traffic_from_profile(src) if args.config == "c3@1024" else None
+    roof = {
+        "bound": "alu",
+        "achieved": achieved / 1e12,
+        "peak": VALU_PEAK / 1e12,
+        "unit": "Tlane-slot/s",
+        "frac": achieved / VALU_PEAK,
+        "traffic": traffic,
+        "kernel": "topn_resident_kernel" if w.top_n is not None else "dense_q8_kernel",
+        "kernel_us": t_att * 1e6,
+        "slots_per_launch": slots,
+        "hbm_bytes_per_launch_alg": algorithmic_bytes(w),
+        "hbm_frac": algorithmic_bytes(w) / t_att / HBM_PEAK,
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, g, args.cpu_budget)
+        log(f"cpu baseline: {cpu['value']:.3e} pairs/s on {cpu['cores']} threads ({cpu['sample']})")
+    kept = "dense" if w.top_n is None else f"N={w.top_n}"
+    line = {
+        "metric": METRIC,
+        "value": w.pairs / dt_s,
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dt_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "b1+f32" if w.av_mode == 0 else "b1+u8/i8",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: B={w.B} H={w.H} n={w.n} d={w.d} {kept} {w.dtype} "
+                        f"{'plain sign' if w.mode == 0 else 'mean-centred scaled sign'}"
+                        f"{' + rel-pos bias' if w.bias else ''}, {'fp32' if w.av_mode == 0 else 'uint8 x int8'} A*V",
+            "global_batch": w.B,
+            "heads": w.H,
+            "seq_len": w.n,
+            "head_dim": w.d,
+            "top_n": w.top_n,
+            "parallelism": "single GPU",
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

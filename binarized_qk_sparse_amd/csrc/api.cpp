@@ -146,7 +146,9 @@ int had_attention_topn(const uint32_t* qbits, const uint32_t* kbits, const float
   const int64_t keep = top_n < n ? top_n : n;
   if (keep > HAD_MAX_TOPN) return fail(HAD_ERR_UNSUPPORTED, fn, "min(top_n, n) above HAD_MAX_TOPN");
   const int v_kind = av_mode == HAD_AV_Q8 ? 2 : (v_dtype == HAD_BF16 ? 1 : 0);
-  if (n > topn_max_n(v_kind)) return fail(HAD_ERR_UNSUPPORTED, fn, "n too large for the top-N kernel");
+  const bool streaming = n > topn_max_n(v_kind);
+  if (streaming && keep > topn_stream_max_keep())
+    return fail(HAD_ERR_UNSUPPORTED, fn, "min(top_n, n) too large for the long-sequence kernel");
   hipStream_t s = static_cast<hipStream_t>(stream);
   AttnParams p{};
   p.qbits = qbits;
@@ -182,7 +184,7 @@ int had_attention_topn(const uint32_t* qbits, const uint32_t* kbits, const float
     p.v = q.vq;
     p.vscale = q.vscale;
   }
-  return launch_status(launch_topn(p, s), fn);
+  return launch_status(streaming ? launch_topn_stream(p, s) : launch_topn(p, s), fn);
 }
 
 int binattn_dense_q8(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q, const float* alpha_k,

@@ -37,58 +37,59 @@ HAD_DEVICE float dpp_f(float v) {
                                                                0xf, 0xf, false));
 }
 
-// Sum over all 64 lanes; the result is wave-uniform.
-HAD_DEVICE int wave_sum_i32(int v) {
-  v += dpp_i<kRowRor8>(v);
-  v += dpp_i<kRowRor4>(v);
-  v += dpp_i<kRowRor2>(v);
-  v += dpp_i<kRowRor1>(v);
-  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
-         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+// Full-wave reductions on the DPP network: quad swaps, row rotations, then the
+// row broadcasts carry the partial sums up to lane 63.  Result is wave-uniform.
+constexpr int kQuadSwap1 = 0xb1;  // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4e;  // quad_perm [2,3,0,1]
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+template <int CTRL, int ROWMASK>
+HAD_DEVICE int dppm_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWMASK, 0xf, false);
 }
+
+HAD_DEVICE int wave_sum_i32(int v) {
+  v += dpp_i<kQuadSwap1>(v);
+  v += dpp_i<kQuadSwap2>(v);
+  v += dpp_i<kRowRor4>(v);
+  v += dpp_i<kRowRor8>(v);
+  v += dppm_i<kRowBcast15, 0xa>(v);
+  v += dppm_i<kRowBcast31, 0xc>(v);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+HAD_DEVICE float as_f(int v) { return __builtin_bit_cast(float, v); }
+HAD_DEVICE int as_i(float v) { return __builtin_bit_cast(int, v); }
 
 HAD_DEVICE float wave_sum_f32(float v) {
-  v += dpp_f<kRowRor8>(v);
+  v += dpp_f<kQuadSwap1>(v);
+  v += dpp_f<kQuadSwap2>(v);
   v += dpp_f<kRowRor4>(v);
-  v += dpp_f<kRowRor2>(v);
-  v += dpp_f<kRowRor1>(v);
-  float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-  float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
-  float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-  float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
-  return (a + b) + (c + d);
+  v += dpp_f<kRowRor8>(v);
+  v += as_f(dppm_i<kRowBcast15, 0xa>(as_i(v)));
+  v += as_f(dppm_i<kRowBcast31, 0xc>(as_i(v)));
+  return as_f(__builtin_amdgcn_readlane(as_i(v), 63));
 }
 
+// Max over the wave (the masked-off rows of the broadcasts see -inf).
 HAD_DEVICE float wave_max_f32(float v) {
-  v = fmaxf(v, dpp_f<kRowRor8>(v));
+  v = fmaxf(v, dpp_f<kQuadSwap1>(v));
+  v = fmaxf(v, dpp_f<kQuadSwap2>(v));
   v = fmaxf(v, dpp_f<kRowRor4>(v));
-  v = fmaxf(v, dpp_f<kRowRor2>(v));
-  v = fmaxf(v, dpp_f<kRowRor1>(v));
-  float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-  float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
-  float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-  float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
-  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+  v = fmaxf(v, dpp_f<kRowRor8>(v));
+  v = fmaxf(v, as_f(__builtin_amdgcn_update_dpp(as_i(-INFINITY), as_i(v), kRowBcast15, 0xa, 0xf, false)));
+  v = fmaxf(v, as_f(__builtin_amdgcn_update_dpp(as_i(-INFINITY), as_i(v), kRowBcast31, 0xc, 0xf, false)));
+  return as_f(__builtin_amdgcn_readlane(as_i(v), 63));
 }
 
 HAD_DEVICE uint32_t wave_min_u32(uint32_t v) {
-  v = min(v, (uint32_t)dpp_i<kRowRor8>((int)v));
+  v = min(v, (uint32_t)dpp_i<kQuadSwap1>((int)v));
+  v = min(v, (uint32_t)dpp_i<kQuadSwap2>((int)v));
   v = min(v, (uint32_t)dpp_i<kRowRor4>((int)v));
-  v = min(v, (uint32_t)dpp_i<kRowRor2>((int)v));
-  v = min(v, (uint32_t)dpp_i<kRowRor1>((int)v));
-  uint32_t a = __builtin_amdgcn_readlane((int)v, 0), b = __builtin_amdgcn_readlane((int)v, 16);
-  uint32_t c = __builtin_amdgcn_readlane((int)v, 32), d = __builtin_amdgcn_readlane((int)v, 48);
-  return min(min(a, b), min(c, d));
-}
-
-HAD_DEVICE uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)dpp_i<kRowRor8>((int)v));
-  v = max(v, (uint32_t)dpp_i<kRowRor4>((int)v));
-  v = max(v, (uint32_t)dpp_i<kRowRor2>((int)v));
-  v = max(v, (uint32_t)dpp_i<kRowRor1>((int)v));
-  uint32_t a = __builtin_amdgcn_readlane((int)v, 0), b = __builtin_amdgcn_readlane((int)v, 16);
-  uint32_t c = __builtin_amdgcn_readlane((int)v, 32), d = __builtin_amdgcn_readlane((int)v, 48);
-  return max(max(a, b), max(c, d));
+  v = min(v, (uint32_t)dpp_i<kRowRor8>((int)v));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, kRowBcast15, 0xa, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, kRowBcast31, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Exclusive prefix sum over lanes (lane 0 gets 0) and the wave total.

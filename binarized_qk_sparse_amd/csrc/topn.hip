@@ -82,7 +82,36 @@ HAD_DEVICE int count_ge_f(const float (&l)[NS], float t) {
   return c;
 }
 
-template <int NS, bool FK, int VK>
+// Reduce-scatter of the eight key groups' partial sums (group k = lane >> 3
+// holds channels 8g..8g+7, g = lane & 7): three butterfly levels over lane bits
+// 5, 4, 3 leave lane (k, g) with the total of channel 8g + k.
+template <typename T>
+HAD_DEVICE T reduce_scatter8(T (&acc)[8], int k) {
+  const bool u4 = k & 4, u2 = k & 2, u1 = k & 1;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const T snd = u4 ? acc[c] : acc[c + 4];
+    const T kp = u4 ? acc[c + 4] : acc[c];
+    acc[c] = kp + __shfl_xor(snd, 32, 64);
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const T snd = u2 ? acc[c] : acc[c + 2];
+    const T kp = u2 ? acc[c + 2] : acc[c];
+    acc[c] = kp + __shfl_xor(snd, 16, 64);
+  }
+  const T snd = u1 ? acc[0] : acc[1];
+  const T kp = u1 ? acc[1] : acc[0];
+  T other;
+  if constexpr (sizeof(T) == 4 && T(0.5) != T(0)) {
+    other = dpp_f<kRowRor8>(snd);  // lane ^ 8 within the 16-lane row
+  } else {
+    other = dpp_i<kRowRor8>(snd);
+  }
+  return kp + other;
+}
+
+template <int NS, bool FK, int VK, bool PAD>
 __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int ROWB = row_bytes<VK>();
@@ -110,16 +139,18 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
     const float* src = a.bias + (size_t)hh * (2 * n - 1) + ob;
     for (int o = threadIdx.x; o < cnt; o += blockDim.x) biasw[o] = src[o];
   }
-  // ---- key codes: slot s of this lane is key 64 s + lane; slots from
-  // full_slots on may hold padding keys (j >= n)
+  // ---- the tile's query codes (and scales), one query per lane: read back with v_readlane
+  const size_t qrow = (size_t)bh * n + i0 + lane;
+  const uint2 qlane = (i0 + lane < i1) ? reinterpret_cast<const uint2*>(a.qbits)[qrow] : make_uint2(0u, 0u);
+  const float aqlane = (FK && a.aq != nullptr && i0 + lane < i1) ? a.aq[qrow] : 1.0f;
+  // ---- key codes: slot s of this lane is key 64 s + lane (PAD: j >= n are padding)
   uint32_t k0[NS], k1[NS];
   float akv[NS];
-  const int full_slots = n / 64;
   const uint2* kb = reinterpret_cast<const uint2*>(a.kbits) + (size_t)bh * n;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int j = 64 * s + lane;
-    const bool ok = j < n;
+    const bool ok = !PAD || j < n;
     const uint2 kk = ok ? kb[j] : make_uint2(0u, 0u);
     k0[s] = kk.x;
     k1[s] = kk.y;
@@ -129,22 +160,22 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
 
   uint2* list = reinterpret_cast<uint2*>(smem + a.list_off) + wave * a.lcap;
   uint2* cand = reinterpret_cast<uint2*>(smem + a.cand_off) + wave * 64;
-  const uint2* qb = reinterpret_cast<const uint2*>(a.qbits);
   int tau_prev = 27;  // Hamming-level guess; each query starts from the last one's
 
   for (int i = i0 + wave; i < i1; i += nwaves) {
     const size_t row = (size_t)bh * n + i;
-    const uint2 qq = qb[row];
-    float lmax = 0.0f;  // float keys: largest logit of the row
-    int hmin = 0;       // integer keys: smallest distance of the row
+    const uint32_t q0 = __builtin_amdgcn_readlane(qlane.x, i - i0);
+    const uint32_t q1 = __builtin_amdgcn_readlane(qlane.y, i - i0);
+    float ref = 0.0f;  // float keys: softmax reference (the row's largest logit)
+    int tref = 0;      // integer keys: softmax reference level (the threshold tau)
 
     if (!FK) {
       // ------------------------------------------------ integer keys
       uint32_t hv[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        hv[s] = __builtin_popcount(k1[s] ^ qq.y) + __builtin_popcount(k0[s] ^ qq.x);
-        if (s >= full_slots && 64 * s + lane >= n) hv[s] = 65u;  // padding: above every real distance
+        hv[s] = __builtin_popcount(k1[s] ^ q1) + __builtin_popcount(k0[s] ^ q0);
+        if (PAD && 64 * s + lane >= n) hv[s] = 65u;  // above every real distance
       }
       uint32_t P[NP];
 #pragma unroll
@@ -152,7 +183,7 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
         uint32_t b[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) b[q] = (4 * m + q < NS) ? hv[4 * m + q] : 65u;
-        P[m] = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+        P[m] = ((b[3] << 8 | b[2]) << 16) | (b[1] << 8 | b[0]);
       }
       int tau, less;
       if (keep >= n) {
@@ -160,7 +191,7 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
         less = keep;
       } else {
         int lo, hi, clo;
-        const int t = min(max(tau_prev, 0), 64);
+        int t = tau_prev;
         const int c = count_le<NP>(P, t);
         if (c >= keep) {
           hi = t;
@@ -202,52 +233,57 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
       // ---- compaction: all h < tau, then the first (keep - less) keys with h == tau
       int r = keep - less;
       int base = 0;
-      uint32_t hmin_l = 255u;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const uint64_t Lm = ballot(hv[s] < (uint32_t)tau);
-        uint64_t Sm = Lm;
+        const bool lt = hv[s] < (uint32_t)tau;
+        bool sel = lt;
+        uint64_t Sm = ballot(lt);
         if (r > 0) {
-          const uint64_t Em = ballot(hv[s] == (uint32_t)tau);
+          const bool eq = hv[s] == (uint32_t)tau;
+          const uint64_t Em = ballot(eq);
           const int e = __builtin_popcountll(Em);
           if (e <= r) {
+            sel = lt || eq;
             Sm |= Em;
             r -= e;
           } else {
             uint64_t x = Em;
             for (int k = 0; k < r; ++k) x &= x - 1;  // drop the r lowest set bits
-            Sm |= Em ^ x;
+            const uint64_t take = Em ^ x;
+            sel = lt || ((take >> lane) & 1u);
+            Sm |= take;
             r = 0;
           }
         }
-        if ((Sm >> lane) & 1u) {
-          const int pos = base + (int)mask_rank(Sm);
-          if (pos < a.lcap) list[pos] = make_uint2((uint32_t)(64 * s + lane), hv[s]);
-          hmin_l = min(hmin_l, hv[s]);
+        if (sel) {
+          const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(Sm >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)Sm, (uint32_t)base));
+          list[pos] = make_uint2((uint32_t)(64 * s + lane), hv[s]);  // exactly keep keys are selected
         }
         base += __builtin_popcountll(Sm);
       }
-      hmin = (int)wave_min_u32(hmin_l);
+      tref = tau;
     } else {
       // ------------------------------------------------ float keys
-      const float aqv = a.aq != nullptr ? a.aq[row] : 1.0f;
+      const float aqv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, aqlane), i - i0));
       float lg[NS];
       const int boff = n - 1 - ob - i;  // bias window index of key j is j + boff
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int j = 64 * s + lane;
-        const int hd = __builtin_popcount(k0[s] ^ qq.x) + __builtin_popcount(k1[s] ^ qq.y);
-        const float bias = (a.bias != nullptr && j < n) ? biasw[j + boff] : 0.0f;
+        const int hd = __builtin_popcount(k0[s] ^ q0) + __builtin_popcount(k1[s] ^ q1);
+        const bool ok = !PAD || j < n;
+        const float bias = (a.bias != nullptr && ok) ? biasw[j + boff] : 0.0f;
         const float l = canonical_logit(aqv, akv[s], kD - 2 * hd, a.isd, bias);
-        lg[s] = __fadd_rn(l, 0.0f);  // -0 and +0 compare equal
-        if (s >= full_slots && j >= n) lg[s] = -INFINITY;  // padding
+        lg[s] = ok ? __fadd_rn(l, 0.0f) : -INFINITY;  // -0 and +0 compare equal
       }
       float vstar;
       int jstar;
-      lmax = -INFINITY;
+      float lmax = -INFINITY;
 #pragma unroll
       for (int s = 0; s < NS; ++s) lmax = fmaxf(lmax, lg[s]);
       lmax = wave_max_f32(lmax);
+      ref = lmax;
       if (keep >= n) {
         vstar = -INFINITY;  // everything real is kept
         jstar = INT_MAX;
@@ -331,21 +367,26 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int j = 64 * s + lane;
-        const bool sel = j < n && (lg[s] > vstar || (lg[s] == vstar && j <= jstar));
+        const bool sel = (!PAD || j < n) && (lg[s] > vstar || (lg[s] == vstar && j <= jstar));
         const uint64_t Sm = ballot(sel);
-        const int pos = base + (int)mask_rank(Sm);
-        if (sel && pos < a.lcap) list[pos] = make_uint2((uint32_t)j, __builtin_bit_cast(uint32_t, lg[s]));
+        if (sel) {
+          const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(Sm >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)Sm, (uint32_t)base));
+          if (pos < a.lcap) list[pos] = make_uint2((uint32_t)j, __builtin_bit_cast(uint32_t, lg[s]));
+        }
         base += __builtin_popcountll(Sm);
       }
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
     // ---------------------------------------------------- softmax over the kept list
+    // float keys: e_j = exp(l_j - max l).  Integer keys: e_j = exp(l_j - l(tau)) =
+    // exp(2 (tau - h_j) / sqrt(d)); the shift cancels in the normalisation and
+    // stays below exp(2 (d + 1) / sqrt(d)), far from float overflow.
     float z = 0.0f;
     for (int e = lane; e < keep; e += 64) {
       const uint32_t sc = list[e].y;
-      const float x = FK ? __builtin_bit_cast(float, sc) - lmax : (float)(hmin - (int)sc) * a.exp_c;
-      const float ex = FK ? __expf(x) : exp2f(x);
+      const float ex = FK ? __expf(__builtin_bit_cast(float, sc) - ref) : exp2f((float)(tref - (int)sc) * a.exp_c);
       z += ex;
       list[e].y = __builtin_bit_cast(uint32_t, ex);
     }
@@ -378,27 +419,10 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
           acc[4 + c] += aq8 * (int)(int8_t)(raw.y >> (8 * c));
         }
       }
-      const bool u4 = k & 4, u2 = k & 2, u1 = k & 1;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int snd = u4 ? acc[c] : acc[c + 4];
-        const int kp = u4 ? acc[c + 4] : acc[c];
-        acc[c] = kp + __shfl_xor(snd, 32, 64);
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int snd = u2 ? acc[c] : acc[c + 2];
-        const int kp = u2 ? acc[c + 2] : acc[c];
-        acc[c] = kp + __shfl_xor(snd, 16, 64);
-      }
-      {
-        const int snd = u1 ? acc[0] : acc[1];
-        const int kp = u1 ? acc[1] : acc[0];
-        acc[0] = kp + __shfl_xor(snd, 8, 64);
-      }
+      const int tot = reduce_scatter8<int>(acc, k);
       const int ch = 8 * g + k;
       const float sc = a.vscale[(size_t)bh * kD + ch];
-      a.out[row * kD + ch] = __fdiv_rn(__fmul_rn((float)acc[0], sc), 255.0f);
+      a.out[row * kD + ch] = __fdiv_rn(__fmul_rn((float)tot, sc), 255.0f);
     } else {
       float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       for (int t = 0; t < a.lcap; t += 8) {
@@ -427,52 +451,42 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
           acc[7] = __builtin_fmaf(p, r1.w, acc[7]);
         }
       }
-      const bool u4 = k & 4, u2 = k & 2, u1 = k & 1;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float snd = u4 ? acc[c] : acc[c + 4];
-        const float kp = u4 ? acc[c + 4] : acc[c];
-        acc[c] = kp + __shfl_xor(snd, 32, 64);
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const float snd = u2 ? acc[c] : acc[c + 2];
-        const float kp = u2 ? acc[c + 2] : acc[c];
-        acc[c] = kp + __shfl_xor(snd, 16, 64);
-      }
-      {
-        const float snd = u1 ? acc[0] : acc[1];
-        const float kp = u1 ? acc[1] : acc[0];
-        acc[0] = kp + __shfl_xor(snd, 8, 64);
-      }
-      a.out[row * kD + 8 * g + k] = acc[0];
+      a.out[row * kD + 8 * g + k] = reduce_scatter8<float>(acc, k);
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   }
 }
 
-template <int NS, bool FK, int VK>
+template <int NS, bool FK, int VK, bool PAD>
 hipError_t launch_one(const TopnKArgs& ka, dim3 grid, dim3 block, uint32_t lds, hipStream_t s) {
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&topn_resident_kernel<NS, FK, VK>),
+      reinterpret_cast<const void*>(&topn_resident_kernel<NS, FK, VK, PAD>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((topn_resident_kernel<NS, FK, VK>), grid, block, lds, s, ka);
+  hipLaunchKernelGGL((topn_resident_kernel<NS, FK, VK, PAD>), grid, block, lds, s, ka);
   return hipGetLastError();
 }
 
+template <int NS, bool FK, int VK>
+hipError_t launch_pad(const TopnKArgs& ka, bool pad, dim3 grid, dim3 block, uint32_t lds, hipStream_t s) {
+  return pad ? launch_one<NS, FK, VK, true>(ka, grid, block, lds, s)
+             : launch_one<NS, FK, VK, false>(ka, grid, block, lds, s);
+}
+
 template <int NS, bool FK>
-hipError_t launch_vk(const TopnKArgs& ka, int vk, dim3 grid, dim3 block, uint32_t lds, hipStream_t s) {
+hipError_t launch_vk(const TopnKArgs& ka, int vk, bool pad, dim3 grid, dim3 block, uint32_t lds, hipStream_t s) {
   switch (vk) {
-    case 0: return launch_one<NS, FK, 0>(ka, grid, block, lds, s);
-    case 1: return launch_one<NS, FK, 1>(ka, grid, block, lds, s);
-    default: return launch_one<NS, FK, 2>(ka, grid, block, lds, s);
+    case 0: return launch_pad<NS, FK, 0>(ka, pad, grid, block, lds, s);
+    case 1: return launch_pad<NS, FK, 1>(ka, pad, grid, block, lds, s);
+    default: return launch_pad<NS, FK, 2>(ka, pad, grid, block, lds, s);
   }
 }
 
 template <int NS>
-hipError_t launch_ns(const TopnKArgs& ka, bool fk, int vk, dim3 grid, dim3 block, uint32_t lds, hipStream_t s) {
-  return fk ? launch_vk<NS, true>(ka, vk, grid, block, lds, s) : launch_vk<NS, false>(ka, vk, grid, block, lds, s);
+hipError_t launch_ns(const TopnKArgs& ka, bool fk, int vk, bool pad, dim3 grid, dim3 block, uint32_t lds,
+                     hipStream_t s) {
+  return fk ? launch_vk<NS, true>(ka, vk, pad, grid, block, lds, s)
+            : launch_vk<NS, false>(ka, vk, pad, grid, block, lds, s);
 }
 
 uint32_t align16(uint32_t x) { return (x + 15u) & ~15u; }
@@ -529,13 +543,14 @@ hipError_t launch_topn(const AttnParams& p, hipStream_t s) {
   const uint32_t lds = ka.cand_off + (fk ? 64u * 8u * nw : 0u);
   const dim3 grid((unsigned)(p.B * p.H * ka.tiles));
   const dim3 block((unsigned)(64 * nw));
+  const bool pad = p.n != (int64_t)NS * 64;  // padding keys exist in the last slots
   switch (NS) {
-    case 1: return launch_ns<1>(ka, fk, vk, grid, block, lds, s);
-    case 2: return launch_ns<2>(ka, fk, vk, grid, block, lds, s);
-    case 4: return launch_ns<4>(ka, fk, vk, grid, block, lds, s);
-    case 8: return launch_ns<8>(ka, fk, vk, grid, block, lds, s);
-    case 12: return launch_ns<12>(ka, fk, vk, grid, block, lds, s);
-    default: return launch_ns<16>(ka, fk, vk, grid, block, lds, s);
+    case 1: return launch_ns<1>(ka, fk, vk, pad, grid, block, lds, s);
+    case 2: return launch_ns<2>(ka, fk, vk, pad, grid, block, lds, s);
+    case 4: return launch_ns<4>(ka, fk, vk, pad, grid, block, lds, s);
+    case 8: return launch_ns<8>(ka, fk, vk, pad, grid, block, lds, s);
+    case 12: return launch_ns<12>(ka, fk, vk, pad, grid, block, lds, s);
+    default: return launch_ns<16>(ka, fk, vk, pad, grid, block, lds, s);
   }
 }
 

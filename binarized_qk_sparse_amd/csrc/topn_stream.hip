@@ -1,0 +1,383 @@
+// Top-N binarized attention for long sequences (n above what one workgroup can
+// hold on chip), one wavefront per query.
+//
+// Same method and arithmetic as the resident kernel (Hamming Attention
+// Distillation summary: per-query top-N; BinaryAttention sections 2.2-2.4:
+// scaled codes, bias, quantized A*V).  Differences:
+//  * keys stream through LDS in chunks of kChunk keys (codes, alpha_k and the
+//    bias offsets the workgroup's queries touch), shared by the workgroup's
+//    waves, which process one query each in lockstep over the chunks;
+//  * the top-N is streaming: a per-wave candidate buffer in LDS admits keys
+//    whose logit beats the current threshold; when it fills, an exact
+//    selection (ties to the lower key index) keeps the best N and raises the
+//    threshold.  Keys arrive in ascending j, so a later key with a logit equal
+//    to the threshold can never displace a kept one, and the buffer stays in
+//    ascending key order;
+//  * V (or int8 V) rows are gathered from global memory (L2), eight lanes per
+//    kept key.
+#include <float.h>
+#include <limits.h>
+
+#include "had_device.hpp"
+#include "had_internal.h"
+#include "../../include/had.h"
+
+namespace had {
+namespace {
+
+constexpr int kD = 64;
+constexpr int kWaves = 16;
+constexpr int kChunk = 2048;  // keys per LDS chunk
+constexpr int kCap = 768;     // candidate-buffer entries per wave
+constexpr int kR = kCap / 64;
+
+struct StreamKArgs {
+  const uint32_t* qbits;
+  const uint32_t* kbits;
+  const float* aq;
+  const float* ak;
+  const float* bias;
+  const void* v;
+  const float* vscale;
+  float* out;
+  int32_t* idx;
+  int H, n, keep, lcap, tiles;
+  float isd;
+};
+
+// LDS layout (bytes)
+constexpr uint32_t kCodeOff = 0;                                  // uint2[kChunk]
+constexpr uint32_t kAkOff = kCodeOff + kChunk * 8;                 // float[kChunk]
+constexpr uint32_t kBiasOff = kAkOff + kChunk * 4;                 // float[kChunk + kWaves]
+constexpr uint32_t kBufOff = kBiasOff + (kChunk + 64) * 4;         // uint2[kWaves][kCap]
+constexpr uint32_t kCandOff = kBufOff + kWaves * kCap * 8;         // uint2[kWaves][64]
+constexpr uint32_t kLdsTotal = kCandOff + kWaves * 64 * 8;
+
+template <int VK>
+constexpr int row_bytes() {
+  return VK == 0 ? kD * 4 : (VK == 1 ? kD * 2 : kD);
+}
+
+// Exact top-`keep` of the first `cnt` buffer entries (entry order = key order),
+// ties to the earlier entry.  Rewrites the buffer with the kept entries in
+// order and returns their count (min(cnt, keep)); `vstar` receives the value
+// of the worst kept entry and `lmax` the best.
+HAD_DEVICE int select_compact(uint2* buf, uint2* cand, int cnt, int keep, int lane, float* vstar_out,
+                              float* lmax_out) {
+  float vals[kR];
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const int e = lane + 64 * r;
+    vals[r] = e < cnt ? __builtin_bit_cast(float, buf[e].x) : -INFINITY;
+  }
+  float lmax = -INFINITY, lmin = INFINITY;
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    lmax = fmaxf(lmax, vals[r]);
+    lmin = fminf(lmin, vals[r] == -INFINITY ? INFINITY : vals[r]);
+  }
+  lmax = wave_max_f32(lmax);
+  lmin = -wave_max_f32(-lmin);
+  *lmax_out = lmax;
+  auto count_ge = [&](float t) {
+    int c = 0;
+#pragma unroll
+    for (int r = 0; r < kR; ++r) c += __builtin_popcountll(ballot(vals[r] >= t));
+    return c;
+  };
+  if (cnt <= keep) {
+    *vstar_out = lmin;
+    return cnt;
+  }
+  float vstar;
+  int need;
+  const int ctop = count_ge(lmax);
+  if (ctop >= keep) {
+    vstar = lmax;
+    need = keep;
+  } else {
+    float lo = lmin, hi = lmax;
+    int clo = cnt, chi = ctop;
+    bool split = true;
+    while (clo - chi > 64) {
+      const float mid = 0.5f * lo + 0.5f * hi;
+      if (!(mid > lo && mid < hi)) {
+        split = false;
+        break;
+      }
+      const int cm = count_ge(mid);
+      if (cm >= keep) {
+        lo = mid;
+        clo = cm;
+      } else {
+        hi = mid;
+        chi = cm;
+      }
+    }
+    if (!split) {
+      vstar = lo;
+      need = keep - chi;
+    } else {
+      int cb = 0;
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        const bool c = vals[r] >= lo && vals[r] < hi;
+        const uint64_t m = ballot(c);
+        const int pos = cb + (int)mask_rank(m);
+        if (c && pos < 64) cand[pos] = make_uint2(ordered_key(vals[r]), 0u);
+        cb += __builtin_popcountll(m);
+      }
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      const uint32_t ck = lane < cb ? cand[lane].x : 0u;
+      const int rr = keep - chi;
+      uint32_t L = ordered_key(lo), R = ordered_key(hi);
+      while (R - L > 1u) {
+        const uint32_t M = L + ((R - L) >> 1);
+        if (__builtin_popcountll(ballot(ck >= M)) >= rr)
+          L = M;
+        else
+          R = M;
+      }
+      vstar = from_ordered_key(L);
+      need = keep - chi - __builtin_popcountll(ballot(ck > L));
+    }
+  }
+  // the need-th entry (in order) holding vstar
+  int estar = INT_MAX, seen = 0;
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const uint64_t Em = ballot(vals[r] == vstar);
+    const int e = __builtin_popcountll(Em);
+    if (estar == INT_MAX && seen + e >= need) {
+      uint64_t x = Em;
+      for (int k = 0; k < need - seen - 1; ++k) x &= x - 1;
+      estar = 64 * r + (int)__builtin_ctzll(x);
+    }
+    seen += e;
+  }
+  // keep l > vstar, or l == vstar up to entry estar; rewrite in order
+  uint2 ent[kR];
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const int e = lane + 64 * r;
+    ent[r] = e < cnt ? buf[e] : make_uint2(0u, 0u);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  int base = 0;
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const int e = lane + 64 * r;
+    const bool sel = vals[r] > vstar || (vals[r] == vstar && e <= estar);
+    const uint64_t Sm = ballot(sel);
+    if (sel) buf[base + (int)mask_rank(Sm)] = ent[r];
+    base += __builtin_popcountll(Sm);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  *vstar_out = vstar;
+  return base;
+}
+
+template <typename T>
+HAD_DEVICE T reduce_scatter8(T (&acc)[8], int k) {
+  const bool u4 = k & 4, u2 = k & 2, u1 = k & 1;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const T snd = u4 ? acc[c] : acc[c + 4];
+    const T kp = u4 ? acc[c + 4] : acc[c];
+    acc[c] = kp + __shfl_xor(snd, 32, 64);
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const T snd = u2 ? acc[c] : acc[c + 2];
+    const T kp = u2 ? acc[c + 2] : acc[c];
+    acc[c] = kp + __shfl_xor(snd, 16, 64);
+  }
+  const T snd = u1 ? acc[0] : acc[1];
+  const T kp = u1 ? acc[1] : acc[0];
+  return kp + __shfl_xor(snd, 8, 64);
+}
+
+template <int VK>
+__global__ __launch_bounds__(1024) void topn_stream_kernel(const StreamKArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int ROWB = row_bytes<VK>();
+  uint2* codes = reinterpret_cast<uint2*>(smem + kCodeOff);
+  float* aks = reinterpret_cast<float*>(smem + kAkOff);
+  float* biasw = reinterpret_cast<float*>(smem + kBiasOff);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint2* buf = reinterpret_cast<uint2*>(smem + kBufOff) + wave * kCap;
+  uint2* cand = reinterpret_cast<uint2*>(smem + kCandOff) + wave * 64;
+  const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / a.tiles, tile = wg % a.tiles, hh = bh % a.H;
+  const int n = a.n, keep = a.keep;
+  const int i0 = tile * kWaves;  // one query per wave
+  const int i = i0 + wave;
+  const bool live = i < n;  // uniform per wave
+  const int ic = live ? i : n - 1;
+  const size_t row = (size_t)bh * n + ic;
+  const uint2 qq = reinterpret_cast<const uint2*>(a.qbits)[row];
+  const float aqv = a.aq != nullptr ? a.aq[row] : 1.0f;
+  const uint2* kb = reinterpret_cast<const uint2*>(a.kbits) + (size_t)bh * n;
+  const float* akg = a.ak != nullptr ? a.ak + (size_t)bh * n : nullptr;
+  const int ilast = min(n, i0 + kWaves) - 1;
+
+  float theta = -INFINITY;  // admit l > theta
+  int cnt = 0;
+  for (int c0 = 0; c0 < n; c0 += kChunk) {
+    const int cl = min(kChunk, n - c0);
+    __syncthreads();
+    for (int t = threadIdx.x; t < cl; t += blockDim.x) {
+      codes[t] = kb[c0 + t];
+      aks[t] = akg != nullptr ? akg[c0 + t] : 1.0f;
+    }
+    // bias offsets o = j - i + n - 1 for j in [c0, c0+cl), i in [i0, ilast]
+    const int ob = c0 - ilast + n - 1;
+    if (a.bias != nullptr) {
+      const int cntb = cl + (ilast - i0);
+      const float* src = a.bias + (size_t)hh * (2 * n - 1) + ob;
+      for (int t = threadIdx.x; t < cntb; t += blockDim.x) biasw[t] = src[t];
+    }
+    __syncthreads();
+    if (!live) continue;
+    const int boff = ilast - i;  // bias window index of chunk key t is t + boff
+    for (int s0 = 0; s0 < cl; s0 += 64) {
+      const int t = s0 + lane;
+      const bool ok = t < cl;
+      const uint2 kk = codes[ok ? t : 0];
+      const int hd = __builtin_popcount(kk.x ^ qq.x) + __builtin_popcount(kk.y ^ qq.y);
+      const float b = a.bias != nullptr ? biasw[(ok ? t : 0) + boff] : 0.0f;
+      float l = canonical_logit(aqv, aks[ok ? t : 0], kD - 2 * hd, a.isd, b);
+      l = __fadd_rn(l, 0.0f);
+      const bool adm = ok && l > theta;
+      const uint64_t m = ballot(adm);
+      if (m != 0) {
+        if (adm) buf[cnt + (int)mask_rank(m)] = make_uint2(__builtin_bit_cast(uint32_t, l), (uint32_t)(c0 + t));
+        cnt += __builtin_popcountll(m);
+        if (cnt > kCap - 64) {
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          float lm;
+          cnt = select_compact(buf, cand, cnt, keep, lane, &theta, &lm);
+        }
+      }
+    }
+  }
+  if (!live) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  float lmax;
+  float vs;
+  cnt = select_compact(buf, cand, cnt, keep, lane, &vs, &lmax);  // cnt == keep now
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+
+  // ---- softmax over the kept entries (buffer order = ascending key index)
+  float z = 0.0f;
+  for (int e = lane; e < cnt; e += 64) {
+    const float ex = __expf(__builtin_bit_cast(float, buf[e].x) - lmax);
+    z += ex;
+    buf[e].x = __builtin_bit_cast(uint32_t, ex);
+  }
+  const float inv_z = 1.0f / wave_sum_f32(z);
+  for (int e = lane; e < a.lcap; e += 64) {
+    uint2 ent = e < cnt ? buf[e] : make_uint2(0u, 0u);
+    const float p = __builtin_bit_cast(float, ent.x) * inv_z;
+    if (VK == 2) {
+      const float qv = fminf(fmaxf(rintf(255.0f * p), 0.0f), 255.0f);
+      ent.x = e < cnt ? (uint32_t)qv : 0u;
+    } else {
+      ent.x = e < cnt ? __builtin_bit_cast(uint32_t, p) : 0u;
+    }
+    buf[e] = ent;
+    if (a.idx != nullptr && e < cnt) a.idx[row * keep + e] = (int32_t)ent.y;
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+
+  // ---- A*V: eight lanes per kept key, eight channels per lane, rows from global memory
+  const int k = lane >> 3, g = lane & 7;
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + (size_t)bh * n * ROWB;
+  if (VK == 2) {
+    int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int t = 0; t < a.lcap; t += 8) {
+      const uint2 ent = buf[t + k];
+      const uint2 raw = *reinterpret_cast<const uint2*>(vbase + (size_t)ent.y * ROWB + g * 8);
+      const int aq8 = (int)ent.x;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        acc[c] += aq8 * (int)(int8_t)(raw.x >> (8 * c));
+        acc[4 + c] += aq8 * (int)(int8_t)(raw.y >> (8 * c));
+      }
+    }
+    const int tot = reduce_scatter8<int>(acc, k);
+    const int ch = 8 * g + k;
+    a.out[row * kD + ch] = __fdiv_rn(__fmul_rn((float)tot, a.vscale[(size_t)bh * kD + ch]), 255.0f);
+  } else {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int t = 0; t < a.lcap; t += 8) {
+      const uint2 ent = buf[t + k];
+      const float p = __builtin_bit_cast(float, ent.x);
+      if (VK == 1) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(vbase + (size_t)ent.y * ROWB + g * 16);
+        acc[0] = __builtin_fmaf(p, bf16_lo(raw.x), acc[0]);
+        acc[1] = __builtin_fmaf(p, bf16_hi(raw.x), acc[1]);
+        acc[2] = __builtin_fmaf(p, bf16_lo(raw.y), acc[2]);
+        acc[3] = __builtin_fmaf(p, bf16_hi(raw.y), acc[3]);
+        acc[4] = __builtin_fmaf(p, bf16_lo(raw.z), acc[4]);
+        acc[5] = __builtin_fmaf(p, bf16_hi(raw.z), acc[5]);
+        acc[6] = __builtin_fmaf(p, bf16_lo(raw.w), acc[6]);
+        acc[7] = __builtin_fmaf(p, bf16_hi(raw.w), acc[7]);
+      } else {
+        const float4 r0 = *reinterpret_cast<const float4*>(vbase + (size_t)ent.y * ROWB + g * 32);
+        const float4 r1 = *reinterpret_cast<const float4*>(vbase + (size_t)ent.y * ROWB + g * 32 + 16);
+        acc[0] = __builtin_fmaf(p, r0.x, acc[0]);
+        acc[1] = __builtin_fmaf(p, r0.y, acc[1]);
+        acc[2] = __builtin_fmaf(p, r0.z, acc[2]);
+        acc[3] = __builtin_fmaf(p, r0.w, acc[3]);
+        acc[4] = __builtin_fmaf(p, r1.x, acc[4]);
+        acc[5] = __builtin_fmaf(p, r1.y, acc[5]);
+        acc[6] = __builtin_fmaf(p, r1.z, acc[6]);
+        acc[7] = __builtin_fmaf(p, r1.w, acc[7]);
+      }
+    }
+    a.out[row * kD + 8 * g + k] = reduce_scatter8<float>(acc, k);
+  }
+}
+
+template <int VK>
+hipError_t launch_vk(const StreamKArgs& ka, dim3 grid, hipStream_t s) {
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&topn_stream_kernel<VK>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsTotal);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((topn_stream_kernel<VK>), grid, dim3(64 * kWaves), kLdsTotal, s, ka);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t topn_stream_max_keep() { return kCap - 64; }
+
+hipError_t launch_topn_stream(const AttnParams& p, hipStream_t s) {
+  if (p.d != kD || p.keep > topn_stream_max_keep()) return hipErrorInvalidValue;
+  StreamKArgs ka{};
+  ka.qbits = p.qbits;
+  ka.kbits = p.kbits;
+  ka.aq = p.alpha_q;
+  ka.ak = p.alpha_k;
+  ka.bias = p.bias;
+  ka.v = p.v;
+  ka.vscale = p.vscale;
+  ka.out = p.out;
+  ka.idx = p.idx;
+  ka.H = (int)p.H;
+  ka.n = (int)p.n;
+  ka.keep = (int)p.keep;
+  ka.lcap = (int)((p.keep + 7) / 8 * 8);
+  ka.tiles = (int)((p.n + kWaves - 1) / kWaves);
+  ka.isd = (float)(1.0 / sqrt((double)p.d));
+  const dim3 grid((unsigned)(p.B * p.H * ka.tiles));
+  switch (p.v_kind) {
+    case 0: return launch_vk<0>(ka, grid, s);
+    case 1: return launch_vk<1>(ka, grid, s);
+    default: return launch_vk<2>(ka, grid, s);
+  }
+}
+
+}  // namespace had

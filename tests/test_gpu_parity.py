@@ -198,3 +198,69 @@ def test_dense_q8_c4_full_size_sampled():
     ref = oracle.attention(p["oq"], p["ok"], f32(p["v"]), alpha_q=p["oaq"], alpha_k=p["oak"], bias=p["obias"],
                            top_n=None, av_mode=oracle.AV_Q8, rows=rows)
     _check_q8(out.cpu().numpy().reshape(-1, 64)[rows], vq.cpu().numpy(), sc.cpu().numpy(), ref, rows, w.n, "c4")
+
+
+def test_graph_replays_match_eager():
+    # the benchmark replays a captured HIP graph: every replay must equal the eager result
+    w = synth.c3(256)
+    p = packed_inputs(w)
+    eager = ops.had_attention_topn(p["dq"], p["dk"], p["dv"], w.top_n)
+    out = torch.empty_like(eager)
+    g = torch.cuda.CUDAGraph()
+    ops.had_attention_topn(p["dq"], p["dk"], p["dv"], w.top_n, out=out)  # warm-up outside capture
+    with torch.cuda.graph(g):
+        ops.had_attention_topn(p["dq"], p["dk"], p["dv"], w.top_n, out=out)
+    for _ in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+
+
+# ------------------------------------------------------------------ long sequences (streaming kernel)
+@pytest.mark.parametrize("n,N", [(1025, 1), (1500, 30), (2048, 256), (3000, 700), (4100, 120)])
+@pytest.mark.parametrize("keys", ["int", "alpha_bias"])
+@pytest.mark.parametrize("av", [synth.AV_F32, synth.AV_Q8])
+def test_topn_long_sequence_matches_oracle(n, N, keys, av):
+    mode = synth.MEAN_SIGN if keys == "alpha_bias" else synth.SIGN
+    qb, kb, aq, ak, T, v = _topn_case(1, 2, n, N, torch.bfloat16, mode, keys != "int", seed=4)
+    dt = lambda a: None if a is None else torch.from_numpy(a).to(DEV)
+    ws = ops.workspace(1, 2, n, 64)
+    out, idx = ops.had_attention_topn(dt(qb.view(np.int32)), dt(kb.view(np.int32)), v.to(DEV), N, alpha_q=dt(aq),
+                                      alpha_k=dt(ak), bias=dt(T), av_mode=av, want_idx=True, ws=ws)
+    torch.cuda.synchronize()
+    rows = sample_rows(2 * n, 700, n)
+    ref = oracle.attention(qb, kb, f32(v), alpha_q=aq, alpha_k=ak, bias=T, top_n=N, av_mode=av, rows=rows,
+                           want_idx=True)
+    keep = min(N, n)
+    assert np.array_equal(idx.cpu().numpy().reshape(-1, keep)[rows], ref["idx"])
+    got = out.cpu().numpy().reshape(-1, 64)[rows]
+    if av == synth.AV_F32:
+        assert_close(got, ref["out"], f"long n={n} N={N}")
+    else:
+        vq, sc = ops.workspace_view(ws, 1, 2, n, 64)
+        _check_q8(got, vq.cpu().numpy(), sc.cpu().numpy(), ref, rows, n, f"long q8 n={n}")
+
+
+def test_topn_c5_full_size_sampled():
+    w = synth.workload("c5")
+    g = synth.generate(w)
+    ws = ops.workspace(w.B, w.H, w.n, w.d)
+    q, k, v = g["q"].to(DEV), g["k"].to(DEV), g["v"].to(DEV)
+    qb, aq, _ = ops.had_pack(q, w.mode, ws=ws)
+    kb, ak, _ = ops.had_pack(k, w.mode, ws=ws)
+    bias = g["bias"].to(DEV)
+    out, idx = ops.had_attention_topn(qb, kb, v, w.top_n, alpha_q=aq, alpha_k=ak, bias=bias, av_mode=w.av_mode,
+                                      want_idx=True, ws=ws)
+    torch.cuda.synchronize()
+    # the oracle packs the same inputs itself (end-to-end check of the whole path)
+    oq, oaq, _ = oracle.pack(f32(g["q"]), w.mode)
+    okb, oak, _ = oracle.pack(f32(g["k"]), w.mode)
+    assert np.array_equal(qb.cpu().numpy().view(np.uint32), oq)
+    assert np.array_equal(ak.cpu().numpy(), oak)
+    rows = sample_rows(w.B * w.H * w.n, 300, 5)
+    ref = oracle.attention(oq, okb, f32(g["v"]), alpha_q=oaq, alpha_k=oak, bias=g["bias"].numpy(), top_n=w.top_n,
+                           av_mode=w.av_mode, rows=rows, want_idx=True)
+    assert np.array_equal(idx.cpu().numpy().reshape(-1, w.top_n)[rows], ref["idx"])
+    vq, sc = ops.workspace_view(ws, w.B, w.H, w.n, w.d)
+    _check_q8(out.cpu().numpy().reshape(-1, 64)[rows], vq.cpu().numpy(), sc.cpu().numpy(), ref, rows, w.n, "c5")
