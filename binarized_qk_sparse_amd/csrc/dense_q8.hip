@@ -7,17 +7,17 @@
 //
 // gfx950 has no unsigned-by-signed int8 MFMA, so the kernel feeds
 // A' = A_q - 128 (int8) and adds 128 * sum_j Vq[j][c] back:
-//   sum_j A_q Vq = sum_j A' Vq + 128 sum_j Vq.
-// Exact in int32 (|sum| <= 255 * 127 * 256 for the n <= 256 this kernel takes).
+//   sum_j A_q Vq = sum_j A' Vq + 128 sum_j Vq,
+// exact in int32 (|sum| <= 255 * 127 * 256 for the n <= 256 this kernel takes).
 //
-// One wave per 32-query tile; v_mfma_i32_32x32x16_i8 with
-//   A (32 queries x 16 keys):  lane l holds row l%32, keys 8*(l/32)+0..7
-//   B (16 keys x 32 channels): lane l holds column l%32, keys 8*(l/32)+0..7
-//   C (32 x 32 int32):         lane l, element r: row 8*(r/4)+4*(l/32)+r%4, column l%32.
+// One wave per 16-query tile; v_mfma_i32_16x16x32_i8 with
+//   A (16 queries x 32 keys):  lane l holds row l%16, keys 8*(l/16)+0..7
+//   B (32 keys x 16 channels): lane l holds column l%16, keys 8*(l/16)+0..7
+//   C (16 x 16 int32):         lane l, element r: row 4*(l/16)+r, column l%16.
 // Each lane computes the logits of exactly the A elements it feeds (VALU XOR +
-// v_bcnt on the codes, LDS-staged key codes), keeps them in VGPRs for the
-// row max / row sum / quantize passes, and the matrix cores do the contraction
-// over all keys against the int8 V tile staged (transposed) in LDS.
+// v_bcnt on LDS-staged key codes), keeps them in VGPRs through the row max,
+// row sum and quantize passes, and the matrix cores contract the quantized
+// A against the transposed int8 V tile staged in LDS.
 #include <float.h>
 
 #include "had_device.hpp"
@@ -29,7 +29,7 @@ namespace {
 
 constexpr int kD = 64;
 constexpr int kWaves = 4;
-typedef int v16i __attribute__((ext_vector_type(16)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 
 struct DenseKArgs {
   const uint32_t* qbits;
@@ -40,22 +40,31 @@ struct DenseKArgs {
   const int8_t* vq;
   const float* vscale;
   float* out;
-  int H, n, npad, wgs_per_head;
+  int H, n;
   float isd;
 };
 
-template <int NK>  // key steps of 16; npad = 16 * NK >= n
+// Sum / max of a row whose values live in lanes l, l^16, l^32, l^48.
+HAD_DEVICE float row4_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+HAD_DEVICE float row4_sum(float v) {
+  v += __shfl_xor(v, 16, 64);
+  return v + __shfl_xor(v, 32, 64);
+}
+
+template <int NK, bool BIAS>  // key steps of 32; NPAD = 32 * NK >= n
 __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
-  constexpr int NPAD = 16 * NK;
+  constexpr int NPAD = 32 * NK;
   __shared__ __align__(16) int8_t vqt[kD][NPAD];  // Vq transposed: [channel][key]
   __shared__ __align__(16) uint2 kcode[NPAD];
-  __shared__ float akk[NPAD];
+  __shared__ __align__(16) float akk[NPAD];
   __shared__ int colsum[kD];
-  extern __shared__ float biasw[];  // [2n - 1]
+  extern __shared__ float biasw[];  // [2n - 1 + NPAD]: the table, then zeros read by padding keys
 
   const int tid = threadIdx.x;
-  const int bh = blockIdx.x / a.wgs_per_head;
-  const int part = blockIdx.x % a.wgs_per_head;
+  const int bh = blockIdx.x;
   const int hh = bh % a.H;
   const int n = a.n;
 
@@ -65,12 +74,17 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
     kcode[j] = j < n ? kb[j] : make_uint2(0u, 0u);
     akk[j] = (j < n && a.ak != nullptr) ? a.ak[(size_t)bh * n + j] : 1.0f;
   }
-  if (a.bias != nullptr)
-    for (int o = tid; o < 2 * n - 1; o += 256) biasw[o] = a.bias[(size_t)hh * (2 * n - 1) + o];
-  const int8_t* vsrc = a.vq + (size_t)bh * n * kD;
-  for (int e = tid; e < NPAD * kD; e += 256) {
-    const int j = e / kD, c = e % kD;
-    vqt[c][j] = j < n ? vsrc[(size_t)j * kD + c] : (int8_t)0;
+  if (BIAS)
+    for (int o = tid; o < 2 * n - 1 + NPAD; o += 256)
+      biasw[o] = o < 2 * n - 1 ? a.bias[(size_t)hh * (2 * n - 1) + o] : 0.0f;
+  const uint32_t* vsrc = reinterpret_cast<const uint32_t*>(a.vq + (size_t)bh * n * kD);
+  for (int e = tid; e < NPAD * (kD / 4); e += 256) {
+    const int j = e / (kD / 4), c4 = 4 * (e % (kD / 4));
+    const uint32_t w = j < n ? vsrc[e] : 0u;
+    vqt[c4 + 0][j] = (int8_t)(w);
+    vqt[c4 + 1][j] = (int8_t)(w >> 8);
+    vqt[c4 + 2][j] = (int8_t)(w >> 16);
+    vqt[c4 + 3][j] = (int8_t)(w >> 24);
   }
   __syncthreads();
   if (tid < kD) {
@@ -81,83 +95,94 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
   __syncthreads();
 
   const int wave = tid >> 6, lane = tid & 63;
-  const int tile = part * kWaves + wave;
-  if (tile * 32 >= n) return;
-  const int r32 = lane & 31, khalf = lane >> 5;
-  const int i = tile * 32 + r32;  // this lane's query row (may be padding)
-  const int iq = i < n ? i : n - 1;
-  const size_t row = (size_t)bh * n + iq;
-  const uint2 qq = reinterpret_cast<const uint2*>(a.qbits)[row];
-  const float aqv = a.aq != nullptr ? a.aq[row] : 1.0f;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int tiles = (n + 15) / 16;
+  const float log2e = 1.4426950408889634f;
+  for (int tile = wave; tile < tiles; tile += kWaves) {
+    const int i = tile * 16 + r16;  // this lane's query row (may be padding)
+    const int iq = i < n ? i : n - 1;
+    const size_t row = (size_t)bh * n + iq;
+    const uint2 qq = reinterpret_cast<const uint2*>(a.qbits)[row];
+    const float aqv = a.aq != nullptr ? a.aq[row] : 1.0f;
+    const float* brow = biasw + (n - 1 - iq);  // bias of key j is brow[j]
 
-  // ---- logits of this lane's A elements
-  float lg[NK][8];
-  float m = -INFINITY;
+    // ---- logits of this lane's A elements
+    float lg[NK][8];
+    float m = -INFINITY;
 #pragma unroll
-  for (int ks = 0; ks < NK; ++ks) {
+    for (int ks = 0; ks < NK; ++ks) {
+      const int j0 = ks * 32 + kg * 8;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = ks * 16 + khalf * 8 + e;
-      const uint2 kk = kcode[j];
-      const int h = __builtin_popcount(qq.x ^ kk.x) + __builtin_popcount(qq.y ^ kk.y);
-      const float b = (a.bias != nullptr && j < n) ? biasw[j - iq + n - 1] : 0.0f;
-      float l = canonical_logit(aqv, akk[j], kD - 2 * h, a.isd, b);
-      l = j < n ? l : -INFINITY;
-      lg[ks][e] = l;
-      m = fmaxf(m, l);
+      for (int e = 0; e < 8; ++e) {
+        const int j = j0 + e;
+        const uint2 kk = kcode[j];
+        const int h = __builtin_popcount(qq.x ^ kk.x) + __builtin_popcount(qq.y ^ kk.y);
+        const float b = BIAS ? brow[j] : 0.0f;
+        float l = canonical_logit(aqv, akk[j], kD - 2 * h, a.isd, b);
+        if (ks == NK - 1) l = j < n ? l : -INFINITY;  // only the last step holds padding keys
+        lg[ks][e] = l;
+        m = fmaxf(m, l);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep each step's operand loads short-lived
     }
-  }
-  m = fmaxf(m, __shfl_xor(m, 32, 64));  // the row's other 8-key half lives in lane ^ 32
-  float z = 0.0f;
+    m = row4_max(m);
+    const float mb = m * log2e;
+    float z = 0.0f;
 #pragma unroll
-  for (int ks = 0; ks < NK; ++ks)
+    for (int ks = 0; ks < NK; ++ks)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float ex = __expf(lg[ks][e] - m);
-      lg[ks][e] = ex;
-      z += ex;
-    }
-  z += __shfl_xor(z, 32, 64);
-  const float inv_z = 1.0f / z;
+      for (int e = 0; e < 8; ++e) {
+        const float ex = exp2f(__builtin_fmaf(lg[ks][e], log2e, -mb));
+        lg[ks][e] = ex;
+        z += ex;
+      }
+    const float q255 = 255.0f / row4_sum(z);
 
-  // ---- quantize A and contract on the matrix cores
-  v16i acc0 = {0}, acc1 = {0};
+    // ---- quantize A and contract on the matrix cores
+    v4i acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
-  for (int ks = 0; ks < NK; ++ks) {
-    uint32_t w[2] = {0u, 0u};
+    for (int ks = 0; ks < NK; ++ks) {
+      uint32_t w[2] = {0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float qv = fminf(fmaxf(rintf(255.0f * (lg[ks][e] * inv_z)), 0.0f), 255.0f);
-      const uint32_t a8 = (uint32_t)((int)qv - 128) & 0xffu;
-      w[e >> 2] |= a8 << (8 * (e & 3));
+      for (int e = 0; e < 8; ++e) {
+        const float qv = fminf(fmaxf(rintf(lg[ks][e] * q255), 0.0f), 255.0f);
+        const uint32_t a8 = (uint32_t)((int)qv - 128) & 0xffu;
+        w[e >> 2] |= a8 << (8 * (e & 3));
+      }
+      const long A = (long)(((uint64_t)w[1] << 32) | w[0]);
+      const int kk0 = ks * 32 + kg * 8;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const long B = *reinterpret_cast<const long*>(&vqt[nt * 16 + r16][kk0]);
+        acc[nt] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, acc[nt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    const long A = (long)(((uint64_t)w[1] << 32) | w[0]);
-    const long B0 = *reinterpret_cast<const long*>(&vqt[r32][ks * 16 + khalf * 8]);
-    const long B1 = *reinterpret_cast<const long*>(&vqt[32 + r32][ks * 16 + khalf * 8]);
-    acc0 = __builtin_amdgcn_mfma_i32_32x32x16_i8(A, B0, acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_i32_32x32x16_i8(A, B1, acc1, 0, 0, 0);
-  }
 
-  // ---- dequantize and store
+    // ---- dequantize and store
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int orow = tile * 32 + 8 * (r / 4) + 4 * khalf + (r % 4);
-    if (orow < n) {
-      float* o = a.out + ((size_t)bh * n + orow) * kD;
-      const int c0 = r32, c1 = 32 + r32;
-      const int t0 = acc0[r] + 128 * colsum[c0];
-      const int t1 = acc1[r] + 128 * colsum[c1];
-      o[c0] = __fdiv_rn(__fmul_rn((float)t0, a.vscale[(size_t)bh * kD + c0]), 255.0f);
-      o[c1] = __fdiv_rn(__fmul_rn((float)t1, a.vscale[(size_t)bh * kD + c1]), 255.0f);
+    for (int nt = 0; nt < 4; ++nt) {
+      const int c = nt * 16 + r16;
+      const float sc = a.vscale[(size_t)bh * kD + c];
+      const int cs = 128 * colsum[c];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int orow = tile * 16 + 4 * kg + r;
+        if (orow < n)
+          a.out[((size_t)bh * n + orow) * kD + c] = __fdiv_rn(__fmul_rn((float)(acc[nt][r] + cs), sc), 255.0f);
+      }
     }
   }
 }
 
 template <int NK>
 hipError_t launch_nk(const DenseKArgs& ka, int64_t BH, hipStream_t s) {
-  const dim3 grid((unsigned)(BH * ka.wgs_per_head));
-  const size_t lds = ka.bias != nullptr ? sizeof(float) * (2 * ka.n - 1) : 0;
-  hipLaunchKernelGGL((dense_q8_kernel<NK>), grid, dim3(256), lds, s, ka);
+  if (ka.bias != nullptr) {
+    const size_t lds = sizeof(float) * (2 * ka.n - 1 + 32 * NK);
+    hipLaunchKernelGGL((dense_q8_kernel<NK, true>), dim3((unsigned)BH), dim3(64 * kWaves), lds, s, ka);
+  } else {
+    hipLaunchKernelGGL((dense_q8_kernel<NK, false>), dim3((unsigned)BH), dim3(64 * kWaves), 0, s, ka);
+  }
   return hipGetLastError();
 }
 
@@ -179,17 +204,19 @@ hipError_t launch_dense_q8(const AttnParams& p, hipStream_t s) {
   ka.out = p.out;
   ka.H = (int)p.H;
   ka.n = (int)p.n;
-  const int nk = (int)((p.n + 15) / 16);
-  ka.npad = 16 * nk;
-  const int tiles = (int)((p.n + 31) / 32);
-  ka.wgs_per_head = (tiles + kWaves - 1) / kWaves;
   ka.isd = (float)(1.0 / sqrt((double)p.d));
+  const int nk = (int)((p.n + 31) / 32);
   const int64_t BH = p.B * p.H;
-  if (nk <= 2) return launch_nk<2>(ka, BH, s);
-  if (nk <= 4) return launch_nk<4>(ka, BH, s);
-  if (nk <= 8) return launch_nk<8>(ka, BH, s);
-  if (nk <= 13) return launch_nk<13>(ka, BH, s);
-  return launch_nk<16>(ka, BH, s);
+  switch (nk) {
+    case 1: return launch_nk<1>(ka, BH, s);
+    case 2: return launch_nk<2>(ka, BH, s);
+    case 3: return launch_nk<3>(ka, BH, s);
+    case 4: return launch_nk<4>(ka, BH, s);
+    case 5: return launch_nk<5>(ka, BH, s);
+    case 6: return launch_nk<6>(ka, BH, s);
+    case 7: return launch_nk<7>(ka, BH, s);
+    default: return launch_nk<8>(ka, BH, s);
+  }
 }
 
 }  // namespace had

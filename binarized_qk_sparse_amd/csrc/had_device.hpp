@@ -92,17 +92,36 @@ HAD_DEVICE uint32_t wave_min_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Exclusive prefix sum over lanes (lane 0 gets 0) and the wave total.
-HAD_DEVICE int wave_excl_scan_i32(int v, int* total) {
+HAD_DEVICE uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)dpp_i<kQuadSwap1>((int)v));
+  v = max(v, (uint32_t)dpp_i<kQuadSwap2>((int)v));
+  v = max(v, (uint32_t)dpp_i<kRowRor4>((int)v));
+  v = max(v, (uint32_t)dpp_i<kRowRor8>((int)v));
+  v = max(v, (uint32_t)dppm_i<kRowBcast15, 0xa>((int)v));
+  v = max(v, (uint32_t)dppm_i<kRowBcast31, 0xc>((int)v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Exclusive prefix sum over the 64 lanes on the DPP network (lane 0 gets 0).
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+
+HAD_DEVICE int wave_excl_scan_i32(int v) {
   int x = v;
-  int lane = lane_id();
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  *total = __builtin_amdgcn_readlane(x, 63);
+  x += dpp_i<kRowShr1>(x);  // lanes shifted in from outside the row read 0
+  x += dpp_i<kRowShr2>(x);
+  x += dpp_i<kRowShr4>(x);
+  x += dpp_i<kRowShr8>(x);
+  x += dppm_i<kRowBcast15, 0xa>(x);
+  x += dppm_i<kRowBcast31, 0xc>(x);
   return x - v;
+}
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed fp16 (round to nearest even).
+HAD_DEVICE uint32_t pack_half2(float lo, float hi) {
+  const half2v h = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, h);
 }
 
 // bf16 bits -> float (exact widening).

@@ -6,10 +6,14 @@
 //   S_i  = the N largest l_ij (ties to the lower j)
 //   O_i  = sum_{j in S_i} softmax_S(l)_j V_j           (fp32, or uint8 A x int8 V)
 //
-// Work decomposition.  A workgroup owns one (batch, head) and a tile of
-// consecutive queries; it stages that head's V rows in LDS once, and each of
-// its waves keeps every key's code bits in VGPRs (key j = 64 s + lane lives
-// in slot s of lane j % 64).  Per query the wave
+// Work decomposition.  The work is cut into units of 64 consecutive queries of
+// one (batch, head); each workgroup takes a contiguous run of units (logical
+// workgroup ids are XCD-remapped so the runs sharing a head sit on one XCD's
+// L2).  When its head changes a workgroup stages that head's V rows in LDS --
+// bf16 V as fp16 with a per-head power-of-two scale, so the A*V multiply-add
+// reads it with v_fma_mix_f32 and needs no conversion instruction -- and each
+// wave loads every key's code bits into VGPRs (key j = 64 s + lane lives in
+// slot s of lane j % 64).  Per query the wave
 //   1. forms the logit of every key (VALU XOR + v_bcnt, two words for d = 64),
 //   2. finds the exact top-N threshold without sorting:
 //        integer keys (alpha = 1, no bias): the logit is a function of the
@@ -23,8 +27,11 @@
 //   3. compacts the kept keys into a per-wave list in LDS (ascending j),
 //   4. softmax over the list (fp32), and
 //   5. A*V: eight lanes per kept key, eight channels per lane, V read from LDS
-//      (16-byte reads), fp32 FMA (or int32 multiply-add on int8 V), then a
+//      (16-byte reads), fp32 multiply-add (or int32 on int8 V), then a
 //      butterfly reduce-scatter leaves one output channel per lane.
+// fp16 staging of bf16 V is exact for every |v| >= 2^(k-17) (k the head's
+// scale exponent, 0 unless max|v| >= 2^15) and off by at most 2^(k-25) below,
+// so an output moves by at most 2^(k-25) (the probabilities sum to 1).
 // The kernel is bound by VALU issue; the only HBM traffic is codes, V and O.
 #include <float.h>
 #include <limits.h>
@@ -51,10 +58,10 @@ struct TopnKArgs {
   const float* vscale;
   float* out;
   int32_t* idx;
-  int H, n, keep, lcap, qt, tiles;
+  int H, n, keep, lcap, qt, tiles, units, upw;
   float isd;    // float(1/sqrt(d))
   float exp_c;  // 2*isd*log2(e): integer-key exponent per Hamming step
-  uint32_t list_off, cand_off, bias_off;
+  uint32_t list_off, cand_off, bias_off, red_off, keys_off, trash_off;
 };
 
 template <int VK>
@@ -72,6 +79,22 @@ HAD_DEVICE int count_le(const uint32_t (&P)[NP], int t) {
 #pragma unroll
   for (int m = 0; m < NP; ++m) c = __builtin_popcount((P[m] + add) & 0x80808080u) + c;
   return NP * 256 - wave_sum_i32((int)c);
+}
+
+// Both count_le(t - 1) and count_le(t) with one wave reduction (16-bit halves).
+template <int NP>
+HAD_DEVICE void count_le2(const uint32_t (&P)[NP], int t, int* c_tm1, int* c_t) {
+  const uint32_t add1 = (uint32_t)(128 - t) * 0x01010101u;  // h > t - 1
+  const uint32_t add0 = (uint32_t)(127 - t) * 0x01010101u;  // h > t
+  uint32_t c1 = 0, c0 = 0;
+#pragma unroll
+  for (int m = 0; m < NP; ++m) {
+    c1 = __builtin_popcount((P[m] + add1) & 0x80808080u) + c1;
+    c0 = __builtin_popcount((P[m] + add0) & 0x80808080u) + c0;
+  }
+  const int both = wave_sum_i32((int)((c0 << 16) + c1));
+  *c_tm1 = NP * 256 - (both & 0xffff);
+  *c_t = NP * 256 - (both >> 16);
 }
 
 template <int NS>
@@ -111,6 +134,26 @@ HAD_DEVICE T reduce_scatter8(T (&acc)[8], int k) {
   return kp + other;
 }
 
+// Streams `total` bytes (a multiple of 16) of global memory through f(offset,
+// 16 bytes), eight 16-byte loads in flight per thread before any is used.
+template <typename F>
+HAD_DEVICE void for_each16(const uint8_t* __restrict__ src, uint32_t total, F f) {
+  const uint32_t step = blockDim.x * 16u;
+  for (uint32_t base = threadIdx.x * 16u; base < total; base += 8u * step) {
+    uint4 w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t o = base + k * step;
+      w[k] = o < total ? *reinterpret_cast<const uint4*>(src + o) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t o = base + k * step;
+      if (o < total) f(o, w[k]);
+    }
+  }
+}
+
 template <int NS, bool FK, int VK, bool PAD>
 __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -119,48 +162,109 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
-  const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = wg / a.tiles, tile = wg % a.tiles, hh = bh % a.H;
   const int n = a.n, keep = a.keep;
-  const int i0 = tile * a.qt, i1 = min(n, i0 + a.qt);
-
-  // ---- stage this head's V rows in LDS (16 bytes per thread and step)
-  {
-    const uint8_t* src = static_cast<const uint8_t*>(a.v) + (size_t)bh * n * ROWB;
-    const uint32_t total = (uint32_t)n * ROWB;
-    for (uint32_t o = threadIdx.x * 16u; o < total; o += blockDim.x * 16u)
-      *reinterpret_cast<uint4*>(smem + o) = *reinterpret_cast<const uint4*>(src + o);
-  }
-  // ---- stage the bias offsets this tile touches: o = j - i + n - 1 in [n - i1, 2n - 2 - i0]
-  const int ob = n - i1;
-  float* biasw = reinterpret_cast<float*>(smem + a.bias_off);
-  if (FK && a.bias != nullptr) {
-    const int cnt = n + (i1 - i0) - 1;
-    const float* src = a.bias + (size_t)hh * (2 * n - 1) + ob;
-    for (int o = threadIdx.x; o < cnt; o += blockDim.x) biasw[o] = src[o];
-  }
-  // ---- the tile's query codes (and scales), one query per lane: read back with v_readlane
-  const size_t qrow = (size_t)bh * n + i0 + lane;
-  const uint2 qlane = (i0 + lane < i1) ? reinterpret_cast<const uint2*>(a.qbits)[qrow] : make_uint2(0u, 0u);
-  const float aqlane = (FK && a.aq != nullptr && i0 + lane < i1) ? a.aq[qrow] : 1.0f;
-  // ---- key codes: slot s of this lane is key 64 s + lane (PAD: j >= n are padding)
-  uint32_t k0[NS], k1[NS];
-  float akv[NS];
-  const uint2* kb = reinterpret_cast<const uint2*>(a.kbits) + (size_t)bh * n;
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int j = 64 * s + lane;
-    const bool ok = !PAD || j < n;
-    const uint2 kk = ok ? kb[j] : make_uint2(0u, 0u);
-    k0[s] = kk.x;
-    k1[s] = kk.y;
-    akv[s] = (FK && ok && a.ak != nullptr) ? a.ak[(size_t)bh * n + j] : 1.0f;
-  }
-  __syncthreads();
-
+  const int u0 = (int)xcd_remap(blockIdx.x, gridDim.x) * a.upw;
+  const int u1 = min(a.units, u0 + a.upw);
   uint2* list = reinterpret_cast<uint2*>(smem + a.list_off) + wave * a.lcap;
   uint2* cand = reinterpret_cast<uint2*>(smem + a.cand_off) + wave * 64;
+  uint32_t* keys = reinterpret_cast<uint32_t*>(smem + a.keys_off) + wave * a.lcap;
+  uint32_t* trash = reinterpret_cast<uint32_t*>(smem + a.trash_off) + wave * 64;
+  float* biasw = reinterpret_cast<float*>(smem + a.bias_off);
+  uint32_t* red = reinterpret_cast<uint32_t*>(smem + a.red_off);
+  uint32_t k0[NS], k1[NS];
+  float akv[NS];
+  int staged = -1;
+  float vmul = 1.0f;  // undoes the fp16 staging scale of V
   int tau_prev = 27;  // Hamming-level guess; each query starts from the last one's
+  uint2 qnext;
+  float aqnext;
+  {
+    const int nbh = u0 / a.tiles, ni0 = (u0 % a.tiles) * a.qt;
+    const bool ok = u0 < u1 && ni0 + lane < n;
+    const size_t nrow = (size_t)nbh * n + ni0 + lane;
+    qnext = ok ? reinterpret_cast<const uint2*>(a.qbits)[nrow] : make_uint2(0u, 0u);
+    aqnext = (FK && a.aq != nullptr && ok) ? a.aq[nrow] : 1.0f;
+  }
+
+  for (int u = u0; u < u1; ++u) {
+    const int bh = u / a.tiles, tile = u % a.tiles, hh = bh % a.H;
+    const int i0 = tile * a.qt, i1 = min(n, i0 + a.qt);
+    const bool restage = bh != staged;                       // uniform over the workgroup
+    const bool sync = restage || (FK && a.bias != nullptr);  // LDS contents change this unit
+    if (sync) __syncthreads();  // every wave is done with the previous unit's LDS data
+    if (restage) {
+      staged = bh;
+      // ---- this head's V rows into LDS (16 bytes per thread and step)
+      const uint8_t* src = static_cast<const uint8_t*>(a.v) + (size_t)bh * n * ROWB;
+      const uint32_t total = (uint32_t)n * ROWB;
+      if (VK == 1) {
+        // bf16 -> fp16 with a power-of-two scale 2^-k chosen so max|v| 2^-k < 2^15
+        uint32_t mx = 0;
+        for_each16(src, total, [&](uint32_t, const uint4& w) {
+          mx = max(mx, max(max(w.x & 0x7fffu, w.x >> 16 & 0x7fffu), max(w.y & 0x7fffu, w.y >> 16 & 0x7fffu)));
+          mx = max(mx, max(max(w.z & 0x7fffu, w.z >> 16 & 0x7fffu), max(w.w & 0x7fffu, w.w >> 16 & 0x7fffu)));
+        });
+        mx = wave_max_u32(mx);
+        if (lane == 0) red[wave] = mx;
+        __syncthreads();
+        mx = 0;
+        for (int w = 0; w < nwaves; ++w) mx = max(mx, red[w]);
+        const float vmax = __builtin_bit_cast(float, mx << 16);
+        int e;
+        (void)frexpf(vmax, &e);  // vmax < 2^e
+        const int kexp = max(0, e - 15);
+        const float down = ldexpf(1.0f, -kexp);
+        vmul = ldexpf(1.0f, kexp);
+        for_each16(src, total, [&](uint32_t o, const uint4& w) {
+          uint4 h;
+          h.x = pack_half2(bf16_lo(w.x) * down, bf16_hi(w.x) * down);
+          h.y = pack_half2(bf16_lo(w.y) * down, bf16_hi(w.y) * down);
+          h.z = pack_half2(bf16_lo(w.z) * down, bf16_hi(w.z) * down);
+          h.w = pack_half2(bf16_lo(w.w) * down, bf16_hi(w.w) * down);
+          *reinterpret_cast<uint4*>(smem + o) = h;
+        });
+      } else {
+        for_each16(src, total, [&](uint32_t o, const uint4& w) { *reinterpret_cast<uint4*>(smem + o) = w; });
+      }
+      // ---- key codes.  Float keys: slot s of this lane is key 64 s + lane.  Integer
+      // keys: slot s of lane l is key NS l + s (a lane holds consecutive keys).
+      // PAD: keys j >= n are padding.
+      const uint2* kb = reinterpret_cast<const uint2*>(a.kbits) + (size_t)bh * n;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int j = FK ? 64 * s + lane : NS * lane + s;
+        const bool ok = !PAD || j < n;
+        const uint2 kk = ok ? kb[j] : make_uint2(0u, 0u);
+        k0[s] = kk.x;
+        k1[s] = kk.y;
+        akv[s] = (FK && ok && a.ak != nullptr) ? a.ak[(size_t)bh * n + j] : 1.0f;
+      }
+    }
+    // ---- the bias offsets this tile touches: o = j - i + n - 1 in [n - i1, 2n - 2 - i0]
+    const int ob = n - i1;
+    if (FK && a.bias != nullptr) {
+      const int cnt = n + (i1 - i0) - 1;
+      const float* src = a.bias + (size_t)hh * (2 * n - 1) + ob;
+      for (int o = threadIdx.x; o < cnt; o += 2 * blockDim.x) {
+        const int o2 = o + blockDim.x;
+        const float b0 = src[o];
+        const float b1 = o2 < cnt ? src[o2] : 0.0f;
+        biasw[o] = b0;
+        if (o2 < cnt) biasw[o2] = b1;
+      }
+    }
+    // ---- the tile's query codes (and scales), one query per lane, read back with
+    // v_readlane; the next unit's are fetched now so their latency hides behind this unit
+    const uint2 qlane = qnext;
+    const float aqlane = aqnext;
+    if (u + 1 < u1) {
+      const int nbh = (u + 1) / a.tiles, ni0 = ((u + 1) % a.tiles) * a.qt;
+      const bool ok = ni0 + lane < n;
+      const size_t nrow = (size_t)nbh * n + ni0 + lane;
+      qnext = ok ? reinterpret_cast<const uint2*>(a.qbits)[nrow] : make_uint2(0u, 0u);
+      aqnext = (FK && a.aq != nullptr && ok) ? a.aq[nrow] : 1.0f;
+    }
+    if (sync) __syncthreads();
 
   for (int i = i0 + wave; i < i1; i += nwaves) {
     const size_t row = (size_t)bh * n + i;
@@ -175,7 +279,7 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         hv[s] = __builtin_popcount(k1[s] ^ q1) + __builtin_popcount(k0[s] ^ q0);
-        if (PAD && 64 * s + lane >= n) hv[s] = 65u;  // above every real distance
+        if (PAD && NS * lane + s >= n) hv[s] = 65u;  // above every real distance
       }
       uint32_t P[NP];
 #pragma unroll
@@ -190,31 +294,23 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
         tau = 65;  // every real key is below the padding level
         less = keep;
       } else {
+        // invariant once bracketed: count_le(lo) = clo < keep <= count_le(hi)
         int lo, hi, clo;
-        int t = tau_prev;
-        const int c = count_le<NP>(P, t);
-        if (c >= keep) {
+        const int t = tau_prev;  // in [1, 64]
+        int ctm1, ct;
+        count_le2<NP>(P, t, &ctm1, &ct);
+        if (ctm1 < keep && ct >= keep) {
+          lo = t - 1;
           hi = t;
-          const int c1 = t > 0 ? count_le<NP>(P, t - 1) : 0;
-          if (c1 < keep) {
-            lo = t - 1;
-            clo = c1;
-          } else {
-            hi = t - 1;
-            lo = -1;
-            clo = 0;
-          }
-        } else {
+          clo = ctm1;
+        } else if (ct < keep) {
           lo = t;
-          clo = c;
-          const int c1 = count_le<NP>(P, t + 1);
-          if (c1 >= keep) {
-            hi = t + 1;
-          } else {
-            lo = t + 1;
-            clo = c1;
-            hi = 64;
-          }
+          clo = ct;
+          hi = 64;
+        } else {
+          hi = t - 1;
+          lo = -1;
+          clo = 0;
         }
         while (hi - lo > 1) {
           const int mid = (lo + hi) >> 1;
@@ -228,39 +324,55 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
         }
         tau = hi;
         less = clo;
-        tau_prev = tau;
+        tau_prev = max(tau, 1);
       }
-      // ---- compaction: all h < tau, then the first (keep - less) keys with h == tau
-      int r = keep - less;
-      int base = 0;
+      // ---- tie cutoff and compaction, all in VALU (no per-slot scalar work).
+      // Keys are lane-major, so ascending j is lane order, then slot order.  Per lane:
+      // c_lt keys below tau and c_eq keys at tau (SWAR counts on the packed
+      // distances); a prefix over lanes of c_eq hands each lane `take` of the
+      // keep - less keys at tau (lowest j first); a prefix of c_lt + take gives the
+      // lane's first list position.
+      const int r = keep - less;
+      const uint32_t ad0 = (uint32_t)(128 - tau) * 0x01010101u;  // bit 7: h >= tau
+      const uint32_t ad1 = (uint32_t)(127 - tau) * 0x01010101u;  // bit 7: h >= tau + 1
+      int c_lt = 0, c_eq = 0;
+      uint32_t eqw[NP];
+#pragma unroll
+      for (int m = 0; m < NP; ++m) {
+        const uint32_t ge0 = (P[m] + ad0) & 0x80808080u;
+        const uint32_t ge1 = (P[m] + ad1) & 0x80808080u;
+        eqw[m] = ge0 ^ ge1;
+        c_lt += 4 - __builtin_popcount(ge0);
+        c_eq += __builtin_popcount(eqw[m]);
+      }
+      const int eq_before = wave_excl_scan_i32(c_eq);
+      const int take = min(max(r - eq_before, 0), c_eq);
+      const int lbase = wave_excl_scan_i32(c_lt + take);
+      // slot of this lane's take-th key at tau: the number of slots whose running
+      // count of keys at tau is still below take (byte-wise prefix counts)
+      int scut = 0;
+      uint32_t carry = 0;
+      const uint32_t adt = (uint32_t)(128 - take) * 0x01010101u;  // bit 7: count >= take
+#pragma unroll
+      for (int m = 0; m < NP; ++m) {
+        uint32_t x = eqw[m] >> 7;  // 0/1 per byte
+        x += x << 8;
+        x += x << 16;
+        x += carry * 0x01010101u;
+        carry = x >> 24;
+        scut += 4 - __builtin_popcount((x + adt) & 0x80808080u);
+      }
+      // selected: (h, s) <= (tau, scut) lexicographically, or h < tau when take == 0
+      // (a strict bound, so tau = 0 with take = 0 selects nothing)
+      const uint32_t lim = take > 0 ? (((uint32_t)tau << 5) | (uint32_t)scut) + 1u : ((uint32_t)tau << 5);
+      int pos = lbase;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const bool lt = hv[s] < (uint32_t)tau;
-        bool sel = lt;
-        uint64_t Sm = ballot(lt);
-        if (r > 0) {
-          const bool eq = hv[s] == (uint32_t)tau;
-          const uint64_t Em = ballot(eq);
-          const int e = __builtin_popcountll(Em);
-          if (e <= r) {
-            sel = lt || eq;
-            Sm |= Em;
-            r -= e;
-          } else {
-            uint64_t x = Em;
-            for (int k = 0; k < r; ++k) x &= x - 1;  // drop the r lowest set bits
-            const uint64_t take = Em ^ x;
-            sel = lt || ((take >> lane) & 1u);
-            Sm |= take;
-            r = 0;
-          }
-        }
-        if (sel) {
-          const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(Sm >> 32),
-                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)Sm, (uint32_t)base));
-          list[pos] = make_uint2((uint32_t)(64 * s + lane), hv[s]);  // exactly keep keys are selected
-        }
-        base += __builtin_popcountll(Sm);
+        const uint32_t w = (hv[s] << 5) | (uint32_t)s;
+        const bool sel = w < lim;
+        uint32_t* dst = sel ? keys + pos : trash + lane;
+        *dst = (w << 6) | (uint32_t)lane;  // h, slot, lane: j = NS * lane + slot
+        pos += sel ? 1 : 0;
       }
       tref = tau;
     } else {
@@ -383,25 +495,34 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
     // float keys: e_j = exp(l_j - max l).  Integer keys: e_j = exp(l_j - l(tau)) =
     // exp(2 (tau - h_j) / sqrt(d)); the shift cancels in the normalisation and
     // stays below exp(2 (d + 1) / sqrt(d)), far from float overflow.
+    // Unnormalised weights go to the list; fp32 paths scale the output by 1/Z at
+    // the end, the int8 path needs p itself for A_q and normalises here.
     float z = 0.0f;
-    for (int e = lane; e < keep; e += 64) {
-      const uint32_t sc = list[e].y;
-      const float ex = FK ? __expf(__builtin_bit_cast(float, sc) - ref) : exp2f((float)(tref - (int)sc) * a.exp_c);
-      z += ex;
-      list[e].y = __builtin_bit_cast(uint32_t, ex);
-    }
-    const float inv_z = 1.0f / wave_sum_f32(z);
     for (int e = lane; e < a.lcap; e += 64) {
-      uint2 ent = e < keep ? list[e] : make_uint2(0u, 0u);
-      const float p = __builtin_bit_cast(float, ent.y) * inv_z;
-      if (VK == 2) {
-        const float qv = fminf(fmaxf(rintf(255.0f * p), 0.0f), 255.0f);
-        ent.y = e < keep ? (uint32_t)qv : 0u;
-      } else {
-        ent.y = e < keep ? __builtin_bit_cast(uint32_t, p) : 0u;
+      uint2 ent = make_uint2(0u, 0u);
+      if (e < keep) {
+        float ex;
+        if (FK) {
+          ent = list[e];
+          ex = __expf(__builtin_bit_cast(float, ent.y) - ref);
+        } else {
+          const uint32_t key = keys[e];  // h << 11 | slot << 6 | lane
+          ent.x = (uint32_t)NS * (key & 63u) + ((key >> 6) & 31u);
+          ex = exp2f((float)(tref - (int)(key >> 11)) * a.exp_c);
+        }
+        z += ex;
+        ent.y = __builtin_bit_cast(uint32_t, ex);
+        if (a.idx != nullptr) a.idx[row * keep + e] = (int32_t)ent.x;
       }
       list[e] = ent;
-      if (a.idx != nullptr && e < keep) a.idx[row * keep + e] = (int32_t)ent.x;
+    }
+    const float inv_z = __builtin_amdgcn_rcpf(wave_sum_f32(z));
+    if (VK == 2) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      for (int e = lane; e < keep; e += 64) {
+        const float p = __builtin_bit_cast(float, list[e].y) * inv_z;
+        list[e].y = (uint32_t)fminf(fmaxf(rintf(255.0f * p), 0.0f), 255.0f);
+      }
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
@@ -409,14 +530,20 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
     const int k = lane >> 3, g = lane & 7;
     if (VK == 2) {
       int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int t = 0; t < a.lcap; t += 8) {
-        const uint2 ent = list[t + k];
-        const uint2 raw = *reinterpret_cast<const uint2*>(smem + ent.x * ROWB + g * 8);
-        const int aq8 = (int)ent.y;
+      for (int t = 0; t < a.lcap; t += 32) {
+        uint2 ent[4], raw[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          acc[c] += aq8 * (int)(int8_t)(raw.x >> (8 * c));
-          acc[4 + c] += aq8 * (int)(int8_t)(raw.y >> (8 * c));
+        for (int u4 = 0; u4 < 4; ++u4) ent[u4] = list[t + 8 * u4 + k];
+#pragma unroll
+        for (int u4 = 0; u4 < 4; ++u4) raw[u4] = *reinterpret_cast<const uint2*>(smem + ent[u4].x * ROWB + g * 8);
+#pragma unroll
+        for (int u4 = 0; u4 < 4; ++u4) {
+          const int aq8 = (int)ent[u4].y;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            acc[c] += aq8 * (int)(int8_t)(raw[u4].x >> (8 * c));
+            acc[4 + c] += aq8 * (int)(int8_t)(raw[u4].y >> (8 * c));
+          }
         }
       }
       const int tot = reduce_scatter8<int>(acc, k);
@@ -425,35 +552,54 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
       a.out[row * kD + ch] = __fdiv_rn(__fmul_rn((float)tot, sc), 255.0f);
     } else {
       float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int t = 0; t < a.lcap; t += 8) {
-        const uint2 ent = list[t + k];
-        const float p = __builtin_bit_cast(float, ent.y);
-        if (VK == 1) {
-          const uint4 raw = *reinterpret_cast<const uint4*>(smem + ent.x * ROWB + g * 16);
-          acc[0] = __builtin_fmaf(p, bf16_lo(raw.x), acc[0]);
-          acc[1] = __builtin_fmaf(p, bf16_hi(raw.x), acc[1]);
-          acc[2] = __builtin_fmaf(p, bf16_lo(raw.y), acc[2]);
-          acc[3] = __builtin_fmaf(p, bf16_hi(raw.y), acc[3]);
-          acc[4] = __builtin_fmaf(p, bf16_lo(raw.z), acc[4]);
-          acc[5] = __builtin_fmaf(p, bf16_hi(raw.z), acc[5]);
-          acc[6] = __builtin_fmaf(p, bf16_lo(raw.w), acc[6]);
-          acc[7] = __builtin_fmaf(p, bf16_hi(raw.w), acc[7]);
+      // four entries per group in flight: their list reads, then their row reads, then the math
+      for (int t = 0; t < a.lcap; t += 32) {
+        uint2 ent[4];
+#pragma unroll
+        for (int u4 = 0; u4 < 4; ++u4) ent[u4] = list[t + 8 * u4 + k];
+        if (VK == 1) {  // fp16 rows: the widening folds into v_fma_mix_f32
+          uint4 raw[4];
+#pragma unroll
+          for (int u4 = 0; u4 < 4; ++u4) raw[u4] = *reinterpret_cast<const uint4*>(smem + ent[u4].x * ROWB + g * 16);
+#pragma unroll
+          for (int u4 = 0; u4 < 4; ++u4) {
+            const float p = __builtin_bit_cast(float, ent[u4].y);
+            const half2v h0 = __builtin_bit_cast(half2v, raw[u4].x), h1 = __builtin_bit_cast(half2v, raw[u4].y);
+            const half2v h2 = __builtin_bit_cast(half2v, raw[u4].z), h3 = __builtin_bit_cast(half2v, raw[u4].w);
+            acc[0] = __builtin_fmaf(p, (float)h0.x, acc[0]);
+            acc[1] = __builtin_fmaf(p, (float)h0.y, acc[1]);
+            acc[2] = __builtin_fmaf(p, (float)h1.x, acc[2]);
+            acc[3] = __builtin_fmaf(p, (float)h1.y, acc[3]);
+            acc[4] = __builtin_fmaf(p, (float)h2.x, acc[4]);
+            acc[5] = __builtin_fmaf(p, (float)h2.y, acc[5]);
+            acc[6] = __builtin_fmaf(p, (float)h3.x, acc[6]);
+            acc[7] = __builtin_fmaf(p, (float)h3.y, acc[7]);
+          }
         } else {
-          const float4 r0 = *reinterpret_cast<const float4*>(smem + ent.x * ROWB + g * 32);
-          const float4 r1 = *reinterpret_cast<const float4*>(smem + ent.x * ROWB + g * 32 + 16);
-          acc[0] = __builtin_fmaf(p, r0.x, acc[0]);
-          acc[1] = __builtin_fmaf(p, r0.y, acc[1]);
-          acc[2] = __builtin_fmaf(p, r0.z, acc[2]);
-          acc[3] = __builtin_fmaf(p, r0.w, acc[3]);
-          acc[4] = __builtin_fmaf(p, r1.x, acc[4]);
-          acc[5] = __builtin_fmaf(p, r1.y, acc[5]);
-          acc[6] = __builtin_fmaf(p, r1.z, acc[6]);
-          acc[7] = __builtin_fmaf(p, r1.w, acc[7]);
+          float4 r0[4], r1[4];
+#pragma unroll
+          for (int u4 = 0; u4 < 4; ++u4) {
+            r0[u4] = *reinterpret_cast<const float4*>(smem + ent[u4].x * ROWB + g * 32);
+            r1[u4] = *reinterpret_cast<const float4*>(smem + ent[u4].x * ROWB + g * 32 + 16);
+          }
+#pragma unroll
+          for (int u4 = 0; u4 < 4; ++u4) {
+            const float p = __builtin_bit_cast(float, ent[u4].y);
+            acc[0] = __builtin_fmaf(p, r0[u4].x, acc[0]);
+            acc[1] = __builtin_fmaf(p, r0[u4].y, acc[1]);
+            acc[2] = __builtin_fmaf(p, r0[u4].z, acc[2]);
+            acc[3] = __builtin_fmaf(p, r0[u4].w, acc[3]);
+            acc[4] = __builtin_fmaf(p, r1[u4].x, acc[4]);
+            acc[5] = __builtin_fmaf(p, r1[u4].y, acc[5]);
+            acc[6] = __builtin_fmaf(p, r1[u4].z, acc[6]);
+            acc[7] = __builtin_fmaf(p, r1[u4].w, acc[7]);
+          }
         }
       }
-      a.out[row * kD + 8 * g + k] = reduce_scatter8<float>(acc, k);
+      a.out[row * kD + 8 * g + k] = reduce_scatter8<float>(acc, k) * (vmul * inv_z);
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  }
   }
 }
 
@@ -525,7 +671,7 @@ hipError_t launch_topn(const AttnParams& p, hipStream_t s) {
   ka.H = (int)p.H;
   ka.n = (int)p.n;
   ka.keep = (int)p.keep;
-  ka.lcap = (int)((p.keep + 7) / 8 * 8);
+  ka.lcap = (int)((p.keep + 31) / 32 * 32);
   ka.qt = kQTile;
   ka.tiles = (int)((p.n + kQTile - 1) / kQTile);
   ka.isd = (float)(1.0 / sqrt((double)p.d));
@@ -533,15 +679,23 @@ hipError_t launch_topn(const AttnParams& p, hipStream_t s) {
   const uint32_t vbytes = align16((uint32_t)p.n * rowb);
   const uint32_t bias_bytes = fk ? align16((uint32_t)(p.n + kQTile - 1) * 4u) : 0u;
   // as many waves as LDS allows (lists and candidate buffers are per wave)
-  const uint32_t per_wave = (uint32_t)ka.lcap * 8u + (fk ? 64u * 8u : 0u);
+  const uint32_t per_wave = (uint32_t)ka.lcap * (fk ? 8u : 12u) + (fk ? 64u * 8u : 256u);
+  const uint32_t fixed = vbytes + bias_bytes + 4u * kMaxWaves;
   int nw = kMaxWaves;
-  while (nw > 1 && vbytes + bias_bytes + per_wave * nw > kLdsBytes) --nw;
-  if (vbytes + bias_bytes + per_wave * nw > kLdsBytes) return hipErrorInvalidValue;
+  while (nw > 1 && fixed + per_wave * nw > kLdsBytes) --nw;
+  if (fixed + per_wave * nw > kLdsBytes) return hipErrorInvalidValue;
   ka.bias_off = vbytes;
   ka.list_off = vbytes + bias_bytes;
   ka.cand_off = ka.list_off + (uint32_t)ka.lcap * 8u * nw;
-  const uint32_t lds = ka.cand_off + (fk ? 64u * 8u * nw : 0u);
-  const dim3 grid((unsigned)(p.B * p.H * ka.tiles));
+  ka.red_off = ka.cand_off + (fk ? 64u * 8u * nw : 0u);
+  ka.keys_off = ka.red_off + 4u * kMaxWaves;
+  ka.trash_off = ka.keys_off + (fk ? 0u : (uint32_t)ka.lcap * 4u * nw);
+  const uint32_t lds = ka.trash_off + (fk ? 0u : 256u * nw);
+  // persistent workgroups: one per CU, each taking a contiguous run of units
+  ka.units = (int)(p.B * p.H * ka.tiles);
+  const int target = 256;
+  ka.upw = (ka.units + target - 1) / target;
+  const dim3 grid((unsigned)((ka.units + ka.upw - 1) / ka.upw));
   const dim3 block((unsigned)(64 * nw));
   const bool pad = p.n != (int64_t)NS * 64;  // padding keys exist in the last slots
   switch (NS) {

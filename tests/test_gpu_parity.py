@@ -264,3 +264,19 @@ def test_topn_c5_full_size_sampled():
     assert np.array_equal(idx.cpu().numpy().reshape(-1, w.top_n)[rows], ref["idx"])
     vq, sc = ops.workspace_view(ws, w.B, w.H, w.n, w.d)
     _check_q8(out.cpu().numpy().reshape(-1, 64)[rows], vq.cpu().numpy(), sc.cpu().numpy(), ref, rows, w.n, "c5")
+
+
+def test_topn_zero_distance_ties():
+    # identical codes give Hamming distance 0 for many keys: the threshold level is
+    # the lowest one and the tie budget runs out part-way through the keys
+    g = np.random.default_rng(6)
+    B, H, n = 1, 2, 256
+    x = g.standard_normal((B, H, n, 64)).astype(np.float32)
+    x[:, :, ::3] = x[:, :, :1]  # every third key equals key 0
+    qb, _, _ = oracle.pack(x, oracle.SIGN)
+    v = torch.from_numpy(g.standard_normal((B, H, n, 64)).astype(np.float32)).to(torch.bfloat16)
+    for N in (1, 5, 40, 85, 86, 200):
+        out, idx = _run_topn(qb, qb, None, None, None, v, N)
+        ref = oracle.attention(qb, qb, f32(v), top_n=N, want_idx=True)
+        assert np.array_equal(idx, ref["idx"]), N
+        assert_close(out, ref["out"], f"zero-distance ties N={N}")
