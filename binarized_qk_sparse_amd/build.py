@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhad.so")
-SOURCES = ["api.cpp", "pack.hip", "vquant.hip", "topn.hip", "topn_stream.hip", "dense_q8.hip"]
+SOURCES = ["api.cpp", "pack.hip", "vquant.hip", "topn.hip", "topn_mfma.hip", "topn_stream.hip", "dense_q8.hip"]
 ARCH = "gfx950"
 
 

@@ -184,7 +184,9 @@ int had_attention_topn(const uint32_t* qbits, const uint32_t* kbits, const float
     p.v = q.vq;
     p.vscale = q.vscale;
   }
-  return launch_status(streaming ? launch_topn_stream(p, s) : launch_topn(p, s), fn);
+  if (streaming) return launch_status(launch_topn_stream(p, s), fn);
+  if (topn_mfma_supported(p)) return launch_status(launch_topn_mfma(p, s), fn);
+  return launch_status(launch_topn(p, s), fn);
 }
 
 int binattn_dense_q8(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q, const float* alpha_k,

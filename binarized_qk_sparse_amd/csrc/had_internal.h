@@ -50,6 +50,8 @@ struct AttnParams {
   int32_t* idx;
 };
 hipError_t launch_topn(const AttnParams& p, hipStream_t s);
+bool topn_mfma_supported(const AttnParams& p);
+hipError_t launch_topn_mfma(const AttnParams& p, hipStream_t s);
 hipError_t launch_topn_stream(const AttnParams& p, hipStream_t s);
 int64_t topn_stream_max_keep();
 hipError_t launch_dense_q8(const AttnParams& p, hipStream_t s);

@@ -1,0 +1,483 @@
+// Top-N binarized attention with integer logits (alpha = 1, no bias) and bf16
+// V, for n <= 1024: exact top-N selection on VALU, A*V on bf16 matrix cores.
+//
+// Method (Hamming Attention Distillation, summary "main points"/"method";
+// BinaryAttention sections 2.2-2.3):
+//   l_ij = (d - 2 h_ij) / sqrt(d),  h_ij = popcount(q_i XOR k_j)
+//   S_i  = the N largest l_ij, ties to the lower j
+//   O_i  = sum_{j in S_i} softmax_S(l)_j V_j                  (fp32)
+// With alpha = 1 and no bias the logit is a function of h alone, so S_i is
+// { h < tau } plus the lowest-indexed keys at h = tau, where tau is the
+// smallest level with #{h <= tau} >= N; and the softmax weight relative to the
+// threshold is w(tau - h) = exp(2 (tau - h) / sqrt(d)), a table of 65 values.
+//
+// Work decomposition.  A wave owns a tile of 16 queries of one (batch, head).
+// Lane l serves query row r = l % 16 and key quarter g = l / 16 (keys
+// [g Q, (g+1) Q), Q = n_pad / 4): the same (row, key) split as the A operand
+// of v_mfma_f32_16x16x32_bf16, so no data moves between selection and the
+// matrix cores.
+//   1. Hamming distances: each lane loads one key code per 16 keys and the
+//      16 lanes of a row share them through DPP row broadcasts, folded into
+//      the XOR (v_xor_b32_dpp row_newbcast); v_bcnt_u32_b32 accumulates the
+//      two words.  Distances are byte-packed four to a register.
+//   2. Threshold: per-lane SWAR counts (add / and / popcount, four keys per
+//      instruction) summed over the query's four lanes, starting from a guess
+//      and bracketing per lane.
+//   3. Ties: each lane takes its share of the keys at tau, lowest j first
+//      (exclusive prefix over the four quarters, then a running count over the
+//      lane's keys in ascending order).
+//   4. Weights: index byte = h - tau + 65 (plus 128 for a key at tau that is
+//      not taken) into an LDS table of w split as bf16 hi + bf16 lo
+//      (hi = rne(w), lo = rne(w - hi): 16 significant bits), zero for h > tau.
+//   5. A*V: the masked weight row of the tile (16 queries x 32 keys per step)
+//      times V (exact in bf16, staged transposed in LDS), hi and lo into one
+//      fp32 accumulator; a constant all-ones operand accumulates the softmax
+//      normaliser Z in the same layout, and O = acc / Z.
+// The selection is exact (bit-identical index sets); the weights carry a
+// relative error below 2^-16, far inside the fp32 output tolerance.
+#include <float.h>
+#include <limits.h>
+
+#include <algorithm>
+#include <type_traits>
+
+#include "had_device.hpp"
+#include "had_internal.h"
+#include "../../include/had.h"
+
+namespace had {
+namespace {
+
+constexpr int kD = 64;
+constexpr uint32_t kC = 0x01010101u;
+constexpr uint32_t kM = 0x80808080u;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct MfmaKArgs {
+  const uint32_t* qbits;  // [BH, n, 2]
+  const uint32_t* kbits;  // [BH, n, 2]
+  const uint32_t* v;      // bf16 [BH, n, 64], read as pairs
+  float* out;             // [BH, n, 64]
+  int32_t* idx;           // [BH, n, keep] or null
+  int n, keep;
+  int tiles;  // 16-query tiles per head
+  int split;  // workgroups per head
+  int tpw;    // tiles per workgroup
+  int t0;     // first threshold guess
+  float exp_c;  // 2 / sqrt(d) * log2(e)
+};
+
+// Value of lane S of this lane's 16-lane row (DPP row_newbcast; folds into the
+// consuming VALU instruction).
+template <int S>
+HAD_DEVICE uint32_t row_bcast(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + S, 0xf, 0xf, false);
+}
+
+template <int N>
+struct Seq {
+  template <class F>
+  HAD_DEVICE static void run(F&& f) {
+    Seq<N - 1>::run(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+};
+template <>
+struct Seq<0> {
+  template <class F>
+  HAD_DEVICE static void run(F&&) {}
+};
+
+// Sum over the four lanes of one query row (lanes r, r+16, r+32, r+48).
+HAD_DEVICE int quad_rows_sum(int v) {
+  v += __shfl_xor(v, 16, 64);
+  return v + __shfl_xor(v, 32, 64);
+}
+
+// Exclusive prefix over the key quarters g = 0..3 of one query row.
+HAD_DEVICE int quad_rows_excl(int v, int g) {
+  const int lane = (int)lane_id();
+  int a = __shfl(v, (lane - 16) & 63, 64);
+  int s = v + (g >= 1 ? a : 0);
+  a = __shfl(s, (lane - 32) & 63, 64);
+  s += (g >= 2 ? a : 0);
+  return s - v;
+}
+
+// Keys of this lane with h <= t (per-lane t), four byte-packed distances per word.
+template <int NW>
+HAD_DEVICE int lane_count_le(const uint32_t (&P)[NW], int t) {
+  const uint32_t add = (uint32_t)(127 - t) * kC;  // bit 7 of b + add: b > t
+  uint32_t c = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) c = __builtin_popcount((P[w] + add) & kM) + c;
+  return 4 * NW - (int)c;
+}
+
+// Both lane_count_le(t - 1) (.x) and lane_count_le(t) (.y).
+template <int NW>
+HAD_DEVICE int2 lane_count_le2(const uint32_t (&P)[NW], int t) {
+  const uint32_t add1 = (uint32_t)(128 - t) * kC;  // b > t - 1
+  const uint32_t add0 = (uint32_t)(127 - t) * kC;  // b > t
+  uint32_t c1 = 0, c0 = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    c1 = __builtin_popcount((P[w] + add1) & kM) + c1;
+    c0 = __builtin_popcount((P[w] + add0) & kM) + c0;
+  }
+  return make_int2(4 * NW - (int)c1, 4 * NW - (int)c0);
+}
+
+HAD_DEVICE uint32_t bf16_rne_bits(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Waves per workgroup: enough that each thread prefetches at most four 32-byte V pieces.
+constexpr int mfma_waves(int nk) { return nk >= 32 ? 16 : (nk >= 16 ? 8 : 4); }
+
+// IDX: also write the kept-index list (a separate instance, so that the common
+// kernel carries none of its code).
+template <int NK, bool PAD, bool IDX>
+__global__ __launch_bounds__(64 * mfma_waves(NK)) void topn_mfma_kernel(const MfmaKArgs a) {
+  constexpr int NWV = mfma_waves(NK);
+  constexpr int KG = 8 * NK;       // keys per lane (one quarter of the padded row)
+  constexpr int NW = 2 * NK;       // byte-packed distance words per lane
+  constexpr int NP = 32 * NK;      // padded keys
+  constexpr int VS = NP + 8;       // V^T row stride in bf16 (16 bytes of skew per channel)
+  // The weight table is the kernel's only static LDS array, so its address is
+  // fixed at compile time and a lookup address is just index * 4.
+  __shared__ __align__(16) uint32_t tab[256];
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint16_t* vt = reinterpret_cast<uint16_t*>(smem);  // [64][VS]
+
+  const int lane = (int)lane_id();
+  const int g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr int nwv = NWV;  // the launch always uses 64 * NWV threads
+  const int bh = blockIdx.x / a.split, part = blockIdx.x % a.split;
+  const int tbeg = part * a.tpw, tend = min(a.tiles, tbeg + a.tpw);
+  const int n = a.n, keep = a.keep;
+  const size_t hb = (size_t)bh * n;
+
+  // ---- V of this head: loads issued now, consumed after the first tile's selection
+  constexpr int kPieces = NP / 2 * 8;  // (key pair, 8-channel block) pieces of 2 x 16 bytes
+  constexpr int kPf = kPieces / (64 * NWV);
+  static_assert(kPf * 64 * NWV == kPieces, "pieces must split evenly over the threads");
+  uint4 pf[kPf][2];
+  {
+    const uint4* vsrc = reinterpret_cast<const uint4*>(a.v + hb * (kD / 2));
+#pragma unroll
+    for (int p = 0; p < kPf; ++p) {
+      const int piece = threadIdx.x + p * 64 * NWV;
+      const int jp = piece >> 3, cb = piece & 7;
+      const int j0 = 2 * jp, j1 = 2 * jp + 1;
+      // unconditional loads (clamped rows) and selects keep this free of branches;
+      // padding keys stage as zeros
+      pf[p][0] = vsrc[(size_t)(PAD ? min(j0, n - 1) : j0) * 8 + cb];
+      pf[p][1] = vsrc[(size_t)(PAD ? min(j1, n - 1) : j1) * 8 + cb];
+      if (PAD) {
+        const bool z0 = j0 >= n, z1 = j1 >= n;
+        pf[p][0] = make_uint4(z0 ? 0u : pf[p][0].x, z0 ? 0u : pf[p][0].y, z0 ? 0u : pf[p][0].z, z0 ? 0u : pf[p][0].w);
+        pf[p][1] = make_uint4(z1 ? 0u : pf[p][1].x, z1 ? 0u : pf[p][1].y, z1 ? 0u : pf[p][1].z, z1 ? 0u : pf[p][1].w);
+      }
+    }
+  }
+
+  // one prefetched piece -> V^T in LDS: channels 8cb..8cb+7 of keys 2jp, 2jp + 1
+  auto stage_piece = [&](int p) {
+    const int piece = threadIdx.x + p * 64 * NWV;
+    const int jp = piece >> 3, cb = piece & 7;
+    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&pf[p][0]);
+    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&pf[p][1]);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(vt + (size_t)(8 * cb) * VS + 2 * jp);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // channel 2e (low halves) and 2e + 1 (high halves) of the two keys
+      dst[(2 * e) * (VS / 2)] = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
+      dst[(2 * e + 1) * (VS / 2)] = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
+    }
+  };
+  constexpr int kSteps = KG / 16;  // Hamming steps of 16 keys per lane row
+  constexpr int kStageAt = kSteps > kPf ? kSteps - kPf : 0;  // step that writes piece 0
+
+  int tq = a.t0;  // per-lane threshold guess, carried from tile to tile
+  uint32_t P[NW];
+  int tau = 0, less = 0, cl_lo = 0, cl_hi = 0;
+
+  // Steps 1-2 for tile t: distances into P, then tau, the query's count below tau
+  // (less) and this lane's counts at tau - 1 and tau.  STAGE: also move the
+  // prefetched V pieces into LDS, one per Hamming step near the end.
+  auto select = [&](int t, auto stage_tag) {
+    constexpr bool STAGE = decltype(stage_tag)::value;
+    const int i = t * 16 + r;
+    // ------------------------------------------------ 1. Hamming distances
+    const uint2 q = i < n ? reinterpret_cast<const uint2*>(a.qbits)[hb + i] : make_uint2(0u, 0u);
+    const uint2* kb = reinterpret_cast<const uint2*>(a.kbits) + hb;
+    auto kload = [&](int m) {
+      const int j = g * KG + 16 * m + r;  // the key this lane loads for its row
+      return kb[PAD ? min(j, n - 1) : j];  // padding keys: any code (their bytes are overwritten)
+    };
+    uint2 kc = kload(0);
+#pragma unroll
+    for (int m = 0; m < kSteps; ++m) {
+      const uint2 kcur = kc;
+      if (m + 1 < kSteps) kc = kload(m + 1);
+      uint32_t hv[16];
+      Seq<16>::run([&](auto s) {
+        constexpr int S = decltype(s)::value;
+        uint32_t h = __builtin_popcount(row_bcast<S>(kcur.x) ^ q.x);
+        hv[S] = __builtin_popcount(row_bcast<S>(kcur.y) ^ q.y) + h;
+      });
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t word = (hv[4 * w + 3] << 24) | (hv[4 * w + 2] << 16) | (hv[4 * w + 1] << 8) | hv[4 * w];
+        if (PAD) {
+          // padding keys (j >= n) get a byte of at least 65, above every real distance:
+          // h | 0x41 lies in [65, 127], which keeps all byte sums below carry
+          const int real = n - (g * KG + 16 * m + 4 * w);  // real keys in this word
+          const uint32_t pm = real >= 4 ? 0u : (real <= 0 ? 0x41414141u : (0x41414141u << (8 * real)));
+          word |= pm;
+        }
+        P[4 * m + w] = word;
+      }
+      if (STAGE && m >= kStageAt && m - kStageAt < kPf) stage_piece(m - kStageAt);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (STAGE)
+#pragma unroll
+      for (int p = kSteps - kStageAt; p < kPf; ++p) stage_piece(p);
+    // ------------------------------------------------ 2. threshold
+    // Invariant once bracketed: C(lo) < keep <= C(hi), C(t) = #{h <= t} over the
+    // query's keys; cl_lo / cl_hi are this lane's share of C(lo) / C(hi).
+    // (written as selects: conditional stores to different variables would be
+    // merged into a store through a selected address, which forces them to memory)
+    int lo, hi, clo, llo, lhi;
+    {
+      const int2 cc = lane_count_le2<NW>(P, tq);
+      const int both = quad_rows_sum((cc.y << 16) | cc.x);
+      const int ta = both & 0xffff, tb = both >> 16;
+      const bool below = ta >= keep;            // tau < tq - 1 ... tau <= tq - 1
+      const bool at = !below && tb >= keep;     // tau == tq
+      // below: (lo, hi) = (-1, tq - 1); at: (tq - 1, tq); above: (tq, 65)
+      lo = below ? -1 : (at ? tq - 1 : tq);
+      hi = below ? tq - 1 : (at ? tq : 65);     // C(65) = n >= keep: a placeholder bound
+      clo = below ? 0 : (at ? ta : tb);
+      llo = below ? 0 : (at ? cc.x : cc.y);
+      lhi = below ? cc.x : (at ? cc.y : 0);
+    }
+    while (__builtin_amdgcn_ballot_w64(hi - lo > 1) != 0) {
+      // probe next to the guess first, then bisect
+      const bool open = hi - lo > 1;
+      int mid = hi == 65 ? lo + 1 : (lo == -1 ? hi - 1 : (lo + hi) >> 1);
+      mid = open ? mid : hi;  // settled lanes re-count harmlessly
+      const int cm = lane_count_le<NW>(P, mid);
+      const int tm = quad_rows_sum(cm);
+      const bool up = open && tm >= keep;   // mid becomes the upper bound
+      const bool dn = open && tm < keep;    // mid becomes the lower bound
+      hi = up ? mid : hi;
+      lhi = up ? cm : lhi;
+      lo = dn ? mid : lo;
+      clo = dn ? tm : clo;
+      llo = dn ? cm : llo;
+    }
+    cl_lo = llo;
+    cl_hi = lhi;
+    tau = hi;
+    less = clo;
+    tq = max(tau, 1);
+  };
+
+  const int tfirst = tbeg + wave;
+  if (tfirst < tend) {
+    select(tfirst, std::true_type{});
+  } else {
+#pragma unroll
+    for (int p = 0; p < kPf; ++p) stage_piece(p);
+  }
+  // ---- the weight table; then every wave's V^T pieces are in place
+  for (int e = threadIdx.x; e < 256; e += 64 * NWV) {
+    uint32_t ent = 0u;
+    if (e >= 1 && e <= 65) {
+      const float w = exp2f((float)(65 - e) * a.exp_c);  // w(tau - h), h = e + tau - 65
+      const uint32_t hi16 = bf16_rne_bits(w);
+      const float rest = w - __builtin_bit_cast(float, hi16 << 16);
+      ent = hi16 | (bf16_rne_bits(rest) << 16);
+    }
+    tab[e] = ent;
+  }
+  __syncthreads();
+
+  for (int t = tfirst; t < tend; t += nwv) {
+    if (t != tfirst) select(t, std::false_type{});
+    const int i = t * 16 + r;  // this lane's query
+    // ------------------------------------------------ 3. ties
+    const int ceq = cl_hi - cl_lo;                 // this lane's keys at tau
+    const int before = quad_rows_excl(ceq, g);     // keys at tau in lower quarters
+    const int take = min(max(keep - less - before, 0), ceq);
+    const uint32_t kidx = (uint32_t)(65 - tau) * kC;
+
+    // ------------------------------------------------ 4-5. weights and A*V
+    f32x4 acc[4], accz;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accz = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+    const uint16_t* vrow = vt + (size_t)r * VS + g * KG;
+    int run = 0;  // keys at tau met so far in this lane (ascending j)
+    // optional kept-index list: this lane's keys follow those of the lower quarters
+    int32_t* idst = nullptr;
+    int ipos = 0;
+    if (IDX) {
+      ipos = quad_rows_excl(cl_lo + take, g);
+      idst = a.idx + (hb + (i < n ? i : 0)) * (size_t)keep;
+    }
+#pragma unroll
+    for (int c = 0; c < NK; ++c) {
+      uint32_t I0 = P[2 * c] + kidx, I1 = P[2 * c + 1] + kidx;  // h - tau + 65 per byte
+      const uint32_t E0 = ((I0 + 63u * kC) ^ (I0 + 62u * kC)) & kM;  // h == tau
+      const uint32_t E1 = ((I1 + 63u * kC) ^ (I1 + 62u * kC)) & kM;
+      const int run1 = __builtin_popcount(E1) + (__builtin_popcount(E0) + run);
+      uint32_t U0 = run1 <= take ? 0u : E0, U1 = run1 <= take ? 0u : E1;  // keys at tau not taken
+      const bool part = run < take && run1 > take;
+      if (__builtin_amdgcn_ballot_w64(part) != 0 && part) {
+        // keep the first take - run keys at tau of this step (bytes of E0, then E1)
+        const uint32_t rem = (uint32_t)(take - run);
+        const uint32_t x0 = E0 >> 7, x1 = E1 >> 7;
+        const uint32_t p0 = x0 + (x0 << 8) + (x0 << 16) + (x0 << 24);  // inclusive ranks
+        const uint32_t p1 = x1 + (x1 << 8) + (x1 << 16) + (x1 << 24) + (uint32_t)__builtin_popcount(E0) * kC;
+        const uint32_t ad = (127u - rem) * kC;  // bit 7: rank >= rem + 1
+        U0 = E0 & (p0 + ad);
+        U1 = E1 & (p1 + ad);
+      }
+      run = run1;
+      I0 |= U0;
+      I1 |= U1;
+      if (IDX && i < n) {
+        // kept keys have a table index in [1, 65]
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const uint32_t ib = ((b < 4 ? I0 : I1) >> (8 * (b & 3))) & 0xffu;
+          if (ib <= 65u) idst[ipos++] = g * KG + 8 * c + b;
+        }
+      }
+      // table entries (hi | lo << 16) of the eight keys, then hi and lo operands
+      uint32_t ent[8];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        ent[b] = tab[(I0 >> (8 * b)) & 0xffu];
+        ent[4 + b] = tab[(I1 >> (8 * b)) & 0xffu];
+      }
+      uint32_t ah[4], al[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ah[e] = __builtin_amdgcn_perm(ent[2 * e + 1], ent[2 * e], 0x05040100u);
+        al[e] = __builtin_amdgcn_perm(ent[2 * e + 1], ent[2 * e], 0x07060302u);
+      }
+      const bf16x8 A_hi = __builtin_bit_cast(bf16x8, make_uint4(ah[0], ah[1], ah[2], ah[3]));
+      const bf16x8 A_lo = __builtin_bit_cast(bf16x8, make_uint4(al[0], al[1], al[2], al[3]));
+      bf16x8 Bv[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+        Bv[tt] = *reinterpret_cast<const bf16x8*>(vrow + (size_t)(16 * tt) * VS + 8 * c);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, Bv[tt], acc[tt], 0, 0, 0);
+      accz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, ones, accz, 0, 0, 0);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, Bv[tt], acc[tt], 0, 0, 0);
+      accz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, ones, accz, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ------------------------------------------------ output: rows 4g + e, channel 16 tt + r
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = t * 16 + 4 * g + e;
+      const float inv = 1.0f / accz[e];
+      if (row < n) {
+        float* o = a.out + (hb + row) * kD + r;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) o[16 * tt] = acc[tt][e] * inv;
+      }
+    }
+
+  }
+}
+
+template <int NK, bool PAD, bool IDX>
+hipError_t launch_nk(const MfmaKArgs& ka, dim3 grid, dim3 block, uint32_t lds, hipStream_t s) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&topn_mfma_kernel<NK, PAD, IDX>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      160 * 1024 - 1024);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((topn_mfma_kernel<NK, PAD, IDX>), grid, block, lds, s, ka);
+  return hipGetLastError();
+}
+
+template <int NK>
+hipError_t launch_pad(const MfmaKArgs& ka, bool pad, dim3 grid, dim3 block, uint32_t lds, hipStream_t s) {
+  if (ka.idx != nullptr)
+    return pad ? launch_nk<NK, true, true>(ka, grid, block, lds, s) : launch_nk<NK, false, true>(ka, grid, block, lds, s);
+  return pad ? launch_nk<NK, true, false>(ka, grid, block, lds, s) : launch_nk<NK, false, false>(ka, grid, block, lds, s);
+}
+
+// Smallest t with P(Binomial(d, 1/2) <= t) >= keep / n: the expected threshold
+// for codes of independent signs, a starting guess only.
+int threshold_guess(int64_t d, int64_t keep, int64_t n) {
+  double c = 1.0, cdf = 0.0;
+  const double total = ldexp(1.0, (int)d);
+  for (int t = 0; t <= d; ++t) {
+    cdf += c / total;
+    if (cdf >= (double)keep / (double)n) return t;
+    c = c * (double)(d - t) / (double)(t + 1);
+  }
+  return (int)d;
+}
+
+}  // namespace
+
+bool topn_mfma_supported(const AttnParams& p) {
+  return p.d == kD && p.v_kind == 1 && p.alpha_q == nullptr && p.alpha_k == nullptr && p.bias == nullptr &&
+         p.n >= 1 && p.n <= 1024;
+}
+
+hipError_t launch_topn_mfma(const AttnParams& p, hipStream_t s) {
+  if (!topn_mfma_supported(p)) return hipErrorInvalidValue;
+  int NK = 2;  // 32-key steps per lane quarter step: n_pad = 32 NK (NK even)
+  while (32 * NK < p.n) NK *= 2;
+  MfmaKArgs ka{};
+  ka.qbits = p.qbits;
+  ka.kbits = p.kbits;
+  ka.v = static_cast<const uint32_t*>(p.v);
+  ka.out = p.out;
+  ka.idx = p.idx;
+  ka.n = (int)p.n;
+  ka.keep = (int)p.keep;
+  ka.tiles = (int)((p.n + 15) / 16);
+  ka.t0 = std::max(1, threshold_guess(p.d, p.keep, p.n));
+  ka.exp_c = (float)(2.0 / sqrt((double)p.d) * 1.4426950408889634);
+  const int64_t BH = p.B * p.H;
+  const uint32_t lds = (uint32_t)(kD * (32 * NK + 8) * 2);  // dynamic part: V^T
+  // workgroups of one head each; as many per head as the CUs allow
+  const int per_cu = std::max(1, std::min(4, (int)((160u * 1024u) / (lds + 1024u))));
+  int split = (int)std::max<int64_t>(1, (256 * per_cu) / BH);
+  split = min(split, ka.tiles);
+  ka.tpw = (ka.tiles + split - 1) / split;
+  ka.split = (ka.tiles + ka.tpw - 1) / ka.tpw;  // no workgroup without a tile
+  split = ka.split;
+  const dim3 grid((unsigned)(BH * split));
+  const dim3 block((unsigned)(64 * mfma_waves(NK)));
+  const bool pad = p.n != 32 * NK;
+  switch (NK) {
+    case 2: return launch_pad<2>(ka, pad, grid, block, lds, s);
+    case 4: return launch_pad<4>(ka, pad, grid, block, lds, s);
+    case 8: return launch_pad<8>(ka, pad, grid, block, lds, s);
+    case 16: return launch_pad<16>(ka, pad, grid, block, lds, s);
+    default: return launch_pad<32>(ka, pad, grid, block, lds, s);
+  }
+}
+
+}  // namespace had
