@@ -62,8 +62,7 @@ struct MfmaKArgs {
   int32_t* idx;           // [BH, n, keep] or null
   int n, keep;
   int tiles;  // 16-query tiles per head
-  int split;  // workgroups per head
-  int tpw;    // tiles per workgroup
+  int split;  // workgroups per head (four tiles each)
   int t0;     // first threshold guess
   float exp_c;  // 2 / sqrt(d) * log2(e)
 };
@@ -72,7 +71,8 @@ struct MfmaKArgs {
 // consuming VALU instruction).
 template <int S>
 HAD_DEVICE uint32_t row_bcast(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + S, 0xf, 0xf, false);
+  // every lane reads a valid source lane, so no "old" value is needed
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x150 + S, 0xf, 0xf, true);
 }
 
 template <int N>
@@ -134,47 +134,59 @@ HAD_DEVICE uint32_t bf16_rne_bits(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Waves per workgroup: enough that each thread prefetches at most four 32-byte V pieces.
-constexpr int mfma_waves(int nk) { return nk >= 32 ? 16 : (nk >= 16 ? 8 : 4); }
+// Work decomposition over the GPU: a workgroup of four waves (one per SIMD)
+// takes four consecutive tiles of one head; several workgroups share a CU.
+// V^T of the head is staged in rounds (one key subset of every quarter per
+// round), so a workgroup needs little LDS and the restaging of one workgroup
+// overlaps the work of the others on the same CU.
+constexpr int kWaves = 4;
+constexpr int mfma_rounds(int nk) { return nk >= 32 ? 4 : (nk >= 16 ? 2 : 1); }
 
 // IDX: also write the kept-index list (a separate instance, so that the common
 // kernel carries none of its code).
 template <int NK, bool PAD, bool IDX>
-__global__ __launch_bounds__(64 * mfma_waves(NK)) void topn_mfma_kernel(const MfmaKArgs a) {
-  constexpr int NWV = mfma_waves(NK);
-  constexpr int KG = 8 * NK;       // keys per lane (one quarter of the padded row)
-  constexpr int NW = 2 * NK;       // byte-packed distance words per lane
-  constexpr int NP = 32 * NK;      // padded keys
-  constexpr int VS = NP + 8;       // V^T row stride in bf16 (16 bytes of skew per channel)
+__global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs a) {
+  constexpr int R = mfma_rounds(NK);
+  constexpr int NKR = NK / R;     // 32-key MFMA steps per round
+  constexpr int KG = 8 * NK;      // keys per lane quarter
+  constexpr int KR = 8 * NKR;     // keys per quarter and round
+  constexpr int NW = 2 * NK;      // byte-packed distance words per lane
+  constexpr int VS = 4 * KR + 8;  // V^T row stride in bf16 (16 bytes of skew per channel)
   // The weight table is the kernel's only static LDS array, so its address is
   // fixed at compile time and a lookup address is just index * 4.
   __shared__ __align__(16) uint32_t tab[256];
   extern __shared__ __align__(16) uint8_t smem[];
-  uint16_t* vt = reinterpret_cast<uint16_t*>(smem);  // [64][VS]
+  uint16_t* vt = reinterpret_cast<uint16_t*>(smem);  // [64 channels][VS]: one round of V^T
 
   const int lane = (int)lane_id();
   const int g = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  constexpr int nwv = NWV;  // the launch always uses 64 * NWV threads
-  const int bh = blockIdx.x / a.split, part = blockIdx.x % a.split;
-  const int tbeg = part * a.tpw, tend = min(a.tiles, tbeg + a.tpw);
   const int n = a.n, keep = a.keep;
+  const int bh = blockIdx.x / a.split;                 // the head
+  const int t = (blockIdx.x % a.split) * kWaves + wave;  // this wave's tile
+  const bool have = t < a.tiles;                       // wave-uniform
   const size_t hb = (size_t)bh * n;
+  const int i = t * 16 + r;  // this lane's query
 
-  // ---- V of this head: loads issued now, consumed after the first tile's selection
-  constexpr int kPieces = NP / 2 * 8;  // (key pair, 8-channel block) pieces of 2 x 16 bytes
-  constexpr int kPf = kPieces / (64 * NWV);
-  static_assert(kPf * 64 * NWV == kPieces, "pieces must split evenly over the threads");
+  // ---- V^T staging.  Piece p of a round: a key pair and an 8-channel block;
+  // loads are unconditional (clamped rows) with selects, so no branch splits the
+  // code around them; padding keys stage as zeros.
+  constexpr int PS = 16 * KR;  // pieces per round
+  constexpr int kPf = PS / (64 * kWaves);
+  static_assert(kPf * 64 * kWaves == PS, "pieces must split evenly over the threads");
   uint4 pf[kPf][2];
-  {
-    const uint4* vsrc = reinterpret_cast<const uint4*>(a.v + hb * (kD / 2));
+  const uint4* vsrc = reinterpret_cast<const uint4*>(a.v + hb * (kD / 2));
+  auto piece = [&](int p, int rr, int* cb, int* lk) {
+    const int q = threadIdx.x + p * 64 * kWaves;
+    *cb = q & 7;
+    *lk = 2 * (q >> 3);  // local key column: quarter lk / KR, key lk % KR of the round
+    return (*lk / KR) * KG + rr * KR + (*lk % KR);
+  };
+  auto load_round = [&](int rr) {
 #pragma unroll
     for (int p = 0; p < kPf; ++p) {
-      const int piece = threadIdx.x + p * 64 * NWV;
-      const int jp = piece >> 3, cb = piece & 7;
-      const int j0 = 2 * jp, j1 = 2 * jp + 1;
-      // unconditional loads (clamped rows) and selects keep this free of branches;
-      // padding keys stage as zeros
+      int cb, lk;
+      const int j0 = piece(p, rr, &cb, &lk), j1 = j0 + 1;
       pf[p][0] = vsrc[(size_t)(PAD ? min(j0, n - 1) : j0) * 8 + cb];
       pf[p][1] = vsrc[(size_t)(PAD ? min(j1, n - 1) : j1) * 8 + cb];
       if (PAD) {
@@ -183,15 +195,14 @@ __global__ __launch_bounds__(64 * mfma_waves(NK)) void topn_mfma_kernel(const Mf
         pf[p][1] = make_uint4(z1 ? 0u : pf[p][1].x, z1 ? 0u : pf[p][1].y, z1 ? 0u : pf[p][1].z, z1 ? 0u : pf[p][1].w);
       }
     }
-  }
-
-  // one prefetched piece -> V^T in LDS: channels 8cb..8cb+7 of keys 2jp, 2jp + 1
+  };
+  // prefetched piece p -> V^T: channels 8cb..8cb+7 of local keys lk, lk + 1
   auto stage_piece = [&](int p) {
-    const int piece = threadIdx.x + p * 64 * NWV;
-    const int jp = piece >> 3, cb = piece & 7;
+    int cb, lk;
+    (void)piece(p, 0, &cb, &lk);
     const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&pf[p][0]);
     const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&pf[p][1]);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(vt + (size_t)(8 * cb) * VS + 2 * jp);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(vt + (size_t)(8 * cb) * VS + lk);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       // channel 2e (low halves) and 2e + 1 (high halves) of the two keys
@@ -200,30 +211,29 @@ __global__ __launch_bounds__(64 * mfma_waves(NK)) void topn_mfma_kernel(const Mf
     }
   };
   constexpr int kSteps = KG / 16;  // Hamming steps of 16 keys per lane row
-  constexpr int kStageAt = kSteps > kPf ? kSteps - kPf : 0;  // step that writes piece 0
 
-  int tq = a.t0;  // per-lane threshold guess, carried from tile to tile
+  load_round(0);
+
   uint32_t P[NW];
   int tau = 0, less = 0, cl_lo = 0, cl_hi = 0;
-
-  // Steps 1-2 for tile t: distances into P, then tau, the query's count below tau
-  // (less) and this lane's counts at tau - 1 and tau.  STAGE: also move the
-  // prefetched V pieces into LDS, one per Hamming step near the end.
-  auto select = [&](int t, auto stage_tag) {
-    constexpr bool STAGE = decltype(stage_tag)::value;
-    const int i = t * 16 + r;
+  if (have) {
     // ------------------------------------------------ 1. Hamming distances
-    const uint2 q = i < n ? reinterpret_cast<const uint2*>(a.qbits)[hb + i] : make_uint2(0u, 0u);
+    // (an unconditional load: a branch here would separate the DPP reads below from
+    // their XORs; rows past n only feed outputs that are never stored)
+    const uint2 q = reinterpret_cast<const uint2*>(a.qbits)[hb + min(i, n - 1)];
     const uint2* kb = reinterpret_cast<const uint2*>(a.kbits) + hb;
     auto kload = [&](int m) {
       const int j = g * KG + 16 * m + r;  // the key this lane loads for its row
       return kb[PAD ? min(j, n - 1) : j];  // padding keys: any code (their bytes are overwritten)
     };
-    uint2 kc = kload(0);
+    // key codes three steps ahead; V pieces of round 0 stored over the last steps
+    uint2 kq[4];
+#pragma unroll
+    for (int m = 0; m < 3 && m < kSteps; ++m) kq[m] = kload(m);
 #pragma unroll
     for (int m = 0; m < kSteps; ++m) {
-      const uint2 kcur = kc;
-      if (m + 1 < kSteps) kc = kload(m + 1);
+      const uint2 kcur = kq[m & 3];
+      if (m + 3 < kSteps) kq[(m + 3) & 3] = kload(m + 3);
       uint32_t hv[16];
       Seq<16>::run([&](auto s) {
         constexpr int S = decltype(s)::value;
@@ -242,27 +252,28 @@ __global__ __launch_bounds__(64 * mfma_waves(NK)) void topn_mfma_kernel(const Mf
         }
         P[4 * m + w] = word;
       }
-      if (STAGE && m >= kStageAt && m - kStageAt < kPf) stage_piece(m - kStageAt);
-      __builtin_amdgcn_sched_barrier(0);
+      // (with fewer steps than pieces, every piece is stored after the loop)
+      if (kSteps >= kPf && m >= kSteps - kPf) stage_piece(m - (kSteps - kPf));
+      __builtin_amdgcn_sched_barrier(0);  // (no branch may enter this loop: the DPP reads must fold)
     }
-    if (STAGE)
 #pragma unroll
-      for (int p = kSteps - kStageAt; p < kPf; ++p) stage_piece(p);
+    for (int p = kSteps >= kPf ? kPf : 0; p < kPf; ++p) stage_piece(p);
+
     // ------------------------------------------------ 2. threshold
     // Invariant once bracketed: C(lo) < keep <= C(hi), C(t) = #{h <= t} over the
-    // query's keys; cl_lo / cl_hi are this lane's share of C(lo) / C(hi).
-    // (written as selects: conditional stores to different variables would be
-    // merged into a store through a selected address, which forces them to memory)
+    // query's keys; llo / lhi are this lane's share of C(lo) / C(hi).  (Written
+    // as selects: conditional stores to different variables would be merged into
+    // a store through a selected address, which forces them to memory.)
+    const int tq = a.t0;
     int lo, hi, clo, llo, lhi;
     {
       const int2 cc = lane_count_le2<NW>(P, tq);
       const int both = quad_rows_sum((cc.y << 16) | cc.x);
       const int ta = both & 0xffff, tb = both >> 16;
-      const bool below = ta >= keep;            // tau < tq - 1 ... tau <= tq - 1
-      const bool at = !below && tb >= keep;     // tau == tq
-      // below: (lo, hi) = (-1, tq - 1); at: (tq - 1, tq); above: (tq, 65)
+      const bool below = ta >= keep;         // tau <= tq - 1
+      const bool at = !below && tb >= keep;  // tau == tq
       lo = below ? -1 : (at ? tq - 1 : tq);
-      hi = below ? tq - 1 : (at ? tq : 65);     // C(65) = n >= keep: a placeholder bound
+      hi = below ? tq - 1 : (at ? tq : 65);  // C(65) = n >= keep: a placeholder bound
       clo = below ? 0 : (at ? ta : tb);
       llo = below ? 0 : (at ? cc.x : cc.y);
       lhi = below ? cc.x : (at ? cc.y : 0);
@@ -274,30 +285,24 @@ __global__ __launch_bounds__(64 * mfma_waves(NK)) void topn_mfma_kernel(const Mf
       mid = open ? mid : hi;  // settled lanes re-count harmlessly
       const int cm = lane_count_le<NW>(P, mid);
       const int tm = quad_rows_sum(cm);
-      const bool up = open && tm >= keep;   // mid becomes the upper bound
-      const bool dn = open && tm < keep;    // mid becomes the lower bound
+      const bool up = open && tm >= keep;  // mid becomes the upper bound
+      const bool dn = open && tm < keep;   // mid becomes the lower bound
       hi = up ? mid : hi;
       lhi = up ? cm : lhi;
       lo = dn ? mid : lo;
       clo = dn ? tm : clo;
       llo = dn ? cm : llo;
     }
-    cl_lo = llo;
-    cl_hi = lhi;
     tau = hi;
     less = clo;
-    tq = max(tau, 1);
-  };
-
-  const int tfirst = tbeg + wave;
-  if (tfirst < tend) {
-    select(tfirst, std::true_type{});
+    cl_lo = llo;
+    cl_hi = lhi;
   } else {
 #pragma unroll
     for (int p = 0; p < kPf; ++p) stage_piece(p);
   }
-  // ---- the weight table; then every wave's V^T pieces are in place
-  for (int e = threadIdx.x; e < 256; e += 64 * NWV) {
+  // ---- the weight table; then every wave's round-0 pieces are in place
+  for (int e = threadIdx.x; e < 256; e += 64 * kWaves) {
     uint32_t ent = 0u;
     if (e >= 1 && e <= 65) {
       const float w = exp2f((float)(65 - e) * a.exp_c);  // w(tau - h), h = e + tau - 65
@@ -309,101 +314,111 @@ __global__ __launch_bounds__(64 * mfma_waves(NK)) void topn_mfma_kernel(const Mf
   }
   __syncthreads();
 
-  for (int t = tfirst; t < tend; t += nwv) {
-    if (t != tfirst) select(t, std::false_type{});
-    const int i = t * 16 + r;  // this lane's query
-    // ------------------------------------------------ 3. ties
-    const int ceq = cl_hi - cl_lo;                 // this lane's keys at tau
-    const int before = quad_rows_excl(ceq, g);     // keys at tau in lower quarters
-    const int take = min(max(keep - less - before, 0), ceq);
-    const uint32_t kidx = (uint32_t)(65 - tau) * kC;
+  // ------------------------------------------------ 3. ties
+  const int ceq = cl_hi - cl_lo;              // this lane's keys at tau
+  const int before = quad_rows_excl(ceq, g);  // keys at tau in lower quarters
+  const int take = min(max(keep - less - before, 0), ceq);
+  const uint32_t kidx = (uint32_t)(65 - tau) * kC;
 
-    // ------------------------------------------------ 4-5. weights and A*V
-    f32x4 acc[4], accz;
+  // ------------------------------------------------ 4-5. weights and A*V
+  f32x4 acc[4], accz;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accz = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 ones;
+  for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  accz = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 ones;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
-    const uint16_t* vrow = vt + (size_t)r * VS + g * KG;
-    int run = 0;  // keys at tau met so far in this lane (ascending j)
-    // optional kept-index list: this lane's keys follow those of the lower quarters
-    int32_t* idst = nullptr;
-    int ipos = 0;
-    if (IDX) {
-      ipos = quad_rows_excl(cl_lo + take, g);
-      idst = a.idx + (hb + (i < n ? i : 0)) * (size_t)keep;
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+  const uint16_t* vrow = vt + (size_t)r * VS + g * KR;
+  int run = 0;  // keys at tau met so far in this lane (ascending j)
+  // optional kept-index list: this lane's keys follow those of the lower quarters
+  int32_t* idst = nullptr;
+  int ipos = 0;
+  if (IDX) {
+    ipos = quad_rows_excl(cl_lo + take, g);
+    idst = a.idx + (hb + (i < n ? i : 0)) * (size_t)keep;
+  }
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    if (rr > 0) {
+      __syncthreads();  // every wave is done with the previous round's V^T
+      load_round(rr);
+#pragma unroll
+      for (int p = 0; p < kPf; ++p) stage_piece(p);
+      __syncthreads();
     }
+    if (have) {
 #pragma unroll
-    for (int c = 0; c < NK; ++c) {
-      uint32_t I0 = P[2 * c] + kidx, I1 = P[2 * c + 1] + kidx;  // h - tau + 65 per byte
-      const uint32_t E0 = ((I0 + 63u * kC) ^ (I0 + 62u * kC)) & kM;  // h == tau
-      const uint32_t E1 = ((I1 + 63u * kC) ^ (I1 + 62u * kC)) & kM;
-      const int run1 = __builtin_popcount(E1) + (__builtin_popcount(E0) + run);
-      uint32_t U0 = run1 <= take ? 0u : E0, U1 = run1 <= take ? 0u : E1;  // keys at tau not taken
-      const bool part = run < take && run1 > take;
-      if (__builtin_amdgcn_ballot_w64(part) != 0 && part) {
-        // keep the first take - run keys at tau of this step (bytes of E0, then E1)
-        const uint32_t rem = (uint32_t)(take - run);
-        const uint32_t x0 = E0 >> 7, x1 = E1 >> 7;
-        const uint32_t p0 = x0 + (x0 << 8) + (x0 << 16) + (x0 << 24);  // inclusive ranks
-        const uint32_t p1 = x1 + (x1 << 8) + (x1 << 16) + (x1 << 24) + (uint32_t)__builtin_popcount(E0) * kC;
-        const uint32_t ad = (127u - rem) * kC;  // bit 7: rank >= rem + 1
-        U0 = E0 & (p0 + ad);
-        U1 = E1 & (p1 + ad);
-      }
-      run = run1;
-      I0 |= U0;
-      I1 |= U1;
-      if (IDX && i < n) {
-        // kept keys have a table index in [1, 65]
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          const uint32_t ib = ((b < 4 ? I0 : I1) >> (8 * (b & 3))) & 0xffu;
-          if (ib <= 65u) idst[ipos++] = g * KG + 8 * c + b;
+      for (int cl = 0; cl < NKR; ++cl) {
+        const int c = rr * NKR + cl;  // step over the lane's keys g KG + 8c + 0..7
+        uint32_t I0 = P[2 * c] + kidx, I1 = P[2 * c + 1] + kidx;  // h - tau + 65 per byte
+        const uint32_t E0 = ((I0 + 63u * kC) ^ (I0 + 62u * kC)) & kM;  // h == tau
+        const uint32_t E1 = ((I1 + 63u * kC) ^ (I1 + 62u * kC)) & kM;
+        const int run1 = __builtin_popcount(E1) + (__builtin_popcount(E0) + run);
+        uint32_t U0 = run1 <= take ? 0u : E0, U1 = run1 <= take ? 0u : E1;  // keys at tau not taken
+        const bool part = run < take && run1 > take;
+        if (__builtin_amdgcn_ballot_w64(part) != 0 && part) {
+          // keep the first take - run keys at tau of this step (bytes of E0, then E1)
+          const uint32_t rem = (uint32_t)(take - run);
+          const uint32_t x0 = E0 >> 7, x1 = E1 >> 7;
+          const uint32_t p0 = x0 + (x0 << 8) + (x0 << 16) + (x0 << 24);  // inclusive ranks
+          const uint32_t p1 = x1 + (x1 << 8) + (x1 << 16) + (x1 << 24) + (uint32_t)__builtin_popcount(E0) * kC;
+          const uint32_t ad = (127u - rem) * kC;  // bit 7: rank >= rem + 1
+          U0 = E0 & (p0 + ad);
+          U1 = E1 & (p1 + ad);
         }
+        run = run1;
+        I0 |= U0;
+        I1 |= U1;
+        if (IDX && i < n) {
+          // kept keys have a table index in [1, 65]
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            const uint32_t ib = ((b < 4 ? I0 : I1) >> (8 * (b & 3))) & 0xffu;
+            if (ib <= 65u) idst[ipos++] = g * KG + 8 * c + b;
+          }
+        }
+        // table entries (hi | lo << 16) of the eight keys, then hi and lo operands
+        uint32_t ent[8];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          ent[b] = tab[(I0 >> (8 * b)) & 0xffu];
+          ent[4 + b] = tab[(I1 >> (8 * b)) & 0xffu];
+        }
+        uint32_t ah[4], al[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ah[e] = __builtin_amdgcn_perm(ent[2 * e + 1], ent[2 * e], 0x05040100u);
+          al[e] = __builtin_amdgcn_perm(ent[2 * e + 1], ent[2 * e], 0x07060302u);
+        }
+        const bf16x8 A_hi = __builtin_bit_cast(bf16x8, make_uint4(ah[0], ah[1], ah[2], ah[3]));
+        const bf16x8 A_lo = __builtin_bit_cast(bf16x8, make_uint4(al[0], al[1], al[2], al[3]));
+        bf16x8 Bv[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          Bv[tt] = *reinterpret_cast<const bf16x8*>(vrow + (size_t)(16 * tt) * VS + 8 * cl);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, Bv[tt], acc[tt], 0, 0, 0);
+        accz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, ones, accz, 0, 0, 0);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, Bv[tt], acc[tt], 0, 0, 0);
+        accz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, ones, accz, 0, 0, 0);
       }
-      // table entries (hi | lo << 16) of the eight keys, then hi and lo operands
-      uint32_t ent[8];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        ent[b] = tab[(I0 >> (8 * b)) & 0xffu];
-        ent[4 + b] = tab[(I1 >> (8 * b)) & 0xffu];
-      }
-      uint32_t ah[4], al[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ah[e] = __builtin_amdgcn_perm(ent[2 * e + 1], ent[2 * e], 0x05040100u);
-        al[e] = __builtin_amdgcn_perm(ent[2 * e + 1], ent[2 * e], 0x07060302u);
-      }
-      const bf16x8 A_hi = __builtin_bit_cast(bf16x8, make_uint4(ah[0], ah[1], ah[2], ah[3]));
-      const bf16x8 A_lo = __builtin_bit_cast(bf16x8, make_uint4(al[0], al[1], al[2], al[3]));
-      bf16x8 Bv[4];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-        Bv[tt] = *reinterpret_cast<const bf16x8*>(vrow + (size_t)(16 * tt) * VS + 8 * c);
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, Bv[tt], acc[tt], 0, 0, 0);
-      accz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, ones, accz, 0, 0, 0);
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, Bv[tt], acc[tt], 0, 0, 0);
-      accz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, ones, accz, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
     }
+  }
+  if (!have) return;
 
-    // ------------------------------------------------ output: rows 4g + e, channel 16 tt + r
+  // ------------------------------------------------ output: rows 4g + e, channel 16 tt + r
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = t * 16 + 4 * g + e;
-      const float inv = 1.0f / accz[e];
-      if (row < n) {
-        float* o = a.out + (hb + row) * kD + r;
+  for (int e = 0; e < 4; ++e) {
+    const int row = t * 16 + 4 * g + e;
+    const float inv = 1.0f / accz[e];
+    if (row < n) {
+      float* o = a.out + (hb + row) * kD + r;
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) o[16 * tt] = acc[tt][e] * inv;
-      }
+      for (int tt = 0; tt < 4; ++tt) o[16 * tt] = acc[tt][e] * inv;
     }
-
   }
 }
 
@@ -460,16 +475,11 @@ hipError_t launch_topn_mfma(const AttnParams& p, hipStream_t s) {
   ka.t0 = std::max(1, threshold_guess(p.d, p.keep, p.n));
   ka.exp_c = (float)(2.0 / sqrt((double)p.d) * 1.4426950408889634);
   const int64_t BH = p.B * p.H;
-  const uint32_t lds = (uint32_t)(kD * (32 * NK + 8) * 2);  // dynamic part: V^T
-  // workgroups of one head each; as many per head as the CUs allow
-  const int per_cu = std::max(1, std::min(4, (int)((160u * 1024u) / (lds + 1024u))));
-  int split = (int)std::max<int64_t>(1, (256 * per_cu) / BH);
-  split = min(split, ka.tiles);
-  ka.tpw = (ka.tiles + split - 1) / split;
-  ka.split = (ka.tiles + ka.tpw - 1) / ka.tpw;  // no workgroup without a tile
-  split = ka.split;
-  const dim3 grid((unsigned)(BH * split));
-  const dim3 block((unsigned)(64 * mfma_waves(NK)));
+  const uint32_t lds = (uint32_t)(kD * (32 * NK / mfma_rounds(NK) + 8) * 2);  // dynamic part: one V^T round
+  ka.split = (ka.tiles + kWaves - 1) / kWaves;
+  if (BH * ka.split >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(BH * ka.split));
+  const dim3 block((unsigned)(64 * kWaves));
   const bool pad = p.n != 32 * NK;
   switch (NK) {
     case 2: return launch_pad<2>(ka, pad, grid, block, lds, s);
