@@ -70,17 +70,32 @@ def algorithmic_bytes(w) -> float:
     return b * bh
 
 
-def traffic_from_profile(kernel_src: str):
+def attention_kernel(w):
+    """(kernel name, source file) of the attention launch, by the library's dispatch rule:
+    dense softmax -> dense_q8; n above the resident limit (512 keys for fp32 V, 1024
+    otherwise) -> the streaming kernel; bf16 V with integer logits (plain sign, no
+    bias) and fp32 A*V -> the matrix-core kernel; anything else -> the resident kernel."""
+    if w.top_n is None:
+        return "dense_q8_kernel", "dense_q8.hip"
+    resident_max = 512 if (w.dtype == "f32" and w.av_mode == 0) else 1024
+    if w.n > resident_max:
+        return "topn_stream_kernel", "topn_stream.hip"
+    if w.dtype == "bf16" and w.mode == 0 and not w.bias and w.av_mode == 0:
+        return "topn_mfma_kernel", "topn_mfma.hip"
+    return "topn_resident_kernel", "topn.hip"
+
+
+def traffic_from_profile(config: str, kernel: str, kernel_src: str):
     """HBM bytes per launch from the committed rocprof counter summary, if it was
-    taken on the current kernel source; otherwise None."""
-    path = os.path.join(ROOT, "profiles", "topn_c3_n1024_traffic.json")
+    taken on this workload with the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"{config.replace('@', '_n')}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     with open(kernel_src, "rb") as f:
         h = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("kernel_sha256") != h:
+    if rec.get("kernel_sha256") != h or not rec.get("kernel", "").startswith(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -236,8 +251,9 @@ def main():
 
     slots = algorithmic_slots(w)
     achieved = slots / t_att
-    src = os.path.join(ROOT, "binarized_qk_sparse_amd", "csrc", "dense_q8.hip" if w.top_n is None else "topn.hip")
-    traffic = traffic_from_profile(src) if args.config == "c3@1024" else None
+    kname, ksrc = attention_kernel(w)
+    src = os.path.join(ROOT, "binarized_qk_sparse_amd", "csrc", ksrc)
+    traffic = traffic_from_profile(args.config, kname, src)
     roof = {
         "bound": "alu",
         "achieved": achieved / 1e12,
@@ -245,7 +261,7 @@ def main():
         "unit": "Tlane-slot/s",
         "frac": achieved / VALU_PEAK,
         "traffic": traffic,
-        "kernel": "topn_resident_kernel" if w.top_n is not None else "dense_q8_kernel",
+        "kernel": kname,
         "kernel_us": t_att * 1e6,
         "slots_per_launch": slots,
         "hbm_bytes_per_launch_alg": algorithmic_bytes(w),

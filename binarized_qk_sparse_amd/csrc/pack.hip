@@ -10,6 +10,8 @@
 // read once (twice for the mean pass) and d/8 bytes (+4 for alpha) are
 // written per token.  Loads are 16-byte vectors, eight channels per lane and
 // d/8 consecutive lanes per token row, so a wave reads whole rows.
+#include <algorithm>
+
 #include "had_device.hpp"
 #include "had_internal.h"
 #include "../../include/had.h"
@@ -84,78 +86,78 @@ __global__ __launch_bounds__(kThreads) void mu_final_kernel(const double* __rest
   mu[id] = (float)(s / (double)n);
 }
 
-// One token row per D/8 lanes: code bits, and alpha for MEAN_SIGN.
+// 32 channels (one code word) per lane, D/32 lanes per token row: the word
+// needs no lane exchange, and a wave reads 64 consecutive 32-channel runs.
+// MEAN_SIGN subtracts mu and sums |x - mu| in float64 for alpha (the D/32 lanes
+// of a row add their partial sums).  Plain SIGN also writes mu = 0 when asked
+// (mu_zero, BH*D floats), so no separate fill launch is needed.
 template <typename T, int D, bool MEAN>
-__global__ __launch_bounds__(kThreads) void pack_rows_kernel(const T* __restrict__ x, int64_t rows,
-                                                             int64_t n, const float* __restrict__ mu,
+__global__ __launch_bounds__(kThreads) void pack_rows_kernel(const T* __restrict__ x, uint32_t rows, uint32_t n,
+                                                             const float* __restrict__ mu,
                                                              uint32_t* __restrict__ bits,
-                                                             float* __restrict__ alpha) {
-  constexpr int TPR = D / 8;
-  constexpr int RPP = kThreads / TPR;
-  constexpr int W = D / 32;
-  const int t = threadIdx.x;
-  const int cg = t % TPR;
-  const int64_t r = (int64_t)blockIdx.x * RPP + t / TPR;
+                                                             float* __restrict__ alpha,
+                                                             float* __restrict__ mu_zero, uint32_t mu_count) {
+  constexpr int LPR = D / 32;
+  const uint32_t tid = blockIdx.x * kThreads + threadIdx.x;
+  if (!MEAN && mu_zero != nullptr && tid < mu_count) mu_zero[tid] = 0.0f;
+  const uint32_t r = tid / LPR, part = tid % LPR;
   const bool live = r < rows;
-  float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (live) load8<T>(x + r * D + 8 * cg, v);
-  if (MEAN && live) {
-    const float* m = mu + (r / n) * D + 8 * cg;
-    const float4 m0 = *reinterpret_cast<const float4*>(m);
-    const float4 m1 = *reinterpret_cast<const float4*>(m + 4);
-    v[0] = __fsub_rn(v[0], m0.x); v[1] = __fsub_rn(v[1], m0.y);
-    v[2] = __fsub_rn(v[2], m0.z); v[3] = __fsub_rn(v[3], m0.w);
-    v[4] = __fsub_rn(v[4], m1.x); v[5] = __fsub_rn(v[5], m1.y);
-    v[6] = __fsub_rn(v[6], m1.z); v[7] = __fsub_rn(v[7], m1.w);
+  const uint32_t rr = live ? r : rows - 1;  // dead lanes read a valid row, write nothing
+  float v[32];
+  const T* src = x + (size_t)rr * D + 32 * part;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float e[8];
+    load8<T>(src + 8 * k, e);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[8 * k + c] = e[c];
   }
-  uint32_t b8 = 0;
   double asum = 0.0;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    b8 |= (uint32_t)(v[c] < 0.0f) << c;
-    if (MEAN) asum += fabs((double)v[c]);
-  }
-  // four lanes (32 channels) make one word
-  uint32_t w = b8 << (8 * (cg & 3));
-  w |= __shfl_xor(w, 1, 64);
-  w |= __shfl_xor(w, 2, 64);
   if (MEAN) {
+    const float* m = mu + (size_t)(rr / n) * D + 32 * part;
 #pragma unroll
-    for (int off = 1; off < TPR; off <<= 1) asum += __shfl_xor(asum, off, 64);
+    for (int k = 0; k < 8; ++k) {
+      const float4 mm = *reinterpret_cast<const float4*>(m + 4 * k);
+      v[4 * k + 0] = __fsub_rn(v[4 * k + 0], mm.x);
+      v[4 * k + 1] = __fsub_rn(v[4 * k + 1], mm.y);
+      v[4 * k + 2] = __fsub_rn(v[4 * k + 2], mm.z);
+      v[4 * k + 3] = __fsub_rn(v[4 * k + 3], mm.w);
+    }
+#pragma unroll
+    for (int c = 0; c < 32; ++c) asum += fabs((double)v[c]);
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) asum += __shfl_xor(asum, off, 64);
   }
+  uint32_t w = 0;
+#pragma unroll
+  for (int c = 0; c < 32; ++c) w |= (uint32_t)(v[c] < 0.0f) << c;
   if (!live) return;
-  if ((cg & 3) == 0) bits[r * W + cg / 4] = w;
-  if (cg == 0 && alpha != nullptr) alpha[r] = MEAN ? (float)(asum / (double)D) : 1.0f;
-}
-
-__global__ __launch_bounds__(kThreads) void fill_f32_kernel(float* __restrict__ p, int64_t count, float v) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i < count) p[i] = v;
+  bits[(size_t)r * (D / 32) + part] = w;
+  if (part == 0 && alpha != nullptr) alpha[r] = MEAN ? (float)(asum / (double)D) : 1.0f;
 }
 
 template <typename T, int D>
 hipError_t launch_typed(const PackParams& p, hipStream_t s) {
   const T* x = static_cast<const T*>(p.x);
   const int64_t rows = p.BH * p.n;
-  constexpr int RPP = kThreads / (D / 8);
-  const unsigned grid = (unsigned)((rows + RPP - 1) / RPP);
+  const int64_t threads = rows * (D / 32);
   if (p.mode == HAD_MEAN_SIGN) {
+    const unsigned grid = (unsigned)((threads + kThreads - 1) / kThreads);
     const int64_t chunks = pack_chunks(p.n);
     hipLaunchKernelGGL((colsum_partial_kernel<T, D>), dim3((unsigned)(p.BH * chunks)), dim3(kThreads), 0,
                        s, x, p.n, chunks, p.partial);
     const unsigned g2 = (unsigned)((p.BH * D + kThreads - 1) / kThreads);
     hipLaunchKernelGGL(mu_final_kernel, dim3(g2), dim3(kThreads), 0, s, p.partial, p.BH, p.n, chunks, D,
                        p.mu);
-    hipLaunchKernelGGL((pack_rows_kernel<T, D, true>), dim3(grid), dim3(kThreads), 0, s, x, rows, p.n,
-                       p.mu, p.bits, p.alpha);
+    hipLaunchKernelGGL((pack_rows_kernel<T, D, true>), dim3(grid), dim3(kThreads), 0, s, x, (uint32_t)rows,
+                       (uint32_t)p.n, p.mu, p.bits, p.alpha, nullptr, 0u);
   } else {
-    if (p.mu != nullptr) {
-      const int64_t count = p.BH * D;
-      hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)((count + kThreads - 1) / kThreads)), dim3(kThreads),
-                         0, s, p.mu, count, 0.0f);
-    }
-    hipLaunchKernelGGL((pack_rows_kernel<T, D, false>), dim3(grid), dim3(kThreads), 0, s, x, rows, p.n,
-                       nullptr, p.bits, p.alpha);
+    // the launch covers max(rows * D/32, BH * D) threads: the first BH * D also write mu = 0
+    const int64_t mu_count = p.mu != nullptr ? p.BH * D : 0;
+    const int64_t need = std::max<int64_t>(threads, mu_count);
+    const unsigned g = (unsigned)((need + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL((pack_rows_kernel<T, D, false>), dim3(g), dim3(kThreads), 0, s, x, (uint32_t)rows,
+                       (uint32_t)p.n, nullptr, p.bits, p.alpha, p.mu, (uint32_t)mu_count);
   }
   return hipGetLastError();
 }

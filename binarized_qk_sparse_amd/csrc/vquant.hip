@@ -72,29 +72,41 @@ __global__ __launch_bounds__(kThreads) void vscale_kernel(const float* __restric
   scale[id] = __fdiv_rn(m, 127.0f);
 }
 
-HAD_DEVICE uint32_t q8(float x, float s) {
+// clamp(rint(fl(x / s)), -127, 127).  x * (1/s) (v_rcp_f32 and one multiply)
+// is within 2 ulp of the correctly rounded quotient fl(x / s), i.e. within
+// 2^-16 for |x / s| <= 128, so the two can round to different integers only
+// when the quotient lies near a tie k + 1/2; there the exact division decides
+// (as it does for a denormal scale, whose reciprocal is not representable).
+HAD_DEVICE uint32_t q8(float x, float s, float inv) {
   if (!(s > 0.0f)) return 0u;
-  float r = rintf(__fdiv_rn(x, s));
+  float y = x * inv;
+  if (s < 0x1p-125f || fabsf(y - floorf(y) - 0.5f) < 0x1p-12f) y = __fdiv_rn(x, s);
+  float r = rintf(y);
   r = fminf(fmaxf(r, -127.0f), 127.0f);
   return (uint32_t)((int32_t)r) & 0xffu;
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void vq_kernel(const T* __restrict__ v, int64_t rows, int64_t n,
+__global__ __launch_bounds__(kThreads) void vq_kernel(const T* __restrict__ v, uint32_t rows, uint32_t n,
                                                       const float* __restrict__ scale, int8_t* __restrict__ vq) {
   constexpr int TPR = D / 8;
   constexpr int RPP = kThreads / TPR;
   const int t = threadIdx.x;
   const int cg = t % TPR;
-  const int64_t r = (int64_t)blockIdx.x * RPP + t / TPR;
+  const uint32_t r = blockIdx.x * RPP + t / TPR;
   if (r >= rows) return;
   float x[8];
-  load8v<T>(v + r * D + 8 * cg, x);
-  const float* s = scale + (r / n) * D + 8 * cg;
+  load8v<T>(v + (size_t)r * D + 8 * cg, x);
+  const float4* sp = reinterpret_cast<const float4*>(scale + (size_t)(r / n) * D + 8 * cg);
+  const float4 s0 = sp[0], s1 = sp[1];
+  const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  uint32_t b[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) b[c] = q8(x[c], s[c], __builtin_amdgcn_rcpf(s[c]));
   uint2 o;
-  o.x = q8(x[0], s[0]) | (q8(x[1], s[1]) << 8) | (q8(x[2], s[2]) << 16) | (q8(x[3], s[3]) << 24);
-  o.y = q8(x[4], s[4]) | (q8(x[5], s[5]) << 8) | (q8(x[6], s[6]) << 16) | (q8(x[7], s[7]) << 24);
-  *reinterpret_cast<uint2*>(vq + r * D + 8 * cg) = o;
+  o.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+  o.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+  *reinterpret_cast<uint2*>(vq + (size_t)r * D + 8 * cg) = o;
 }
 
 template <typename T, int D>
@@ -108,7 +120,7 @@ hipError_t launch_typed(const VQuantParams& p, hipStream_t s) {
   const int64_t rows = p.BH * p.n;
   constexpr int RPP = kThreads / (D / 8);
   hipLaunchKernelGGL((vq_kernel<T, D>), dim3((unsigned)((rows + RPP - 1) / RPP)), dim3(kThreads), 0, s, v,
-                     rows, p.n, p.vscale, p.vq);
+                     (uint32_t)rows, (uint32_t)p.n, p.vscale, p.vq);
   return hipGetLastError();
 }
 
