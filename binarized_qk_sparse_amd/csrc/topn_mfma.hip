@@ -162,8 +162,11 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   const int g = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = a.n, keep = a.keep;
-  const int bh = blockIdx.x / a.split;                 // the head
-  const int t = (blockIdx.x % a.split) * kWaves + wave;  // this wave's tile
+  // logical workgroup ids are XCD-major, so the workgroups of one head share an
+  // XCD's L2 (hardware workgroup w runs on XCD w % 8)
+  const int wg = (int)xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / a.split;                 // the head
+  const int t = (wg % a.split) * kWaves + wave;  // this wave's tile
   const bool have = t < a.tiles;                       // wave-uniform
   const size_t hb = (size_t)bh * n;
   const int i = t * 16 + r;  // this lane's query
