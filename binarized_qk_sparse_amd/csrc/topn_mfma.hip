@@ -105,28 +105,33 @@ HAD_DEVICE int quad_rows_excl(int v, int g) {
   return s - v;
 }
 
-// Keys of this lane with h <= t (per-lane t), four byte-packed distances per word.
+// Counts of this lane's keys with h <= t, from sums of absolute differences:
+// with S(x) = sum over the lane's keys of |h - x| (v_sad_u8, four byte-packed
+// distances per instruction), |h - (t+1)| - |h - t| is +1 for h <= t and -1
+// otherwise, so #{h <= t} = (S(t+1) - S(t) + N) / 2 for N keys.  All terms are
+// exact small integers.
 template <int NW>
-HAD_DEVICE int lane_count_le(const uint32_t (&P)[NW], int t) {
-  const uint32_t add = (uint32_t)(127 - t) * kC;  // bit 7 of b + add: b > t
-  uint32_t c = 0;
+HAD_DEVICE uint32_t lane_sad(const uint32_t (&P)[NW], uint32_t x) {
+  const uint32_t xb = x * kC;
+  uint32_t acc = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) c = __builtin_popcount((P[w] + add) & kM) + c;
-  return 4 * NW - (int)c;
+  for (int w = 0; w < NW; ++w) acc = __builtin_amdgcn_sad_u8(P[w], xb, acc);
+  return acc;
 }
 
-// Both lane_count_le(t - 1) (.x) and lane_count_le(t) (.y).
+// Keys of this lane with h <= t (per-lane t in [0, 64]).
+template <int NW>
+HAD_DEVICE int lane_count_le(const uint32_t (&P)[NW], int t) {
+  return ((int)lane_sad<NW>(P, (uint32_t)t + 1u) - (int)lane_sad<NW>(P, (uint32_t)t) + 4 * NW) >> 1;
+}
+
+// Both lane_count_le(t - 1) (.x) and lane_count_le(t) (.y), t in [1, 64].
 template <int NW>
 HAD_DEVICE int2 lane_count_le2(const uint32_t (&P)[NW], int t) {
-  const uint32_t add1 = (uint32_t)(128 - t) * kC;  // b > t - 1
-  const uint32_t add0 = (uint32_t)(127 - t) * kC;  // b > t
-  uint32_t c1 = 0, c0 = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    c1 = __builtin_popcount((P[w] + add1) & kM) + c1;
-    c0 = __builtin_popcount((P[w] + add0) & kM) + c0;
-  }
-  return make_int2(4 * NW - (int)c1, 4 * NW - (int)c0);
+  const int sm = (int)lane_sad<NW>(P, (uint32_t)t - 1u);
+  const int s0 = (int)lane_sad<NW>(P, (uint32_t)t);
+  const int sp = (int)lane_sad<NW>(P, (uint32_t)t + 1u);
+  return make_int2((s0 - sm + 4 * NW) >> 1, (sp - s0 + 4 * NW) >> 1);
 }
 
 HAD_DEVICE uint32_t bf16_rne_bits(float x) {
