@@ -3,14 +3,17 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3@1024]
 
 A step is one pass of the whole path over one batch already resident in HBM:
-pack Q, pack K (and quantize V on the q8 paths), then attention.  The step is
-captured once into a HIP graph and replayed, so the timed region holds GPU
-work only.  The line printed on stdout is the only output on stdout:
+pack Q, pack K (and quantize V on the q8 paths), then attention.  The K timed
+steps are captured into one HIP graph, replayed once untimed and then once
+inside the timed region, so that region holds GPU work only, with no host
+launch gap between steps.  The line printed on stdout is the only output on
+stdout:
 
   value         query-key pairs per second of the whole step (B*H*n^2 / time)
   roofline      the dominant kernel (attention) against the VALU issue roof:
                 algorithmic VALU lane-slots per launch / the kernel's average
-                duration (HIP events on the stream it runs on), against
+                duration (a pair of HIP events around each launch, on the
+                stream it runs on), against
                 256 CU * 64 lanes * 2.4 GHz
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
 """
@@ -218,36 +221,40 @@ def main():
     for _ in range(3):
         step()
     torch.cuda.synchronize()
+    # warm-up: W replays of a one-step graph; the timed region is ONE replay of a graph that holds
+    # exactly K steps (so no host launch gap sits between steps), after one untimed replay of it
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step()
     for _ in range(args.warmup):
         graph.replay()
+    graph_k = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_k):
+        for _ in range(args.steps):
+            step()
+    graph_k.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        graph.replay()
+    graph_k.replay()
     torch.cuda.synchronize()
     dt_s = (time.perf_counter() - t0) / args.steps
-    log(f"{w.name}: step {dt_s * 1e6:.1f} us over {args.steps} graph replays")
+    log(f"{w.name}: step {dt_s * 1e6:.1f} us ({args.steps} steps in one graph replay)")
+    del graph_k
 
-    # the dominant kernel alone: HIP events on the stream it is launched on
-    att_graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(att_graph):
+    # the dominant kernel alone: a pair of HIP events around each of R launches on the stream they
+    # run on, so each pair brackets exactly one launch (back-to-back launches in one graph overlap
+    # the tail of one with the start of the next, and separate graph replays add a launch gap)
+    R = 50
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(R)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(R)]
+    for i in range(R):
+        starts[i].record(stream)
         attend()
-    for _ in range(5):
-        att_graph.replay()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    reps = max(args.steps, 50)
-    stream = torch.cuda.current_stream()  # graph replays run on the replaying stream
-    e0.record(stream)
-    for _ in range(reps):
-        att_graph.replay()
-    e1.record(stream)
+        ends[i].record(stream)
     torch.cuda.synchronize()
-    t_att = e0.elapsed_time(e1) / 1e3 / reps
-    log(f"{w.name}: attention {t_att * 1e6:.2f} us per launch (HIP events, {reps} launches)")
+    t_att = sum(starts[i].elapsed_time(ends[i]) for i in range(R)) / 1e3 / R
+    log(f"{w.name}: attention {t_att * 1e6:.2f} us per launch (HIP events around each of {R} launches)")
 
     slots = algorithmic_slots(w)
     achieved = slots / t_att

@@ -39,6 +39,8 @@ def _flags():
         "-munsafe-fp-atomics",
         # packed fp32 VALU ops stay off: plain v_fma_f32 / v_add_f32 only
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # matrix-core results and accumulators in VGPRs: no accumulator-register copies
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wall",
         "-Wno-unused-function",
         f"-I{os.path.join(ROOT, 'include')}",
