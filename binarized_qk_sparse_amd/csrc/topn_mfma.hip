@@ -30,9 +30,11 @@
 //      not taken) into an LDS table of w split as bf16 hi + bf16 lo
 //      (hi = rne(w), lo = rne(w - hi): 16 significant bits), zero for h > tau.
 //   5. A*V: the masked weight row of the tile (16 queries x 32 keys per step)
-//      times V (exact in bf16, staged transposed in LDS), hi and lo into one
-//      fp32 accumulator; a constant all-ones operand accumulates the softmax
-//      normaliser Z in the same layout, and O = acc / Z.
+//      times V (exact in bf16), hi and lo into one fp32 accumulator; a
+//      constant all-ones operand accumulates the softmax normaliser Z in the
+//      same layout, and O = acc / Z.  V rows reach LDS by direct-to-LDS loads
+//      in their natural layout (one round of keys ahead, two buffers) and the
+//      B operands come out of LDS through transposing reads.
 // The selection is exact (bit-identical index sets); the weights carry a
 // relative error below 2^-16, far inside the fp32 output tolerance.
 #include <float.h>
@@ -52,6 +54,11 @@ constexpr int kD = 64;
 constexpr uint32_t kC = 0x01010101u;
 constexpr uint32_t kM = 0x80808080u;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) void lds_void;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct MfmaKArgs {
@@ -141,27 +148,45 @@ HAD_DEVICE uint32_t bf16_rne_bits(float x) {
 
 // Work decomposition over the GPU: a workgroup of four waves (one per SIMD)
 // takes four consecutive tiles of one head; several workgroups share a CU.
-// V^T of the head is staged in rounds (one key subset of every quarter per
-// round), so a workgroup needs little LDS and the restaging of one workgroup
-// overlaps the work of the others on the same CU.
+// V of the head passes through LDS in rounds of KR keys per quarter (4 KR
+// rows of 128 bytes), double-buffered: the rows of round r + 1 are requested
+// when round r starts, so a workgroup needs little LDS and the loads overlap
+// the work.
 constexpr int kWaves = 4;
-constexpr int mfma_rounds(int nk) { return nk >= 32 ? 4 : (nk >= 16 ? 2 : 1); }
+constexpr int round_keys(int nk) { return nk >= 4 ? 32 : 8 * nk; }  // KR
+constexpr int round_bytes(int nk) { return 4 * round_keys(nk) * 128; }
+constexpr int v_buffers(int nk) { return 8 * nk > round_keys(nk) ? 2 : 1; }
+
+// V rows in LDS.  Row lk = g KR + kk of a round buffer holds key g KG + rr KR
+// + kk (quarter g) in 128 bytes; its 32-byte channel block b (channels 16 b ..
+// 16 b + 15) sits at block position b ^ vswz(lk), vswz(lk) = (g + bit 1 of lk)
+// mod 4.  A transposing read of the B operand then touches every bank equally
+// (each group of 16 lanes reads rows g KR + 8c + e0 + 0..3 of one block), and
+// the direct-to-LDS loads write whole rows in order.
+HAD_DEVICE uint32_t vswz(uint32_t g, uint32_t lk) { return (g + ((lk >> 1) & 1u)) & 3u; }
+
+// s_waitcnt with vmcnt(0) only (expcnt and lgkmcnt left at their maxima)
+HAD_DEVICE void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 // IDX: also write the kept-index list (a separate instance, so that the common
 // kernel carries none of its code).
 template <int NK, bool PAD, bool IDX>
 __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs a) {
-  constexpr int R = mfma_rounds(NK);
-  constexpr int NKR = NK / R;     // 32-key MFMA steps per round
-  constexpr int KG = 8 * NK;      // keys per lane quarter
-  constexpr int KR = 8 * NKR;     // keys per quarter and round
-  constexpr int NW = 2 * NK;      // byte-packed distance words per lane
-  constexpr int VS = 4 * KR + 8;  // V^T row stride in bf16 (16 bytes of skew per channel)
-  // The weight table is the kernel's only static LDS array, so its address is
-  // fixed at compile time and a lookup address is just index * 4.
+  constexpr int KG = 8 * NK;            // keys per lane quarter
+  constexpr int KR = round_keys(NK);    // keys per quarter and round
+  constexpr int R = KG / KR;            // rounds
+  constexpr int NKR = KR / 8;           // 32-key MFMA steps per round
+  constexpr int NW = 2 * NK;            // byte-packed distance words per lane
+  constexpr int RB = round_bytes(NK);   // bytes of one round buffer
+  static_assert(R * KR == KG && KR % 8 == 0, "rounds must tile the quarter");
+  // The weight table is a static LDS array, so its address is fixed at compile
+  // time and a lookup address is index * 4 plus an immediate offset.
   __shared__ __align__(16) uint32_t tab[256];
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint16_t* vt = reinterpret_cast<uint16_t*>(smem);  // [64 channels][VS]: one round of V^T
+  // the V row buffers, as separate arrays so that the compiler can tell the round being
+  // read from the round being loaded
+  __shared__ __align__(16) uint8_t vbuf0[RB];
+  __shared__ __align__(16) uint8_t vbuf1[v_buffers(NK) > 1 ? RB : 16];
+  auto vbuf = [&](int rr) { return (lds_u8*)((rr & 1) ? vbuf1 : vbuf0); };
 
   const int lane = (int)lane_id();
   const int g = lane >> 4, r = lane & 15;
@@ -176,51 +201,32 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   const size_t hb = (size_t)bh * n;
   const int i = t * 16 + r;  // this lane's query
 
-  // ---- V^T staging.  Piece p of a round: a key pair and an 8-channel block;
-  // loads are unconditional (clamped rows) with selects, so no branch splits the
-  // code around them; padding keys stage as zeros.
-  constexpr int PS = 16 * KR;  // pieces per round
-  constexpr int kPf = PS / (64 * kWaves);
-  static_assert(kPf * 64 * kWaves == PS, "pieces must split evenly over the threads");
-  uint4 pf[kPf][2];
-  const uint4* vsrc = reinterpret_cast<const uint4*>(a.v + hb * (kD / 2));
-  auto piece = [&](int p, int rr, int* cb, int* lk) {
-    const int q = threadIdx.x + p * 64 * kWaves;
-    *cb = q & 7;
-    *lk = 2 * (q >> 3);  // local key column: quarter lk / KR, key lk % KR of the round
-    return (*lk / KR) * KG + rr * KR + (*lk % KR);
-  };
-  auto load_round = [&](int rr) {
+  // ---- V rows into LDS.  Wave w loads the KR rows of quarter w of a round, eight
+  // rows per instruction (lane l: row 8 m + l / 8, 16-byte piece l % 8, i.e. block
+  // (l % 8) / 2 ^ vswz, half l % 2).  Padding keys load row n - 1: their weights are 0.
+  const uint16_t* vh = reinterpret_cast<const uint16_t*>(a.v) + hb * kD;
+  const uint32_t lrow = (uint32_t)lane >> 3;
+  const uint32_t piece = (uint32_t)lane & 7u;
+  const uint32_t vcol = 16u * (((piece >> 1) ^ vswz((uint32_t)wave, lrow))) + 8u * (piece & 1u);
+  auto issue_round = [&](int rr) {
+    lds_u8* buf = vbuf(rr) + wave * KR * 128;
 #pragma unroll
-    for (int p = 0; p < kPf; ++p) {
-      int cb, lk;
-      const int j0 = piece(p, rr, &cb, &lk), j1 = j0 + 1;
-      pf[p][0] = vsrc[(size_t)(PAD ? min(j0, n - 1) : j0) * 8 + cb];
-      pf[p][1] = vsrc[(size_t)(PAD ? min(j1, n - 1) : j1) * 8 + cb];
-      if (PAD) {
-        const bool z0 = j0 >= n, z1 = j1 >= n;
-        pf[p][0] = make_uint4(z0 ? 0u : pf[p][0].x, z0 ? 0u : pf[p][0].y, z0 ? 0u : pf[p][0].z, z0 ? 0u : pf[p][0].w);
-        pf[p][1] = make_uint4(z1 ? 0u : pf[p][1].x, z1 ? 0u : pf[p][1].y, z1 ? 0u : pf[p][1].z, z1 ? 0u : pf[p][1].w);
-      }
-    }
-  };
-  // prefetched piece p -> V^T: channels 8cb..8cb+7 of local keys lk, lk + 1
-  auto stage_piece = [&](int p) {
-    int cb, lk;
-    (void)piece(p, 0, &cb, &lk);
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&pf[p][0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&pf[p][1]);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(vt + (size_t)(8 * cb) * VS + lk);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      // channel 2e (low halves) and 2e + 1 (high halves) of the two keys
-      dst[(2 * e) * (VS / 2)] = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
-      dst[(2 * e + 1) * (VS / 2)] = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
+    for (int m = 0; m < KR / 8; ++m) {
+      int key = wave * KG + rr * KR + 8 * m + (int)lrow;
+      if (PAD) key = min(key, n - 1);
+      __builtin_amdgcn_global_load_lds(vh + (size_t)key * kD + vcol,
+                                       (lds_void*)(buf + m * 1024), 16, 0, 0);
     }
   };
   constexpr int kSteps = KG / 16;  // Hamming steps of 16 keys per lane row
 
-  load_round(0);
+  // The V rows of rounds 0 and 1 are requested once the key codes have arrived: a
+  // function with direct-to-LDS loads gets only full waits (vmcnt(0)) for its other
+  // vector loads, so any load still in flight at such a wait would stall on them.
+  auto issue_first = [&]() {
+    issue_round(0);
+    if (R > 1) issue_round(1);
+  };
 
   uint32_t P[NW];
   int tau = 0, less = 0, cl_lo = 0, cl_hi = 0;
@@ -234,14 +240,15 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
       const int j = g * KG + 16 * m + r;  // the key this lane loads for its row
       return kb[PAD ? min(j, n - 1) : j];  // padding keys: any code (their bytes are overwritten)
     };
-    // key codes three steps ahead; V pieces of round 0 stored over the last steps
-    uint2 kq[4];
+    // every key code of the lane up front (they take the registers that the packed
+    // distances fill later, so the peak does not grow)
+    uint2 kq[kSteps];
 #pragma unroll
-    for (int m = 0; m < 3 && m < kSteps; ++m) kq[m] = kload(m);
+    for (int m = 0; m < kSteps; ++m) kq[m] = kload(m);
 #pragma unroll
     for (int m = 0; m < kSteps; ++m) {
-      const uint2 kcur = kq[m & 3];
-      if (m + 3 < kSteps) kq[(m + 3) & 3] = kload(m + 3);
+      const uint2 kcur = kq[m];
+      if (m == 1) issue_first();  // (step 0, in its own scheduling region, waited for the codes)
       uint32_t hv[16];
       Seq<16>::run([&](auto s) {
         constexpr int S = decltype(s)::value;
@@ -260,12 +267,9 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
         }
         P[4 * m + w] = word;
       }
-      // (with fewer steps than pieces, every piece is stored after the loop)
-      if (kSteps >= kPf && m >= kSteps - kPf) stage_piece(m - (kSteps - kPf));
       __builtin_amdgcn_sched_barrier(0);  // (no branch may enter this loop: the DPP reads must fold)
     }
-#pragma unroll
-    for (int p = kSteps >= kPf ? kPf : 0; p < kPf; ++p) stage_piece(p);
+    if (kSteps == 1) issue_first();
 
     // ------------------------------------------------ 2. threshold
     // Invariant once bracketed: C(lo) < keep <= C(hi), C(t) = #{h <= t} over the
@@ -306,10 +310,9 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
     cl_lo = llo;
     cl_hi = lhi;
   } else {
-#pragma unroll
-    for (int p = 0; p < kPf; ++p) stage_piece(p);
+    issue_first();
   }
-  // ---- the weight table; then every wave's round-0 pieces are in place
+  // ---- the weight table; then the rows of round 0 (and 1) are in place
   for (int e = threadIdx.x; e < 256; e += 64 * kWaves) {
     uint32_t ent = 0u;
     if (e >= 1 && e <= 65) {
@@ -320,6 +323,7 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
     }
     tab[e] = ent;
   }
+  wait_vmem();  // this wave's direct-to-LDS loads
   __syncthreads();
 
   // ------------------------------------------------ 3. ties
@@ -336,7 +340,14 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
-  const uint16_t* vrow = vt + (size_t)r * VS + g * KR;
+  // B operand of channel tile tt by two transposing reads: in each group of 16 lanes
+  // (K group g), lane s points at row g KR + s / 4 (+ 8c + e0) and channels
+  // 16 tt + 4 (s % 4) .. + 3; lane s then receives channel 16 tt + s of keys e0 .. e0 + 3
+  const uint32_t vrow0 = (uint32_t)(g * KR + (r >> 2));
+  const uint32_t vsw = vswz((uint32_t)g, vrow0);
+  uint32_t voff[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) voff[tt] = vrow0 * 128u + 32u * ((uint32_t)tt ^ vsw) + 8u * (uint32_t)(r & 3);
   int run = 0;  // keys at tau met so far in this lane (ascending j)
   // optional kept-index list: this lane's keys follow those of the lower quarters
   int32_t* idst = nullptr;
@@ -348,11 +359,10 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
     if (rr > 0) {
-      __syncthreads();  // every wave is done with the previous round's V^T
-      load_round(rr);
-#pragma unroll
-      for (int p = 0; p < kPf; ++p) stage_piece(p);
+      // round rr's rows have landed, and every wave is done with buffer (rr + 1) & 1
+      wait_vmem();
       __syncthreads();
+      if (rr + 1 < R) issue_round(rr + 1);
     }
     if (have) {
 #pragma unroll
@@ -402,8 +412,12 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
         const bf16x8 A_lo = __builtin_bit_cast(bf16x8, make_uint4(al[0], al[1], al[2], al[3]));
         bf16x8 Bv[4];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-          Bv[tt] = *reinterpret_cast<const bf16x8*>(vrow + (size_t)(16 * tt) * VS + 8 * cl);
+        for (int tt = 0; tt < 4; ++tt) {
+          lds_u8* const ad = vbuf(rr) + voff[tt] + 8 * cl * 128;
+          const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)ad);
+          const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(ad + 4 * 128));
+          Bv[tt] = __builtin_bit_cast(bf16x8, i16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]});
+        }
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
           acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, Bv[tt], acc[tt], 0, 0, 0);
@@ -431,20 +445,16 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
 }
 
 template <int NK, bool PAD, bool IDX>
-hipError_t launch_nk(const MfmaKArgs& ka, dim3 grid, dim3 block, uint32_t lds, hipStream_t s) {
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&topn_mfma_kernel<NK, PAD, IDX>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      160 * 1024 - 1024);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((topn_mfma_kernel<NK, PAD, IDX>), grid, block, lds, s, ka);
+hipError_t launch_nk(const MfmaKArgs& ka, dim3 grid, dim3 block, hipStream_t s) {
+  hipLaunchKernelGGL((topn_mfma_kernel<NK, PAD, IDX>), grid, block, 0, s, ka);
   return hipGetLastError();
 }
 
 template <int NK>
-hipError_t launch_pad(const MfmaKArgs& ka, bool pad, dim3 grid, dim3 block, uint32_t lds, hipStream_t s) {
+hipError_t launch_pad(const MfmaKArgs& ka, bool pad, dim3 grid, dim3 block, hipStream_t s) {
   if (ka.idx != nullptr)
-    return pad ? launch_nk<NK, true, true>(ka, grid, block, lds, s) : launch_nk<NK, false, true>(ka, grid, block, lds, s);
-  return pad ? launch_nk<NK, true, false>(ka, grid, block, lds, s) : launch_nk<NK, false, false>(ka, grid, block, lds, s);
+    return pad ? launch_nk<NK, true, true>(ka, grid, block, s) : launch_nk<NK, false, true>(ka, grid, block, s);
+  return pad ? launch_nk<NK, true, false>(ka, grid, block, s) : launch_nk<NK, false, false>(ka, grid, block, s);
 }
 
 // Smallest t with P(Binomial(d, 1/2) <= t) >= keep / n: the expected threshold
@@ -483,18 +493,17 @@ hipError_t launch_topn_mfma(const AttnParams& p, hipStream_t s) {
   ka.t0 = std::max(1, threshold_guess(p.d, p.keep, p.n));
   ka.exp_c = (float)(2.0 / sqrt((double)p.d) * 1.4426950408889634);
   const int64_t BH = p.B * p.H;
-  const uint32_t lds = (uint32_t)(kD * (32 * NK / mfma_rounds(NK) + 8) * 2);  // dynamic part: one V^T round
   ka.split = (ka.tiles + kWaves - 1) / kWaves;
   if (BH * ka.split >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(BH * ka.split));
   const dim3 block((unsigned)(64 * kWaves));
   const bool pad = p.n != 32 * NK;
   switch (NK) {
-    case 2: return launch_pad<2>(ka, pad, grid, block, lds, s);
-    case 4: return launch_pad<4>(ka, pad, grid, block, lds, s);
-    case 8: return launch_pad<8>(ka, pad, grid, block, lds, s);
-    case 16: return launch_pad<16>(ka, pad, grid, block, lds, s);
-    default: return launch_pad<32>(ka, pad, grid, block, lds, s);
+    case 2: return launch_pad<2>(ka, pad, grid, block, s);
+    case 4: return launch_pad<4>(ka, pad, grid, block, s);
+    case 8: return launch_pad<8>(ka, pad, grid, block, s);
+    case 16: return launch_pad<16>(ka, pad, grid, block, s);
+    default: return launch_pad<32>(ka, pad, grid, block, s);
   }
 }
 
