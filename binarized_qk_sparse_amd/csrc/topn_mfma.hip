@@ -55,6 +55,9 @@ constexpr uint32_t kC = 0x01010101u;
 constexpr uint32_t kM = 0x80808080u;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -179,14 +182,22 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   constexpr int NW = 2 * NK;            // byte-packed distance words per lane
   constexpr int RB = round_bytes(NK);   // bytes of one round buffer
   static_assert(R * KR == KG && KR % 8 == 0, "rounds must tile the quarter");
-  // The weight table is a static LDS array, so its address is fixed at compile
-  // time and a lookup address is index * 4 plus an immediate offset.
+  constexpr int NP = 32 * NK;           // padded keys
+  constexpr int KQS = KG * 32 + 16;     // bytes per key quarter of fp4 operands (16 of skew)
+  constexpr int VB = (RB > 2 * KQS ? RB : 2 * KQS);  // bytes per LDS buffer
+  // Static LDS arrays, at addresses fixed at compile time (a lookup address is
+  // index * 4 plus an immediate offset): the weight table and the byte -> eight
+  // fp4 nibble tables of the codes.
   __shared__ __align__(16) uint32_t tab[256];
-  // the V row buffers, as separate arrays so that the compiler can tell the round being
-  // read from the round being loaded
-  __shared__ __align__(16) uint8_t vbuf0[RB];
-  __shared__ __align__(16) uint8_t vbuf1[v_buffers(NK) > 1 ? RB : 16];
+  __shared__ __align__(16) uint32_t lut_k[256];  // key bits -> -x/2: bit 1 (x = -1) -> +0.5 (0x1), else -0.5 (0x9)
+  __shared__ __align__(16) uint32_t lut_q[256];  // query bits -> x: bit 1 -> -1.0 (0xA), else +1.0 (0x2)
+  // Two buffers: first the fp4 key operands (quarters 0, 1 in the first, 2, 3 in
+  // the second), then the V rows of alternate rounds.  Separate arrays, so that the
+  // compiler can tell the round being read from the round being loaded.
+  __shared__ __align__(16) uint8_t vbuf0[VB];
+  __shared__ __align__(16) uint8_t vbuf1[VB];
   auto vbuf = [&](int rr) { return (lds_u8*)((rr & 1) ? vbuf1 : vbuf0); };
+  auto kxq = [&](int quarter) { return (lds_u8*)(quarter >= 2 ? vbuf1 : vbuf0) + (quarter & 1) * KQS; };
 
   const int lane = (int)lane_id();
   const int g = lane >> 4, r = lane & 15;
@@ -218,59 +229,110 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
                                        (lds_void*)(buf + m * 1024), 16, 0, 0);
     }
   };
-  constexpr int kSteps = KG / 16;  // Hamming steps of 16 keys per lane row
-
-  // The V rows of rounds 0 and 1 are requested once the key codes have arrived: a
-  // function with direct-to-LDS loads gets only full waits (vmcnt(0)) for its other
-  // vector loads, so any load still in flight at such a wait would stall on them.
-  auto issue_first = [&]() {
-    issue_round(0);
-    if (R > 1) issue_round(1);
-  };
+  // ---- tables: softmax weights, and the fp4 nibbles of code bytes
+  for (int e = threadIdx.x; e < 256; e += 64 * kWaves) {
+    uint32_t ent = 0u;
+    if (e >= 1 && e <= 65) {
+      const float w = exp2f((float)(65 - e) * a.exp_c);  // w(tau - h), h = e + tau - 65
+      const uint32_t hi16 = bf16_rne_bits(w);
+      const float rest = w - __builtin_bit_cast(float, hi16 << 16);
+      ent = hi16 | (bf16_rne_bits(rest) << 16);
+    }
+    tab[e] = ent;
+    uint32_t nk = 0u, nq = 0u;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool neg = (e >> b) & 1;
+      nk |= (neg ? 0x1u : 0x9u) << (4 * b);
+      nq |= (neg ? 0xAu : 0x2u) << (4 * b);
+    }
+    lut_k[e] = nk;
+    lut_q[e] = nq;
+  }
+  // the codes: the query of this lane, and the keys this thread expands (loaded
+  // before any direct-to-LDS load, whose presence makes every wait a full wait)
+  const uint2 q = reinterpret_cast<const uint2*>(a.qbits)[hb + min(i, n - 1)];
+  const uint2* kb = reinterpret_cast<const uint2*>(a.kbits) + hb;
+  constexpr int KU = (NP + 64 * kWaves - 1) / (64 * kWaves);  // keys per thread
+  uint2 kc[KU];
+#pragma unroll
+  for (int u = 0; u < KU; ++u) {
+    const int j = min((int)threadIdx.x + u * 64 * kWaves, NP - 1);
+    kc[u] = kb[PAD ? min(j, n - 1) : j];  // padding keys: any code (their distances are overwritten)
+  }
+  __syncthreads();
+  // ---- fp4 operands of every key of the head: key j = g' KG + k goes to quarter
+  // g' at k * 32: dims 0-31 in bytes 0-15, dims 32-63 in bytes 16-31
+#pragma unroll
+  for (int u = 0; u < KU; ++u) {
+    const int j = (int)threadIdx.x + u * 64 * kWaves;
+    if (NP % (64 * kWaves) == 0 || j < NP) {
+      const uint2 c = kc[u];
+      lds_u32x4* dst = (lds_u32x4*)(kxq(j / KG) + (j % KG) * 32);
+      dst[0] = u32x4{lut_k[c.x & 0xffu], lut_k[(c.x >> 8) & 0xffu], lut_k[(c.x >> 16) & 0xffu], lut_k[c.x >> 24]};
+      dst[1] = u32x4{lut_k[c.y & 0xffu], lut_k[(c.y >> 8) & 0xffu], lut_k[(c.y >> 16) & 0xffu], lut_k[c.y >> 24]};
+    }
+  }
+  __syncthreads();
 
   uint32_t P[NW];
   int tau = 0, less = 0, cl_lo = 0, cl_hi = 0;
   if (have) {
-    // ------------------------------------------------ 1. Hamming distances
-    // (an unconditional load: a branch here would separate the DPP reads below from
-    // their XORs; rows past n only feed outputs that are never stored)
-    const uint2 q = reinterpret_cast<const uint2*>(a.qbits)[hb + min(i, n - 1)];
-    const uint2* kb = reinterpret_cast<const uint2*>(a.kbits) + hb;
-    auto kload = [&](int m) {
-      const int j = g * KG + 16 * m + r;  // the key this lane loads for its row
-      return kb[PAD ? min(j, n - 1) : j];  // padding keys: any code (their bytes are overwritten)
-    };
-    // every key code of the lane up front (they take the registers that the packed
-    // distances fill later, so the peak does not grow)
-    uint2 kq[kSteps];
+    // ------------------------------------------------ 1. Hamming distances on the matrix cores
+    // v_mfma_scale_f32_16x16x128_f8f6f4 (fp4 operands, unit scales): row rho of A is
+    // key (rho / 4) KG + 4b + rho % 4 of block b as -x/2, column r of B is query r as
+    // +-1, K = the 64 dims (lanes of K-blocks 2, 3 carry zeros in B), C starts at 32:
+    // C = 32 - dot / 2 = h exactly (every partial sum is a multiple of 1/2 below 2^6).
+    // Lane (g, r) then holds the distances of query r to keys g KG + 4b + 0..3: one
+    // byte-packed word P[b].
+    const uint32_t qw = (g & 1) ? q.y : q.x;
+    const bool qz = g >= 2;
+    v8i Bq;
+    Bq[0] = qz ? 0 : (int)lut_q[qw & 0xffu];
+    Bq[1] = qz ? 0 : (int)lut_q[(qw >> 8) & 0xffu];
+    Bq[2] = qz ? 0 : (int)lut_q[(qw >> 16) & 0xffu];
+    Bq[3] = qz ? 0 : (int)lut_q[qw >> 24];
+    Bq[4] = Bq[5] = Bq[6] = Bq[7] = 0;
+    const lds_u8* ka = kxq(r >> 2) + (r & 3) * 32 + (g & 1) * 16;
+    // eight independent products in flight before any result is read
+    constexpr int G = NW < 8 ? NW : 8;
 #pragma unroll
-    for (int m = 0; m < kSteps; ++m) kq[m] = kload(m);
+    for (int b0 = 0; b0 < NW; b0 += G) {
+      f32x4 c[G];
 #pragma unroll
-    for (int m = 0; m < kSteps; ++m) {
-      const uint2 kcur = kq[m];
-      if (m == 1) issue_first();  // (step 0, in its own scheduling region, waited for the codes)
-      uint32_t hv[16];
-      Seq<16>::run([&](auto s) {
-        constexpr int S = decltype(s)::value;
-        uint32_t h = __builtin_popcount(row_bcast<S>(kcur.x) ^ q.x);
-        hv[S] = __builtin_popcount(row_bcast<S>(kcur.y) ^ q.y) + h;
-      });
+      for (int j = 0; j < G; ++j) {
+        const u32x4 av = *(const lds_u32x4*)(ka + (b0 + j) * 128);
+        v8i A;
+        A[0] = (int)av[0]; A[1] = (int)av[1]; A[2] = (int)av[2]; A[3] = (int)av[3];
+        A[4] = A[5] = A[6] = A[7] = 0;
+        c[j] = f32x4{32.0f, 32.0f, 32.0f, 32.0f};
+        c[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bq, c[j], 4, 4, 0, 127, 0, 127);
+      }
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t word = (hv[4 * w + 3] << 24) | (hv[4 * w + 2] << 16) | (hv[4 * w + 1] << 8) | hv[4 * w];
+      for (int j = 0; j < G; ++j) {
+        const int b = b0 + j;
+        uint32_t word = __builtin_amdgcn_cvt_pk_u8_f32(c[j][0], 0, 0u);
+        word = __builtin_amdgcn_cvt_pk_u8_f32(c[j][1], 1, word);
+        word = __builtin_amdgcn_cvt_pk_u8_f32(c[j][2], 2, word);
+        word = __builtin_amdgcn_cvt_pk_u8_f32(c[j][3], 3, word);
         if (PAD) {
           // padding keys (j >= n) get a byte of at least 65, above every real distance:
           // h | 0x41 lies in [65, 127], which keeps all byte sums below carry
-          const int real = n - (g * KG + 16 * m + 4 * w);  // real keys in this word
+          const int real = n - (g * KG + 4 * b);  // real keys in this word
           const uint32_t pm = real >= 4 ? 0u : (real <= 0 ? 0x41414141u : (0x41414141u << (8 * real)));
           word |= pm;
         }
-        P[4 * m + w] = word;
+        P[b] = word;
       }
-      __builtin_amdgcn_sched_barrier(0);  // (no branch may enter this loop: the DPP reads must fold)
     }
-    if (kSteps == 1) issue_first();
+  }
+  // ---- every wave is done with the key operands: the V rows of rounds 0 and 1
+  // replace them, while the threshold is found
+  __syncthreads();
+  issue_round(0);
+  if (R > 1) issue_round(1);
 
+  if (have) {
     // ------------------------------------------------ 2. threshold
     // Invariant once bracketed: C(lo) < keep <= C(hi), C(t) = #{h <= t} over the
     // query's keys; llo / lhi are this lane's share of C(lo) / C(hi).  (Written
@@ -309,20 +371,8 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
     less = clo;
     cl_lo = llo;
     cl_hi = lhi;
-  } else {
-    issue_first();
   }
-  // ---- the weight table; then the rows of round 0 (and 1) are in place
-  for (int e = threadIdx.x; e < 256; e += 64 * kWaves) {
-    uint32_t ent = 0u;
-    if (e >= 1 && e <= 65) {
-      const float w = exp2f((float)(65 - e) * a.exp_c);  // w(tau - h), h = e + tau - 65
-      const uint32_t hi16 = bf16_rne_bits(w);
-      const float rest = w - __builtin_bit_cast(float, hi16 << 16);
-      ent = hi16 | (bf16_rne_bits(rest) << 16);
-    }
-    tab[e] = ent;
-  }
+  // ---- the rows of round 0 (and 1) are in place
   wait_vmem();  // this wave's direct-to-LDS loads
   __syncthreads();
 
