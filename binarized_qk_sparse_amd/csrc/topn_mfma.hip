@@ -406,6 +406,75 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
     ipos = quad_rows_excl(cl_lo + take, g);
     idst = a.idx + (hb + (i < n ? i : 0)) * (size_t)keep;
   }
+  // One 32-key step c over the lane's keys g KG + 8c + 0..7: prep applies the tie
+  // cut and reads the weight-table entries, make_a builds the A operands from them,
+  // products issues the matrix-core products.  The table and B reads of a step are
+  // in flight while the products of the previous step run.
+  auto prep = [&](int rr, int cl, uint32_t (&ent)[8]) {
+    const int c = rr * NKR + cl;
+    uint32_t I0 = P[2 * c] + kidx, I1 = P[2 * c + 1] + kidx;  // h - tau + 65 per byte
+    const uint32_t E0 = ((I0 + 63u * kC) ^ (I0 + 62u * kC)) & kM;  // h == tau
+    const uint32_t E1 = ((I1 + 63u * kC) ^ (I1 + 62u * kC)) & kM;
+    const int run1 = __builtin_popcount(E1) + (__builtin_popcount(E0) + run);
+    uint32_t U0 = run1 <= take ? 0u : E0, U1 = run1 <= take ? 0u : E1;  // keys at tau not taken
+    const bool part = run < take && run1 > take;
+    if (__builtin_amdgcn_ballot_w64(part) != 0 && part) {
+      // keep the first take - run keys at tau of this step (bytes of E0, then E1)
+      const uint32_t rem = (uint32_t)(take - run);
+      const uint32_t x0 = E0 >> 7, x1 = E1 >> 7;
+      const uint32_t p0 = x0 + (x0 << 8) + (x0 << 16) + (x0 << 24);  // inclusive ranks
+      const uint32_t p1 = x1 + (x1 << 8) + (x1 << 16) + (x1 << 24) + (uint32_t)__builtin_popcount(E0) * kC;
+      const uint32_t ad = (127u - rem) * kC;  // bit 7: rank >= rem + 1
+      U0 = E0 & (p0 + ad);
+      U1 = E1 & (p1 + ad);
+    }
+    run = run1;
+    I0 |= U0;
+    I1 |= U1;
+    if (IDX && i < n) {
+      // kept keys have a table index in [1, 65]
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const uint32_t ib = ((b < 4 ? I0 : I1) >> (8 * (b & 3))) & 0xffu;
+        if (ib <= 65u) idst[ipos++] = g * KG + 8 * c + b;
+      }
+    }
+    // table entries (hi | lo << 16) of the eight keys
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      ent[b] = tab[(I0 >> (8 * b)) & 0xffu];
+      ent[4 + b] = tab[(I1 >> (8 * b)) & 0xffu];
+    }
+  };
+  auto loadB = [&](int rr, int cl, bf16x8 (&Bv)[4]) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      lds_u8* const ad = vbuf(rr) + voff[tt] + 8 * cl * 128;
+      const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)ad);
+      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(ad + 4 * 128));
+      Bv[tt] = __builtin_bit_cast(bf16x8, i16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]});
+    }
+  };
+  auto make_a = [&](const uint32_t (&ent)[8], bf16x8& A_hi, bf16x8& A_lo) {
+    uint32_t ah[4], al[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ah[e] = __builtin_amdgcn_perm(ent[2 * e + 1], ent[2 * e], 0x05040100u);
+      al[e] = __builtin_amdgcn_perm(ent[2 * e + 1], ent[2 * e], 0x07060302u);
+    }
+    A_hi = __builtin_bit_cast(bf16x8, make_uint4(ah[0], ah[1], ah[2], ah[3]));
+    A_lo = __builtin_bit_cast(bf16x8, make_uint4(al[0], al[1], al[2], al[3]));
+  };
+  auto products = [&](const bf16x8& A_hi, const bf16x8& A_lo, const bf16x8 (&Bv)[4]) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, Bv[tt], acc[tt], 0, 0, 0);
+    accz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, ones, accz, 0, 0, 0);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, Bv[tt], acc[tt], 0, 0, 0);
+    accz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, ones, accz, 0, 0, 0);
+  };
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
     if (rr > 0) {
@@ -415,67 +484,20 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
       if (rr + 1 < R) issue_round(rr + 1);
     }
     if (have) {
+      // step cl: A operands of cl, then the tie cut and table reads of cl + 1, the
+      // products of cl, and the B reads of cl + 1
+      bf16x8 Bv[2][4];
+      uint32_t ent[2][8];
+      loadB(rr, 0, Bv[0]);
+      prep(rr, 0, ent[0]);
 #pragma unroll
       for (int cl = 0; cl < NKR; ++cl) {
-        const int c = rr * NKR + cl;  // step over the lane's keys g KG + 8c + 0..7
-        uint32_t I0 = P[2 * c] + kidx, I1 = P[2 * c + 1] + kidx;  // h - tau + 65 per byte
-        const uint32_t E0 = ((I0 + 63u * kC) ^ (I0 + 62u * kC)) & kM;  // h == tau
-        const uint32_t E1 = ((I1 + 63u * kC) ^ (I1 + 62u * kC)) & kM;
-        const int run1 = __builtin_popcount(E1) + (__builtin_popcount(E0) + run);
-        uint32_t U0 = run1 <= take ? 0u : E0, U1 = run1 <= take ? 0u : E1;  // keys at tau not taken
-        const bool part = run < take && run1 > take;
-        if (__builtin_amdgcn_ballot_w64(part) != 0 && part) {
-          // keep the first take - run keys at tau of this step (bytes of E0, then E1)
-          const uint32_t rem = (uint32_t)(take - run);
-          const uint32_t x0 = E0 >> 7, x1 = E1 >> 7;
-          const uint32_t p0 = x0 + (x0 << 8) + (x0 << 16) + (x0 << 24);  // inclusive ranks
-          const uint32_t p1 = x1 + (x1 << 8) + (x1 << 16) + (x1 << 24) + (uint32_t)__builtin_popcount(E0) * kC;
-          const uint32_t ad = (127u - rem) * kC;  // bit 7: rank >= rem + 1
-          U0 = E0 & (p0 + ad);
-          U1 = E1 & (p1 + ad);
-        }
-        run = run1;
-        I0 |= U0;
-        I1 |= U1;
-        if (IDX && i < n) {
-          // kept keys have a table index in [1, 65]
-#pragma unroll
-          for (int b = 0; b < 8; ++b) {
-            const uint32_t ib = ((b < 4 ? I0 : I1) >> (8 * (b & 3))) & 0xffu;
-            if (ib <= 65u) idst[ipos++] = g * KG + 8 * c + b;
-          }
-        }
-        // table entries (hi | lo << 16) of the eight keys, then hi and lo operands
-        uint32_t ent[8];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          ent[b] = tab[(I0 >> (8 * b)) & 0xffu];
-          ent[4 + b] = tab[(I1 >> (8 * b)) & 0xffu];
-        }
-        uint32_t ah[4], al[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ah[e] = __builtin_amdgcn_perm(ent[2 * e + 1], ent[2 * e], 0x05040100u);
-          al[e] = __builtin_amdgcn_perm(ent[2 * e + 1], ent[2 * e], 0x07060302u);
-        }
-        const bf16x8 A_hi = __builtin_bit_cast(bf16x8, make_uint4(ah[0], ah[1], ah[2], ah[3]));
-        const bf16x8 A_lo = __builtin_bit_cast(bf16x8, make_uint4(al[0], al[1], al[2], al[3]));
-        bf16x8 Bv[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          lds_u8* const ad = vbuf(rr) + voff[tt] + 8 * cl * 128;
-          const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)ad);
-          const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(ad + 4 * 128));
-          Bv[tt] = __builtin_bit_cast(bf16x8, i16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]});
-        }
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-          acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, Bv[tt], acc[tt], 0, 0, 0);
-        accz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, ones, accz, 0, 0, 0);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-          acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, Bv[tt], acc[tt], 0, 0, 0);
-        accz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, ones, accz, 0, 0, 0);
+        bf16x8 A_hi, A_lo;
+        make_a(ent[cl & 1], A_hi, A_lo);
+        if (cl + 1 < NKR) prep(rr, cl + 1, ent[(cl + 1) & 1]);
+        products(A_hi, A_lo, Bv[cl & 1]);
+        if (cl + 1 < NKR) loadB(rr, cl + 1, Bv[(cl + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);  // (keeps the next step's operand build after these reads)
       }
     }
   }
