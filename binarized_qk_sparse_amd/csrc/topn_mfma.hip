@@ -183,8 +183,8 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   constexpr int RB = round_bytes(NK);   // bytes of one round buffer
   static_assert(R * KR == KG && KR % 8 == 0, "rounds must tile the quarter");
   constexpr int NP = 32 * NK;           // padded keys
-  constexpr int KQS = KG * 32 + 16;     // bytes per key quarter of fp4 operands (16 of skew)
-  constexpr int VB = (RB > 2 * KQS ? RB : 2 * KQS);  // bytes per LDS buffer
+  constexpr int KQB = KG * 32;          // bytes of fp4 operands per key quarter
+  constexpr int VB = (RB > 2 * KQB + 256 ? RB : 2 * KQB + 256);  // bytes per LDS buffer
   // Static LDS arrays, at addresses fixed at compile time (a lookup address is
   // index * 4 plus an immediate offset): the weight table and the byte -> eight
   // fp4 nibble tables of the codes.
@@ -197,7 +197,14 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   __shared__ __align__(16) uint8_t vbuf0[VB];
   __shared__ __align__(16) uint8_t vbuf1[VB];
   auto vbuf = [&](int rr) { return (lds_u8*)((rr & 1) ? vbuf1 : vbuf0); };
-  auto kxq = [&](int quarter) { return (lds_u8*)(quarter >= 2 ? vbuf1 : vbuf0) + (quarter & 1) * KQS; };
+  // Quarter q of the fp4 key operands starts at an LDS address of 16 (q & 1) + 128 (q >> 1)
+  // modulo 256: the 16 lanes of a K-block then read four 16-byte slots of each quarter
+  // that together cover every bank once (64 banks of 4 bytes), or twice (32 banks).
+  auto kxq = [&](int quarter) {
+    lds_u8* const b = (lds_u8*)(quarter >= 2 ? vbuf1 : vbuf0) + (quarter & 1) * KQB;
+    const uint32_t want = 16u * (uint32_t)(quarter & 1) + 128u * (uint32_t)(quarter >> 1);
+    return b + ((want - (uint32_t)(uintptr_t)b) & 255u);
+  };
 
   const int lane = (int)lane_id();
   const int g = lane >> 4, r = lane & 15;
@@ -416,9 +423,11 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
     const uint32_t E0 = ((I0 + 63u * kC) ^ (I0 + 62u * kC)) & kM;  // h == tau
     const uint32_t E1 = ((I1 + 63u * kC) ^ (I1 + 62u * kC)) & kM;
     const int run1 = __builtin_popcount(E1) + (__builtin_popcount(E0) + run);
-    uint32_t U0 = run1 <= take ? 0u : E0, U1 = run1 <= take ? 0u : E1;  // keys at tau not taken
-    const bool part = run < take && run1 > take;
-    if (__builtin_amdgcn_ballot_w64(part) != 0 && part) {
+    // keys at tau not taken: all of them once the lane's count passes take, the
+    // first ones of this step kept where it passes take inside the step
+    const uint32_t over = run1 > take ? ~0u : 0u;
+    uint32_t U0 = E0 & over, U1 = E1 & over;
+    if (run < take && run1 > take) {
       // keep the first take - run keys at tau of this step (bytes of E0, then E1)
       const uint32_t rem = (uint32_t)(take - run);
       const uint32_t x0 = E0 >> 7, x1 = E1 >> 7;
