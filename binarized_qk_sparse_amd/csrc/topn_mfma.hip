@@ -162,11 +162,13 @@ constexpr int v_buffers(int nk) { return 8 * nk > round_keys(nk) ? 2 : 1; }
 
 // V rows in LDS.  Row lk = g KR + kk of a round buffer holds key g KG + rr KR
 // + kk (quarter g) in 128 bytes; its 32-byte channel block b (channels 16 b ..
-// 16 b + 15) sits at block position b ^ vswz(lk), vswz(lk) = (g + bit 1 of lk)
-// mod 4.  A transposing read of the B operand then touches every bank equally
-// (each group of 16 lanes reads rows g KR + 8c + e0 + 0..3 of one block), and
-// the direct-to-LDS loads write whole rows in order.
-HAD_DEVICE uint32_t vswz(uint32_t g, uint32_t lk) { return (g + ((lk >> 1) & 1u)) & 3u; }
+// 16 b + 15) sits at block position b ^ vswz(lk), vswz(lk) = (g + lk) mod 4.  A
+// transposing read of the B operand (each group of 16 lanes reads rows
+// g KR + 8c + e0 + 0..3 of one block) then finds its four rows in four different
+// 32-byte bank windows, and the groups of two quarters in eight: no bank conflicts
+// with 32 banks of 4 bytes or with 64.  The direct-to-LDS loads write whole rows in
+// order.
+HAD_DEVICE uint32_t vswz(uint32_t g, uint32_t lk) { return (g + lk) & 3u; }
 
 // s_waitcnt with vmcnt(0) only (expcnt and lgkmcnt left at their maxima)
 HAD_DEVICE void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
