@@ -11,10 +11,13 @@ stdout:
 
   value         query-key pairs per second of the whole step (B*H*n^2 / time)
   roofline      the dominant kernel (attention) against the VALU issue roof:
-                algorithmic VALU lane-slots per launch / the kernel's average
-                duration (a pair of HIP events around each launch, on the
-                stream it runs on), against
-                256 CU * 64 lanes * 2.4 GHz
+                algorithmic VALU lane-slots per launch / the kernel's mean
+                duration (a pair of HIP events around each of 100 launches, on
+                the stream it runs on), against 256 CU * 64 lanes * 2.4 GHz;
+                beside it the median, the median with L2 and the last-level
+                cache flushed before each launch (cold), and the fraction of the
+                measured integer-VALU ceiling (libhad_ubench.so: XOR + popcount
+                chains; also v_exp_f32 and a device copy)
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -144,6 +147,48 @@ def cpu_baseline(w, g, budget_s: float):
     }
 
 
+def measured_ceilings(torch, dev) -> dict:
+    """Measured ceilings beside the datasheet peaks: integer VALU (independent XOR + popcount
+    chains, 2 lane-ops per step, libhad_ubench.so), v_exp_f32, and a 256 MiB device copy."""
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "binarized_qk_sparse_amd", "libhad_ubench.so"))
+    for f in (lib.hub_xor_bcnt, lib.hub_exp):
+        f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        f.restype = ctypes.c_int
+    blocks, iters = 256 * 16, 1024
+    out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps=5):
+        for _ in range(2):
+            assert fn() == 0
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            assert fn() == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps
+
+    s = stream.cuda_stream
+    t_x = timed(lambda: lib.hub_xor_bcnt(out.data_ptr(), blocks, iters, s))
+    t_e = timed(lambda: lib.hub_exp(out.data_ptr(), blocks, iters, s))
+    nbytes = 256 << 20
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    t_c = timed(lambda: (dst.copy_(src), 0)[1])
+    del src, dst, out
+    valu = blocks * 256 * iters * 8 * 2 / t_x
+    return {
+        "valu_int_tlane_ops": valu / 1e12,
+        "clock_ghz_at_full_valu": valu / (256 * 64) / 1e9,
+        "exp_t_per_s": blocks * 256 * iters * 8 / t_e / 1e12,
+        "copy_gb_per_s": 2 * nbytes / t_c / 1e9,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,7 +289,7 @@ def main():
     # the dominant kernel alone: a pair of HIP events around each of R launches on the stream they
     # run on, so each pair brackets exactly one launch (back-to-back launches in one graph overlap
     # the tail of one with the start of the next, and separate graph replays add a launch gap)
-    R = 50
+    R = 100
     stream = torch.cuda.current_stream()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(R)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(R)]
@@ -253,8 +298,29 @@ def main():
         attend()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    t_att = sum(starts[i].elapsed_time(ends[i]) for i in range(R)) / 1e3 / R
-    log(f"{w.name}: attention {t_att * 1e6:.2f} us per launch (HIP events around each of {R} launches)")
+    durs = sorted(starts[i].elapsed_time(ends[i]) / 1e3 for i in range(R))
+    t_att = sum(durs) / R
+    t_med = durs[R // 2]
+    log(f"{w.name}: attention {t_att * 1e6:.2f} us mean, {t_med * 1e6:.2f} us median per launch "
+        f"(HIP events around each of {R} launches, warm)")
+    # cold: L2 and the last-level cache flushed by a 512 MiB read-modify-write before each launch
+    flush = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
+    RC = 20
+    cs = [torch.cuda.Event(enable_timing=True) for _ in range(RC)]
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(RC)]
+    for i in range(RC):
+        flush.add_(1.0)
+        cs[i].record(stream)
+        attend()
+        ce[i].record(stream)
+    torch.cuda.synchronize()
+    t_cold = sorted(cs[i].elapsed_time(ce[i]) / 1e3 for i in range(RC))[RC // 2]
+    del flush
+    log(f"{w.name}: attention {t_cold * 1e6:.2f} us median per launch, cold ({RC} launches)")
+    ceil = measured_ceilings(torch, dev)
+    log(f"measured ceilings: XOR+popcount {ceil['valu_int_tlane_ops']:.1f} T lane-ops/s "
+        f"(clock ~{ceil['clock_ghz_at_full_valu']:.2f} GHz), v_exp_f32 {ceil['exp_t_per_s']:.2f} T/s, "
+        f"device copy {ceil['copy_gb_per_s']:.0f} GB/s")
 
     slots = algorithmic_slots(w)
     achieved = slots / t_att
@@ -270,6 +336,10 @@ def main():
         "traffic": traffic,
         "kernel": kname,
         "kernel_us": t_att * 1e6,
+        "kernel_us_median": t_med * 1e6,
+        "kernel_us_cold_median": t_cold * 1e6,
+        "frac_of_measured_valu_ceiling": achieved / (ceil["valu_int_tlane_ops"] * 1e12),
+        "measured_ceilings": ceil,
         "slots_per_launch": slots,
         "hbm_bytes_per_launch_alg": algorithmic_bytes(w),
         "hbm_frac": algorithmic_bytes(w) / t_att / HBM_PEAK,

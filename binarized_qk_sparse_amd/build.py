@@ -3,7 +3,9 @@
     python -m binarized_qk_sparse_amd.build
 
 Each source is compiled to an object in ``_build/`` (in parallel), then linked
-into ``binarized_qk_sparse_amd/libhad.so``.
+into ``binarized_qk_sparse_amd/libhad.so``.  ``libhad_ubench.so`` (the measured
+VALU and v_exp ceilings that bench.py reports beside the datasheet peaks) is
+linked from ``ubench.hip`` alone.
 """
 from __future__ import annotations
 
@@ -19,6 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhad.so")
 SOURCES = ["api.cpp", "pack.hip", "vquant.hip", "topn.hip", "topn_mfma.hip", "topn_stream.hip", "dense_q8.hip"]
+UBENCH_LIB = os.path.join(PKG, "libhad_ubench.so")
+UBENCH_SOURCES = ["ubench.hip"]
 ARCH = "gfx950"
 
 
@@ -59,18 +63,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(lib: str, objs) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + UBENCH_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(LIB, objs[: len(SOURCES)])
+    _link(UBENCH_LIB, objs[len(SOURCES):])
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {os.path.basename(UBENCH_LIB)}")
     return LIB
 
 

@@ -26,6 +26,17 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_ceiling_library_loads_and_exports():
+    """libhad_ubench.so (the measured VALU, v_exp and copy ceilings bench.py reports) is built beside
+    libhad.so and exports its two launchers; it rejects bad sizes before any launch."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "binarized_qk_sparse_amd", "libhad_ubench.so"))
+    for name in ("hub_xor_bcnt", "hub_exp"):
+        f = getattr(lib, name)
+        f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        assert f(None, 1, 1, None) == 1
+        assert f(ctypes.c_void_p(256), 0, 1, None) == 1
+
+
 def test_header_constants_match_binding():
     with open(os.path.join(ROOT, "include", "had.h")) as f:
         text = f.read()
