@@ -129,21 +129,6 @@ HAD_DEVICE uint32_t lane_sad(const uint32_t (&P)[NW], uint32_t x) {
   return acc;
 }
 
-// Keys of this lane with h <= t (per-lane t in [0, 64]).
-template <int NW>
-HAD_DEVICE int lane_count_le(const uint32_t (&P)[NW], int t) {
-  return ((int)lane_sad<NW>(P, (uint32_t)t + 1u) - (int)lane_sad<NW>(P, (uint32_t)t) + 4 * NW) >> 1;
-}
-
-// Both lane_count_le(t - 1) (.x) and lane_count_le(t) (.y), t in [1, 64].
-template <int NW>
-HAD_DEVICE int2 lane_count_le2(const uint32_t (&P)[NW], int t) {
-  const int sm = (int)lane_sad<NW>(P, (uint32_t)t - 1u);
-  const int s0 = (int)lane_sad<NW>(P, (uint32_t)t);
-  const int sp = (int)lane_sad<NW>(P, (uint32_t)t + 1u);
-  return make_int2((s0 - sm + 4 * NW) >> 1, (sp - s0 + 4 * NW) >> 1);
-}
-
 HAD_DEVICE uint32_t bf16_rne_bits(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
@@ -349,32 +334,51 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
     // a store through a selected address, which forces them to memory.)
     const int tq = a.t0;
     int lo, hi, clo, llo, lhi;
+    // sums kept at the bracket's inner edges, sl = S(lo + 1) and sh = S(hi), so that a
+    // probe next to an edge needs one new sum instead of two
+    int sl, sh;
     {
-      const int2 cc = lane_count_le2<NW>(P, tq);
-      const int both = quad_rows_sum((cc.y << 16) | cc.x);
+      const int sm = (int)lane_sad<NW>(P, (uint32_t)tq - 1u);
+      const int s0 = (int)lane_sad<NW>(P, (uint32_t)tq);
+      const int sp = (int)lane_sad<NW>(P, (uint32_t)tq + 1u);
+      const int cx = (s0 - sm + 4 * NW) >> 1, cy = (sp - s0 + 4 * NW) >> 1;  // C(tq - 1), C(tq)
+      const int both = quad_rows_sum((cy << 16) | cx);
       const int ta = both & 0xffff, tb = both >> 16;
       const bool below = ta >= keep;         // tau <= tq - 1
       const bool at = !below && tb >= keep;  // tau == tq
       lo = below ? -1 : (at ? tq - 1 : tq);
       hi = below ? tq - 1 : (at ? tq : 65);  // C(65) = n >= keep: a placeholder bound
       clo = below ? 0 : (at ? ta : tb);
-      llo = below ? 0 : (at ? cc.x : cc.y);
-      lhi = below ? cc.x : (at ? cc.y : 0);
+      llo = below ? 0 : (at ? cx : cy);
+      lhi = below ? cx : (at ? cy : 0);
+      sl = sp;  // S(lo + 1) when lo = tq
+      sh = sm;  // S(hi) when hi = tq - 1
     }
     while (__builtin_amdgcn_ballot_w64(hi - lo > 1) != 0) {
       // probe next to the guess first, then bisect
       const bool open = hi - lo > 1;
       int mid = hi == 65 ? lo + 1 : (lo == -1 ? hi - 1 : (lo + hi) >> 1);
       mid = open ? mid : hi;  // settled lanes re-count harmlessly
-      const int cm = lane_count_le<NW>(P, mid);
+      const bool next_lo = mid == lo + 1 && lo >= 0;  // (sl is defined once lo >= 0)
+      const bool next_hi = mid == hi - 1 && hi < 65 && !next_lo;  // (sh is defined once hi < 65)
+      // C(mid) = (S(mid + 1) - S(mid) + count) / 2
+      const int s1 = (int)lane_sad<NW>(P, (uint32_t)(next_lo ? mid + 1 : mid));
+      int smid = next_lo ? sl : s1, snext = next_lo ? s1 : sh;
+      if (__builtin_amdgcn_ballot_w64(open && !next_lo && !next_hi) != 0) {
+        const int s2 = (int)lane_sad<NW>(P, (uint32_t)mid + 1u);
+        snext = (next_lo || next_hi) ? snext : s2;
+      }
+      const int cm = (snext - smid + 4 * NW) >> 1;
       const int tm = quad_rows_sum(cm);
       const bool up = open && tm >= keep;  // mid becomes the upper bound
       const bool dn = open && tm < keep;   // mid becomes the lower bound
       hi = up ? mid : hi;
       lhi = up ? cm : lhi;
+      sh = up ? smid : sh;
       lo = dn ? mid : lo;
       clo = dn ? tm : clo;
       llo = dn ? cm : llo;
+      sl = dn ? snext : sl;
     }
     tau = hi;
     less = clo;
