@@ -74,16 +74,23 @@ __global__ __launch_bounds__(kThreads) void colsum_partial_kernel(const T* __res
   }
 }
 
-// mu[bh][c] = float(sum over chunks / n).
-__global__ __launch_bounds__(kThreads) void mu_final_kernel(const double* __restrict__ partial,
-                                                            int64_t BH, int64_t n, int64_t chunks,
-                                                            int D, float* __restrict__ mu) {
-  const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (id >= BH * D) return;
-  const int64_t bh = id / D, c = id % D;
+// mu[bh][c] = float(sum over chunks / n).  One workgroup per (b, h): kThreads / D
+// groups of threads take interleaved chunks and LDS adds the group sums (float64;
+// the order of the additions moves mu by far less than one float32 ulp).
+__global__ __launch_bounds__(kThreads) void mu_final_kernel(const double* __restrict__ partial, int64_t n,
+                                                            int64_t chunks, int D, float* __restrict__ mu) {
+  __shared__ double red[kThreads];
+  const int64_t bh = blockIdx.x;
+  const int groups = kThreads / D;
+  const int c = threadIdx.x % D, grp = threadIdx.x / D;
   double s = 0.0;
-  for (int64_t k = 0; k < chunks; ++k) s += partial[(bh * chunks + k) * D + c];
-  mu[id] = (float)(s / (double)n);
+  for (int64_t k = grp; k < chunks; k += groups) s += partial[(bh * chunks + k) * D + c];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  if (grp == 0) {
+    for (int q = 1; q < groups; ++q) s += red[q * D + c];
+    mu[bh * D + c] = (float)(s / (double)n);
+  }
 }
 
 // 32 channels (one code word) per lane, D/32 lanes per token row: the word
@@ -136,6 +143,64 @@ __global__ __launch_bounds__(kThreads) void pack_rows_kernel(const T* __restrict
   if (part == 0 && alpha != nullptr) alpha[r] = MEAN ? (float)(asum / (double)D) : 1.0f;
 }
 
+// MEAN_SIGN with mu finished in the pack launch: when a workgroup's rows span at
+// most two heads (n >= rows per workgroup), its first 2D threads sum the column
+// partials of those heads (float64, chunks in index order, as mu_final_kernel
+// does) into LDS, and the workgroup holding a head's first row writes mu.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void pack_rows_mean_fused_kernel(const T* __restrict__ x, uint32_t rows,
+                                                                        uint32_t n, uint32_t chunks,
+                                                                        const double* __restrict__ partial,
+                                                                        float* __restrict__ mu,
+                                                                        uint32_t* __restrict__ bits,
+                                                                        float* __restrict__ alpha) {
+  constexpr int LPR = D / 32;
+  constexpr int RPW = kThreads / LPR;  // rows per workgroup
+  __shared__ float mus[2][D];
+  const uint32_t r0 = blockIdx.x * RPW;
+  const uint32_t h0 = r0 / n;
+  const uint32_t nh = (uint32_t)(rows / n);
+  if (threadIdx.x < 2 * D) {
+    const uint32_t hh = h0 + threadIdx.x / D, c = threadIdx.x % D;
+    float m = 0.0f;
+    if (hh < nh) {
+      double acc = 0.0;
+      for (uint32_t k = 0; k < chunks; ++k) acc += partial[((size_t)hh * chunks + k) * D + c];
+      m = (float)(acc / (double)n);
+      if ((size_t)hh * n >= r0 && (size_t)hh * n < (size_t)r0 + RPW) mu[(size_t)hh * D + c] = m;
+    }
+    mus[threadIdx.x / D][c] = m;
+  }
+  __syncthreads();
+  const uint32_t tid = blockIdx.x * kThreads + threadIdx.x;
+  const uint32_t r = tid / LPR, part = tid % LPR;
+  const bool live = r < rows;
+  const uint32_t rr = live ? r : rows - 1;
+  float v[32];
+  const T* src = x + (size_t)rr * D + 32 * part;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float e[8];
+    load8<T>(src + 8 * k, e);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[8 * k + c] = e[c];
+  }
+  const float* m = &mus[min(rr / n - h0, 1u)][32 * part];
+#pragma unroll
+  for (int c = 0; c < 32; ++c) v[c] = __fsub_rn(v[c], m[c]);
+  double asum = 0.0;
+#pragma unroll
+  for (int c = 0; c < 32; ++c) asum += fabs((double)v[c]);
+#pragma unroll
+  for (int off = 1; off < LPR; off <<= 1) asum += __shfl_xor(asum, off, 64);
+  uint32_t w = 0;
+#pragma unroll
+  for (int c = 0; c < 32; ++c) w |= (uint32_t)(v[c] < 0.0f) << c;
+  if (!live) return;
+  bits[(size_t)r * (D / 32) + part] = w;
+  if (part == 0 && alpha != nullptr) alpha[r] = (float)(asum / (double)D);
+}
+
 template <typename T, int D>
 hipError_t launch_typed(const PackParams& p, hipStream_t s) {
   const T* x = static_cast<const T*>(p.x);
@@ -146,8 +211,14 @@ hipError_t launch_typed(const PackParams& p, hipStream_t s) {
     const int64_t chunks = pack_chunks(p.n);
     hipLaunchKernelGGL((colsum_partial_kernel<T, D>), dim3((unsigned)(p.BH * chunks)), dim3(kThreads), 0,
                        s, x, p.n, chunks, p.partial);
-    const unsigned g2 = (unsigned)((p.BH * D + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL(mu_final_kernel, dim3(g2), dim3(kThreads), 0, s, p.partial, p.BH, p.n, chunks, D,
+    // a workgroup's rows span at most two heads, and re-summing their few partials per
+    // workgroup costs less than a launch
+    if (p.n >= kThreads / (D / 32) && chunks <= 4) {
+      hipLaunchKernelGGL((pack_rows_mean_fused_kernel<T, D>), dim3(grid), dim3(kThreads), 0, s, x, (uint32_t)rows,
+                         (uint32_t)p.n, (uint32_t)chunks, p.partial, p.mu, p.bits, p.alpha);
+      return hipGetLastError();
+    }
+    hipLaunchKernelGGL(mu_final_kernel, dim3((unsigned)p.BH), dim3(kThreads), 0, s, p.partial, p.n, chunks, D,
                        p.mu);
     hipLaunchKernelGGL((pack_rows_kernel<T, D, true>), dim3(grid), dim3(kThreads), 0, s, x, (uint32_t)rows,
                        (uint32_t)p.n, p.mu, p.bits, p.alpha, nullptr, 0u);

@@ -62,14 +62,22 @@ __global__ __launch_bounds__(kThreads) void vmax_partial_kernel(const T* __restr
   }
 }
 
-__global__ __launch_bounds__(kThreads) void vscale_kernel(const float* __restrict__ partial, int64_t BH,
-                                                          int64_t chunks, int D, float* __restrict__ scale) {
-  const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (id >= BH * D) return;
-  const int64_t bh = id / D, c = id % D;
+// scale[bh][c] = max over chunks / 127.  One workgroup per (b, h): kThreads / D
+// groups of threads take interleaved chunks, LDS takes the max of the groups.
+__global__ __launch_bounds__(kThreads) void vscale_kernel(const float* __restrict__ partial, int64_t chunks, int D,
+                                                          float* __restrict__ scale) {
+  __shared__ float red[kThreads];
+  const int64_t bh = blockIdx.x;
+  const int groups = kThreads / D;
+  const int c = threadIdx.x % D, grp = threadIdx.x / D;
   float m = 0.0f;
-  for (int64_t k = 0; k < chunks; ++k) m = fmaxf(m, partial[(bh * chunks + k) * D + c]);
-  scale[id] = __fdiv_rn(m, 127.0f);
+  for (int64_t k = grp; k < chunks; k += groups) m = fmaxf(m, partial[(bh * chunks + k) * D + c]);
+  red[threadIdx.x] = m;
+  __syncthreads();
+  if (grp == 0) {
+    for (int q = 1; q < groups; ++q) m = fmaxf(m, red[q * D + c]);
+    scale[bh * D + c] = __fdiv_rn(m, 127.0f);
+  }
 }
 
 // clamp(rint(fl(x / s)), -127, 127).  x * (1/s) (v_rcp_f32 and one multiply)
@@ -109,14 +117,66 @@ __global__ __launch_bounds__(kThreads) void vq_kernel(const T* __restrict__ v, u
   *reinterpret_cast<uint2*>(vq + (size_t)r * D + 8 * cg) = o;
 }
 
+// The quantize pass with the scales finished in the same launch: when a
+// workgroup's rows span at most two (b, h) slices (n >= rows per workgroup), its
+// first 2D threads take the max over the chunk partials of those slices and
+// divide by 127 (as vscale_kernel does) into LDS; the workgroup holding a slice's
+// first row writes its scales.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void vq_fused_kernel(const T* __restrict__ v, uint32_t rows, uint32_t n,
+                                                            uint32_t chunks, const float* __restrict__ partial,
+                                                            float* __restrict__ scale, int8_t* __restrict__ vq) {
+  constexpr int TPR = D / 8;
+  constexpr int RPP = kThreads / TPR;
+  __shared__ float sc[2][D];
+  const uint32_t r0 = blockIdx.x * RPP;
+  const uint32_t h0 = r0 / n;
+  const uint32_t nh = rows / n;
+  if (threadIdx.x < 2 * D) {
+    const uint32_t hh = h0 + threadIdx.x / D, c = threadIdx.x % D;
+    float q = 0.0f;
+    if (hh < nh) {
+      float m = 0.0f;
+      for (uint32_t k = 0; k < chunks; ++k) m = fmaxf(m, partial[((size_t)hh * chunks + k) * D + c]);
+      q = __fdiv_rn(m, 127.0f);
+      if ((size_t)hh * n >= r0 && (size_t)hh * n < (size_t)r0 + RPP) scale[(size_t)hh * D + c] = q;
+    }
+    sc[threadIdx.x / D][c] = q;
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  const int cg = t % TPR;
+  const uint32_t r = r0 + t / TPR;
+  if (r >= rows) return;
+  float x[8];
+  load8v<T>(v + (size_t)r * D + 8 * cg, x);
+  const float* sp = &sc[min(r / n - h0, 1u)][8 * cg];
+  uint32_t b[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) b[c] = q8(x[c], sp[c], __builtin_amdgcn_rcpf(sp[c]));
+  uint2 o;
+  o.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+  o.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+  *reinterpret_cast<uint2*>(vq + (size_t)r * D + 8 * cg) = o;
+}
+
 template <typename T, int D>
 hipError_t launch_typed(const VQuantParams& p, hipStream_t s) {
   const T* v = static_cast<const T*>(p.v);
   const int64_t chunks = vq_chunks(p.n);
   hipLaunchKernelGGL((vmax_partial_kernel<T, D>), dim3((unsigned)(p.BH * chunks)), dim3(kThreads), 0, s, v,
                      p.n, chunks, p.vmax_partial);
-  hipLaunchKernelGGL(vscale_kernel, dim3((unsigned)((p.BH * D + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                     s, p.vmax_partial, p.BH, chunks, D, p.vscale);
+  // a workgroup's rows span at most two slices, and taking the max of their few partials
+  // per workgroup costs less than a launch
+  if (p.n >= kThreads / (D / 8) && chunks <= 4) {
+    const int64_t rows = p.BH * p.n;
+    constexpr int RPP = kThreads / (D / 8);
+    hipLaunchKernelGGL((vq_fused_kernel<T, D>), dim3((unsigned)((rows + RPP - 1) / RPP)), dim3(kThreads), 0, s, v,
+                       (uint32_t)rows, (uint32_t)p.n, (uint32_t)chunks, p.vmax_partial, p.vscale, p.vq);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(vscale_kernel, dim3((unsigned)p.BH), dim3(kThreads), 0, s, p.vmax_partial, chunks, D,
+                     p.vscale);
   const int64_t rows = p.BH * p.n;
   constexpr int RPP = kThreads / (D / 8);
   hipLaunchKernelGGL((vq_kernel<T, D>), dim3((unsigned)((rows + RPP - 1) / RPP)), dim3(kThreads), 0, s, v,
