@@ -30,6 +30,7 @@ EXPORTS = (
     "had_status_str",
     "had_workspace_bytes",
     "had_pack",
+    "had_pack_qk",
     "had_attention_topn",
     "binattn_dense_q8",
 )
@@ -59,6 +60,8 @@ def load() -> ctypes.CDLL:
     lib.had_workspace_bytes.restype = SZ
     lib.had_pack.argtypes = [P, I, I64, I64, I64, I64, I, P, P, P, P, SZ, P]
     lib.had_pack.restype = I
+    lib.had_pack_qk.argtypes = [P, P, I, I64, I64, I64, I64, I, P, P, P, P, P, P, P, SZ, P]
+    lib.had_pack_qk.restype = I
     lib.had_attention_topn.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, I64, I64, I, P, P, P, SZ, P]
     lib.had_attention_topn.restype = I
     lib.binattn_dense_q8.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, I64, P, P, SZ, P]

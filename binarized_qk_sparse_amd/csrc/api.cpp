@@ -26,6 +26,8 @@ WorkspaceLayout workspace_layout(int64_t B, int64_t H, int64_t n, int64_t d) {
   off = align256(off + sizeof(float) * (size_t)(BH * d));
   w.vmax_partial = off;
   off = align256(off + sizeof(float) * (size_t)(BH * vq_chunks(n) * d));
+  w.pack_partial2 = off;  // (last, so the regions above keep their offsets)
+  off = align256(off + sizeof(double) * (size_t)(BH * pack_chunks(n) * d));
   w.total = off;
   return w;
 }
@@ -106,30 +108,65 @@ size_t had_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d) {
   return workspace_layout(B, H, n, d).total;
 }
 
-int had_pack(const void* x, int x_dtype, int64_t B, int64_t H, int64_t n, int64_t d, int mode, uint32_t* bits,
-             float* alpha, float* mu, void* workspace, size_t workspace_bytes, void* stream) {
-  static const char* fn = "had_pack";
-  if (x == nullptr || bits == nullptr) return fail(HAD_ERR_INVALID_ARG, fn, "NULL tensor");
+namespace {
+
+// Shared checks of had_pack and had_pack_qk; fills everything but the tensor sets.
+int pack_common(int64_t B, int64_t H, int64_t n, int64_t d, int x_dtype, int mode, PackParams* p,
+                const char* fn) {
   if (!sizes_ok(B, H, n, d)) return fail(HAD_ERR_INVALID_ARG, fn, "sizes must be positive and B*H*n*d < 2^31");
   if (x_dtype != HAD_F32 && x_dtype != HAD_BF16) return fail(HAD_ERR_INVALID_ARG, fn, "unknown x_dtype");
   if (mode != HAD_SIGN && mode != HAD_MEAN_SIGN) return fail(HAD_ERR_INVALID_ARG, fn, "unknown mode");
   if (d != 32 && d != 64 && d != 128) return fail(HAD_ERR_UNSUPPORTED, fn, "d must be 32, 64 or 128");
   if (n > HAD_MAX_N) return fail(HAD_ERR_UNSUPPORTED, fn, "n above HAD_MAX_N");
+  p->x_dtype = x_dtype;
+  p->BH = B * H;
+  p->n = n;
+  p->d = d;
+  p->mode = mode;
+  return HAD_OK;
+}
+
+}  // namespace
+
+int had_pack(const void* x, int x_dtype, int64_t B, int64_t H, int64_t n, int64_t d, int mode, uint32_t* bits,
+             float* alpha, float* mu, void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "had_pack";
+  if (x == nullptr || bits == nullptr) return fail(HAD_ERR_INVALID_ARG, fn, "NULL tensor");
   PackParams p{};
-  p.x = x;
-  p.x_dtype = x_dtype;
-  p.BH = B * H;
-  p.n = n;
-  p.d = d;
-  p.mode = mode;
-  p.bits = bits;
-  p.alpha = alpha;
-  p.mu = mu;
+  int st = pack_common(B, H, n, d, x_dtype, mode, &p, fn);
+  if (st != HAD_OK) return st;
+  p.count = 1;
+  p.set[0] = PackSet{x, bits, alpha, mu, nullptr};
   if (mode == HAD_MEAN_SIGN) {
     if (alpha == nullptr || mu == nullptr) return fail(HAD_ERR_INVALID_ARG, fn, "MEAN_SIGN needs alpha and mu");
-    const int st = check_workspace(workspace, workspace_bytes, B, H, n, d, fn);
+    st = check_workspace(workspace, workspace_bytes, B, H, n, d, fn);
     if (st != HAD_OK) return st;
-    p.partial = reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + workspace_layout(B, H, n, d).pack_partial);
+    p.set[0].partial =
+        reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + workspace_layout(B, H, n, d).pack_partial);
+  }
+  return launch_status(launch_pack(p, static_cast<hipStream_t>(stream)), fn);
+}
+
+int had_pack_qk(const void* q, const void* k, int x_dtype, int64_t B, int64_t H, int64_t n, int64_t d, int mode,
+                uint32_t* qbits, uint32_t* kbits, float* alpha_q, float* alpha_k, float* mu_q, float* mu_k,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "had_pack_qk";
+  if (q == nullptr || k == nullptr || qbits == nullptr || kbits == nullptr)
+    return fail(HAD_ERR_INVALID_ARG, fn, "NULL tensor");
+  PackParams p{};
+  int st = pack_common(B, H, n, d, x_dtype, mode, &p, fn);
+  if (st != HAD_OK) return st;
+  p.count = 2;
+  p.set[0] = PackSet{q, qbits, alpha_q, mu_q, nullptr};
+  p.set[1] = PackSet{k, kbits, alpha_k, mu_k, nullptr};
+  if (mode == HAD_MEAN_SIGN) {
+    if (alpha_q == nullptr || alpha_k == nullptr || mu_q == nullptr || mu_k == nullptr)
+      return fail(HAD_ERR_INVALID_ARG, fn, "MEAN_SIGN needs alpha and mu for Q and K");
+    st = check_workspace(workspace, workspace_bytes, B, H, n, d, fn);
+    if (st != HAD_OK) return st;
+    const WorkspaceLayout w = workspace_layout(B, H, n, d);
+    p.set[0].partial = reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + w.pack_partial);
+    p.set[1].partial = reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + w.pack_partial2);
   }
   return launch_status(launch_pack(p, static_cast<hipStream_t>(stream)), fn);
 }

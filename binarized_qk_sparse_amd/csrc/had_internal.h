@@ -7,15 +7,19 @@
 namespace had {
 
 // ---- packing (pack.hip)
-struct PackParams {
+struct PackSet {
   const void* x;
-  int x_dtype;  // HAD_F32 / HAD_BF16
-  int64_t BH, n, d;
-  int mode;  // HAD_SIGN / HAD_MEAN_SIGN
   uint32_t* bits;
   float* alpha;
   float* mu;
   double* partial;  // MEAN_SIGN: [BH, chunks, d] float64 column sums
+};
+struct PackParams {
+  int x_dtype;  // HAD_F32 / HAD_BF16
+  int64_t BH, n, d;
+  int mode;   // HAD_SIGN / HAD_MEAN_SIGN
+  int count;  // tensors packed by the launches: 1 (had_pack) or 2 (had_pack_qk)
+  PackSet set[2];
 };
 constexpr int kPackChunk = 256;  // tokens per column-sum chunk
 inline int64_t pack_chunks(int64_t n) { return (n + kPackChunk - 1) / kPackChunk; }
@@ -59,6 +63,7 @@ hipError_t launch_dense_q8(const AttnParams& p, hipStream_t s);
 // Device scratch layout inside the caller's workspace.
 struct WorkspaceLayout {
   size_t pack_partial;  // offset of double[BH, pack_chunks, d]
+  size_t pack_partial2;  // offset of the second tensor's (had_pack_qk)
   size_t vq;            // offset of int8[BH, n, d]
   size_t vscale;        // offset of float[BH, d]
   size_t vmax_partial;  // offset of float[BH, vq_chunks, d]

@@ -41,16 +41,28 @@ HAD_DEVICE void load8<uint16_t>(const uint16_t* p, float (&v)[8]) {
   v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
 }
 
+// One or two tensors per launch (had_pack_qk packs Q and K together): the grid
+// holds `count` equal halves, and a workgroup takes the tensor of its half.
+struct Sets {
+  const void* x[2];
+  uint32_t* bits[2];
+  float* alpha[2];
+  float* mu[2];
+  double* partial[2];
+};
+
 // Column sums over one chunk of tokens, in float64: partial[bh][chunk][c].
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void colsum_partial_kernel(const T* __restrict__ x, int64_t n,
-                                                                  int64_t chunks,
-                                                                  double* __restrict__ partial) {
+__global__ __launch_bounds__(kThreads) void colsum_partial_kernel(const Sets S, int64_t n, int64_t chunks,
+                                                                  int64_t per) {
   constexpr int TPR = D / 8;          // threads per token row
   constexpr int RPP = kThreads / TPR;  // rows per pass
   __shared__ double red[RPP][D];
-  const int64_t bh = blockIdx.x / chunks;
-  const int64_t chunk = blockIdx.x % chunks;
+  const int set = (int)(blockIdx.x / per);
+  const int64_t b = blockIdx.x % per;
+  const T* __restrict__ x = static_cast<const T*>(S.x[set]);
+  const int64_t bh = b / chunks;
+  const int64_t chunk = b % chunks;
   const int t = threadIdx.x;
   const int r_off = t / TPR, cg = t % TPR;
   double s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -70,17 +82,19 @@ __global__ __launch_bounds__(kThreads) void colsum_partial_kernel(const T* __res
   if (t < D) {
     double acc = 0.0;
     for (int rp = 0; rp < RPP; ++rp) acc += red[rp][t];
-    partial[(bh * chunks + chunk) * D + t] = acc;
+    S.partial[set][(bh * chunks + chunk) * D + t] = acc;
   }
 }
 
 // mu[bh][c] = float(sum over chunks / n).  One workgroup per (b, h): kThreads / D
 // groups of threads take interleaved chunks and LDS adds the group sums (float64;
 // the order of the additions moves mu by far less than one float32 ulp).
-__global__ __launch_bounds__(kThreads) void mu_final_kernel(const double* __restrict__ partial, int64_t n,
-                                                            int64_t chunks, int D, float* __restrict__ mu) {
+__global__ __launch_bounds__(kThreads) void mu_final_kernel(const Sets S, int64_t BH, int64_t n, int64_t chunks,
+                                                            int D) {
   __shared__ double red[kThreads];
-  const int64_t bh = blockIdx.x;
+  const int set = (int)(blockIdx.x / BH);
+  const int64_t bh = blockIdx.x % BH;
+  const double* __restrict__ partial = S.partial[set];
   const int groups = kThreads / D;
   const int c = threadIdx.x % D, grp = threadIdx.x / D;
   double s = 0.0;
@@ -89,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void mu_final_kernel(const double* __rest
   __syncthreads();
   if (grp == 0) {
     for (int q = 1; q < groups; ++q) s += red[q * D + c];
-    mu[bh * D + c] = (float)(s / (double)n);
+    S.mu[set][bh * D + c] = (float)(s / (double)n);
   }
 }
 
@@ -97,16 +111,38 @@ __global__ __launch_bounds__(kThreads) void mu_final_kernel(const double* __rest
 // needs no lane exchange, and a wave reads 64 consecutive 32-channel runs.
 // MEAN_SIGN subtracts mu and sums |x - mu| in float64 for alpha (the D/32 lanes
 // of a row add their partial sums).  Plain SIGN also writes mu = 0 when asked
-// (mu_zero, BH*D floats), so no separate fill launch is needed.
-template <typename T, int D, bool MEAN>
-__global__ __launch_bounds__(kThreads) void pack_rows_kernel(const T* __restrict__ x, uint32_t rows, uint32_t n,
-                                                             const float* __restrict__ mu,
-                                                             uint32_t* __restrict__ bits,
-                                                             float* __restrict__ alpha,
-                                                             float* __restrict__ mu_zero, uint32_t mu_count) {
+// (mu_count = BH*D floats), so no separate fill launch is needed.
+// FUSED (MEAN_SIGN, a workgroup's rows within at most two heads): mu is finished
+// here instead of by mu_final_kernel, the first 2D threads summing the column
+// partials of those heads into LDS; the workgroup holding a head's first row
+// writes it.
+template <typename T, int D, bool MEAN, bool FUSED>
+__global__ __launch_bounds__(kThreads) void pack_rows_kernel(const Sets S, uint32_t rows, uint32_t n,
+                                                             uint32_t per, uint32_t mu_count, uint32_t chunks) {
   constexpr int LPR = D / 32;
-  const uint32_t tid = blockIdx.x * kThreads + threadIdx.x;
-  if (!MEAN && mu_zero != nullptr && tid < mu_count) mu_zero[tid] = 0.0f;
+  constexpr int RPW = kThreads / LPR;  // rows per workgroup
+  const int set = (int)(blockIdx.x / per);
+  const uint32_t blk = blockIdx.x % per;
+  const T* __restrict__ x = static_cast<const T*>(S.x[set]);
+  const uint32_t tid = blk * kThreads + threadIdx.x;
+  if (!MEAN && S.mu[set] != nullptr && tid < mu_count) S.mu[set][tid] = 0.0f;
+  __shared__ float mus[FUSED ? 2 : 1][FUSED ? D : 1];
+  const uint32_t h0 = blk * RPW / n;
+  if (FUSED) {
+    if (threadIdx.x < 2 * D) {
+      const uint32_t hh = h0 + threadIdx.x / D, c = threadIdx.x % D;
+      float m = 0.0f;
+      if (hh < rows / n) {
+        double acc = 0.0;
+        for (uint32_t k = 0; k < chunks; ++k) acc += S.partial[set][((size_t)hh * chunks + k) * D + c];
+        m = (float)(acc / (double)n);
+        if ((size_t)hh * n >= (size_t)blk * RPW && (size_t)hh * n < (size_t)blk * RPW + RPW)
+          S.mu[set][(size_t)hh * D + c] = m;
+      }
+      mus[threadIdx.x / D][c] = m;
+    }
+    __syncthreads();
+  }
   const uint32_t r = tid / LPR, part = tid % LPR;
   const bool live = r < rows;
   const uint32_t rr = live ? r : rows - 1;  // dead lanes read a valid row, write nothing
@@ -121,15 +157,9 @@ __global__ __launch_bounds__(kThreads) void pack_rows_kernel(const T* __restrict
   }
   double asum = 0.0;
   if (MEAN) {
-    const float* m = mu + (size_t)(rr / n) * D + 32 * part;
+    const float* m = FUSED ? &mus[min(rr / n - h0, 1u)][32 * part] : S.mu[set] + (size_t)(rr / n) * D + 32 * part;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float4 mm = *reinterpret_cast<const float4*>(m + 4 * k);
-      v[4 * k + 0] = __fsub_rn(v[4 * k + 0], mm.x);
-      v[4 * k + 1] = __fsub_rn(v[4 * k + 1], mm.y);
-      v[4 * k + 2] = __fsub_rn(v[4 * k + 2], mm.z);
-      v[4 * k + 3] = __fsub_rn(v[4 * k + 3], mm.w);
-    }
+    for (int c = 0; c < 32; ++c) v[c] = __fsub_rn(v[c], m[c]);
 #pragma unroll
     for (int c = 0; c < 32; ++c) asum += fabs((double)v[c]);
 #pragma unroll
@@ -139,96 +169,45 @@ __global__ __launch_bounds__(kThreads) void pack_rows_kernel(const T* __restrict
 #pragma unroll
   for (int c = 0; c < 32; ++c) w |= (uint32_t)(v[c] < 0.0f) << c;
   if (!live) return;
-  bits[(size_t)r * (D / 32) + part] = w;
-  if (part == 0 && alpha != nullptr) alpha[r] = MEAN ? (float)(asum / (double)D) : 1.0f;
-}
-
-// MEAN_SIGN with mu finished in the pack launch: when a workgroup's rows span at
-// most two heads (n >= rows per workgroup), its first 2D threads sum the column
-// partials of those heads (float64, chunks in index order, as mu_final_kernel
-// does) into LDS, and the workgroup holding a head's first row writes mu.
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void pack_rows_mean_fused_kernel(const T* __restrict__ x, uint32_t rows,
-                                                                        uint32_t n, uint32_t chunks,
-                                                                        const double* __restrict__ partial,
-                                                                        float* __restrict__ mu,
-                                                                        uint32_t* __restrict__ bits,
-                                                                        float* __restrict__ alpha) {
-  constexpr int LPR = D / 32;
-  constexpr int RPW = kThreads / LPR;  // rows per workgroup
-  __shared__ float mus[2][D];
-  const uint32_t r0 = blockIdx.x * RPW;
-  const uint32_t h0 = r0 / n;
-  const uint32_t nh = (uint32_t)(rows / n);
-  if (threadIdx.x < 2 * D) {
-    const uint32_t hh = h0 + threadIdx.x / D, c = threadIdx.x % D;
-    float m = 0.0f;
-    if (hh < nh) {
-      double acc = 0.0;
-      for (uint32_t k = 0; k < chunks; ++k) acc += partial[((size_t)hh * chunks + k) * D + c];
-      m = (float)(acc / (double)n);
-      if ((size_t)hh * n >= r0 && (size_t)hh * n < (size_t)r0 + RPW) mu[(size_t)hh * D + c] = m;
-    }
-    mus[threadIdx.x / D][c] = m;
-  }
-  __syncthreads();
-  const uint32_t tid = blockIdx.x * kThreads + threadIdx.x;
-  const uint32_t r = tid / LPR, part = tid % LPR;
-  const bool live = r < rows;
-  const uint32_t rr = live ? r : rows - 1;
-  float v[32];
-  const T* src = x + (size_t)rr * D + 32 * part;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    float e[8];
-    load8<T>(src + 8 * k, e);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) v[8 * k + c] = e[c];
-  }
-  const float* m = &mus[min(rr / n - h0, 1u)][32 * part];
-#pragma unroll
-  for (int c = 0; c < 32; ++c) v[c] = __fsub_rn(v[c], m[c]);
-  double asum = 0.0;
-#pragma unroll
-  for (int c = 0; c < 32; ++c) asum += fabs((double)v[c]);
-#pragma unroll
-  for (int off = 1; off < LPR; off <<= 1) asum += __shfl_xor(asum, off, 64);
-  uint32_t w = 0;
-#pragma unroll
-  for (int c = 0; c < 32; ++c) w |= (uint32_t)(v[c] < 0.0f) << c;
-  if (!live) return;
-  bits[(size_t)r * (D / 32) + part] = w;
-  if (part == 0 && alpha != nullptr) alpha[r] = (float)(asum / (double)D);
+  S.bits[set][(size_t)r * (D / 32) + part] = w;
+  if (part == 0 && S.alpha[set] != nullptr) S.alpha[set][r] = MEAN ? (float)(asum / (double)D) : 1.0f;
 }
 
 template <typename T, int D>
 hipError_t launch_typed(const PackParams& p, hipStream_t s) {
-  const T* x = static_cast<const T*>(p.x);
+  Sets S{};
+  for (int k = 0; k < p.count; ++k) {
+    S.x[k] = p.set[k].x;
+    S.bits[k] = p.set[k].bits;
+    S.alpha[k] = p.set[k].alpha;
+    S.mu[k] = p.set[k].mu;
+    S.partial[k] = p.set[k].partial;
+  }
+  const unsigned cnt = (unsigned)p.count;
   const int64_t rows = p.BH * p.n;
   const int64_t threads = rows * (D / 32);
   if (p.mode == HAD_MEAN_SIGN) {
-    const unsigned grid = (unsigned)((threads + kThreads - 1) / kThreads);
+    const unsigned per = (unsigned)((threads + kThreads - 1) / kThreads);
     const int64_t chunks = pack_chunks(p.n);
-    hipLaunchKernelGGL((colsum_partial_kernel<T, D>), dim3((unsigned)(p.BH * chunks)), dim3(kThreads), 0,
-                       s, x, p.n, chunks, p.partial);
+    hipLaunchKernelGGL((colsum_partial_kernel<T, D>), dim3(cnt * (unsigned)(p.BH * chunks)), dim3(kThreads), 0,
+                       s, S, p.n, chunks, p.BH * chunks);
     // a workgroup's rows span at most two heads, and re-summing their few partials per
     // workgroup costs less than a launch
     if (p.n >= kThreads / (D / 32) && chunks <= 4) {
-      hipLaunchKernelGGL((pack_rows_mean_fused_kernel<T, D>), dim3(grid), dim3(kThreads), 0, s, x, (uint32_t)rows,
-                         (uint32_t)p.n, (uint32_t)chunks, p.partial, p.mu, p.bits, p.alpha);
+      hipLaunchKernelGGL((pack_rows_kernel<T, D, true, true>), dim3(cnt * per), dim3(kThreads), 0, s, S,
+                         (uint32_t)rows, (uint32_t)p.n, per, 0u, (uint32_t)chunks);
       return hipGetLastError();
     }
-    hipLaunchKernelGGL(mu_final_kernel, dim3((unsigned)p.BH), dim3(kThreads), 0, s, p.partial, p.n, chunks, D,
-                       p.mu);
-    hipLaunchKernelGGL((pack_rows_kernel<T, D, true>), dim3(grid), dim3(kThreads), 0, s, x, (uint32_t)rows,
-                       (uint32_t)p.n, p.mu, p.bits, p.alpha, nullptr, 0u);
+    hipLaunchKernelGGL(mu_final_kernel, dim3(cnt * (unsigned)p.BH), dim3(kThreads), 0, s, S, p.BH, p.n, chunks, D);
+    hipLaunchKernelGGL((pack_rows_kernel<T, D, true, false>), dim3(cnt * per), dim3(kThreads), 0, s, S,
+                       (uint32_t)rows, (uint32_t)p.n, per, 0u, 0u);
   } else {
-    // the launch covers max(rows * D/32, BH * D) threads: the first BH * D also write mu = 0
-    const int64_t mu_count = p.mu != nullptr ? p.BH * D : 0;
+    // the launch covers max(rows * D/32, BH * D) threads per tensor: the first BH * D also write mu = 0
+    const int64_t mu_count = p.BH * D;
     const int64_t need = std::max<int64_t>(threads, mu_count);
-    const unsigned g = (unsigned)((need + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL((pack_rows_kernel<T, D, false>), dim3(g), dim3(kThreads), 0, s, x, (uint32_t)rows,
-                       (uint32_t)p.n, nullptr, p.bits, p.alpha, p.mu, (uint32_t)mu_count);
+    const unsigned per = (unsigned)((need + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL((pack_rows_kernel<T, D, false, false>), dim3(cnt * per), dim3(kThreads), 0, s, S,
+                       (uint32_t)rows, (uint32_t)p.n, per, (uint32_t)mu_count, 0u);
   }
   return hipGetLastError();
 }

@@ -66,6 +66,30 @@ def had_pack(x: torch.Tensor, mode: int = HAD_SIGN, ws: Optional[torch.Tensor] =
     return bits, alpha, mu
 
 
+def had_pack_qk(q: torch.Tensor, k: torch.Tensor, mode: int = HAD_SIGN, ws: Optional[torch.Tensor] = None):
+    """Q and K [B,H,n,d] (same dtype and shape) -> ((qbits, alpha_q, mu_q), (kbits, alpha_k, mu_k)),
+    each exactly what had_pack gives for that tensor, from one set of launches."""
+    _dev(q, "q")
+    _dev(k, "k")
+    if q.shape != k.shape or q.dtype != k.dtype:
+        raise ValueError("q and k must share shape and dtype")
+    B, H, n, d = q.shape
+    outs = []
+    for _ in range(2):
+        outs.append((torch.empty((B, H, n, d // 32), dtype=torch.int32, device=q.device),
+                     torch.empty((B, H, n), dtype=torch.float32, device=q.device),
+                     torch.empty((B, H, d), dtype=torch.float32, device=q.device)))
+    if mode == HAD_MEAN_SIGN and ws is None:
+        ws = workspace(B, H, n, d, q.device)
+    wsz = 0 if ws is None else ws.numel()
+    (qb, aq, mq), (kb, ak, mk) = outs
+    st = _lib.load().had_pack_qk(q.data_ptr(), k.data_ptr(), _dtype_code(q), B, H, n, d, mode, qb.data_ptr(),
+                                 kb.data_ptr(), aq.data_ptr(), ak.data_ptr(), mq.data_ptr(), mk.data_ptr(),
+                                 _ptr(ws), wsz, _stream())
+    _lib.check("had_pack_qk", st)
+    return outs[0], outs[1]
+
+
 def had_attention_topn(qbits: torch.Tensor, kbits: torch.Tensor, v: torch.Tensor, top_n: int, *,
                        alpha_q: Optional[torch.Tensor] = None, alpha_k: Optional[torch.Tensor] = None,
                        bias: Optional[torch.Tensor] = None, av_mode: int = HAD_AV_F32, want_idx: bool = False,

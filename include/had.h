@@ -78,7 +78,7 @@ const char* had_status_str(int status);
 
 /*
  * Bytes of device workspace any entry point needs for these sizes (a single
- * buffer of this size serves had_pack, had_attention_topn and
+ * buffer of this size serves had_pack, had_pack_qk, had_attention_topn and
  * binattn_dense_q8).  Multiple of 256.  Contents need not be initialised.
  */
 size_t had_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d);
@@ -105,6 +105,23 @@ size_t had_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d);
 int had_pack(const void* x, int x_dtype, int64_t B, int64_t H, int64_t n, int64_t d, int mode,
              uint32_t* bits, float* alpha, float* mu, void* workspace, size_t workspace_bytes,
              void* stream);
+
+/*
+ * had_pack_qk -- binarize and bit-pack Q and K of one layer in one set of launches
+ * (the same passages as had_pack).  Each output is exactly what had_pack gives for
+ * that tensor alone; Q and K share x_dtype, sizes and mode.
+ *
+ *  q, k              [B,H,n,d] of x_dtype
+ *  qbits, kbits      out uint32 [B,H,n,d/32]
+ *  alpha_q, alpha_k  out float32 [B,H,n] (required for MEAN_SIGN, may be NULL for SIGN)
+ *  mu_q, mu_k        out float32 [B,H,d] (required for MEAN_SIGN, may be NULL for SIGN)
+ *  workspace, workspace_bytes: as for had_pack (the layout holds the column-sum
+ *           partials of both tensors).
+ * Errors: as had_pack.  Buffers are caller-owned; nothing is allocated.
+ */
+int had_pack_qk(const void* q, const void* k, int x_dtype, int64_t B, int64_t H, int64_t n, int64_t d, int mode,
+                uint32_t* qbits, uint32_t* kbits, float* alpha_q, float* alpha_k, float* mu_q, float* mu_k,
+                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * had_attention_topn -- attention over each query's top-N keys.

@@ -91,6 +91,27 @@ def test_pack_validation(args, want):
 
 @pytest.mark.parametrize("args,want", [
     (dict(q=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(k=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(kbits=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(H=0), _lib.HAD_ERR_INVALID_ARG),
+    (dict(mode=3), _lib.HAD_ERR_INVALID_ARG),
+    (dict(d=96), _lib.HAD_ERR_UNSUPPORTED),
+    (dict(mode=1, mu_k=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(mode=1, ws=None), _lib.HAD_ERR_WORKSPACE),
+    (dict(mode=1, wsz=64), _lib.HAD_ERR_WORKSPACE),
+])
+def test_pack_qk_validation(args, want):
+    a = dict(q=FAKE, k=FAKE, dtype=_lib.HAD_F32, B=1, H=2, n=64, d=64, mode=0, qbits=FAKE, kbits=FAKE,
+             alpha_q=FAKE, alpha_k=FAKE, mu_q=FAKE, mu_k=FAKE, ws=FAKE, wsz=1 << 30)
+    a.update(args)
+    st = _lib.load().had_pack_qk(a["q"], a["k"], a["dtype"], a["B"], a["H"], a["n"], a["d"], a["mode"],
+                                 a["qbits"], a["kbits"], a["alpha_q"], a["alpha_k"], a["mu_q"], a["mu_k"],
+                                 a["ws"], a["wsz"], None)
+    assert st == want
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(q=None), _lib.HAD_ERR_INVALID_ARG),
     (dict(v=None), _lib.HAD_ERR_INVALID_ARG),
     (dict(out=None), _lib.HAD_ERR_INVALID_ARG),
     (dict(top_n=0), _lib.HAD_ERR_INVALID_ARG),

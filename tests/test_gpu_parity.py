@@ -57,6 +57,29 @@ def test_pack_ragged_and_special_values(d, n, dtype, mode):
     assert np.array_equal(mu.cpu().numpy(), om)
 
 
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("n", [1, 100, 197, 700])
+@pytest.mark.parametrize("mode", [synth.SIGN, synth.MEAN_SIGN])
+def test_pack_qk_matches_oracle_and_pack(d, n, mode):
+    """had_pack_qk: both tensors exactly as the oracle (and had_pack) gives them, across the
+    one-launch-per-pass path (n >= rows per workgroup, few chunks) and the separate-mu path."""
+    g = np.random.default_rng([5, d, n, mode])
+    xq = (g.standard_normal((2, 3, n, d)) + g.standard_normal((1, 3, 1, d))).astype(np.float32)
+    xk = (0.5 * g.standard_normal((2, 3, n, d)) - g.standard_normal((1, 3, 1, d))).astype(np.float32)
+    xq[1, 2, :, 3] = 0.25  # a constant channel: x - mu is exactly 0 there
+    q, k = torch.from_numpy(xq).to(torch.bfloat16), torch.from_numpy(xk).to(torch.bfloat16)
+    (qb, aq, mq), (kb, ak, mk) = ops.had_pack_qk(q.to(DEV), k.to(DEV), mode)
+    pq = ops.had_pack(q.to(DEV), mode)
+    torch.cuda.synchronize()
+    for got, x, one in (((qb, aq, mq), q, pq), ((kb, ak, mk), k, None)):
+        ob, oa, om = oracle.pack(f32(x), mode)
+        assert np.array_equal(u32(got[0]), ob), "code bits differ"
+        assert np.array_equal(got[1].cpu().numpy(), oa), "alpha differs"
+        assert np.array_equal(got[2].cpu().numpy(), om), "mu differs"
+        if one is not None:
+            assert np.array_equal(u32(one[0]), u32(got[0]))
+
+
 # ------------------------------------------------------------------ top-N, fp32 A*V
 def _topn_case(B, H, n, N, vdtype, mode, bias, seed, av=synth.AV_F32):
     g = np.random.default_rng([11, B, H, n, N, seed])
