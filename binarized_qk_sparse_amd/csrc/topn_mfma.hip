@@ -193,6 +193,7 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
     return b + ((want - (uint32_t)(uintptr_t)b) & 255u);
   };
 
+  __builtin_amdgcn_s_setprio(3);
   const int lane = (int)lane_id();
   const int g = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -498,6 +499,12 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
       __syncthreads();
       if (rr + 1 < R) issue_round(rr + 1);
     }
+    // Issue priority falls as a wave advances (3 in the first quarter of the rounds,
+    // 0 in the last): the workgroups sharing a CU then advance together instead of
+    // oldest first, and the SIMDs keep several waves to choose from to the end.
+    if (rr * 4 / R == 1) __builtin_amdgcn_s_setprio(2);
+    if (rr * 4 / R == 2 && (rr - 1) * 4 / R != 2) __builtin_amdgcn_s_setprio(1);
+    if (rr * 4 / R == 3 && (rr - 1) * 4 / R != 3) __builtin_amdgcn_s_setprio(0);
     if (have) {
       // step cl: A operands of cl, then the tie cut and table reads of cl + 1, the
       // products of cl, and the B reads of cl + 1
