@@ -129,6 +129,15 @@ HAD_DEVICE uint32_t lane_sad(const uint32_t (&P)[NW], uint32_t x) {
   return acc;
 }
 
+// x + (x << 8) + (x << 16) + (x << 24), as two shift-adds: the compiler would
+// otherwise fold the sum into a quarter-rate v_mul_lo_u32.
+HAD_DEVICE uint32_t byte_prefix(uint32_t x) {
+  uint32_t y, z;
+  asm("v_lshl_add_u32 %0, %1, 8, %1" : "=v"(y) : "v"(x));
+  asm("v_lshl_add_u32 %0, %1, 16, %1" : "=v"(z) : "v"(y));
+  return z;
+}
+
 HAD_DEVICE uint32_t bf16_rne_bits(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
@@ -176,6 +185,7 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   // index * 4 plus an immediate offset): the weight table and the byte -> eight
   // fp4 nibble tables of the codes.
   __shared__ __align__(16) uint32_t tab[256];
+  __shared__ __align__(16) uint32_t one_pairs[4];  // bf16 (1, 1) pairs: the all-ones B operand
   __shared__ __align__(16) uint32_t lut_k[256];  // key bits -> -x/2: bit 1 (x = -1) -> +0.5 (0x1), else -0.5 (0x9)
   __shared__ __align__(16) uint32_t lut_q[256];  // query bits -> x: bit 1 -> -1.0 (0xA), else +1.0 (0x2)
   // Two buffers: first the fp4 key operands (quarters 0, 1 in the first, 2, 3 in
@@ -234,6 +244,7 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
       ent = hi16 | (bf16_rne_bits(rest) << 16);
     }
     tab[e] = ent;
+    if (e < 4) one_pairs[e] = 0x3f803f80u;
     uint32_t nk = 0u, nq = 0u;
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
@@ -401,9 +412,8 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
   accz = f32x4{0.f, 0.f, 0.f, 0.f};
-  bf16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+  // (read from LDS once: a constant operand would be rematerialized at every step)
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(lds_u8*)one_pairs);
   // B operand of channel tile tt by two transposing reads: in each group of 16 lanes
   // (K group g), lane s points at row g KR + s / 4 (+ 8c + e0) and channels
   // 16 tt + 4 (s % 4) .. + 3; lane s then receives channel 16 tt + s of keys e0 .. e0 + 3
@@ -438,9 +448,9 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
       // keep the first take - run keys at tau of this step (bytes of E0, then E1)
       const uint32_t rem = (uint32_t)(take - run);
       const uint32_t x0 = E0 >> 7, x1 = E1 >> 7;
-      const uint32_t p0 = x0 + (x0 << 8) + (x0 << 16) + (x0 << 24);  // inclusive ranks
-      const uint32_t p1 = x1 + (x1 << 8) + (x1 << 16) + (x1 << 24) + (uint32_t)__builtin_popcount(E0) * kC;
-      const uint32_t ad = (127u - rem) * kC;  // bit 7: rank >= rem + 1
+      const uint32_t p0 = byte_prefix(x0);  // inclusive ranks
+      const uint32_t p1 = byte_prefix(x1) + byte_prefix((uint32_t)__builtin_popcount(E0));  // (a byte broadcast)
+      const uint32_t ad = byte_prefix(127u - rem);  // bit 7: rank >= rem + 1 (rem in [1, 7])
       U0 = E0 & (p0 + ad);
       U1 = E1 & (p1 + ad);
     }
