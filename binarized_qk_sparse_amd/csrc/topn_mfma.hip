@@ -138,6 +138,14 @@ HAD_DEVICE uint32_t byte_prefix(uint32_t x) {
   return z;
 }
 
+// (a ^ b) + c in one instruction (the compiler would rewrite ~((a ^ b) + c) as a
+// subtraction and a separate xor)
+HAD_DEVICE uint32_t xor_add(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t y;
+  asm("v_xad_u32 %0, %1, %2, %3" : "=v"(y) : "v"(a), "v"(b), "s"(c));
+  return y;
+}
+
 HAD_DEVICE uint32_t bf16_rne_bits(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
@@ -406,6 +414,8 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   const int before = quad_rows_excl(ceq, g);  // keys at tau in lower quarters
   const int take = min(max(keep - less - before, 0), ceq);
   const uint32_t kidx = (uint32_t)(65 - tau) * kC;
+  const uint32_t ktau = (uint32_t)tau * kC;
+  const uint32_t kcut = 127u - (uint32_t)take;
 
   // ------------------------------------------------ 4-5. weights and A*V
   f32x4 acc[4], accz;
@@ -436,27 +446,27 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   // in flight while the products of the previous step run.
   auto prep = [&](int rr, int cl, uint32_t (&ent)[8]) {
     const int c = rr * NKR + cl;
-    uint32_t I0 = P[2 * c] + kidx, I1 = P[2 * c + 1] + kidx;  // h - tau + 65 per byte
-    const uint32_t E0 = ((I0 + 63u * kC) ^ (I0 + 62u * kC)) & kM;  // h == tau
-    const uint32_t E1 = ((I1 + 63u * kC) ^ (I1 + 62u * kC)) & kM;
-    const int run1 = __builtin_popcount(E1) + (__builtin_popcount(E0) + run);
+    const uint32_t P0 = P[2 * c], P1 = P[2 * c + 1];
+    // keys at tau: a byte of (P ^ tau) + 0x7f has bit 7 clear exactly where h == tau
+    // (every byte of P ^ tau is below 0x80, so no carry crosses a byte)
+    const uint32_t E0 = ~xor_add(P0, ktau, 0x7f7f7f7fu) & kM;
+    const uint32_t E1 = ~xor_add(P1, ktau, 0x7f7f7f7fu) & kM;
+    const int mid = __builtin_popcount(E0) + run;
+    const int run1 = __builtin_popcount(E1) + mid;
     // keys at tau not taken: all of them once the lane's count passes take, the
     // first ones of this step kept where it passes take inside the step
-    const uint32_t over = run1 > take ? ~0u : 0u;
-    uint32_t U0 = E0 & over, U1 = E1 & over;
-    if (run < take && run1 > take) {
-      // keep the first take - run keys at tau of this step (bytes of E0, then E1)
-      const uint32_t rem = (uint32_t)(take - run);
-      const uint32_t x0 = E0 >> 7, x1 = E1 >> 7;
-      const uint32_t p0 = byte_prefix(x0);  // inclusive ranks
-      const uint32_t p1 = byte_prefix(x1) + byte_prefix((uint32_t)__builtin_popcount(E0));  // (a byte broadcast)
-      const uint32_t ad = byte_prefix(127u - rem);  // bit 7: rank >= rem + 1 (rem in [1, 7])
-      U0 = E0 & (p0 + ad);
-      U1 = E1 & (p1 + ad);
+    const bool over = run1 > take;
+    uint32_t U0 = over ? E0 : 0u, U1 = over ? E1 : 0u;
+    if (over && !(run >= take)) {
+      // a key at tau with inclusive rank k in its word is cut when run + k > take
+      // (mid + k for the second word): byte b of byte_prefix((E >> 7) + 127 - take + run)
+      // is 127 - take + run + rank_b, in [120, 134], with bit 7 set exactly then
+      U0 = E0 & byte_prefix((E0 >> 7) + kcut + (uint32_t)run);
+      U1 = E1 & byte_prefix((E1 >> 7) + kcut + (uint32_t)mid);
     }
     run = run1;
-    I0 |= U0;
-    I1 |= U1;
+    // h - tau + 65 per byte, plus 128 for a key at tau that is not taken
+    const uint32_t I0 = P0 + kidx + U0, I1 = P1 + kidx + U1;
     if (IDX && i < n) {
       // kept keys have a table index in [1, 65]
 #pragma unroll
