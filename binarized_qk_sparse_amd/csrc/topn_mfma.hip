@@ -232,14 +232,22 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   const uint32_t lrow = (uint32_t)lane >> 3;
   const uint32_t piece = (uint32_t)lane & 7u;
   const uint32_t vcol = 16u * (((piece >> 1) ^ vswz((uint32_t)wave, lrow))) + 8u * (piece & 1u);
+  // (the row part of the address is wave-uniform: a scalar base plus this lane's
+  // 32-bit offset, so the loads cost no vector address arithmetic)
+  const uint32_t lane_off = lrow * 128u + vcol * 2u;
   auto issue_round = [&](int rr) {
     lds_u8* buf = vbuf(rr) + wave * KR * 128;
 #pragma unroll
     for (int m = 0; m < KR / 8; ++m) {
-      int key = wave * KG + rr * KR + 8 * m + (int)lrow;
-      if (PAD) key = min(key, n - 1);
-      __builtin_amdgcn_global_load_lds(vh + (size_t)key * kD + vcol,
-                                       (lds_void*)(buf + m * 1024), 16, 0, 0);
+      const int key0 = wave * KG + rr * KR + 8 * m;  // this instruction's first row
+      const char* src;
+      if (PAD) {
+        const int key = min(key0 + (int)lrow, n - 1);
+        src = reinterpret_cast<const char*>(vh) + (size_t)key * (kD * 2) + vcol * 2u;
+      } else {
+        src = reinterpret_cast<const char*>(vh) + (size_t)key0 * (kD * 2) + lane_off;
+      }
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + m * 1024), 16, 0, 0);
     }
   };
   // ---- tables: softmax weights, and the fp4 nibbles of code bytes
