@@ -301,34 +301,41 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   int tau = 0, less = 0, cl_lo = 0, cl_hi = 0;
   if (have) {
     // ------------------------------------------------ 1. Hamming distances on the matrix cores
-    // v_mfma_scale_f32_16x16x128_f8f6f4 (fp4 operands, unit scales): row rho of A is
-    // key (rho / 4) KG + 4b + rho % 4 of block b as -x/2, column r of B is query r as
-    // +-1, K = the 64 dims (lanes of K-blocks 2, 3 carry zeros in B), C starts at 32:
-    // C = 32 - dot / 2 = h exactly (every partial sum is a multiple of 1/2 below 2^6).
-    // Lane (g, r) then holds the distances of query r to keys g KG + 4b + 0..3: one
-    // byte-packed word P[b].
+    // v_mfma_scale_f32_16x16x128_f8f6f4 (fp4 operands, unit scales): column r of B
+    // is query r as +-1 and C starts at 32, so C = 32 - dot / 2 = h exactly (every
+    // partial sum is a multiple of 1/2 below 2^6).  K holds two blocks of keys: lanes
+    // of K-blocks 0, 1 load the 64 dims of block b (keys (rho / 4) KG + 4b + rho % 4
+    // in row rho, as -x/2) and lanes of K-blocks 2, 3 those of block b + 1, so one LDS
+    // read serves two products: one with the query in K-blocks 0, 1 of B (zeros in
+    // 2, 3), the other with it in K-blocks 2, 3.  Lane (g, r) then holds the distances
+    // of query r to keys g KG + 4b + 0..3: one byte-packed word P[b].
     const uint32_t qw = (g & 1) ? q.y : q.x;
-    const bool qz = g >= 2;
-    v8i Bq;
-    Bq[0] = qz ? 0 : (int)lut_q[qw & 0xffu];
-    Bq[1] = qz ? 0 : (int)lut_q[(qw >> 8) & 0xffu];
-    Bq[2] = qz ? 0 : (int)lut_q[(qw >> 16) & 0xffu];
-    Bq[3] = qz ? 0 : (int)lut_q[qw >> 24];
-    Bq[4] = Bq[5] = Bq[6] = Bq[7] = 0;
-    const lds_u8* ka = kxq(r >> 2) + (r & 3) * 32 + (g & 1) * 16;
-    // eight independent products in flight before any result is read
+    const int q0 = (int)lut_q[qw & 0xffu], q1 = (int)lut_q[(qw >> 8) & 0xffu];
+    const int q2 = (int)lut_q[(qw >> 16) & 0xffu], q3 = (int)lut_q[qw >> 24];
+    const bool upper = g >= 2;
+    v8i Bq[2];  // query in K-blocks 0, 1 / in K-blocks 2, 3
+    Bq[0][0] = upper ? 0 : q0; Bq[0][1] = upper ? 0 : q1; Bq[0][2] = upper ? 0 : q2; Bq[0][3] = upper ? 0 : q3;
+    Bq[1][0] = upper ? q0 : 0; Bq[1][1] = upper ? q1 : 0; Bq[1][2] = upper ? q2 : 0; Bq[1][3] = upper ? q3 : 0;
+    Bq[0][4] = Bq[0][5] = Bq[0][6] = Bq[0][7] = 0;
+    Bq[1][4] = Bq[1][5] = Bq[1][6] = Bq[1][7] = 0;
+    const lds_u8* ka = kxq(r >> 2) + (r & 3) * 32 + (g & 1) * 16 + (g >> 1) * 128;
+    // eight independent products (four reads) in flight before any result is read
     constexpr int G = NW < 8 ? NW : 8;
+    static_assert(NW % 2 == 0 && G % 2 == 0, "products come in pairs");
 #pragma unroll
     for (int b0 = 0; b0 < NW; b0 += G) {
       f32x4 c[G];
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
+      for (int j = 0; j < G; j += 2) {
         const u32x4 av = *(const lds_u32x4*)(ka + (b0 + j) * 128);
         v8i A;
         A[0] = (int)av[0]; A[1] = (int)av[1]; A[2] = (int)av[2]; A[3] = (int)av[3];
         A[4] = A[5] = A[6] = A[7] = 0;
-        c[j] = f32x4{32.0f, 32.0f, 32.0f, 32.0f};
-        c[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bq, c[j], 4, 4, 0, 127, 0, 127);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          c[j + h] = f32x4{32.0f, 32.0f, 32.0f, 32.0f};
+          c[j + h] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bq[h], c[j + h], 4, 4, 0, 127, 0, 127);
+        }
       }
 #pragma unroll
       for (int j = 0; j < G; ++j) {
