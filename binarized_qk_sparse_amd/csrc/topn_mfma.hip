@@ -115,6 +115,9 @@ HAD_DEVICE int quad_rows_excl(int v, int g) {
   return s - v;
 }
 
+// x (below 256) in every byte: one byte permute instead of a quarter-rate multiply
+HAD_DEVICE uint32_t byte_bcast(uint32_t x) { return __builtin_amdgcn_perm(0u, x, 0u); }
+
 // Counts of this lane's keys with h <= t, from sums of absolute differences:
 // with S(x) = sum over the lane's keys of |h - x| (v_sad_u8, four byte-packed
 // distances per instruction), |h - (t+1)| - |h - t| is +1 for h <= t and -1
@@ -122,7 +125,7 @@ HAD_DEVICE int quad_rows_excl(int v, int g) {
 // exact small integers.
 template <int NW>
 HAD_DEVICE uint32_t lane_sad(const uint32_t (&P)[NW], uint32_t x) {
-  const uint32_t xb = x * kC;
+  const uint32_t xb = byte_bcast(x);
   uint32_t acc = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) acc = __builtin_amdgcn_sad_u8(P[w], xb, acc);
@@ -261,15 +264,15 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
     }
     tab[e] = ent;
     if (e < 4) one_pairs[e] = 0x3f803f80u;
-    uint32_t nk = 0u, nq = 0u;
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const bool neg = (e >> b) & 1;
-      nk |= (neg ? 0x1u : 0x9u) << (4 * b);
-      nq |= (neg ? 0xAu : 0x2u) << (4 * b);
-    }
-    lut_k[e] = nk;
-    lut_q[e] = nq;
+    // bit b of e to bit 4b (three shift-or-mask steps), then to bit 3 of nibble b:
+    // a set code bit turns 0x9 (-0.5) into 0x1 (+0.5) for keys, 0x2 (+1) into 0xA (-1)
+    // for queries
+    uint32_t sp = (uint32_t)e;
+    sp = (sp | (sp << 12)) & 0x000f000fu;
+    sp = (sp | (sp << 6)) & 0x03030303u;
+    sp = (sp | (sp << 3)) & 0x11111111u;
+    lut_k[e] = 0x99999999u ^ (sp << 3);
+    lut_q[e] = 0x22222222u ^ (sp << 3);
   }
   // the codes: the query of this lane, and the keys this thread expands (loaded
   // before any direct-to-LDS load, whose presence makes every wait a full wait)
@@ -428,8 +431,8 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   const int ceq = cl_hi - cl_lo;              // this lane's keys at tau
   const int before = quad_rows_excl(ceq, g);  // keys at tau in lower quarters
   const int take = min(max(keep - less - before, 0), ceq);
-  const uint32_t kidx = (uint32_t)(65 - tau) * kC;
-  const uint32_t ktau = (uint32_t)tau * kC;
+  const uint32_t kidx = byte_bcast((uint32_t)(65 - tau));
+  const uint32_t ktau = byte_bcast((uint32_t)tau);
   const uint32_t kcut = 127u - (uint32_t)take;
 
   // ------------------------------------------------ 4-5. weights and A*V
