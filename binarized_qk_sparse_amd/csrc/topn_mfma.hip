@@ -304,57 +304,67 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   int tau = 0, less = 0, cl_lo = 0, cl_hi = 0;
   if (have) {
     // ------------------------------------------------ 1. Hamming distances on the matrix cores
-    // v_mfma_scale_f32_16x16x128_f8f6f4 (fp4 operands, unit scales): column r of B
-    // is query r as +-1 and C starts at 32, so C = 32 - dot / 2 = h exactly (every
-    // partial sum is a multiple of 1/2 below 2^6).  K holds two blocks of keys: lanes
-    // of K-blocks 0, 1 load the 64 dims of block b (keys (rho / 4) KG + 4b + rho % 4
-    // in row rho, as -x/2) and lanes of K-blocks 2, 3 those of block b + 1, so one LDS
-    // read serves two products: one with the query in K-blocks 0, 1 of B (zeros in
-    // 2, 3), the other with it in K-blocks 2, 3.  Lane (g, r) then holds the distances
-    // of query r to keys g KG + 4b + 0..3: one byte-packed word P[b].
+    // v_mfma_scale_f32_16x16x128_f8f6f4 on fp4 operands: column r of B is query r as
+    // +-1 in all four K-blocks, and row rho of A holds two blocks of keys: K-blocks
+    // 0, 1 the 64 dims of key (rho / 4) KG + 4b + rho % 4 as -x/2, K-blocks 2, 3 those
+    // of the same key of block b + 1, the latter scaled by 2^8 (the per-block E8M0
+    // scale of A).  From C = 2^22 + 32 + 256 * 32, the product is
+    //   C = 2^22 + h(b) + 256 h(b + 1)
+    // exactly: every partial sum is a multiple of 1/2 below 2^23, where fp32 steps by
+    // 1/2.  The float's bits are then 0x4A800000 + 2 h(b) + 512 h(b + 1): byte 0
+    // holds 2 h(b) and byte 1 holds 2 h(b + 1).  One LDS read and one product give
+    // the distances of two key blocks; byte permutes gather them and a shift halves
+    // them.  Lane (g, r) ends with the distances of query r to keys g KG + 4b + 0..3:
+    // one byte-packed word P[b].
     const uint32_t qw = (g & 1) ? q.y : q.x;
-    const int q0 = (int)lut_q[qw & 0xffu], q1 = (int)lut_q[(qw >> 8) & 0xffu];
-    const int q2 = (int)lut_q[(qw >> 16) & 0xffu], q3 = (int)lut_q[qw >> 24];
-    const bool upper = g >= 2;
-    v8i Bq[2];  // query in K-blocks 0, 1 / in K-blocks 2, 3
-    Bq[0][0] = upper ? 0 : q0; Bq[0][1] = upper ? 0 : q1; Bq[0][2] = upper ? 0 : q2; Bq[0][3] = upper ? 0 : q3;
-    Bq[1][0] = upper ? q0 : 0; Bq[1][1] = upper ? q1 : 0; Bq[1][2] = upper ? q2 : 0; Bq[1][3] = upper ? q3 : 0;
-    Bq[0][4] = Bq[0][5] = Bq[0][6] = Bq[0][7] = 0;
-    Bq[1][4] = Bq[1][5] = Bq[1][6] = Bq[1][7] = 0;
+    v8i Bq;
+    Bq[0] = (int)lut_q[qw & 0xffu];
+    Bq[1] = (int)lut_q[(qw >> 8) & 0xffu];
+    Bq[2] = (int)lut_q[(qw >> 16) & 0xffu];
+    Bq[3] = (int)lut_q[qw >> 24];
+    Bq[4] = Bq[5] = Bq[6] = Bq[7] = 0;
+    const int scale_a = g >= 2 ? 127 + 8 : 127;  // E8M0: 2^8 for block b + 1
     const lds_u8* ka = kxq(r >> 2) + (r & 3) * 32 + (g & 1) * 16 + (g >> 1) * 128;
-    // eight independent products (four reads) in flight before any result is read
+    // four independent products (eight key blocks) in flight before any result is read
     constexpr int G = NW < 8 ? NW : 8;
-    static_assert(NW % 2 == 0 && G % 2 == 0, "products come in pairs");
+    static_assert(NW % 2 == 0 && G % 2 == 0, "key blocks come in pairs");
+    constexpr float kC0 = 4194304.0f + 32.0f + 256.0f * 32.0f;
 #pragma unroll
     for (int b0 = 0; b0 < NW; b0 += G) {
-      f32x4 c[G];
+      f32x4 c[G / 2];
 #pragma unroll
-      for (int j = 0; j < G; j += 2) {
-        const u32x4 av = *(const lds_u32x4*)(ka + (b0 + j) * 128);
+      for (int j = 0; j < G / 2; ++j) {
+        const u32x4 av = *(const lds_u32x4*)(ka + (b0 + 2 * j) * 128);
         v8i A;
         A[0] = (int)av[0]; A[1] = (int)av[1]; A[2] = (int)av[2]; A[3] = (int)av[3];
         A[4] = A[5] = A[6] = A[7] = 0;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          c[j + h] = f32x4{32.0f, 32.0f, 32.0f, 32.0f};
-          c[j + h] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bq[h], c[j + h], 4, 4, 0, 127, 0, 127);
-        }
+        c[j] = f32x4{kC0, kC0, kC0, kC0};
+        c[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bq, c[j], 4, 4, 0, scale_a, 0, 127);
       }
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const int b = b0 + j;
-        uint32_t word = __builtin_amdgcn_cvt_pk_u8_f32(c[j][0], 0, 0u);
-        word = __builtin_amdgcn_cvt_pk_u8_f32(c[j][1], 1, word);
-        word = __builtin_amdgcn_cvt_pk_u8_f32(c[j][2], 2, word);
-        word = __builtin_amdgcn_cvt_pk_u8_f32(c[j][3], 3, word);
-        if (PAD) {
-          // padding keys (j >= n) get a byte of at least 65, above every real distance:
-          // h | 0x41 lies in [65, 127], which keeps all byte sums below carry
-          const int real = n - (g * KG + 4 * b);  // real keys in this word
-          const uint32_t pm = real >= 4 ? 0u : (real <= 0 ? 0x41414141u : (0x41414141u << (8 * real)));
-          word |= pm;
+      for (int j = 0; j < G / 2; ++j) {
+        // (elements copied out first: a bit cast of a vector element reads element 0)
+        const float e0 = c[j][0], e1 = c[j][1], e2 = c[j][2], e3 = c[j][3];
+        const uint32_t f0 = __builtin_bit_cast(uint32_t, e0), f1 = __builtin_bit_cast(uint32_t, e1);
+        const uint32_t f2 = __builtin_bit_cast(uint32_t, e2), f3 = __builtin_bit_cast(uint32_t, e3);
+        const uint32_t t01 = __builtin_amdgcn_perm(f1, f0, 0x05010400u);  // 2h: b.0, b.1, b+1.0, b+1.1
+        const uint32_t t23 = __builtin_amdgcn_perm(f3, f2, 0x05010400u);  // 2h: b.2, b.3, b+1.2, b+1.3
+        uint32_t w2[2];
+        w2[0] = __builtin_amdgcn_perm(t23, t01, 0x05040100u) >> 1;  // (every byte of 2h is even)
+        w2[1] = __builtin_amdgcn_perm(t23, t01, 0x07060302u) >> 1;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int b = b0 + 2 * j + h2;
+          uint32_t word = w2[h2];
+          if (PAD) {
+            // padding keys (j >= n) get a byte of at least 65, above every real distance:
+            // h | 0x41 lies in [65, 127], which keeps all byte sums below carry
+            const int real = n - (g * KG + 4 * b);  // real keys in this word
+            const uint32_t pm = real >= 4 ? 0u : (real <= 0 ? 0x41414141u : (0x41414141u << (8 * real)));
+            word |= pm;
+          }
+          P[b] = word;
         }
-        P[b] = word;
       }
     }
   }
@@ -490,7 +500,7 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
 #pragma unroll
       for (int b = 0; b < 8; ++b) {
         const uint32_t ib = ((b < 4 ? I0 : I1) >> (8 * (b & 3))) & 0xffu;
-        if (ib <= 65u) idst[ipos++] = g * KG + 8 * c + b;
+        if (ib <= 65u && ipos < keep) idst[ipos++] = g * KG + 8 * c + b;
       }
     }
     // table entries (hi | lo << 16) of the eight keys
