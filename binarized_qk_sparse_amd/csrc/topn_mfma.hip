@@ -1,5 +1,6 @@
 // Top-N binarized attention with integer logits (alpha = 1, no bias) and bf16
-// V, for n <= 1024: exact top-N selection on VALU, A*V on bf16 matrix cores.
+// V, for n <= 1024: distances and A*V on the matrix cores, exact top-N
+// selection on VALU.
 //
 // Method (Hamming Attention Distillation, summary "main points"/"method";
 // BinaryAttention sections 2.2-2.3):
@@ -16,13 +17,14 @@
 // [g Q, (g+1) Q), Q = n_pad / 4): the same (row, key) split as the A operand
 // of v_mfma_f32_16x16x32_bf16, so no data moves between selection and the
 // matrix cores.
-//   1. Hamming distances: each lane loads one key code per 16 keys and the
-//      16 lanes of a row share them through DPP row broadcasts, folded into
-//      the XOR (v_xor_b32_dpp row_newbcast); v_bcnt_u32_b32 accumulates the
-//      two words.  Distances are byte-packed four to a register.
-//   2. Threshold: per-lane SWAR counts (add / and / popcount, four keys per
-//      instruction) summed over the query's four lanes, starting from a guess
-//      and bracketing per lane.
+//   1. Hamming distances on fp4 matrix cores: the workgroup expands the head's
+//      key codes once into LDS as fp4 operands (-x/2), each wave multiplies them
+//      by its queries (+-1) with v_mfma_scale_f32_16x16x128_f8f6f4, two key
+//      blocks per product (the second scaled by 2^8), and byte permutes pack
+//      the exact distances four to a register.
+//   2. Threshold: per-lane counts from sums of absolute differences (v_sad_u8,
+//      four keys per instruction) summed over the query's four lanes, starting
+//      from a guess, bracketing and bisecting.
 //   3. Ties: each lane takes its share of the keys at tau, lowest j first
 //      (exclusive prefix over the four quarters, then a running count over the
 //      lane's keys in ascending order).
