@@ -579,7 +579,7 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int row = t * 16 + 4 * g + e;
-    const float inv = 1.0f / accz[e];
+    const float inv = __builtin_amdgcn_rcpf(accz[e]);  // (1 ulp; Z >= 1: the weight at tau is 1)
     if (row < n) {
       float* o = a.out + (hb + row) * kD + r;
 #pragma unroll
