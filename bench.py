@@ -152,13 +152,17 @@ def cpu_baseline(w, g, budget_s: float):
 
 def measured_ceilings(torch, dev) -> dict:
     """Measured ceilings beside the datasheet peaks: integer VALU (independent XOR + popcount
-    chains, 2 lane-ops per step, libhad_ubench.so), v_exp_f32, and a 256 MiB device copy."""
+    chains, 2 lane-ops per step, libhad_ubench.so), v_exp_f32, a 256 MiB device copy, and the
+    VALU issue cycles one 16x16x32 bf16 matrix-core product takes from its SIMD (the same VALU
+    chains with and without ten products per loop, three waves per SIMD)."""
     import ctypes
 
     lib = ctypes.CDLL(os.path.join(ROOT, "binarized_qk_sparse_amd", "libhad_ubench.so"))
     for f in (lib.hub_xor_bcnt, lib.hub_exp):
         f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         f.restype = ctypes.c_int
+    lib.hub_coissue.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.hub_coissue.restype = ctypes.c_int
     blocks, iters = 256 * 16, 1024
     out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
@@ -178,6 +182,13 @@ def measured_ceilings(torch, dev) -> dict:
     s = stream.cuda_stream
     t_x = timed(lambda: lib.hub_xor_bcnt(out.data_ptr(), blocks, iters, s))
     t_e = timed(lambda: lib.hub_exp(out.data_ptr(), blocks, iters, s))
+    # three workgroups of four waves per CU: three waves per SIMD, as in the top-N kernel
+    cblocks, citers = 256 * 3, 512
+    t_v = timed(lambda: lib.hub_coissue(out.data_ptr(), cblocks, citers, 0, s))
+    t_vm = timed(lambda: lib.hub_coissue(out.data_ptr(), cblocks, citers, 1, s))
+    simd_valu = cblocks * 4 * citers * 120 / 1024  # VALU instructions per SIMD
+    clock = simd_valu * 4 / t_v  # the VALU-only loop keeps the issue port busy
+    simd_mfma = cblocks * 4 * citers * 10 / 1024
     nbytes = 256 << 20
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -189,6 +200,7 @@ def measured_ceilings(torch, dev) -> dict:
         "clock_ghz_at_full_valu": valu / (256 * 64) / 1e9,
         "exp_t_per_s": blocks * 256 * iters * 8 / t_e / 1e12,
         "copy_gb_per_s": 2 * nbytes / t_c / 1e9,
+        "mfma_valu_issue_cycles": (t_vm - t_v) * clock / simd_mfma,
     }
 
 

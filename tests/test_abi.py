@@ -27,14 +27,18 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_ceiling_library_loads_and_exports():
-    """libhad_ubench.so (the measured VALU, v_exp and copy ceilings bench.py reports) is built beside
-    libhad.so and exports its two launchers; it rejects bad sizes before any launch."""
+    """libhad_ubench.so (the measured VALU, v_exp, co-issue and copy ceilings bench.py reports) is
+    built beside libhad.so and exports its three launchers; they reject bad sizes before any launch."""
     lib = ctypes.CDLL(os.path.join(ROOT, "binarized_qk_sparse_amd", "libhad_ubench.so"))
     for name in ("hub_xor_bcnt", "hub_exp"):
         f = getattr(lib, name)
         f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         assert f(None, 1, 1, None) == 1
         assert f(ctypes.c_void_p(256), 0, 1, None) == 1
+    f = lib.hub_coissue
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert f(None, 1, 1, 1, None) == 1
+    assert f(ctypes.c_void_p(256), 1, 0, 0, None) == 1
 
 
 def test_header_constants_match_binding():
