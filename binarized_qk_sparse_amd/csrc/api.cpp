@@ -78,13 +78,17 @@ int check_attention(const uint32_t* qbits, const uint32_t* kbits, const void* v,
     return fail(HAD_ERR_INVALID_ARG, fn, "NULL tensor");
   if (!sizes_ok(B, H, n, d)) return fail(HAD_ERR_INVALID_ARG, fn, "sizes must be positive and B*H*n*d < 2^31");
   if (v_dtype != HAD_F32 && v_dtype != HAD_BF16) return fail(HAD_ERR_INVALID_ARG, fn, "unknown v_dtype");
-  if (d != 64) return fail(HAD_ERR_UNSUPPORTED, fn, "attention kernels take d = 64");
+  if (d != 64 && d != 128) return fail(HAD_ERR_UNSUPPORTED, fn, "attention kernels take d = 64 or 128");
   if (n > HAD_MAX_N) return fail(HAD_ERR_UNSUPPORTED, fn, "n above HAD_MAX_N");
   return HAD_OK;
 }
 
-// Largest n the top-N kernel handles (V of one head staged in LDS).
-int64_t topn_max_n(int v_kind) { return v_kind == 0 ? 512 : 1024; }
+// Largest n the resident top-N kernels handle (V of one head staged in LDS; at
+// head_dim 128 the rows are twice as long).
+int64_t topn_max_n(int v_kind, int64_t d) {
+  const int64_t base = v_kind == 0 ? 512 : 1024;
+  return d == 128 ? base / 2 : base;
+}
 
 }  // namespace
 
@@ -183,7 +187,7 @@ int had_attention_topn(const uint32_t* qbits, const uint32_t* kbits, const float
   const int64_t keep = top_n < n ? top_n : n;
   if (keep > HAD_MAX_TOPN) return fail(HAD_ERR_UNSUPPORTED, fn, "min(top_n, n) above HAD_MAX_TOPN");
   const int v_kind = av_mode == HAD_AV_Q8 ? 2 : (v_dtype == HAD_BF16 ? 1 : 0);
-  const bool streaming = n > topn_max_n(v_kind);
+  const bool streaming = n > topn_max_n(v_kind, d);
   if (streaming && keep > topn_stream_max_keep())
     return fail(HAD_ERR_UNSUPPORTED, fn, "min(top_n, n) too large for the long-sequence kernel");
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -27,7 +27,7 @@
 namespace had {
 namespace {
 
-constexpr int kD = 64;
+// head_dim D is 64 or 128 (codes of D / 32 words, D / 16 channel tiles)
 constexpr int kWaves = 4;
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -54,13 +54,14 @@ HAD_DEVICE float row4_sum(float v) {
   return v + __shfl_xor(v, 32, 64);
 }
 
-template <int NK, bool BIAS>  // key steps of 32; NPAD = 32 * NK >= n
+template <int NK, bool BIAS, int D>  // key steps of 32; NPAD = 32 * NK >= n
 __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
   constexpr int NPAD = 32 * NK;
-  __shared__ __align__(16) int8_t vqt[kD][NPAD];  // Vq transposed: [channel][key]
-  __shared__ __align__(16) uint2 kcode[NPAD];
+  constexpr int NT = D / 16;  // channel tiles
+  __shared__ __align__(16) int8_t vqt[D][NPAD];  // Vq transposed: [channel][key]
+  __shared__ __align__(16) Code<D> kcode[NPAD];
   __shared__ __align__(16) float akk[NPAD];
-  __shared__ int colsum[kD];
+  __shared__ int colsum[D];
   extern __shared__ float biasw[];  // [2n - 1 + NPAD]: the table, then zeros read by padding keys
 
   const int tid = threadIdx.x;
@@ -69,17 +70,20 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
   const int n = a.n;
 
   // ---- stage codes, scales, bias table and the transposed int8 V of this head
-  const uint2* kb = reinterpret_cast<const uint2*>(a.kbits) + (size_t)bh * n;
   for (int j = tid; j < NPAD; j += 256) {
-    kcode[j] = j < n ? kb[j] : make_uint2(0u, 0u);
+    Code<D> c = load_code<D>(a.kbits, (size_t)bh * n + (j < n ? j : 0));
+    if (j >= n)
+#pragma unroll
+      for (int w = 0; w < D / 32; ++w) c.w[w] = 0u;
+    kcode[j] = c;
     akk[j] = (j < n && a.ak != nullptr) ? a.ak[(size_t)bh * n + j] : 1.0f;
   }
   if (BIAS)
     for (int o = tid; o < 2 * n - 1 + NPAD; o += 256)
       biasw[o] = o < 2 * n - 1 ? a.bias[(size_t)hh * (2 * n - 1) + o] : 0.0f;
-  const uint32_t* vsrc = reinterpret_cast<const uint32_t*>(a.vq + (size_t)bh * n * kD);
-  for (int e = tid; e < NPAD * (kD / 4); e += 256) {
-    const int j = e / (kD / 4), c4 = 4 * (e % (kD / 4));
+  const uint32_t* vsrc = reinterpret_cast<const uint32_t*>(a.vq + (size_t)bh * n * D);
+  for (int e = tid; e < NPAD * (D / 4); e += 256) {
+    const int j = e / (D / 4), c4 = 4 * (e % (D / 4));
     const uint32_t w = j < n ? vsrc[e] : 0u;
     vqt[c4 + 0][j] = (int8_t)(w);
     vqt[c4 + 1][j] = (int8_t)(w >> 8);
@@ -87,7 +91,7 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
     vqt[c4 + 3][j] = (int8_t)(w >> 24);
   }
   __syncthreads();
-  if (tid < kD) {
+  if (tid < D) {
     int s = 0;
     for (int j = 0; j < NPAD; ++j) s += vqt[tid][j];
     colsum[tid] = s;
@@ -102,7 +106,7 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
     const int i = tile * 16 + r16;  // this lane's query row (may be padding)
     const int iq = i < n ? i : n - 1;
     const size_t row = (size_t)bh * n + iq;
-    const uint2 qq = reinterpret_cast<const uint2*>(a.qbits)[row];
+    const Code<D> qq = load_code<D>(a.qbits, row);
     const float aqv = a.aq != nullptr ? a.aq[row] : 1.0f;
     const float* brow = biasw + (n - 1 - iq);  // bias of key j is brow[j]
 
@@ -115,10 +119,9 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int j = j0 + e;
-        const uint2 kk = kcode[j];
-        const int h = __builtin_popcount(qq.x ^ kk.x) + __builtin_popcount(qq.y ^ kk.y);
+        const int h = hamming<D>(qq, kcode[j]);
         const float b = BIAS ? brow[j] : 0.0f;
-        float l = canonical_logit(aqv, akk[j], kD - 2 * h, a.isd, b);
+        float l = canonical_logit(aqv, akk[j], D - 2 * h, a.isd, b);
         if (ks == NK - 1) l = j < n ? l : -INFINITY;  // only the last step holds padding keys
         lg[ks][e] = l;
         m = fmaxf(m, l);
@@ -139,7 +142,9 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
     const float q255 = 255.0f / row4_sum(z);
 
     // ---- quantize A and contract on the matrix cores
-    v4i acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+    v4i acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = v4i{0, 0, 0, 0};
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
       uint32_t w[2] = {0u, 0u};
@@ -152,7 +157,7 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
       const long A = (long)(((uint64_t)w[1] << 32) | w[0]);
       const int kk0 = ks * 32 + kg * 8;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         const long B = *reinterpret_cast<const long*>(&vqt[nt * 16 + r16][kk0]);
         acc[nt] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, acc[nt], 0, 0, 0);
       }
@@ -161,29 +166,34 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
 
     // ---- dequantize and store
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       const int c = nt * 16 + r16;
-      const float sc = a.vscale[(size_t)bh * kD + c];
+      const float sc = a.vscale[(size_t)bh * D + c];
       const int cs = 128 * colsum[c];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int orow = tile * 16 + 4 * kg + r;
         if (orow < n)
-          a.out[((size_t)bh * n + orow) * kD + c] = __fdiv_rn(__fmul_rn((float)(acc[nt][r] + cs), sc), 255.0f);
+          a.out[((size_t)bh * n + orow) * D + c] = __fdiv_rn(__fmul_rn((float)(acc[nt][r] + cs), sc), 255.0f);
       }
     }
   }
 }
 
-template <int NK>
-hipError_t launch_nk(const DenseKArgs& ka, int64_t BH, hipStream_t s) {
+template <int NK, int D>
+hipError_t launch_nkd(const DenseKArgs& ka, int64_t BH, hipStream_t s) {
   if (ka.bias != nullptr) {
     const size_t lds = sizeof(float) * (2 * ka.n - 1 + 32 * NK);
-    hipLaunchKernelGGL((dense_q8_kernel<NK, true>), dim3((unsigned)BH), dim3(64 * kWaves), lds, s, ka);
+    hipLaunchKernelGGL((dense_q8_kernel<NK, true, D>), dim3((unsigned)BH), dim3(64 * kWaves), lds, s, ka);
   } else {
-    hipLaunchKernelGGL((dense_q8_kernel<NK, false>), dim3((unsigned)BH), dim3(64 * kWaves), 0, s, ka);
+    hipLaunchKernelGGL((dense_q8_kernel<NK, false, D>), dim3((unsigned)BH), dim3(64 * kWaves), 0, s, ka);
   }
   return hipGetLastError();
+}
+
+template <int NK>
+hipError_t launch_nk(const DenseKArgs& ka, int d, int64_t BH, hipStream_t s) {
+  return d == 128 ? launch_nkd<NK, 128>(ka, BH, s) : launch_nkd<NK, 64>(ka, BH, s);
 }
 
 }  // namespace
@@ -192,7 +202,7 @@ hipError_t launch_nk(const DenseKArgs& ka, int64_t BH, hipStream_t s) {
 int64_t dense_q8_max_n() { return 256; }
 
 hipError_t launch_dense_q8(const AttnParams& p, hipStream_t s) {
-  if (p.d != kD || p.n > dense_q8_max_n()) return hipErrorInvalidValue;
+  if ((p.d != 64 && p.d != 128) || p.n > dense_q8_max_n()) return hipErrorInvalidValue;
   DenseKArgs ka{};
   ka.qbits = p.qbits;
   ka.kbits = p.kbits;
@@ -208,14 +218,14 @@ hipError_t launch_dense_q8(const AttnParams& p, hipStream_t s) {
   const int nk = (int)((p.n + 31) / 32);
   const int64_t BH = p.B * p.H;
   switch (nk) {
-    case 1: return launch_nk<1>(ka, BH, s);
-    case 2: return launch_nk<2>(ka, BH, s);
-    case 3: return launch_nk<3>(ka, BH, s);
-    case 4: return launch_nk<4>(ka, BH, s);
-    case 5: return launch_nk<5>(ka, BH, s);
-    case 6: return launch_nk<6>(ka, BH, s);
-    case 7: return launch_nk<7>(ka, BH, s);
-    default: return launch_nk<8>(ka, BH, s);
+    case 1: return launch_nk<1>(ka, (int)p.d, BH, s);
+    case 2: return launch_nk<2>(ka, (int)p.d, BH, s);
+    case 3: return launch_nk<3>(ka, (int)p.d, BH, s);
+    case 4: return launch_nk<4>(ka, (int)p.d, BH, s);
+    case 5: return launch_nk<5>(ka, (int)p.d, BH, s);
+    case 6: return launch_nk<6>(ka, (int)p.d, BH, s);
+    case 7: return launch_nk<7>(ka, (int)p.d, BH, s);
+    default: return launch_nk<8>(ka, (int)p.d, BH, s);
   }
 }
 

@@ -146,6 +146,40 @@ HAD_DEVICE float canonical_logit(float aq, float ak, int dot, float inv_sqrt_d, 
   return __fadd_rn(v, bias);
 }
 
+// The packed code of one token for head_dim D: D / 32 words, bit c % 32 of word
+// c / 32 set for a -1 code (the layout had_pack writes).
+template <int D>
+struct Code {
+  uint32_t w[D / 32];
+};
+
+template <int D>
+HAD_DEVICE Code<D> load_code(const uint32_t* base, size_t row) {
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  Code<D> c;
+  if constexpr (D == 64) {
+    const uint2 v = reinterpret_cast<const uint2*>(base)[row];
+    c.w[0] = v.x;
+    c.w[1] = v.y;
+  } else {
+    const uint4 v = reinterpret_cast<const uint4*>(base)[row];
+    c.w[0] = v.x;
+    c.w[1] = v.y;
+    c.w[2] = v.z;
+    c.w[3] = v.w;
+  }
+  return c;
+}
+
+// Hamming distance of two codes.
+template <int D>
+HAD_DEVICE int hamming(const Code<D>& x, const Code<D>& y) {
+  int h = 0;
+#pragma unroll
+  for (int w = 0; w < D / 32; ++w) h = __builtin_popcount(x.w[w] ^ y.w[w]) + h;
+  return h;
+}
+
 // XCD-aware remap of the linear workgroup id: consecutive logical ids land on
 // the same XCD (hardware dispatches workgroup w to XCD w % 8), so the blocks
 // that share a head's keys and values share one L2.

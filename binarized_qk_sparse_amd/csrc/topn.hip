@@ -43,7 +43,7 @@
 namespace had {
 namespace {
 
-constexpr int kD = 64;      // head_dim of these kernels
+// head_dim D is 64 (codes of two words; every path) or 128 (four words; float keys)
 constexpr int kQTile = 64;  // queries per workgroup tile
 constexpr int kMaxWaves = 16;
 constexpr uint32_t kLdsBytes = 160 * 1024;
@@ -64,10 +64,11 @@ struct TopnKArgs {
   uint32_t list_off, cand_off, bias_off, red_off, keys_off, trash_off;
 };
 
-template <int VK>
+template <int VK, int D>
 constexpr int row_bytes() {
-  return VK == 0 ? kD * 4 : (VK == 1 ? kD * 2 : kD);
+  return VK == 0 ? D * 4 : (VK == 1 ? D * 2 : D);
 }
+
 
 // Uniform: number of keys j (over all lanes and slots) with hv <= t, t in [0, 64].
 // Distances are byte-packed four to a register; a byte b satisfies b > t exactly
@@ -154,10 +155,12 @@ HAD_DEVICE void for_each16(const uint8_t* __restrict__ src, uint32_t total, F f)
   }
 }
 
-template <int NS, bool FK, int VK, bool PAD>
+template <int NS, bool FK, int VK, bool PAD, int D>
 __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) {
+  static_assert(D == 64 || (D == 128 && FK), "head_dim 128 takes the float-key path");
+  constexpr int W = D / 32;
   extern __shared__ __align__(16) uint8_t smem[];
-  constexpr int ROWB = row_bytes<VK>();
+  constexpr int ROWB = row_bytes<VK, D>();
   constexpr int NP = (NS + 3) / 4;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -171,18 +174,18 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
   uint32_t* trash = reinterpret_cast<uint32_t*>(smem + a.trash_off) + wave * 64;
   float* biasw = reinterpret_cast<float*>(smem + a.bias_off);
   uint32_t* red = reinterpret_cast<uint32_t*>(smem + a.red_off);
-  uint32_t k0[NS], k1[NS];
+  uint32_t kw[W][NS];  // key code words: word w of slot s
   float akv[NS];
   int staged = -1;
   float vmul = 1.0f;  // undoes the fp16 staging scale of V
   int tau_prev = 27;  // Hamming-level guess; each query starts from the last one's
-  uint2 qnext;
+  Code<D> qnext;
   float aqnext;
   {
     const int nbh = u0 / a.tiles, ni0 = (u0 % a.tiles) * a.qt;
     const bool ok = u0 < u1 && ni0 + lane < n;
     const size_t nrow = (size_t)nbh * n + ni0 + lane;
-    qnext = ok ? reinterpret_cast<const uint2*>(a.qbits)[nrow] : make_uint2(0u, 0u);
+    qnext = load_code<D>(a.qbits, ok ? nrow : 0);
     aqnext = (FK && a.aq != nullptr && ok) ? a.aq[nrow] : 1.0f;
   }
 
@@ -229,14 +232,13 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
       // ---- key codes.  Float keys: slot s of this lane is key 64 s + lane.  Integer
       // keys: slot s of lane l is key NS l + s (a lane holds consecutive keys).
       // PAD: keys j >= n are padding.
-      const uint2* kb = reinterpret_cast<const uint2*>(a.kbits) + (size_t)bh * n;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int j = FK ? 64 * s + lane : NS * lane + s;
         const bool ok = !PAD || j < n;
-        const uint2 kk = ok ? kb[j] : make_uint2(0u, 0u);
-        k0[s] = kk.x;
-        k1[s] = kk.y;
+        const Code<D> kk = load_code<D>(a.kbits, (size_t)bh * n + (ok ? j : 0));
+#pragma unroll
+        for (int w = 0; w < W; ++w) kw[w][s] = ok ? kk.w[w] : 0u;
         akv[s] = (FK && ok && a.ak != nullptr) ? a.ak[(size_t)bh * n + j] : 1.0f;
       }
     }
@@ -255,21 +257,22 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
     }
     // ---- the tile's query codes (and scales), one query per lane, read back with
     // v_readlane; the next unit's are fetched now so their latency hides behind this unit
-    const uint2 qlane = qnext;
+    const Code<D> qlane = qnext;
     const float aqlane = aqnext;
     if (u + 1 < u1) {
       const int nbh = (u + 1) / a.tiles, ni0 = ((u + 1) % a.tiles) * a.qt;
       const bool ok = ni0 + lane < n;
       const size_t nrow = (size_t)nbh * n + ni0 + lane;
-      qnext = ok ? reinterpret_cast<const uint2*>(a.qbits)[nrow] : make_uint2(0u, 0u);
+      qnext = load_code<D>(a.qbits, ok ? nrow : 0);
       aqnext = (FK && a.aq != nullptr && ok) ? a.aq[nrow] : 1.0f;
     }
     if (sync) __syncthreads();
 
   for (int i = i0 + wave; i < i1; i += nwaves) {
     const size_t row = (size_t)bh * n + i;
-    const uint32_t q0 = __builtin_amdgcn_readlane(qlane.x, i - i0);
-    const uint32_t q1 = __builtin_amdgcn_readlane(qlane.y, i - i0);
+    uint32_t qw[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) qw[w] = __builtin_amdgcn_readlane(qlane.w[w], i - i0);
     float ref = 0.0f;  // float keys: softmax reference (the row's largest logit)
     int tref = 0;      // integer keys: softmax reference level (the threshold tau)
 
@@ -278,7 +281,7 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
       uint32_t hv[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        hv[s] = __builtin_popcount(k1[s] ^ q1) + __builtin_popcount(k0[s] ^ q0);
+        hv[s] = __builtin_popcount(kw[1][s] ^ qw[1]) + __builtin_popcount(kw[0][s] ^ qw[0]);
         if (PAD && NS * lane + s >= n) hv[s] = 65u;  // above every real distance
       }
       uint32_t P[NP];
@@ -383,10 +386,12 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int j = 64 * s + lane;
-        const int hd = __builtin_popcount(k0[s] ^ q0) + __builtin_popcount(k1[s] ^ q1);
+        int hd = 0;
+#pragma unroll
+        for (int w = 0; w < W; ++w) hd = __builtin_popcount(kw[w][s] ^ qw[w]) + hd;
         const bool ok = !PAD || j < n;
         const float bias = (a.bias != nullptr && ok) ? biasw[j + boff] : 0.0f;
-        const float l = canonical_logit(aqv, akv[s], kD - 2 * hd, a.isd, bias);
+        const float l = canonical_logit(aqv, akv[s], D - 2 * hd, a.isd, bias);
         lg[s] = ok ? __fadd_rn(l, 0.0f) : -INFINITY;  // -0 and +0 compare equal
       }
       float vstar;
@@ -527,112 +532,122 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
     // ---------------------------------------------------- A*V
+    // (per block of 64 channels: head_dim 128 takes two)
     const int k = lane >> 3, g = lane & 7;
-    if (VK == 2) {
-      int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int t = 0; t < a.lcap; t += 32) {
-        uint2 ent[4], raw[4];
 #pragma unroll
-        for (int u4 = 0; u4 < 4; ++u4) ent[u4] = list[t + 8 * u4 + k];
+    for (int cb = 0; cb < D / 64; ++cb) {
+      constexpr int EB = ROWB / D;  // bytes per V element
+      const uint8_t* const vrow0 = smem + cb * 64 * EB;
+      if (VK == 2) {
+        int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int t = 0; t < a.lcap; t += 32) {
+          uint2 ent[4], raw[4];
 #pragma unroll
-        for (int u4 = 0; u4 < 4; ++u4) raw[u4] = *reinterpret_cast<const uint2*>(smem + ent[u4].x * ROWB + g * 8);
+          for (int u4 = 0; u4 < 4; ++u4) ent[u4] = list[t + 8 * u4 + k];
 #pragma unroll
-        for (int u4 = 0; u4 < 4; ++u4) {
-          const int aq8 = (int)ent[u4].y;
+          for (int u4 = 0; u4 < 4; ++u4) raw[u4] = *reinterpret_cast<const uint2*>(vrow0 + ent[u4].x * ROWB + g * 8);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            acc[c] += aq8 * (int)(int8_t)(raw[u4].x >> (8 * c));
-            acc[4 + c] += aq8 * (int)(int8_t)(raw[u4].y >> (8 * c));
+          for (int u4 = 0; u4 < 4; ++u4) {
+            const int aq8 = (int)ent[u4].y;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              acc[c] += aq8 * (int)(int8_t)(raw[u4].x >> (8 * c));
+              acc[4 + c] += aq8 * (int)(int8_t)(raw[u4].y >> (8 * c));
+            }
           }
         }
-      }
-      const int tot = reduce_scatter8<int>(acc, k);
-      const int ch = 8 * g + k;
-      const float sc = a.vscale[(size_t)bh * kD + ch];
-      a.out[row * kD + ch] = __fdiv_rn(__fmul_rn((float)tot, sc), 255.0f);
-    } else {
-      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      // four entries per group in flight: their list reads, then their row reads, then the math
-      for (int t = 0; t < a.lcap; t += 32) {
-        uint2 ent[4];
+        const int tot = reduce_scatter8<int>(acc, k);
+        const int ch = cb * 64 + 8 * g + k;
+        const float sc = a.vscale[(size_t)bh * D + ch];
+        a.out[row * D + ch] = __fdiv_rn(__fmul_rn((float)tot, sc), 255.0f);
+      } else {
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        // four entries per group in flight: their list reads, then their row reads, then the math
+        for (int t = 0; t < a.lcap; t += 32) {
+          uint2 ent[4];
 #pragma unroll
-        for (int u4 = 0; u4 < 4; ++u4) ent[u4] = list[t + 8 * u4 + k];
-        if (VK == 1) {  // fp16 rows: the widening folds into v_fma_mix_f32
-          uint4 raw[4];
+          for (int u4 = 0; u4 < 4; ++u4) ent[u4] = list[t + 8 * u4 + k];
+          if (VK == 1) {  // fp16 rows: the widening folds into v_fma_mix_f32
+            uint4 raw[4];
 #pragma unroll
-          for (int u4 = 0; u4 < 4; ++u4) raw[u4] = *reinterpret_cast<const uint4*>(smem + ent[u4].x * ROWB + g * 16);
+            for (int u4 = 0; u4 < 4; ++u4) raw[u4] = *reinterpret_cast<const uint4*>(vrow0 + ent[u4].x * ROWB + g * 16);
 #pragma unroll
-          for (int u4 = 0; u4 < 4; ++u4) {
-            const float p = __builtin_bit_cast(float, ent[u4].y);
-            const half2v h0 = __builtin_bit_cast(half2v, raw[u4].x), h1 = __builtin_bit_cast(half2v, raw[u4].y);
-            const half2v h2 = __builtin_bit_cast(half2v, raw[u4].z), h3 = __builtin_bit_cast(half2v, raw[u4].w);
-            acc[0] = __builtin_fmaf(p, (float)h0.x, acc[0]);
-            acc[1] = __builtin_fmaf(p, (float)h0.y, acc[1]);
-            acc[2] = __builtin_fmaf(p, (float)h1.x, acc[2]);
-            acc[3] = __builtin_fmaf(p, (float)h1.y, acc[3]);
-            acc[4] = __builtin_fmaf(p, (float)h2.x, acc[4]);
-            acc[5] = __builtin_fmaf(p, (float)h2.y, acc[5]);
-            acc[6] = __builtin_fmaf(p, (float)h3.x, acc[6]);
-            acc[7] = __builtin_fmaf(p, (float)h3.y, acc[7]);
-          }
-        } else {
-          float4 r0[4], r1[4];
+            for (int u4 = 0; u4 < 4; ++u4) {
+              const float p = __builtin_bit_cast(float, ent[u4].y);
+              const half2v h0 = __builtin_bit_cast(half2v, raw[u4].x), h1 = __builtin_bit_cast(half2v, raw[u4].y);
+              const half2v h2 = __builtin_bit_cast(half2v, raw[u4].z), h3 = __builtin_bit_cast(half2v, raw[u4].w);
+              acc[0] = __builtin_fmaf(p, (float)h0.x, acc[0]);
+              acc[1] = __builtin_fmaf(p, (float)h0.y, acc[1]);
+              acc[2] = __builtin_fmaf(p, (float)h1.x, acc[2]);
+              acc[3] = __builtin_fmaf(p, (float)h1.y, acc[3]);
+              acc[4] = __builtin_fmaf(p, (float)h2.x, acc[4]);
+              acc[5] = __builtin_fmaf(p, (float)h2.y, acc[5]);
+              acc[6] = __builtin_fmaf(p, (float)h3.x, acc[6]);
+              acc[7] = __builtin_fmaf(p, (float)h3.y, acc[7]);
+            }
+          } else {
+            float4 r0[4], r1[4];
 #pragma unroll
-          for (int u4 = 0; u4 < 4; ++u4) {
-            r0[u4] = *reinterpret_cast<const float4*>(smem + ent[u4].x * ROWB + g * 32);
-            r1[u4] = *reinterpret_cast<const float4*>(smem + ent[u4].x * ROWB + g * 32 + 16);
-          }
+            for (int u4 = 0; u4 < 4; ++u4) {
+              r0[u4] = *reinterpret_cast<const float4*>(vrow0 + ent[u4].x * ROWB + g * 32);
+              r1[u4] = *reinterpret_cast<const float4*>(vrow0 + ent[u4].x * ROWB + g * 32 + 16);
+            }
 #pragma unroll
-          for (int u4 = 0; u4 < 4; ++u4) {
-            const float p = __builtin_bit_cast(float, ent[u4].y);
-            acc[0] = __builtin_fmaf(p, r0[u4].x, acc[0]);
-            acc[1] = __builtin_fmaf(p, r0[u4].y, acc[1]);
-            acc[2] = __builtin_fmaf(p, r0[u4].z, acc[2]);
-            acc[3] = __builtin_fmaf(p, r0[u4].w, acc[3]);
-            acc[4] = __builtin_fmaf(p, r1[u4].x, acc[4]);
-            acc[5] = __builtin_fmaf(p, r1[u4].y, acc[5]);
-            acc[6] = __builtin_fmaf(p, r1[u4].z, acc[6]);
-            acc[7] = __builtin_fmaf(p, r1[u4].w, acc[7]);
+            for (int u4 = 0; u4 < 4; ++u4) {
+              const float p = __builtin_bit_cast(float, ent[u4].y);
+              acc[0] = __builtin_fmaf(p, r0[u4].x, acc[0]);
+              acc[1] = __builtin_fmaf(p, r0[u4].y, acc[1]);
+              acc[2] = __builtin_fmaf(p, r0[u4].z, acc[2]);
+              acc[3] = __builtin_fmaf(p, r0[u4].w, acc[3]);
+              acc[4] = __builtin_fmaf(p, r1[u4].x, acc[4]);
+              acc[5] = __builtin_fmaf(p, r1[u4].y, acc[5]);
+              acc[6] = __builtin_fmaf(p, r1[u4].z, acc[6]);
+              acc[7] = __builtin_fmaf(p, r1[u4].w, acc[7]);
+            }
           }
         }
+        a.out[row * D + cb * 64 + 8 * g + k] = reduce_scatter8<float>(acc, k) * (vmul * inv_z);
       }
-      a.out[row * kD + 8 * g + k] = reduce_scatter8<float>(acc, k) * (vmul * inv_z);
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   }
   }
 }
 
-template <int NS, bool FK, int VK, bool PAD>
+template <int NS, bool FK, int VK, bool PAD, int D>
 hipError_t launch_one(const TopnKArgs& ka, dim3 grid, dim3 block, uint32_t lds, hipStream_t s) {
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&topn_resident_kernel<NS, FK, VK, PAD>),
+      reinterpret_cast<const void*>(&topn_resident_kernel<NS, FK, VK, PAD, D>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((topn_resident_kernel<NS, FK, VK, PAD>), grid, block, lds, s, ka);
+  hipLaunchKernelGGL((topn_resident_kernel<NS, FK, VK, PAD, D>), grid, block, lds, s, ka);
   return hipGetLastError();
 }
 
-template <int NS, bool FK, int VK>
+template <int NS, bool FK, int VK, int D>
 hipError_t launch_pad(const TopnKArgs& ka, bool pad, dim3 grid, dim3 block, uint32_t lds, hipStream_t s) {
-  return pad ? launch_one<NS, FK, VK, true>(ka, grid, block, lds, s)
-             : launch_one<NS, FK, VK, false>(ka, grid, block, lds, s);
+  return pad ? launch_one<NS, FK, VK, true, D>(ka, grid, block, lds, s)
+             : launch_one<NS, FK, VK, false, D>(ka, grid, block, lds, s);
 }
 
-template <int NS, bool FK>
+template <int NS, bool FK, int D>
 hipError_t launch_vk(const TopnKArgs& ka, int vk, bool pad, dim3 grid, dim3 block, uint32_t lds, hipStream_t s) {
   switch (vk) {
-    case 0: return launch_pad<NS, FK, 0>(ka, pad, grid, block, lds, s);
-    case 1: return launch_pad<NS, FK, 1>(ka, pad, grid, block, lds, s);
-    default: return launch_pad<NS, FK, 2>(ka, pad, grid, block, lds, s);
+    case 0: return launch_pad<NS, FK, 0, D>(ka, pad, grid, block, lds, s);
+    case 1: return launch_pad<NS, FK, 1, D>(ka, pad, grid, block, lds, s);
+    default: return launch_pad<NS, FK, 2, D>(ka, pad, grid, block, lds, s);
   }
 }
 
 template <int NS>
-hipError_t launch_ns(const TopnKArgs& ka, bool fk, int vk, bool pad, dim3 grid, dim3 block, uint32_t lds,
+hipError_t launch_ns(const TopnKArgs& ka, bool fk, int vk, bool pad, int d, dim3 grid, dim3 block, uint32_t lds,
                      hipStream_t s) {
-  return fk ? launch_vk<NS, true>(ka, vk, pad, grid, block, lds, s)
-            : launch_vk<NS, false>(ka, vk, pad, grid, block, lds, s);
+  if (d == 128) {
+    if constexpr (NS <= 8) return launch_vk<NS, true, 128>(ka, vk, pad, grid, block, lds, s);
+    return hipErrorInvalidValue;
+  }
+  return fk ? launch_vk<NS, true, 64>(ka, vk, pad, grid, block, lds, s)
+            : launch_vk<NS, false, 64>(ka, vk, pad, grid, block, lds, s);
 }
 
 uint32_t align16(uint32_t x) { return (x + 15u) & ~15u; }
@@ -652,12 +667,13 @@ static int resident_slots(int64_t n) {
 }
 
 hipError_t launch_topn(const AttnParams& p, hipStream_t s) {
-  if (p.d != kD) return hipErrorInvalidValue;
+  if (p.d != 64 && p.d != 128) return hipErrorInvalidValue;
   const int NS = resident_slots(p.n);
-  if (NS == 0) return hipErrorInvalidValue;
-  const bool fk = p.alpha_q != nullptr || p.alpha_k != nullptr || p.bias != nullptr;
+  if (NS == 0 || (p.d == 128 && NS > 8)) return hipErrorInvalidValue;
+  // head_dim 128 always takes the float-key path (exact for integer keys as well)
+  const bool fk = p.alpha_q != nullptr || p.alpha_k != nullptr || p.bias != nullptr || p.d != 64;
   const int vk = p.v_kind;
-  const int rowb = vk == 0 ? kD * 4 : (vk == 1 ? kD * 2 : kD);
+  const int rowb = (int)p.d * (vk == 0 ? 4 : (vk == 1 ? 2 : 1));
   TopnKArgs ka{};
   ka.qbits = p.qbits;
   ka.kbits = p.kbits;
@@ -699,12 +715,12 @@ hipError_t launch_topn(const AttnParams& p, hipStream_t s) {
   const dim3 block((unsigned)(64 * nw));
   const bool pad = p.n != (int64_t)NS * 64;  // padding keys exist in the last slots
   switch (NS) {
-    case 1: return launch_ns<1>(ka, fk, vk, pad, grid, block, lds, s);
-    case 2: return launch_ns<2>(ka, fk, vk, pad, grid, block, lds, s);
-    case 4: return launch_ns<4>(ka, fk, vk, pad, grid, block, lds, s);
-    case 8: return launch_ns<8>(ka, fk, vk, pad, grid, block, lds, s);
-    case 12: return launch_ns<12>(ka, fk, vk, pad, grid, block, lds, s);
-    default: return launch_ns<16>(ka, fk, vk, pad, grid, block, lds, s);
+    case 1: return launch_ns<1>(ka, fk, vk, pad, (int)p.d, grid, block, lds, s);
+    case 2: return launch_ns<2>(ka, fk, vk, pad, (int)p.d, grid, block, lds, s);
+    case 4: return launch_ns<4>(ka, fk, vk, pad, (int)p.d, grid, block, lds, s);
+    case 8: return launch_ns<8>(ka, fk, vk, pad, (int)p.d, grid, block, lds, s);
+    case 12: return launch_ns<12>(ka, fk, vk, pad, (int)p.d, grid, block, lds, s);
+    default: return launch_ns<16>(ka, fk, vk, pad, (int)p.d, grid, block, lds, s);
   }
 }
 

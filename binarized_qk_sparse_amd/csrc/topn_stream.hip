@@ -25,7 +25,7 @@
 namespace had {
 namespace {
 
-constexpr int kD = 64;
+// head_dim D is 64 or 128 (codes of D / 32 words)
 constexpr int kWaves = 16;
 constexpr int kChunk = 2048;  // keys per LDS chunk
 constexpr int kCap = 768;     // candidate-buffer entries per wave
@@ -45,17 +45,21 @@ struct StreamKArgs {
   float isd;
 };
 
-// LDS layout (bytes)
-constexpr uint32_t kCodeOff = 0;                                  // uint2[kChunk]
-constexpr uint32_t kAkOff = kCodeOff + kChunk * 8;                 // float[kChunk]
-constexpr uint32_t kBiasOff = kAkOff + kChunk * 4;                 // float[kChunk + kWaves]
-constexpr uint32_t kBufOff = kBiasOff + (kChunk + 64) * 4;         // uint2[kWaves][kCap]
-constexpr uint32_t kCandOff = kBufOff + kWaves * kCap * 8;         // uint2[kWaves][64]
-constexpr uint32_t kLdsTotal = kCandOff + kWaves * 64 * 8;
+// LDS layout (bytes) for head_dim D
+template <int D>
+struct Lds {
+  static constexpr uint32_t kCodeOff = 0;                           // Code<D>[kChunk]
+  static constexpr uint32_t kAkOff = kCodeOff + kChunk * (D / 8);   // float[kChunk]
+  static constexpr uint32_t kBiasOff = kAkOff + kChunk * 4;         // float[kChunk + kWaves]
+  static constexpr uint32_t kBufOff = kBiasOff + (kChunk + 64) * 4;  // uint2[kWaves][kCap]
+  static constexpr uint32_t kCandOff = kBufOff + kWaves * kCap * 8;  // uint2[kWaves][64]
+  static constexpr uint32_t kTotal = kCandOff + kWaves * 64 * 8;
+};
+static_assert(Lds<128>::kTotal <= 160 * 1024, "LDS");
 
-template <int VK>
+template <int VK, int D>
 constexpr int row_bytes() {
-  return VK == 0 ? kD * 4 : (VK == 1 ? kD * 2 : kD);
+  return VK == 0 ? D * 4 : (VK == 1 ? D * 2 : D);
 }
 
 // Exact top-`keep` of the first `cnt` buffer entries (entry order = key order),
@@ -197,17 +201,18 @@ HAD_DEVICE T reduce_scatter8(T (&acc)[8], int k) {
   return kp + __shfl_xor(snd, 8, 64);
 }
 
-template <int VK>
+template <int VK, int D>
 __global__ __launch_bounds__(1024) void topn_stream_kernel(const StreamKArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  constexpr int ROWB = row_bytes<VK>();
-  uint2* codes = reinterpret_cast<uint2*>(smem + kCodeOff);
-  float* aks = reinterpret_cast<float*>(smem + kAkOff);
-  float* biasw = reinterpret_cast<float*>(smem + kBiasOff);
+  constexpr int ROWB = row_bytes<VK, D>();
+  using L = Lds<D>;
+  Code<D>* codes = reinterpret_cast<Code<D>*>(smem + L::kCodeOff);
+  float* aks = reinterpret_cast<float*>(smem + L::kAkOff);
+  float* biasw = reinterpret_cast<float*>(smem + L::kBiasOff);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  uint2* buf = reinterpret_cast<uint2*>(smem + kBufOff) + wave * kCap;
-  uint2* cand = reinterpret_cast<uint2*>(smem + kCandOff) + wave * 64;
+  uint2* buf = reinterpret_cast<uint2*>(smem + L::kBufOff) + wave * kCap;
+  uint2* cand = reinterpret_cast<uint2*>(smem + L::kCandOff) + wave * 64;
   const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / a.tiles, tile = wg % a.tiles, hh = bh % a.H;
   const int n = a.n, keep = a.keep;
@@ -216,9 +221,9 @@ __global__ __launch_bounds__(1024) void topn_stream_kernel(const StreamKArgs a) 
   const bool live = i < n;  // uniform per wave
   const int ic = live ? i : n - 1;
   const size_t row = (size_t)bh * n + ic;
-  const uint2 qq = reinterpret_cast<const uint2*>(a.qbits)[row];
+  const Code<D> qq = load_code<D>(a.qbits, row);
   const float aqv = a.aq != nullptr ? a.aq[row] : 1.0f;
-  const uint2* kb = reinterpret_cast<const uint2*>(a.kbits) + (size_t)bh * n;
+  const size_t kb = (size_t)bh * n;  // first key row of the head
   const float* akg = a.ak != nullptr ? a.ak + (size_t)bh * n : nullptr;
   const int ilast = min(n, i0 + kWaves) - 1;
 
@@ -228,7 +233,7 @@ __global__ __launch_bounds__(1024) void topn_stream_kernel(const StreamKArgs a) 
     const int cl = min(kChunk, n - c0);
     __syncthreads();
     for (int t = threadIdx.x; t < cl; t += blockDim.x) {
-      codes[t] = kb[c0 + t];
+      codes[t] = load_code<D>(a.kbits, kb + c0 + t);
       aks[t] = akg != nullptr ? akg[c0 + t] : 1.0f;
     }
     // bias offsets o = j - i + n - 1 for j in [c0, c0+cl), i in [i0, ilast]
@@ -244,10 +249,9 @@ __global__ __launch_bounds__(1024) void topn_stream_kernel(const StreamKArgs a) 
     for (int s0 = 0; s0 < cl; s0 += 64) {
       const int t = s0 + lane;
       const bool ok = t < cl;
-      const uint2 kk = codes[ok ? t : 0];
-      const int hd = __builtin_popcount(kk.x ^ qq.x) + __builtin_popcount(kk.y ^ qq.y);
+      const int hd = hamming<D>(codes[ok ? t : 0], qq);
       const float b = a.bias != nullptr ? biasw[(ok ? t : 0) + boff] : 0.0f;
-      float l = canonical_logit(aqv, aks[ok ? t : 0], kD - 2 * hd, a.isd, b);
+      float l = canonical_logit(aqv, aks[ok ? t : 0], D - 2 * hd, a.isd, b);
       l = __fadd_rn(l, 0.0f);
       const bool adm = ok && l > theta;
       const uint64_t m = ballot(adm);
@@ -291,63 +295,77 @@ __global__ __launch_bounds__(1024) void topn_stream_kernel(const StreamKArgs a) 
   }
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
-  // ---- A*V: eight lanes per kept key, eight channels per lane, rows from global memory
+  // ---- A*V: eight lanes per kept key, eight channels per lane, rows from global memory,
+  // per block of 64 channels (head_dim 128 takes two)
   const int k = lane >> 3, g = lane & 7;
-  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + (size_t)bh * n * ROWB;
-  if (VK == 2) {
-    int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int t = 0; t < a.lcap; t += 8) {
-      const uint2 ent = buf[t + k];
-      const uint2 raw = *reinterpret_cast<const uint2*>(vbase + (size_t)ent.y * ROWB + g * 8);
-      const int aq8 = (int)ent.x;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        acc[c] += aq8 * (int)(int8_t)(raw.x >> (8 * c));
-        acc[4 + c] += aq8 * (int)(int8_t)(raw.y >> (8 * c));
+  for (int cb = 0; cb < D / 64; ++cb) {
+    const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + (size_t)bh * n * ROWB + cb * 64 * (ROWB / D);
+    if (VK == 2) {
+      int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int t = 0; t < a.lcap; t += 8) {
+        const uint2 ent = buf[t + k];
+        const uint2 raw = *reinterpret_cast<const uint2*>(vbase + (size_t)ent.y * ROWB + g * 8);
+        const int aq8 = (int)ent.x;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc[c] += aq8 * (int)(int8_t)(raw.x >> (8 * c));
+          acc[4 + c] += aq8 * (int)(int8_t)(raw.y >> (8 * c));
+        }
       }
-    }
-    const int tot = reduce_scatter8<int>(acc, k);
-    const int ch = 8 * g + k;
-    a.out[row * kD + ch] = __fdiv_rn(__fmul_rn((float)tot, a.vscale[(size_t)bh * kD + ch]), 255.0f);
-  } else {
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int t = 0; t < a.lcap; t += 8) {
-      const uint2 ent = buf[t + k];
-      const float p = __builtin_bit_cast(float, ent.x);
-      if (VK == 1) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(vbase + (size_t)ent.y * ROWB + g * 16);
-        acc[0] = __builtin_fmaf(p, bf16_lo(raw.x), acc[0]);
-        acc[1] = __builtin_fmaf(p, bf16_hi(raw.x), acc[1]);
-        acc[2] = __builtin_fmaf(p, bf16_lo(raw.y), acc[2]);
-        acc[3] = __builtin_fmaf(p, bf16_hi(raw.y), acc[3]);
-        acc[4] = __builtin_fmaf(p, bf16_lo(raw.z), acc[4]);
-        acc[5] = __builtin_fmaf(p, bf16_hi(raw.z), acc[5]);
-        acc[6] = __builtin_fmaf(p, bf16_lo(raw.w), acc[6]);
-        acc[7] = __builtin_fmaf(p, bf16_hi(raw.w), acc[7]);
-      } else {
-        const float4 r0 = *reinterpret_cast<const float4*>(vbase + (size_t)ent.y * ROWB + g * 32);
-        const float4 r1 = *reinterpret_cast<const float4*>(vbase + (size_t)ent.y * ROWB + g * 32 + 16);
-        acc[0] = __builtin_fmaf(p, r0.x, acc[0]);
-        acc[1] = __builtin_fmaf(p, r0.y, acc[1]);
-        acc[2] = __builtin_fmaf(p, r0.z, acc[2]);
-        acc[3] = __builtin_fmaf(p, r0.w, acc[3]);
-        acc[4] = __builtin_fmaf(p, r1.x, acc[4]);
-        acc[5] = __builtin_fmaf(p, r1.y, acc[5]);
-        acc[6] = __builtin_fmaf(p, r1.z, acc[6]);
-        acc[7] = __builtin_fmaf(p, r1.w, acc[7]);
+      const int tot = reduce_scatter8<int>(acc, k);
+      const int ch = cb * 64 + 8 * g + k;
+      a.out[row * D + ch] = __fdiv_rn(__fmul_rn((float)tot, a.vscale[(size_t)bh * D + ch]), 255.0f);
+    } else {
+      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int t = 0; t < a.lcap; t += 8) {
+        const uint2 ent = buf[t + k];
+        const float p = __builtin_bit_cast(float, ent.x);
+        if (VK == 1) {
+          const uint4 raw = *reinterpret_cast<const uint4*>(vbase + (size_t)ent.y * ROWB + g * 16);
+          acc[0] = __builtin_fmaf(p, bf16_lo(raw.x), acc[0]);
+          acc[1] = __builtin_fmaf(p, bf16_hi(raw.x), acc[1]);
+          acc[2] = __builtin_fmaf(p, bf16_lo(raw.y), acc[2]);
+          acc[3] = __builtin_fmaf(p, bf16_hi(raw.y), acc[3]);
+          acc[4] = __builtin_fmaf(p, bf16_lo(raw.z), acc[4]);
+          acc[5] = __builtin_fmaf(p, bf16_hi(raw.z), acc[5]);
+          acc[6] = __builtin_fmaf(p, bf16_lo(raw.w), acc[6]);
+          acc[7] = __builtin_fmaf(p, bf16_hi(raw.w), acc[7]);
+        } else {
+          const float4 r0 = *reinterpret_cast<const float4*>(vbase + (size_t)ent.y * ROWB + g * 32);
+          const float4 r1 = *reinterpret_cast<const float4*>(vbase + (size_t)ent.y * ROWB + g * 32 + 16);
+          acc[0] = __builtin_fmaf(p, r0.x, acc[0]);
+          acc[1] = __builtin_fmaf(p, r0.y, acc[1]);
+          acc[2] = __builtin_fmaf(p, r0.z, acc[2]);
+          acc[3] = __builtin_fmaf(p, r0.w, acc[3]);
+          acc[4] = __builtin_fmaf(p, r1.x, acc[4]);
+          acc[5] = __builtin_fmaf(p, r1.y, acc[5]);
+          acc[6] = __builtin_fmaf(p, r1.z, acc[6]);
+          acc[7] = __builtin_fmaf(p, r1.w, acc[7]);
+        }
       }
+      a.out[row * D + cb * 64 + 8 * g + k] = reduce_scatter8<float>(acc, k);
     }
-    a.out[row * kD + 8 * g + k] = reduce_scatter8<float>(acc, k);
   }
 }
 
-template <int VK>
+template <int VK, int D>
 hipError_t launch_vk(const StreamKArgs& ka, dim3 grid, hipStream_t s) {
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&topn_stream_kernel<VK>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsTotal);
+  constexpr uint32_t lds = Lds<D>::kTotal;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&topn_stream_kernel<VK, D>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((topn_stream_kernel<VK>), grid, dim3(64 * kWaves), kLdsTotal, s, ka);
+  hipLaunchKernelGGL((topn_stream_kernel<VK, D>), grid, dim3(64 * kWaves), lds, s, ka);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const StreamKArgs& ka, int vk, dim3 grid, hipStream_t s) {
+  switch (vk) {
+    case 0: return launch_vk<0, D>(ka, grid, s);
+    case 1: return launch_vk<1, D>(ka, grid, s);
+    default: return launch_vk<2, D>(ka, grid, s);
+  }
 }
 
 }  // namespace
@@ -355,7 +373,7 @@ hipError_t launch_vk(const StreamKArgs& ka, dim3 grid, hipStream_t s) {
 int64_t topn_stream_max_keep() { return kCap - 64; }
 
 hipError_t launch_topn_stream(const AttnParams& p, hipStream_t s) {
-  if (p.d != kD || p.keep > topn_stream_max_keep()) return hipErrorInvalidValue;
+  if ((p.d != 64 && p.d != 128) || p.keep > topn_stream_max_keep()) return hipErrorInvalidValue;
   StreamKArgs ka{};
   ka.qbits = p.qbits;
   ka.kbits = p.kbits;
@@ -373,11 +391,7 @@ hipError_t launch_topn_stream(const AttnParams& p, hipStream_t s) {
   ka.tiles = (int)((p.n + kWaves - 1) / kWaves);
   ka.isd = (float)(1.0 / sqrt((double)p.d));
   const dim3 grid((unsigned)(p.B * p.H * ka.tiles));
-  switch (p.v_kind) {
-    case 0: return launch_vk<0>(ka, grid, s);
-    case 1: return launch_vk<1>(ka, grid, s);
-    default: return launch_vk<2>(ka, grid, s);
-  }
+  return p.d == 128 ? launch_d<128>(ka, p.v_kind, grid, s) : launch_d<64>(ka, p.v_kind, grid, s);
 }
 
 }  // namespace had

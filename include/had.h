@@ -30,7 +30,7 @@
  *    error status nothing is launched and no output is touched.  Faults that
  *    happen on the device surface at the caller's next synchronisation.
  *  - d must be 32, 64 or 128 (bits per token: d/32 uint32 words) for packing;
- *    the attention entry points take d = 64.
+ *    the attention entry points take d = 64 or d = 128.
  *  - Relative-position bias: `bias_table` is float32 [H, 2n-1] and
  *    B[i][j] = bias_table[h][j - i + n - 1]; NULL means B = 0.
  *  - alpha pointers: float32 [B, H, n]; NULL means alpha = 1.

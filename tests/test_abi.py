@@ -122,7 +122,8 @@ def test_pack_qk_validation(args, want):
     (dict(av=3), _lib.HAD_ERR_INVALID_ARG),
     (dict(vdt=9), _lib.HAD_ERR_INVALID_ARG),
     (dict(H=0), _lib.HAD_ERR_INVALID_ARG),
-    (dict(d=128), _lib.HAD_ERR_UNSUPPORTED),
+    (dict(d=32), _lib.HAD_ERR_UNSUPPORTED),
+    (dict(d=256), _lib.HAD_ERR_UNSUPPORTED),
     (dict(n=1 << 20), _lib.HAD_ERR_UNSUPPORTED),
     (dict(top_n=5000, n=8192), _lib.HAD_ERR_UNSUPPORTED),
     (dict(av=1, ws=None), _lib.HAD_ERR_WORKSPACE),

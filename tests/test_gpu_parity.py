@@ -81,11 +81,11 @@ def test_pack_qk_matches_oracle_and_pack(d, n, mode):
 
 
 # ------------------------------------------------------------------ top-N, fp32 A*V
-def _topn_case(B, H, n, N, vdtype, mode, bias, seed, av=synth.AV_F32):
-    g = np.random.default_rng([11, B, H, n, N, seed])
-    xq = (g.standard_normal((B, H, n, 64)) + 0.3 * g.standard_normal((1, H, 1, 64))).astype(np.float32)
-    xk = (g.standard_normal((B, H, n, 64)) + 0.3 * g.standard_normal((1, H, 1, 64))).astype(np.float32)
-    v = torch.from_numpy(g.standard_normal((B, H, n, 64)).astype(np.float32)).to(vdtype)
+def _topn_case(B, H, n, N, vdtype, mode, bias, seed, av=synth.AV_F32, d=64):
+    g = np.random.default_rng([11, B, H, n, N, seed] + ([d] if d != 64 else []))
+    xq = (g.standard_normal((B, H, n, d)) + 0.3 * g.standard_normal((1, H, 1, d))).astype(np.float32)
+    xk = (g.standard_normal((B, H, n, d)) + 0.3 * g.standard_normal((1, H, 1, d))).astype(np.float32)
+    v = torch.from_numpy(g.standard_normal((B, H, n, d)).astype(np.float32)).to(vdtype)
     T = (0.05 * g.standard_normal((H, 2 * n - 1))).astype(np.float32) if bias else None
     qb, aq, _ = oracle.pack(xq, mode)
     kb, ak, _ = oracle.pack(xk, mode)
@@ -309,3 +309,54 @@ def test_topn_zero_distance_ties():
         ref = oracle.attention(qb, qb, f32(v), top_n=N, want_idx=True)
         assert np.array_equal(idx, ref["idx"]), N
         assert_close(out, ref["out"], f"zero-distance ties N={N}")
+
+
+# ------------------------------------------------------------------ head_dim 128
+# The same entry points at d = 128 (codes of four words): the resident kernel up to
+# n = 512 (256 with fp32 V), the long-sequence kernel beyond, and the dense q8 kernel.
+@pytest.mark.parametrize("n,N,vdtype", [(1, 1, torch.float32), (65, 7, torch.float32), (197, 30, torch.bfloat16),
+                                        (256, 120, torch.float32), (300, 30, torch.float32),
+                                        (512, 120, torch.bfloat16), (700, 64, torch.bfloat16),
+                                        (1500, 256, torch.bfloat16)])
+@pytest.mark.parametrize("keys", ["int", "bias", "alpha_bias"])
+def test_topn_d128_matches_oracle(n, N, vdtype, keys):
+    mode = synth.MEAN_SIGN if keys == "alpha_bias" else synth.SIGN
+    qb, kb, aq, ak, T, v = _topn_case(1, 2, n, N, vdtype, mode, keys != "int", seed=5, d=128)
+    out, idx = _run_topn(qb, kb, aq, ak, T, v, N)
+    rows = sample_rows(2 * n, 600, n)
+    ref = oracle.attention(qb, kb, f32(v), alpha_q=aq, alpha_k=ak, bias=T, top_n=N, rows=rows, want_idx=True)
+    keep = min(N, n)
+    assert np.array_equal(idx.reshape(-1, keep)[rows], ref["idx"]), "kept index sets differ"
+    assert_close(out.reshape(-1, 128)[rows], ref["out"], f"d=128 n={n} N={N} {keys}")
+
+
+@pytest.mark.parametrize("n,N", [(197, 30), (512, 64), (1300, 120)])
+def test_topn_q8_d128_matches_oracle(n, N):
+    qb, kb, aq, ak, T, v = _topn_case(1, 2, n, N, torch.bfloat16, synth.MEAN_SIGN, True, seed=6, d=128)
+    dt = lambda a: torch.from_numpy(a).to(DEV)
+    ws = ops.workspace(1, 2, n, 128)
+    out, idx = ops.had_attention_topn(dt(qb.view(np.int32)), dt(kb.view(np.int32)), v.to(DEV), N, alpha_q=dt(aq),
+                                      alpha_k=dt(ak), bias=dt(T), av_mode=ops.HAD_AV_Q8, want_idx=True, ws=ws)
+    torch.cuda.synchronize()
+    vq, sc = ops.workspace_view(ws, 1, 2, n, 128)
+    rows = sample_rows(2 * n, 600, n)
+    ref = oracle.attention(qb, kb, f32(v), alpha_q=aq, alpha_k=ak, bias=T, top_n=N, av_mode=oracle.AV_Q8,
+                           rows=rows, want_idx=True)
+    keep = min(N, n)
+    assert np.array_equal(idx.cpu().numpy().reshape(-1, keep)[rows], ref["idx"])
+    _check_q8(out.cpu().numpy().reshape(-1, 128)[rows], vq.cpu().numpy(), sc.cpu().numpy(), ref, rows, n,
+              f"q8 d=128 n={n}")
+
+
+@pytest.mark.parametrize("n", [1, 33, 197, 256])
+def test_dense_q8_d128(n):
+    qb, kb, aq, ak, T, v = _topn_case(2, 2, n, n, torch.bfloat16, synth.MEAN_SIGN, True, seed=7, d=128)
+    dt = lambda a: torch.from_numpy(a).to(DEV)
+    ws = ops.workspace(2, 2, n, 128)
+    out = ops.binattn_dense_q8(dt(qb.view(np.int32)), dt(kb.view(np.int32)), v.to(DEV), alpha_q=dt(aq),
+                               alpha_k=dt(ak), bias=dt(T), ws=ws)
+    torch.cuda.synchronize()
+    vq, sc = ops.workspace_view(ws, 2, 2, n, 128)
+    ref = oracle.attention(qb, kb, f32(v), alpha_q=aq, alpha_k=ak, bias=T, top_n=None, av_mode=oracle.AV_Q8)
+    _check_q8(out.cpu().numpy().reshape(-1, 128), vq.cpu().numpy(), sc.cpu().numpy(),
+              {**ref, "out": ref["out"].reshape(-1, 128)}, np.arange(2 * 2 * n), n, f"dense d=128 n={n}")
