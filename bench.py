@@ -82,14 +82,17 @@ def algorithmic_bytes(w) -> float:
 def attention_kernel(w):
     """(kernel name, source file) of the attention launch, by the library's dispatch rule:
     dense softmax -> dense_q8; n above the resident limit (512 keys for fp32 V, 1024
-    otherwise) -> the streaming kernel; bf16 V with integer logits (plain sign, no
-    bias) and fp32 A*V -> the matrix-core kernel; anything else -> the resident kernel."""
+    otherwise, half that at head_dim 128) -> the streaming kernel; head_dim 64 with bf16
+    V, integer logits (plain sign, no bias) and fp32 A*V -> the matrix-core kernel;
+    anything else -> the resident kernel."""
     if w.top_n is None:
         return "dense_q8_kernel", "dense_q8.hip"
     resident_max = 512 if (w.dtype == "f32" and w.av_mode == 0) else 1024
+    if w.d == 128:
+        resident_max //= 2  # rows twice as long in LDS
     if w.n > resident_max:
         return "topn_stream_kernel", "topn_stream.hip"
-    if w.dtype == "bf16" and w.mode == 0 and not w.bias and w.av_mode == 0:
+    if w.d == 64 and w.dtype == "bf16" and w.mode == 0 and not w.bias and w.av_mode == 0:
         return "topn_mfma_kernel", "topn_mfma.hip"
     return "topn_resident_kernel", "topn.hip"
 

@@ -80,6 +80,9 @@ WORKLOADS: Dict[str, Workload] = {
     "c3": Workload("c3", 2, 4, 12, 1024, 64, 120, "bf16", SIGN, False, AV_F32, "chan_std"),
     "c4": Workload("c4", 3, 64, 12, 197, 64, None, "bf16", MEAN_SIGN, True, AV_Q8, "chan_mean"),
     "c5": Workload("c5", 4, 1, 16, 16384, 64, 256, "bf16", MEAN_SIGN, True, AV_Q8, "iid"),
+    # the long-context sweep at head_dim 128 (the kernel shape of BinaryAttention's
+    # speed-versus-length figure); "c3d128@n" scales N = 15 n / 128 like c3
+    "c3d128": Workload("c3d128", 5, 4, 12, 1024, 128, 120, "bf16", SIGN, False, AV_F32, "chan_std"),
 }
 
 C3_SWEEP = (128, 256, 512, 1024)
