@@ -170,10 +170,12 @@ def _brute_topn(l, N):
     return sorted(order[: min(N, n)])
 
 
-@pytest.mark.parametrize("N", [1, 5, 30, 64, 200])
-def test_topn_matches_brute_force_full_sort(N):
-    g = np.random.default_rng(8 + N)
-    B, H, n, d = 1, 2, 64, 32  # d=32: only 33 logit levels, so ties are everywhere
+@pytest.mark.parametrize("N,d", [(1, 32), (5, 32), (30, 32), (64, 32), (200, 32), (5, 128), (30, 128)])
+def test_topn_matches_brute_force_full_sort(N, d):
+    g = np.random.default_rng(8 + N + d)
+    # d=32: only 33 logit levels, so ties are everywhere; d=128: four code words per row and an
+    # irrational 1/sqrt(d), which keeps distinct integer products distinct and equal ones tied
+    B, H, n = 1, 2, 64
     xq = g.standard_normal((B, H, n, d)).astype(np.float32)
     xk = g.standard_normal((B, H, n, d)).astype(np.float32)
     v = g.standard_normal((B, H, n, d)).astype(np.float32)
@@ -227,9 +229,9 @@ def _case(seed, B=2, H=2, n=48, d=64, mode=oracle.MEAN_SIGN, bias=True):
     return xq, xk, v, T, qb, kb, aq, ak
 
 
-@pytest.mark.parametrize("mode", [oracle.SIGN, oracle.MEAN_SIGN])
-def test_dense_equals_textbook_attention(mode):
-    xq, xk, v, T, qb, kb, aq, ak = _case(10, mode=mode)
+@pytest.mark.parametrize("mode,d", [(oracle.SIGN, 64), (oracle.MEAN_SIGN, 64), (oracle.MEAN_SIGN, 128)])
+def test_dense_equals_textbook_attention(mode, d):
+    xq, xk, v, T, qb, kb, aq, ak = _case(10, mode=mode, d=d)
     if mode == oracle.MEAN_SIGN:
         # the codes are sign(x - mu); hand SDPA the centred inputs' signs
         _, _, mq = oracle.pack(xq, mode)
@@ -240,8 +242,9 @@ def test_dense_equals_textbook_attention(mode):
     assert np.allclose(got, want, rtol=1e-5, atol=1e-6)
 
 
-def test_topn_equals_masked_textbook_attention():
-    xq, xk, v, T, qb, kb, aq, ak = _case(11)
+@pytest.mark.parametrize("d", [64, 128])
+def test_topn_equals_masked_textbook_attention(d):
+    xq, xk, v, T, qb, kb, aq, ak = _case(11, d=d)
     _, _, mq = oracle.pack(xq, oracle.MEAN_SIGN)
     _, _, mk = oracle.pack(xk, oracle.MEAN_SIGN)
     yq, yk = xq - mq[:, :, None, :], xk - mk[:, :, None, :]
@@ -252,7 +255,7 @@ def test_topn_equals_masked_textbook_attention():
     dot = np.einsum("bhic,bhjc->bhij", _signs(yq), _signs(yk))
     i = np.arange(n)[:, None]
     j = np.arange(n)[None, :]
-    l = (aq[..., :, None] * ak[..., None, :]).astype(np.float64) * dot / 8.0 + T[:, j - i + n - 1][None]
+    l = (aq[..., :, None] * ak[..., None, :]).astype(np.float64) * dot / np.sqrt(d) + T[:, j - i + n - 1][None]
     keep = np.zeros((B, H, n, n), bool)
     for b in range(B):
         for h in range(H):
@@ -323,9 +326,9 @@ def test_q8_uniform_attention_closed_form():
     assert np.array_equal(r["out"][0, 0], np.broadcast_to(want, (n, d)))
 
 
-@pytest.mark.parametrize("N", [5, None])
-def test_q8_integer_product_and_error_bound(N):
-    xq, xk, v, T, qb, kb, aq, ak = _case(17, n=40)
+@pytest.mark.parametrize("N,d", [(5, 64), (None, 64), (5, 128)])
+def test_q8_integer_product_and_error_bound(N, d):
+    xq, xk, v, T, qb, kb, aq, ak = _case(17, n=40, d=d)
     fp = oracle.attention(qb, kb, v, alpha_q=aq, alpha_k=ak, bias=T, top_n=N, want_idx=True)
     q8 = oracle.attention(qb, kb, v, alpha_q=aq, alpha_k=ak, bias=T, top_n=N, av_mode=oracle.AV_Q8,
                           want_idx=True, want_aq8=True)
