@@ -18,6 +18,8 @@
 #include <float.h>
 #include <limits.h>
 
+#include <type_traits>
+
 #include "had_device.hpp"
 #include "had_internal.h"
 #include "../../include/had.h"
@@ -56,6 +58,21 @@ struct Lds {
   static constexpr uint32_t kTotal = kCandOff + kWaves * 64 * 8;
 };
 static_assert(Lds<128>::kTotal <= 160 * 1024, "LDS");
+static_assert(kChunk % (64 * kWaves) == 0, "chunk loads");
+
+// d - 2 h for two codes: popcounts chained through the accumulate operand of
+// v_bcnt_u32_b32 and one 24-bit multiply-add (the compiler would otherwise add
+// the popcounts, shift and subtract).
+template <int D>
+HAD_DEVICE int code_dot(const Code<D>& x, const Code<D>& y) {
+  uint32_t h;
+  asm("v_bcnt_u32_b32 %0, %1, 0" : "=v"(h) : "v"(x.w[0] ^ y.w[0]));
+#pragma unroll
+  for (int w = 1; w < D / 32; ++w) asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(h) : "v"(x.w[w] ^ y.w[w]), "v"(h));
+  int dot;
+  asm("v_mad_i32_i24 %0, %1, -2, %2" : "=v"(dot) : "v"(h), "v"(D));
+  return dot;
+}
 
 template <int VK, int D>
 constexpr int row_bytes() {
@@ -181,6 +198,90 @@ HAD_DEVICE int select_compact(uint2* buf, uint2* cand, int cnt, int keep, int la
   return base;
 }
 
+// Entries an intermediate compaction may keep above the top-`keep`.
+constexpr int kSlack = 64;
+
+template <int R>
+HAD_DEVICE int count_ge_rows(const float (&v)[R], float t) {
+  int c = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) c += __builtin_popcountll(ballot(v[r] >= t));
+  return c;
+}
+
+// Intermediate compaction, cheaper than the exact selection: finds a value t
+// with keep <= #{l >= t} <= keep + kSlack by interpolation search between theta
+// (every entry is above it) and the largest entry, keeps the entries with
+// l >= t in order, raises theta to t and returns their count.  This drops no
+// entry of the final selection: t is at most the keep-th largest value, and a
+// later key with l <= t ranks below the keep kept entries at or above t (equal
+// values go to the lower key index).  Returns -1 when no such t turns up within
+// a few steps (heavy ties); the caller then runs the exact selection.
+HAD_DEVICE int compact_approx(uint2* buf, int cnt, int keep, int lane, float* theta) {
+  uint2 ent[kR];
+  float vals[kR];
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const int e = lane + 64 * r;
+    ent[r] = e < cnt ? buf[e] : make_uint2(0xff800000u, 0u);  // -inf: empty slot
+    vals[r] = __builtin_bit_cast(float, ent[r].x);
+  }
+  float hi = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < kR; ++r) hi = fmaxf(hi, vals[r]);
+  hi = wave_max_f32(hi);
+  float lo = *theta;
+  if (lo == -INFINITY) {
+    float m = INFINITY;
+#pragma unroll
+    for (int r = 0; r < kR; ++r) m = fminf(m, vals[r] == -INFINITY ? INFINITY : vals[r]);
+    lo = -wave_max_f32(-m);  // the smallest entry: #{l >= lo} = cnt
+  }
+  int clo = cnt, chi = count_ge_rows(vals, hi);
+  const int top = keep + kSlack;
+  float t = hi;
+  int ct = chi;
+  if (chi < keep) {
+    ct = -1;
+    for (int it = 0; it < 8; ++it) {
+      float f = (float)(clo - (keep + kSlack / 2)) / (float)(clo - chi);
+      f = fminf(fmaxf(f, 0.125f), 0.875f);
+      const float mid = lo + f * (hi - lo);
+      if (!(mid > lo && mid < hi)) break;
+      const int cm = count_ge_rows(vals, mid);
+      if (cm < keep) {
+        hi = mid;
+        chi = cm;
+      } else if (cm > top) {
+        lo = mid;
+        clo = cm;
+      } else {
+        t = mid;
+        ct = cm;
+        break;
+      }
+    }
+  }
+  if (ct < keep || ct > top) return -1;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  int base = 0;
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const bool sel = vals[r] >= t;
+    const uint64_t Sm = ballot(sel);
+    if (sel) buf[base + (int)mask_rank(Sm)] = ent[r];
+    base += __builtin_popcountll(Sm);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  *theta = t;
+  return base;
+}
+
+// eight fp32 channels of a row
+struct F8 {
+  float4 a, b;
+};
+
 template <typename T>
 HAD_DEVICE T reduce_scatter8(T (&acc)[8], int k) {
   const bool u4 = k & 4, u2 = k & 2, u1 = k & 1;
@@ -227,41 +328,120 @@ __global__ __launch_bounds__(1024) void topn_stream_kernel(const StreamKArgs a) 
   const float* akg = a.ak != nullptr ? a.ak + (size_t)bh * n : nullptr;
   const int ilast = min(n, i0 + kWaves) - 1;
 
+  // A chunk's key codes, alpha_k and bias window go global -> registers -> LDS;
+  // the next chunk's loads are issued before the current chunk is processed, so
+  // they land while it runs.  Bias offsets o = j - i + n - 1 for j in the chunk
+  // and i in [i0, ilast]; zero without a table.  Adding +0 turns a -0 entry into
+  // +0, so no logit v + b is ever -0 (an exact zero sum rounds to +0) and equal
+  // logits have equal bits.
+  constexpr int kPer = kChunk / (64 * kWaves);
+  Code<D> pcode[kPer];
+  float pak[kPer], pbias[kPer + 1];
+  const float* biash = a.bias != nullptr ? a.bias + (size_t)hh * (2 * n - 1) : nullptr;
+  auto fetch_chunk = [&](int c0) {
+    const int cl = min(kChunk, n - c0);
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int t = (int)threadIdx.x + r * 64 * kWaves;
+      if (t < cl) {
+        pcode[r] = load_code<D>(a.kbits, kb + c0 + t);
+        pak[r] = akg != nullptr ? akg[c0 + t] : 1.0f;
+      }
+    }
+    const int ob = c0 - ilast + n - 1;
+    const int cntb = cl + (ilast - i0);
+#pragma unroll
+    for (int r = 0; r <= kPer; ++r) {
+      const int t = (int)threadIdx.x + r * 64 * kWaves;
+      if (t < cntb) pbias[r] = biash != nullptr ? biash[ob + t] : 0.0f;
+    }
+  };
+  auto store_chunk = [&](int c0) {
+    const int cl = min(kChunk, n - c0);
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int t = (int)threadIdx.x + r * 64 * kWaves;
+      if (t < cl) {
+        codes[t] = pcode[r];
+        aks[t] = pak[r];
+      }
+    }
+    const int cntb = cl + (ilast - i0);
+#pragma unroll
+    for (int r = 0; r <= kPer; ++r) {
+      const int t = (int)threadIdx.x + r * 64 * kWaves;
+      if (t < cntb) biasw[t] = __fadd_rn(pbias[r], 0.0f);
+    }
+  };
+
   float theta = -INFINITY;  // admit l > theta
   int cnt = 0;
+  // intermediate compactions may leave up to keep + kSlack entries when that
+  // still frees room for two more groups
+  const bool approx = keep + kSlack <= kCap - 128;
+  fetch_chunk(0);
   for (int c0 = 0; c0 < n; c0 += kChunk) {
     const int cl = min(kChunk, n - c0);
     __syncthreads();
-    for (int t = threadIdx.x; t < cl; t += blockDim.x) {
-      codes[t] = load_code<D>(a.kbits, kb + c0 + t);
-      aks[t] = akg != nullptr ? akg[c0 + t] : 1.0f;
-    }
-    // bias offsets o = j - i + n - 1 for j in [c0, c0+cl), i in [i0, ilast]
-    const int ob = c0 - ilast + n - 1;
-    if (a.bias != nullptr) {
-      const int cntb = cl + (ilast - i0);
-      const float* src = a.bias + (size_t)hh * (2 * n - 1) + ob;
-      for (int t = threadIdx.x; t < cntb; t += blockDim.x) biasw[t] = src[t];
-    }
+    store_chunk(c0);
+    if (c0 + kChunk < n) fetch_chunk(c0 + kChunk);
     __syncthreads();
     if (!live) continue;
     const int boff = ilast - i;  // bias window index of chunk key t is t + boff
-    for (int s0 = 0; s0 < cl; s0 += 64) {
-      const int t = s0 + lane;
-      const bool ok = t < cl;
-      const int hd = hamming<D>(codes[ok ? t : 0], qq);
-      const float b = a.bias != nullptr ? biasw[(ok ? t : 0) + boff] : 0.0f;
-      float l = canonical_logit(aqv, aks[ok ? t : 0], D - 2 * hd, a.isd, b);
-      l = __fadd_rn(l, 0.0f);
-      const bool adm = ok && l > theta;
-      const uint64_t m = ballot(adm);
-      if (m != 0) {
-        if (adm) buf[cnt + (int)mask_rank(m)] = make_uint2(__builtin_bit_cast(uint32_t, l), (uint32_t)(c0 + t));
-        cnt += __builtin_popcountll(m);
-        if (cnt > kCap - 64) {
-          __atomic_signal_fence(__ATOMIC_SEQ_CST);
-          float lm;
-          cnt = select_compact(buf, cand, cnt, keep, lane, &theta, &lm);
+    // Blocks of four 64-key groups.  The buffer holds at most kCap - 64 entries
+    // between groups, so one more group always fits.  Fast path (a full block
+    // whose admitted keys keep that bound): four logits with fixed LDS offsets,
+    // then the four appends.  Otherwise (a partial block, or a block that fills
+    // the buffer) the groups go one at a time with bounds checks, compacting
+    // when the bound is passed; that path recomputes the logits and runs a few
+    // times per query.
+    const Code<D>* cp = codes + lane;
+    const float* akp = aks + lane;
+    const float* bp = biasw + boff + lane;
+    for (int s0 = 0; s0 < cl; s0 += 256) {
+      if (s0 + 256 <= cl) {
+        float l[4];
+        uint64_t m[4];
+        int tot = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          l[u] = canonical_logit(aqv, akp[s0 + 64 * u], code_dot<D>(cp[s0 + 64 * u], qq), a.isd,
+                                 bp[s0 + 64 * u]);
+          m[u] = ballot(l[u] > theta);
+          tot += __builtin_popcountll(m[u]);
+        }
+        if (cnt + tot <= kCap - 64) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (m[u] != 0) {
+              if (l[u] > theta)
+                buf[cnt + (int)mask_rank(m[u])] =
+                    make_uint2(__builtin_bit_cast(uint32_t, l[u]), (uint32_t)(c0 + s0 + 64 * u + lane));
+              cnt += __builtin_popcountll(m[u]);
+            }
+          }
+          continue;
+        }
+      }
+      for (int g0 = s0; g0 < min(s0 + 256, cl); g0 += 64) {
+        const int t = g0 + lane;
+        const bool ok = t < cl;
+        const int tc = ok ? t : 0;
+        const float l = canonical_logit(aqv, aks[tc], D - 2 * hamming<D>(codes[tc], qq), a.isd, biasw[tc + boff]);
+        const bool adm = ok && l > theta;
+        const uint64_t m = ballot(adm);
+        if (m != 0) {
+          if (adm) buf[cnt + (int)mask_rank(m)] = make_uint2(__builtin_bit_cast(uint32_t, l), (uint32_t)(c0 + t));
+          cnt += __builtin_popcountll(m);
+          if (cnt > kCap - 64) {
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            int kept = approx ? compact_approx(buf, cnt, keep, lane, &theta) : -1;
+            if (kept < 0) {
+              float lm;
+              kept = select_compact(buf, cand, cnt, keep, lane, &theta, &lm);
+            }
+            cnt = kept;
+          }
         }
       }
     }
@@ -296,54 +476,69 @@ __global__ __launch_bounds__(1024) void topn_stream_kernel(const StreamKArgs a) 
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
   // ---- A*V: eight lanes per kept key, eight channels per lane, rows from global memory,
-  // per block of 64 channels (head_dim 128 takes two)
+  // per block of 64 channels (head_dim 128 takes two).  Four kept keys per lane are
+  // fetched before any is used, so four row loads are in flight at once.
   const int k = lane >> 3, g = lane & 7;
+  using Raw = typename std::conditional<VK == 2, uint2, typename std::conditional<VK == 1, uint4, F8>::type>::type;
+  using Acc = typename std::conditional<VK == 2, int, float>::type;
+  constexpr int U = 4;
 #pragma unroll
   for (int cb = 0; cb < D / 64; ++cb) {
     const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + (size_t)bh * n * ROWB + cb * 64 * (ROWB / D);
-    if (VK == 2) {
-      int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int t = 0; t < a.lcap; t += 8) {
-        const uint2 ent = buf[t + k];
-        const uint2 raw = *reinterpret_cast<const uint2*>(vbase + (size_t)ent.y * ROWB + g * 8);
-        const int aq8 = (int)ent.x;
+    auto fetch = [&](uint32_t j) -> Raw {
+      return *reinterpret_cast<const Raw*>(vbase + (size_t)j * ROWB + g * sizeof(Raw));
+    };
+    Acc acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    auto accum = [&](uint32_t w, const Raw& raw) {
+      if constexpr (VK == 2) {
+        const int aq8 = (int)w;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           acc[c] += aq8 * (int)(int8_t)(raw.x >> (8 * c));
           acc[4 + c] += aq8 * (int)(int8_t)(raw.y >> (8 * c));
         }
+      } else if constexpr (VK == 1) {
+        const float p = __builtin_bit_cast(float, w);
+        acc[0] = __builtin_fmaf(p, bf16_lo(raw.x), acc[0]);
+        acc[1] = __builtin_fmaf(p, bf16_hi(raw.x), acc[1]);
+        acc[2] = __builtin_fmaf(p, bf16_lo(raw.y), acc[2]);
+        acc[3] = __builtin_fmaf(p, bf16_hi(raw.y), acc[3]);
+        acc[4] = __builtin_fmaf(p, bf16_lo(raw.z), acc[4]);
+        acc[5] = __builtin_fmaf(p, bf16_hi(raw.z), acc[5]);
+        acc[6] = __builtin_fmaf(p, bf16_lo(raw.w), acc[6]);
+        acc[7] = __builtin_fmaf(p, bf16_hi(raw.w), acc[7]);
+      } else {
+        const float p = __builtin_bit_cast(float, w);
+        acc[0] = __builtin_fmaf(p, raw.a.x, acc[0]);
+        acc[1] = __builtin_fmaf(p, raw.a.y, acc[1]);
+        acc[2] = __builtin_fmaf(p, raw.a.z, acc[2]);
+        acc[3] = __builtin_fmaf(p, raw.a.w, acc[3]);
+        acc[4] = __builtin_fmaf(p, raw.b.x, acc[4]);
+        acc[5] = __builtin_fmaf(p, raw.b.y, acc[5]);
+        acc[6] = __builtin_fmaf(p, raw.b.z, acc[6]);
+        acc[7] = __builtin_fmaf(p, raw.b.w, acc[7]);
       }
+    };
+    int t = 0;
+    for (; t + 8 * U <= a.lcap; t += 8 * U) {
+      uint2 ent[U];
+      Raw raw[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) ent[u] = buf[t + 8 * u + k];
+#pragma unroll
+      for (int u = 0; u < U; ++u) raw[u] = fetch(ent[u].y);
+#pragma unroll
+      for (int u = 0; u < U; ++u) accum(ent[u].x, raw[u]);
+    }
+    for (; t < a.lcap; t += 8) {
+      const uint2 ent = buf[t + k];
+      accum(ent.x, fetch(ent.y));
+    }
+    if constexpr (VK == 2) {
       const int tot = reduce_scatter8<int>(acc, k);
       const int ch = cb * 64 + 8 * g + k;
       a.out[row * D + ch] = __fdiv_rn(__fmul_rn((float)tot, a.vscale[(size_t)bh * D + ch]), 255.0f);
     } else {
-      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int t = 0; t < a.lcap; t += 8) {
-        const uint2 ent = buf[t + k];
-        const float p = __builtin_bit_cast(float, ent.x);
-        if (VK == 1) {
-          const uint4 raw = *reinterpret_cast<const uint4*>(vbase + (size_t)ent.y * ROWB + g * 16);
-          acc[0] = __builtin_fmaf(p, bf16_lo(raw.x), acc[0]);
-          acc[1] = __builtin_fmaf(p, bf16_hi(raw.x), acc[1]);
-          acc[2] = __builtin_fmaf(p, bf16_lo(raw.y), acc[2]);
-          acc[3] = __builtin_fmaf(p, bf16_hi(raw.y), acc[3]);
-          acc[4] = __builtin_fmaf(p, bf16_lo(raw.z), acc[4]);
-          acc[5] = __builtin_fmaf(p, bf16_hi(raw.z), acc[5]);
-          acc[6] = __builtin_fmaf(p, bf16_lo(raw.w), acc[6]);
-          acc[7] = __builtin_fmaf(p, bf16_hi(raw.w), acc[7]);
-        } else {
-          const float4 r0 = *reinterpret_cast<const float4*>(vbase + (size_t)ent.y * ROWB + g * 32);
-          const float4 r1 = *reinterpret_cast<const float4*>(vbase + (size_t)ent.y * ROWB + g * 32 + 16);
-          acc[0] = __builtin_fmaf(p, r0.x, acc[0]);
-          acc[1] = __builtin_fmaf(p, r0.y, acc[1]);
-          acc[2] = __builtin_fmaf(p, r0.z, acc[2]);
-          acc[3] = __builtin_fmaf(p, r0.w, acc[3]);
-          acc[4] = __builtin_fmaf(p, r1.x, acc[4]);
-          acc[5] = __builtin_fmaf(p, r1.y, acc[5]);
-          acc[6] = __builtin_fmaf(p, r1.z, acc[6]);
-          acc[7] = __builtin_fmaf(p, r1.w, acc[7]);
-        }
-      }
       a.out[row * D + cb * 64 + 8 * g + k] = reduce_scatter8<float>(acc, k);
     }
   }

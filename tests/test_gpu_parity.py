@@ -271,6 +271,24 @@ def test_topn_long_sequence_matches_oracle(n, N, keys, av):
         _check_q8(got, vq.cpu().numpy(), sc.cpu().numpy(), ref, rows, n, f"long q8 n={n}")
 
 
+@pytest.mark.parametrize("N", [100, 600])
+def test_topn_long_sequence_all_ties(N):
+    # every key equal to the query: one logit value for all 3000 keys, so no
+    # threshold can split the candidate buffer and each compaction falls back to
+    # the exact selection, which keeps the lowest key indices
+    n = 3000
+    g = np.random.default_rng(8)
+    x = np.repeat(g.standard_normal((1, 1, 1, 64)).astype(np.float32), n, axis=2)
+    qb, _, _ = oracle.pack(x, oracle.SIGN)
+    v = torch.from_numpy(g.standard_normal((1, 1, n, 64)).astype(np.float32)).to(torch.bfloat16)
+    rows = sample_rows(n, 200, 9)
+    out, idx = _run_topn(qb, qb, None, None, None, v, N)
+    ref = oracle.attention(qb, qb, f32(v), top_n=N, rows=rows, want_idx=True)
+    assert np.array_equal(idx.reshape(-1, N)[rows], ref["idx"])
+    assert np.all(idx.reshape(-1, N) == np.arange(N))
+    assert_close(out.reshape(-1, 64)[rows], ref["out"], f"all ties N={N}")
+
+
 def test_topn_c5_full_size_sampled():
     w = synth.workload("c5")
     g = synth.generate(w)
