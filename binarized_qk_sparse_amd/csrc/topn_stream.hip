@@ -4,15 +4,17 @@
 // Same method and arithmetic as the resident kernel (Hamming Attention
 // Distillation summary: per-query top-N; BinaryAttention sections 2.2-2.4:
 // scaled codes, bias, quantized A*V).  Differences:
-//  * keys stream through LDS in chunks of kChunk keys (codes, alpha_k and the
+//  * keys stream through LDS in chunks of 128 keys per wave (codes, alpha_k and the
 //    bias offsets the workgroup's queries touch), shared by the workgroup's
 //    waves, which process one query each in lockstep over the chunks;
 //  * the top-N is streaming: a per-wave candidate buffer in LDS admits keys
-//    whose logit beats the current threshold; when it fills, an exact
-//    selection (ties to the lower key index) keeps the best N and raises the
-//    threshold.  Keys arrive in ascending j, so a later key with a logit equal
-//    to the threshold can never displace a kept one, and the buffer stays in
-//    ascending key order;
+//    whose logit beats the current threshold; when it fills, an interpolation
+//    search finds a value with between N and N + 64 entries at or above it,
+//    which becomes the threshold (an exact selection, ties to the lower key
+//    index, when heavy ties defeat the search), and the exact selection runs
+//    once more at the end.  Keys arrive in ascending j, so a later key with a
+//    logit equal to the threshold can never displace a kept one, and the buffer
+//    stays in ascending key order;
 //  * V (or int8 V) rows are gathered from global memory (L2), eight lanes per
 //    kept key.
 #include <float.h>
@@ -27,11 +29,11 @@
 namespace had {
 namespace {
 
-// head_dim D is 64 or 128 (codes of D / 32 words)
-constexpr int kWaves = 16;
-constexpr int kChunk = 2048;  // keys per LDS chunk
+// head_dim D is 64 or 128 (codes of D / 32 words).  A workgroup of W waves
+// (W = 8 or 16) streams keys in LDS chunks of 128 W.
 constexpr int kCap = 768;     // candidate-buffer entries per wave
 constexpr int kR = kCap / 64;
+constexpr int kG = 4;         // 64-key groups per block of the key loop
 
 struct StreamKArgs {
   const uint32_t* qbits;
@@ -47,18 +49,19 @@ struct StreamKArgs {
   float isd;
 };
 
-// LDS layout (bytes) for head_dim D
-template <int D>
+// LDS layout (bytes) for head_dim D and W waves
+template <int D, int W>
 struct Lds {
+  static constexpr int kChunk = 128 * W;                             // keys per chunk
   static constexpr uint32_t kCodeOff = 0;                           // Code<D>[kChunk]
   static constexpr uint32_t kAkOff = kCodeOff + kChunk * (D / 8);   // float[kChunk]
-  static constexpr uint32_t kBiasOff = kAkOff + kChunk * 4;         // float[kChunk + kWaves]
-  static constexpr uint32_t kBufOff = kBiasOff + (kChunk + 64) * 4;  // uint2[kWaves][kCap]
-  static constexpr uint32_t kCandOff = kBufOff + kWaves * kCap * 8;  // uint2[kWaves][64]
-  static constexpr uint32_t kTotal = kCandOff + kWaves * 64 * 8;
+  static constexpr uint32_t kBiasOff = kAkOff + kChunk * 4;         // float[kChunk + W]
+  static constexpr uint32_t kBufOff = kBiasOff + (kChunk + 64) * 4;  // uint2[W][kCap]
+  static constexpr uint32_t kCandOff = kBufOff + W * kCap * 8;      // uint2[W][64]
+  static constexpr uint32_t kTotal = kCandOff + W * 64 * 8;
 };
-static_assert(Lds<128>::kTotal <= 160 * 1024, "LDS");
-static_assert(kChunk % (64 * kWaves) == 0, "chunk loads");
+static_assert(Lds<128, 16>::kTotal <= 160 * 1024, "LDS");
+static_assert(2 * Lds<128, 8>::kTotal <= 160 * 1024, "LDS: two workgroups of eight waves per CU");
 
 // d - 2 h for two codes: popcounts chained through the accumulate operand of
 // v_bcnt_u32_b32 and one 24-bit multiply-add (the compiler would otherwise add
@@ -302,11 +305,13 @@ HAD_DEVICE T reduce_scatter8(T (&acc)[8], int k) {
   return kp + __shfl_xor(snd, 8, 64);
 }
 
-template <int VK, int D>
-__global__ __launch_bounds__(1024) void topn_stream_kernel(const StreamKArgs a) {
+template <int VK, int D, int W>
+__global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int ROWB = row_bytes<VK, D>();
-  using L = Lds<D>;
+  using L = Lds<D, W>;
+  constexpr int kWaves = W;
+  constexpr int kChunk = L::kChunk;
   Code<D>* codes = reinterpret_cast<Code<D>*>(smem + L::kCodeOff);
   float* aks = reinterpret_cast<float*>(smem + L::kAkOff);
   float* biasw = reinterpret_cast<float*>(smem + L::kBiasOff);
@@ -388,23 +393,23 @@ __global__ __launch_bounds__(1024) void topn_stream_kernel(const StreamKArgs a) 
     __syncthreads();
     if (!live) continue;
     const int boff = ilast - i;  // bias window index of chunk key t is t + boff
-    // Blocks of four 64-key groups.  The buffer holds at most kCap - 64 entries
+    // Blocks of kG 64-key groups.  The buffer holds at most kCap - 64 entries
     // between groups, so one more group always fits.  Fast path (a full block
-    // whose admitted keys keep that bound): four logits with fixed LDS offsets,
-    // then the four appends.  Otherwise (a partial block, or a block that fills
+    // whose admitted keys keep that bound): kG logits with fixed LDS offsets,
+    // then the kG appends.  Otherwise (a partial block, or a block that fills
     // the buffer) the groups go one at a time with bounds checks, compacting
     // when the bound is passed; that path recomputes the logits and runs a few
     // times per query.
     const Code<D>* cp = codes + lane;
     const float* akp = aks + lane;
     const float* bp = biasw + boff + lane;
-    for (int s0 = 0; s0 < cl; s0 += 256) {
-      if (s0 + 256 <= cl) {
-        float l[4];
-        uint64_t m[4];
+    for (int s0 = 0; s0 < cl; s0 += 64 * kG) {
+      if (s0 + 64 * kG <= cl) {
+        float l[kG];
+        uint64_t m[kG];
         int tot = 0;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kG; ++u) {
           l[u] = canonical_logit(aqv, akp[s0 + 64 * u], code_dot<D>(cp[s0 + 64 * u], qq), a.isd,
                                  bp[s0 + 64 * u]);
           m[u] = ballot(l[u] > theta);
@@ -412,7 +417,7 @@ __global__ __launch_bounds__(1024) void topn_stream_kernel(const StreamKArgs a) 
         }
         if (cnt + tot <= kCap - 64) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
+          for (int u = 0; u < kG; ++u) {
             if (m[u] != 0) {
               if (l[u] > theta)
                 buf[cnt + (int)mask_rank(m[u])] =
@@ -423,7 +428,7 @@ __global__ __launch_bounds__(1024) void topn_stream_kernel(const StreamKArgs a) 
           continue;
         }
       }
-      for (int g0 = s0; g0 < min(s0 + 256, cl); g0 += 64) {
+      for (int g0 = s0; g0 < min(s0 + 64 * kG, cl); g0 += 64) {
         const int t = g0 + lane;
         const bool ok = t < cl;
         const int tc = ok ? t : 0;
@@ -544,22 +549,32 @@ __global__ __launch_bounds__(1024) void topn_stream_kernel(const StreamKArgs a) 
   }
 }
 
-template <int VK, int D>
-hipError_t launch_vk(const StreamKArgs& ka, dim3 grid, hipStream_t s) {
-  constexpr uint32_t lds = Lds<D>::kTotal;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&topn_stream_kernel<VK, D>),
+template <int VK, int D, int W>
+hipError_t launch_vk(StreamKArgs ka, int64_t BH, hipStream_t s) {
+  constexpr uint32_t lds = Lds<D, W>::kTotal;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&topn_stream_kernel<VK, D, W>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((topn_stream_kernel<VK, D>), grid, dim3(64 * kWaves), lds, s, ka);
+  ka.tiles = (ka.n + W - 1) / W;
+  const dim3 grid((unsigned)(BH * ka.tiles));
+  hipLaunchKernelGGL((topn_stream_kernel<VK, D, W>), grid, dim3(64 * W), lds, s, ka);
   return hipGetLastError();
 }
 
+// Sixteen waves per workgroup (one per CU) for the longest sequences, where the
+// larger chunks halve the key traffic into LDS; eight (two workgroups per CU)
+// below, where the two workgroups' selection and A*V tails overlap.
+template <int VK, int D>
+hipError_t launch_w(const StreamKArgs& ka, int64_t BH, hipStream_t s) {
+  return ka.n > 4096 ? launch_vk<VK, D, 16>(ka, BH, s) : launch_vk<VK, D, 8>(ka, BH, s);
+}
+
 template <int D>
-hipError_t launch_d(const StreamKArgs& ka, int vk, dim3 grid, hipStream_t s) {
+hipError_t launch_d(const StreamKArgs& ka, int vk, int64_t BH, hipStream_t s) {
   switch (vk) {
-    case 0: return launch_vk<0, D>(ka, grid, s);
-    case 1: return launch_vk<1, D>(ka, grid, s);
-    default: return launch_vk<2, D>(ka, grid, s);
+    case 0: return launch_w<0, D>(ka, BH, s);
+    case 1: return launch_w<1, D>(ka, BH, s);
+    default: return launch_w<2, D>(ka, BH, s);
   }
 }
 
@@ -583,10 +598,9 @@ hipError_t launch_topn_stream(const AttnParams& p, hipStream_t s) {
   ka.n = (int)p.n;
   ka.keep = (int)p.keep;
   ka.lcap = (int)((p.keep + 7) / 8 * 8);
-  ka.tiles = (int)((p.n + kWaves - 1) / kWaves);
   ka.isd = (float)(1.0 / sqrt((double)p.d));
-  const dim3 grid((unsigned)(p.B * p.H * ka.tiles));
-  return p.d == 128 ? launch_d<128>(ka, p.v_kind, grid, s) : launch_d<64>(ka, p.v_kind, grid, s);
+  const int64_t BH = p.B * p.H;
+  return p.d == 128 ? launch_d<128>(ka, p.v_kind, BH, s) : launch_d<64>(ka, p.v_kind, BH, s);
 }
 
 }  // namespace had
