@@ -138,6 +138,35 @@ HAD_DEVICE float from_ordered_key(uint32_t k) {
   return __builtin_bit_cast(float, b);
 }
 
+// The rr-th largest (1-based) of the values x held by lanes [0, cnt) of the wave
+// (1 <= rr <= cnt <= 64), by quickselect: each round compares every live value
+// with a pivot read from one live lane and keeps the side that holds the rank.
+// A round removes at least the pivot, so at most cnt rounds run; the pivot lane
+// is the first live one at or after a start position that moves every round, so
+// values in lane order do not make every round remove only one value.
+HAD_DEVICE uint32_t wave_select_desc(uint32_t x, int cnt, int rr) {
+  uint64_t live = cnt >= 64 ? ~0ull : ((1ull << cnt) - 1ull);
+  int rem = rr;
+  uint32_t start = 0;
+  for (;;) {
+    const uint64_t from = live & (~0ull << start);
+    const int p = (int)__builtin_ctzll(from != 0 ? from : live);
+    const uint32_t pv = (uint32_t)__builtin_amdgcn_readlane((int)x, p);
+    const uint64_t gt = ballot(x > pv) & live;
+    const int g = __builtin_popcountll(gt);
+    if (g >= rem) {
+      live = gt;
+    } else {
+      const uint64_t eq = ballot(x == pv) & live;
+      const int e = __builtin_popcountll(eq);
+      if (g + e >= rem) return pv;
+      rem -= g + e;
+      live &= ~(gt | eq);
+    }
+    start = (start + 23u) & 63u;
+  }
+}
+
 // Canonical float32 logit: each operation rounded as written, no contraction.
 HAD_DEVICE float canonical_logit(float aq, float ak, int dot, float inv_sqrt_d, float bias) {
   float t = __fmul_rn(aq, ak);

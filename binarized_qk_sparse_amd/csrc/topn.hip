@@ -22,7 +22,7 @@
 //        byte-packed distances (SWAR add/and/popcount), starting from the
 //        previous query's tau.
 //        float keys: bisection on the logit value until at most 64 candidates
-//        straddle the threshold, then an exact radix search among them;
+//        straddle the threshold, then an exact quickselect among them;
 //      ties at the threshold go to the lower key index;
 //   3. compacts the kept keys into a per-wave list in LDS (ascending j),
 //   4. softmax over the list (fp32), and
@@ -451,15 +451,8 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             const uint32_t ck = lane < cb ? cand[lane].x : 0u;
             const int rr = keep - chi;  // how many candidates to take
-            // largest T with #{ck >= T} >= rr: the rr-th largest candidate
-            uint32_t L = ordered_key(lo), R = ordered_key(hi);
-            while (R - L > 1u) {
-              const uint32_t M = L + ((R - L) >> 1);
-              if (__builtin_popcountll(ballot(ck >= M)) >= rr)
-                L = M;
-              else
-                R = M;
-            }
+            // the rr-th largest candidate (lanes >= cb hold 0, below every key)
+            const uint32_t L = wave_select_desc(ck, cb, rr);
             vstar = from_ordered_key(L);
             need = keep - chi - __builtin_popcountll(ballot(ck > L));
           }

@@ -154,14 +154,7 @@ HAD_DEVICE int select_compact(uint2* buf, uint2* cand, int cnt, int keep, int la
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       const uint32_t ck = lane < cb ? cand[lane].x : 0u;
       const int rr = keep - chi;
-      uint32_t L = ordered_key(lo), R = ordered_key(hi);
-      while (R - L > 1u) {
-        const uint32_t M = L + ((R - L) >> 1);
-        if (__builtin_popcountll(ballot(ck >= M)) >= rr)
-          L = M;
-        else
-          R = M;
-      }
+      const uint32_t L = wave_select_desc(ck, cb, rr);  // lanes >= cb hold 0, below every key
       vstar = from_ordered_key(L);
       need = keep - chi - __builtin_popcountll(ballot(ck > L));
     }
