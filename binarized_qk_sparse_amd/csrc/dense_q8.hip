@@ -81,20 +81,38 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
   if (BIAS)
     for (int o = tid; o < 2 * n - 1 + NPAD; o += 256)
       biasw[o] = o < 2 * n - 1 ? a.bias[(size_t)hh * (2 * n - 1) + o] : 0.0f;
-  const uint32_t* vsrc = reinterpret_cast<const uint32_t*>(a.vq + (size_t)bh * n * D);
-  for (int e = tid; e < NPAD * (D / 4); e += 256) {
-    const int j = e / (D / 4), c4 = 4 * (e % (D / 4));
-    const uint32_t w = j < n ? vsrc[e] : 0u;
-    vqt[c4 + 0][j] = (int8_t)(w);
-    vqt[c4 + 1][j] = (int8_t)(w >> 8);
-    vqt[c4 + 2][j] = (int8_t)(w >> 16);
-    vqt[c4 + 3][j] = (int8_t)(w >> 24);
+  // int8 V transposed, four keys x four channels per step: one 32-bit load per
+  // key, a byte transpose by v_perm, one 32-bit LDS store per channel.  Threads
+  // with consecutive ids take consecutive key blocks of one channel group, so the
+  // stores of a wave fill consecutive words of the same rows.
+  const uint8_t* vsrc = reinterpret_cast<const uint8_t*>(a.vq + (size_t)bh * n * D);
+  constexpr int KB = NPAD / 4;  // key blocks
+  for (int e = tid; e < KB * (D / 4); e += 256) {
+    const int jb = 4 * (e % KB), c4 = 4 * (e / KB);
+    uint32_t w[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      w[r] = jb + r < n ? *reinterpret_cast<const uint32_t*>(vsrc + (size_t)(jb + r) * D + c4) : 0u;
+    const uint32_t lo01 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // w0.b0 w1.b0 w0.b1 w1.b1
+    const uint32_t hi01 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // w0.b2 w1.b2 w0.b3 w1.b3
+    const uint32_t lo23 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+    *reinterpret_cast<uint32_t*>(&vqt[c4 + 0][jb]) = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+    *reinterpret_cast<uint32_t*>(&vqt[c4 + 1][jb]) = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+    *reinterpret_cast<uint32_t*>(&vqt[c4 + 2][jb]) = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+    *reinterpret_cast<uint32_t*>(&vqt[c4 + 3][jb]) = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
   }
   __syncthreads();
-  if (tid < D) {
+  // column sums of int8 V: four threads per channel, each a quarter of the key
+  // blocks summed four keys at a time by v_dot4_i32_i8 against ones
+  for (int e = tid; e < 4 * D; e += 256) {
+    const int c = e >> 2, part = e & 3;
     int s = 0;
-    for (int j = 0; j < NPAD; ++j) s += vqt[tid][j];
-    colsum[tid] = s;
+    for (int b = part; b < KB; b += 4)
+      s = __builtin_amdgcn_sdot4(*reinterpret_cast<const int*>(&vqt[c][4 * b]), 0x01010101, s, false);
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    if (part == 0) colsum[c] = s;
   }
   __syncthreads();
 
@@ -147,14 +165,12 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
     for (int nt = 0; nt < NT; ++nt) acc[nt] = v4i{0, 0, 0, 0};
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
+      // v_cvt_pk_u8_f32 rounds to nearest even, clamps to [0, 255] and writes
+      // the byte in place: A_q four to a register; xor 0x80 turns each into A_q - 128
       uint32_t w[2] = {0u, 0u};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float qv = fminf(fmaxf(rintf(lg[ks][e] * q255), 0.0f), 255.0f);
-        const uint32_t a8 = (uint32_t)((int)qv - 128) & 0xffu;
-        w[e >> 2] |= a8 << (8 * (e & 3));
-      }
-      const long A = (long)(((uint64_t)w[1] << 32) | w[0]);
+      for (int e = 0; e < 8; ++e) w[e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(lg[ks][e] * q255, e & 3, w[e >> 2]);
+      const long A = (long)((((uint64_t)w[1] << 32) | w[0]) ^ 0x8080808080808080ull);
       const int kk0 = ks * 32 + kg * 8;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
