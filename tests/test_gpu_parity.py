@@ -57,6 +57,20 @@ def test_pack_ragged_and_special_values(d, n, dtype, mode):
     assert np.array_equal(mu.cpu().numpy(), om)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_pack_sign_nonfinite(dtype):
+    # plain sign is the test x < 0: -inf gives the -1 code, +inf and NaN (either sign) +1
+    x = np.random.default_rng(12).standard_normal((1, 2, 37, 64)).astype(np.float32)
+    x[0, 0, 0, :6] = [-np.inf, np.inf, np.nan, -np.nan, -0.0, 0.0]
+    x[0, 1, 36, -4:] = [-np.inf, -np.nan, np.inf, -1e-30]
+    xt = torch.from_numpy(x).to(dtype)
+    bits, alpha, mu = ops.had_pack(xt.to(DEV), synth.SIGN)
+    torch.cuda.synchronize()
+    ob, oa, om = oracle.pack(f32(xt), synth.SIGN)
+    assert np.array_equal(u32(bits), ob)
+    assert np.array_equal(alpha.cpu().numpy(), oa) and np.array_equal(mu.cpu().numpy(), om)
+
+
 @pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("n", [1, 100, 197, 700])
 @pytest.mark.parametrize("mode", [synth.SIGN, synth.MEAN_SIGN])
