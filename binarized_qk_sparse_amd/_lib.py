@@ -33,6 +33,7 @@ EXPORTS = (
     "had_pack_qk",
     "had_attention_topn",
     "binattn_dense_q8",
+    "binattn_dense_q8_fused",
 )
 
 _lib = None
@@ -66,6 +67,8 @@ def load() -> ctypes.CDLL:
     lib.had_attention_topn.restype = I
     lib.binattn_dense_q8.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, I64, P, P, SZ, P]
     lib.binattn_dense_q8.restype = I
+    lib.binattn_dense_q8_fused.argtypes = [P, P, I, I, P, P, I, I64, I64, I64, I64, P, P]
+    lib.binattn_dense_q8_fused.restype = I
     if lib.had_abi_version() != HAD_ABI_VERSION:
         raise ImportError("libhad.so ABI version mismatch")
     _lib = lib

@@ -10,8 +10,6 @@
 
 namespace had {
 
-int64_t dense_q8_max_n();
-
 static size_t align256(size_t x) { return (x + 255u) & ~(size_t)255u; }
 
 WorkspaceLayout workspace_layout(int64_t B, int64_t H, int64_t n, int64_t d) {
@@ -270,6 +268,33 @@ int binattn_dense_q8(const uint32_t* qbits, const uint32_t* kbits, const float* 
   p.out = out;
   p.idx = nullptr;
   return launch_status(launch_dense_q8(p, s), fn);
+}
+
+int binattn_dense_q8_fused(const void* q, const void* k, int qk_dtype, int mode, const float* bias_table,
+                           const void* v, int v_dtype, int64_t B, int64_t H, int64_t n, int64_t d, float* out,
+                           void* stream) {
+  static const char* fn = "binattn_dense_q8_fused";
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return fail(HAD_ERR_INVALID_ARG, fn, "NULL tensor");
+  if (!sizes_ok(B, H, n, d)) return fail(HAD_ERR_INVALID_ARG, fn, "sizes must be positive and B*H*n*d < 2^31");
+  if (qk_dtype != HAD_F32 && qk_dtype != HAD_BF16) return fail(HAD_ERR_INVALID_ARG, fn, "unknown qk_dtype");
+  if (v_dtype != HAD_F32 && v_dtype != HAD_BF16) return fail(HAD_ERR_INVALID_ARG, fn, "unknown v_dtype");
+  if (mode != HAD_SIGN && mode != HAD_MEAN_SIGN) return fail(HAD_ERR_INVALID_ARG, fn, "unknown mode");
+  if (d != 64 && d != 128) return fail(HAD_ERR_UNSUPPORTED, fn, "d must be 64 or 128");
+  if (n > dense_q8_max_n()) return fail(HAD_ERR_UNSUPPORTED, fn, "n above what one workgroup stages");
+  DenseFusedParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.qk_dtype = qk_dtype;
+  p.v_dtype = v_dtype;
+  p.mode = mode;
+  p.bias = bias_table;
+  p.B = B;
+  p.H = H;
+  p.n = n;
+  p.d = d;
+  p.out = out;
+  return launch_status(launch_dense_q8_fused(p, static_cast<hipStream_t>(stream)), fn);
 }
 
 }  // extern "C"

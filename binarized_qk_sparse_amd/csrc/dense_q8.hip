@@ -20,6 +20,8 @@
 // A against the transposed int8 V tile staged in LDS.
 #include <float.h>
 
+#include <type_traits>
+
 #include "had_device.hpp"
 #include "had_internal.h"
 #include "../../include/had.h"
@@ -42,7 +44,40 @@ struct DenseKArgs {
   float* out;
   int H, n;
   float isd;
+  // fused entry point: raw Q, K, V (each fp32 or bf16) instead of the above
+  const void* xq;
+  const void* xk;
+  const void* xv;
+  int qk_bf16, v_bf16, mean;
 };
+
+// Eight consecutive elements from index i of a fp32 or bf16 tensor (16- or 32-byte read).
+HAD_DEVICE void load8_any(const void* base, size_t i, bool bf16, float (&v)[8]) {
+  if (bf16) {
+    const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + i);
+    v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x);
+    v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+    v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z);
+    v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + i);
+    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + i + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+// Four consecutive elements (8- or 16-byte read).
+HAD_DEVICE void load4_any(const void* base, size_t i, bool bf16, float (&v)[4]) {
+  if (bf16) {
+    const uint2 a = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + i);
+    v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x);
+    v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + i);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  }
+}
 
 // Sum / max of a row whose values live in lanes l, l^16, l^32, l^48.
 HAD_DEVICE float row4_max(float v) {
@@ -54,14 +89,28 @@ HAD_DEVICE float row4_sum(float v) {
   return v + __shfl_xor(v, 32, 64);
 }
 
-template <int NK, bool BIAS, int D>  // key steps of 32; NPAD = 32 * NK >= n
+// FUSED (binattn_dense_q8_fused): the workgroup also binarizes Q and K and
+// quantizes V of its head into LDS first, with the arithmetic, thread layout
+// and summation order of the separate passes (had_pack's column sums, codes and
+// alpha; the V scale and int8 codes of the attention entry points), so both
+// routes give the same bits.
+template <int NK, bool BIAS, int D, bool FUSED>  // key steps of 32; NPAD = 32 * NK >= n
 __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
   constexpr int NPAD = 32 * NK;
   constexpr int NT = D / 16;  // channel tiles
+  constexpr int FP = FUSED ? NPAD : 1;
+  constexpr int FD = FUSED ? D : 1;
+  constexpr int RPP = 256 / (D / 8);  // rows per pass with eight channels per thread
   __shared__ __align__(16) int8_t vqt[D][NPAD];  // Vq transposed: [channel][key]
   __shared__ __align__(16) Code<D> kcode[NPAD];
   __shared__ __align__(16) float akk[NPAD];
   __shared__ int colsum[D];
+  __shared__ __align__(16) Code<D> qcode[FP];      // fused: query codes
+  __shared__ float aqs[FP];                        // fused: query alphas
+  __shared__ float vsc[FD];                        // fused: V scales
+  __shared__ float mus[FUSED ? 2 : 1][FD];         // fused: mu of Q and K
+  __shared__ double dred[FUSED ? RPP : 1][FD];     // fused: column-sum partials
+  __shared__ float fred[FUSED ? RPP : 1][FD];      // fused: column-max partials
   extern __shared__ float biasw[];  // [2n - 1 + NPAD]: the table, then zeros read by padding keys
 
   const int tid = threadIdx.x;
@@ -69,14 +118,115 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
   const int hh = bh % a.H;
   const int n = a.n;
 
-  // ---- stage codes, scales, bias table and the transposed int8 V of this head
-  for (int j = tid; j < NPAD; j += 256) {
-    Code<D> c = load_code<D>(a.kbits, (size_t)bh * n + (j < n ? j : 0));
-    if (j >= n)
+  if constexpr (FUSED) {
+    const bool qkb = a.qk_bf16 != 0, mean = a.mean != 0;
+    const int r_off = tid / (D / 8), cg = tid % (D / 8);
+    // ---- mu (mean reading): per-channel column sums in float64 over the head's tokens
+    if (mean) {
 #pragma unroll
-      for (int w = 0; w < D / 32; ++w) c.w[w] = 0u;
-    kcode[j] = c;
-    akk[j] = (j < n && a.ak != nullptr) ? a.ak[(size_t)bh * n + j] : 1.0f;
+      for (int t = 0; t < 2; ++t) {
+        const void* x = t == 0 ? a.xq : a.xk;
+        double sm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int k = 0; k < 256 / RPP; ++k) {
+          const int r = r_off + RPP * k;
+          if (r < n) {
+            float v[8];
+            load8_any(x, ((size_t)bh * n + r) * D + 8 * cg, qkb, v);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) sm[c] += (double)v[c];
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) dred[r_off][8 * cg + c] = sm[c];
+        __syncthreads();
+        if (tid < D) {
+          double acc = 0.0;
+          for (int rp = 0; rp < RPP; ++rp) acc += dred[rp][tid];
+          mus[t][tid] = (float)((0.0 + acc) / (double)n);
+        }
+        __syncthreads();
+      }
+    }
+    // ---- codes (x - mu < 0, or x < 0) and alpha = mean |x - mu|: D/32 lanes per token
+    constexpr int LPR = D / 32;
+    constexpr int RPW = 256 / LPR;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const void* x = t == 0 ? a.xq : a.xk;
+      Code<D>* code = t == 0 ? qcode : kcode;
+      float* al = t == 0 ? aqs : akk;
+      const int part = tid % LPR;
+      for (int r0 = 0; r0 < n; r0 += RPW) {
+        const int r = r0 + tid / LPR;
+        const bool live = r < n;
+        const int rr = live ? r : n - 1;  // dead lanes read a valid row, write nothing
+        float v[32];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float e[8];
+          load8_any(x, ((size_t)bh * n + rr) * D + 32 * part + 8 * k, qkb, e);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) v[8 * k + c] = e[c];
+        }
+        double asum = 0.0;
+        if (mean) {
+          const float* m = &mus[t][32 * part];
+#pragma unroll
+          for (int c = 0; c < 32; ++c) v[c] = __fsub_rn(v[c], m[c]);
+#pragma unroll
+          for (int c = 0; c < 32; ++c) asum += fabs((double)v[c]);
+#pragma unroll
+          for (int off = 1; off < LPR; off <<= 1) asum += __shfl_xor(asum, off, 64);
+        }
+        uint32_t w = 0;
+#pragma unroll
+        for (int c = 0; c < 32; ++c) w |= (uint32_t)(v[c] < 0.0f) << c;
+        if (live) {
+          code[rr].w[part] = w;
+          if (part == 0) al[rr] = mean ? (float)(asum / (double)D) : 1.0f;
+        }
+      }
+    }
+    for (int j = n + tid; j < NPAD; j += 256) {  // padding keys: code 0, alpha 1
+#pragma unroll
+      for (int w = 0; w < D / 32; ++w) kcode[j].w[w] = 0u;
+      akk[j] = 1.0f;
+    }
+    // ---- V scales: per-channel max |v| over the head's tokens, / 127
+    {
+      const bool vb = a.v_bf16 != 0;
+      float mx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int k = 0; k < 256 / RPP; ++k) {
+        const int r = r_off + RPP * k;
+        if (r < n) {
+          float v[8];
+          load8_any(a.xv, ((size_t)bh * n + r) * D + 8 * cg, vb, v);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) mx[c] = fmaxf(mx[c], fabsf(v[c]));
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) fred[r_off][8 * cg + c] = mx[c];
+      __syncthreads();
+      if (tid < D) {
+        float acc = 0.0f;
+        for (int rp = 0; rp < RPP; ++rp) acc = fmaxf(acc, fred[rp][tid]);
+        vsc[tid] = __fdiv_rn(acc, 127.0f);
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- stage codes, scales, bias table and the transposed int8 V of this head
+  if constexpr (!FUSED) {
+    for (int j = tid; j < NPAD; j += 256) {
+      Code<D> c = load_code<D>(a.kbits, (size_t)bh * n + (j < n ? j : 0));
+      if (j >= n)
+#pragma unroll
+        for (int w = 0; w < D / 32; ++w) c.w[w] = 0u;
+      kcode[j] = c;
+      akk[j] = (j < n && a.ak != nullptr) ? a.ak[(size_t)bh * n + j] : 1.0f;
+    }
   }
   if (BIAS)
     for (int o = tid; o < 2 * n - 1 + NPAD; o += 256)
@@ -85,14 +235,34 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
   // key, a byte transpose by v_perm, one 32-bit LDS store per channel.  Threads
   // with consecutive ids take consecutive key blocks of one channel group, so the
   // stores of a wave fill consecutive words of the same rows.
-  const uint8_t* vsrc = reinterpret_cast<const uint8_t*>(a.vq + (size_t)bh * n * D);
+  // (fused: the int8 codes come from V itself, with the scales above)
   constexpr int KB = NPAD / 4;  // key blocks
   for (int e = tid; e < KB * (D / 4); e += 256) {
     const int jb = 4 * (e % KB), c4 = 4 * (e / KB);
     uint32_t w[4];
+    if constexpr (FUSED) {
+      float s4[4], inv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      w[r] = jb + r < n ? *reinterpret_cast<const uint32_t*>(vsrc + (size_t)(jb + r) * D + c4) : 0u;
+      for (int c = 0; c < 4; ++c) {
+        s4[c] = vsc[c4 + c];
+        inv[c] = __builtin_amdgcn_rcpf(s4[c]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        w[r] = 0u;
+        if (jb + r < n) {
+          float x[4];
+          load4_any(a.xv, ((size_t)bh * n + jb + r) * D + c4, a.v_bf16 != 0, x);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) w[r] |= quant_i8(x[c], s4[c], inv[c]) << (8 * c);
+        }
+      }
+    } else {
+      const uint8_t* vsrc = reinterpret_cast<const uint8_t*>(a.vq + (size_t)bh * n * D);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        w[r] = jb + r < n ? *reinterpret_cast<const uint32_t*>(vsrc + (size_t)(jb + r) * D + c4) : 0u;
+    }
     const uint32_t lo01 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // w0.b0 w1.b0 w0.b1 w1.b1
     const uint32_t hi01 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // w0.b2 w1.b2 w0.b3 w1.b3
     const uint32_t lo23 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
@@ -124,8 +294,15 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
     const int i = tile * 16 + r16;  // this lane's query row (may be padding)
     const int iq = i < n ? i : n - 1;
     const size_t row = (size_t)bh * n + iq;
-    const Code<D> qq = load_code<D>(a.qbits, row);
-    const float aqv = a.aq != nullptr ? a.aq[row] : 1.0f;
+    Code<D> qq;
+    float aqv;
+    if constexpr (FUSED) {
+      qq = qcode[iq];
+      aqv = aqs[iq];
+    } else {
+      qq = load_code<D>(a.qbits, row);
+      aqv = a.aq != nullptr ? a.aq[row] : 1.0f;
+    }
     const float* brow = biasw + (n - 1 - iq);  // bias of key j is brow[j]
 
     // ---- logits of this lane's A elements
@@ -184,7 +361,7 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int c = nt * 16 + r16;
-      const float sc = a.vscale[(size_t)bh * D + c];
+      const float sc = FUSED ? vsc[c] : a.vscale[(size_t)bh * D + c];
       const int cs = 128 * colsum[c];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -196,20 +373,34 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
   }
 }
 
-template <int NK, int D>
+template <int NK, int D, bool FUSED>
 hipError_t launch_nkd(const DenseKArgs& ka, int64_t BH, hipStream_t s) {
   if (ka.bias != nullptr) {
     const size_t lds = sizeof(float) * (2 * ka.n - 1 + 32 * NK);
-    hipLaunchKernelGGL((dense_q8_kernel<NK, true, D>), dim3((unsigned)BH), dim3(64 * kWaves), lds, s, ka);
+    hipLaunchKernelGGL((dense_q8_kernel<NK, true, D, FUSED>), dim3((unsigned)BH), dim3(64 * kWaves), lds, s, ka);
   } else {
-    hipLaunchKernelGGL((dense_q8_kernel<NK, false, D>), dim3((unsigned)BH), dim3(64 * kWaves), 0, s, ka);
+    hipLaunchKernelGGL((dense_q8_kernel<NK, false, D, FUSED>), dim3((unsigned)BH), dim3(64 * kWaves), 0, s, ka);
   }
   return hipGetLastError();
 }
 
-template <int NK>
-hipError_t launch_nk(const DenseKArgs& ka, int d, int64_t BH, hipStream_t s) {
-  return d == 128 ? launch_nkd<NK, 128>(ka, BH, s) : launch_nkd<NK, 64>(ka, BH, s);
+template <bool FUSED>
+hipError_t launch_n(const DenseKArgs& ka, int d, int64_t BH, hipStream_t s) {
+  const int nk = (ka.n + 31) / 32;
+  auto go = [&](auto NKc) {
+    constexpr int NK = decltype(NKc)::value;
+    return d == 128 ? launch_nkd<NK, 128, FUSED>(ka, BH, s) : launch_nkd<NK, 64, FUSED>(ka, BH, s);
+  };
+  switch (nk) {
+    case 1: return go(std::integral_constant<int, 1>{});
+    case 2: return go(std::integral_constant<int, 2>{});
+    case 3: return go(std::integral_constant<int, 3>{});
+    case 4: return go(std::integral_constant<int, 4>{});
+    case 5: return go(std::integral_constant<int, 5>{});
+    case 6: return go(std::integral_constant<int, 6>{});
+    case 7: return go(std::integral_constant<int, 7>{});
+    default: return go(std::integral_constant<int, 8>{});
+  }
 }
 
 }  // namespace
@@ -231,18 +422,24 @@ hipError_t launch_dense_q8(const AttnParams& p, hipStream_t s) {
   ka.H = (int)p.H;
   ka.n = (int)p.n;
   ka.isd = (float)(1.0 / sqrt((double)p.d));
-  const int nk = (int)((p.n + 31) / 32);
-  const int64_t BH = p.B * p.H;
-  switch (nk) {
-    case 1: return launch_nk<1>(ka, (int)p.d, BH, s);
-    case 2: return launch_nk<2>(ka, (int)p.d, BH, s);
-    case 3: return launch_nk<3>(ka, (int)p.d, BH, s);
-    case 4: return launch_nk<4>(ka, (int)p.d, BH, s);
-    case 5: return launch_nk<5>(ka, (int)p.d, BH, s);
-    case 6: return launch_nk<6>(ka, (int)p.d, BH, s);
-    case 7: return launch_nk<7>(ka, (int)p.d, BH, s);
-    default: return launch_nk<8>(ka, (int)p.d, BH, s);
-  }
+  return launch_n<false>(ka, (int)p.d, p.B * p.H, s);
+}
+
+hipError_t launch_dense_q8_fused(const DenseFusedParams& p, hipStream_t s) {
+  if ((p.d != 64 && p.d != 128) || p.n > dense_q8_max_n()) return hipErrorInvalidValue;
+  DenseKArgs ka{};
+  ka.bias = p.bias;
+  ka.out = p.out;
+  ka.H = (int)p.H;
+  ka.n = (int)p.n;
+  ka.isd = (float)(1.0 / sqrt((double)p.d));
+  ka.xq = p.q;
+  ka.xk = p.k;
+  ka.xv = p.v;
+  ka.qk_bf16 = p.qk_dtype == HAD_BF16;
+  ka.v_bf16 = p.v_dtype == HAD_BF16;
+  ka.mean = p.mode == HAD_MEAN_SIGN;
+  return launch_n<true>(ka, (int)p.d, p.B * p.H, s);
 }
 
 }  // namespace had

@@ -167,6 +167,21 @@ HAD_DEVICE uint32_t wave_select_desc(uint32_t x, int cnt, int rr) {
   }
 }
 
+// Per-channel int8 code of x at scale s (inv = v_rcp_f32(s)):
+// clamp(rint(fl(x / s)), -127, 127) as a byte, 0 when s is 0.  x * (1/s) is
+// within 2 ulp of the correctly rounded quotient fl(x / s), i.e. within 2^-16
+// for |x / s| <= 128, so the two can round to different integers only when the
+// quotient lies near a tie k + 1/2; there the exact division decides (as it
+// does for a denormal scale, whose reciprocal is not representable).
+HAD_DEVICE uint32_t quant_i8(float x, float s, float inv) {
+  if (!(s > 0.0f)) return 0u;
+  float y = x * inv;
+  if (s < 0x1p-125f || fabsf(y - floorf(y) - 0.5f) < 0x1p-12f) y = __fdiv_rn(x, s);
+  float r = rintf(y);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (uint32_t)((int32_t)r) & 0xffu;
+}
+
 // Canonical float32 logit: each operation rounded as written, no contraction.
 HAD_DEVICE float canonical_logit(float aq, float ak, int dot, float inv_sqrt_d, float bias) {
   float t = __fmul_rn(aq, ak);

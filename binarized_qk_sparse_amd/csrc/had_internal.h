@@ -59,6 +59,20 @@ hipError_t launch_topn_mfma(const AttnParams& p, hipStream_t s);
 hipError_t launch_topn_stream(const AttnParams& p, hipStream_t s);
 int64_t topn_stream_max_keep();
 hipError_t launch_dense_q8(const AttnParams& p, hipStream_t s);
+int64_t dense_q8_max_n();
+
+// ---- binarize + quantize + dense q8 attention in one launch (dense_q8.hip)
+struct DenseFusedParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  int qk_dtype, v_dtype;  // HAD_F32 / HAD_BF16
+  int mode;               // HAD_SIGN / HAD_MEAN_SIGN
+  const float* bias;
+  int64_t B, H, n, d;
+  float* out;
+};
+hipError_t launch_dense_q8_fused(const DenseFusedParams& p, hipStream_t s);
 
 // Device scratch layout inside the caller's workspace.
 struct WorkspaceLayout {

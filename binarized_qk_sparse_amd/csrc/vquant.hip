@@ -80,20 +80,6 @@ __global__ __launch_bounds__(kThreads) void vscale_kernel(const float* __restric
   }
 }
 
-// clamp(rint(fl(x / s)), -127, 127).  x * (1/s) (v_rcp_f32 and one multiply)
-// is within 2 ulp of the correctly rounded quotient fl(x / s), i.e. within
-// 2^-16 for |x / s| <= 128, so the two can round to different integers only
-// when the quotient lies near a tie k + 1/2; there the exact division decides
-// (as it does for a denormal scale, whose reciprocal is not representable).
-HAD_DEVICE uint32_t q8(float x, float s, float inv) {
-  if (!(s > 0.0f)) return 0u;
-  float y = x * inv;
-  if (s < 0x1p-125f || fabsf(y - floorf(y) - 0.5f) < 0x1p-12f) y = __fdiv_rn(x, s);
-  float r = rintf(y);
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
-  return (uint32_t)((int32_t)r) & 0xffu;
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void vq_kernel(const T* __restrict__ v, uint32_t rows, uint32_t n,
                                                       const float* __restrict__ scale, int8_t* __restrict__ vq) {
@@ -110,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void vq_kernel(const T* __restrict__ v, u
   const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
   uint32_t b[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) b[c] = q8(x[c], s[c], __builtin_amdgcn_rcpf(s[c]));
+  for (int c = 0; c < 8; ++c) b[c] = quant_i8(x[c], s[c], __builtin_amdgcn_rcpf(s[c]));
   uint2 o;
   o.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
   o.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
@@ -153,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void vq_fused_kernel(const T* __restrict_
   const float* sp = &sc[min(r / n - h0, 1u)][8 * cg];
   uint32_t b[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) b[c] = q8(x[c], sp[c], __builtin_amdgcn_rcpf(sp[c]));
+  for (int c = 0; c < 8; ++c) b[c] = quant_i8(x[c], sp[c], __builtin_amdgcn_rcpf(sp[c]));
   uint2 o;
   o.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
   o.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);

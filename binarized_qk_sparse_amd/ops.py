@@ -131,6 +131,23 @@ def binattn_dense_q8(qbits: torch.Tensor, kbits: torch.Tensor, v: torch.Tensor, 
     return out
 
 
+def binattn_dense_q8_fused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: int = HAD_MEAN_SIGN, *,
+                           bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Binarize Q, K and quantize V on chip, then dense q8 attention, in one launch (n <= 256);
+    returns out f32 [B,H,n,d], the same bits as had_pack_qk followed by binattn_dense_q8."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, nm)
+    if q.shape != k.shape or q.dtype != k.dtype or v.shape != q.shape:
+        raise ValueError("q, k and v must share a shape, and q and k a dtype")
+    B, H, n, d = v.shape
+    if out is None:
+        out = torch.empty((B, H, n, d), dtype=torch.float32, device=v.device)
+    st = _lib.load().binattn_dense_q8_fused(q.data_ptr(), k.data_ptr(), _dtype_code(q), int(mode), _ptr(bias),
+                                            v.data_ptr(), _dtype_code(v), B, H, n, d, out.data_ptr(), _stream())
+    _lib.check("binattn_dense_q8_fused", st)
+    return out
+
+
 def workspace_view(ws: torch.Tensor, B: int, H: int, n: int, d: int):
     """(vq int8 [B,H,n,d], vscale f32 [B,H,d]) views of a workspace after a quantized call."""
     import math

@@ -169,6 +169,29 @@ int binattn_dense_q8(const uint32_t* qbits, const uint32_t* kbits, const float* 
                      int64_t B, int64_t H, int64_t n, int64_t d, float* out, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/*
+ * binattn_dense_q8_fused -- binattn_dense_q8 with the binarization and the V
+ * quantization in the same launch, for short sequences (BinaryAttention
+ * section 2.2 codes and scales, section 2.3 logits, section 2.4 quantized A*V).
+ * One workgroup per (batch, head) binarizes that head's Q and K and quantizes
+ * its V in on-chip memory, then runs the dense q8 attention on them.
+ *
+ *  q, k        [B,H,n,d] of qk_dtype (HAD_F32 or HAD_BF16)
+ *  mode        HAD_SIGN or HAD_MEAN_SIGN (as had_pack)
+ *  bias_table  float32 [H,2n-1] or NULL (B = 0)
+ *  v           [B,H,n,d] of v_dtype (HAD_F32 or HAD_BF16)
+ *  out         out float32 [B,H,n,d]
+ *
+ * The result is bit-identical to had_pack_qk followed by binattn_dense_q8 on
+ * the same inputs (same arithmetic, summation order and rounding).  No
+ * workspace and no intermediate tensor: codes, alpha, mu and the int8 V are not
+ * returned.  n <= 256 and d = 64 or 128, else HAD_ERR_UNSUPPORTED; other errors
+ * as had_pack and binattn_dense_q8.
+ */
+int binattn_dense_q8_fused(const void* q, const void* k, int qk_dtype, int mode, const float* bias_table,
+                           const void* v, int v_dtype, int64_t B, int64_t H, int64_t n, int64_t d, float* out,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

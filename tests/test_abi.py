@@ -153,3 +153,23 @@ def test_dense_validation(args, want):
     st = _lib.load().binattn_dense_q8(a["q"], a["k"], None, None, None, a["v"], _lib.HAD_BF16, a["B"], a["H"],
                                       a["n"], a["d"], a["out"], a["ws"], a["wsz"], None)
     assert st == want
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(q=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(v=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(out=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(B=0), _lib.HAD_ERR_INVALID_ARG),
+    (dict(qkdt=5), _lib.HAD_ERR_INVALID_ARG),
+    (dict(vdt=5), _lib.HAD_ERR_INVALID_ARG),
+    (dict(mode=2), _lib.HAD_ERR_INVALID_ARG),
+    (dict(d=32), _lib.HAD_ERR_UNSUPPORTED),
+    (dict(n=257), _lib.HAD_ERR_UNSUPPORTED),
+])
+def test_dense_fused_validation(args, want):
+    a = dict(q=FAKE, k=FAKE, qkdt=_lib.HAD_BF16, mode=_lib.HAD_MEAN_SIGN, v=FAKE, vdt=_lib.HAD_BF16, B=2, H=3, n=197,
+             d=64, out=FAKE)
+    a.update(args)
+    st = _lib.load().binattn_dense_q8_fused(a["q"], a["k"], a["qkdt"], a["mode"], None, a["v"], a["vdt"], a["B"],
+                                            a["H"], a["n"], a["d"], a["out"], None)
+    assert st == want
