@@ -215,6 +215,9 @@ def main():
     ap.add_argument("--config", default="c3@1024")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused", action="store_true",
+                    help="dense workloads with n <= 256: a step is one binattn_dense_q8_fused launch (binarize, "
+                         "quantize and attend on chip) instead of had_pack_qk + binattn_dense_q8")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the reference kernel that scales "
                          "the HBM byte counters) and exit")
@@ -240,6 +243,9 @@ def main():
     from binarized_qk_sparse_amd import ops, synth
 
     w = synth.workload(args.config)
+    if args.fused and (w.top_n is not None or w.n > 256):
+        print("--fused takes dense workloads with n <= 256 (c4)", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     g = synth.generate(w)
@@ -267,7 +273,10 @@ def main():
 
     def attend():
         s = torch.cuda.current_stream().cuda_stream
-        if w.top_n is None:
+        if args.fused:
+            st = lib.binattn_dense_q8_fused(q.data_ptr(), k.data_ptr(), dt, w.mode, pb, v.data_ptr(),
+                                            ops._dtype_code(v), w.B, w.H, w.n, w.d, out.data_ptr(), s)
+        elif w.top_n is None:
             st = lib.binattn_dense_q8(qb.data_ptr(), kb.data_ptr(), pa, pk, pb, v.data_ptr(), dt, w.B, w.H, w.n,
                                       w.d, out.data_ptr(), ws.data_ptr(), ws.numel(), s)
         else:
@@ -276,7 +285,8 @@ def main():
         ops._lib.check("attention", st)
 
     def step():
-        pack()
+        if not args.fused:  # the fused launch binarizes Q and K itself
+            pack()
         attend()
 
     # eager warm-up (also initialises the kernels' one-time launch attributes)
@@ -410,6 +420,8 @@ def main():
             "head_dim": w.d,
             "top_n": w.top_n,
             "parallelism": "single GPU",
+            "entry_points": "binattn_dense_q8_fused" if args.fused else
+                            ("had_pack_qk + " + ("binattn_dense_q8" if w.top_n is None else "had_attention_topn")),
         },
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -119,23 +119,36 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
   const int n = a.n;
 
   if constexpr (FUSED) {
-    const bool qkb = a.qk_bf16 != 0, mean = a.mean != 0;
+    const bool qkb = a.qk_bf16 != 0, vb = a.v_bf16 != 0, mean = a.mean != 0;
     const int r_off = tid / (D / 8), cg = tid % (D / 8);
+    // Column passes: thread (r_off, cg) takes channels 8 cg .. 8 cg + 7 of rows
+    // r_off + RPP k, k ascending (the separate passes' layout and order); four
+    // rows' reads are issued before any is used.
+    auto col_pass = [&](const void* x, bool bf16, auto&& use) {
+      constexpr int IT = 256 / RPP;  // rows per thread (n <= 256)
+      constexpr int G = IT < 4 ? IT : 4;
+#pragma unroll
+      for (int k0 = 0; k0 < IT; k0 += G) {
+        float v[G][8];
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+          const int r = r_off + RPP * (k0 + u);
+          if (r < n) load8_any(x, ((size_t)bh * n + r) * D + 8 * cg, bf16, v[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < G; ++u)
+          if (r_off + RPP * (k0 + u) < n) use(v[u]);
+      }
+    };
     // ---- mu (mean reading): per-channel column sums in float64 over the head's tokens
     if (mean) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const void* x = t == 0 ? a.xq : a.xk;
         double sm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int k = 0; k < 256 / RPP; ++k) {
-          const int r = r_off + RPP * k;
-          if (r < n) {
-            float v[8];
-            load8_any(x, ((size_t)bh * n + r) * D + 8 * cg, qkb, v);
+        col_pass(t == 0 ? a.xq : a.xk, qkb, [&](const float(&v)[8]) {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) sm[c] += (double)v[c];
-          }
-        }
+          for (int c = 0; c < 8; ++c) sm[c] += (double)v[c];
+        });
 #pragma unroll
         for (int c = 0; c < 8; ++c) dred[r_off][8 * cg + c] = sm[c];
         __syncthreads();
@@ -147,15 +160,23 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
         __syncthreads();
       }
     }
+    // ---- V scales: per-channel max |v| over the head's tokens, / 127
+    {
+      float mx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      col_pass(a.xv, vb, [&](const float(&v)[8]) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) mx[c] = fmaxf(mx[c], fabsf(v[c]));
+      });
+#pragma unroll
+      for (int c = 0; c < 8; ++c) fred[r_off][8 * cg + c] = mx[c];
+    }
     // ---- codes (x - mu < 0, or x < 0) and alpha = mean |x - mu|: D/32 lanes per token
     constexpr int LPR = D / 32;
     constexpr int RPW = 256 / LPR;
+    const int part = tid % LPR;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const void* x = t == 0 ? a.xq : a.xk;
-      Code<D>* code = t == 0 ? qcode : kcode;
-      float* al = t == 0 ? aqs : akk;
-      const int part = tid % LPR;
       for (int r0 = 0; r0 < n; r0 += RPW) {
         const int r = r0 + tid / LPR;
         const bool live = r < n;
@@ -182,8 +203,8 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
 #pragma unroll
         for (int c = 0; c < 32; ++c) w |= (uint32_t)(v[c] < 0.0f) << c;
         if (live) {
-          code[rr].w[part] = w;
-          if (part == 0) al[rr] = mean ? (float)(asum / (double)D) : 1.0f;
+          (t == 0 ? qcode : kcode)[rr].w[part] = w;
+          if (part == 0) (t == 0 ? aqs : akk)[rr] = mean ? (float)(asum / (double)D) : 1.0f;
         }
       }
     }
@@ -192,29 +213,13 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
       for (int w = 0; w < D / 32; ++w) kcode[j].w[w] = 0u;
       akk[j] = 1.0f;
     }
-    // ---- V scales: per-channel max |v| over the head's tokens, / 127
-    {
-      const bool vb = a.v_bf16 != 0;
-      float mx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int k = 0; k < 256 / RPP; ++k) {
-        const int r = r_off + RPP * k;
-        if (r < n) {
-          float v[8];
-          load8_any(a.xv, ((size_t)bh * n + r) * D + 8 * cg, vb, v);
-#pragma unroll
-          for (int c = 0; c < 8; ++c) mx[c] = fmaxf(mx[c], fabsf(v[c]));
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) fred[r_off][8 * cg + c] = mx[c];
-      __syncthreads();
-      if (tid < D) {
-        float acc = 0.0f;
-        for (int rp = 0; rp < RPP; ++rp) acc = fmaxf(acc, fred[rp][tid]);
-        vsc[tid] = __fdiv_rn(acc, 127.0f);
-      }
-      __syncthreads();
+    __syncthreads();  // the column maxima of V are in LDS
+    if (tid < D) {
+      float acc = 0.0f;
+      for (int rp = 0; rp < RPP; ++rp) acc = fmaxf(acc, fred[rp][tid]);
+      vsc[tid] = __fdiv_rn(acc, 127.0f);
     }
+    __syncthreads();
   }
 
   // ---- stage codes, scales, bias table and the transposed int8 V of this head
