@@ -22,6 +22,7 @@ SIGN = 0
 MEAN_SIGN = 1
 AV_F32 = 0
 AV_Q8 = 1
+AV_Q4 = 2  # 4-bit V: 7 levels each side of zero, stored as int8
 
 _lib = None
 
@@ -51,6 +52,8 @@ def _load():
     lib.oracle_logits.restype = None
     lib.oracle_vquant.argtypes = [P, I64, I64, I64, I64, P, P]
     lib.oracle_vquant.restype = None
+    lib.oracle_vquant_levels.argtypes = [P, I64, I64, I64, I64, ctypes.c_int, P, P]
+    lib.oracle_vquant_levels.restype = None
     lib.oracle_attention.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_int,
                                      P, I64, P, P, P]
     lib.oracle_attention.restype = ctypes.c_int
@@ -104,13 +107,14 @@ def logits(qbits, kbits, alpha_q=None, alpha_k=None, bias=None):
     return ham, lg
 
 
-def vquant(v: np.ndarray):
-    """v float32 [B,H,n,d] -> (vq int8 [B,H,n,d], scale float32 [B,H,d])."""
+def vquant(v: np.ndarray, levels: int = 127):
+    """v float32 [B,H,n,d] -> (vq int8 [B,H,n,d], scale float32 [B,H,d]); ``levels`` 127 (int8)
+    or 7 (4-bit V)."""
     v = _c(v, np.float32)
     B, H, n, d = v.shape
     vq = np.zeros((B, H, n, d), np.int8)
     sc = np.zeros((B, H, d), np.float32)
-    _load().oracle_vquant(_ptr(v), B, H, n, d, _ptr(vq), _ptr(sc))
+    _load().oracle_vquant_levels(_ptr(v), B, H, n, d, int(levels), _ptr(vq), _ptr(sc))
     return vq, sc
 
 
@@ -134,10 +138,11 @@ def attention(qbits, kbits, v, *, alpha_q=None, alpha_k=None, bias=None, top_n=N
     nrows = B * H * n if r is None else r.shape[0]
     out = np.zeros((nrows, d), np.float32)
     idx = np.zeros((nrows, keep), np.int32) if want_idx else None
-    a8 = np.zeros((nrows, keep), np.int32) if (want_aq8 and av_mode == AV_Q8) else None
+    quant = av_mode in (AV_Q8, AV_Q4)
+    a8 = np.zeros((nrows, keep), np.int32) if (want_aq8 and quant) else None
     vq = sc = None
-    if av_mode == AV_Q8:
-        vq, sc = vquant(v)
+    if quant:
+        vq, sc = vquant(v, 127 if av_mode == AV_Q8 else 7)
     aq, ak, T = _c(alpha_q, np.float32), _c(alpha_k, np.float32), _c(bias, np.float32)
     rc = _load().oracle_attention(_ptr(qbits), _ptr(kbits), _ptr(aq), _ptr(ak), _ptr(T), _ptr(v),
                                   _ptr(vq), _ptr(sc), B, H, n, d, N, av_mode, _ptr(r), nrows,
@@ -149,6 +154,6 @@ def attention(qbits, kbits, v, *, alpha_q=None, alpha_k=None, bias=None, top_n=N
         res["idx"] = idx if rows is not None else idx.reshape(B, H, n, keep)
     if a8 is not None:
         res["aq8"] = a8 if rows is not None else a8.reshape(B, H, n, keep)
-    if av_mode == AV_Q8:
+    if quant:
         res["vq"], res["vscale"] = vq, sc
     return res

@@ -49,6 +49,7 @@
 #define OR_MEAN_SIGN 1
 #define OR_AV_F32 0
 #define OR_AV_Q8 1
+#define OR_AV_Q4 2
 
 /* Number of threads the OpenMP loops below use. */
 int oracle_threads(void) {
@@ -161,11 +162,15 @@ void oracle_logits(const uint32_t* qb, const uint32_t* kb, const float* aq, cons
 }
 
 /* --------------------------------------------------------- V quantization
- * [BA] 2.4: per-channel int8 quantization of V.
- * scale[c] = max_j |V[j][c]| / 127 (float32 division); Vq = clamp(rint(V/scale), -127, 127),
- * 0 where the scale is 0.
+ * [BA] 2.4: per-channel integer quantization of V with `levels` levels each
+ * side of zero: 127 (int8, the pages' design) or 7 (the 4-bit V that the pages
+ * name as the next step).
+ * scale[c] = max_j |V[j][c]| / levels (float32 division);
+ * Vq = clamp(rint(V/scale), -levels, levels), 0 where the scale is 0.
  */
-void oracle_vquant(const float* v, int64_t B, int64_t H, int64_t n, int64_t d, int8_t* vq, float* scale) {
+void oracle_vquant_levels(const float* v, int64_t B, int64_t H, int64_t n, int64_t d, int levels, int8_t* vq,
+                          float* scale) {
+    const float lv = (float)levels;
     for (int64_t bh = 0; bh < B * H; ++bh) {
         const float* vs = v + bh * n * d;
         for (int64_t c = 0; c < d; ++c) {
@@ -174,20 +179,24 @@ void oracle_vquant(const float* v, int64_t B, int64_t H, int64_t n, int64_t d, i
                 float a = fabsf(vs[j * d + c]);
                 if (a > mx) mx = a;
             }
-            float sc = mx / 127.0f;
+            float sc = mx / lv;
             scale[bh * d + c] = sc;
             for (int64_t j = 0; j < n; ++j) {
                 int32_t q = 0;
                 if (sc > 0.0f) {
                     float r = rintf(vs[j * d + c] / sc);
-                    if (r > 127.0f) r = 127.0f;
-                    if (r < -127.0f) r = -127.0f;
+                    if (r > lv) r = lv;
+                    if (r < -lv) r = -lv;
                     q = (int32_t)r;
                 }
                 vq[(bh * n + j) * d + c] = (int8_t)q;
             }
         }
     }
+}
+
+void oracle_vquant(const float* v, int64_t B, int64_t H, int64_t n, int64_t d, int8_t* vq, float* scale) {
+    oracle_vquant_levels(v, B, H, n, d, 127, vq, scale);
 }
 
 typedef struct {
@@ -214,13 +223,14 @@ static int by_index(const void* pa, const void* pb) {
  *   logits over all keys -> keep the top-N ([HAD] summary: top N attention
  *   scores per query) -> softmax over the kept set ([BA] 2.3) -> A*V in
  *   float64 (av_mode F32, [HAD]: full-precision A*V) or as uint8 A times
- *   per-channel int8 V with integer accumulation (av_mode Q8, [BA] 2.4).
+ *   per-channel integer V with integer accumulation (av_mode Q8 or Q4,
+ *   [BA] 2.4; the two differ only in the quantization of V done beforehand).
  *
  * rows     flat query-row indices to compute (NULL: all B*H*n rows in order)
  * out      float32 [nrows, d]
  * idx      int32 [nrows, min(N,n)] kept key indices in ascending order, or NULL
- * aq8      int32 [nrows, min(N,n)] A_q of those keys (Q8 only), or NULL
- * vq/vscale  int8 [B,H,n,d] and float32 [B,H,d] from oracle_vquant (Q8 only)
+ * aq8      int32 [nrows, min(N,n)] A_q of those keys (Q8/Q4 only), or NULL
+ * vq/vscale  int8 [B,H,n,d] and float32 [B,H,d] from oracle_vquant_levels (Q8/Q4 only)
  * Returns 0, or -1 if an int32 accumulator would overflow (Q8).
  */
 int oracle_attention(const uint32_t* qb, const uint32_t* kb, const float* aq, const float* ak,

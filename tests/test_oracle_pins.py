@@ -351,6 +351,54 @@ def test_q8_integer_product_and_error_bound(N, d):
     assert np.all(np.abs(q8["out"] - fp["out"]) <= bound)
 
 
+def test_vquant_q4_closed_form_and_rounding():
+    # 4-bit V (7 levels each side): per-channel scale s with max |V| = 7 s gives scale s
+    # exactly and integer multiples back; half-way values round to even; |code| <= 7
+    g = np.random.default_rng(18)
+    d, n = 64, 50
+    s = 2.0 ** g.integers(-6, 3, d)
+    k = g.integers(-6, 7, (n, d)).astype(np.float64)
+    k[0] = 7.0
+    k[1] = -7.0
+    v = (k * s).astype(np.float32)[None, None]
+    vq, sc = oracle.vquant(v, 7)
+    assert np.array_equal(sc[0, 0], s.astype(np.float32))
+    assert np.array_equal(vq[0, 0], k.astype(np.int8))
+    col = np.array([2.5, -3.5, 0.5, 7.0], np.float32)
+    vh = np.repeat(col[:, None], 32, axis=1)[None, None]
+    vq2, sc2 = oracle.vquant(vh, 7)
+    assert sc2[0, 0, 0] == 1.0 and list(vq2[0, 0, :, 0]) == [2, -4, 0, 7]
+    x = g.standard_normal((1, 2, 40, 64)).astype(np.float32)
+    vq3, sc3 = oracle.vquant(x, 7)
+    assert np.abs(vq3).max() == 7
+    # the int8 quantizer of the same tensor is a different, finer grid
+    vq4, sc4 = oracle.vquant(x, 127)
+    assert np.allclose(sc4 * 127, sc3 * 7, rtol=1e-6)
+
+
+@pytest.mark.parametrize("N", [5, None])
+def test_q4_integer_product_and_error_bound(N):
+    xq, xk, v, T, qb, kb, aq, ak = _case(19, n=40)
+    fp = oracle.attention(qb, kb, v, alpha_q=aq, alpha_k=ak, bias=T, top_n=N, want_idx=True)
+    q4 = oracle.attention(qb, kb, v, alpha_q=aq, alpha_k=ak, bias=T, top_n=N, av_mode=oracle.AV_Q4,
+                          want_idx=True, want_aq8=True)
+    assert np.array_equal(fp["idx"], q4["idx"])
+    vq, sc = oracle.vquant(v, 7)
+    assert np.array_equal(q4["vq"], vq) and np.array_equal(q4["vscale"], sc)
+    B, H, n, d = v.shape
+    keep = q4["idx"].shape[-1]
+    vqt = torch.from_numpy(vq.astype(np.int64))
+    idx = torch.from_numpy(q4["idx"].astype(np.int64))
+    rows = torch.gather(vqt[:, :, None].expand(B, H, n, n, d), 3, idx[..., None].expand(B, H, n, keep, d))
+    acc = torch.einsum("bhik,bhikc->bhic", torch.from_numpy(q4["aq8"].astype(np.int64)), rows).numpy()
+    scb = sc[:, :, None, :]
+    want = ((acc.astype(np.float32) * scb).astype(np.float32) / np.float32(255)).astype(np.float32)
+    assert np.array_equal(q4["out"], want)
+    # A_q rounding moves each weight by at most 1/510, V by at most s_c / 2
+    bound = (keep / 510.0) * 7 * scb + scb / 2 + 1e-6
+    assert np.all(np.abs(q4["out"] - fp["out"]) <= bound)
+
+
 # ------------------------------------------------------------------ pages' constants
 def test_golden_constants_from_the_pages():
     with open(os.path.join(GOLDEN, "page_constants.json")) as f:
