@@ -74,7 +74,7 @@ def algorithmic_bytes(w) -> float:
     if w.bias:
         b += 4 * (2 * w.n - 1) / w.B
     vbytes = 2 if w.dtype == "bf16" else 4
-    b += w.n * w.d * (1 if w.av_mode == 1 else vbytes) + (4 * w.d if w.av_mode == 1 else 0)
+    b += w.n * w.d * (1 if w.av_mode != 0 else vbytes) + (4 * w.d if w.av_mode != 0 else 0)
     b += 4 * w.n * w.d
     return b * bh
 
@@ -408,12 +408,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "b1+f32" if w.av_mode == 0 else "b1+u8/i8",
+        "dtype": "b1+f32" if w.av_mode == 0 else ("b1+u8/i8" if w.av_mode == 1 else "b1+u8/i4"),
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: B={w.B} H={w.H} n={w.n} d={w.d} {kept} {w.dtype} "
                         f"{'plain sign' if w.mode == 0 else 'mean-centred scaled sign'}"
-                        f"{' + rel-pos bias' if w.bias else ''}, {'fp32' if w.av_mode == 0 else 'uint8 x int8'} A*V",
+                        f"{' + rel-pos bias' if w.bias else ''}, {['fp32', 'uint8 x int8', 'uint8 x int4'][w.av_mode]} A*V",
             "global_batch": w.B,
             "heads": w.H,
             "seq_len": w.n,

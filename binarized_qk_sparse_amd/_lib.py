@@ -23,6 +23,7 @@ HAD_SIGN = 0
 HAD_MEAN_SIGN = 1
 HAD_AV_F32 = 0
 HAD_AV_Q8 = 1
+HAD_AV_Q4 = 2
 HAD_ABI_VERSION = 1
 
 EXPORTS = (

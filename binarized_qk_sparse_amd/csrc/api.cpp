@@ -181,10 +181,12 @@ int had_attention_topn(const uint32_t* qbits, const uint32_t* kbits, const float
   int st = check_attention(qbits, kbits, v, v_dtype, B, H, n, d, out, fn);
   if (st != HAD_OK) return st;
   if (top_n < 1) return fail(HAD_ERR_INVALID_ARG, fn, "top_n must be >= 1");
-  if (av_mode != HAD_AV_F32 && av_mode != HAD_AV_Q8) return fail(HAD_ERR_INVALID_ARG, fn, "unknown av_mode");
+  if (av_mode != HAD_AV_F32 && av_mode != HAD_AV_Q8 && av_mode != HAD_AV_Q4)
+    return fail(HAD_ERR_INVALID_ARG, fn, "unknown av_mode");
   const int64_t keep = top_n < n ? top_n : n;
   if (keep > HAD_MAX_TOPN) return fail(HAD_ERR_UNSUPPORTED, fn, "min(top_n, n) above HAD_MAX_TOPN");
-  const int v_kind = av_mode == HAD_AV_Q8 ? 2 : (v_dtype == HAD_BF16 ? 1 : 0);
+  const bool quant = av_mode != HAD_AV_F32;
+  const int v_kind = quant ? 2 : (v_dtype == HAD_BF16 ? 1 : 0);
   const bool streaming = n > topn_max_n(v_kind, d);
   if (streaming && keep > topn_stream_max_keep())
     return fail(HAD_ERR_UNSUPPORTED, fn, "min(top_n, n) too large for the long-sequence kernel");
@@ -204,7 +206,7 @@ int had_attention_topn(const uint32_t* qbits, const uint32_t* kbits, const float
   p.keep = keep;
   p.out = out;
   p.idx = idx_out;
-  if (av_mode == HAD_AV_Q8) {
+  if (quant) {
     st = check_workspace(workspace, workspace_bytes, B, H, n, d, fn);
     if (st != HAD_OK) return st;
     const WorkspaceLayout w = workspace_layout(B, H, n, d);
@@ -218,6 +220,7 @@ int had_attention_topn(const uint32_t* qbits, const uint32_t* kbits, const float
     q.vmax_partial = reinterpret_cast<float*>(ws + w.vmax_partial);
     q.vscale = reinterpret_cast<float*>(ws + w.vscale);
     q.vq = reinterpret_cast<int8_t*>(ws + w.vq);
+    q.levels = av_mode == HAD_AV_Q4 ? 7 : 127;
     hipError_t e = launch_vquant(q, s);
     if (e != hipSuccess) return launch_status(e, fn);
     p.v = q.vq;
@@ -249,6 +252,7 @@ int binattn_dense_q8(const uint32_t* qbits, const uint32_t* kbits, const float* 
   q.vmax_partial = reinterpret_cast<float*>(ws + w.vmax_partial);
   q.vscale = reinterpret_cast<float*>(ws + w.vscale);
   q.vq = reinterpret_cast<int8_t*>(ws + w.vq);
+  q.levels = 127;
   hipError_t e = launch_vquant(q, s);
   if (e != hipSuccess) return launch_status(e, fn);
   AttnParams p{};

@@ -167,18 +167,20 @@ HAD_DEVICE uint32_t wave_select_desc(uint32_t x, int cnt, int rr) {
   }
 }
 
-// Per-channel int8 code of x at scale s (inv = v_rcp_f32(s)):
-// clamp(rint(fl(x / s)), -127, 127) as a byte, 0 when s is 0.  x * (1/s) is
-// within 2 ulp of the correctly rounded quotient fl(x / s), i.e. within 2^-16
-// for |x / s| <= 128, so the two can round to different integers only when the
-// quotient lies near a tie k + 1/2; there the exact division decides (as it
-// does for a denormal scale, whose reciprocal is not representable).
+// Per-channel integer code of x at scale s (inv = v_rcp_f32(s)) with L levels
+// each side of zero (127: int8; 7: 4-bit V): clamp(rint(fl(x / s)), -L, L) as a
+// byte, 0 when s is 0.  x * (1/s) is within 2 ulp of the correctly rounded
+// quotient fl(x / s), i.e. within 2^-16 for |x / s| <= 128, so the two can round
+// to different integers only when the quotient lies near a tie k + 1/2; there
+// the exact division decides (as it does for a denormal scale, whose reciprocal
+// is not representable).
+template <int L = 127>
 HAD_DEVICE uint32_t quant_i8(float x, float s, float inv) {
   if (!(s > 0.0f)) return 0u;
   float y = x * inv;
   if (s < 0x1p-125f || fabsf(y - floorf(y) - 0.5f) < 0x1p-12f) y = __fdiv_rn(x, s);
   float r = rintf(y);
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  r = fminf(fmaxf(r, -(float)L), (float)L);
   return (uint32_t)((int32_t)r) & 0xffu;
 }
 

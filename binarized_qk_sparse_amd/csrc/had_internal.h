@@ -33,6 +33,7 @@ struct VQuantParams {
   float* vmax_partial;  // [BH, chunks, d]
   float* vscale;        // [BH, d]
   int8_t* vq;           // [BH, n, d]
+  int levels;           // 127 (int8) or 7 (4-bit values)
 };
 constexpr int kVqChunk = 256;
 inline int64_t vq_chunks(int64_t n) { return (n + kVqChunk - 1) / kVqChunk; }

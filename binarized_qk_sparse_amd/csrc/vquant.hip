@@ -1,7 +1,9 @@
-// Per-channel int8 quantization of V (BinaryAttention, section 2.4: V is
-// quantized per channel to int8 because its channels can hold outliers).
-//   scale[c] = max_j |V[j][c]| / 127          (float32, correctly rounded)
-//   Vq[j][c] = clamp(rint(V[j][c] / scale[c]), -127, 127), 0 if scale is 0
+// Per-channel integer quantization of V (BinaryAttention, section 2.4: V is
+// quantized per channel to int8 because its channels can hold outliers; the
+// conclusion names 4-bit V as the next step), with L levels each side of zero,
+// L = 127 (int8) or 7 (4-bit values, stored one per byte):
+//   scale[c] = max_j |V[j][c]| / L          (float32, correctly rounded)
+//   Vq[j][c] = clamp(rint(V[j][c] / scale[c]), -L, L), 0 if scale is 0
 // A streaming pass bound by HBM bandwidth: a max pass over V, then a quantize
 // pass that reads V again and writes one byte per element.
 #include "had_device.hpp"
@@ -65,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void vmax_partial_kernel(const T* __restr
 // scale[bh][c] = max over chunks / 127.  One workgroup per (b, h): kThreads / D
 // groups of threads take interleaved chunks, LDS takes the max of the groups.
 __global__ __launch_bounds__(kThreads) void vscale_kernel(const float* __restrict__ partial, int64_t chunks, int D,
-                                                          float* __restrict__ scale) {
+                                                          float levels, float* __restrict__ scale) {
   __shared__ float red[kThreads];
   const int64_t bh = blockIdx.x;
   const int groups = kThreads / D;
@@ -76,11 +78,11 @@ __global__ __launch_bounds__(kThreads) void vscale_kernel(const float* __restric
   __syncthreads();
   if (grp == 0) {
     for (int q = 1; q < groups; ++q) m = fmaxf(m, red[q * D + c]);
-    scale[bh * D + c] = __fdiv_rn(m, 127.0f);
+    scale[bh * D + c] = __fdiv_rn(m, levels);
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int L>
 __global__ __launch_bounds__(kThreads) void vq_kernel(const T* __restrict__ v, uint32_t rows, uint32_t n,
                                                       const float* __restrict__ scale, int8_t* __restrict__ vq) {
   constexpr int TPR = D / 8;
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void vq_kernel(const T* __restrict__ v, u
   const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
   uint32_t b[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) b[c] = quant_i8(x[c], s[c], __builtin_amdgcn_rcpf(s[c]));
+  for (int c = 0; c < 8; ++c) b[c] = quant_i8<L>(x[c], s[c], __builtin_amdgcn_rcpf(s[c]));
   uint2 o;
   o.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
   o.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
@@ -106,9 +108,9 @@ __global__ __launch_bounds__(kThreads) void vq_kernel(const T* __restrict__ v, u
 // The quantize pass with the scales finished in the same launch: when a
 // workgroup's rows span at most two (b, h) slices (n >= rows per workgroup), its
 // first 2D threads take the max over the chunk partials of those slices and
-// divide by 127 (as vscale_kernel does) into LDS; the workgroup holding a slice's
+// divide by L (as vscale_kernel does) into LDS; the workgroup holding a slice's
 // first row writes its scales.
-template <typename T, int D>
+template <typename T, int D, int L>
 __global__ __launch_bounds__(kThreads) void vq_fused_kernel(const T* __restrict__ v, uint32_t rows, uint32_t n,
                                                             uint32_t chunks, const float* __restrict__ partial,
                                                             float* __restrict__ scale, int8_t* __restrict__ vq) {
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void vq_fused_kernel(const T* __restrict_
     if (hh < nh) {
       float m = 0.0f;
       for (uint32_t k = 0; k < chunks; ++k) m = fmaxf(m, partial[((size_t)hh * chunks + k) * D + c]);
-      q = __fdiv_rn(m, 127.0f);
+      q = __fdiv_rn(m, (float)L);
       if ((size_t)hh * n >= r0 && (size_t)hh * n < (size_t)r0 + RPP) scale[(size_t)hh * D + c] = q;
     }
     sc[threadIdx.x / D][c] = q;
@@ -139,15 +141,15 @@ __global__ __launch_bounds__(kThreads) void vq_fused_kernel(const T* __restrict_
   const float* sp = &sc[min(r / n - h0, 1u)][8 * cg];
   uint32_t b[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) b[c] = quant_i8(x[c], sp[c], __builtin_amdgcn_rcpf(sp[c]));
+  for (int c = 0; c < 8; ++c) b[c] = quant_i8<L>(x[c], sp[c], __builtin_amdgcn_rcpf(sp[c]));
   uint2 o;
   o.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
   o.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
   *reinterpret_cast<uint2*>(vq + (size_t)r * D + 8 * cg) = o;
 }
 
-template <typename T, int D>
-hipError_t launch_typed(const VQuantParams& p, hipStream_t s) {
+template <typename T, int D, int L>
+hipError_t launch_levels(const VQuantParams& p, hipStream_t s) {
   const T* v = static_cast<const T*>(p.v);
   const int64_t chunks = vq_chunks(p.n);
   hipLaunchKernelGGL((vmax_partial_kernel<T, D>), dim3((unsigned)(p.BH * chunks)), dim3(kThreads), 0, s, v,
@@ -157,17 +159,22 @@ hipError_t launch_typed(const VQuantParams& p, hipStream_t s) {
   if (p.n >= kThreads / (D / 8) && chunks <= 4) {
     const int64_t rows = p.BH * p.n;
     constexpr int RPP = kThreads / (D / 8);
-    hipLaunchKernelGGL((vq_fused_kernel<T, D>), dim3((unsigned)((rows + RPP - 1) / RPP)), dim3(kThreads), 0, s, v,
-                       (uint32_t)rows, (uint32_t)p.n, (uint32_t)chunks, p.vmax_partial, p.vscale, p.vq);
+    hipLaunchKernelGGL((vq_fused_kernel<T, D, L>), dim3((unsigned)((rows + RPP - 1) / RPP)), dim3(kThreads), 0, s,
+                       v, (uint32_t)rows, (uint32_t)p.n, (uint32_t)chunks, p.vmax_partial, p.vscale, p.vq);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(vscale_kernel, dim3((unsigned)p.BH), dim3(kThreads), 0, s, p.vmax_partial, chunks, D,
+  hipLaunchKernelGGL(vscale_kernel, dim3((unsigned)p.BH), dim3(kThreads), 0, s, p.vmax_partial, chunks, D, (float)L,
                      p.vscale);
   const int64_t rows = p.BH * p.n;
   constexpr int RPP = kThreads / (D / 8);
-  hipLaunchKernelGGL((vq_kernel<T, D>), dim3((unsigned)((rows + RPP - 1) / RPP)), dim3(kThreads), 0, s, v,
+  hipLaunchKernelGGL((vq_kernel<T, D, L>), dim3((unsigned)((rows + RPP - 1) / RPP)), dim3(kThreads), 0, s, v,
                      (uint32_t)rows, (uint32_t)p.n, p.vscale, p.vq);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const VQuantParams& p, hipStream_t s) {
+  return p.levels == 7 ? launch_levels<T, D, 7>(p, s) : launch_levels<T, D, 127>(p, s);
 }
 
 template <typename T>

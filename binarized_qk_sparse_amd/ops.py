@@ -11,7 +11,7 @@ from typing import Optional, Tuple
 import torch
 
 from . import _lib
-from ._lib import (HAD_AV_F32, HAD_AV_Q8, HAD_BF16, HAD_F32, HAD_MEAN_SIGN,  # noqa: F401
+from ._lib import (HAD_AV_F32, HAD_AV_Q4, HAD_AV_Q8, HAD_BF16, HAD_F32, HAD_MEAN_SIGN,  # noqa: F401
                    HAD_SIGN, HadError)
 
 

@@ -25,6 +25,7 @@ on, which are not available here):
 * ``c5`` high-resolution ViT: 1024x1024 image at patch 8 -> n=16384; batch 1,
   16 heads, d=64, bf16 Q/K/V iid N(0,1); mean-centred scaled sign;
   relative-position table; top-256; uint8 A x int8 V over the kept set.
+  ``c5q4`` is the same with 4-bit V (7 levels each side of zero).
 
 Second arguments of N(., .) are standard deviations.  Generation: NumPy
 ``default_rng([config_index, n, tensor_id])`` in float32, tensor ids Q=1, K=2,
@@ -44,6 +45,7 @@ SIGN = 0
 MEAN_SIGN = 1
 AV_F32 = 0
 AV_Q8 = 1
+AV_Q4 = 2
 
 
 @dataclasses.dataclass(frozen=True)
@@ -58,7 +60,7 @@ class Workload:
     dtype: str  # "f32" or "bf16"
     mode: int  # SIGN or MEAN_SIGN
     bias: bool
-    av_mode: int  # AV_F32 or AV_Q8
+    av_mode: int  # AV_F32, AV_Q8 or AV_Q4
     qk_law: str  # "iid", "chan_std", "chan_mean"
 
     @property
@@ -80,6 +82,8 @@ WORKLOADS: Dict[str, Workload] = {
     "c3": Workload("c3", 2, 4, 12, 1024, 64, 120, "bf16", SIGN, False, AV_F32, "chan_std"),
     "c4": Workload("c4", 3, 64, 12, 197, 64, None, "bf16", MEAN_SIGN, True, AV_Q8, "chan_mean"),
     "c5": Workload("c5", 4, 1, 16, 16384, 64, 256, "bf16", MEAN_SIGN, True, AV_Q8, "iid"),
+    # c5 with 4-bit V (the next step BinaryAttention's conclusion names); same draws as c5
+    "c5q4": Workload("c5q4", 4, 1, 16, 16384, 64, 256, "bf16", MEAN_SIGN, True, AV_Q4, "iid"),
     # the long-context sweep at head_dim 128 (the kernel shape of BinaryAttention's
     # speed-versus-length figure); "c3d128@n" scales N = 15 n / 128 like c3
     "c3d128": Workload("c3d128", 5, 4, 12, 1024, 128, 120, "bf16", SIGN, False, AV_F32, "chan_std"),

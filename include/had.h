@@ -66,6 +66,7 @@ extern "C" {
 /* A*V modes */
 #define HAD_AV_F32 0 /* fp32 probabilities times V, fp32 accumulation */
 #define HAD_AV_Q8 1  /* uint8 A (scale 1/255) times per-channel int8 V, int32 accumulation */
+#define HAD_AV_Q4 2  /* as HAD_AV_Q8 with 4-bit V: 7 levels each side of zero (scale max|V|/7) */
 
 /* Largest sizes the kernels accept. */
 #define HAD_MAX_N 65536
@@ -135,13 +136,14 @@ int had_pack_qk(const void* q, const void* k, int x_dtype, int64_t B, int64_t H,
  *  bias_table     float32 [H,2n-1] or NULL (B = 0)
  *  v              [B,H,n,d] of v_dtype (HAD_F32 or HAD_BF16)
  *  top_n          N >= 1; N >= n keeps every key (dense softmax)
- *  av_mode        HAD_AV_F32 or HAD_AV_Q8
+ *  av_mode        HAD_AV_F32, HAD_AV_Q8 or HAD_AV_Q4
  *  out            out float32 [B,H,n,d]
  *  idx_out        optional out int32 [B,H,n,min(N,n)]: kept key indices of
  *                 each query in ascending order; NULL to skip
- *  workspace      >= had_workspace_bytes(B,H,n,d) bytes (HAD_AV_Q8 only; may
- *                 be NULL for HAD_AV_F32).  On return (after the stream has
- *                 run) it holds the int8 V and its per-channel scales.
+ *  workspace      >= had_workspace_bytes(B,H,n,d) bytes (HAD_AV_Q8 and
+ *                 HAD_AV_Q4; may be NULL for HAD_AV_F32).  On return (after
+ *                 the stream has run) it holds the integer V (one byte per
+ *                 element) and its per-channel scales.
  *
  *  Logit, in float32 with each operation rounded as written:
  *      t = alpha_q*alpha_k;  u = t*(d-2h);  v = u*float(1/sqrt(d));  l = v + B
@@ -149,6 +151,9 @@ int had_pack_qk(const void* q, const void* k, int x_dtype, int64_t B, int64_t H,
  *  Softmax in float32 over the kept set.  HAD_AV_Q8: scale_c = max_j|V[j][c]|/127
  *  over all n tokens, Vq = clamp(rint(V/scale_c), -127, 127),
  *  A_q = clamp(rint(255 p), 0, 255), O = float(sum A_q*Vq) * scale_c / 255.
+ *  HAD_AV_Q4 (the 4-bit V that BinaryAttention's conclusion names as the next
+ *  step): the same with 7 in place of 127.  gfx950 has no 4-bit integer matrix
+ *  instruction, so the 4-bit codes are kept one per byte and use the int8 path.
  */
 int had_attention_topn(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q,
                        const float* alpha_k, const float* bias_table, const void* v, int v_dtype,

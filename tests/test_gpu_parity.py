@@ -199,16 +199,18 @@ def _check_q8(out, ws_vq, ws_sc, ref, rows, n, what):
 
 
 @pytest.mark.parametrize("n,N", [(5, 3), (197, 30), (256, 256), (700, 64), (1024, 120)])
-def test_topn_q8_matches_oracle(n, N):
+@pytest.mark.parametrize("av", [synth.AV_Q8, synth.AV_Q4])
+def test_topn_q8_matches_oracle(n, N, av):
     qb, kb, aq, ak, T, v = _topn_case(2, 2, n, N, torch.bfloat16, synth.MEAN_SIGN, True, seed=2)
     dt = lambda a: torch.from_numpy(a).to(DEV)
     ws = ops.workspace(2, 2, n, 64)
     out, idx = ops.had_attention_topn(dt(qb.view(np.int32)), dt(kb.view(np.int32)), v.to(DEV), N, alpha_q=dt(aq),
-                                      alpha_k=dt(ak), bias=dt(T), av_mode=ops.HAD_AV_Q8, want_idx=True, ws=ws)
+                                      alpha_k=dt(ak), bias=dt(T), av_mode=av, want_idx=True, ws=ws)
     torch.cuda.synchronize()
     vq, sc = ops.workspace_view(ws, 2, 2, n, 64)
-    ref = oracle.attention(qb, kb, f32(v), alpha_q=aq, alpha_k=ak, bias=T, top_n=N, av_mode=oracle.AV_Q8,
-                           want_idx=True)
+    ref = oracle.attention(qb, kb, f32(v), alpha_q=aq, alpha_k=ak, bias=T, top_n=N, av_mode=av, want_idx=True)
+    if av == synth.AV_Q4:
+        assert np.abs(vq.cpu().numpy()).max() == 7
     assert np.array_equal(idx.cpu().numpy(), ref["idx"])
     rows = np.arange(2 * 2 * n)
     _check_q8(out.cpu().numpy().reshape(-1, 64), vq.cpu().numpy(), sc.cpu().numpy(),
@@ -263,7 +265,7 @@ def test_graph_replays_match_eager():
 # ------------------------------------------------------------------ long sequences (streaming kernel)
 @pytest.mark.parametrize("n,N", [(1025, 1), (1500, 30), (2048, 256), (3000, 700), (4100, 120)])
 @pytest.mark.parametrize("keys", ["int", "alpha_bias"])
-@pytest.mark.parametrize("av", [synth.AV_F32, synth.AV_Q8])
+@pytest.mark.parametrize("av", [synth.AV_F32, synth.AV_Q8, synth.AV_Q4])
 def test_topn_long_sequence_matches_oracle(n, N, keys, av):
     mode = synth.MEAN_SIGN if keys == "alpha_bias" else synth.SIGN
     qb, kb, aq, ak, T, v = _topn_case(1, 2, n, N, torch.bfloat16, mode, keys != "int", seed=4)
@@ -303,8 +305,9 @@ def test_topn_long_sequence_all_ties(N):
     assert_close(out.reshape(-1, 64)[rows], ref["out"], f"all ties N={N}")
 
 
-def test_topn_c5_full_size_sampled():
-    w = synth.workload("c5")
+@pytest.mark.parametrize("name", ["c5", "c5q4"])
+def test_topn_c5_full_size_sampled(name):
+    w = synth.workload(name)
     g = synth.generate(w)
     ws = ops.workspace(w.B, w.H, w.n, w.d)
     q, k, v = g["q"].to(DEV), g["k"].to(DEV), g["v"].to(DEV)
@@ -324,7 +327,7 @@ def test_topn_c5_full_size_sampled():
                            av_mode=w.av_mode, rows=rows, want_idx=True)
     assert np.array_equal(idx.cpu().numpy().reshape(-1, w.top_n)[rows], ref["idx"])
     vq, sc = ops.workspace_view(ws, w.B, w.H, w.n, w.d)
-    _check_q8(out.cpu().numpy().reshape(-1, 64)[rows], vq.cpu().numpy(), sc.cpu().numpy(), ref, rows, w.n, "c5")
+    _check_q8(out.cpu().numpy().reshape(-1, 64)[rows], vq.cpu().numpy(), sc.cpu().numpy(), ref, rows, w.n, name)
 
 
 def test_topn_zero_distance_ties():
