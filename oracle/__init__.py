@@ -48,14 +48,14 @@ def _load():
     I64 = ctypes.c_int64
     lib.oracle_pack.argtypes = [P, I64, I64, I64, I64, ctypes.c_int, P, P, P]
     lib.oracle_pack.restype = None
-    lib.oracle_logits.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, P]
+    lib.oracle_logits.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, I64, P, P]
     lib.oracle_logits.restype = None
     lib.oracle_vquant.argtypes = [P, I64, I64, I64, I64, P, P]
     lib.oracle_vquant.restype = None
     lib.oracle_vquant_levels.argtypes = [P, I64, I64, I64, I64, ctypes.c_int, P, P]
     lib.oracle_vquant_levels.restype = None
-    lib.oracle_attention.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_int,
-                                     P, I64, P, P, P]
+    lib.oracle_attention.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, P, P, P, I64, I64, I64, I64, I64,
+                                     ctypes.c_int, P, I64, P, P, P]
     lib.oracle_attention.restype = ctypes.c_int
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
@@ -93,7 +93,22 @@ def pack(x: np.ndarray, mode: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     return bits, alpha, mu
 
 
-def logits(qbits, kbits, alpha_q=None, alpha_k=None, bias=None):
+def _bias2d_args(bias2d, n):
+    """(R, C, X, gh, gw, cls) of a two-dimensional decomposable bias, or the absent form.
+
+    ``bias2d`` is None or a dict: ``grid`` (gh, gw), ``row`` float32 [H, 2gh-1], ``col``
+    float32 [H, 2gw-1] and, with a leading class token, ``cls`` float32 [H, 3]
+    (class->patch, patch->class, class->class); n must be gh*gw (+1 with a class token)."""
+    if bias2d is None:
+        return None, None, None, 0, 0, 0
+    gh, gw = (int(x) for x in bias2d["grid"])
+    X = _c(bias2d.get("cls"), np.float32)
+    cls = 0 if X is None else 1
+    assert n == cls + gh * gw, "n must be the grid size plus the class token"
+    return _c(bias2d["row"], np.float32), _c(bias2d["col"], np.float32), X, gh, gw, cls
+
+
+def logits(qbits, kbits, alpha_q=None, alpha_k=None, bias=None, bias2d=None):
     """Full (hamming int32, logits float32) matrices [B,H,n,n]."""
     qbits = _c(qbits, np.uint32)
     kbits = _c(kbits, np.uint32)
@@ -102,8 +117,9 @@ def logits(qbits, kbits, alpha_q=None, alpha_k=None, bias=None):
     ham = np.zeros((B, H, n, n), np.int32)
     lg = np.zeros((B, H, n, n), np.float32)
     aq, ak, T = _c(alpha_q, np.float32), _c(alpha_k, np.float32), _c(bias, np.float32)
-    _load().oracle_logits(_ptr(qbits), _ptr(kbits), _ptr(aq), _ptr(ak), _ptr(T), B, H, n, d,
-                          _ptr(ham), _ptr(lg))
+    R, C, X, gh, gw, cls = _bias2d_args(bias2d, n)
+    _load().oracle_logits(_ptr(qbits), _ptr(kbits), _ptr(aq), _ptr(ak), _ptr(T), _ptr(R), _ptr(C), _ptr(X), gh, gw,
+                          cls, B, H, n, d, _ptr(ham), _ptr(lg))
     return ham, lg
 
 
@@ -118,9 +134,12 @@ def vquant(v: np.ndarray, levels: int = 127):
     return vq, sc
 
 
-def attention(qbits, kbits, v, *, alpha_q=None, alpha_k=None, bias=None, top_n=None,
+def attention(qbits, kbits, v, *, alpha_q=None, alpha_k=None, bias=None, bias2d=None, top_n=None,
               av_mode=AV_F32, rows=None, want_idx=False, want_aq8=False):
     """Attention for the given flat query rows (all rows if ``rows`` is None).
+
+    ``bias`` is the 1-D offset table [H, 2n-1]; ``bias2d`` the two-dimensional
+    decomposable form (see ``_bias2d_args``); at most one of them is given.
 
     ``top_n=None`` keeps every key.  Returns a dict with ``out`` float32
     [nrows, d] (or [B,H,n,d] when rows is None), and optionally ``idx`` and
@@ -144,7 +163,10 @@ def attention(qbits, kbits, v, *, alpha_q=None, alpha_k=None, bias=None, top_n=N
     if quant:
         vq, sc = vquant(v, 127 if av_mode == AV_Q8 else 7)
     aq, ak, T = _c(alpha_q, np.float32), _c(alpha_k, np.float32), _c(bias, np.float32)
-    rc = _load().oracle_attention(_ptr(qbits), _ptr(kbits), _ptr(aq), _ptr(ak), _ptr(T), _ptr(v),
+    assert bias is None or bias2d is None
+    R, C, X, gh, gw, cls = _bias2d_args(bias2d, n)
+    rc = _load().oracle_attention(_ptr(qbits), _ptr(kbits), _ptr(aq), _ptr(ak), _ptr(T), _ptr(R), _ptr(C), _ptr(X),
+                                  gh, gw, cls, _ptr(v),
                                   _ptr(vq), _ptr(sc), B, H, n, d, N, av_mode, _ptr(r), nrows,
                                   _ptr(out), _ptr(idx), _ptr(a8))
     if rc != 0:

@@ -129,32 +129,62 @@ static int32_t hamming(const uint32_t* a, const uint32_t* b, int64_t W) {
 /* float(1/sqrt(d)): the 1/sqrt(d) factor of [BA] 2.3, rounded once. */
 static float inv_sqrt_d(int64_t d) { return (float)(1.0 / sqrt((double)d)); }
 
-/* The logit of query i, key j ([BA] 2.3 with the scaled codes of [BA] 2.2). */
+/* Decomposable two-dimensional relative-position bias ([BA] 4.4: a sum of
+ * biases that keeps the bias memory negligible; [BA] 2.3 for the bias itself).
+ * Tokens are an optional leading class token (cls = 1) followed by a gh x gw
+ * grid of patches in row-major order.  For two patches the bias is a row term
+ * plus a column term, each a per-head table over the signed offsets:
+ *     R[h][r_j - r_i + gh - 1] + C[h][c_j - c_i + gw - 1]    (float32 sum)
+ * and a pair involving the class token takes one of three per-head values
+ * X[h][0] (class -> patch), X[h][1] (patch -> class), X[h][2] (class -> class). */
+typedef struct {
+    const float* R;   /* [H, 2 gh - 1] */
+    const float* C;   /* [H, 2 gw - 1] */
+    const float* X;   /* [H, 3] (cls = 1 only) */
+    int64_t gh, gw, cls;
+} bias2d_t;
+
+static float bias2d_value(const bias2d_t* b, int64_t h, int64_t i, int64_t j) {
+    const int64_t ci = i < b->cls, cj = j < b->cls;
+    if (ci && cj) return b->X[h * 3 + 2];
+    if (ci) return b->X[h * 3 + 0];
+    if (cj) return b->X[h * 3 + 1];
+    const int64_t pi = i - b->cls, pj = j - b->cls;
+    const int64_t ri = pi / b->gw, cli = pi % b->gw, rj = pj / b->gw, clj = pj % b->gw;
+    return b->R[h * (2 * b->gh - 1) + (rj - ri + b->gh - 1)] + b->C[h * (2 * b->gw - 1) + (clj - cli + b->gw - 1)];
+}
+
+/* The logit of query i, key j ([BA] 2.3 with the scaled codes of [BA] 2.2):
+ * bias from the 1-D offset table T, the 2-D decomposable form b2, or none. */
 static float logit(const uint32_t* qb, const uint32_t* kb, const float* aq, const float* ak,
-                   const float* T, int64_t n, int64_t d, int64_t bh, int64_t h_idx, int64_t i, int64_t j,
-                   int32_t* ham_out) {
+                   const float* T, const bias2d_t* b2, int64_t n, int64_t d, int64_t bh, int64_t h_idx, int64_t i,
+                   int64_t j, int32_t* ham_out) {
     const int64_t W = d / 32;
     int32_t h = hamming(qb + (bh * n + i) * W, kb + (bh * n + j) * W, W);
     int32_t dot = (int32_t)d - 2 * h;
     float t = (aq ? aq[bh * n + i] : 1.0f) * (ak ? ak[bh * n + j] : 1.0f);
     float u = t * (float)dot;
     float v = u * inv_sqrt_d(d);
-    float l = T ? v + T[h_idx * (2 * n - 1) + (j - i + n - 1)] : v;
+    float l = v;
+    if (b2) l = v + bias2d_value(b2, h_idx, i, j);
+    else if (T) l = v + T[h_idx * (2 * n - 1) + (j - i + n - 1)];
     if (ham_out) *ham_out = h;
     return l;
 }
 
 /* Full Hamming-distance and logit matrices, [B,H,n,n] each (small cases). */
 void oracle_logits(const uint32_t* qb, const uint32_t* kb, const float* aq, const float* ak,
-                   const float* T, int64_t B, int64_t H, int64_t n, int64_t d,
-                   int32_t* ham, float* logits) {
+                   const float* T, const float* R2, const float* C2, const float* X2, int64_t gh, int64_t gw,
+                   int64_t cls, int64_t B, int64_t H, int64_t n, int64_t d, int32_t* ham, float* logits) {
+    const bias2d_t b2v = {R2, C2, X2, gh, gw, cls};
+    const bias2d_t* b2 = R2 ? &b2v : NULL;
     for (int64_t b = 0; b < B; ++b)
         for (int64_t h = 0; h < H; ++h) {
             int64_t bh = b * H + h;
             for (int64_t i = 0; i < n; ++i)
                 for (int64_t j = 0; j < n; ++j) {
                     int32_t hd;
-                    float l = logit(qb, kb, aq, ak, T, n, d, bh, h, i, j, &hd);
+                    float l = logit(qb, kb, aq, ak, T, b2, n, d, bh, h, i, j, &hd);
                     if (ham) ham[(bh * n + i) * n + j] = hd;
                     if (logits) logits[(bh * n + i) * n + j] = l;
                 }
@@ -234,9 +264,12 @@ static int by_index(const void* pa, const void* pb) {
  * Returns 0, or -1 if an int32 accumulator would overflow (Q8).
  */
 int oracle_attention(const uint32_t* qb, const uint32_t* kb, const float* aq, const float* ak,
-                     const float* T, const float* v, const int8_t* vq, const float* vscale,
+                     const float* T, const float* R2, const float* C2, const float* X2, int64_t gh, int64_t gw,
+                     int64_t cls, const float* v, const int8_t* vq, const float* vscale,
                      int64_t B, int64_t H, int64_t n, int64_t d, int64_t top_n, int av_mode,
                      const int64_t* rows, int64_t nrows, float* out, int32_t* idx, int32_t* aq8) {
+    const bias2d_t b2v = {R2, C2, X2, gh, gw, cls};
+    const bias2d_t* b2 = R2 ? &b2v : NULL;
     const int64_t keep = top_n < n ? top_n : n;
     int failed = 0;
     if (rows == NULL) nrows = B * H * n;
@@ -248,7 +281,7 @@ int oracle_attention(const uint32_t* qb, const uint32_t* kb, const float* aq, co
         int32_t* kept = (int32_t*)malloc((size_t)keep * sizeof(int32_t));
         double* p = (double*)malloc((size_t)n * sizeof(double));
         for (int64_t j = 0; j < n; ++j) {
-            s[j].l = logit(qb, kb, aq, ak, T, n, d, bh, h, i, j, NULL);
+            s[j].l = logit(qb, kb, aq, ak, T, b2, n, d, bh, h, i, j, NULL);
             s[j].j = (int32_t)j;
         }
         qsort(s, (size_t)n, sizeof(scored_t), by_logit_then_index);

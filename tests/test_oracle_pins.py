@@ -290,6 +290,98 @@ def test_single_token():
     assert np.allclose(r["out"][0, 0], v[0, 0], atol=np.abs(v).max() / 127)
 
 
+# ------------------------------------------------------------------ two-dimensional decomposable bias
+def _bias2d_case(seed, H, gh, gw, cls):
+    g = np.random.default_rng(seed)
+    b2 = {"grid": (gh, gw), "row": (0.3 * g.standard_normal((H, 2 * gh - 1))).astype(np.float32),
+          "col": (0.3 * g.standard_normal((H, 2 * gw - 1))).astype(np.float32)}
+    if cls:
+        b2["cls"] = (0.3 * g.standard_normal((H, 3))).astype(np.float32)
+    return b2
+
+
+def _bias2d_dense(b2, H):
+    """The bias matrix [H, n, n] written out token pair by token pair."""
+    gh, gw = b2["grid"]
+    cls = 1 if "cls" in b2 else 0
+    n = cls + gh * gw
+    out = np.zeros((H, n, n), np.float32)
+    for h in range(H):
+        for i in range(n):
+            for j in range(n):
+                if i < cls and j < cls:
+                    out[h, i, j] = b2["cls"][h, 2]
+                elif i < cls:
+                    out[h, i, j] = b2["cls"][h, 0]
+                elif j < cls:
+                    out[h, i, j] = b2["cls"][h, 1]
+                else:
+                    ri, ci = divmod(i - cls, gw)
+                    rj, cj = divmod(j - cls, gw)
+                    out[h, i, j] = np.float32(b2["row"][h, rj - ri + gh - 1]) + np.float32(b2["col"][h, cj - ci + gw - 1])
+    return out
+
+
+@pytest.mark.parametrize("gh,gw,cls", [(3, 5, 1), (4, 4, 0), (2, 7, 1)])
+def test_bias2d_logits_add_the_written_out_bias(gh, gw, cls):
+    H = 2
+    n = cls + gh * gw
+    g = np.random.default_rng(40 + gh)
+    x = g.standard_normal((1, H, n, 64)).astype(np.float32)
+    y = g.standard_normal((1, H, n, 64)).astype(np.float32)
+    qb, aq, _ = oracle.pack(x, oracle.MEAN_SIGN)
+    kb, ak, _ = oracle.pack(y, oracle.MEAN_SIGN)
+    b2 = _bias2d_case(gh * 10 + gw, H, gh, gw, cls)
+    _, plain = oracle.logits(qb, kb, aq, ak)
+    _, lg = oracle.logits(qb, kb, aq, ak, bias2d=b2)
+    dense = _bias2d_dense(b2, H)
+    assert np.array_equal(lg, (plain + dense[None]).astype(np.float32))
+    # a transposed offset (r_i - r_j) or the row and column tables swapped give other values
+    wrong = dict(b2, row=b2["row"][:, ::-1].copy())
+    assert not np.array_equal(_bias2d_dense(wrong, H), dense)
+
+
+def test_bias2d_single_row_is_the_1d_offset_table():
+    # one grid row and no class token: B[i][j] = R[0] + C[j - i + n - 1], the 1-D table R[0] + C
+    H, gw = 2, 9
+    b2 = _bias2d_case(3, H, 1, gw, 0)
+    g = np.random.default_rng(41)
+    qb, _, _ = oracle.pack(g.standard_normal((1, H, gw, 64)).astype(np.float32), oracle.SIGN)
+    kb, _, _ = oracle.pack(g.standard_normal((1, H, gw, 64)).astype(np.float32), oracle.SIGN)
+    T = (b2["row"][:, :1] + b2["col"]).astype(np.float32)
+    assert np.array_equal(oracle.logits(qb, kb, bias2d=b2)[1], oracle.logits(qb, kb, bias=T)[1])
+
+
+def test_topn_bias2d_equals_masked_textbook_attention():
+    H, gh, gw, cls = 2, 4, 6, 1
+    n = cls + gh * gw
+    xq, xk, v, _, qb, kb, aq, ak = _case(42, H=H, n=n, bias=False)
+    _, _, mq = oracle.pack(xq, oracle.MEAN_SIGN)
+    _, _, mk = oracle.pack(xk, oracle.MEAN_SIGN)
+    yq, yk = xq - mq[:, :, None, :], xk - mk[:, :, None, :]
+    b2 = _bias2d_case(5, H, gh, gw, cls)
+    dense = _bias2d_dense(b2, H)
+    N = 7
+    res = oracle.attention(qb, kb, v, alpha_q=aq, alpha_k=ak, bias2d=b2, top_n=N, want_idx=True)
+    B = xq.shape[0]
+    dot = np.einsum("bhic,bhjc->bhij", _signs(yq), _signs(yk))
+    l = (aq[..., :, None] * ak[..., None, :]).astype(np.float64) * dot / 8.0 + dense[None]
+    keep = np.zeros((B, H, n, n), bool)
+    for b in range(B):
+        for h in range(H):
+            for q in range(n):
+                sel = _brute_topn(l[b, h, q], N)
+                assert list(res["idx"][b, h, q]) == sel
+                keep[b, h, q, sel] = True
+    q = torch.from_numpy(_signs(yq) * aq[..., None].astype(np.float64))
+    k = torch.from_numpy(_signs(yk) * ak[..., None].astype(np.float64))
+    mask = torch.from_numpy(dense.astype(np.float64))[None].expand(B, -1, -1, -1).clone()
+    mask[~torch.from_numpy(keep)] = float("-inf")
+    want = torch.nn.functional.scaled_dot_product_attention(q, k, torch.from_numpy(v.astype(np.float64)),
+                                                            attn_mask=mask).numpy()
+    assert np.allclose(res["out"], want, rtol=1e-5, atol=1e-6)
+
+
 # ------------------------------------------------------------------ quantized path
 def test_vquant_closed_form_and_rounding():
     # per-channel scale s (a power of two) with max |V| = 127 s: scale is s exactly
