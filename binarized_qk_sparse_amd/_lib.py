@@ -35,6 +35,8 @@ EXPORTS = (
     "had_attention_topn",
     "binattn_dense_q8",
     "binattn_dense_q8_fused",
+    "had_attention_topn_2d",
+    "binattn_dense_q8_2d",
 )
 
 _lib = None
@@ -70,6 +72,11 @@ def load() -> ctypes.CDLL:
     lib.binattn_dense_q8.restype = I
     lib.binattn_dense_q8_fused.argtypes = [P, P, I, I, P, P, I, I64, I64, I64, I64, P, P]
     lib.binattn_dense_q8_fused.restype = I
+    lib.had_attention_topn_2d.argtypes = [P, P, P, P, P, P, P, I64, I64, P, I, I64, I64, I64, I64, I64, I, P, P, P,
+                                          SZ, P]
+    lib.had_attention_topn_2d.restype = I
+    lib.binattn_dense_q8_2d.argtypes = [P, P, P, P, P, P, P, I64, I64, P, I, I64, I64, I64, I64, P, P, SZ, P]
+    lib.binattn_dense_q8_2d.restype = I
     if lib.had_abi_version() != HAD_ABI_VERSION:
         raise ImportError("libhad.so ABI version mismatch")
     _lib = lib

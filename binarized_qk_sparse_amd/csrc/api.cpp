@@ -81,6 +81,32 @@ int check_attention(const uint32_t* qbits, const uint32_t* kbits, const void* v,
   return HAD_OK;
 }
 
+// Two-dimensional decomposable bias of the *_2d entry points (row == NULL: none).
+struct Bias2dArgs {
+  const float* row = nullptr;
+  const float* col = nullptr;
+  const float* cls = nullptr;
+  int64_t gh = 0, gw = 0;
+};
+
+int check_bias2d(const Bias2dArgs& b, int64_t n, const char* fn) {
+  if (b.row == nullptr) return HAD_OK;
+  if (b.gh < 1 || b.gw < 1) return fail(HAD_ERR_INVALID_ARG, fn, "grid sizes must be positive");
+  if (b.gh > 32767 || b.gw > 65535) return fail(HAD_ERR_UNSUPPORTED, fn, "grid too large for the position codes");
+  if (n != b.gh * b.gw + (b.cls != nullptr ? 1 : 0))
+    return fail(HAD_ERR_INVALID_ARG, fn, "n must be grid_h * grid_w, plus one with a class token");
+  return HAD_OK;
+}
+
+void set_bias2d(AttnParams* p, const Bias2dArgs& b) {
+  p->brow = b.row;
+  p->bcol = b.col;
+  p->bcls = b.cls;
+  p->gh = (int)b.gh;
+  p->gw = (int)b.gw;
+  p->cls = b.cls != nullptr ? 1 : 0;
+}
+
 // Largest n the resident top-N kernels handle (V of one head staged in LDS; at
 // head_dim 128 the rows are twice as long).
 int64_t topn_max_n(int v_kind, int64_t d) {
@@ -173,12 +199,13 @@ int had_pack_qk(const void* q, const void* k, int x_dtype, int64_t B, int64_t H,
   return launch_status(launch_pack(p, static_cast<hipStream_t>(stream)), fn);
 }
 
-int had_attention_topn(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q, const float* alpha_k,
-                       const float* bias_table, const void* v, int v_dtype, int64_t B, int64_t H, int64_t n,
-                       int64_t d, int64_t top_n, int av_mode, float* out, int32_t* idx_out, void* workspace,
-                       size_t workspace_bytes, void* stream) {
-  static const char* fn = "had_attention_topn";
+static int topn_impl(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q, const float* alpha_k,
+                     const float* bias_table, const Bias2dArgs& b2, const void* v, int v_dtype, int64_t B, int64_t H,
+                     int64_t n, int64_t d, int64_t top_n, int av_mode, float* out, int32_t* idx_out, void* workspace,
+                     size_t workspace_bytes, void* stream, const char* fn) {
   int st = check_attention(qbits, kbits, v, v_dtype, B, H, n, d, out, fn);
+  if (st != HAD_OK) return st;
+  st = check_bias2d(b2, n, fn);
   if (st != HAD_OK) return st;
   if (top_n < 1) return fail(HAD_ERR_INVALID_ARG, fn, "top_n must be >= 1");
   if (av_mode != HAD_AV_F32 && av_mode != HAD_AV_Q8 && av_mode != HAD_AV_Q4)
@@ -190,6 +217,8 @@ int had_attention_topn(const uint32_t* qbits, const uint32_t* kbits, const float
   const bool streaming = n > topn_max_n(v_kind, d);
   if (streaming && keep > topn_stream_max_keep())
     return fail(HAD_ERR_UNSUPPORTED, fn, "min(top_n, n) too large for the long-sequence kernel");
+  if (streaming && b2.row != nullptr && bias2d_floats(b2.gh, b2.gw) > topn_stream_bias2d_max(n))
+    return fail(HAD_ERR_UNSUPPORTED, fn, "grid too long for the long-sequence kernel's bias tables");
   hipStream_t s = static_cast<hipStream_t>(stream);
   AttnParams p{};
   p.qbits = qbits;
@@ -197,6 +226,7 @@ int had_attention_topn(const uint32_t* qbits, const uint32_t* kbits, const float
   p.alpha_q = alpha_q;
   p.alpha_k = alpha_k;
   p.bias = bias_table;
+  set_bias2d(&p, b2);
   p.v = v;
   p.v_kind = v_kind;
   p.B = B;
@@ -231,11 +261,32 @@ int had_attention_topn(const uint32_t* qbits, const uint32_t* kbits, const float
   return launch_status(launch_topn(p, s), fn);
 }
 
-int binattn_dense_q8(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q, const float* alpha_k,
-                     const float* bias_table, const void* v, int v_dtype, int64_t B, int64_t H, int64_t n, int64_t d,
-                     float* out, void* workspace, size_t workspace_bytes, void* stream) {
-  static const char* fn = "binattn_dense_q8";
+int had_attention_topn(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q, const float* alpha_k,
+                       const float* bias_table, const void* v, int v_dtype, int64_t B, int64_t H, int64_t n,
+                       int64_t d, int64_t top_n, int av_mode, float* out, int32_t* idx_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return topn_impl(qbits, kbits, alpha_q, alpha_k, bias_table, Bias2dArgs{}, v, v_dtype, B, H, n, d, top_n, av_mode,
+                   out, idx_out, workspace, workspace_bytes, stream, "had_attention_topn");
+}
+
+int had_attention_topn_2d(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q, const float* alpha_k,
+                          const float* row_table, const float* col_table, const float* cls_table, int64_t grid_h,
+                          int64_t grid_w, const void* v, int v_dtype, int64_t B, int64_t H, int64_t n, int64_t d,
+                          int64_t top_n, int av_mode, float* out, int32_t* idx_out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  static const char* fn = "had_attention_topn_2d";
+  if (row_table == nullptr || col_table == nullptr) return fail(HAD_ERR_INVALID_ARG, fn, "NULL bias table");
+  return topn_impl(qbits, kbits, alpha_q, alpha_k, nullptr, Bias2dArgs{row_table, col_table, cls_table, grid_h, grid_w},
+                   v, v_dtype, B, H, n, d, top_n, av_mode, out, idx_out, workspace, workspace_bytes, stream, fn);
+}
+
+static int dense_impl(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q, const float* alpha_k,
+                      const float* bias_table, const Bias2dArgs& b2, const void* v, int v_dtype, int64_t B, int64_t H,
+                      int64_t n, int64_t d, float* out, void* workspace, size_t workspace_bytes, void* stream,
+                      const char* fn) {
   int st = check_attention(qbits, kbits, v, v_dtype, B, H, n, d, out, fn);
+  if (st != HAD_OK) return st;
+  st = check_bias2d(b2, n, fn);
   if (st != HAD_OK) return st;
   if (n > dense_q8_max_n()) return fail(HAD_ERR_UNSUPPORTED, fn, "n too large for the dense kernel");
   st = check_workspace(workspace, workspace_bytes, B, H, n, d, fn);
@@ -261,6 +312,7 @@ int binattn_dense_q8(const uint32_t* qbits, const uint32_t* kbits, const float* 
   p.alpha_q = alpha_q;
   p.alpha_k = alpha_k;
   p.bias = bias_table;
+  set_bias2d(&p, b2);
   p.v = q.vq;
   p.v_kind = 2;
   p.vscale = q.vscale;
@@ -272,6 +324,23 @@ int binattn_dense_q8(const uint32_t* qbits, const uint32_t* kbits, const float* 
   p.out = out;
   p.idx = nullptr;
   return launch_status(launch_dense_q8(p, s), fn);
+}
+
+int binattn_dense_q8(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q, const float* alpha_k,
+                     const float* bias_table, const void* v, int v_dtype, int64_t B, int64_t H, int64_t n, int64_t d,
+                     float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return dense_impl(qbits, kbits, alpha_q, alpha_k, bias_table, Bias2dArgs{}, v, v_dtype, B, H, n, d, out, workspace,
+                    workspace_bytes, stream, "binattn_dense_q8");
+}
+
+int binattn_dense_q8_2d(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q, const float* alpha_k,
+                        const float* row_table, const float* col_table, const float* cls_table, int64_t grid_h,
+                        int64_t grid_w, const void* v, int v_dtype, int64_t B, int64_t H, int64_t n, int64_t d,
+                        float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  static const char* fn = "binattn_dense_q8_2d";
+  if (row_table == nullptr || col_table == nullptr) return fail(HAD_ERR_INVALID_ARG, fn, "NULL bias table");
+  return dense_impl(qbits, kbits, alpha_q, alpha_k, nullptr, Bias2dArgs{row_table, col_table, cls_table, grid_h, grid_w},
+                    v, v_dtype, B, H, n, d, out, workspace, workspace_bytes, stream, fn);
 }
 
 int binattn_dense_q8_fused(const void* q, const void* k, int qk_dtype, int mode, const float* bias_table,

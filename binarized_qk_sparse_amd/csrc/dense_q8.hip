@@ -44,6 +44,11 @@ struct DenseKArgs {
   float* out;
   int H, n;
   float isd;
+  // two-dimensional decomposable bias in place of `bias` (brow2 != NULL)
+  const float* brow2;
+  const float* bcol2;
+  const float* bcls2;
+  int gh, gw, cls;
   // fused entry point: raw Q, K, V (each fp32 or bf16) instead of the above
   const void* xq;
   const void* xk;
@@ -111,7 +116,9 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
   __shared__ float mus[FUSED ? 2 : 1][FD];         // fused: mu of Q and K
   __shared__ double dred[FUSED ? RPP : 1][FD];     // fused: column-sum partials
   __shared__ float fred[FUSED ? RPP : 1][FD];      // fused: column-max partials
-  extern __shared__ float biasw[];  // [2n - 1 + NPAD]: the table, then zeros read by padding keys
+  // BIAS: the 1-D table [2n - 1 + NPAD] (zeros read by padding keys), or the
+  // two-dimensional tables followed by the key position codes [NPAD]
+  extern __shared__ float biasw[];
 
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;
@@ -233,9 +240,17 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
       akk[j] = (j < n && a.ak != nullptr) ? a.ak[(size_t)bh * n + j] : 1.0f;
     }
   }
-  if (BIAS)
-    for (int o = tid; o < 2 * n - 1 + NPAD; o += 256)
-      biasw[o] = o < 2 * n - 1 ? a.bias[(size_t)hh * (2 * n - 1) + o] : 0.0f;
+  const bool b2 = BIAS && a.brow2 != nullptr;  // uniform
+  uint32_t* kposs = reinterpret_cast<uint32_t*>(biasw + (b2 ? bias2d_floats(a.gh, a.gw) : 0));
+  if (BIAS) {
+    if (b2) {
+      stage_bias2d(biasw, a.brow2, a.bcol2, a.bcls2, hh, a.gh, a.gw, tid, 256);
+      for (int j = tid; j < NPAD; j += 256) kposs[j] = j < n ? grid_pos(j, a.gw, a.cls) : 0u;
+    } else {
+      for (int o = tid; o < 2 * n - 1 + NPAD; o += 256)
+        biasw[o] = o < 2 * n - 1 ? a.bias[(size_t)hh * (2 * n - 1) + o] : 0.0f;
+    }
+  }
   // int8 V transposed, four keys x four channels per step: one 32-bit load per
   // key, a byte transpose by v_perm, one 32-bit LDS store per channel.  Threads
   // with consecutive ids take consecutive key blocks of one channel group, so the
@@ -308,7 +323,8 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
       qq = load_code<D>(a.qbits, row);
       aqv = a.aq != nullptr ? a.aq[row] : 1.0f;
     }
-    const float* brow = biasw + (n - 1 - iq);  // bias of key j is brow[j]
+    const float* brow = biasw + (n - 1 - iq);  // 1-D table: bias of key j is brow[j]
+    const uint32_t qpos = b2 ? grid_pos(iq, a.gw, a.cls) : 0u;
 
     // ---- logits of this lane's A elements
     float lg[NK][8];
@@ -320,7 +336,7 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
       for (int e = 0; e < 8; ++e) {
         const int j = j0 + e;
         const int h = hamming<D>(qq, kcode[j]);
-        const float b = BIAS ? brow[j] : 0.0f;
+        const float b = BIAS ? (b2 ? bias2d_pair(biasw, a.gh, a.gw, qpos, kposs[j]) : brow[j]) : 0.0f;
         float l = canonical_logit(aqv, akk[j], D - 2 * h, a.isd, b);
         if (ks == NK - 1) l = j < n ? l : -INFINITY;  // only the last step holds padding keys
         lg[ks][e] = l;
@@ -380,8 +396,8 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
 
 template <int NK, int D, bool FUSED>
 hipError_t launch_nkd(const DenseKArgs& ka, int64_t BH, hipStream_t s) {
-  if (ka.bias != nullptr) {
-    const size_t lds = sizeof(float) * (2 * ka.n - 1 + 32 * NK);
+  if (ka.bias != nullptr || ka.brow2 != nullptr) {
+    const size_t lds = sizeof(float) * ((ka.brow2 != nullptr ? bias2d_floats(ka.gh, ka.gw) : 2 * ka.n - 1) + 32 * NK);
     hipLaunchKernelGGL((dense_q8_kernel<NK, true, D, FUSED>), dim3((unsigned)BH), dim3(64 * kWaves), lds, s, ka);
   } else {
     hipLaunchKernelGGL((dense_q8_kernel<NK, false, D, FUSED>), dim3((unsigned)BH), dim3(64 * kWaves), 0, s, ka);
@@ -421,6 +437,12 @@ hipError_t launch_dense_q8(const AttnParams& p, hipStream_t s) {
   ka.aq = p.alpha_q;
   ka.ak = p.alpha_k;
   ka.bias = p.bias;
+  ka.brow2 = p.brow;
+  ka.bcol2 = p.bcol;
+  ka.bcls2 = p.bcls;
+  ka.gh = p.gh;
+  ka.gw = p.gw;
+  ka.cls = p.cls;
   ka.vq = static_cast<const int8_t*>(p.v);
   ka.vscale = p.vscale;
   ka.out = p.out;

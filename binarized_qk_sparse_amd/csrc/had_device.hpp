@@ -184,6 +184,38 @@ HAD_DEVICE uint32_t quant_i8(float x, float s, float inv) {
   return (uint32_t)((int32_t)r) & 0xffu;
 }
 
+// ---- two-dimensional decomposable bias (row + column offset tables, class token)
+// Position code of token t: bit 31 marks the class token, bits 16..30 hold the
+// grid row and bits 0..15 the column (both 0 for the class token, so every
+// table index below stays in range).
+HAD_DEVICE uint32_t grid_pos(int t, int gw, int cls) {
+  if (t < cls) return 0x80000000u;
+  const int p = t - cls;
+  const int r = p / gw;
+  return ((uint32_t)r << 16) | (uint32_t)(p - r * gw);
+}
+
+// The tables of head h, [rows 2gh-1 | columns 2gw-1 | class->patch, patch->class,
+// class->class], into tab[0 .. bias2d floats) (threads tid, tid + nt, ...).
+HAD_DEVICE void stage_bias2d(float* tab, const float* R, const float* C, const float* X, int h, int gh, int gw,
+                             int tid, int nt) {
+  const int nr = 2 * gh - 1, nc = 2 * gw - 1;
+  for (int k = tid; k < nr + nc + 3; k += nt)
+    tab[k] = k < nr ? R[(size_t)h * nr + k]
+                    : (k < nr + nc ? C[(size_t)h * nc + (k - nr)] : (X != nullptr ? X[h * 3 + (k - nr - nc)] : 0.0f));
+}
+
+// Bias of the pair (query at qpos, key at kpos): R[rj - ri + gh - 1] + C[cj - ci + gw - 1]
+// (rounded once) between patches, a class value when either is the class token.
+HAD_DEVICE float bias2d_pair(const float* tab, int gh, int gw, uint32_t qpos, uint32_t kpos) {
+  const int ri = (int)((qpos >> 16) & 0x7fffu), ci = (int)(qpos & 0xffffu);
+  const int rj = (int)((kpos >> 16) & 0x7fffu), cj = (int)(kpos & 0xffffu);
+  const float pp = __fadd_rn(tab[rj - ri + gh - 1], tab[(2 * gh - 1) + cj - ci + gw - 1]);
+  const float* X = tab + (2 * gh - 1) + (2 * gw - 1);
+  const bool qc = (qpos >> 31) != 0, kc = (kpos >> 31) != 0;
+  return qc ? (kc ? X[2] : X[0]) : (kc ? X[1] : pp);
+}
+
 // Canonical float32 logit: each operation rounded as written, no contraction.
 HAD_DEVICE float canonical_logit(float aq, float ak, int dot, float inv_sqrt_d, float bias) {
   float t = __fmul_rn(aq, ak);

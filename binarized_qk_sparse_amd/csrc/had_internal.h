@@ -53,12 +53,22 @@ struct AttnParams {
   int64_t keep;  // min(top_n, n)
   float* out;
   int32_t* idx;
+  // two-dimensional decomposable bias (in place of `bias`, which is then NULL):
+  // row and column offset tables over a gh x gw patch grid that follows `cls`
+  // (0 or 1) class tokens, and the class token's three values; brow == NULL: none
+  const float* brow;
+  const float* bcol;
+  const float* bcls;
+  int gh, gw, cls;
 };
+// floats of the staged two-dimensional bias tables: rows, columns, class values
+__host__ __device__ inline int64_t bias2d_floats(int64_t gh, int64_t gw) { return (2 * gh - 1) + (2 * gw - 1) + 3; }
 hipError_t launch_topn(const AttnParams& p, hipStream_t s);
 bool topn_mfma_supported(const AttnParams& p);
 hipError_t launch_topn_mfma(const AttnParams& p, hipStream_t s);
 hipError_t launch_topn_stream(const AttnParams& p, hipStream_t s);
 int64_t topn_stream_max_keep();
+int64_t topn_stream_bias2d_max(int64_t n);
 hipError_t launch_dense_q8(const AttnParams& p, hipStream_t s);
 int64_t dense_q8_max_n();
 

@@ -62,6 +62,12 @@ struct TopnKArgs {
   float isd;    // float(1/sqrt(d))
   float exp_c;  // 2*isd*log2(e): integer-key exponent per Hamming step
   uint32_t list_off, cand_off, bias_off, red_off, keys_off, trash_off;
+  // two-dimensional decomposable bias (brow != NULL; float keys): tables and the
+  // key position codes are staged per head at bias_off
+  const float* brow;
+  const float* bcol;
+  const float* bcls;
+  int gh, gw, cls;
 };
 
 template <int VK, int D>
@@ -194,6 +200,7 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
     const int i0 = tile * a.qt, i1 = min(n, i0 + a.qt);
     const bool restage = bh != staged;                       // uniform over the workgroup
     const bool sync = restage || (FK && a.bias != nullptr);  // LDS contents change this unit
+    const bool b2 = FK && a.brow != nullptr;                 // uniform
     if (sync) __syncthreads();  // every wave is done with the previous unit's LDS data
     if (restage) {
       staged = bh;
@@ -241,6 +248,12 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
         for (int w = 0; w < W; ++w) kw[w][s] = ok ? kk.w[w] : 0u;
         akv[s] = (FK && ok && a.ak != nullptr) ? a.ak[(size_t)bh * n + j] : 1.0f;
       }
+    }
+    // ---- two-dimensional bias: this head's tables, then the key position codes
+    if (b2 && restage) {
+      stage_bias2d(biasw, a.brow, a.bcol, a.bcls, hh, a.gh, a.gw, (int)threadIdx.x, (int)blockDim.x);
+      uint32_t* kp = reinterpret_cast<uint32_t*>(biasw + bias2d_floats(a.gh, a.gw));
+      for (int j = threadIdx.x; j < n; j += blockDim.x) kp[j] = grid_pos(j, a.gw, a.cls);
     }
     // ---- the bias offsets this tile touches: o = j - i + n - 1 in [n - i1, 2n - 2 - i0]
     const int ob = n - i1;
@@ -383,6 +396,8 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
       const float aqv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, aqlane), i - i0));
       float lg[NS];
       const int boff = n - 1 - ob - i;  // bias window index of key j is j + boff
+      const uint32_t qpos = b2 ? grid_pos(i, a.gw, a.cls) : 0u;
+      const uint32_t* kposs = reinterpret_cast<const uint32_t*>(biasw + (b2 ? bias2d_floats(a.gh, a.gw) : 0));
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int j = 64 * s + lane;
@@ -390,7 +405,9 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
 #pragma unroll
         for (int w = 0; w < W; ++w) hd = __builtin_popcount(kw[w][s] ^ qw[w]) + hd;
         const bool ok = !PAD || j < n;
-        const float bias = (a.bias != nullptr && ok) ? biasw[j + boff] : 0.0f;
+        const float bias = !ok ? 0.0f
+                               : (b2 ? bias2d_pair(biasw, a.gh, a.gw, qpos, kposs[j])
+                                     : (a.bias != nullptr ? biasw[j + boff] : 0.0f));
         const float l = canonical_logit(aqv, akv[s], D - 2 * hd, a.isd, bias);
         lg[s] = ok ? __fadd_rn(l, 0.0f) : -INFINITY;  // -0 and +0 compare equal
       }
@@ -664,7 +681,7 @@ hipError_t launch_topn(const AttnParams& p, hipStream_t s) {
   const int NS = resident_slots(p.n);
   if (NS == 0 || (p.d == 128 && NS > 8)) return hipErrorInvalidValue;
   // head_dim 128 always takes the float-key path (exact for integer keys as well)
-  const bool fk = p.alpha_q != nullptr || p.alpha_k != nullptr || p.bias != nullptr || p.d != 64;
+  const bool fk = p.alpha_q != nullptr || p.alpha_k != nullptr || p.bias != nullptr || p.brow != nullptr || p.d != 64;
   const int vk = p.v_kind;
   const int rowb = (int)p.d * (vk == 0 ? 4 : (vk == 1 ? 2 : 1));
   TopnKArgs ka{};
@@ -673,6 +690,12 @@ hipError_t launch_topn(const AttnParams& p, hipStream_t s) {
   ka.aq = p.alpha_q;
   ka.ak = p.alpha_k;
   ka.bias = p.bias;
+  ka.brow = p.brow;
+  ka.bcol = p.bcol;
+  ka.bcls = p.bcls;
+  ka.gh = p.gh;
+  ka.gw = p.gw;
+  ka.cls = p.cls;
   ka.v = p.v;
   ka.vscale = p.vscale;
   ka.out = p.out;
@@ -686,7 +709,8 @@ hipError_t launch_topn(const AttnParams& p, hipStream_t s) {
   ka.isd = (float)(1.0 / sqrt((double)p.d));
   ka.exp_c = (float)(2.0 * (double)ka.isd * 1.4426950408889634);
   const uint32_t vbytes = align16((uint32_t)p.n * rowb);
-  const uint32_t bias_bytes = fk ? align16((uint32_t)(p.n + kQTile - 1) * 4u) : 0u;
+  uint32_t bias_bytes = fk ? align16((uint32_t)(p.n + kQTile - 1) * 4u) : 0u;
+  if (p.brow != nullptr) bias_bytes = align16((uint32_t)(bias2d_floats(p.gh, p.gw) + p.n) * 4u);
   // as many waves as LDS allows (lists and candidate buffers are per wave)
   const uint32_t per_wave = (uint32_t)ka.lcap * (fk ? 8u : 12u) + (fk ? 64u * 8u : 256u);
   const uint32_t fixed = vbytes + bias_bytes + 4u * kMaxWaves;

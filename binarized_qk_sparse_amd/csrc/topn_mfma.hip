@@ -618,7 +618,7 @@ int threshold_guess(int64_t d, int64_t keep, int64_t n) {
 
 bool topn_mfma_supported(const AttnParams& p) {
   return p.d == kD && p.v_kind == 1 && p.alpha_q == nullptr && p.alpha_k == nullptr && p.bias == nullptr &&
-         p.n >= 1 && p.n <= 1024;
+         p.brow == nullptr && p.n >= 1 && p.n <= 1024;
 }
 
 hipError_t launch_topn_mfma(const AttnParams& p, hipStream_t s) {

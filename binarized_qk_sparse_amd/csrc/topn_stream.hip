@@ -47,6 +47,11 @@ struct StreamKArgs {
   int32_t* idx;
   int H, n, keep, lcap, tiles;
   float isd;
+  // two-dimensional decomposable bias in place of `bias` (brow != NULL)
+  const float* brow;
+  const float* bcol;
+  const float* bcls;
+  int gh, gw, cls;
 };
 
 // LDS layout (bytes) for head_dim D and W waves
@@ -58,7 +63,9 @@ struct Lds {
   static constexpr uint32_t kBiasOff = kAkOff + kChunk * 4;         // float[kChunk + W]
   static constexpr uint32_t kBufOff = kBiasOff + (kChunk + 64) * 4;  // uint2[W][kCap]
   static constexpr uint32_t kCandOff = kBufOff + W * kCap * 8;      // uint2[W][64]
-  static constexpr uint32_t kTotal = kCandOff + W * 64 * 8;
+  static constexpr int kTab = W == 16 ? 1024 : 512;                  // floats of two-dimensional bias tables
+  static constexpr uint32_t kTabOff = kCandOff + W * 64 * 8;         // float[kTab]
+  static constexpr uint32_t kTotal = kTabOff + kTab * 4;
 };
 static_assert(Lds<128, 16>::kTotal <= 160 * 1024, "LDS");
 static_assert(2 * Lds<128, 8>::kTotal <= 160 * 1024, "LDS: two workgroups of eight waves per CU");
@@ -307,7 +314,8 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
   constexpr int kChunk = L::kChunk;
   Code<D>* codes = reinterpret_cast<Code<D>*>(smem + L::kCodeOff);
   float* aks = reinterpret_cast<float*>(smem + L::kAkOff);
-  float* biasw = reinterpret_cast<float*>(smem + L::kBiasOff);
+  float* biasw = reinterpret_cast<float*>(smem + L::kBiasOff);  // 1-D: bias window; 2-D: key position codes
+  float* tab = reinterpret_cast<float*>(smem + L::kTabOff);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint2* buf = reinterpret_cast<uint2*>(smem + L::kBufOff) + wave * kCap;
@@ -322,6 +330,14 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
   const size_t row = (size_t)bh * n + ic;
   const Code<D> qq = load_code<D>(a.qbits, row);
   const float aqv = a.aq != nullptr ? a.aq[row] : 1.0f;
+  const bool b2 = a.brow != nullptr;  // uniform
+  const uint32_t qpos = b2 ? grid_pos(ic, a.gw, a.cls) : 0u;
+  // two-dimensional bias: the head's tables, each entry + 0 (no -0, as for the 1-D
+  // window below); the chunk loop's first barrier orders them before any use
+  if (b2) {
+    stage_bias2d(tab, a.brow, a.bcol, a.bcls, hh, a.gh, a.gw, (int)threadIdx.x, (int)blockDim.x);
+    for (int k = threadIdx.x; k < bias2d_floats(a.gh, a.gw); k += blockDim.x) tab[k] = __fadd_rn(tab[k], 0.0f);
+  }
   const size_t kb = (size_t)bh * n;  // first key row of the head
   const float* akg = a.ak != nullptr ? a.ak + (size_t)bh * n : nullptr;
   const int ilast = min(n, i0 + kWaves) - 1;
@@ -368,7 +384,8 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
 #pragma unroll
     for (int r = 0; r <= kPer; ++r) {
       const int t = (int)threadIdx.x + r * 64 * kWaves;
-      if (t < cntb) biasw[t] = __fadd_rn(pbias[r], 0.0f);
+      if (t < cntb)
+        biasw[t] = b2 ? __builtin_bit_cast(float, grid_pos(c0 + t, a.gw, a.cls)) : __fadd_rn(pbias[r], 0.0f);
     }
   };
 
@@ -396,6 +413,10 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
     const Code<D>* cp = codes + lane;
     const float* akp = aks + lane;
     const float* bp = biasw + boff + lane;
+    const uint32_t* kp = reinterpret_cast<const uint32_t*>(biasw) + lane;  // 2-D: position code of key t
+    auto bias_of = [&](const float* w1d, const uint32_t* kpos) {
+      return b2 ? bias2d_pair(tab, a.gh, a.gw, qpos, *kpos) : *w1d;
+    };
     for (int s0 = 0; s0 < cl; s0 += 64 * kG) {
       if (s0 + 64 * kG <= cl) {
         float l[kG];
@@ -404,7 +425,7 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
 #pragma unroll
         for (int u = 0; u < kG; ++u) {
           l[u] = canonical_logit(aqv, akp[s0 + 64 * u], code_dot<D>(cp[s0 + 64 * u], qq), a.isd,
-                                 bp[s0 + 64 * u]);
+                                 bias_of(bp + s0 + 64 * u, kp + s0 + 64 * u));
           m[u] = ballot(l[u] > theta);
           tot += __builtin_popcountll(m[u]);
         }
@@ -425,7 +446,8 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
         const int t = g0 + lane;
         const bool ok = t < cl;
         const int tc = ok ? t : 0;
-        const float l = canonical_logit(aqv, aks[tc], D - 2 * hamming<D>(codes[tc], qq), a.isd, biasw[tc + boff]);
+        const float l = canonical_logit(aqv, aks[tc], D - 2 * hamming<D>(codes[tc], qq), a.isd,
+                                        bias_of(biasw + tc + boff, reinterpret_cast<const uint32_t*>(biasw) + tc));
         const bool adm = ok && l > theta;
         const uint64_t m = ballot(adm);
         if (m != 0) {
@@ -575,6 +597,9 @@ hipError_t launch_d(const StreamKArgs& ka, int vk, int64_t BH, hipStream_t s) {
 
 int64_t topn_stream_max_keep() { return kCap - 64; }
 
+// Largest two-dimensional bias tables (floats) the kernel stages for sequences of n keys.
+int64_t topn_stream_bias2d_max(int64_t n) { return n > 4096 ? Lds<64, 16>::kTab : Lds<64, 8>::kTab; }
+
 hipError_t launch_topn_stream(const AttnParams& p, hipStream_t s) {
   if ((p.d != 64 && p.d != 128) || p.keep > topn_stream_max_keep()) return hipErrorInvalidValue;
   StreamKArgs ka{};
@@ -583,6 +608,12 @@ hipError_t launch_topn_stream(const AttnParams& p, hipStream_t s) {
   ka.aq = p.alpha_q;
   ka.ak = p.alpha_k;
   ka.bias = p.bias;
+  ka.brow = p.brow;
+  ka.bcol = p.bcol;
+  ka.bcls = p.bcls;
+  ka.gh = p.gh;
+  ka.gw = p.gw;
+  ka.cls = p.cls;
   ka.v = p.v;
   ka.vscale = p.vscale;
   ka.out = p.out;

@@ -90,11 +90,22 @@ def had_pack_qk(q: torch.Tensor, k: torch.Tensor, mode: int = HAD_SIGN, ws: Opti
     return outs[0], outs[1]
 
 
+def _bias2d(bias2d):
+    """(row, col, cls, grid_h, grid_w) pointers and sizes of a two-dimensional bias dict
+    {"grid": (gh, gw), "row": [H, 2gh-1], "col": [H, 2gw-1], optional "cls": [H, 3]} (device float32)."""
+    gh, gw = (int(x) for x in bias2d["grid"])
+    for nm in ("row", "col", "cls"):
+        if bias2d.get(nm) is not None:
+            _dev(bias2d[nm], nm)
+    return _ptr(bias2d["row"]), _ptr(bias2d["col"]), _ptr(bias2d.get("cls")), gh, gw
+
+
 def had_attention_topn(qbits: torch.Tensor, kbits: torch.Tensor, v: torch.Tensor, top_n: int, *,
                        alpha_q: Optional[torch.Tensor] = None, alpha_k: Optional[torch.Tensor] = None,
-                       bias: Optional[torch.Tensor] = None, av_mode: int = HAD_AV_F32, want_idx: bool = False,
-                       ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
-    """Top-N attention; returns out f32 [B,H,n,d] (and idx int32 [B,H,n,min(N,n)] if asked)."""
+                       bias: Optional[torch.Tensor] = None, bias2d: Optional[dict] = None, av_mode: int = HAD_AV_F32,
+                       want_idx: bool = False, ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """Top-N attention; returns out f32 [B,H,n,d] (and idx int32 [B,H,n,min(N,n)] if asked).
+    ``bias2d`` (see ``_bias2d``) selects had_attention_topn_2d in place of the 1-D ``bias``."""
     for t, nm in ((qbits, "qbits"), (kbits, "kbits"), (v, "v")):
         _dev(t, nm)
     B, H, n, d = v.shape
@@ -102,9 +113,18 @@ def had_attention_topn(qbits: torch.Tensor, kbits: torch.Tensor, v: torch.Tensor
     if out is None:
         out = torch.empty((B, H, n, d), dtype=torch.float32, device=v.device)
     idx = torch.empty((B, H, n, keep), dtype=torch.int32, device=v.device) if want_idx else None
-    if av_mode == HAD_AV_Q8 and ws is None:
+    if av_mode != HAD_AV_F32 and ws is None:
         ws = workspace(B, H, n, d, v.device)
     wsz = 0 if ws is None else ws.numel()
+    if bias2d is not None:
+        if bias is not None:
+            raise ValueError("give bias or bias2d, not both")
+        st = _lib.load().had_attention_topn_2d(qbits.data_ptr(), kbits.data_ptr(), _ptr(alpha_q), _ptr(alpha_k),
+                                               *_bias2d(bias2d), v.data_ptr(), _dtype_code(v), B, H, n, d,
+                                               int(top_n), av_mode, out.data_ptr(), _ptr(idx), _ptr(ws), wsz,
+                                               _stream())
+        _lib.check("had_attention_topn_2d", st)
+        return (out, idx) if want_idx else out
     st = _lib.load().had_attention_topn(qbits.data_ptr(), kbits.data_ptr(), _ptr(alpha_q), _ptr(alpha_k),
                                         _ptr(bias), v.data_ptr(), _dtype_code(v), B, H, n, d, int(top_n),
                                         av_mode, out.data_ptr(), _ptr(idx), _ptr(ws), wsz, _stream())
@@ -114,9 +134,10 @@ def had_attention_topn(qbits: torch.Tensor, kbits: torch.Tensor, v: torch.Tensor
 
 def binattn_dense_q8(qbits: torch.Tensor, kbits: torch.Tensor, v: torch.Tensor, *,
                      alpha_q: Optional[torch.Tensor] = None, alpha_k: Optional[torch.Tensor] = None,
-                     bias: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Dense softmax, uint8 A x per-channel int8 V; returns out f32 [B,H,n,d]."""
+                     bias: Optional[torch.Tensor] = None, bias2d: Optional[dict] = None,
+                     ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Dense softmax, uint8 A x per-channel int8 V; returns out f32 [B,H,n,d].
+    ``bias2d`` selects binattn_dense_q8_2d in place of the 1-D ``bias``."""
     for t, nm in ((qbits, "qbits"), (kbits, "kbits"), (v, "v")):
         _dev(t, nm)
     B, H, n, d = v.shape
@@ -124,6 +145,14 @@ def binattn_dense_q8(qbits: torch.Tensor, kbits: torch.Tensor, v: torch.Tensor, 
         out = torch.empty((B, H, n, d), dtype=torch.float32, device=v.device)
     if ws is None:
         ws = workspace(B, H, n, d, v.device)
+    if bias2d is not None:
+        if bias is not None:
+            raise ValueError("give bias or bias2d, not both")
+        st = _lib.load().binattn_dense_q8_2d(qbits.data_ptr(), kbits.data_ptr(), _ptr(alpha_q), _ptr(alpha_k),
+                                             *_bias2d(bias2d), v.data_ptr(), _dtype_code(v), B, H, n, d,
+                                             out.data_ptr(), ws.data_ptr(), ws.numel(), _stream())
+        _lib.check("binattn_dense_q8_2d", st)
+        return out
     st = _lib.load().binattn_dense_q8(qbits.data_ptr(), kbits.data_ptr(), _ptr(alpha_q), _ptr(alpha_k),
                                       _ptr(bias), v.data_ptr(), _dtype_code(v), B, H, n, d, out.data_ptr(),
                                       ws.data_ptr(), ws.numel(), _stream())

@@ -175,6 +175,37 @@ int binattn_dense_q8(const uint32_t* qbits, const uint32_t* kbits, const float* 
                      size_t workspace_bytes, void* stream);
 
 /*
+ * had_attention_topn_2d, binattn_dense_q8_2d -- had_attention_topn and
+ * binattn_dense_q8 with a two-dimensional decomposable relative-position bias in
+ * place of bias_table (BinaryAttention section 4.4: a bias that is a sum of
+ * terms keeps the bias memory negligible at high resolution; section 2.3 for the
+ * bias in the logit).  The n tokens are an optional class token followed by a
+ * grid_h x grid_w grid of patches in row-major order (n = grid_h*grid_w, plus 1
+ * with a class token).  For patches i = (r_i, c_i) and j = (r_j, c_j):
+ *     B[i][j] = row_table[h][r_j - r_i + grid_h - 1] + col_table[h][c_j - c_i + grid_w - 1]
+ * (one float32 addition); with cls_table (float32 [H,3]) the class token is
+ * token 0 and B = cls_table[h][0] for class -> patch, [1] for patch -> class,
+ * [2] for class -> class.  cls_table NULL: no class token.
+ *
+ *  row_table   float32 [H, 2*grid_h-1]     col_table   float32 [H, 2*grid_w-1]
+ *
+ * All other arguments, the arithmetic and the errors as the 1-D entry points.
+ * HAD_ERR_INVALID_ARG: NULL table, grid sizes < 1 or n inconsistent with the grid;
+ * HAD_ERR_UNSUPPORTED: grid_h > 32767 or grid_w > 65535, or (top-N, n above the
+ * resident limit) 2*(grid_h+grid_w)+1 above 1024 floats (512 for n <= 4096).
+ */
+int had_attention_topn_2d(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q,
+                          const float* alpha_k, const float* row_table, const float* col_table,
+                          const float* cls_table, int64_t grid_h, int64_t grid_w, const void* v, int v_dtype,
+                          int64_t B, int64_t H, int64_t n, int64_t d, int64_t top_n, int av_mode, float* out,
+                          int32_t* idx_out, void* workspace, size_t workspace_bytes, void* stream);
+int binattn_dense_q8_2d(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q,
+                        const float* alpha_k, const float* row_table, const float* col_table,
+                        const float* cls_table, int64_t grid_h, int64_t grid_w, const void* v, int v_dtype,
+                        int64_t B, int64_t H, int64_t n, int64_t d, float* out, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
  * binattn_dense_q8_fused -- binattn_dense_q8 with the binarization and the V
  * quantization in the same launch, for short sequences (BinaryAttention
  * section 2.2 codes and scales, section 2.3 logits, section 2.4 quantized A*V).

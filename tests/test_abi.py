@@ -173,3 +173,33 @@ def test_dense_fused_validation(args, want):
     st = _lib.load().binattn_dense_q8_fused(a["q"], a["k"], a["qkdt"], a["mode"], None, a["v"], a["vdt"], a["B"],
                                             a["H"], a["n"], a["d"], a["out"], None)
     assert st == want
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(row=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(col=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(gh=0), _lib.HAD_ERR_INVALID_ARG),
+    (dict(n=196), _lib.HAD_ERR_INVALID_ARG),                 # class token given: n must be 197
+    (dict(cls=None), _lib.HAD_ERR_INVALID_ARG),              # no class token: n must be 196
+    (dict(gh=1, gw=5000, n=5001), _lib.HAD_ERR_UNSUPPORTED),  # long sequence, tables above its LDS space
+    (dict(gh=40000, gw=1, n=40001), _lib.HAD_ERR_UNSUPPORTED),
+    (dict(q=None), _lib.HAD_ERR_INVALID_ARG),
+])
+def test_attention_2d_validation(args, want):
+    a = dict(q=FAKE, k=FAKE, row=FAKE, col=FAKE, cls=FAKE, gh=14, gw=14, v=FAKE, vdt=_lib.HAD_BF16, B=1, H=1, n=197,
+             d=64, top_n=30, av=0, out=FAKE, ws=FAKE, wsz=1 << 30)
+    a.update(args)
+    st = _lib.load().had_attention_topn_2d(a["q"], a["k"], None, None, a["row"], a["col"], a["cls"], a["gh"], a["gw"],
+                                           a["v"], a["vdt"], a["B"], a["H"], a["n"], a["d"], a["top_n"], a["av"],
+                                           a["out"], None, a["ws"], a["wsz"], None)
+    assert st == want
+
+
+def test_dense_2d_validation():
+    lib = _lib.load()
+    st = lib.binattn_dense_q8_2d(FAKE, FAKE, None, None, FAKE, FAKE, None, 14, 14, FAKE, _lib.HAD_BF16, 1, 1, 197, 64,
+                                 FAKE, FAKE, 1 << 30, None)
+    assert st == _lib.HAD_ERR_INVALID_ARG  # 14 x 14 without a class token is 196 tokens
+    st = lib.binattn_dense_q8_2d(FAKE, FAKE, None, None, FAKE, None, FAKE, 14, 14, FAKE, _lib.HAD_BF16, 1, 1, 197, 64,
+                                 FAKE, FAKE, 1 << 30, None)
+    assert st == _lib.HAD_ERR_INVALID_ARG
