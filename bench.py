@@ -128,6 +128,8 @@ def cpu_baseline(w, g, budget_s: float):
     if w.mode == 0:
         aq = ak = None
     bias = None if g["bias"] is None else g["bias"].numpy()
+    b2 = None if g.get("bias2d") is None else {k: (x.numpy() if hasattr(x, "numpy") else x)
+                                                for k, x in g["bias2d"].items()}
     total = w.B * w.H * w.n
     rows_done, t_att, count = 0, 0.0, 256
     rng = np.random.default_rng(12345)
@@ -137,7 +139,8 @@ def cpu_baseline(w, g, budget_s: float):
         size = min(count, total - rows_done)
         rows = np.sort(rng.choice(total, size=size, replace=False)).astype(np.int64)
         t1 = time.perf_counter()
-        oracle.attention(qb, kb, v, alpha_q=aq, alpha_k=ak, bias=bias, top_n=w.top_n, av_mode=w.av_mode, rows=rows)
+        oracle.attention(qb, kb, v, alpha_q=aq, alpha_k=ak, bias=bias, bias2d=b2, top_n=w.top_n, av_mode=w.av_mode,
+                         rows=rows)
         t_att += time.perf_counter() - t1
         rows_done += len(rows)
         count *= 2
@@ -265,6 +268,14 @@ def main():
     pa = aq.data_ptr() if w.mode == 1 else None
     pk = ak.data_ptr() if w.mode == 1 else None
     pb = None if bias is None else bias.data_ptr()
+    b2 = None
+    if g.get("bias2d") is not None:  # two-dimensional decomposable bias: the *_2d entry points
+        b2d = {k: (x.to(dev) if hasattr(x, "to") else x) for k, x in g["bias2d"].items()}
+        b2 = (b2d["row"].data_ptr(), b2d["col"].data_ptr(), b2d["cls"].data_ptr() if "cls" in b2d else None,
+              b2d["grid"][0], b2d["grid"][1])
+        if args.fused:
+            print("--fused takes the 1-D bias table only", file=sys.stderr)
+            sys.exit(2)
     def pack():
         s = torch.cuda.current_stream().cuda_stream  # the capture stream while a graph records
         ops._lib.check("had_pack_qk", lib.had_pack_qk(q.data_ptr(), k.data_ptr(), dt, w.B, w.H, w.n, w.d, w.mode,
@@ -276,9 +287,16 @@ def main():
         if args.fused:
             st = lib.binattn_dense_q8_fused(q.data_ptr(), k.data_ptr(), dt, w.mode, pb, v.data_ptr(),
                                             ops._dtype_code(v), w.B, w.H, w.n, w.d, out.data_ptr(), s)
+        elif w.top_n is None and b2 is not None:
+            st = lib.binattn_dense_q8_2d(qb.data_ptr(), kb.data_ptr(), pa, pk, *b2, v.data_ptr(), dt, w.B, w.H, w.n,
+                                         w.d, out.data_ptr(), ws.data_ptr(), ws.numel(), s)
         elif w.top_n is None:
             st = lib.binattn_dense_q8(qb.data_ptr(), kb.data_ptr(), pa, pk, pb, v.data_ptr(), dt, w.B, w.H, w.n,
                                       w.d, out.data_ptr(), ws.data_ptr(), ws.numel(), s)
+        elif b2 is not None:
+            st = lib.had_attention_topn_2d(qb.data_ptr(), kb.data_ptr(), pa, pk, *b2, v.data_ptr(), dt, w.B, w.H, w.n,
+                                           w.d, w.top_n, w.av_mode, out.data_ptr(), None, ws.data_ptr(), ws.numel(),
+                                           s)
         else:
             st = lib.had_attention_topn(qb.data_ptr(), kb.data_ptr(), pa, pk, pb, v.data_ptr(), dt, w.B, w.H, w.n,
                                         w.d, w.top_n, w.av_mode, out.data_ptr(), None, ws.data_ptr(), ws.numel(), s)
@@ -413,7 +431,8 @@ def main():
         "config": {
             "workload": f"{w.name}: B={w.B} H={w.H} n={w.n} d={w.d} {kept} {w.dtype} "
                         f"{'plain sign' if w.mode == 0 else 'mean-centred scaled sign'}"
-                        f"{' + rel-pos bias' if w.bias else ''}, {['fp32', 'uint8 x int8', 'uint8 x int4'][w.av_mode]} A*V",
+                        f"{'' if not w.bias else (' + rel-pos bias' if w.grid is None else f' + 2-D rel-pos bias over a {w.grid[0]}x{w.grid[1]} grid')}"
+                        f", {['fp32', 'uint8 x int8', 'uint8 x int4'][w.av_mode]} A*V",
             "global_batch": w.B,
             "heads": w.H,
             "seq_len": w.n,

@@ -92,7 +92,7 @@ struct Bias2dArgs {
 int check_bias2d(const Bias2dArgs& b, int64_t n, const char* fn) {
   if (b.row == nullptr) return HAD_OK;
   if (b.gh < 1 || b.gw < 1) return fail(HAD_ERR_INVALID_ARG, fn, "grid sizes must be positive");
-  if (b.gh > 32767 || b.gw > 65535) return fail(HAD_ERR_UNSUPPORTED, fn, "grid too large for the position codes");
+  if (b.gh > 13000 || b.gw > 13000) return fail(HAD_ERR_UNSUPPORTED, fn, "grid too large for the position codes");
   if (n != b.gh * b.gw + (b.cls != nullptr ? 1 : 0))
     return fail(HAD_ERR_INVALID_ARG, fn, "n must be grid_h * grid_w, plus one with a class token");
   return HAD_OK;
@@ -217,7 +217,7 @@ static int topn_impl(const uint32_t* qbits, const uint32_t* kbits, const float* 
   const bool streaming = n > topn_max_n(v_kind, d);
   if (streaming && keep > topn_stream_max_keep())
     return fail(HAD_ERR_UNSUPPORTED, fn, "min(top_n, n) too large for the long-sequence kernel");
-  if (streaming && b2.row != nullptr && bias2d_floats(b2.gh, b2.gw) > topn_stream_bias2d_max(n))
+  if (streaming && b2.row != nullptr && bias2d_floats(b2.gh, b2.gw, b2.cls != nullptr) > topn_stream_bias2d_max(n))
     return fail(HAD_ERR_UNSUPPORTED, fn, "grid too long for the long-sequence kernel's bias tables");
   hipStream_t s = static_cast<hipStream_t>(stream);
   AttnParams p{};

@@ -99,7 +99,9 @@ HAD_DEVICE float row4_sum(float v) {
 // and summation order of the separate passes (had_pack's column sums, codes and
 // alpha; the V scale and int8 codes of the attention entry points), so both
 // routes give the same bits.
-template <int NK, bool BIAS, int D, bool FUSED>  // key steps of 32; NPAD = 32 * NK >= n
+// B2 (with BIAS): the two-dimensional bias, a separate instance so that the 1-D
+// path carries none of its code.
+template <int NK, bool BIAS, int D, bool FUSED, bool B2 = false>  // key steps of 32; NPAD = 32 * NK >= n
 __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
   constexpr int NPAD = 32 * NK;
   constexpr int NT = D / 16;  // channel tiles
@@ -240,12 +242,12 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
       akk[j] = (j < n && a.ak != nullptr) ? a.ak[(size_t)bh * n + j] : 1.0f;
     }
   }
-  const bool b2 = BIAS && a.brow2 != nullptr;  // uniform
-  uint32_t* kposs = reinterpret_cast<uint32_t*>(biasw + (b2 ? bias2d_floats(a.gh, a.gw) : 0));
+  constexpr bool b2 = BIAS && B2;
+  uint32_t* kposs = reinterpret_cast<uint32_t*>(biasw + (b2 ? bias2d_floats(a.gh, a.gw, a.cls) : 0));
   if (BIAS) {
     if (b2) {
-      stage_bias2d(biasw, a.brow2, a.bcol2, a.bcls2, hh, a.gh, a.gw, tid, 256);
-      for (int j = tid; j < NPAD; j += 256) kposs[j] = j < n ? grid_pos(j, a.gw, a.cls) : 0u;
+      stage_bias2d(biasw, a.brow2, a.bcol2, a.bcls2, hh, a.gh, a.gw, a.cls, tid, 256);
+      for (int j = tid; j < NPAD; j += 256) kposs[j] = bias2d_key(j < n ? j : n - 1, a.gh, a.gw, a.cls);
     } else {
       for (int o = tid; o < 2 * n - 1 + NPAD; o += 256)
         biasw[o] = o < 2 * n - 1 ? a.bias[(size_t)hh * (2 * n - 1) + o] : 0.0f;
@@ -324,7 +326,7 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
       aqv = a.aq != nullptr ? a.aq[row] : 1.0f;
     }
     const float* brow = biasw + (n - 1 - iq);  // 1-D table: bias of key j is brow[j]
-    const uint32_t qpos = b2 ? grid_pos(iq, a.gw, a.cls) : 0u;
+    const int2 qb2 = b2 ? bias2d_query(iq, a.gh, a.gw, a.cls) : make_int2(0, 0);
 
     // ---- logits of this lane's A elements
     float lg[NK][8];
@@ -336,7 +338,7 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
       for (int e = 0; e < 8; ++e) {
         const int j = j0 + e;
         const int h = hamming<D>(qq, kcode[j]);
-        const float b = BIAS ? (b2 ? bias2d_pair(biasw, a.gh, a.gw, qpos, kposs[j]) : brow[j]) : 0.0f;
+        const float b = BIAS ? (b2 ? bias2d_lookup(biasw, qb2, kposs[j]) : brow[j]) : 0.0f;
         float l = canonical_logit(aqv, akk[j], D - 2 * h, a.isd, b);
         if (ks == NK - 1) l = j < n ? l : -INFINITY;  // only the last step holds padding keys
         lg[ks][e] = l;
@@ -396,8 +398,16 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
 
 template <int NK, int D, bool FUSED>
 hipError_t launch_nkd(const DenseKArgs& ka, int64_t BH, hipStream_t s) {
-  if (ka.bias != nullptr || ka.brow2 != nullptr) {
-    const size_t lds = sizeof(float) * ((ka.brow2 != nullptr ? bias2d_floats(ka.gh, ka.gw) : 2 * ka.n - 1) + 32 * NK);
+  if constexpr (!FUSED) {
+    if (ka.brow2 != nullptr) {
+      const size_t lds = sizeof(float) * (bias2d_floats(ka.gh, ka.gw, ka.cls) + 32 * NK);
+      hipLaunchKernelGGL((dense_q8_kernel<NK, true, D, false, true>), dim3((unsigned)BH), dim3(64 * kWaves), lds, s,
+                         ka);
+      return hipGetLastError();
+    }
+  }
+  if (ka.bias != nullptr) {
+    const size_t lds = sizeof(float) * (2 * ka.n - 1 + 32 * NK);
     hipLaunchKernelGGL((dense_q8_kernel<NK, true, D, FUSED>), dim3((unsigned)BH), dim3(64 * kWaves), lds, s, ka);
   } else {
     hipLaunchKernelGGL((dense_q8_kernel<NK, false, D, FUSED>), dim3((unsigned)BH), dim3(64 * kWaves), 0, s, ka);

@@ -185,35 +185,55 @@ HAD_DEVICE uint32_t quant_i8(float x, float s, float inv) {
 }
 
 // ---- two-dimensional decomposable bias (row + column offset tables, class token)
-// Position code of token t: bit 31 marks the class token, bits 16..30 hold the
-// grid row and bits 0..15 the column (both 0 for the class token, so every
-// table index below stays in range).
-HAD_DEVICE uint32_t grid_pos(int t, int gw, int cls) {
-  if (t < cls) return 0x80000000u;
+// The tables are staged with the class token's values folded in, so that every
+// pair costs two table reads and one addition whatever its kind:
+//   row part  R': [0, 2gh-1) R; with a class token also [2gh-1, 3gh-1) patch->class,
+//                 [3gh-1, 4gh-1) class->patch, and 5gh-2 class->class;
+//   column part C' (after R'): [0, 2gw-1) C, zeros elsewhere (5gw-1 entries with a
+//                 class token).
+// Key code: (kr << 16) | kc, with (rj, cj) for a patch and (2gh-1, 2gw-1) for the
+// class token; query bases: (gh-1-ri, gw-1-ci) for a patch and (3gh-1, 3gw-1) for
+// the class token.  B = R'[kr + qr] + C'[kc + qc]: for two patches that is
+// R[rj - ri + gh - 1] + C[cj - ci + gw - 1], and a class-token pair adds 0 to its
+// value.
+HAD_DEVICE int bias2d_rows(int gh, int cls) { return cls ? 5 * gh - 1 : 2 * gh - 1; }
+HAD_DEVICE int bias2d_cols(int gw, int cls) { return cls ? 5 * gw - 1 : 2 * gw - 1; }
+
+HAD_DEVICE void stage_bias2d(float* tab, const float* R, const float* C, const float* X, int h, int gh, int gw,
+                             int cls, int tid, int nt) {
+  const int nr = bias2d_rows(gh, cls), nc = bias2d_cols(gw, cls);
+  for (int k = tid; k < nr + nc; k += nt) {
+    float v = 0.0f;
+    if (k < nr) {
+      if (k < 2 * gh - 1) v = R[(size_t)h * (2 * gh - 1) + k];
+      else if (k < 3 * gh - 1) v = X[h * 3 + 1];
+      else if (k < 4 * gh - 1) v = X[h * 3 + 0];
+      else if (k == 5 * gh - 2) v = X[h * 3 + 2];
+    } else if (k - nr < 2 * gw - 1) {
+      v = C[(size_t)h * (2 * gw - 1) + (k - nr)];
+    }
+    tab[k] = v;
+  }
+}
+
+HAD_DEVICE uint32_t bias2d_key(int t, int gh, int gw, int cls) {
+  if (t < cls) return ((uint32_t)(2 * gh - 1) << 16) | (uint32_t)(2 * gw - 1);
   const int p = t - cls;
   const int r = p / gw;
   return ((uint32_t)r << 16) | (uint32_t)(p - r * gw);
 }
 
-// The tables of head h, [rows 2gh-1 | columns 2gw-1 | class->patch, patch->class,
-// class->class], into tab[0 .. bias2d floats) (threads tid, tid + nt, ...).
-HAD_DEVICE void stage_bias2d(float* tab, const float* R, const float* C, const float* X, int h, int gh, int gw,
-                             int tid, int nt) {
-  const int nr = 2 * gh - 1, nc = 2 * gw - 1;
-  for (int k = tid; k < nr + nc + 3; k += nt)
-    tab[k] = k < nr ? R[(size_t)h * nr + k]
-                    : (k < nr + nc ? C[(size_t)h * nc + (k - nr)] : (X != nullptr ? X[h * 3 + (k - nr - nc)] : 0.0f));
+// Query bases into the staged tables (the column base includes the row part's length).
+HAD_DEVICE int2 bias2d_query(int i, int gh, int gw, int cls) {
+  const int nr = bias2d_rows(gh, cls);
+  if (i < cls) return make_int2(3 * gh - 1, nr + 3 * gw - 1);
+  const int p = i - cls;
+  const int r = p / gw;
+  return make_int2(gh - 1 - r, nr + gw - 1 - (p - r * gw));
 }
 
-// Bias of the pair (query at qpos, key at kpos): R[rj - ri + gh - 1] + C[cj - ci + gw - 1]
-// (rounded once) between patches, a class value when either is the class token.
-HAD_DEVICE float bias2d_pair(const float* tab, int gh, int gw, uint32_t qpos, uint32_t kpos) {
-  const int ri = (int)((qpos >> 16) & 0x7fffu), ci = (int)(qpos & 0xffffu);
-  const int rj = (int)((kpos >> 16) & 0x7fffu), cj = (int)(kpos & 0xffffu);
-  const float pp = __fadd_rn(tab[rj - ri + gh - 1], tab[(2 * gh - 1) + cj - ci + gw - 1]);
-  const float* X = tab + (2 * gh - 1) + (2 * gw - 1);
-  const bool qc = (qpos >> 31) != 0, kc = (kpos >> 31) != 0;
-  return qc ? (kc ? X[2] : X[0]) : (kc ? X[1] : pp);
+HAD_DEVICE float bias2d_lookup(const float* tab, int2 q, uint32_t key) {
+  return __fadd_rn(tab[(int)(key >> 16) + q.x], tab[(int)(key & 0xffffu) + q.y]);
 }
 
 // Canonical float32 logit: each operation rounded as written, no contraction.

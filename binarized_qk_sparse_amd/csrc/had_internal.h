@@ -61,8 +61,11 @@ struct AttnParams {
   const float* bcls;
   int gh, gw, cls;
 };
-// floats of the staged two-dimensional bias tables: rows, columns, class values
-__host__ __device__ inline int64_t bias2d_floats(int64_t gh, int64_t gw) { return (2 * gh - 1) + (2 * gw - 1) + 3; }
+// floats of the staged two-dimensional bias tables (rows and columns with the
+// class token's values folded in; see had_device.hpp)
+__host__ __device__ inline int64_t bias2d_floats(int64_t gh, int64_t gw, int64_t cls) {
+  return cls ? (5 * gh - 1) + (5 * gw - 1) : (2 * gh - 1) + (2 * gw - 1);
+}
 hipError_t launch_topn(const AttnParams& p, hipStream_t s);
 bool topn_mfma_supported(const AttnParams& p);
 hipError_t launch_topn_mfma(const AttnParams& p, hipStream_t s);

@@ -161,7 +161,9 @@ HAD_DEVICE void for_each16(const uint8_t* __restrict__ src, uint32_t total, F f)
   }
 }
 
-template <int NS, bool FK, int VK, bool PAD, int D>
+// B2 (float keys only): the two-dimensional bias, a separate instance so that the
+// 1-D path carries none of its code
+template <int NS, bool FK, int VK, bool PAD, int D, bool B2 = false>
 __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) {
   static_assert(D == 64 || (D == 128 && FK), "head_dim 128 takes the float-key path");
   constexpr int W = D / 32;
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
     const int i0 = tile * a.qt, i1 = min(n, i0 + a.qt);
     const bool restage = bh != staged;                       // uniform over the workgroup
     const bool sync = restage || (FK && a.bias != nullptr);  // LDS contents change this unit
-    const bool b2 = FK && a.brow != nullptr;                 // uniform
+    constexpr bool b2 = FK && B2;
     if (sync) __syncthreads();  // every wave is done with the previous unit's LDS data
     if (restage) {
       staged = bh;
@@ -251,9 +253,9 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
     }
     // ---- two-dimensional bias: this head's tables, then the key position codes
     if (b2 && restage) {
-      stage_bias2d(biasw, a.brow, a.bcol, a.bcls, hh, a.gh, a.gw, (int)threadIdx.x, (int)blockDim.x);
-      uint32_t* kp = reinterpret_cast<uint32_t*>(biasw + bias2d_floats(a.gh, a.gw));
-      for (int j = threadIdx.x; j < n; j += blockDim.x) kp[j] = grid_pos(j, a.gw, a.cls);
+      stage_bias2d(biasw, a.brow, a.bcol, a.bcls, hh, a.gh, a.gw, a.cls, (int)threadIdx.x, (int)blockDim.x);
+      uint32_t* kp = reinterpret_cast<uint32_t*>(biasw + bias2d_floats(a.gh, a.gw, a.cls));
+      for (int j = threadIdx.x; j < n; j += blockDim.x) kp[j] = bias2d_key(j, a.gh, a.gw, a.cls);
     }
     // ---- the bias offsets this tile touches: o = j - i + n - 1 in [n - i1, 2n - 2 - i0]
     const int ob = n - i1;
@@ -396,8 +398,8 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
       const float aqv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, aqlane), i - i0));
       float lg[NS];
       const int boff = n - 1 - ob - i;  // bias window index of key j is j + boff
-      const uint32_t qpos = b2 ? grid_pos(i, a.gw, a.cls) : 0u;
-      const uint32_t* kposs = reinterpret_cast<const uint32_t*>(biasw + (b2 ? bias2d_floats(a.gh, a.gw) : 0));
+      const int2 qb2 = b2 ? bias2d_query(i, a.gh, a.gw, a.cls) : make_int2(0, 0);
+      const uint32_t* kposs = reinterpret_cast<const uint32_t*>(biasw + (b2 ? bias2d_floats(a.gh, a.gw, a.cls) : 0));
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int j = 64 * s + lane;
@@ -406,7 +408,7 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
         for (int w = 0; w < W; ++w) hd = __builtin_popcount(kw[w][s] ^ qw[w]) + hd;
         const bool ok = !PAD || j < n;
         const float bias = !ok ? 0.0f
-                               : (b2 ? bias2d_pair(biasw, a.gh, a.gw, qpos, kposs[j])
+                               : (b2 ? bias2d_lookup(biasw, qb2, kposs[j])
                                      : (a.bias != nullptr ? biasw[j + boff] : 0.0f));
         const float l = canonical_logit(aqv, akv[s], D - 2 * hd, a.isd, bias);
         lg[s] = ok ? __fadd_rn(l, 0.0f) : -INFINITY;  // -0 and +0 compare equal
@@ -624,14 +626,22 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
   }
 }
 
-template <int NS, bool FK, int VK, bool PAD, int D>
-hipError_t launch_one(const TopnKArgs& ka, dim3 grid, dim3 block, uint32_t lds, hipStream_t s) {
+template <int NS, bool FK, int VK, bool PAD, int D, bool B2>
+hipError_t launch_inst(const TopnKArgs& ka, dim3 grid, dim3 block, uint32_t lds, hipStream_t s) {
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&topn_resident_kernel<NS, FK, VK, PAD, D>),
+      reinterpret_cast<const void*>(&topn_resident_kernel<NS, FK, VK, PAD, D, B2>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((topn_resident_kernel<NS, FK, VK, PAD, D>), grid, block, lds, s, ka);
+  hipLaunchKernelGGL((topn_resident_kernel<NS, FK, VK, PAD, D, B2>), grid, block, lds, s, ka);
   return hipGetLastError();
+}
+
+template <int NS, bool FK, int VK, bool PAD, int D>
+hipError_t launch_one(const TopnKArgs& ka, dim3 grid, dim3 block, uint32_t lds, hipStream_t s) {
+  if constexpr (FK) {
+    if (ka.brow != nullptr) return launch_inst<NS, FK, VK, PAD, D, true>(ka, grid, block, lds, s);
+  }
+  return launch_inst<NS, FK, VK, PAD, D, false>(ka, grid, block, lds, s);
 }
 
 template <int NS, bool FK, int VK, int D>
@@ -710,7 +720,7 @@ hipError_t launch_topn(const AttnParams& p, hipStream_t s) {
   ka.exp_c = (float)(2.0 * (double)ka.isd * 1.4426950408889634);
   const uint32_t vbytes = align16((uint32_t)p.n * rowb);
   uint32_t bias_bytes = fk ? align16((uint32_t)(p.n + kQTile - 1) * 4u) : 0u;
-  if (p.brow != nullptr) bias_bytes = align16((uint32_t)(bias2d_floats(p.gh, p.gw) + p.n) * 4u);
+  if (p.brow != nullptr) bias_bytes = align16((uint32_t)(bias2d_floats(p.gh, p.gw, p.cls) + p.n) * 4u);
   // as many waves as LDS allows (lists and candidate buffers are per wave)
   const uint32_t per_wave = (uint32_t)ka.lcap * (fk ? 8u : 12u) + (fk ? 64u * 8u : 256u);
   const uint32_t fixed = vbytes + bias_bytes + 4u * kMaxWaves;

@@ -63,7 +63,7 @@ struct Lds {
   static constexpr uint32_t kBiasOff = kAkOff + kChunk * 4;         // float[kChunk + W]
   static constexpr uint32_t kBufOff = kBiasOff + (kChunk + 64) * 4;  // uint2[W][kCap]
   static constexpr uint32_t kCandOff = kBufOff + W * kCap * 8;      // uint2[W][64]
-  static constexpr int kTab = W == 16 ? 1024 : 512;                  // floats of two-dimensional bias tables
+  static constexpr int kTab = W == 16 ? 1536 : 512;                  // floats of two-dimensional bias tables
   static constexpr uint32_t kTabOff = kCandOff + W * 64 * 8;         // float[kTab]
   static constexpr uint32_t kTotal = kTabOff + kTab * 4;
 };
@@ -305,7 +305,9 @@ HAD_DEVICE T reduce_scatter8(T (&acc)[8], int k) {
   return kp + __shfl_xor(snd, 8, 64);
 }
 
-template <int VK, int D, int W>
+// B2: the two-dimensional bias (a.brow != NULL), a separate instance so that the
+// 1-D path carries none of its code
+template <int VK, int D, int W, bool B2>
 __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int ROWB = row_bytes<VK, D>();
@@ -330,13 +332,13 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
   const size_t row = (size_t)bh * n + ic;
   const Code<D> qq = load_code<D>(a.qbits, row);
   const float aqv = a.aq != nullptr ? a.aq[row] : 1.0f;
-  const bool b2 = a.brow != nullptr;  // uniform
-  const uint32_t qpos = b2 ? grid_pos(ic, a.gw, a.cls) : 0u;
+  constexpr bool b2 = B2;
+  const int2 qb2 = b2 ? bias2d_query(ic, a.gh, a.gw, a.cls) : make_int2(0, 0);
   // two-dimensional bias: the head's tables, each entry + 0 (no -0, as for the 1-D
   // window below); the chunk loop's first barrier orders them before any use
   if (b2) {
-    stage_bias2d(tab, a.brow, a.bcol, a.bcls, hh, a.gh, a.gw, (int)threadIdx.x, (int)blockDim.x);
-    for (int k = threadIdx.x; k < bias2d_floats(a.gh, a.gw); k += blockDim.x) tab[k] = __fadd_rn(tab[k], 0.0f);
+    stage_bias2d(tab, a.brow, a.bcol, a.bcls, hh, a.gh, a.gw, a.cls, (int)threadIdx.x, (int)blockDim.x);
+    for (int k = threadIdx.x; k < bias2d_floats(a.gh, a.gw, a.cls); k += blockDim.x) tab[k] = __fadd_rn(tab[k], 0.0f);
   }
   const size_t kb = (size_t)bh * n;  // first key row of the head
   const float* akg = a.ak != nullptr ? a.ak + (size_t)bh * n : nullptr;
@@ -385,7 +387,8 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
     for (int r = 0; r <= kPer; ++r) {
       const int t = (int)threadIdx.x + r * 64 * kWaves;
       if (t < cntb)
-        biasw[t] = b2 ? __builtin_bit_cast(float, grid_pos(c0 + t, a.gw, a.cls)) : __fadd_rn(pbias[r], 0.0f);
+        biasw[t] = b2 ? __builtin_bit_cast(float, bias2d_key(min(c0 + t, n - 1), a.gh, a.gw, a.cls))
+                      : __fadd_rn(pbias[r], 0.0f);
     }
   };
 
@@ -415,7 +418,7 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
     const float* bp = biasw + boff + lane;
     const uint32_t* kp = reinterpret_cast<const uint32_t*>(biasw) + lane;  // 2-D: position code of key t
     auto bias_of = [&](const float* w1d, const uint32_t* kpos) {
-      return b2 ? bias2d_pair(tab, a.gh, a.gw, qpos, *kpos) : *w1d;
+      return b2 ? bias2d_lookup(tab, qb2, *kpos) : *w1d;
     };
     for (int s0 = 0; s0 < cl; s0 += 64 * kG) {
       if (s0 + 64 * kG <= cl) {
@@ -564,16 +567,22 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
   }
 }
 
-template <int VK, int D, int W>
-hipError_t launch_vk(StreamKArgs ka, int64_t BH, hipStream_t s) {
+template <int VK, int D, int W, bool B2>
+hipError_t launch_b2(StreamKArgs ka, int64_t BH, hipStream_t s) {
   constexpr uint32_t lds = Lds<D, W>::kTotal;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&topn_stream_kernel<VK, D, W>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&topn_stream_kernel<VK, D, W, B2>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)lds);
   if (attr != hipSuccess) return attr;
   ka.tiles = (ka.n + W - 1) / W;
   const dim3 grid((unsigned)(BH * ka.tiles));
-  hipLaunchKernelGGL((topn_stream_kernel<VK, D, W>), grid, dim3(64 * W), lds, s, ka);
+  hipLaunchKernelGGL((topn_stream_kernel<VK, D, W, B2>), grid, dim3(64 * W), lds, s, ka);
   return hipGetLastError();
+}
+
+template <int VK, int D, int W>
+hipError_t launch_vk(const StreamKArgs& ka, int64_t BH, hipStream_t s) {
+  return ka.brow != nullptr ? launch_b2<VK, D, W, true>(ka, BH, s) : launch_b2<VK, D, W, false>(ka, BH, s);
 }
 
 // Sixteen waves per workgroup (one per CU) for the longest sequences, where the

@@ -26,6 +26,9 @@ on, which are not available here):
   16 heads, d=64, bf16 Q/K/V iid N(0,1); mean-centred scaled sign;
   relative-position table; top-256; uint8 A x int8 V over the kept set.
   ``c5q4`` is the same with 4-bit V (7 levels each side of zero).
+* ``c4b2d``, ``c5b2d``: c4 and c5 with the two-dimensional decomposable bias
+  (row and column offset tables ~ N(0, 0.02^2) per head, tensor id 7, over
+  the 14 x 14 grid after DeiT's class token and the 128 x 128 grid).
 
 Second arguments of N(., .) are standard deviations.  Generation: NumPy
 ``default_rng([config_index, n, tensor_id])`` in float32, tensor ids Q=1, K=2,
@@ -62,6 +65,7 @@ class Workload:
     bias: bool
     av_mode: int  # AV_F32, AV_Q8 or AV_Q4
     qk_law: str  # "iid", "chan_std", "chan_mean"
+    grid: Optional[tuple] = None  # (gh, gw): two-dimensional decomposable bias over a patch grid
 
     @property
     def pairs(self) -> int:
@@ -84,6 +88,10 @@ WORKLOADS: Dict[str, Workload] = {
     "c5": Workload("c5", 4, 1, 16, 16384, 64, 256, "bf16", MEAN_SIGN, True, AV_Q8, "iid"),
     # c5 with 4-bit V (the next step BinaryAttention's conclusion names); same draws as c5
     "c5q4": Workload("c5q4", 4, 1, 16, 16384, 64, 256, "bf16", MEAN_SIGN, True, AV_Q4, "iid"),
+    # c4 and c5 with the two-dimensional decomposable bias in place of the 1-D table:
+    # DeiT-B's class token plus 14 x 14 patches, and the 128 x 128 patch grid
+    "c4b2d": Workload("c4b2d", 3, 64, 12, 197, 64, None, "bf16", MEAN_SIGN, True, AV_Q8, "chan_mean", (14, 14)),
+    "c5b2d": Workload("c5b2d", 4, 1, 16, 16384, 64, 256, "bf16", MEAN_SIGN, True, AV_Q8, "iid", (128, 128)),
     # the long-context sweep at head_dim 128 (the kernel shape of BinaryAttention's
     # speed-versus-length figure); "c3d128@n" scales N = 15 n / 128 like c3
     "c3d128": Workload("c3d128", 5, 4, 12, 1024, 128, 120, "bf16", SIGN, False, AV_F32, "chan_std"),
@@ -136,14 +144,23 @@ def generate(w: Workload, *, B: Optional[int] = None, H: Optional[int] = None) -
     elif w.qk_law == "chan_mean":
         q += (0.5 * _rng(w, 5).standard_normal((1, Hv, 1, w.d))).astype(np.float32)
         k += (0.5 * _rng(w, 6).standard_normal((1, Hv, 1, w.d))).astype(np.float32)
-    bias = None
-    if w.bias:
+    bias = bias2d = None
+    if w.bias and w.grid is None:
         bias = torch.from_numpy((0.02 * _rng(w, 4).standard_normal((Hv, 2 * w.n - 1))).astype(np.float32))
+    elif w.bias:
+        gh, gw = w.grid
+        g = _rng(w, 7)
+        bias2d = {"grid": (gh, gw),
+                  "row": torch.from_numpy((0.02 * g.standard_normal((Hv, 2 * gh - 1))).astype(np.float32)),
+                  "col": torch.from_numpy((0.02 * g.standard_normal((Hv, 2 * gw - 1))).astype(np.float32))}
+        if w.n == gh * gw + 1:
+            bias2d["cls"] = torch.from_numpy((0.02 * g.standard_normal((Hv, 3))).astype(np.float32))
     return {
         "q": _round(q, w.dtype),
         "k": _round(k, w.dtype),
         "v": _round(v, w.dtype),
         "bias": bias,
+        "bias2d": bias2d,
         "workload": w,
         "B": Bv,
         "H": Hv,

@@ -191,8 +191,10 @@ int binattn_dense_q8(const uint32_t* qbits, const uint32_t* kbits, const float* 
  *
  * All other arguments, the arithmetic and the errors as the 1-D entry points.
  * HAD_ERR_INVALID_ARG: NULL table, grid sizes < 1 or n inconsistent with the grid;
- * HAD_ERR_UNSUPPORTED: grid_h > 32767 or grid_w > 65535, or (top-N, n above the
- * resident limit) 2*(grid_h+grid_w)+1 above 1024 floats (512 for n <= 4096).
+ * HAD_ERR_UNSUPPORTED: grid_h or grid_w above 13000, or (top-N with n above the
+ * resident limit, where the tables live in on-chip memory beside the key chunks)
+ * tables of (2*grid_h-1)+(2*grid_w-1) floats, 5*(grid_h+grid_w)-2 with a class
+ * token, above 1536 (512 for n <= 4096).
  */
 int had_attention_topn_2d(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q,
                           const float* alpha_k, const float* row_table, const float* col_table,

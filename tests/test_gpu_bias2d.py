@@ -110,3 +110,32 @@ def test_bias2d_single_row_equals_1d_table_on_device():
     o1, i1 = ops.had_attention_topn(*args, alpha_q=_dt(aq), alpha_k=_dt(ak), bias=_dt(T), want_idx=True)
     torch.cuda.synchronize()
     assert torch.equal(i1, i2) and torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("name", ["c4b2d", "c5b2d"])
+def test_bias2d_full_size_workloads_sampled(name):
+    # c5b2d runs the long-sequence kernel with sixteen waves (n = 16384); c4b2d the dense kernel
+    w = synth.workload(name)
+    g = synth.generate(w)
+    ws = ops.workspace(w.B, w.H, w.n, w.d)
+    q, k, v = g["q"].to(DEV), g["k"].to(DEV), g["v"].to(DEV)
+    qb, aq, _ = ops.had_pack(q, w.mode, ws=ws)
+    kb, ak, _ = ops.had_pack(k, w.mode, ws=ws)
+    b2 = {key: (x.to(DEV) if hasattr(x, "to") else x) for key, x in g["bias2d"].items()}
+    if w.top_n is None:
+        out = ops.binattn_dense_q8(qb, kb, v, alpha_q=aq, alpha_k=ak, bias2d=b2, ws=ws)
+        idx = None
+    else:
+        out, idx = ops.had_attention_topn(qb, kb, v, w.top_n, alpha_q=aq, alpha_k=ak, bias2d=b2, av_mode=w.av_mode,
+                                          want_idx=True, ws=ws)
+    torch.cuda.synchronize()
+    ob, oaq, _ = oracle.pack(f32(g["q"]), w.mode)
+    okb, oak, _ = oracle.pack(f32(g["k"]), w.mode)
+    rows = sample_rows(w.B * w.H * w.n, 300, 8)
+    ob2 = {key: (x.numpy() if hasattr(x, "numpy") else x) for key, x in g["bias2d"].items()}
+    ref = oracle.attention(ob, okb, f32(g["v"]), alpha_q=oaq, alpha_k=oak, bias2d=ob2, top_n=w.top_n,
+                           av_mode=w.av_mode, rows=rows, want_idx=idx is not None)
+    if idx is not None:
+        assert np.array_equal(idx.cpu().numpy().reshape(-1, w.top_n)[rows], ref["idx"])
+    diff = np.abs(out.cpu().numpy().reshape(-1, w.d)[rows] - ref["out"])
+    assert np.all(diff <= q8_tolerance(ref["vscale"], rows, w.n) + 1e-6)
