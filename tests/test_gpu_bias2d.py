@@ -69,8 +69,9 @@ def test_topn_bias2d_matches_oracle(gh, gw, cls, N, d, mode, vdtype):
 
 
 @pytest.mark.parametrize("av", [synth.AV_Q8, synth.AV_Q4])
-def test_topn_bias2d_quantized_long(av):
-    n, qb, kb, aq, ak, b2, v = _case(1, 2, 48, 48, 0, 64, synth.MEAN_SIGN, torch.bfloat16, seed=2)
+@pytest.mark.parametrize("gh,gw,cls", [(48, 48, 0), (16, 20, 1)])  # long-sequence, resident kernel
+def test_topn_bias2d_quantized(av, gh, gw, cls):
+    n, qb, kb, aq, ak, b2, v = _case(1, 2, gh, gw, cls, 64, synth.MEAN_SIGN, torch.bfloat16, seed=2)
     ws = ops.workspace(1, 2, n, 64)
     out, idx = ops.had_attention_topn(_dt(qb.view(np.int32)), _dt(kb.view(np.int32)), v.to(DEV), 256,
                                       alpha_q=_dt(aq), alpha_k=_dt(ak), bias2d=_dev2d(b2), av_mode=av,
