@@ -484,12 +484,14 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
     buf[e].x = __builtin_bit_cast(uint32_t, ex);
   }
   const float inv_z = 1.0f / wave_sum_f32(z);
+  int asum = 0;  // q8: sum of A_q over the kept set
   for (int e = lane; e < a.lcap; e += 64) {
     uint2 ent = e < cnt ? buf[e] : make_uint2(0u, 0u);
     const float p = __builtin_bit_cast(float, ent.x) * inv_z;
     if (VK == 2) {
       const float qv = fminf(fmaxf(rintf(255.0f * p), 0.0f), 255.0f);
       ent.x = e < cnt ? (uint32_t)qv : 0u;
+      asum += (int)ent.x;
     } else {
       ent.x = e < cnt ? __builtin_bit_cast(uint32_t, p) : 0u;
     }
@@ -497,6 +499,55 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
     if (a.idx != nullptr && e < cnt) a.idx[row * keep + e] = (int32_t)ent.y;
   }
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
+
+  if constexpr (VK == 2) {
+    // ---- integer A*V with v_dot4_u32_u8: lane (key slot ks = lane / 16, channels c4 .. c4 + 3,
+    // c4 = 4 (lane % 16)) takes four kept keys per step, 16 keys per step over the wave.  The
+    // four keys' 32-bit reads of their channels are byte-transposed into one word per channel,
+    // and V_q + 128 (xor 0x80, unsigned) is multiplied with the packed A_q: the sum is
+    // sum A_q V_q + 128 sum A_q, exact in 32 bits (255 * 255 * 704 < 2^32).
+    const int total_a = wave_sum_i32(asum);
+    const int c4 = 4 * (lane & 15), ks = lane >> 4;
+#pragma unroll
+    for (int cb = 0; cb < D / 64; ++cb) {
+      const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + (size_t)bh * n * ROWB + cb * 64 + c4;
+      uint32_t acc[4] = {0u, 0u, 0u, 0u};
+      for (int t = 0; t < a.lcap; t += 16) {
+        const uint4 e01 = *reinterpret_cast<const uint4*>(buf + t + 4 * ks);
+        const uint4 e23 = *reinterpret_cast<const uint4*>(buf + t + 4 * ks + 2);
+        uint32_t w[4];
+        w[0] = *reinterpret_cast<const uint32_t*>(vbase + (size_t)e01.y * ROWB);
+        w[1] = *reinterpret_cast<const uint32_t*>(vbase + (size_t)e01.w * ROWB);
+        w[2] = *reinterpret_cast<const uint32_t*>(vbase + (size_t)e23.y * ROWB);
+        w[3] = *reinterpret_cast<const uint32_t*>(vbase + (size_t)e23.w * ROWB);
+        const uint32_t a4 = e01.x | (e01.z << 8) | (e23.x << 16) | (e23.z << 24);
+        const uint32_t lo01 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // w0.b0 w1.b0 w0.b1 w1.b1
+        const uint32_t hi01 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // w0.b2 w1.b2 w0.b3 w1.b3
+        const uint32_t lo23 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+        const uint32_t hi23 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+        const uint32_t vt[4] = {__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
+                                __builtin_amdgcn_perm(lo23, lo01, 0x07060302u),
+                                __builtin_amdgcn_perm(hi23, hi01, 0x05040100u),
+                                __builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_udot4(a4, vt[c] ^ 0x80808080u, acc[c], false);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        acc[c] += (uint32_t)__shfl_xor((int)acc[c], 16, 64);
+        acc[c] += (uint32_t)__shfl_xor((int)acc[c], 32, 64);
+      }
+      if (ks == 0) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int ch = cb * 64 + c4 + c;
+          const int tot = (int)(acc[c] - 128u * (uint32_t)total_a);
+          a.out[row * D + ch] = __fdiv_rn(__fmul_rn((float)tot, a.vscale[(size_t)bh * D + ch]), 255.0f);
+        }
+      }
+    }
+    return;
+  }
 
   // ---- A*V: eight lanes per kept key, eight channels per lane, rows from global memory,
   // per block of 64 channels (head_dim 128 takes two).  Four kept keys per lane are
@@ -630,7 +681,7 @@ hipError_t launch_topn_stream(const AttnParams& p, hipStream_t s) {
   ka.H = (int)p.H;
   ka.n = (int)p.n;
   ka.keep = (int)p.keep;
-  ka.lcap = (int)((p.keep + 7) / 8 * 8);
+  ka.lcap = (int)((p.keep + 15) / 16 * 16);
   ka.isd = (float)(1.0 / sqrt((double)p.d));
   const int64_t BH = p.B * p.H;
   return p.d == 128 ? launch_d<128>(ka, p.v_kind, BH, s) : launch_d<64>(ka, p.v_kind, BH, s);
