@@ -9,7 +9,7 @@
 //    waves, which process one query each in lockstep over the chunks;
 //  * the top-N is streaming: a per-wave candidate buffer in LDS admits keys
 //    whose logit beats the current threshold; when it fills, an interpolation
-//    search finds a value with between N and N + 64 entries at or above it,
+//    search finds a value with between N and N + 128 entries at or above it,
 //    which becomes the threshold (an exact selection, ties to the lower key
 //    index, when heavy ties defeat the search), and the exact selection runs
 //    once more at the end.  Keys arrive in ascending j, so a later key with a
@@ -202,7 +202,7 @@ HAD_DEVICE int select_compact(uint2* buf, uint2* cand, int cnt, int keep, int la
 }
 
 // Entries an intermediate compaction may keep above the top-`keep`.
-constexpr int kSlack = 64;
+constexpr int kSlack = 128;
 
 template <int R>
 HAD_DEVICE int count_ge_rows(const float (&v)[R], float t) {
