@@ -187,6 +187,7 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
   int staged = -1;
   float vmul = 1.0f;  // undoes the fp16 staging scale of V
   int tau_prev = 27;  // Hamming-level guess; each query starts from the last one's
+  float wlo = 0.0f, whi = 0.0f;  // float keys: the last query's final threshold bracket (empty: none)
   Code<D> qnext;
   float aqnext;
   {
@@ -424,19 +425,39 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
         vstar = -INFINITY;  // everything real is kept
         jstar = INT_MAX;
       } else {
-        float lmin = INFINITY;
+        auto row_min = [&]() {
+          float m = INFINITY;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) lmin = fminf(lmin, lg[s] == -INFINITY ? INFINITY : lg[s]);
-        lmin = -wave_max_f32(-lmin);
+          for (int s = 0; s < NS; ++s) m = fminf(m, lg[s] == -INFINITY ? INFINITY : lg[s]);
+          return -wave_max_f32(-m);
+        };
         int need;  // keys still to take at value vstar (lowest j first)
         const int ctop = count_ge_f<NS>(lg, lmax);
         if (ctop >= keep) {
           vstar = lmax;
           need = keep;
         } else {
-          // invariant: cnt(>= lo) >= keep > cnt(>= hi)
-          float lo = lmin, hi = lmax;
-          int clo = n, chi = ctop;
+          // invariant: cnt(>= lo) >= keep > cnt(>= hi).  The search starts from the last
+          // query's final bracket when its counts keep the invariant on this row (neighbouring
+          // queries have close thresholds), else from [min, max] of the row.
+          float lo, hi;
+          int clo, chi;
+          if (wlo < whi && wlo < lmax) {
+            const float b = fminf(whi, lmax);
+            const int ca = count_ge_f<NS>(lg, wlo);
+            if (ca >= keep) {
+              const int cb = b == lmax ? ctop : count_ge_f<NS>(lg, b);
+              if (cb < keep) {
+                lo = wlo, clo = ca, hi = b, chi = cb;
+              } else {
+                lo = b, clo = cb, hi = lmax, chi = ctop;
+              }
+            } else {
+              lo = row_min(), clo = n, hi = wlo, chi = ca;
+            }
+          } else {
+            lo = row_min(), clo = n, hi = lmax, chi = ctop;
+          }
           bool split = true;
           while (clo - chi > 64) {
             const float mid = 0.5f * lo + 0.5f * hi;
@@ -453,6 +474,8 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
               chi = cm;
             }
           }
+          wlo = lo;
+          whi = hi;
           if (!split) {
             vstar = lo;  // hi is the next float after lo: every candidate equals lo
             need = keep - chi;
