@@ -55,6 +55,9 @@ def _dt(a):
     (1, 40, 0, 12, 64, synth.SIGN, torch.bfloat16),       # one grid row: the 1-D table's case
     (40, 40, 1, 64, 64, synth.MEAN_SIGN, torch.bfloat16),  # long-sequence kernel (n = 1601)
     (20, 30, 0, 100, 128, synth.SIGN, torch.bfloat16),     # long-sequence kernel at head_dim 128
+    (1, 1, 0, 3, 64, synth.SIGN, torch.float32),           # a single token
+    (1, 1, 1, 1, 64, synth.MEAN_SIGN, torch.bfloat16),     # class token and one patch
+    (2, 1, 1, 5, 64, synth.MEAN_SIGN, torch.bfloat16),     # one grid column, N >= n
 ])
 def test_topn_bias2d_matches_oracle(gh, gw, cls, N, d, mode, vdtype):
     n, qb, kb, aq, ak, b2, v = _case(1, 2, gh, gw, cls, d, mode, vdtype, seed=1)
