@@ -146,7 +146,7 @@ def cpu_baseline(w, g, budget_s: float):
         count *= 2
     per_row = t_att / rows_done + t_pack / total
     value = w.n / per_row  # pairs per second
-    return {
+    res = {
         "value": value,
         "unit": "pairs/s",
         "cores": oracle.threads(),
@@ -154,6 +154,19 @@ def cpu_baseline(w, g, budget_s: float):
         "sample": f"{rows_done} query rows of {w.name} (random, seeded) in {t_att:.1f} s plus the full Q/K pack "
                   f"({t_pack:.2f} s) scaled per row",
     }
+    if w.n <= 1024:
+        # the same oracle on one thread, on a sample of at most 1024 rows (attention only)
+        threads = oracle.threads()
+        oracle.set_threads(1)
+        try:
+            rows = np.sort(rng.choice(total, size=min(1024, total), replace=False)).astype(np.int64)
+            t1 = time.perf_counter()
+            oracle.attention(qb, kb, v, alpha_q=aq, alpha_k=ak, bias=bias, bias2d=b2, top_n=w.top_n,
+                             av_mode=w.av_mode, rows=rows)
+            res["value_1thread"] = w.n * len(rows) / (time.perf_counter() - t1)
+        finally:
+            oracle.set_threads(threads)
+    return res
 
 
 def measured_ceilings(torch, dev) -> dict:
