@@ -97,6 +97,19 @@ def attention_kernel(w):
     return "topn_resident_kernel", "topn.hip"
 
 
+def path_dtype(w, kname: str) -> str:
+    """The arithmetic types of the attention path: 1-bit codes for the logits, then the A*V
+    operands.  The matrix-core top-N kernel multiplies bf16 V by softmax weights split into
+    bf16 high and low parts (16 significant bits) and accumulates in fp32."""
+    if w.av_mode == 1:
+        return "b1+u8/i8"
+    if w.av_mode == 2:
+        return "b1+u8/i4"
+    if kname == "topn_mfma_kernel":
+        return "b1+bf16x2 weights*bf16 V, f32 acc"
+    return "b1+f32"
+
+
 def traffic_from_profile(config: str, kernel: str, kernel_src: str):
     """HBM bytes per launch from the committed rocprof counter summary, if it was
     taken on this workload with the current kernel source; otherwise None."""
@@ -110,6 +123,18 @@ def traffic_from_profile(config: str, kernel: str, kernel_src: str):
     if rec.get("kernel_sha256") != h or not rec.get("kernel", "").startswith(kernel):
         return None
     return rec.get("bytes_per_launch")
+
+
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (empty when unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
 
 
 def cpu_baseline(w, g, budget_s: float):
@@ -150,6 +175,8 @@ def cpu_baseline(w, g, budget_s: float):
         "value": value,
         "unit": "pairs/s",
         "cores": oracle.threads(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{rows_done} query rows of {w.name} (random, seeded) in {t_att:.1f} s plus the full Q/K pack "
                   f"({t_pack:.2f} s) scaled per row",
@@ -439,7 +466,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "b1+f32" if w.av_mode == 0 else ("b1+u8/i8" if w.av_mode == 1 else "b1+u8/i4"),
+        "dtype": path_dtype(w, kname),
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: B={w.B} H={w.H} n={w.n} d={w.d} {kept} {w.dtype} "

@@ -24,12 +24,15 @@ HAD_MEAN_SIGN = 1
 HAD_AV_F32 = 0
 HAD_AV_Q8 = 1
 HAD_AV_Q4 = 2
+HAD_WS_VQ = 0
+HAD_WS_VSCALE = 1
 HAD_ABI_VERSION = 1
 
 EXPORTS = (
     "had_abi_version",
     "had_status_str",
     "had_workspace_bytes",
+    "had_workspace_region",
     "had_pack",
     "had_pack_qk",
     "had_attention_topn",
@@ -62,6 +65,8 @@ def load() -> ctypes.CDLL:
     lib.had_status_str.restype = ctypes.c_char_p
     lib.had_workspace_bytes.argtypes = [I64, I64, I64, I64]
     lib.had_workspace_bytes.restype = SZ
+    lib.had_workspace_region.argtypes = [I64, I64, I64, I64, I, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
+    lib.had_workspace_region.restype = I
     lib.had_pack.argtypes = [P, I, I64, I64, I64, I64, I, P, P, P, P, SZ, P]
     lib.had_pack.restype = I
     lib.had_pack_qk.argtypes = [P, P, I, I64, I64, I64, I64, I, P, P, P, P, P, P, P, SZ, P]

@@ -136,6 +136,23 @@ size_t had_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d) {
   return workspace_layout(B, H, n, d).total;
 }
 
+int had_workspace_region(int64_t B, int64_t H, int64_t n, int64_t d, int region, size_t* offset, size_t* bytes) {
+  if (offset == nullptr || bytes == nullptr || !sizes_ok(B, H, n, d)) return HAD_ERR_INVALID_ARG;
+  const WorkspaceLayout w = workspace_layout(B, H, n, d);
+  switch (region) {
+    case HAD_WS_VQ:
+      *offset = w.vq;
+      *bytes = (size_t)(B * H * n * d);
+      return HAD_OK;
+    case HAD_WS_VSCALE:
+      *offset = w.vscale;
+      *bytes = sizeof(float) * (size_t)(B * H * d);
+      return HAD_OK;
+    default:
+      return HAD_ERR_INVALID_ARG;
+  }
+}
+
 namespace {
 
 // Shared checks of had_pack and had_pack_qk; fills everything but the tensor sets.

@@ -53,7 +53,6 @@ namespace had {
 namespace {
 
 constexpr int kD = 64;
-constexpr uint32_t kC = 0x01010101u;
 constexpr uint32_t kM = 0x80808080u;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -204,16 +203,20 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   // Two buffers: first the fp4 key operands (quarters 0, 1 in the first, 2, 3 in
   // the second), then the V rows of alternate rounds.  Separate arrays, so that the
   // compiler can tell the round being read from the round being loaded.
-  __shared__ __align__(16) uint8_t vbuf0[VB];
-  __shared__ __align__(16) uint8_t vbuf1[VB];
+  // (256-byte aligned, so that the bank offsets of the key quarters below are
+  // compile-time constants and never depend on where the compiler places them)
+  __shared__ __align__(256) uint8_t vbuf0[VB];
+  __shared__ __align__(256) uint8_t vbuf1[VB];
   auto vbuf = [&](int rr) { return (lds_u8*)((rr & 1) ? vbuf1 : vbuf0); };
   // Quarter q of the fp4 key operands starts at an LDS address of 16 (q & 1) + 128 (q >> 1)
   // modulo 256: the 16 lanes of a K-block then read four 16-byte slots of each quarter
   // that together cover every bank once (64 banks of 4 bytes), or twice (32 banks).
+  // Both quarters of a buffer fit: quarter 0 at offset 0 or 128, quarter 1 at KQB
+  // rounded up by 16 or 144 (KQB is a multiple of 256), within VB >= 2 KQB + 256.
+  static_assert(KQB % 256 == 0 && VB >= 2 * KQB + 256, "fp4 key quarters and their bank offsets fit a buffer");
   auto kxq = [&](int quarter) {
-    lds_u8* const b = (lds_u8*)(quarter >= 2 ? vbuf1 : vbuf0) + (quarter & 1) * KQB;
     const uint32_t want = 16u * (uint32_t)(quarter & 1) + 128u * (uint32_t)(quarter >> 1);
-    return b + ((want - (uint32_t)(uintptr_t)b) & 255u);
+    return (lds_u8*)(quarter >= 2 ? vbuf1 : vbuf0) + (quarter & 1) * KQB + want;
   };
 
   __builtin_amdgcn_s_setprio(3);

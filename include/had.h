@@ -84,6 +84,19 @@ const char* had_status_str(int status);
  */
 size_t had_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d);
 
+/* Regions of the workspace that hold results after a quantized attention call. */
+#define HAD_WS_VQ 0     /* int8 V, [B,H,n,d], one byte per element */
+#define HAD_WS_VSCALE 1 /* float32 per-channel V scales, [B,H,d] */
+
+/*
+ * Byte offset and size of region `region` (HAD_WS_VQ or HAD_WS_VSCALE) inside a
+ * workspace of had_workspace_bytes(B,H,n,d) bytes, so that a caller can read the
+ * integer V and its scales that a quantized attention call leaves there.  Writes
+ * *offset and *bytes and returns HAD_OK; HAD_ERR_INVALID_ARG for an unknown
+ * region, NULL outputs or sizes had_workspace_bytes rejects.  Host-only.
+ */
+int had_workspace_region(int64_t B, int64_t H, int64_t n, int64_t d, int region, size_t* offset, size_t* bytes);
+
 /*
  * had_pack -- binarize and bit-pack one of Q or K.
  * (Hamming Attention Distillation, abstract: {-1,+1} keys and queries;

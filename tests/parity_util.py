@@ -38,6 +38,13 @@ def sample_rows(total: int, count: int, seed: int) -> np.ndarray:
     return np.sort(g.choice(total, size=count, replace=False)).astype(np.int64)
 
 
+def rows_per_head(BH: int, n: int, per_head: int, seed: int) -> np.ndarray:
+    """A seeded sample of ``per_head`` query rows from every (batch, head) slice, flat and sorted."""
+    g = np.random.default_rng([78, seed, BH, n])
+    take = min(per_head, n)
+    return np.concatenate([bh * n + np.sort(g.choice(n, size=take, replace=False)) for bh in range(BH)]).astype(np.int64)
+
+
 def packed_inputs(w: synth.Workload, B=None, H=None, dev="cuda"):
     """Seeded inputs plus the oracle's codes/scales; the GPU copies go to `dev`."""
     g = synth.generate(w, B=B, H=H)

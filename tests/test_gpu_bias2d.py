@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from binarized_qk_sparse_amd import ops, synth
-from parity_util import assert_close, f32, q8_tolerance, sample_rows
+from parity_util import assert_close, f32, q8_tolerance, rows_per_head, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -117,7 +117,7 @@ def test_bias2d_single_row_equals_1d_table_on_device():
 
 
 @pytest.mark.parametrize("name", ["c4b2d", "c5b2d"])
-def test_bias2d_full_size_workloads_sampled(name):
+def test_bias2d_full_size_workloads(name):
     # c5b2d runs the long-sequence kernel with sixteen waves (n = 16384); c4b2d the dense kernel
     w = synth.workload(name)
     g = synth.generate(w)
@@ -135,7 +135,8 @@ def test_bias2d_full_size_workloads_sampled(name):
     torch.cuda.synchronize()
     ob, oaq, _ = oracle.pack(f32(g["q"]), w.mode)
     okb, oak, _ = oracle.pack(f32(g["k"]), w.mode)
-    rows = sample_rows(w.B * w.H * w.n, 300, 8)
+    # every row of c4b2d; 256 rows from every head of c5b2d (the oracle sorts 16384 keys per row)
+    rows = np.arange(w.B * w.H * w.n, dtype=np.int64) if w.n <= 1024 else rows_per_head(w.B * w.H, w.n, 256, 8)
     ob2 = {key: (x.numpy() if hasattr(x, "numpy") else x) for key, x in g["bias2d"].items()}
     ref = oracle.attention(ob, okb, f32(g["v"]), alpha_q=oaq, alpha_k=oak, bias2d=ob2, top_n=w.top_n,
                            av_mode=w.av_mode, rows=rows, want_idx=idx is not None)
