@@ -27,6 +27,7 @@ HAD_AV_Q4 = 2
 HAD_WS_VQ = 0
 HAD_WS_VSCALE = 1
 HAD_ABI_VERSION = 1
+HAD_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = (
     "had_abi_version",
@@ -40,6 +41,7 @@ EXPORTS = (
     "binattn_dense_q8_fused",
     "had_attention_topn_2d",
     "binattn_dense_q8_2d",
+    "binattn_dense_q8_noalloc",
 )
 
 _lib = None
@@ -82,6 +84,8 @@ def load() -> ctypes.CDLL:
     lib.had_attention_topn_2d.restype = I
     lib.binattn_dense_q8_2d.argtypes = [P, P, P, P, P, P, P, I64, I64, P, I, I64, I64, I64, I64, P, P, SZ, P]
     lib.binattn_dense_q8_2d.restype = I
+    lib.binattn_dense_q8_noalloc.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, I64, P, P]
+    lib.binattn_dense_q8_noalloc.restype = I
     if lib.had_abi_version() != HAD_ABI_VERSION:
         raise ImportError("libhad.so ABI version mismatch")
     _lib = lib

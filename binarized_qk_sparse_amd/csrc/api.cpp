@@ -297,15 +297,23 @@ int had_attention_topn_2d(const uint32_t* qbits, const uint32_t* kbits, const fl
                    v, v_dtype, B, H, n, d, top_n, av_mode, out, idx_out, workspace, workspace_bytes, stream, fn);
 }
 
-static int dense_impl(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q, const float* alpha_k,
-                      const float* bias_table, const Bias2dArgs& b2, const void* v, int v_dtype, int64_t B, int64_t H,
-                      int64_t n, int64_t d, float* out, void* workspace, size_t workspace_bytes, void* stream,
-                      const char* fn) {
+// Every check of the dense entry points except the workspace's.
+static int dense_checks(const uint32_t* qbits, const uint32_t* kbits, const Bias2dArgs& b2, const void* v, int v_dtype,
+                        int64_t B, int64_t H, int64_t n, int64_t d, float* out, const char* fn) {
   int st = check_attention(qbits, kbits, v, v_dtype, B, H, n, d, out, fn);
   if (st != HAD_OK) return st;
   st = check_bias2d(b2, n, fn);
   if (st != HAD_OK) return st;
   if (n > dense_q8_max_n()) return fail(HAD_ERR_UNSUPPORTED, fn, "n too large for the dense kernel");
+  return HAD_OK;
+}
+
+static int dense_impl(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q, const float* alpha_k,
+                      const float* bias_table, const Bias2dArgs& b2, const void* v, int v_dtype, int64_t B, int64_t H,
+                      int64_t n, int64_t d, float* out, void* workspace, size_t workspace_bytes, void* stream,
+                      const char* fn) {
+  int st = dense_checks(qbits, kbits, b2, v, v_dtype, B, H, n, d, out, fn);
+  if (st != HAD_OK) return st;
   st = check_workspace(workspace, workspace_bytes, B, H, n, d, fn);
   if (st != HAD_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -346,9 +354,29 @@ static int dense_impl(const uint32_t* qbits, const uint32_t* kbits, const float*
 int binattn_dense_q8(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q, const float* alpha_k,
                      const float* bias_table, const void* v, int v_dtype, int64_t B, int64_t H, int64_t n, int64_t d,
                      float* out, void* workspace, size_t workspace_bytes, void* stream) {
-  return dense_impl(qbits, kbits, alpha_q, alpha_k, bias_table, Bias2dArgs{}, v, v_dtype, B, H, n, d, out, workspace,
-                    workspace_bytes, stream, "binattn_dense_q8");
+  return had::dense_q8_entry(qbits, kbits, alpha_q, alpha_k, bias_table, v, v_dtype, B, H, n, d, out, workspace,
+                             workspace_bytes, stream, "binattn_dense_q8");
 }
+
+}  // extern "C"
+
+namespace had {
+int dense_q8_entry(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q, const float* alpha_k,
+                   const float* bias_table, const void* v, int v_dtype, int64_t B, int64_t H, int64_t n, int64_t d,
+                   float* out, void* workspace, size_t workspace_bytes, void* stream, const char* fn) {
+  return dense_impl(qbits, kbits, alpha_q, alpha_k, bias_table, Bias2dArgs{}, v, v_dtype, B, H, n, d, out, workspace,
+                    workspace_bytes, stream, fn);
+}
+
+int dense_q8_check(const uint32_t* qbits, const uint32_t* kbits, const void* v, int v_dtype, int64_t B, int64_t H,
+                   int64_t n, int64_t d, float* out, const char* fn) {
+  return dense_checks(qbits, kbits, Bias2dArgs{}, v, v_dtype, B, H, n, d, out, fn);
+}
+
+int report(int status, const char* fn, const char* why) { return fail(status, fn, why); }
+}  // namespace had
+
+extern "C" {
 
 int binattn_dense_q8_2d(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q, const float* alpha_k,
                         const float* row_table, const float* col_table, const float* cls_table, int64_t grid_h,

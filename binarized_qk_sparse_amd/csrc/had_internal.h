@@ -88,6 +88,17 @@ struct DenseFusedParams {
 };
 hipError_t launch_dense_q8_fused(const DenseFusedParams& p, hipStream_t s);
 
+// binattn_dense_q8 with its checks and dispatch, for entry points that supply the
+// workspace themselves (`fn` names the caller in debug messages).
+int dense_q8_entry(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q, const float* alpha_k,
+                   const float* bias_table, const void* v, int v_dtype, int64_t B, int64_t H, int64_t n, int64_t d,
+                   float* out, void* workspace, size_t workspace_bytes, void* stream, const char* fn);
+// The argument checks of binattn_dense_q8 short of the workspace (no HIP call).
+int dense_q8_check(const uint32_t* qbits, const uint32_t* kbits, const void* v, int v_dtype, int64_t B, int64_t H,
+                   int64_t n, int64_t d, float* out, const char* fn);
+// Returns `status`, printing `why` under HAD_DEBUG.
+int report(int status, const char* fn, const char* why);
+
 // Device scratch layout inside the caller's workspace.
 struct WorkspaceLayout {
   size_t pack_partial;  // offset of double[BH, pack_chunks, d]

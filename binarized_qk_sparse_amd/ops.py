@@ -229,6 +229,24 @@ def binattn_dense_q8(qbits: torch.Tensor, kbits: torch.Tensor, v: torch.Tensor, 
     return out
 
 
+def binattn_dense_q8_noalloc(qbits: torch.Tensor, kbits: torch.Tensor, v: torch.Tensor, *,
+                             alpha_q: Optional[torch.Tensor] = None, alpha_k: Optional[torch.Tensor] = None,
+                             bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """binattn_dense_q8 without a workspace: the library's static device scratch holds the
+    integer V (sizes up to HAD_NOALLOC_SCRATCH_BYTES of workspace); returns out f32 [B,H,n,d].
+    Calls that overlap on one GPU share that scratch and must be ordered by the caller."""
+    _dev(v, "v")
+    B, H, n, d = _check_attention_args(qbits, kbits, v, v.device, alpha_q=alpha_q, alpha_k=alpha_k, bias=bias,
+                                       out=out)
+    if out is None:
+        out = torch.empty((B, H, n, d), dtype=torch.float32, device=v.device)
+    st = _lib.load().binattn_dense_q8_noalloc(qbits.data_ptr(), kbits.data_ptr(), _ptr(alpha_q), _ptr(alpha_k),
+                                              _ptr(bias), v.data_ptr(), _dtype_code(v), B, H, n, d, out.data_ptr(),
+                                              _stream())
+    _lib.check("binattn_dense_q8_noalloc", st)
+    return out
+
+
 def binattn_dense_q8_fused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: int = HAD_MEAN_SIGN, *,
                            bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Binarize Q, K and quantize V on chip, then dense q8 attention, in one launch (n <= 256);

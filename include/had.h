@@ -243,6 +243,27 @@ int binattn_dense_q8_fused(const void* q, const void* k, int qk_dtype, int mode,
                            const void* v, int v_dtype, int64_t B, int64_t H, int64_t n, int64_t d, float* out,
                            void* stream);
 
+/*
+ * binattn_dense_q8_noalloc -- binattn_dense_q8 for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, arithmetic and results as
+ * binattn_dense_q8, without the workspace: the integer V, its scales and the
+ * partial maxima live in a static device array of HAD_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on until the process ends.  No
+ * call allocates or frees memory.
+ *
+ * Sizes whose workspace (had_workspace_bytes(B,H,n,d)) exceeds
+ * HAD_NOALLOC_SCRATCH_BYTES return HAD_ERR_UNSUPPORTED before anything is
+ * enqueued; other errors as binattn_dense_q8.  All calls on one GPU share that
+ * GPU's array: calls that overlap in time on one GPU (on different streams or
+ * host threads) race on it and must be ordered by the caller.  The array keeps
+ * what the last call left; no call reads anything before writing it.
+ */
+#define HAD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int binattn_dense_q8_noalloc(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q,
+                             const float* alpha_k, const float* bias_table, const void* v, int v_dtype,
+                             int64_t B, int64_t H, int64_t n, int64_t d, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -203,3 +203,32 @@ def test_dense_2d_validation():
     st = lib.binattn_dense_q8_2d(FAKE, FAKE, None, None, FAKE, None, FAKE, 14, 14, FAKE, _lib.HAD_BF16, 1, 1, 197, 64,
                                  FAKE, FAKE, 1 << 30, None)
     assert st == _lib.HAD_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("args,want", [
+    (dict(q=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(out=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(n=0), _lib.HAD_ERR_INVALID_ARG),
+    (dict(vdt=4), _lib.HAD_ERR_INVALID_ARG),
+    (dict(d=32), _lib.HAD_ERR_UNSUPPORTED),
+    # a workspace of more than the static scratch: 256 x 16 heads x 256 tokens x 64 channels of int8 V
+    (dict(B=256, H=16, n=256), _lib.HAD_ERR_UNSUPPORTED),
+])
+def test_dense_noalloc_validation(args, want):
+    # every rejection happens before any HIP call (none is possible on this host)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, vdt=_lib.HAD_BF16, B=2, H=3, n=197, d=64, out=FAKE)
+    a.update(args)
+    st = _lib.load().binattn_dense_q8_noalloc(a["q"], a["k"], None, None, None, a["v"], a["vdt"], a["B"], a["H"],
+                                              a["n"], a["d"], a["out"], None)
+    assert st == want
+
+
+def test_noalloc_scratch_limit_matches_header():
+    with open(os.path.join(ROOT, "include", "had.h")) as f:
+        text = f.read()
+    m = re.search(r"#define\s+HAD_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)(\d+)\s*<<\s*(\d+)\)", text)
+    assert m is not None
+    assert int(m.group(1)) << int(m.group(2)) == _lib.HAD_NOALLOC_SCRATCH_BYTES
+    lib = _lib.load()
+    assert lib.had_workspace_bytes(256, 16, 256, 64) > _lib.HAD_NOALLOC_SCRATCH_BYTES
+    assert lib.had_workspace_bytes(64, 12, 197, 64) <= _lib.HAD_NOALLOC_SCRATCH_BYTES  # the DeiT-B dense workload
