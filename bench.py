@@ -81,12 +81,12 @@ def algorithmic_bytes(w) -> float:
 
 def attention_kernel(w):
     """(kernel name, source file) of the attention launch, by the library's dispatch rule:
-    dense softmax -> dense_q8; n above the resident limit (512 keys for fp32 V, 1024
+    dense softmax -> dense_q8 up to 256 tokens, dense_long beyond; n above the resident limit (512 keys for fp32 V, 1024
     otherwise, half that at head_dim 128) -> the streaming kernel; head_dim 64 with bf16
     V, integer logits (plain sign, no bias) and fp32 A*V -> the matrix-core kernel;
     anything else -> the resident kernel."""
     if w.top_n is None:
-        return "dense_q8_kernel", "dense_q8.hip"
+        return ("dense_q8_kernel", "dense_q8.hip") if w.n <= 256 else ("dense_long_kernel", "dense_long.hip")
     resident_max = 512 if (w.dtype == "f32" and w.av_mode == 0) else 1024
     if w.d == 128:
         resident_max //= 2  # rows twice as long in LDS

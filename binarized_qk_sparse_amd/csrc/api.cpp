@@ -304,7 +304,9 @@ static int dense_checks(const uint32_t* qbits, const uint32_t* kbits, const Bias
   if (st != HAD_OK) return st;
   st = check_bias2d(b2, n, fn);
   if (st != HAD_OK) return st;
-  if (n > dense_q8_max_n()) return fail(HAD_ERR_UNSUPPORTED, fn, "n too large for the dense kernel");
+  if (n > dense_q8_max_n() && b2.row != nullptr &&
+      bias2d_floats(b2.gh, b2.gw, b2.cls != nullptr) > dense_long_bias2d_max())
+    return fail(HAD_ERR_UNSUPPORTED, fn, "grid too long for the long-sequence dense kernel's bias tables");
   return HAD_OK;
 }
 
@@ -348,6 +350,7 @@ static int dense_impl(const uint32_t* qbits, const uint32_t* kbits, const float*
   p.keep = n;
   p.out = out;
   p.idx = nullptr;
+  if (n > dense_q8_max_n()) return launch_status(launch_dense_long(p, s), fn);
   return launch_status(launch_dense_q8(p, s), fn);
 }
 

@@ -74,6 +74,9 @@ int64_t topn_stream_max_keep();
 int64_t topn_stream_bias2d_max(int64_t n);
 hipError_t launch_dense_q8(const AttnParams& p, hipStream_t s);
 int64_t dense_q8_max_n();
+// dense q8 attention for n above dense_q8_max_n() (dense_long.hip): keys streamed in tiles
+hipError_t launch_dense_long(const AttnParams& p, hipStream_t s);
+int64_t dense_long_bias2d_max();
 
 // ---- binarize + quantize + dense q8 attention in one launch (dense_q8.hip)
 struct DenseFusedParams {

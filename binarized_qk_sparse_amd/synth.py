@@ -26,6 +26,9 @@ on, which are not available here):
   16 heads, d=64, bf16 Q/K/V iid N(0,1); mean-centred scaled sign;
   relative-position table; top-256; uint8 A x int8 V over the kept set.
   ``c5q4`` is the same with 4-bit V (7 levels each side of zero).
+* ``c4@n``: the DeiT-B dense workload at another length (same batch, heads and laws;
+  the relative-position table grows to 2n-1 offsets): the sweep of the dense
+  kernel over sequence lengths that BinaryAttention's kernel-speed figure runs.
 * ``c4b2d``, ``c5b2d``: c4 and c5 with the two-dimensional decomposable bias
   (row and column offset tables ~ N(0, 0.02^2) per head, tensor id 7, over
   the 14 x 14 grid after DeiT's class token and the 128 x 128 grid).

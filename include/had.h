@@ -179,7 +179,10 @@ int had_attention_topn(const uint32_t* qbits, const uint32_t* kbits, const float
  * uint8 A (scale 1/255) times per-channel int8 V with int32 accumulation
  * (BinaryAttention section 2.4: O = dequant(matmul(quant_u8(A), quant_i8(V)))).
  * Same arguments and arithmetic as had_attention_topn with top_n = n and
- * av_mode = HAD_AV_Q8; the contraction runs on int8 matrix cores.
+ * av_mode = HAD_AV_Q8; the contraction runs on int8 matrix cores.  Any n up to
+ * HAD_MAX_N: up to 256 tokens one workgroup keeps a head on chip; beyond, keys
+ * stream through on-chip memory in tiles, in two passes (row maximum and
+ * normaliser, then the quantized product).
  * workspace is required (>= had_workspace_bytes(B,H,n,d)).
  */
 int binattn_dense_q8(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q,
@@ -204,10 +207,11 @@ int binattn_dense_q8(const uint32_t* qbits, const uint32_t* kbits, const float* 
  *
  * All other arguments, the arithmetic and the errors as the 1-D entry points.
  * HAD_ERR_INVALID_ARG: NULL table, grid sizes < 1 or n inconsistent with the grid;
- * HAD_ERR_UNSUPPORTED: grid_h or grid_w above 13000, or (top-N with n above the
- * resident limit, where the tables live in on-chip memory beside the key chunks)
- * tables of (2*grid_h-1)+(2*grid_w-1) floats, 5*(grid_h+grid_w)-2 with a class
- * token, above 1536 (512 for n <= 4096).
+ * HAD_ERR_UNSUPPORTED: grid_h or grid_w above 13000, or tables of
+ * (2*grid_h-1)+(2*grid_w-1) floats (5*(grid_h+grid_w)-2 with a class token) above
+ * what the kernel keeps on chip beside its key tiles: 1536 for top-N above the
+ * resident limit (512 for n <= 4096), 4096 for the dense entry point above 256
+ * tokens.
  */
 int had_attention_topn_2d(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q,
                           const float* alpha_k, const float* row_table, const float* col_table,
