@@ -24,6 +24,8 @@
 // int32 (each of the two terms stays below 128 * 127 * 65536 < 2^31).
 #include <float.h>
 
+#include <type_traits>
+
 #include "had_device.hpp"
 #include "had_internal.h"
 #include "../../include/had.h"
@@ -65,6 +67,12 @@ HAD_DEVICE float row4_sum_f(float v) {
   v += __shfl_xor(v, 16, 64);
   return v + __shfl_xor(v, 32, 64);
 }
+
+// 2^x by v_exp_f32 alone, without the denormal-range scaling of exp2f.  Every
+// argument here is a logit minus a running or final row maximum (scaled), so at
+// most a rounding error above 0; a result below 2^-126 that flushes to 0 is
+// negligible beside the maximum's own term, which is 1.
+HAD_DEVICE float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Byte offset of key column k (0..63) of channel row c in the transposed V tile.
 // The four 16-byte chunks of a row are rotated by (c / 16) mod 4: one B-operand
@@ -210,27 +218,38 @@ __global__ __launch_bounds__(256) void dense_long_kernel(const DenseLongArgs a) 
     if (t == ntiles) {
       // the row's maximum and normaliser from its four lanes
       const float M = row4_max_f(m_l);
-      const float zr = row4_sum_f(z_l * exp2f(__builtin_fmaf(m_l, log2e, -M * log2e)));
+      const float zr = row4_sum_f(z_l * fast_exp2(__builtin_fmaf(m_l, log2e, -M * log2e)));
       mb = M * log2e;
       q255 = 255.0f / zr;
     }
-    // ---- logits of this lane's 16 keys
+    // ---- logits of this lane's 16 keys (only the last tile holds padding keys)
     float l[16];
+    auto logits = [&](auto full) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int jj = 16 * kg + e;
-      const int dot = D - 2 * hamming<D>(qq, kc[jj]);
-      float b = 0.0f;
-      if constexpr (BIAS == 1) b = bwin[jj + wbase];
-      if constexpr (BIAS == 2) b = bias2d_lookup(tab, qb2, kpos[jj]);
-      float lv;
-      if constexpr (ALPHA) {
-        lv = canonical_logit(aqv, akk[jj], dot, a.isd, b);
-      } else {
-        // alpha = 1: the canonical product 1 * 1 * dot is dot exactly
-        lv = __fadd_rn(__fmul_rn((float)dot, a.isd), b);
+      for (int e = 0; e < 16; ++e) {
+        const int jj = 16 * kg + e;
+        const int dot = code_dot<D>(qq, kc[jj]);
+        float b = 0.0f;
+        if constexpr (BIAS == 1) b = bwin[jj + wbase];
+        if constexpr (BIAS == 2) b = bias2d_lookup(tab, qb2, kpos[jj]);
+        float lv;
+        if constexpr (ALPHA) {
+          lv = canonical_logit(aqv, akk[jj], dot, a.isd, b);
+        } else {
+          // alpha = 1: the canonical product 1 * 1 * dot is dot exactly
+          lv = __fadd_rn(__fmul_rn((float)dot, a.isd), b);
+        }
+        if constexpr (decltype(full)::value) {
+          l[e] = lv;
+        } else {
+          l[e] = j0 + jj < n ? lv : -INFINITY;
+        }
       }
-      l[e] = j0 + jj < n ? lv : -INFINITY;
+    };
+    if (j0 + kKT <= n) {
+      logits(std::true_type{});
+    } else {
+      logits(std::false_type{});
     }
     if (!second) {
       float mx = l[0];
@@ -240,8 +259,8 @@ __global__ __launch_bounds__(256) void dense_long_kernel(const DenseLongArgs a) 
       const float mnb = mn == -INFINITY ? 0.0f : mn * log2e;  // (a lane with only padding so far)
       float s = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s += exp2f(__builtin_fmaf(l[e], log2e, -mnb));
-      z_l = __builtin_fmaf(z_l, exp2f(__builtin_fmaf(m_l, log2e, -mnb)), s);
+      for (int e = 0; e < 16; ++e) s += fast_exp2(__builtin_fmaf(l[e], log2e, -mnb));
+      z_l = __builtin_fmaf(z_l, fast_exp2(__builtin_fmaf(m_l, log2e, -mnb)), s);
       m_l = mn;
     } else {
       // v_cvt_pk_u8_f32 rounds to nearest even, clamps to [0, 255] and writes the
@@ -249,7 +268,7 @@ __global__ __launch_bounds__(256) void dense_long_kernel(const DenseLongArgs a) 
       uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        w[e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(exp2f(__builtin_fmaf(l[e], log2e, -mb)) * q255, e & 3, w[e >> 2]);
+        w[e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(fast_exp2(__builtin_fmaf(l[e], log2e, -mb)) * q255, e & 3, w[e >> 2]);
       const v4i A = v4i{(int)(w[0] ^ 0x80808080u), (int)(w[1] ^ 0x80808080u), (int)(w[2] ^ 0x80808080u),
                         (int)(w[3] ^ 0x80808080u)};
 #pragma unroll

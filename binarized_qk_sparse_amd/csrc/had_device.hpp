@@ -278,6 +278,20 @@ HAD_DEVICE int hamming(const Code<D>& x, const Code<D>& y) {
   return h;
 }
 
+// d - 2 h for two codes: popcounts chained through the accumulate operand of
+// v_bcnt_u32_b32 and one 24-bit multiply-add (the compiler would otherwise add
+// the popcounts, shift and subtract).
+template <int D>
+HAD_DEVICE int code_dot(const Code<D>& x, const Code<D>& y) {
+  uint32_t h;
+  asm("v_bcnt_u32_b32 %0, %1, 0" : "=v"(h) : "v"(x.w[0] ^ y.w[0]));
+#pragma unroll
+  for (int w = 1; w < D / 32; ++w) asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(h) : "v"(x.w[w] ^ y.w[w]), "v"(h));
+  int dot;
+  asm("v_mad_i32_i24 %0, %1, -2, %2" : "=v"(dot) : "v"(h), "v"(D));
+  return dot;
+}
+
 // XCD-aware remap of the linear workgroup id: consecutive logical ids land on
 // the same XCD (hardware dispatches workgroup w to XCD w % 8), so the blocks
 // that share a head's keys and values share one L2.

@@ -70,20 +70,6 @@ struct Lds {
 static_assert(Lds<128, 16>::kTotal <= 160 * 1024, "LDS");
 static_assert(2 * Lds<128, 8>::kTotal <= 160 * 1024, "LDS: two workgroups of eight waves per CU");
 
-// d - 2 h for two codes: popcounts chained through the accumulate operand of
-// v_bcnt_u32_b32 and one 24-bit multiply-add (the compiler would otherwise add
-// the popcounts, shift and subtract).
-template <int D>
-HAD_DEVICE int code_dot(const Code<D>& x, const Code<D>& y) {
-  uint32_t h;
-  asm("v_bcnt_u32_b32 %0, %1, 0" : "=v"(h) : "v"(x.w[0] ^ y.w[0]));
-#pragma unroll
-  for (int w = 1; w < D / 32; ++w) asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(h) : "v"(x.w[w] ^ y.w[w]), "v"(h));
-  int dot;
-  asm("v_mad_i32_i24 %0, %1, -2, %2" : "=v"(dot) : "v"(h), "v"(D));
-  return dot;
-}
-
 template <int VK, int D>
 constexpr int row_bytes() {
   return VK == 0 ? D * 4 : (VK == 1 ? D * 2 : D);
