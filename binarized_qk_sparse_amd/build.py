@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhad.so")
 SOURCES = ["api.cpp", "pack.hip", "vquant.hip", "topn.hip", "topn_mfma.hip", "topn_stream.hip", "dense_q8.hip",
-           "noalloc.hip", "dense_long.hip"]
+           "noalloc.hip", "dense_long.hip", "topn_wide.hip"]
 UBENCH_LIB = os.path.join(PKG, "libhad_ubench.so")
 UBENCH_SOURCES = ["ubench.hip"]
 ARCH = "gfx950"

@@ -228,13 +228,14 @@ static int topn_impl(const uint32_t* qbits, const uint32_t* kbits, const float* 
   if (av_mode != HAD_AV_F32 && av_mode != HAD_AV_Q8 && av_mode != HAD_AV_Q4)
     return fail(HAD_ERR_INVALID_ARG, fn, "unknown av_mode");
   const int64_t keep = top_n < n ? top_n : n;
-  if (keep > HAD_MAX_TOPN) return fail(HAD_ERR_UNSUPPORTED, fn, "min(top_n, n) above HAD_MAX_TOPN");
   const bool quant = av_mode != HAD_AV_F32;
   const int v_kind = quant ? 2 : (v_dtype == HAD_BF16 ? 1 : 0);
+  // above the resident limit: the streaming kernel while its candidate buffer holds
+  // the kept set, the threshold-first kernel beyond
   const bool streaming = n > topn_max_n(v_kind, d);
-  if (streaming && keep > topn_stream_max_keep())
-    return fail(HAD_ERR_UNSUPPORTED, fn, "min(top_n, n) too large for the long-sequence kernel");
-  if (streaming && b2.row != nullptr && bias2d_floats(b2.gh, b2.gw, b2.cls != nullptr) > topn_stream_bias2d_max(n))
+  const bool wide = streaming && keep > topn_stream_max_keep();
+  if (streaming && b2.row != nullptr &&
+      bias2d_floats(b2.gh, b2.gw, b2.cls != nullptr) > (wide ? topn_wide_bias2d_max() : topn_stream_bias2d_max(n)))
     return fail(HAD_ERR_UNSUPPORTED, fn, "grid too long for the long-sequence kernel's bias tables");
   hipStream_t s = static_cast<hipStream_t>(stream);
   AttnParams p{};
@@ -273,6 +274,7 @@ static int topn_impl(const uint32_t* qbits, const uint32_t* kbits, const float* 
     p.v = q.vq;
     p.vscale = q.vscale;
   }
+  if (wide) return launch_status(launch_topn_wide(p, s), fn);
   if (streaming) return launch_status(launch_topn_stream(p, s), fn);
   if (topn_mfma_supported(p)) return launch_status(launch_topn_mfma(p, s), fn);
   return launch_status(launch_topn(p, s), fn);

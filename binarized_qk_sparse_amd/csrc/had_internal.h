@@ -72,6 +72,10 @@ hipError_t launch_topn_mfma(const AttnParams& p, hipStream_t s);
 hipError_t launch_topn_stream(const AttnParams& p, hipStream_t s);
 int64_t topn_stream_max_keep();
 int64_t topn_stream_bias2d_max(int64_t n);
+// top-N above the resident limit with more kept keys than the streaming kernel
+// buffers (topn_wide.hip): threshold by radix selection, then the kept keys
+hipError_t launch_topn_wide(const AttnParams& p, hipStream_t s);
+int64_t topn_wide_bias2d_max();
 hipError_t launch_dense_q8(const AttnParams& p, hipStream_t s);
 int64_t dense_q8_max_n();
 // dense q8 attention for n above dense_q8_max_n() (dense_long.hip): keys streamed in tiles

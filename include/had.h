@@ -68,9 +68,10 @@ extern "C" {
 #define HAD_AV_Q8 1  /* uint8 A (scale 1/255) times per-channel int8 V, int32 accumulation */
 #define HAD_AV_Q4 2  /* as HAD_AV_Q8 with 4-bit V: 7 levels each side of zero (scale max|V|/7) */
 
-/* Largest sizes the kernels accept. */
+/* Largest sizes the kernels accept.  top_n itself is unbounded: min(top_n, n) keys
+ * are kept, so the kept set never exceeds HAD_MAX_TOPN = HAD_MAX_N. */
 #define HAD_MAX_N 65536
-#define HAD_MAX_TOPN 1024
+#define HAD_MAX_TOPN 65536
 
 int had_abi_version(void);
 
@@ -148,7 +149,11 @@ int had_pack_qk(const void* q, const void* k, int x_dtype, int64_t B, int64_t H,
  *  alpha_q, alpha_k  float32 [B,H,n] or NULL (alpha = 1)
  *  bias_table     float32 [H,2n-1] or NULL (B = 0)
  *  v              [B,H,n,d] of v_dtype (HAD_F32 or HAD_BF16)
- *  top_n          N >= 1; N >= n keeps every key (dense softmax)
+ *  top_n          N >= 1; N >= n keeps every key (dense softmax).  Any N at any
+ *                 n: short sequences keep a head on chip; long ones stream keys
+ *                 with a bounded candidate buffer, or, for kept sets beyond it,
+ *                 find the N-th largest logit first (radix selection over the
+ *                 keys) and then gather the kept keys
  *  av_mode        HAD_AV_F32, HAD_AV_Q8 or HAD_AV_Q4
  *  out            out float32 [B,H,n,d]
  *  idx_out        optional out int32 [B,H,n,min(N,n)]: kept key indices of

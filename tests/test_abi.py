@@ -125,7 +125,6 @@ def test_pack_qk_validation(args, want):
     (dict(d=32), _lib.HAD_ERR_UNSUPPORTED),
     (dict(d=256), _lib.HAD_ERR_UNSUPPORTED),
     (dict(n=1 << 20), _lib.HAD_ERR_UNSUPPORTED),
-    (dict(top_n=5000, n=8192), _lib.HAD_ERR_UNSUPPORTED),
     (dict(av=1, ws=None), _lib.HAD_ERR_WORKSPACE),
     (dict(av=1, wsz=100), _lib.HAD_ERR_WORKSPACE),
     (dict(av=1, ws=ctypes.c_void_p(0x1001)), _lib.HAD_ERR_WORKSPACE),
