@@ -236,6 +236,16 @@ HAD_DEVICE float bias2d_lookup(const float* tab, int2 q, uint32_t key) {
   return __fadd_rn(tab[(int)(key >> 16) + q.x], tab[(int)(key & 0xffffu) + q.y]);
 }
 
+// Whether a head's relative-position table leaves the order of the logits of plain
+// sign codes at head_dim 64 to their Hamming levels except within one level: its
+// values (tmin .. tmax over all 2n - 1 entries, none NaN) span less than one logit
+// step 2 / sqrt(64) = 0.25.  l = fl(v(h) + T) with v(h) = (64 - 2h) / 8 exact, so two
+// keys at levels h < h' differ by at least 0.25 - (tmax - tmin) > 0.01 before
+// rounding and by at most 2 * 2^-24 * 1008 through it (|T| <= 1000).
+HAD_DEVICE bool bias_levels_separate(float tmin, float tmax, bool has_nan) {
+  return !has_nan && tmax - tmin < 0.24f && tmax <= 1000.0f && tmin >= -1000.0f;
+}
+
 // Canonical float32 logit: each operation rounded as written, no contraction.
 HAD_DEVICE float canonical_logit(float aq, float ak, int dot, float inv_sqrt_d, float bias) {
   float t = __fmul_rn(aq, ak);

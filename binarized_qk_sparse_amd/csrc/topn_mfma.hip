@@ -55,6 +55,7 @@ namespace {
 constexpr int kD = 64;
 constexpr uint32_t kM = 0x80808080u;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -76,6 +77,10 @@ struct MfmaKArgs {
   int split;  // workgroups per head (four tiles each)
   int t0;     // first threshold guess
   float exp_c;  // 2 / sqrt(d) * log2(e)
+  // float keys: plain sign codes with a relative-position table
+  const float* bias;  // [H, 2n - 1], B[i][j] = bias[h][j - i + n - 1]
+  int H;
+  float isd;  // float(1 / sqrt(d))
 };
 
 // Value of lane S of this lane's 16-lane row (DPP row_newbcast; folds into the
@@ -104,6 +109,11 @@ struct Seq<0> {
 HAD_DEVICE int quad_rows_sum(int v) {
   v += __shfl_xor(v, 16, 64);
   return v + __shfl_xor(v, 32, 64);
+}
+
+HAD_DEVICE float quad_rows_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
 }
 
 // Exclusive prefix over the key quarters g = 0..3 of one query row.
@@ -179,10 +189,25 @@ HAD_DEVICE uint32_t vswz(uint32_t g, uint32_t lk) { return (g + lk) & 3u; }
 // s_waitcnt with vmcnt(0) only (expcnt and lgkmcnt left at their maxima)
 HAD_DEVICE void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
+// Byte k of the result is 0x80 where bit k of x (x < 16) is set.
+HAD_DEVICE uint32_t spread_nibble(uint32_t x) { return (((x & 0xfu) * 0x204081u) & 0x01010101u) << 7; }
+
 // IDX: also write the kept-index list (a separate instance, so that the common
 // kernel carries none of its code).
-template <int NK, bool PAD, bool IDX>
+// FK (float keys): plain sign codes with a relative-position table B.  The logit
+// l = fl(v(h) + T[o]) with v(h) = (d - 2h) / sqrt(d) is no longer a function of h
+// alone, but when the head's table spans less than one logit step (2 / sqrt(d),
+// with a margin for the rounding of the sum) every key at a level h < h' outranks
+// every key at h'.  The level threshold tau is then found exactly as for integer
+// logits, every key below tau is kept, and only the keys at tau need a float
+// selection: the rr = N - #{h < tau} best by (l desc, j asc).  The weights are
+// exp(l - v(tau) - max T) = w(tau - h) exp(T[o] - max T), a level table times a
+// per-offset table, each product split into bf16 high and low parts.  Heads whose
+// table spans a step or more take every key of a row as a candidate of the float
+// selection and weigh each kept key by its own exp(l - max l).
+template <int NK, bool PAD, bool IDX, bool FK>
 __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs a) {
+  static_assert(!FK || NK <= 8, "float keys: up to 256 keys (a lane's keys at one level fit 64 bits)");
   constexpr int KG = 8 * NK;            // keys per lane quarter
   constexpr int KR = round_keys(NK);    // keys per quarter and round
   constexpr int R = KG / KR;            // rounds
@@ -200,6 +225,12 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   __shared__ __align__(16) uint32_t one_pairs[4];  // bf16 (1, 1) pairs: the all-ones B operand
   __shared__ __align__(16) uint32_t lut_k[256];  // key bits -> -x/2: bit 1 (x = -1) -> +0.5 (0x1), else -0.5 (0x9)
   __shared__ __align__(16) uint32_t lut_q[256];  // query bits -> x: bit 1 -> -1.0 (0xA), else +1.0 (0x2)
+  // float keys: the head's table T[o] (o = j - i + n - 1), exp(T[o] - max T) (zero past
+  // the table), the level weights w(65 - e) as floats, and the table test's partials
+  __shared__ __align__(16) float ttab[FK ? 2 * NP : 1];
+  __shared__ __align__(16) float wtab[FK ? 2 * NP : 1];
+  __shared__ __align__(16) float ftab[FK ? 256 : 1];
+  __shared__ float hred[FK ? 3 * kWaves : 1];
   // Two buffers: first the fp4 key operands (quarters 0, 1 in the first, 2, 3 in
   // the second), then the V rows of alternate rounds.  Separate arrays, so that the
   // compiler can tell the round being read from the round being loaded.
@@ -232,6 +263,17 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   const bool have = t < a.tiles;                       // wave-uniform
   const size_t hb = (size_t)bh * n;
   const int i = t * 16 + r;  // this lane's query
+  // float keys: this thread's entries of the head's table, loaded with the codes
+  constexpr int TPT = FK ? (2 * NP + 64 * kWaves - 1) / (64 * kWaves) : 1;  // entries per thread
+  float tl[TPT];
+  if constexpr (FK) {
+    const float* th = a.bias + (size_t)(bh % a.H) * (2 * n - 1);
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int o = (int)threadIdx.x + u * 64 * kWaves;
+      tl[u] = o < 2 * n - 1 ? th[o] : 0.0f;
+    }
+  }
 
   // ---- V rows into LDS.  Wave w loads the KR rows of quarter w of a round, eight
   // rows per instruction (lane l: row 8 m + l / 8, 16-byte piece l % 8, i.e. block
@@ -268,6 +310,7 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
       ent = hi16 | (bf16_rne_bits(rest) << 16);
     }
     tab[e] = ent;
+    if constexpr (FK) ftab[e] = (e >= 1 && e <= 65) ? exp2f((float)(65 - e) * a.exp_c) : 0.0f;
     if (e < 4) one_pairs[e] = 0x3f803f80u;
     // bit b of e to bit 4b (three shift-or-mask steps), then to bit 3 of nibble b:
     // a set code bit turns 0x9 (-0.5) into 0x1 (+0.5) for keys, 0x2 (+1) into 0xA (-1)
@@ -290,7 +333,45 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
     const int j = min((int)threadIdx.x + u * 64 * kWaves, NP - 1);
     kc[u] = kb[PAD ? min(j, n - 1) : j];  // padding keys: any code (their distances are overwritten)
   }
+  if constexpr (FK) {
+    float tmin = INFINITY, tmax = -INFINITY, tnan = 0.0f;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int o = (int)threadIdx.x + u * 64 * kWaves;
+      if (o < 2 * NP) ttab[o] = __fadd_rn(tl[u], 0.0f);  // (no -0 entry)
+      if (o < 2 * n - 1) {
+        tmin = fminf(tmin, tl[u]);
+        tmax = fmaxf(tmax, tl[u]);
+        tnan = tl[u] == tl[u] ? tnan : 1.0f;
+      }
+    }
+    tmin = -wave_max_f32(-tmin);
+    tmax = wave_max_f32(tmax);
+    tnan = wave_max_f32(tnan);
+    if (lane == 0) {
+      hred[wave] = tmin;
+      hred[kWaves + wave] = tmax;
+      hred[2 * kWaves + wave] = tnan;
+    }
+  }
   __syncthreads();
+  bool slow = false;  // float keys: the head's table spans a logit step or more
+  if constexpr (FK) {
+    float tmin = hred[0], tmax = hred[kWaves], tnan = hred[2 * kWaves];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      tmin = fminf(tmin, hred[w]);
+      tmax = fmaxf(tmax, hred[kWaves + w]);
+      tnan = fmaxf(tnan, hred[2 * kWaves + w]);
+    }
+    slow = !bias_levels_separate(tmin, tmax, tnan != 0.0f);  // uniform over the workgroup
+    // exp(T - max T) for the weights of the level-ordered heads (entries past the table: 0)
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int o = (int)threadIdx.x + u * 64 * kWaves;
+      if (o < 2 * NP) wtab[o] = o < 2 * n - 1 ? __expf(ttab[o] - tmax) : 0.0f;
+    }
+  }
   // ---- fp4 operands of every key of the head: key j = g' KG + k goes to quarter
   // g' at k * 32: dims 0-31 in bytes 0-15, dims 32-63 in bytes 16-31
 #pragma unroll
@@ -438,6 +519,186 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
     cl_lo = llo;
     cl_hi = lhi;
   }
+  // ---- float keys: the exact selection (while the rows of rounds 0 and 1 land).
+  // Level-ordered heads: every key below tau is kept and the row keeps the
+  // rr = N - #{h < tau} best of its keys at tau by (l desc, j asc), l = fl(v(tau) +
+  // T[o]); a lane caches the logits of its first twelve keys at tau and reads the
+  // rest from the table on every pass.  Other heads: every real key is a candidate
+  // (rr = N), its logit fl(v(h) + T[o]) formed from its distance byte.  The search
+  // walks the row's distinct candidate values from the end nearer the rank (the
+  // values negated when that is the low end): each round counts the values at or
+  // above the current one and finds the next one below, in one pass and one pair
+  // of reductions, and stops at the first value with at least rs at or above it.
+  uint64_t nkb = 0;    // level-ordered heads: this lane's keys at tau that are not kept (bit p: key g KG + p)
+  uint64_t keepm = 0;  // other heads: this lane's kept keys
+  int kt_lane = 0;     // this lane's kept candidates
+  int obase = 0;       // offset o of this lane's key g KG + p is obase + p
+  float lmax = 0.0f;   // other heads: the row's largest logit
+  if constexpr (FK) {
+    const int iq = i < n ? i : n - 1;
+    obase = g * KG - iq + n - 1;
+    if (have) {
+      const float vtau = __fmul_rn((float)(kD - 2 * tau), a.isd);
+      const int nreal = PAD ? min(max(n - g * KG, 0), KG) : KG;  // this lane's real keys
+      uint64_t cm;  // candidate bits
+      if (!slow) {
+        const uint32_t kt = byte_bcast((uint32_t)tau);
+        cm = 0;
+#pragma unroll
+        for (int b = 0; b < NW; ++b) {
+          const uint32_t E = ~xor_add(P[b], kt, 0x7f7f7f7fu) & kM;
+          const uint32_t nib = ((E >> 7) & 1u) | ((E >> 14) & 2u) | ((E >> 21) & 4u) | (E >> 28);
+          cm |= (uint64_t)nib << (4 * b);
+        }
+      } else {
+        cm = nreal >= 64 ? ~0ull : ((1ull << nreal) - 1ull);
+      }
+      const int M = quad_rows_sum(__builtin_popcountll(cm));  // the row's candidates
+      const int rr = slow ? keep : keep - less;               // 1 <= rr <= M
+      const bool low = 2 * rr > M + 1;                        // the rank is nearer the low end
+      const int rs = low ? M - rr + 1 : rr;                   // rank from the searched end
+      // logit of key p of this lane's quarter (level-ordered heads: a key at tau)
+      auto logit_tau = [&](int p) { return __fadd_rn(vtau, ttab[obase + p]); };
+      auto logit_of = [&](uint32_t h, int p) {
+        return __fadd_rn(__fmul_rn((float)(kD - 2 * (int)h), a.isd), ttab[obase + p]);
+      };
+      constexpr int kCache = 12;
+      float bl[kCache];
+#pragma unroll
+      for (int k = 0; k < kCache; ++k) bl[k] = -INFINITY;
+      bool over = false;
+      if (!slow) {
+        uint64_t rest = cm;
+#pragma unroll
+        for (int k = 0; k < kCache; ++k) {
+          if (__builtin_amdgcn_ballot_w64(rest != 0) == 0) break;
+          if (rest != 0) {
+            const float x = logit_tau(__builtin_ctzll(rest));
+            bl[k] = low ? -x : x;
+            rest &= rest - 1;
+          }
+        }
+        over = rest != 0;
+      }
+      // one pass over this lane's candidates y (searched domain): count(y >= t) and
+      // max{y < t}
+      auto scan = [&](float t, int& ge, float& below) {
+        ge = 0;
+        below = -INFINITY;
+        auto take = [&](float y) {
+          ge += y >= t ? 1 : 0;
+          below = y < t ? fmaxf(below, y) : below;
+        };
+        if (slow) {
+#pragma unroll
+          for (int b = 0; b < NW; ++b)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int p = 4 * b + k;
+              if (p < nreal) {
+                const float x = logit_of((P[b] >> (8 * k)) & 0xffu, p);
+                take(low ? -x : x);
+              }
+            }
+        } else if (!over) {
+#pragma unroll
+          for (int k = 0; k < kCache; ++k) take(bl[k]);  // (-inf fillers count nowhere)
+        } else {
+          for (uint64_t q = cm; q != 0; q &= q - 1) {
+            const float x = logit_tau(__builtin_ctzll(q));
+            take(low ? -x : x);
+          }
+        }
+      };
+      int ge;
+      float L;
+      scan(INFINITY, ge, L);
+      L = quad_rows_max(L);  // the top value
+      int above = 0;         // searched values strictly above L
+      bool done = false;
+      // every round moves an unfinished row one distinct value down (at most M of
+      // them); the bound only guards against values the table test let through
+      for (int it = 0; it <= 4 * KG && __builtin_amdgcn_ballot_w64(!done) != 0; ++it) {
+        float nb;
+        scan(L, ge, nb);
+        const int c = quad_rows_sum(ge);
+        nb = quad_rows_max(nb);
+        if (!done) {
+          if (c >= rs) {
+            done = true;
+          } else {
+            above = c;
+            L = nb;
+          }
+        }
+      }
+      // L is the rs-th largest searched value.  In logits the threshold is L (or -L),
+      // with `above` (or M - #{searched >= L}) of the row's candidates strictly above it.
+      int cge, eq = 0;
+      float unused;
+      scan(L, cge, unused);
+      const int cnt_ge = quad_rows_sum(cge);
+      const int gt = low ? M - cnt_ge : above;
+      const int takeq = rr - gt;  // candidates equal to the threshold that are kept, lowest j first
+      if (slow) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < NW; ++b)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int p = 4 * b + k;
+            if (p < nreal) {
+              const float x = logit_of((P[b] >> (8 * k)) & 0xffu, p);
+              mx = fmaxf(mx, x);
+              eq += (low ? -x : x) == L ? 1 : 0;
+            }
+          }
+        lmax = quad_rows_max(mx);
+        int seen = quad_rows_excl(eq, g);
+#pragma unroll
+        for (int b = 0; b < NW; ++b)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int p = 4 * b + k;
+            if (p < nreal) {
+              const float x = logit_of((P[b] >> (8 * k)) & 0xffu, p);
+              const float y = low ? -x : x;
+              bool kept = low ? y < L : y > L;
+              if (y == L) {
+                kept = seen < takeq;
+                ++seen;
+              }
+              if (kept) {
+                keepm |= 1ull << p;
+                ++kt_lane;
+              }
+            }
+          }
+      } else {
+        for (uint64_t q = cm; q != 0; q &= q - 1) {
+          const float x = logit_tau(__builtin_ctzll(q));
+          eq += (low ? -x : x) == L ? 1 : 0;
+        }
+        int seen = quad_rows_excl(eq, g);
+        for (uint64_t q = cm; q != 0; q &= q - 1) {
+          const int p = __builtin_ctzll(q);
+          const float x = logit_tau(p);
+          const float y = low ? -x : x;
+          bool kept = low ? y < L : y > L;
+          if (y == L) {
+            kept = seen < takeq;
+            ++seen;
+          }
+          if (kept) {
+            ++kt_lane;
+          } else {
+            nkb |= 1ull << p;
+          }
+        }
+        kt_lane += cl_lo;  // every key below tau
+      }
+    }
+  }
   // ---- the rows of round 0 (and 1) are in place
   wait_vmem();  // this wave's direct-to-LDS loads
   __syncthreads();
@@ -470,7 +731,7 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   int32_t* idst = nullptr;
   int ipos = 0;
   if (IDX) {
-    ipos = quad_rows_excl(cl_lo + take, g);
+    ipos = quad_rows_excl(FK ? kt_lane : cl_lo + take, g);
     idst = a.idx + (hb + (i < n ? i : 0)) * (size_t)keep;
   }
   // One 32-key step c over the lane's keys g KG + 8c + 0..7: prep applies the tie
@@ -480,6 +741,39 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   auto prep = [&](int rr, int cl, uint32_t (&ent)[8]) {
     const int c = rr * NKR + cl;
     const uint32_t P0 = P[2 * c], P1 = P[2 * c + 1];
+    if constexpr (FK) {
+      if (slow) {
+        // every key's own weight exp(l - max l), zero where not kept (float bits in ent)
+        const uint32_t km = (uint32_t)(keepm >> (8 * c)) & 0xffu;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const uint32_t h = ((b < 4 ? P0 : P1) >> (8 * (b & 3))) & 0xffu;
+          const float l = __fadd_rn(__fmul_rn((float)(kD - 2 * (int)h), a.isd), ttab[obase + 8 * c + b]);
+          const bool kept = (km >> b) & 1u;
+          ent[b] = __builtin_bit_cast(uint32_t, kept ? __expf(l - lmax) : 0.0f);
+          if (IDX && kept && i < n && ipos < keep) idst[ipos++] = g * KG + 8 * c + b;
+        }
+        return;
+      }
+      // keys at tau that are not kept get + 128; the weight is the level weight times
+      // exp(T[o] - max T) (float bits in ent)
+      const uint32_t I0 = P0 + kidx + spread_nibble((uint32_t)(nkb >> (8 * c)) & 0xfu);
+      const uint32_t I1 = P1 + kidx + spread_nibble((uint32_t)(nkb >> (8 * c + 4)) & 0xfu);
+      if (IDX && i < n) {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const uint32_t ib = ((b < 4 ? I0 : I1) >> (8 * (b & 3))) & 0xffu;
+          if (ib <= 65u && ipos < keep) idst[ipos++] = g * KG + 8 * c + b;
+        }
+      }
+      const float* wb = wtab + obase + 8 * c;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        ent[b] = __builtin_bit_cast(uint32_t, ftab[(I0 >> (8 * b)) & 0xffu] * wb[b]);
+        ent[4 + b] = __builtin_bit_cast(uint32_t, ftab[(I1 >> (8 * b)) & 0xffu] * wb[4 + b]);
+      }
+      return;
+    }
     // keys at tau: a byte of (P ^ tau) + 0x7f has bit 7 clear exactly where h == tau
     // (every byte of P ^ tau is below 0x80, so no carry crosses a byte)
     const uint32_t E0 = ~xor_add(P0, ktau, 0x7f7f7f7fu) & kM;
@@ -526,6 +820,22 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   };
   auto make_a = [&](const uint32_t (&ent)[8], bf16x8& A_hi, bf16x8& A_lo) {
     uint32_t ah[4], al[4];
+    if constexpr (FK) {
+      // w = hi + lo: hi = bf16(w) and lo = bf16(w - hi), both rounded to nearest even
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float w0 = __builtin_bit_cast(float, ent[2 * e]), w1 = __builtin_bit_cast(float, ent[2 * e + 1]);
+        const bf16x2 h = {(__bf16)w0, (__bf16)w1};
+        const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+        const bf16x2 lo = {(__bf16)(w0 - __builtin_bit_cast(float, hb << 16)),
+                           (__bf16)(w1 - __builtin_bit_cast(float, hb & 0xffff0000u))};
+        ah[e] = hb;
+        al[e] = __builtin_bit_cast(uint32_t, lo);
+      }
+      A_hi = __builtin_bit_cast(bf16x8, make_uint4(ah[0], ah[1], ah[2], ah[3]));
+      A_lo = __builtin_bit_cast(bf16x8, make_uint4(al[0], al[1], al[2], al[3]));
+      return;
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       ah[e] = __builtin_amdgcn_perm(ent[2 * e + 1], ent[2 * e], 0x05040100u);
@@ -591,17 +901,17 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   }
 }
 
-template <int NK, bool PAD, bool IDX>
+template <int NK, bool PAD, bool IDX, bool FK>
 hipError_t launch_nk(const MfmaKArgs& ka, dim3 grid, dim3 block, hipStream_t s) {
-  hipLaunchKernelGGL((topn_mfma_kernel<NK, PAD, IDX>), grid, block, 0, s, ka);
+  hipLaunchKernelGGL((topn_mfma_kernel<NK, PAD, IDX, FK>), grid, block, 0, s, ka);
   return hipGetLastError();
 }
 
-template <int NK>
+template <int NK, bool FK>
 hipError_t launch_pad(const MfmaKArgs& ka, bool pad, dim3 grid, dim3 block, hipStream_t s) {
   if (ka.idx != nullptr)
-    return pad ? launch_nk<NK, true, true>(ka, grid, block, s) : launch_nk<NK, false, true>(ka, grid, block, s);
-  return pad ? launch_nk<NK, true, false>(ka, grid, block, s) : launch_nk<NK, false, false>(ka, grid, block, s);
+    return pad ? launch_nk<NK, true, true, FK>(ka, grid, block, s) : launch_nk<NK, false, true, FK>(ka, grid, block, s);
+  return pad ? launch_nk<NK, true, false, FK>(ka, grid, block, s) : launch_nk<NK, false, false, FK>(ka, grid, block, s);
 }
 
 // Smallest t with P(Binomial(d, 1/2) <= t) >= keep / n: the expected threshold
@@ -620,8 +930,10 @@ int threshold_guess(int64_t d, int64_t keep, int64_t n) {
 }  // namespace
 
 bool topn_mfma_supported(const AttnParams& p) {
-  return p.d == kD && p.v_kind == 1 && p.alpha_q == nullptr && p.alpha_k == nullptr && p.bias == nullptr &&
-         p.brow == nullptr && p.n >= 1 && p.n <= 1024;
+  const bool base = p.d == kD && p.v_kind == 1 && p.alpha_q == nullptr && p.alpha_k == nullptr &&
+                    p.brow == nullptr && p.n >= 1;
+  if (p.bias == nullptr) return base && p.n <= 1024;
+  return base && p.n <= 256;  // float keys: the heads whose table passes the level test
 }
 
 hipError_t launch_topn_mfma(const AttnParams& p, hipStream_t s) {
@@ -639,18 +951,28 @@ hipError_t launch_topn_mfma(const AttnParams& p, hipStream_t s) {
   ka.tiles = (int)((p.n + 15) / 16);
   ka.t0 = std::max(1, threshold_guess(p.d, p.keep, p.n));
   ka.exp_c = (float)(2.0 / sqrt((double)p.d) * 1.4426950408889634);
+  ka.bias = p.bias;
+  ka.H = (int)p.H;
+  ka.isd = (float)(1.0 / sqrt((double)p.d));
   const int64_t BH = p.B * p.H;
   ka.split = (ka.tiles + kWaves - 1) / kWaves;
   if (BH * ka.split >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(BH * ka.split));
   const dim3 block((unsigned)(64 * kWaves));
   const bool pad = p.n != 32 * NK;
+  if (p.bias != nullptr) {
+    switch (NK) {
+      case 2: return launch_pad<2, true>(ka, pad, grid, block, s);
+      case 4: return launch_pad<4, true>(ka, pad, grid, block, s);
+      default: return launch_pad<8, true>(ka, pad, grid, block, s);
+    }
+  }
   switch (NK) {
-    case 2: return launch_pad<2>(ka, pad, grid, block, s);
-    case 4: return launch_pad<4>(ka, pad, grid, block, s);
-    case 8: return launch_pad<8>(ka, pad, grid, block, s);
-    case 16: return launch_pad<16>(ka, pad, grid, block, s);
-    default: return launch_pad<32>(ka, pad, grid, block, s);
+    case 2: return launch_pad<2, false>(ka, pad, grid, block, s);
+    case 4: return launch_pad<4, false>(ka, pad, grid, block, s);
+    case 8: return launch_pad<8, false>(ka, pad, grid, block, s);
+    case 16: return launch_pad<16, false>(ka, pad, grid, block, s);
+    default: return launch_pad<32, false>(ka, pad, grid, block, s);
   }
 }
 
