@@ -563,20 +563,19 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
         return __fadd_rn(__fmul_rn((float)(kD - 2 * (int)h), a.isd), ttab[obase + p]);
       };
       constexpr int kCache = 12;
-      float bl[kCache];
-#pragma unroll
-      for (int k = 0; k < kCache; ++k) bl[k] = -INFINITY;
+      float bl[kCache];  // searched values of the first candidates (-inf: none)
+      int bp[kCache];    // their positions p
       bool over = false;
       if (!slow) {
         uint64_t rest = cm;
 #pragma unroll
         for (int k = 0; k < kCache; ++k) {
-          if (__builtin_amdgcn_ballot_w64(rest != 0) == 0) break;
-          if (rest != 0) {
-            const float x = logit_tau(__builtin_ctzll(rest));
-            bl[k] = low ? -x : x;
-            rest &= rest - 1;
-          }
+          const bool has = rest != 0;
+          const int p = has ? (int)__builtin_ctzll(rest) : 0;
+          const float x = logit_tau(p);  // (position 0 is a valid key when there is none)
+          bl[k] = has ? (low ? -x : x) : -INFINITY;
+          bp[k] = p;
+          rest &= rest - 1;
         }
         over = rest != 0;
       }
@@ -640,8 +639,10 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
       const int cnt_ge = quad_rows_sum(cge);
       const int gt = low ? M - cnt_ge : above;
       const int takeq = rr - gt;  // candidates equal to the threshold that are kept, lowest j first
+      // this lane's candidates equal to the threshold (per-lane branches; the prefix over
+      // the row's lanes runs where every lane takes part)
+      float mx = -INFINITY;
       if (slow) {
-        float mx = -INFINITY;
 #pragma unroll
         for (int b = 0; b < NW; ++b)
 #pragma unroll
@@ -653,8 +654,27 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
               eq += (low ? -x : x) == L ? 1 : 0;
             }
           }
-        lmax = quad_rows_max(mx);
-        int seen = quad_rows_excl(eq, g);
+      } else if (!over) {
+#pragma unroll
+        for (int k = 0; k < kCache; ++k) eq += bl[k] == L ? 1 : 0;
+      } else {
+        for (uint64_t q = cm; q != 0; q &= q - 1) {
+          const float x = logit_tau(__builtin_ctzll(q));
+          eq += (low ? -x : x) == L ? 1 : 0;
+        }
+      }
+      lmax = quad_rows_max(mx);
+      int seen = quad_rows_excl(eq, g);
+      // kept: above the threshold, or equal to it and among the first takeq in key order
+      auto decide = [&](float y) {
+        bool kept = low ? y < L : y > L;
+        if (y == L) {
+          kept = seen < takeq;
+          ++seen;
+        }
+        return kept;
+      };
+      if (slow) {
 #pragma unroll
         for (int b = 0; b < NW; ++b)
 #pragma unroll
@@ -662,41 +682,34 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
             const int p = 4 * b + k;
             if (p < nreal) {
               const float x = logit_of((P[b] >> (8 * k)) & 0xffu, p);
-              const float y = low ? -x : x;
-              bool kept = low ? y < L : y > L;
-              if (y == L) {
-                kept = seen < takeq;
-                ++seen;
-              }
-              if (kept) {
+              if (decide(low ? -x : x)) {
                 keepm |= 1ull << p;
                 ++kt_lane;
               }
             }
           }
-      } else {
-        for (uint64_t q = cm; q != 0; q &= q - 1) {
-          const float x = logit_tau(__builtin_ctzll(q));
-          eq += (low ? -x : x) == L ? 1 : 0;
+      } else if (!over) {
+#pragma unroll
+        for (int k = 0; k < kCache; ++k) {
+          const float y = bl[k];
+          if (y != -INFINITY) {
+            const bool kept = decide(y);
+            kt_lane += kept ? 1 : 0;
+            nkb |= kept ? 0ull : (1ull << bp[k]);
+          }
         }
-        int seen = quad_rows_excl(eq, g);
+      } else {
         for (uint64_t q = cm; q != 0; q &= q - 1) {
           const int p = __builtin_ctzll(q);
           const float x = logit_tau(p);
-          const float y = low ? -x : x;
-          bool kept = low ? y < L : y > L;
-          if (y == L) {
-            kept = seen < takeq;
-            ++seen;
-          }
-          if (kept) {
+          if (decide(low ? -x : x)) {
             ++kt_lane;
           } else {
             nkb |= 1ull << p;
           }
         }
-        kt_lane += cl_lo;  // every key below tau
       }
+      if (!slow) kt_lane += cl_lo;  // every key below tau
     }
   }
   // ---- the rows of round 0 (and 1) are in place
