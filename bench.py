@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 METRIC = "binarized-attention QK pairs/sec at n=1024,12 heads; % of roofline"
 VALU_PEAK = 256 * 64 * 2.4e9  # lane-slots per second: 256 CUs x 64 lanes x 2.4 GHz
 HBM_PEAK = 8.0e12
+STREAM_MAX_KEEP = 704  # most keys the streaming top-N kernel buffers per query (768 entries less one tile)
 
 
 def log(*a):
@@ -79,20 +80,26 @@ def algorithmic_bytes(w) -> float:
     return b * bh
 
 
-def attention_kernel(w):
+def attention_kernel(w, fused=False):
     """(kernel name, source file) of the attention launch, by the library's dispatch rule:
     dense softmax -> dense_q8 up to 256 tokens, dense_long beyond; n above the resident limit (512 keys for fp32 V, 1024
-    otherwise, half that at head_dim 128) -> the streaming kernel; head_dim 64 with bf16
-    V, integer logits (plain sign, no bias) and fp32 A*V -> the matrix-core kernel;
-    anything else -> the resident kernel."""
+    otherwise, half that at head_dim 128) -> the streaming kernel, past its buffer -> the
+    threshold-first kernel; head_dim 64 with bf16 V, plain sign codes, fp32 A*V and no
+    table (up to 1024 tokens) or a 1-D table (up to 256) -> the matrix-core kernel; anything
+    else, and the fused top-N launch -> the resident kernel."""
+    if fused and w.top_n is not None:
+        return "topn_resident_kernel", "topn.hip"
     if w.top_n is None:
         return ("dense_q8_kernel", "dense_q8.hip") if w.n <= 256 else ("dense_long_kernel", "dense_long.hip")
     resident_max = 512 if (w.dtype == "f32" and w.av_mode == 0) else 1024
     if w.d == 128:
         resident_max //= 2  # rows twice as long in LDS
     if w.n > resident_max:
+        if w.top_n > STREAM_MAX_KEEP:
+            return "topn_wide_kernel", "topn_wide.hip"
         return "topn_stream_kernel", "topn_stream.hip"
-    if w.d == 64 and w.dtype == "bf16" and w.mode == 0 and not w.bias and w.av_mode == 0:
+    table_ok = not w.bias or (w.grid is None and w.n <= 256)
+    if w.d == 64 and w.dtype == "bf16" and w.mode == 0 and table_ok and w.av_mode == 0:
         return "topn_mfma_kernel", "topn_mfma.hip"
     return "topn_resident_kernel", "topn.hip"
 
@@ -259,8 +266,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused", action="store_true",
-                    help="dense workloads with n <= 256: a step is one binattn_dense_q8_fused launch (binarize, "
-                         "quantize and attend on chip) instead of had_pack_qk + binattn_dense_q8")
+                    help="a step is one launch that binarizes Q and K on chip: binattn_dense_q8_fused for dense "
+                         "workloads with n <= 256 (in place of had_pack_qk + binattn_dense_q8), "
+                         "had_attention_topn_fused for top-N workloads with fp32 A*V that one workgroup holds "
+                         "(in place of had_pack_qk + had_attention_topn)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the reference kernel that scales "
                          "the HBM byte counters) and exit")
@@ -286,8 +295,13 @@ def main():
     from binarized_qk_sparse_amd import ops, synth
 
     w = synth.workload(args.config)
-    if args.fused and (w.top_n is not None or w.n > 256):
+    if args.fused and w.top_n is None and w.n > 256:
         print("--fused takes dense workloads with n <= 256 (c4)", file=sys.stderr)
+        sys.exit(2)
+    fused_cap = (512 if w.dtype == "f32" else 1024) // (w.d // 64)
+    if args.fused and w.top_n is not None and (w.av_mode != 0 or w.n > fused_cap or (w.mode == 1 and w.n > 256)):
+        print("--fused takes top-N workloads with fp32 A*V and n up to what one workgroup holds (c1, c2)",
+              file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -324,7 +338,11 @@ def main():
 
     def attend():
         s = torch.cuda.current_stream().cuda_stream
-        if args.fused:
+        if args.fused and w.top_n is not None:
+            st = lib.had_attention_topn_fused(q.data_ptr(), k.data_ptr(), dt, w.mode, pb, v.data_ptr(),
+                                              ops._dtype_code(v), w.B, w.H, w.n, w.d, w.top_n, out.data_ptr(), None,
+                                              s)
+        elif args.fused:
             st = lib.binattn_dense_q8_fused(q.data_ptr(), k.data_ptr(), dt, w.mode, pb, v.data_ptr(),
                                             ops._dtype_code(v), w.B, w.H, w.n, w.d, out.data_ptr(), s)
         elif w.top_n is None and b2 is not None:
@@ -428,7 +446,7 @@ def main():
 
     slots = algorithmic_slots(w)
     achieved = slots / t_att
-    kname, ksrc = attention_kernel(w)
+    kname, ksrc = attention_kernel(w, args.fused)
     src = os.path.join(ROOT, "binarized_qk_sparse_amd", "csrc", ksrc)
     traffic = traffic_from_profile(args.config, kname, src)
     roof = {
@@ -479,7 +497,8 @@ def main():
             "head_dim": w.d,
             "top_n": w.top_n,
             "parallelism": "single GPU",
-            "entry_points": "binattn_dense_q8_fused" if args.fused else
+            "entry_points": ("binattn_dense_q8_fused" if w.top_n is None else "had_attention_topn_fused")
+                            if args.fused else
                             ("had_pack_qk + " + ("binattn_dense_q8" if w.top_n is None else "had_attention_topn")),
         },
         "roofline": roof,

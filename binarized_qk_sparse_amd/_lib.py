@@ -42,6 +42,7 @@ EXPORTS = (
     "had_attention_topn_2d",
     "binattn_dense_q8_2d",
     "binattn_dense_q8_noalloc",
+    "had_attention_topn_fused",
 )
 
 _lib = None
@@ -86,6 +87,8 @@ def load() -> ctypes.CDLL:
     lib.binattn_dense_q8_2d.restype = I
     lib.binattn_dense_q8_noalloc.argtypes = [P, P, P, P, P, P, I, I64, I64, I64, I64, P, P]
     lib.binattn_dense_q8_noalloc.restype = I
+    lib.had_attention_topn_fused.argtypes = [P, P, I, I, P, P, I, I64, I64, I64, I64, I64, P, P, P]
+    lib.had_attention_topn_fused.restype = I
     if lib.had_abi_version() != HAD_ABI_VERSION:
         raise ImportError("libhad.so ABI version mismatch")
     _lib = lib

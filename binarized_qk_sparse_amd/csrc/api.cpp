@@ -107,14 +107,18 @@ void set_bias2d(AttnParams* p, const Bias2dArgs& b) {
   p->cls = b.cls != nullptr ? 1 : 0;
 }
 
+int64_t topn_max_n(int v_kind, int64_t d) { return topn_resident_max_n(v_kind, d); }
+
+}  // namespace
+
+namespace had {
 // Largest n the resident top-N kernels handle (V of one head staged in LDS; at
 // head_dim 128 the rows are twice as long).
-int64_t topn_max_n(int v_kind, int64_t d) {
+int64_t topn_resident_max_n(int v_kind, int64_t d) {
   const int64_t base = v_kind == 0 ? 512 : 1024;
   return d == 128 ? base / 2 : base;
 }
-
-}  // namespace
+}  // namespace had
 
 extern "C" {
 
@@ -391,6 +395,38 @@ int binattn_dense_q8_2d(const uint32_t* qbits, const uint32_t* kbits, const floa
   if (row_table == nullptr || col_table == nullptr) return fail(HAD_ERR_INVALID_ARG, fn, "NULL bias table");
   return dense_impl(qbits, kbits, alpha_q, alpha_k, nullptr, Bias2dArgs{row_table, col_table, cls_table, grid_h, grid_w},
                     v, v_dtype, B, H, n, d, out, workspace, workspace_bytes, stream, fn);
+}
+
+int had_attention_topn_fused(const void* q, const void* k, int qk_dtype, int mode, const float* bias_table,
+                             const void* v, int v_dtype, int64_t B, int64_t H, int64_t n, int64_t d, int64_t top_n,
+                             float* out, int32_t* idx_out, void* stream) {
+  static const char* fn = "had_attention_topn_fused";
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return fail(HAD_ERR_INVALID_ARG, fn, "NULL tensor");
+  if (!sizes_ok(B, H, n, d)) return fail(HAD_ERR_INVALID_ARG, fn, "sizes must be positive and B*H*n*d < 2^31");
+  if (qk_dtype != HAD_F32 && qk_dtype != HAD_BF16) return fail(HAD_ERR_INVALID_ARG, fn, "unknown qk_dtype");
+  if (v_dtype != HAD_F32 && v_dtype != HAD_BF16) return fail(HAD_ERR_INVALID_ARG, fn, "unknown v_dtype");
+  if (mode != HAD_SIGN && mode != HAD_MEAN_SIGN) return fail(HAD_ERR_INVALID_ARG, fn, "unknown mode");
+  if (top_n < 1) return fail(HAD_ERR_INVALID_ARG, fn, "top_n must be >= 1");
+  if (d != 64 && d != 128) return fail(HAD_ERR_UNSUPPORTED, fn, "d must be 64 or 128");
+  const int v_kind = v_dtype == HAD_BF16 ? 1 : 0;
+  if (n > topn_max_n(v_kind, d)) return fail(HAD_ERR_UNSUPPORTED, fn, "n above what one workgroup holds on chip");
+  if (mode == HAD_MEAN_SIGN && n > 256) return fail(HAD_ERR_UNSUPPORTED, fn, "mean-centred codes: n above 256");
+  AttnParams p{};
+  p.xq = q;
+  p.xk = k;
+  p.qk_bf16 = qk_dtype == HAD_BF16;
+  p.mean = mode == HAD_MEAN_SIGN;
+  p.bias = bias_table;
+  p.v = v;
+  p.v_kind = v_kind;
+  p.B = B;
+  p.H = H;
+  p.n = n;
+  p.d = d;
+  p.keep = top_n < n ? top_n : n;
+  p.out = out;
+  p.idx = idx_out;
+  return launch_status(launch_topn(p, static_cast<hipStream_t>(stream)), fn);
 }
 
 int binattn_dense_q8_fused(const void* q, const void* k, int qk_dtype, int mode, const float* bias_table,

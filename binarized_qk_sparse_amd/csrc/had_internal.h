@@ -60,6 +60,11 @@ struct AttnParams {
   const float* bcol;
   const float* bcls;
   int gh, gw, cls;
+  // fused top-N (resident kernel): raw Q and K (fp32 or bf16) binarized on chip in
+  // place of qbits/kbits/alpha (xk == NULL: not fused)
+  const void* xq;
+  const void* xk;
+  int qk_bf16, mean;
 };
 // floats of the staged two-dimensional bias tables (rows and columns with the
 // class token's values folded in; see had_device.hpp)
@@ -67,6 +72,8 @@ __host__ __device__ inline int64_t bias2d_floats(int64_t gh, int64_t gw, int64_t
   return cls ? (5 * gh - 1) + (5 * gw - 1) : (2 * gh - 1) + (2 * gw - 1);
 }
 hipError_t launch_topn(const AttnParams& p, hipStream_t s);
+// largest n the resident top-N kernel takes for V of kind v_kind (0 f32, 1 bf16, 2 int8)
+int64_t topn_resident_max_n(int v_kind, int64_t d);
 bool topn_mfma_supported(const AttnParams& p);
 hipError_t launch_topn_mfma(const AttnParams& p, hipStream_t s);
 hipError_t launch_topn_stream(const AttnParams& p, hipStream_t s);

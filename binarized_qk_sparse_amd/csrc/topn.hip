@@ -36,6 +36,8 @@
 #include <float.h>
 #include <limits.h>
 
+#include <algorithm>
+
 #include "had_device.hpp"
 #include "had_internal.h"
 #include "../../include/had.h"
@@ -59,6 +61,12 @@ struct TopnKArgs {
   float* out;
   int32_t* idx;
   int H, n, keep, lcap, qt, tiles, units, upw;
+  // fused entry point: raw Q and K (fp32 or bf16) instead of qbits/kbits/alpha; the
+  // head's key codes and scales, the means and the tile's query codes go to LDS at fused_off
+  const void* xq;
+  const void* xk;
+  int qk_bf16, mean;
+  uint32_t fused_off;
   float isd;    // float(1/sqrt(d))
   float exp_c;  // 2*isd*log2(e): integer-key exponent per Hamming step
   uint32_t list_off, cand_off, bias_off, red_off, keys_off, trash_off;
@@ -161,11 +169,47 @@ HAD_DEVICE void for_each16(const uint8_t* __restrict__ src, uint32_t total, F f)
   }
 }
 
-// B2 (float keys only): the two-dimensional bias, a separate instance so that the
-// 1-D path carries none of its code
-template <int NS, bool FK, int VK, bool PAD, int D, bool B2 = false>
+// One 32-channel word of a token's code and the float64 sum of |y| over those
+// channels, y = x (plain sign) or fl(x - mu) (mean-centred), summed in channel
+// order: the arithmetic of had_pack, so both give the same bits.
+HAD_DEVICE uint32_t code_word(const void* x, bool bf16, size_t row, int D, int part, const float* mu, double* asum) {
+  double s = 0.0;
+  uint32_t w = 0;
+#pragma unroll 2
+  for (int k = 0; k < 4; ++k) {
+    float v[8];
+    const size_t e = row * D + 32 * part + 8 * k;
+    if (bf16) {
+      const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + e);
+      v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+      v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+    } else {
+      const float4 q0 = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + e);
+      const float4 q1 = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + e + 4);
+      v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w;
+      v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
+    }
+    if (mu != nullptr) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v[c] = __fsub_rn(v[c], mu[32 * part + 8 * k + c]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) s += fabs((double)v[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) w |= (uint32_t)(v[c] < 0.0f) << (8 * k + c);
+  }
+  *asum = s;
+  return w;
+}
+
+// EXT: 0 plain; 1 (float keys only) the two-dimensional bias, a separate instance so
+// that the 1-D path carries none of its code; 2 the fused entry point (raw Q and K
+// binarized on chip, fp32 or bf16 V)
+template <int NS, bool FK, int VK, bool PAD, int D, int EXT = 0>
 __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) {
   static_assert(D == 64 || (D == 128 && FK), "head_dim 128 takes the float-key path");
+  constexpr bool B2 = EXT == 1;
+  constexpr bool fused = EXT == 2;
   constexpr int W = D / 32;
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int ROWB = row_bytes<VK, D>();
@@ -182,6 +226,13 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
   uint32_t* trash = reinterpret_cast<uint32_t*>(smem + a.trash_off) + wave * 64;
   float* biasw = reinterpret_cast<float*>(smem + a.bias_off);
   uint32_t* red = reinterpret_cast<uint32_t*>(smem + a.red_off);
+  // fused: the head's key code words [n][W] and key scales [n], the means of Q and K
+  // [2][D], and the unit's query code words [64][W] and query scales [64]
+  uint32_t* fcode = reinterpret_cast<uint32_t*>(smem + a.fused_off);
+  float* falpha = reinterpret_cast<float*>(fcode + (size_t)n * W);
+  float* fmu = falpha + n;
+  uint32_t* fqcode = reinterpret_cast<uint32_t*>(fmu + 2 * D);
+  float* fqalpha = reinterpret_cast<float*>(fqcode + 64 * W);
   uint32_t kw[W][NS];  // key code words: word w of slot s
   float akv[NS];
   int staged = -1;
@@ -194,19 +245,96 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
     const int nbh = u0 / a.tiles, ni0 = (u0 % a.tiles) * a.qt;
     const bool ok = u0 < u1 && ni0 + lane < n;
     const size_t nrow = (size_t)nbh * n + ni0 + lane;
-    qnext = load_code<D>(a.qbits, ok ? nrow : 0);
-    aqnext = (FK && a.aq != nullptr && ok) ? a.aq[nrow] : 1.0f;
+    if (!fused) {
+      qnext = load_code<D>(a.qbits, ok ? nrow : 0);
+      aqnext = (FK && a.aq != nullptr && ok) ? a.aq[nrow] : 1.0f;
+    }
   }
 
   for (int u = u0; u < u1; ++u) {
     const int bh = u / a.tiles, tile = u % a.tiles, hh = bh % a.H;
     const int i0 = tile * a.qt, i1 = min(n, i0 + a.qt);
     const bool restage = bh != staged;                       // uniform over the workgroup
-    const bool sync = restage || (FK && a.bias != nullptr);  // LDS contents change this unit
+    const bool sync = restage || fused || (FK && a.bias != nullptr);  // LDS contents change this unit
     constexpr bool b2 = FK && B2;
     if (sync) __syncthreads();  // every wave is done with the previous unit's LDS data
     if (restage) {
       staged = bh;
+      if constexpr (fused) {
+        // ---- binarize this head's queries and keys (mean-centred: after the means of Q
+        // and K) with had_pack's arithmetic and summation order
+        const bool qb = a.qk_bf16 != 0;
+        const int t = (int)threadIdx.x;
+        if (a.mean) {
+          // column sums in float64: thread tt < 256 of set x takes channels 8 cg .. 8 cg + 7
+          // of rows r + RPP k (n <= 256: one chunk); the V area holds the RPP x D partials
+          // of each set; with 512 threads or more Q and K are summed together
+          constexpr int RPP = 256 / (D / 8);
+          const int nset = min(2, (int)blockDim.x / 256);
+          for (int x0 = 0; x0 < 2; x0 += nset) {
+            const int x = x0 + t / 256, tt = t % 256, r = tt / (D / 8), cg = tt % (D / 8);
+            double* part = reinterpret_cast<double*>(smem) + (x - x0) * RPP * D;
+            if (x < x0 + nset) {
+              const void* src = x == 0 ? a.xq : a.xk;
+              double cs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 1
+              for (int k = 0; k < 256 / RPP; ++k) {
+                const int row = r + RPP * k;
+                if (row < n) {
+                  float v[8];
+                  const size_t e = ((size_t)bh * n + row) * D + 8 * cg;
+                  if (qb) {
+                    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + e);
+                    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+                    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+                  } else {
+                    const float* pf = static_cast<const float*>(src) + e;
+                    const float4 w0 = *reinterpret_cast<const float4*>(pf);
+                    const float4 w1 = *reinterpret_cast<const float4*>(pf + 4);
+                    v[0] = w0.x; v[1] = w0.y; v[2] = w0.z; v[3] = w0.w;
+                    v[4] = w1.x; v[5] = w1.y; v[6] = w1.z; v[7] = w1.w;
+                  }
+#pragma unroll
+                  for (int c = 0; c < 8; ++c) cs[c] += (double)v[c];
+                }
+              }
+#pragma unroll
+              for (int c = 0; c < 8; ++c) part[r * D + 8 * cg + c] = cs[c];
+            }
+            __syncthreads();
+            if (t < nset * D) {
+              const int xx = x0 + t / D, c = t % D;
+              const double* pp = reinterpret_cast<const double*>(smem) + (xx - x0) * RPP * D;
+              double acc = 0.0;
+              for (int rp = 0; rp < RPP; ++rp) acc += pp[rp * D + c];
+              fmu[xx * D + c] = (float)((0.0 + acc) / (double)n);
+            }
+            __syncthreads();
+          }
+        }
+        // key codes, then this unit's query codes, in one pass: W consecutive lanes per
+        // row (one word each), as had_pack's rows kernel; dead lanes read a valid row
+        const int nk = n * W, nall = nk + a.qt * W;
+        for (int it0 = 0; it0 < nall; it0 += (int)blockDim.x) {
+          const int it = it0 + t;
+          const bool key = it < nk;
+          const int j = key ? it / W : min(i0 + (min(it, nall - 1) - nk) / W, n - 1);
+          double sm;
+          const uint32_t w = code_word(key ? a.xk : a.xq, qb, (size_t)bh * n + j, D, t % W,
+                                       a.mean ? fmu + (key ? D : 0) : nullptr, &sm);
+#pragma unroll
+          for (int off = 1; off < W; off <<= 1) sm += __shfl_xor(sm, off, 64);
+          const float al = a.mean ? (float)(sm / (double)D) : 1.0f;
+          if (key) {
+            fcode[it] = w;
+            if (t % W == 0) falpha[j] = al;
+          } else if (it < nall) {
+            fqcode[it - nk] = w;
+            if (t % W == 0) fqalpha[(it - nk) / W] = al;
+          }
+        }
+        __syncthreads();  // (the V area's partials are dead; the codes are in place)
+      }
       // ---- this head's V rows into LDS (16 bytes per thread and step)
       const uint8_t* src = static_cast<const uint8_t*>(a.v) + (size_t)bh * n * ROWB;
       const uint32_t total = (uint32_t)n * ROWB;
@@ -246,10 +374,19 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
       for (int s = 0; s < NS; ++s) {
         const int j = FK ? 64 * s + lane : NS * lane + s;
         const bool ok = !PAD || j < n;
-        const Code<D> kk = load_code<D>(a.kbits, (size_t)bh * n + (ok ? j : 0));
+        Code<D> kk;
+        if constexpr (fused) {
+#pragma unroll
+          for (int w = 0; w < W; ++w) kk.w[w] = fcode[(size_t)(ok ? j : 0) * W + w];
+        } else {
+          kk = load_code<D>(a.kbits, (size_t)bh * n + (ok ? j : 0));
+        }
 #pragma unroll
         for (int w = 0; w < W; ++w) kw[w][s] = ok ? kk.w[w] : 0u;
-        akv[s] = (FK && ok && a.ak != nullptr) ? a.ak[(size_t)bh * n + j] : 1.0f;
+        if (fused)
+          akv[s] = (FK && ok) ? falpha[j] : 1.0f;
+        else
+          akv[s] = (FK && ok && a.ak != nullptr) ? a.ak[(size_t)bh * n + j] : 1.0f;
       }
     }
     // ---- two-dimensional bias: this head's tables, then the key position codes
@@ -273,9 +410,23 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
     }
     // ---- the tile's query codes (and scales), one query per lane, read back with
     // v_readlane; the next unit's are fetched now so their latency hides behind this unit
-    const Code<D> qlane = qnext;
-    const float aqlane = aqnext;
-    if (u + 1 < u1) {
+    if (fused && !restage) {
+      // this unit's query codes and scales (with the head's means): the first waves take
+      // W lanes per query row as for the keys
+      const int t = (int)threadIdx.x;
+      if (t < (a.qt * W + 63) / 64 * 64) {  // whole waves (the sums cross lanes)
+        const int r = t / W, i = min(i0 + r, n - 1);
+        double sm;
+        const uint32_t w = code_word(a.xq, a.qk_bf16 != 0, (size_t)bh * n + i, D, t % W, a.mean ? fmu : nullptr, &sm);
+#pragma unroll
+        for (int off = 1; off < W; off <<= 1) sm += __shfl_xor(sm, off, 64);
+        fqcode[t] = w;
+        if (t % W == 0) fqalpha[r] = a.mean ? (float)(sm / (double)D) : 1.0f;
+      }
+    }
+    Code<D> qlane = qnext;
+    float aqlane = aqnext;
+    if (!fused && u + 1 < u1) {
       const int nbh = (u + 1) / a.tiles, ni0 = ((u + 1) % a.tiles) * a.qt;
       const bool ok = ni0 + lane < n;
       const size_t nrow = (size_t)nbh * n + ni0 + lane;
@@ -283,6 +434,11 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
       aqnext = (FK && a.aq != nullptr && ok) ? a.aq[nrow] : 1.0f;
     }
     if (sync) __syncthreads();
+    if constexpr (fused) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) qlane.w[w] = fqcode[lane * W + w];
+      aqlane = fqalpha[lane];
+    }
 
   for (int i = i0 + wave; i < i1; i += nwaves) {
     const size_t row = (size_t)bh * n + i;
@@ -649,22 +805,25 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
   }
 }
 
-template <int NS, bool FK, int VK, bool PAD, int D, bool B2>
+template <int NS, bool FK, int VK, bool PAD, int D, int EXT>
 hipError_t launch_inst(const TopnKArgs& ka, dim3 grid, dim3 block, uint32_t lds, hipStream_t s) {
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&topn_resident_kernel<NS, FK, VK, PAD, D, B2>),
+      reinterpret_cast<const void*>(&topn_resident_kernel<NS, FK, VK, PAD, D, EXT>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((topn_resident_kernel<NS, FK, VK, PAD, D, B2>), grid, block, lds, s, ka);
+  hipLaunchKernelGGL((topn_resident_kernel<NS, FK, VK, PAD, D, EXT>), grid, block, lds, s, ka);
   return hipGetLastError();
 }
 
 template <int NS, bool FK, int VK, bool PAD, int D>
 hipError_t launch_one(const TopnKArgs& ka, dim3 grid, dim3 block, uint32_t lds, hipStream_t s) {
   if constexpr (FK) {
-    if (ka.brow != nullptr) return launch_inst<NS, FK, VK, PAD, D, true>(ka, grid, block, lds, s);
+    if (ka.brow != nullptr) return launch_inst<NS, FK, VK, PAD, D, 1>(ka, grid, block, lds, s);
   }
-  return launch_inst<NS, FK, VK, PAD, D, false>(ka, grid, block, lds, s);
+  if constexpr (VK != 2) {
+    if (ka.xk != nullptr) return launch_inst<NS, FK, VK, PAD, D, 2>(ka, grid, block, lds, s);
+  }
+  return launch_inst<NS, FK, VK, PAD, D, 0>(ka, grid, block, lds, s);
 }
 
 template <int NS, bool FK, int VK, int D>
@@ -714,7 +873,11 @@ hipError_t launch_topn(const AttnParams& p, hipStream_t s) {
   const int NS = resident_slots(p.n);
   if (NS == 0 || (p.d == 128 && NS > 8)) return hipErrorInvalidValue;
   // head_dim 128 always takes the float-key path (exact for integer keys as well)
-  const bool fk = p.alpha_q != nullptr || p.alpha_k != nullptr || p.bias != nullptr || p.brow != nullptr || p.d != 64;
+  const bool fused = p.xk != nullptr;
+  // fused mean-centred codes come with scales: the float-key path
+  const bool fk = p.alpha_q != nullptr || p.alpha_k != nullptr || p.bias != nullptr || p.brow != nullptr ||
+                  p.d != 64 || (fused && p.mean);
+  if (fused && p.mean && p.n > 256) return hipErrorInvalidValue;
   const int vk = p.v_kind;
   const int rowb = (int)p.d * (vk == 0 ? 4 : (vk == 1 ? 2 : 1));
   TopnKArgs ka{};
@@ -722,6 +885,10 @@ hipError_t launch_topn(const AttnParams& p, hipStream_t s) {
   ka.kbits = p.kbits;
   ka.aq = p.alpha_q;
   ka.ak = p.alpha_k;
+  ka.xq = p.xq;
+  ka.xk = p.xk;
+  ka.qk_bf16 = p.qk_bf16;
+  ka.mean = p.mean;
   ka.bias = p.bias;
   ka.brow = p.brow;
   ka.bcol = p.bcol;
@@ -737,16 +904,28 @@ hipError_t launch_topn(const AttnParams& p, hipStream_t s) {
   ka.n = (int)p.n;
   ka.keep = (int)p.keep;
   ka.lcap = (int)((p.keep + 31) / 32 * 32);
-  ka.qt = kQTile;
-  ka.tiles = (int)((p.n + kQTile - 1) / kQTile);
+  // query tiles of 64; when that leaves CUs idle (few heads), smaller tiles so that
+  // about one workgroup per CU runs (each restages its head, cheap at these sizes)
+  const int64_t bh_count = p.B * p.H;
+  int64_t qt = kQTile;
+  if (bh_count * ((p.n + kQTile - 1) / kQTile) < 256)
+    qt = std::max<int64_t>(1, std::min<int64_t>(kQTile, (bh_count * p.n + 255) / 256));
+  ka.qt = (int)qt;
+  ka.tiles = (int)((p.n + qt - 1) / qt);
   ka.isd = (float)(1.0 / sqrt((double)p.d));
   ka.exp_c = (float)(2.0 * (double)ka.isd * 1.4426950408889634);
-  const uint32_t vbytes = align16((uint32_t)p.n * rowb);
+  uint32_t vbytes = align16((uint32_t)p.n * rowb);
+  // fused: key code words and scales, the two means, and one tile's query code words and
+  // scales; the mean-centred column sums use the V area (two sets of 256 x 8 float64)
+  // before V is staged
+  const uint32_t fused_bytes =
+      fused ? align16((uint32_t)(p.n * (p.d / 32) * 4 + p.n * 4 + 2 * p.d * 4 + 64 * (p.d / 32) * 4 + 64 * 4)) : 0u;
+  if (fused && p.mean) vbytes = std::max<uint32_t>(vbytes, 2u * 2048u * 8u);
   uint32_t bias_bytes = fk ? align16((uint32_t)(p.n + kQTile - 1) * 4u) : 0u;
   if (p.brow != nullptr) bias_bytes = align16((uint32_t)(bias2d_floats(p.gh, p.gw, p.cls) + p.n) * 4u);
   // as many waves as LDS allows (lists and candidate buffers are per wave)
   const uint32_t per_wave = (uint32_t)ka.lcap * (fk ? 8u : 12u) + (fk ? 64u * 8u : 256u);
-  const uint32_t fixed = vbytes + bias_bytes + 4u * kMaxWaves;
+  const uint32_t fixed = vbytes + bias_bytes + 4u * kMaxWaves + fused_bytes;
   int nw = kMaxWaves;
   while (nw > 1 && fixed + per_wave * nw > kLdsBytes) --nw;
   if (fixed + per_wave * nw > kLdsBytes) return hipErrorInvalidValue;
@@ -756,7 +935,9 @@ hipError_t launch_topn(const AttnParams& p, hipStream_t s) {
   ka.red_off = ka.cand_off + (fk ? 64u * 8u * nw : 0u);
   ka.keys_off = ka.red_off + 4u * kMaxWaves;
   ka.trash_off = ka.keys_off + (fk ? 0u : (uint32_t)ka.lcap * 4u * nw);
-  const uint32_t lds = ka.trash_off + (fk ? 0u : 256u * nw);
+  ka.fused_off = ka.trash_off + (fk ? 0u : 256u * nw);
+  const uint32_t lds = ka.fused_off + fused_bytes;
+  if (fused && nw < 4) return hipErrorInvalidValue;  // (the column sums take 256 threads)
   // persistent workgroups: one per CU, each taking a contiguous run of units
   ka.units = (int)(p.B * p.H * ka.tiles);
   const int target = 256;

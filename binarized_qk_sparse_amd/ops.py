@@ -247,6 +247,32 @@ def binattn_dense_q8_noalloc(qbits: torch.Tensor, kbits: torch.Tensor, v: torch.
     return out
 
 
+def had_attention_topn_fused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, top_n: int, mode: int = HAD_SIGN, *,
+                             bias: Optional[torch.Tensor] = None, want_idx: bool = False,
+                             out: Optional[torch.Tensor] = None):
+    """Binarize Q and K on chip and run the top-N attention (fp32 A*V) in one launch, for
+    sequences one workgroup holds; returns out f32 [B,H,n,d] (and idx int32 [B,H,n,min(N,n)])."""
+    _dev(v, "v")
+    B, H, n, d = _check_input(v, "v", v.device)
+    _check_input(q, "q", v.device)
+    _check_input(k, "k", v.device)
+    if q.shape != k.shape or q.dtype != k.dtype or v.shape != q.shape:
+        raise ValueError("q, k and v must share a shape, and q and k a dtype")
+    if int(top_n) < 1:
+        raise ValueError("top_n must be at least 1")
+    _check(bias, "bias", v.device, (torch.float32,), (H, 2 * n - 1))
+    _check(out, "out", v.device, (torch.float32,), (B, H, n, d))
+    keep = min(int(top_n), n)
+    if out is None:
+        out = torch.empty((B, H, n, d), dtype=torch.float32, device=v.device)
+    idx = torch.empty((B, H, n, keep), dtype=torch.int32, device=v.device) if want_idx else None
+    st = _lib.load().had_attention_topn_fused(q.data_ptr(), k.data_ptr(), _dtype_code(q), int(mode), _ptr(bias),
+                                              v.data_ptr(), _dtype_code(v), B, H, n, d, int(top_n), out.data_ptr(),
+                                              _ptr(idx), _stream())
+    _lib.check("had_attention_topn_fused", st)
+    return (out, idx) if want_idx else out
+
+
 def binattn_dense_q8_fused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mode: int = HAD_MEAN_SIGN, *,
                            bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Binarize Q, K and quantize V on chip, then dense q8 attention, in one launch (n <= 256);

@@ -230,6 +230,36 @@ int binattn_dense_q8_2d(const uint32_t* qbits, const uint32_t* kbits, const floa
                         size_t workspace_bytes, void* stream);
 
 /*
+ * had_attention_topn_fused -- had_pack_qk followed by had_attention_topn (fp32
+ * A*V) in one launch, for sequences one workgroup holds on chip (Hamming
+ * Attention Distillation, abstract and summary "method": {-1,+1} keys and
+ * queries, top-N per query; BinaryAttention section 2.2 for the mean-centred
+ * codes and section 2.3 for the bias).  A workgroup binarizes the keys of its head
+ * (and, mean-centred, takes the means of Q and K) on chip and each query's code
+ * as it goes, with had_pack's arithmetic and summation order, then runs the
+ * top-N attention on them.
+ *
+ *  q, k        [B,H,n,d] of qk_dtype (HAD_F32 or HAD_BF16)
+ *  mode        HAD_SIGN or HAD_MEAN_SIGN (as had_pack)
+ *  bias_table  float32 [H,2n-1] or NULL (B = 0)
+ *  v           [B,H,n,d] of v_dtype (HAD_F32 or HAD_BF16)
+ *  top_n       N >= 1 (N >= n keeps every key)
+ *  out         out float32 [B,H,n,d]
+ *  idx_out     optional out int32 [B,H,n,min(N,n)], ascending key index
+ *
+ * The kept index sets are those of had_pack_qk + had_attention_topn on the same
+ * inputs; the outputs are the same bits where that pair runs the resident kernel
+ * (fp32 V, mean-centred codes or head_dim 128) and within the fp32 tolerance
+ * otherwise.  No workspace and no intermediate tensor.  n up to 512 (fp32 V) or
+ * 1024 (bf16 V), half that at d = 128, and at most 256 for HAD_MEAN_SIGN; d = 64
+ * or 128; else HAD_ERR_UNSUPPORTED.  Other errors as had_pack and
+ * had_attention_topn.
+ */
+int had_attention_topn_fused(const void* q, const void* k, int qk_dtype, int mode, const float* bias_table,
+                             const void* v, int v_dtype, int64_t B, int64_t H, int64_t n, int64_t d, int64_t top_n,
+                             float* out, int32_t* idx_out, void* stream);
+
+/*
  * binattn_dense_q8_fused -- binattn_dense_q8 with the binarization and the V
  * quantization in the same launch, for short sequences (BinaryAttention
  * section 2.2 codes and scales, section 2.3 logits, section 2.4 quantized A*V).

@@ -175,6 +175,30 @@ def test_dense_fused_validation(args, want):
 
 
 @pytest.mark.parametrize("args,want", [
+    (dict(q=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(k=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(out=None), _lib.HAD_ERR_INVALID_ARG),
+    (dict(H=0), _lib.HAD_ERR_INVALID_ARG),
+    (dict(qkdt=5), _lib.HAD_ERR_INVALID_ARG),
+    (dict(vdt=5), _lib.HAD_ERR_INVALID_ARG),
+    (dict(mode=7), _lib.HAD_ERR_INVALID_ARG),
+    (dict(top_n=0), _lib.HAD_ERR_INVALID_ARG),
+    (dict(d=96), _lib.HAD_ERR_UNSUPPORTED),
+    (dict(n=257), _lib.HAD_ERR_UNSUPPORTED),                            # mean-centred: n <= 256
+    (dict(mode=_lib.HAD_SIGN, vdt=_lib.HAD_F32, n=513), _lib.HAD_ERR_UNSUPPORTED),
+    (dict(mode=_lib.HAD_SIGN, n=1025), _lib.HAD_ERR_UNSUPPORTED),
+    (dict(mode=_lib.HAD_SIGN, d=128, n=513), _lib.HAD_ERR_UNSUPPORTED),
+])
+def test_topn_fused_validation(args, want):
+    a = dict(q=FAKE, k=FAKE, qkdt=_lib.HAD_F32, mode=_lib.HAD_MEAN_SIGN, v=FAKE, vdt=_lib.HAD_BF16, B=2, H=3, n=197,
+             d=64, top_n=30, out=FAKE)
+    a.update(args)
+    st = _lib.load().had_attention_topn_fused(a["q"], a["k"], a["qkdt"], a["mode"], None, a["v"], a["vdt"], a["B"],
+                                              a["H"], a["n"], a["d"], a["top_n"], a["out"], None, None)
+    assert st == want
+
+
+@pytest.mark.parametrize("args,want", [
     (dict(row=None), _lib.HAD_ERR_INVALID_ARG),
     (dict(col=None), _lib.HAD_ERR_INVALID_ARG),
     (dict(gh=0), _lib.HAD_ERR_INVALID_ARG),
