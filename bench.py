@@ -144,8 +144,63 @@ def cpu_model() -> str:
     return ""
 
 
-def cpu_baseline(w, g, budget_s: float):
-    """The oracle, as it stands, on a bounded sample of rows of the same workload."""
+def aq_flips(w, gpu_rows, ref):
+    """Count the u8 probabilities A_q where the GPU and the oracle differ, on the rows of one
+    oracle call (q8/q4 A*V).  The V codes and scales are exact on both sides, so each output
+    element O = fl(fl(acc) s_c) / 255 gives back the GPU's integer accumulator acc, and
+    acc_gpu - acc_oracle = sum_j dA_j V_q[j, c] over the kept keys; a row's difference is
+    matched against one key's V_q row (one flip) or two keys' (two flips), each of sign +-1.
+    Returns (flips, rows with a difference, rows not resolved by one or two flips)."""
+    import numpy as np
+
+    vq = ref["vq"].reshape(-1, w.n, w.d).astype(np.int64)  # [B*H, n, d]
+    sc = ref["vscale"].reshape(-1, w.d).astype(np.float32)  # [B*H, d]
+    flips = differ = unresolved = 0
+    for r, row in enumerate(ref["rows"]):
+        bh = int(row) // w.n
+        s = sc[bh]
+        o = gpu_rows[r].astype(np.float32)
+        a0 = np.rint(o.astype(np.float64) * 255.0 / np.where(s > 0, s, 1.0)).astype(np.int64)
+        acc = np.full(w.d, np.iinfo(np.int64).min, np.int64)
+        for dlt in (0, -1, 1, -2, 2):
+            cand = a0 + dlt
+            back = (cand.astype(np.float32) * s) / np.float32(255.0)
+            hit = (back == o) & (acc == np.iinfo(np.int64).min)
+            acc[hit] = cand[hit]
+        keys = ref["idx"][r].astype(np.int64)
+        want = (ref["aq8"][r].astype(np.int64)[:, None] * vq[bh, keys]).sum(axis=0)
+        if np.any(acc == np.iinfo(np.int64).min):
+            differ += 1
+            unresolved += 1
+            continue
+        delta = acc - want
+        if not delta.any():
+            continue
+        differ += 1
+        rowsv = vq[bh, keys]  # [keep, d]
+        one = np.nonzero(np.all(rowsv == delta, axis=1) | np.all(rowsv == -delta, axis=1))[0]
+        if one.size:
+            flips += 1
+            continue
+        found = False
+        for sgn in ((1, -1) if len(keys) <= 1024 else ()):  # the pair search holds keep^2 d booleans
+            rest = delta[None, :] - sgn * rowsv  # remove one key, look for a second
+            hit = np.all(rest[:, None, :] == rowsv[None, :, :], axis=2) | np.all(rest[:, None, :] == -rowsv[None, :, :],
+                                                                                     axis=2)
+            if hit.any():
+                found = True
+                break
+        if found:
+            flips += 2
+        else:
+            unresolved += 1
+    return flips, differ, unresolved
+
+
+def cpu_baseline(w, g, budget_s: float, gpu_out=None):
+    """The oracle, as it stands, on a bounded sample of rows of the same workload; on the
+    quantized A*V path also the count of A_q flips between the GPU's output and the oracle's
+    on the first sample of rows."""
     import numpy as np
 
     import oracle
@@ -167,13 +222,17 @@ def cpu_baseline(w, g, budget_s: float):
     rng = np.random.default_rng(12345)
     # doubling seeded samples of query rows until the budget is spent or the
     # sample covers as many rows as the workload holds
+    flip_ref = None
     while t_att < budget_s and rows_done < total:
         size = min(count, total - rows_done)
         rows = np.sort(rng.choice(total, size=size, replace=False)).astype(np.int64)
+        want = flip_ref is None and gpu_out is not None and w.av_mode != 0
         t1 = time.perf_counter()
-        oracle.attention(qb, kb, v, alpha_q=aq, alpha_k=ak, bias=bias, bias2d=b2, top_n=w.top_n, av_mode=w.av_mode,
-                         rows=rows)
+        ref = oracle.attention(qb, kb, v, alpha_q=aq, alpha_k=ak, bias=bias, bias2d=b2, top_n=w.top_n,
+                               av_mode=w.av_mode, rows=rows, want_idx=want, want_aq8=want)
         t_att += time.perf_counter() - t1
+        if want:
+            flip_ref = dict(ref, rows=rows)
         rows_done += len(rows)
         count *= 2
     per_row = t_att / rows_done + t_pack / total
@@ -188,6 +247,12 @@ def cpu_baseline(w, g, budget_s: float):
         "sample": f"{rows_done} query rows of {w.name} (random, seeded) in {t_att:.1f} s plus the full Q/K pack "
                   f"({t_pack:.2f} s) scaled per row",
     }
+    if flip_ref is not None:
+        gpu_rows = gpu_out.reshape(-1, w.d)[flip_ref["rows"]]
+        f, dif, unres = aq_flips(w, gpu_rows, flip_ref)
+        res["aq_flips"] = {"flips": f, "rows_checked": int(len(flip_ref["rows"])), "rows_differing": dif,
+                           "rows_unresolved": unres,
+                           "note": "u8 probabilities that differ between the GPU and the oracle (fp32 vs fp64 exp)"}
     if w.n <= 1024:
         # the same oracle on one thread, on a sample of at most 1024 rows (attention only)
         threads = oracle.threads()
@@ -470,7 +535,7 @@ def main():
     }
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, g, args.cpu_budget)
+        cpu = cpu_baseline(w, g, args.cpu_budget, gpu_out=out.cpu().numpy())
         log(f"cpu baseline: {cpu['value']:.3e} pairs/s on {cpu['cores']} threads ({cpu['sample']})")
     kept = "dense" if w.top_n is None else f"N={w.top_n}"
     line = {
