@@ -105,25 +105,43 @@ struct Seq<0> {
   HAD_DEVICE static void run(F&&) {}
 };
 
-// Sum over the four lanes of one query row (lanes r, r+16, r+32, r+48).
+// The four lanes of one query row (r, r + 16, r + 32, r + 48) exchange values with
+// the gfx950 permlane swaps, on the VALU: permlane16_swap of a value with itself
+// gives every lane its 16-lane row pair's values (even row, odd row), and
+// permlane32_swap its 32-lane half pair's (lower half, upper half).
+HAD_DEVICE void row_pair(uint32_t v, uint32_t& even, uint32_t& odd) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  even = r[0];
+  odd = r[1];
+}
+HAD_DEVICE void half_pair(uint32_t v, uint32_t& lower, uint32_t& upper) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  lower = r[0];
+  upper = r[1];
+}
+
+// Sum over the four lanes of one query row.
 HAD_DEVICE int quad_rows_sum(int v) {
-  v += __shfl_xor(v, 16, 64);
-  return v + __shfl_xor(v, 32, 64);
+  uint32_t e, o, l, u;
+  row_pair((uint32_t)v, e, o);
+  half_pair(e + o, l, u);
+  return (int)(l + u);
 }
 
 HAD_DEVICE float quad_rows_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  return fmaxf(v, __shfl_xor(v, 32, 64));
+  uint32_t e, o, l, u;
+  row_pair(__builtin_bit_cast(uint32_t, v), e, o);
+  const float m = fmaxf(__builtin_bit_cast(float, e), __builtin_bit_cast(float, o));
+  half_pair(__builtin_bit_cast(uint32_t, m), l, u);
+  return fmaxf(__builtin_bit_cast(float, l), __builtin_bit_cast(float, u));
 }
 
 // Exclusive prefix over the key quarters g = 0..3 of one query row.
 HAD_DEVICE int quad_rows_excl(int v, int g) {
-  const int lane = (int)lane_id();
-  int a = __shfl(v, (lane - 16) & 63, 64);
-  int s = v + (g >= 1 ? a : 0);
-  a = __shfl(s, (lane - 32) & 63, 64);
-  s += (g >= 2 ? a : 0);
-  return s - v;
+  uint32_t e, o, l, u;
+  row_pair((uint32_t)v, e, o);
+  half_pair(e + o, l, u);
+  return (int)(((g & 1) ? e : 0u) + ((g & 2) ? l : 0u));
 }
 
 // x (below 256) in every byte: one byte permute instead of a quarter-rate multiply
