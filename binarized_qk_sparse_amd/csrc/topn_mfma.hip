@@ -607,16 +607,22 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
           below = y < t ? fmaxf(below, y) : below;
         };
         if (slow) {
-#pragma unroll
-          for (int b = 0; b < NW; ++b)
+#pragma unroll 1
+          for (int b = 0; b < NW; ++b) {
+            // (a loop, recomputed on every pass: unrolled, or kept across the passes, the
+            // row's logits would take a register per key, and this rarely taken path for
+            // wide tables would set the register budget of every head)
+            uint32_t pw = P[b];
+            asm volatile("" : "+v"(pw));
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
               const int p = 4 * b + k;
               if (p < nreal) {
-                const float x = logit_of((P[b] >> (8 * k)) & 0xffu, p);
+                const float x = logit_of((pw >> (8 * k)) & 0xffu, p);
                 take(low ? -x : x);
               }
             }
+          }
         } else if (!over) {
 #pragma unroll
           for (int k = 0; k < kCache; ++k) take(bl[k]);  // (-inf fillers count nowhere)
@@ -661,7 +667,7 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
       // the row's lanes runs where every lane takes part)
       float mx = -INFINITY;
       if (slow) {
-#pragma unroll
+#pragma unroll 1
         for (int b = 0; b < NW; ++b)
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
@@ -693,7 +699,7 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
         return kept;
       };
       if (slow) {
-#pragma unroll
+#pragma unroll 1
         for (int b = 0; b < NW; ++b)
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
