@@ -144,6 +144,13 @@ HAD_DEVICE int quad_rows_excl(int v, int g) {
   return (int)(((g & 1) ? e : 0u) + ((g & 2) ? l : 0u));
 }
 
+// A sorting network on 12 inputs (39 comparators in 9 layers; every 0-1 input comes out
+// sorted, which the tests check): comparator (i, j), i < j, leaves the larger value at i.
+constexpr int kSort12[39][2] = {{0, 8}, {1, 7}, {2, 6}, {3, 11}, {4, 10}, {5, 9},  {0, 1}, {2, 5}, {3, 4}, {6, 9},
+                                {7, 8}, {10, 11}, {0, 2}, {1, 6}, {5, 10}, {9, 11}, {0, 3}, {1, 2}, {4, 6}, {5, 7},
+                                {8, 11}, {9, 10}, {1, 4}, {3, 5}, {6, 8}, {7, 10}, {1, 3}, {2, 5}, {6, 9}, {8, 10},
+                                {2, 3}, {4, 5}, {6, 7}, {8, 9}, {4, 6}, {5, 7}, {3, 4}, {5, 6}, {7, 8}};
+
 // x (below 256) in every byte: one byte permute instead of a quarter-rate multiply
 HAD_DEVICE uint32_t byte_bcast(uint32_t x) { return __builtin_amdgcn_perm(0u, x, 0u); }
 
@@ -584,8 +591,9 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
       float bl[kCache];  // searched values of the first candidates (-inf: none)
       int bp[kCache];    // their positions p
       bool over = false;
+      uint64_t rest = 0;  // candidates past the cached ones
       if (!slow) {
-        uint64_t rest = cm;
+        rest = cm;
 #pragma unroll
         for (int k = 0; k < kCache; ++k) {
           const bool has = rest != 0;
@@ -635,23 +643,91 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
       };
       int ge;
       float L;
-      scan(INFINITY, ge, L);
-      L = quad_rows_max(L);  // the top value
-      int above = 0;         // searched values strictly above L
+      int above = 0;  // searched values strictly above L
       bool done = false;
-      // every round moves an unfinished row one distinct value down (at most M of
-      // them); the bound only guards against values the table test let through
-      for (int it = 0; it <= 4 * KG && __builtin_amdgcn_ballot_w64(!done) != 0; ++it) {
-        float nb;
-        scan(L, ge, nb);
-        const int c = quad_rows_sum(ge);
-        nb = quad_rows_max(nb);
-        if (!done) {
-          if (c >= rs) {
-            done = true;
-          } else {
-            above = c;
-            L = nb;
+      bool queued = false;  // the walk below found L
+      if (!slow) {
+        // Walk sorted queues: each lane's twelve largest candidates in descending order.
+        // Each round pops the values at or above L from the queues' heads (a few selects
+        // each, instead of a pass over all cached values), counts them over the row, and
+        // takes the largest remaining head as the next L.  A lane with more candidates
+        // than the queue holds, whose queue runs empty before the row is done, makes
+        // the wave walk again with passes over every candidate (below).
+        float sq[kCache];
+#pragma unroll
+        for (int k = 0; k < kCache; ++k) sq[k] = bl[k];
+#pragma unroll
+        for (int c = 0; c < 39; ++c) {
+          const float hi = fmaxf(sq[kSort12[c][0]], sq[kSort12[c][1]]);
+          const float lo = fminf(sq[kSort12[c][0]], sq[kSort12[c][1]]);
+          sq[kSort12[c][0]] = hi;
+          sq[kSort12[c][1]] = lo;
+        }
+        if (over) {
+          // the rest of this lane's candidates, each inserted where it belongs (the
+          // smallest falls off the end)
+          for (uint64_t q = rest; q != 0; q &= q - 1) {
+            const float x = logit_tau(__builtin_ctzll(q));
+            const float y = low ? -x : x;
+#pragma unroll
+            for (int k = kCache - 1; k >= 1; --k) sq[k] = fmaxf(sq[k], fminf(sq[k - 1], y));
+            sq[0] = fmaxf(sq[0], y);
+          }
+        }
+        int popped = 0;  // this lane's values at or above L
+        bool short_queue = false;  // this lane's queue ran out before its candidates did
+        const int ncand = __builtin_popcountll(cm);
+        L = quad_rows_max(sq[0]);  // the top value
+        for (int it = 0; it <= 4 * KG && __builtin_amdgcn_ballot_w64(!done) != 0; ++it) {
+          // (-inf fillers are below every L; ties pop together, one per pass.  The shift
+          // is a bitwise select under an opaque mask: as a select between neighbouring
+          // elements it is turned into a dynamically indexed read of the queue, a chain
+          // of compares per element)
+          while (__builtin_amdgcn_ballot_w64(sq[0] >= L) != 0) {
+            const bool pop = sq[0] >= L;
+            uint32_t m = pop ? 0xffffffffu : 0u;
+            asm volatile("" : "+v"(m));
+#pragma unroll
+            for (int k = 0; k + 1 < kCache; ++k)
+              sq[k] = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, sq[k]) & ~m) |
+                                                    (__builtin_bit_cast(uint32_t, sq[k + 1]) & m));
+            sq[kCache - 1] = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, sq[kCache - 1]) & ~m) |
+                                                           (0xff800000u & m));
+            popped += pop ? 1 : 0;
+          }
+          const int c = quad_rows_sum(popped);
+          const float nb = quad_rows_max(sq[0]);  // every head is below L now
+          short_queue = short_queue || (!done && popped >= kCache && ncand > kCache);
+          if (!done) {
+            if (c >= rs) {
+              done = true;
+            } else {
+              above = c;
+              L = nb;
+            }
+          }
+        }
+        queued = __builtin_amdgcn_ballot_w64(short_queue) == 0;
+      }
+      if (!queued) {
+        above = 0;
+        done = false;
+        scan(INFINITY, ge, L);
+        L = quad_rows_max(L);  // the top value
+        // every round moves an unfinished row one distinct value down (at most M of
+        // them); the bound only guards against values the table test let through
+        for (int it = 0; it <= 4 * KG && __builtin_amdgcn_ballot_w64(!done) != 0; ++it) {
+          float nb;
+          scan(L, ge, nb);
+          const int c = quad_rows_sum(ge);
+          nb = quad_rows_max(nb);
+          if (!done) {
+            if (c >= rs) {
+              done = true;
+            } else {
+              above = c;
+              L = nb;
+            }
           }
         }
       }
