@@ -198,6 +198,45 @@ HAD_DEVICE int count_ge_rows(const float (&v)[R], float t) {
   return c;
 }
 
+// Sequences of at least this many keys start each row's stream from a threshold taken
+// from the logits of its first chunk.
+constexpr int kSampleMinN = 4096;
+
+// A threshold t from R values per lane such that about m of the wave's values are
+// >= t: an interpolation search between the extremes that stops once [m, m + m / 2 + 8]
+// values are >= t, else returns the highest t tried with at least m values >= t (the
+// minimum at worst).
+template <int R>
+HAD_DEVICE float sample_threshold(const float (&v)[R], int m) {
+  float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    lo = fminf(lo, v[r]);
+    hi = fmaxf(hi, v[r]);
+  }
+  lo = -wave_max_f32(-lo);  // count_ge(lo) = 64 R >= m
+  hi = wave_max_f32(hi);
+  int clo = 64 * R, chi = count_ge_rows(v, hi);
+  if (chi >= m) return hi;
+  const int top = m + m / 2 + 8;
+  for (int it = 0; it < 10; ++it) {
+    float f = (float)(clo - (m + top) / 2) / (float)(clo - chi);
+    f = fminf(fmaxf(f, 0.0625f), 0.9375f);
+    const float mid = lo + f * (hi - lo);
+    if (!(mid > lo && mid < hi)) break;
+    const int cm = count_ge_rows(v, mid);
+    if (cm < m) {
+      hi = mid;
+      chi = cm;
+    } else {
+      lo = mid;
+      clo = cm;
+      if (cm <= top) break;
+    }
+  }
+  return lo;
+}
+
 // Intermediate compaction, cheaper than the exact selection: finds a value t
 // with keep <= #{l >= t} <= keep + kSlack by interpolation search between theta
 // (every entry is above it) and the largest entry, keeps the entries with
@@ -384,13 +423,16 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
   // still frees room for two more groups
   const bool approx = keep + kSlack <= kCap - 128;
   fetch_chunk(0);
+  bool sampled = false;  // theta started from the first chunk's logits
+  bool redo = false;     // this row streams again from theta = -inf
+  for (int pass = 0; pass < 2; ++pass) {
   for (int c0 = 0; c0 < n; c0 += kChunk) {
     const int cl = min(kChunk, n - c0);
     __syncthreads();
     store_chunk(c0);
     if (c0 + kChunk < n) fetch_chunk(c0 + kChunk);
     __syncthreads();
-    if (!live) continue;
+    if (!live || (pass == 1 && !redo)) continue;
     const int boff = ilast - i;  // bias window index of chunk key t is t + boff
     // Blocks of kG 64-key groups.  The buffer holds at most kCap - 64 entries
     // between groups, so one more group always fits.  Fast path (a full block
@@ -406,6 +448,25 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
     auto bias_of = [&](const float* w1d, const uint32_t* kpos) {
       return b2 ? bias2d_lookup(tab, qb2, *kpos) : *w1d;
     };
+    if (pass == 0 && c0 == 0 && n >= kSampleMinN && cl == kChunk) {
+      // Starting threshold from the first chunk's logits (the arithmetic of the loop
+      // below): theta keeps about m of them, m the number of kept keys the chunk is
+      // expected to hold plus three standard deviations, so the row's keep-th largest
+      // logit lies above theta with high probability and the candidate buffer seldom
+      // needs compacting.  Only the admissions change: if fewer than `keep` keys pass
+      // theta, the row streams again from theta = -inf (below), so the selection stays
+      // exact.
+      const float e = (float)keep * (float)kChunk / (float)n;
+      const int m = (int)ceilf(e + 3.0f * sqrtf(e)) + 2;
+      if (2 * m <= kChunk) {
+        float sv[kChunk / 64];
+#pragma unroll
+        for (int r = 0; r < kChunk / 64; ++r)
+          sv[r] = canonical_logit(aqv, akp[64 * r], code_dot<D>(cp[64 * r], qq), a.isd, bias_of(bp + 64 * r, kp + 64 * r));
+        theta = sample_threshold<kChunk / 64>(sv, m);
+        sampled = true;
+      }
+    }
     for (int s0 = 0; s0 < cl; s0 += 64 * kG) {
       if (s0 + 64 * kG <= cl) {
         float l[kG];
@@ -454,6 +515,15 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
         }
       }
     }
+  }
+  // fewer than `keep` keys above the sampled threshold: stream this row again
+  redo = live && pass == 0 && sampled && cnt < keep;
+  if (!__syncthreads_or(redo ? 1 : 0)) break;  // uniform over the workgroup
+  if (redo) {
+    theta = -INFINITY;
+    cnt = 0;
+  }
+  fetch_chunk(0);
   }
   if (!live) return;
   __atomic_signal_fence(__ATOMIC_SEQ_CST);

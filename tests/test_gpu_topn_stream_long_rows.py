@@ -1,6 +1,8 @@
 """GPU parity of the long-sequence top-N kernel on rows that stress its streaming threshold
-(from 4096 keys on): rows whose keys at one even spread of positions (key j = t n / 1024,
-t < 1024) all tie at the top logit or all sit at the bottom, rows tied throughout, and
+(from 4096 keys on, where each row starts from a threshold taken from the logits of its
+first chunk of keys and streams again from minus infinity if fewer than N keys pass it):
+first chunks that tie at the top or sit at the bottom of the row, keys at one even
+spread of positions that tie at the top or sit at the bottom, rows tied throughout, and
 ordinary rows at several n and N.  The candidate buffer then fills with ties, or the
 threshold rises late, and every compaction path of the stream runs.
 
@@ -128,3 +130,38 @@ def test_head_dim_128():
     qb, aq, _ = oracle.pack(xq, synth.MEAN_SIGN)
     kb, ak, _ = oracle.pack(xk, synth.MEAN_SIGN)
     _check(qb, kb, aq, ak, T, v, N, _rows(2, n, 40, 5), "d=128")
+
+
+@pytest.mark.parametrize("N", [1, 300, 700])
+def test_first_chunk_ties_at_the_top(N):
+    # the first 2048 keys equal every query (the largest logit): the starting threshold
+    # is that logit, no key passes it, and the row streams again; the kept set is the N
+    # lowest indices
+    n = 9000
+    g = np.random.default_rng(98)
+    base = g.standard_normal(64).astype(np.float32)
+    xq = np.repeat(base[None, None, None, :], n, axis=2)
+    xk = g.standard_normal((1, 1, n, 64)).astype(np.float32)
+    xk[0, 0, :2048] = base
+    qb, _, _ = oracle.pack(xq, synth.SIGN)
+    kb, _, _ = oracle.pack(xk, synth.SIGN)
+    v = torch.from_numpy(g.standard_normal((1, 1, n, 64)).astype(np.float32)).to(torch.bfloat16)
+    idx = _check(qb, kb, None, None, None, v, N, _rows(1, n, 60, 6), f"first chunk at the top N={N}")
+    assert np.all(idx == np.arange(N))
+
+
+@pytest.mark.parametrize("N", [64, 600])
+def test_first_chunk_at_the_bottom(N):
+    # the first 2048 keys oppose every query (the smallest logit): the starting threshold
+    # is far below the row's kept logits and the stream compacts as it goes
+    n = 7000
+    g = np.random.default_rng(99)
+    base = g.standard_normal(64).astype(np.float32)
+    xq = np.repeat(base[None, None, None, :], n, axis=2)
+    xk = g.standard_normal((1, 1, n, 64)).astype(np.float32)
+    xk[0, 0, :2048] = -base
+    qb, _, _ = oracle.pack(xq, synth.SIGN)
+    kb, _, _ = oracle.pack(xk, synth.SIGN)
+    T = (0.05 * g.standard_normal((1, 2 * n - 1))).astype(np.float32)
+    v = torch.from_numpy(g.standard_normal((1, 1, n, 64)).astype(np.float32)).to(torch.bfloat16)
+    _check(qb, kb, None, None, T, v, N, _rows(1, n, 60, 7), f"first chunk at the bottom N={N}")
