@@ -33,7 +33,7 @@ namespace {
 // (W = 8 or 16) streams keys in LDS chunks of 128 W.
 constexpr int kCap = 768;     // candidate-buffer entries per wave
 constexpr int kR = kCap / 64;
-constexpr int kG = 4;         // 64-key groups per block of the key loop
+constexpr int kG = 8;         // 64-key groups per block of the key loop
 
 struct StreamKArgs {
   const uint32_t* qbits;
