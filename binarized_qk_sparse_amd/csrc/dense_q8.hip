@@ -232,25 +232,32 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
   }
 
   // ---- stage codes, scales, bias table and the transposed int8 V of this head
+  // (not fused: every global load of the staging below -- key codes and scales, the
+  // bias window, int8 V -- is issued before the first store, one memory round trip)
+  static_assert(NPAD <= 256, "one key per thread");
+  Code<D> kc_st{};
+  float ak_st = 1.0f;
   if constexpr (!FUSED) {
-    for (int j = tid; j < NPAD; j += 256) {
-      Code<D> c = load_code<D>(a.kbits, (size_t)bh * n + (j < n ? j : 0));
-      if (j >= n)
-#pragma unroll
-        for (int w = 0; w < D / 32; ++w) c.w[w] = 0u;
-      kcode[j] = c;
-      akk[j] = (j < n && a.ak != nullptr) ? a.ak[(size_t)bh * n + j] : 1.0f;
+    const int j = tid;
+    if (j < NPAD) {
+      kc_st = load_code<D>(a.kbits, (size_t)bh * n + (j < n ? j : 0));
+      ak_st = (j < n && a.ak != nullptr) ? a.ak[(size_t)bh * n + j] : 1.0f;
     }
   }
   constexpr bool b2 = BIAS && B2;
   uint32_t* kposs = reinterpret_cast<uint32_t*>(biasw + (b2 ? bias2d_floats(a.gh, a.gw, a.cls) : 0));
+  constexpr int BIT = (3 * NPAD + 255) / 256;  // 1-D bias window floats per thread: 2n - 1 + NPAD <= 3 NPAD
+  float bv[BIT];
   if (BIAS) {
     if (b2) {
       stage_bias2d(biasw, a.brow2, a.bcol2, a.bcls2, hh, a.gh, a.gw, a.cls, tid, 256);
       for (int j = tid; j < NPAD; j += 256) kposs[j] = bias2d_key(j < n ? j : n - 1, a.gh, a.gw, a.cls);
     } else {
-      for (int o = tid; o < 2 * n - 1 + NPAD; o += 256)
-        biasw[o] = o < 2 * n - 1 ? a.bias[(size_t)hh * (2 * n - 1) + o] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < BIT; ++u) {
+        const int o = tid + 256 * u;
+        bv[u] = o < 2 * n - 1 ? a.bias[(size_t)hh * (2 * n - 1) + o] : 0.0f;
+      }
     }
   }
   // int8 V transposed, four keys x four channels per step: one 32-bit load per
@@ -259,10 +266,55 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
   // stores of a wave fill consecutive words of the same rows.
   // (fused: the int8 codes come from V itself, with the scales above)
   constexpr int KB = NPAD / 4;  // key blocks
+  auto transpose_store = [&](int e, const uint32_t (&w)[4]) {
+    const int jb = 4 * (e % KB), c4 = 4 * (e / KB);
+    const uint32_t lo01 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // w0.b0 w1.b0 w0.b1 w1.b1
+    const uint32_t hi01 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // w0.b2 w1.b2 w0.b3 w1.b3
+    const uint32_t lo23 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+    *reinterpret_cast<uint32_t*>(&vqt[c4 + 0][jb]) = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+    *reinterpret_cast<uint32_t*>(&vqt[c4 + 1][jb]) = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+    *reinterpret_cast<uint32_t*>(&vqt[c4 + 2][jb]) = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+    *reinterpret_cast<uint32_t*>(&vqt[c4 + 3][jb]) = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+  };
+  if constexpr (!FUSED) {
+    // every thread's loads of int8 V are in flight before the first is used (at most
+    // NK / 2 items of four 32-bit loads each at head_dim 64)
+    constexpr int VIT = (KB * (D / 4) + 255) / 256;
+    const uint8_t* vsrc = reinterpret_cast<const uint8_t*>(a.vq + (size_t)bh * n * D);
+    uint32_t wv[VIT][4];
+#pragma unroll
+    for (int u = 0; u < VIT; ++u) {
+      const int e = tid + 256 * u;
+      const int jb = 4 * (e % KB), c4 = 4 * (e / KB);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        wv[u][r] = (e < KB * (D / 4) && jb + r < n) ? *reinterpret_cast<const uint32_t*>(vsrc + (size_t)(jb + r) * D + c4)
+                                                    : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < VIT; ++u)
+      if (tid + 256 * u < KB * (D / 4)) transpose_store(tid + 256 * u, wv[u]);
+  }
+  if (BIAS && !b2) {
+#pragma unroll
+    for (int u = 0; u < BIT; ++u)
+      if (tid + 256 * u < 2 * n - 1 + NPAD) biasw[tid + 256 * u] = bv[u];
+  }
+  if constexpr (!FUSED) {
+    if (tid < NPAD) {
+      if (tid >= n)
+#pragma unroll
+        for (int w = 0; w < D / 32; ++w) kc_st.w[w] = 0u;
+      kcode[tid] = kc_st;
+      akk[tid] = ak_st;
+    }
+  }
+  if constexpr (FUSED) {
   for (int e = tid; e < KB * (D / 4); e += 256) {
     const int jb = 4 * (e % KB), c4 = 4 * (e / KB);
     uint32_t w[4];
-    if constexpr (FUSED) {
+    {
       float s4[4], inv[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -279,20 +331,9 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
           for (int c = 0; c < 4; ++c) w[r] |= quant_i8(x[c], s4[c], inv[c]) << (8 * c);
         }
       }
-    } else {
-      const uint8_t* vsrc = reinterpret_cast<const uint8_t*>(a.vq + (size_t)bh * n * D);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        w[r] = jb + r < n ? *reinterpret_cast<const uint32_t*>(vsrc + (size_t)(jb + r) * D + c4) : 0u;
     }
-    const uint32_t lo01 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // w0.b0 w1.b0 w0.b1 w1.b1
-    const uint32_t hi01 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // w0.b2 w1.b2 w0.b3 w1.b3
-    const uint32_t lo23 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
-    const uint32_t hi23 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
-    *reinterpret_cast<uint32_t*>(&vqt[c4 + 0][jb]) = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
-    *reinterpret_cast<uint32_t*>(&vqt[c4 + 1][jb]) = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
-    *reinterpret_cast<uint32_t*>(&vqt[c4 + 2][jb]) = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
-    *reinterpret_cast<uint32_t*>(&vqt[c4 + 3][jb]) = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+    transpose_store(e, w);
+  }
   }
   __syncthreads();
   // column sums of int8 V: four threads per channel, each a quarter of the key

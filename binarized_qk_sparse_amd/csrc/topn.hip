@@ -239,8 +239,8 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
   float vmul = 1.0f;  // undoes the fp16 staging scale of V
   int tau_prev = 27;  // Hamming-level guess; each query starts from the last one's
   float wlo = 0.0f, whi = 0.0f;  // float keys: the last query's final threshold bracket (empty: none)
-  Code<D> qnext;
-  float aqnext;
+  Code<D> qnext{};
+  float aqnext = 1.0f;
   {
     const int nbh = u0 / a.tiles, ni0 = (u0 % a.tiles) * a.qt;
     const bool ok = u0 < u1 && ni0 + lane < n;
