@@ -33,7 +33,6 @@ namespace {
 // (W = 8 or 16) streams keys in LDS chunks of 128 W.
 constexpr int kCap = 768;     // candidate-buffer entries per wave
 constexpr int kR = kCap / 64;
-constexpr int kG = 8;         // 64-key groups per block of the key loop
 
 struct StreamKArgs {
   const uint32_t* qbits;
@@ -334,6 +333,9 @@ HAD_DEVICE T reduce_scatter8(T (&acc)[8], int k) {
 // 1-D path carries none of its code
 template <int VK, int D, int W, bool B2>
 __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a) {
+  // 64-key groups per block of the key loop: eight at head_dim 64, two at 128 (whose
+  // codes take twice the registers and LDS reads per key)
+  constexpr int kG = D == 64 ? 8 : 2;
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int ROWB = row_bytes<VK, D>();
   using L = Lds<D, W>;
