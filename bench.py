@@ -85,12 +85,15 @@ def attention_kernel(w, fused=False):
     dense softmax -> dense_q8 up to 256 tokens, dense_long beyond; n above the resident limit (512 keys for fp32 V, 1024
     otherwise, half that at head_dim 128) -> the streaming kernel, past its buffer -> the
     threshold-first kernel; head_dim 64 with bf16 V, plain sign codes, fp32 A*V and no
-    table (up to 1024 tokens) or a 1-D table (up to 256) -> the matrix-core kernel; anything
-    else, and the fused top-N launch -> the resident kernel."""
+    table (up to 1024 tokens) or a 1-D table (up to 256) -> the matrix-core kernel, head_dim
+    128 with no table (up to 1024 tokens, ahead of the resident limit) -> its head_dim 128
+    instance; anything else, and the fused top-N launch -> the resident kernel."""
     if fused and w.top_n is not None:
         return "topn_resident_kernel", "topn.hip"
     if w.top_n is None:
         return ("dense_q8_kernel", "dense_q8.hip") if w.n <= 256 else ("dense_long_kernel", "dense_long.hip")
+    if w.d == 128 and w.dtype == "bf16" and w.mode == 0 and not w.bias and w.av_mode == 0 and w.n <= 1024:
+        return "topn_mfma_d128_kernel", "topn_mfma.hip"
     resident_max = 512 if (w.dtype == "f32" and w.av_mode == 0) else 1024
     if w.d == 128:
         resident_max //= 2  # rows twice as long in LDS
@@ -112,7 +115,7 @@ def path_dtype(w, kname: str) -> str:
         return "b1+u8/i8"
     if w.av_mode == 2:
         return "b1+u8/i4"
-    if kname == "topn_mfma_kernel":
+    if kname in ("topn_mfma_kernel", "topn_mfma_d128_kernel"):
         return "b1+bf16x2 weights*bf16 V, f32 acc"
     return "b1+f32"
 

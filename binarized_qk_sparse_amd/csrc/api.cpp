@@ -278,9 +278,11 @@ static int topn_impl(const uint32_t* qbits, const uint32_t* kbits, const float* 
     p.v = q.vq;
     p.vscale = q.vscale;
   }
+  // the matrix-core kernel first: at head_dim 128 it holds up to 1024 keys, past the
+  // resident kernel's limit
+  if (topn_mfma_supported(p)) return launch_status(launch_topn_mfma(p, s), fn);
   if (wide) return launch_status(launch_topn_wide(p, s), fn);
   if (streaming) return launch_status(launch_topn_stream(p, s), fn);
-  if (topn_mfma_supported(p)) return launch_status(launch_topn_mfma(p, s), fn);
   return launch_status(launch_topn(p, s), fn);
 }
 

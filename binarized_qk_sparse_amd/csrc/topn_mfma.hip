@@ -1014,6 +1014,516 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
   }
 }
 
+// ------------------------------------------------------------------ head_dim 128
+// The same decomposition at d = 128 (integer logits, bf16 V).  What changes:
+//  * K = 128 fills a distance product with one key block: from C = 2^22 + 64 the
+//    product of the keys (-x/2) and the queries (+-1) is C = 2^22 + h, float bits
+//    0x4A800000 + 2h (partial sums are multiples of 1/2 below 2^23, so exact).  The
+//    low half-words of four results are clamped to 254, gathered into bytes and
+//    halved: one word of four distance bytes, levels capped at 127;
+//  * the key operands (64 bytes a key) are staged in parts that fit the two buffers;
+//  * with every byte below 0x80 the threshold search, the tie cut and the weight index
+//    (h - tau + 127 into a table of 127 levels) work as at d = 64 whenever tau <= 126,
+//    where every key at a capped level lies above tau.  A wave with a row whose
+//    threshold reaches 127 recomputes its distances exactly on the VALU, finds the
+//    threshold again over levels 0..128, and weighs each key on its own;
+//  * A*V runs in two passes of 64 channels over the same LDS rounds (V rows staged
+//    half a row at a time), the normaliser in the first.
+constexpr int kD2 = 128;
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+template <int NK, bool PAD, bool IDX>
+__global__ __launch_bounds__(64 * kWaves, 3) void topn_mfma_d128_kernel(const MfmaKArgs a) {
+  constexpr int KG = 8 * NK;            // keys per lane quarter
+  constexpr int KR = round_keys(NK);    // keys per quarter and round
+  constexpr int R = KG / KR;            // rounds per channel pass
+  constexpr int NKR = KR / 8;           // 32-key steps per round
+  constexpr int NW = 2 * NK;            // distance words per lane
+  constexpr int RB = round_bytes(NK);
+  constexpr int KQB = KG * 64;                    // fp4 operand bytes per key quarter
+  constexpr int NPART = 4 * KQB > 32768 ? 2 : 1;  // staging parts
+  constexpr int KGP = KG / NPART;                 // keys per quarter and part
+  constexpr int KQP = KQB / NPART;
+  constexpr int NWP = NW / NPART;
+  constexpr int VB = (RB > 2 * KQP + 64 ? RB : 2 * KQP + 64);
+  static_assert(R * KR == KG && KQP % 256 == 0 && NWP % 2 == 0, "parts and rounds tile the quarter");
+  __shared__ __align__(16) uint32_t tab[256];   // w(127 - e) for e in [1, 127], hi | lo << 16
+  __shared__ __align__(16) uint32_t tabg[132];  // exact path: w(k) for k in [0, 128]
+  __shared__ __align__(16) uint32_t one_pairs[4];
+  __shared__ __align__(16) uint32_t lut_k[256];
+  __shared__ __align__(16) uint32_t lut_q[256];
+  __shared__ __align__(256) uint8_t vbuf0[VB];
+  __shared__ __align__(256) uint8_t vbuf1[VB];
+  auto vbuf = [&](int rr) { return (lds_u8*)((rr & 1) ? vbuf1 : vbuf0); };
+  // quarter q of a part at 16 q bytes past a 256-byte boundary: the 16 lanes of a
+  // K-block (four quarters by four keys 64 bytes apart) read 16 distinct 16-byte slots
+  auto kxq = [&](int quarter) {
+    return (lds_u8*)(quarter >= 2 ? vbuf1 : vbuf0) + (quarter & 1) * KQP + 16 * quarter;
+  };
+
+  __builtin_amdgcn_s_setprio(3);
+  const int lane = (int)lane_id();
+  const int g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = a.n, keep = a.keep;
+  const int wg = (int)xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / a.split;
+  const int t = (wg % a.split) * kWaves + wave;
+  const bool have = t < a.tiles;
+  const size_t hb = (size_t)bh * n;
+  const int i = t * 16 + r;
+
+  // ---- V half-rows into LDS: round rg of the two passes (channels 64 (rg / R) ..)
+  const uint16_t* vh = reinterpret_cast<const uint16_t*>(a.v) + hb * kD2;
+  const uint32_t lrow = (uint32_t)lane >> 3;
+  const uint32_t piece = (uint32_t)lane & 7u;
+  const uint32_t vcol = 16u * (((piece >> 1) ^ vswz((uint32_t)wave, lrow))) + 8u * (piece & 1u);
+  const uint32_t lane_off = lrow * 256u + vcol * 2u;
+  // (a wave-uniform base, made explicit, plus a 32-bit lane offset: the loads take the
+  // scalar-base form and no 64-bit address per load is kept in registers)
+  auto issue_round = [&](int rg) {
+    const int pass = rg >= R ? 1 : 0;
+    const int rr = rg - pass * R;
+    lds_u8* buf = vbuf(rg) + wave * KR * 128;
+#pragma unroll
+    for (int m = 0; m < KR / 8; ++m) {
+      const int key0 = wave * KG + rr * KR + 8 * m;
+      const char* src;
+      if (PAD) {
+        // (the clamped offsets recomputed at every round rather than kept for all)
+        uint32_t lr = lrow;
+        asm volatile("" : "+v"(lr));
+        const char* sb = reinterpret_cast<const char*>(vh) + __builtin_amdgcn_readfirstlane(pass * 128);
+        src = sb + ((uint32_t)min(key0 + (int)lr, n - 1) * (kD2 * 2) + vcol * 2u);
+      } else {
+        const char* sb = reinterpret_cast<const char*>(vh) + __builtin_amdgcn_readfirstlane(key0 * (kD2 * 2) + pass * 128);
+        src = sb + lane_off;
+      }
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + m * 1024), 16, 0, 0);
+    }
+  };
+  // ---- the codes: this lane's query and the keys this thread expands, every part
+  const uint4 q = reinterpret_cast<const uint4*>(a.qbits)[hb + min(i, n - 1)];
+  const uint4* kb = reinterpret_cast<const uint4*>(a.kbits) + hb;
+  constexpr int KUP = (4 * KGP + 64 * kWaves - 1) / (64 * kWaves);  // keys per thread and part
+  uint4 kc[NPART * KUP];
+#pragma unroll
+  for (int pt = 0; pt < NPART; ++pt)
+#pragma unroll
+    for (int u = 0; u < KUP; ++u) {
+      const int x = min((int)threadIdx.x + u * 64 * kWaves, 4 * KGP - 1);
+      const int j = (x / KGP) * KG + pt * KGP + x % KGP;
+      kc[pt * KUP + u] = kb[min(j, n - 1)];  // padding keys: any code (their bytes are overwritten)
+    }
+  // ---- tables
+  for (int e = threadIdx.x; e < 256; e += 64 * kWaves) {
+    auto split = [](float w) {
+      const uint32_t hi16 = bf16_rne_bits(w);
+      return hi16 | (bf16_rne_bits(w - __builtin_bit_cast(float, hi16 << 16)) << 16);
+    };
+    tab[e] = (e >= 1 && e <= 127) ? split(exp2f((float)(127 - e) * a.exp_c)) : 0u;
+    if (e <= 128) tabg[e] = split(exp2f((float)e * a.exp_c));
+    if (e < 4) one_pairs[e] = 0x3f803f80u;
+    uint32_t sp = (uint32_t)e;
+    sp = (sp | (sp << 12)) & 0x000f000fu;
+    sp = (sp | (sp << 6)) & 0x03030303u;
+    sp = (sp | (sp << 3)) & 0x11111111u;
+    lut_k[e] = 0x99999999u ^ (sp << 3);
+    lut_q[e] = 0x22222222u ^ (sp << 3);
+  }
+
+  // ---- 1. distances, part by part
+  uint32_t P[NW];
+  const uint32_t qw = g == 0 ? q.x : (g == 1 ? q.y : (g == 2 ? q.z : q.w));  // dims 32 g .. 32 g + 31
+  v8i Bq;
+  constexpr float kC0 = 4194304.0f + 64.0f;
+#pragma unroll
+  for (int pt = 0; pt < NPART; ++pt) {
+    __syncthreads();  // tables written (part 0); the previous part's operands read (part 1)
+#pragma unroll
+    for (int u = 0; u < KUP; ++u) {
+      const int x = (int)threadIdx.x + u * 64 * kWaves;
+      if ((4 * KGP) % (64 * kWaves) == 0 || x < 4 * KGP) {
+        const uint4 c = kc[pt * KUP + u];
+        lds_u32x4* dst = (lds_u32x4*)(kxq(x / KGP) + (x % KGP) * 64);
+        dst[0] = u32x4{lut_k[c.x & 0xffu], lut_k[(c.x >> 8) & 0xffu], lut_k[(c.x >> 16) & 0xffu], lut_k[c.x >> 24]};
+        dst[1] = u32x4{lut_k[c.y & 0xffu], lut_k[(c.y >> 8) & 0xffu], lut_k[(c.y >> 16) & 0xffu], lut_k[c.y >> 24]};
+        dst[2] = u32x4{lut_k[c.z & 0xffu], lut_k[(c.z >> 8) & 0xffu], lut_k[(c.z >> 16) & 0xffu], lut_k[c.z >> 24]};
+        dst[3] = u32x4{lut_k[c.w & 0xffu], lut_k[(c.w >> 8) & 0xffu], lut_k[(c.w >> 16) & 0xffu], lut_k[c.w >> 24]};
+      }
+    }
+    if (pt == 0) {
+      Bq[0] = (int)lut_q[qw & 0xffu];
+      Bq[1] = (int)lut_q[(qw >> 8) & 0xffu];
+      Bq[2] = (int)lut_q[(qw >> 16) & 0xffu];
+      Bq[3] = (int)lut_q[qw >> 24];
+      Bq[4] = Bq[5] = Bq[6] = Bq[7] = 0;
+    }
+    __syncthreads();
+    if (have) {
+      // row rho of A: key (rho / 4) KG + pt KGP + 4 b + rho % 4, K-block g of its dims
+      const lds_u8* ka = kxq(r >> 2) + (r & 3) * 64 + g * 16;
+      constexpr int G = NWP < 8 ? NWP : 8;
+#pragma unroll
+      for (int b0 = 0; b0 < NWP; b0 += G) {
+        f32x4 c[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          const u32x4 av = *(const lds_u32x4*)(ka + (b0 + j) * 256);
+          v8i A;
+          A[0] = (int)av[0]; A[1] = (int)av[1]; A[2] = (int)av[2]; A[3] = (int)av[3];
+          A[4] = A[5] = A[6] = A[7] = 0;
+          c[j] = f32x4{kC0, kC0, kC0, kC0};
+          c[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bq, c[j], 4, 4, 0, 127, 0, 127);
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          const float e0 = c[j][0], e1 = c[j][1], e2 = c[j][2], e3 = c[j][3];
+          const uint32_t f0 = __builtin_bit_cast(uint32_t, e0), f1 = __builtin_bit_cast(uint32_t, e1);
+          const uint32_t f2 = __builtin_bit_cast(uint32_t, e2), f3 = __builtin_bit_cast(uint32_t, e3);
+          // low half-words (2h) of keys 0, 1 and 2, 3, clamped to 254 (level 127)
+          const u16x2 cap = {254, 254};
+          const u16x2 m01 = __builtin_elementwise_min(__builtin_bit_cast(u16x2, __builtin_amdgcn_perm(f1, f0, 0x05040100u)), cap);
+          const u16x2 m23 = __builtin_elementwise_min(__builtin_bit_cast(u16x2, __builtin_amdgcn_perm(f3, f2, 0x05040100u)), cap);
+          // (every byte even: the shift moves no bit across bytes)
+          uint32_t word = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, m23), __builtin_bit_cast(uint32_t, m01), 0x06040200u) >> 1;
+          const int b = pt * NWP + b0 + j;
+          if (PAD) {
+            // padding keys (j >= n) at level 127 with the capped ones
+            const int real = n - (g * KG + 4 * b);
+            word |= real >= 4 ? 0u : (real <= 0 ? 0x7f7f7f7fu : (0x7f7f7f7fu << (8 * real)));
+          }
+          P[b] = word;
+        }
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with the key operands
+  issue_round(0);
+  issue_round(1);
+
+  // ---- 2. threshold: smallest tau with C(tau) >= keep, C(t) = #{h <= t}, by probes
+  // next to the guess and bisection (as at d = 64) over levels below `top`, where
+  // C(top) = every byte of the row is known to reach keep
+  int tau = 0, less = 0, cl_lo = 0, cl_hi = 0;
+  auto search = [&](int top) {
+    const int tq = min(max(a.t0, 1), top - 1);
+    int lo, hi, clo, llo, lhi, sl, sh;
+    {
+      const int sm = (int)lane_sad<NW>(P, (uint32_t)tq - 1u);
+      const int s0 = (int)lane_sad<NW>(P, (uint32_t)tq);
+      const int sp = (int)lane_sad<NW>(P, (uint32_t)tq + 1u);
+      const int cx = (s0 - sm + 4 * NW) >> 1, cy = (sp - s0 + 4 * NW) >> 1;
+      const int both = quad_rows_sum((cy << 16) | cx);
+      const int ta = both & 0xffff, tb = both >> 16;
+      const bool below = ta >= keep;
+      const bool at = !below && tb >= keep;
+      lo = below ? -1 : (at ? tq - 1 : tq);
+      hi = below ? tq - 1 : (at ? tq : top);
+      clo = below ? 0 : (at ? ta : tb);
+      llo = below ? 0 : (at ? cx : cy);
+      lhi = below ? cx : (at ? cy : 0);
+      sl = sp;
+      sh = sm;
+    }
+    while (__builtin_amdgcn_ballot_w64(hi - lo > 1) != 0) {
+      const bool open = hi - lo > 1;
+      int mid = hi == top ? lo + 1 : (lo == -1 ? hi - 1 : (lo + hi) >> 1);
+      mid = open ? mid : hi;
+      const bool next_lo = mid == lo + 1 && lo >= 0;
+      const bool next_hi = mid == hi - 1 && hi < top && !next_lo;
+      const int s1 = (int)lane_sad<NW>(P, (uint32_t)(next_lo ? mid + 1 : mid));
+      int smid = next_lo ? sl : s1, snext = next_lo ? s1 : sh;
+      if (__builtin_amdgcn_ballot_w64(open && !next_lo && !next_hi) != 0) {
+        const int s2 = (int)lane_sad<NW>(P, (uint32_t)mid + 1u);
+        snext = (next_lo || next_hi) ? snext : s2;
+      }
+      const int cm = (snext - smid + 4 * NW) >> 1;
+      const int tm = quad_rows_sum(cm);
+      const bool up = open && tm >= keep;
+      const bool dn = open && tm < keep;
+      hi = up ? mid : hi;
+      lhi = up ? cm : lhi;
+      sh = up ? smid : sh;
+      lo = dn ? mid : lo;
+      clo = dn ? tm : clo;
+      llo = dn ? cm : llo;
+      sl = dn ? snext : sl;
+    }
+    tau = hi;
+    less = clo;
+    cl_lo = llo;
+    cl_hi = lhi;
+  };
+  bool exact = false;  // wave-uniform: a row of this tile keeps keys at a capped level
+  if (have) {
+    search(127);
+    exact = __builtin_amdgcn_ballot_w64(tau >= 127) != 0;
+  }
+  if (exact) {
+    // Levels 127 and 128 and the padding share byte 127.  Count this lane's keys at
+    // level 127 from their codes, then settle tau at 127 or 128 for the rows that
+    // reached it (their C(126) < keep); rows with tau <= 126 keep it.
+    int c127 = 0;
+#pragma unroll
+    for (int b = 0; b < NW; ++b) {
+      const uint32_t x = P[b] ^ 0x7f7f7f7fu;
+      const uint32_t z = ~(((x & 0x7f7f7f7fu) + 0x7f7f7f7fu) | x | 0x7f7f7f7fu);  // bit 7: byte == 127
+      if (z != 0u) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = g * KG + 4 * b + e;
+          if (((z >> (8 * e + 7)) & 1u) && j < n) {
+            const uint4 c = kb[j];
+            const int h = __builtin_popcount(q.x ^ c.x) + __builtin_popcount(q.y ^ c.y) +
+                          __builtin_popcount(q.z ^ c.z) + __builtin_popcount(q.w ^ c.w);
+            c127 += h == 127 ? 1 : 0;
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int c127r = quad_rows_sum(c127);
+    if (tau >= 127) {
+      // (here less = C(126) and cl_lo = this lane's keys below 127; the search never
+      // counted level 127, its upper bound from the start)
+      const int pad = min(max((g + 1) * KG - max(n, g * KG), 0), KG);  // this lane's padding keys
+      if (less + c127r >= keep) {
+        tau = 127;
+        cl_hi = cl_lo + c127;
+      } else {
+        tau = 128;
+        less += c127r;
+        const int c128 = KG - cl_lo - c127 - pad;
+        cl_lo += c127;
+        cl_hi = cl_lo + c128;
+      }
+    }
+  }
+  // ---- the rows of rounds 0 and 1 are in place
+  wait_vmem();
+  __syncthreads();
+
+  // ---- 3. ties
+  const int ceq = cl_hi - cl_lo;
+  const int before = quad_rows_excl(ceq, g);
+  const int take = min(max(keep - less - before, 0), ceq);
+  const uint32_t kidx = byte_bcast((uint32_t)(127 - tau));
+  const uint32_t ktau = byte_bcast((uint32_t)tau);
+  const uint32_t kcut = 127u - (uint32_t)take;
+
+  // ---- 4-5. weights and A*V, two passes of 64 channels
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(lds_u8*)one_pairs);
+  const uint32_t vrow0 = (uint32_t)(g * KR + (r >> 2));
+  const uint32_t vsw = vswz((uint32_t)g, vrow0);
+  uint32_t voff[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) voff[tt] = vrow0 * 128u + 32u * ((uint32_t)tt ^ vsw) + 8u * (uint32_t)(r & 3);
+  auto loadB = [&](int rg, int cl, bf16x8 (&Bv)[4]) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      lds_u8* const ad = vbuf(rg) + voff[tt] + 8 * cl * 128;
+      const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)ad);
+      const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(ad + 4 * 128));
+      Bv[tt] = __builtin_bit_cast(bf16x8, i16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]});
+    }
+  };
+  auto output = [&](int pass, const f32x4 (&acc)[4], const f32x4& accz) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = t * 16 + 4 * g + e;
+      const float inv = __builtin_amdgcn_rcpf(accz[e]);  // (Z >= 1: the weight at tau is 1)
+      if (row < n) {
+        float* o = a.out + (hb + row) * kD2 + 64 * pass + r;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) o[16 * tt] = acc[tt][e] * inv;
+      }
+    }
+  };
+  auto make_a = [&](const uint32_t (&ent)[8], bf16x8& A_hi, bf16x8& A_lo) {
+    uint32_t ah[4], al[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ah[e] = __builtin_amdgcn_perm(ent[2 * e + 1], ent[2 * e], 0x05040100u);
+      al[e] = __builtin_amdgcn_perm(ent[2 * e + 1], ent[2 * e], 0x07060302u);
+    }
+    A_hi = __builtin_bit_cast(bf16x8, make_uint4(ah[0], ah[1], ah[2], ah[3]));
+    A_lo = __builtin_bit_cast(bf16x8, make_uint4(al[0], al[1], al[2], al[3]));
+  };
+  auto run_av = [&]() {
+    f32x4 acc[4], accz;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accz = f32x4{0.f, 0.f, 0.f, 0.f};
+    int run = 0;  // keys at tau met so far in this lane (ascending j)
+    int32_t* idst = nullptr;
+    int ipos = 0;
+    if (IDX) {
+      ipos = quad_rows_excl(cl_lo + take, g);
+      idst = a.idx + (hb + (i < n ? i : 0)) * (size_t)keep;
+    }
+    // step c of the lane's keys g KG + 8 c + 0..7: the tie cut and the table entries
+    // per-pass copies of the tie constants, opaque to the compiler: the second pass
+    // redoes the tie cut instead of keeping the first pass's words for every step
+    uint32_t pk_idx = kidx, pk_tau = ktau, pk_cut = kcut;
+    auto prep = [&](int c, bool list, uint32_t (&ent)[8]) {
+      const uint32_t P0 = P[2 * c], P1 = P[2 * c + 1];
+      const uint32_t E0 = ~xor_add(P0, pk_tau, 0x7f7f7f7fu) & kM;
+      const uint32_t E1 = ~xor_add(P1, pk_tau, 0x7f7f7f7fu) & kM;
+      const int mid = __builtin_popcount(E0) + run;
+      const int run1 = __builtin_popcount(E1) + mid;
+      const bool over = run1 > take;
+      uint32_t U0 = over ? E0 : 0u, U1 = over ? E1 : 0u;
+      if (over && !(run >= take)) {
+        U0 = E0 & byte_prefix((E0 >> 7) + pk_cut + (uint32_t)run);
+        U1 = E1 & byte_prefix((E1 >> 7) + pk_cut + (uint32_t)mid);
+      }
+      run = run1;
+      // h - tau + 127 per byte, plus 128 for a key at tau that is not taken
+      const uint32_t I0 = P0 + pk_idx + U0, I1 = P1 + pk_idx + U1;
+      if (IDX && list && i < n) {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const uint32_t ib = ((b < 4 ? I0 : I1) >> (8 * (b & 3))) & 0xffu;
+          if (ib <= 127u && ipos < keep) idst[ipos++] = g * KG + 8 * c + b;
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        ent[b] = tab[(I0 >> (8 * b)) & 0xffu];
+        ent[4 + b] = tab[(I1 >> (8 * b)) & 0xffu];
+      }
+    };
+    // the passes as a loop (the rounds of a pass unrolled, so that the words of P and
+    // the buffer of each round are fixed at compile time)
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+      asm volatile("" : "+v"(pk_idx), "+v"(pk_tau), "+v"(pk_cut));
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) {
+        const int rg = pass * R + rr;
+        const int par = R % 2 == 0 ? rr : rg;  // the round's buffer parity
+        if (rg > 0) {
+          wait_vmem();
+          __syncthreads();
+          if (rg + 1 < 2 * R) issue_round(rg + 1);
+        }
+        if (rg * 4 / (2 * R) == 1 && (rg - 1) * 4 / (2 * R) != 1) __builtin_amdgcn_s_setprio(2);
+        if (rg * 4 / (2 * R) == 2 && (rg - 1) * 4 / (2 * R) != 2) __builtin_amdgcn_s_setprio(1);
+        if (rg * 4 / (2 * R) == 3 && (rg - 1) * 4 / (2 * R) != 3) __builtin_amdgcn_s_setprio(0);
+        if (have) {
+          bf16x8 Bv[2][4];
+          uint32_t ent[2][8];
+          loadB(par, 0, Bv[0]);
+          prep(rr * NKR, pass == 0, ent[0]);
+#pragma unroll
+          for (int cl = 0; cl < NKR; ++cl) {
+            bf16x8 A_hi, A_lo;
+            make_a(ent[cl & 1], A_hi, A_lo);
+            if (cl + 1 < NKR) prep(rr * NKR + cl + 1, pass == 0, ent[(cl + 1) & 1]);
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+              acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, Bv[cl & 1][tt], acc[tt], 0, 0, 0);
+            if (pass == 0) accz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, ones, accz, 0, 0, 0);
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+              acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, Bv[cl & 1][tt], acc[tt], 0, 0, 0);
+            if (pass == 0) accz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, ones, accz, 0, 0, 0);
+            if (cl + 1 < NKR) loadB(par, cl + 1, Bv[(cl + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      if (pass == 0 && have) {
+        // channels 0..63 done: write them, keep Z, start the second pass
+        output(0, acc, accz);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        run = 0;
+      }
+    }
+    if (have) output(1, acc, accz);
+  };
+  // The exact path: every key's level again from its code (no distance words, so the
+  // loops stay rolled and the registers those of the fast path), the same rounds and
+  // barriers as the fast path.
+  auto run_av_exact = [&]() {
+    f32x4 acc[4], accz;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accz = f32x4{0.f, 0.f, 0.f, 0.f};
+    int run = 0;
+    int32_t* idst = nullptr;
+    int ipos = 0;
+    if (IDX) {
+      ipos = quad_rows_excl(cl_lo + take, g);
+      idst = a.idx + (hb + (i < n ? i : 0)) * (size_t)keep;
+    }
+#pragma unroll 1
+    for (int rg = 0; rg < 2 * R; ++rg) {
+      const int pass = rg >= R ? 1 : 0;
+      const int rr = rg - pass * R;
+      if (rg > 0) {
+        wait_vmem();
+        __syncthreads();
+        if (rg + 1 < 2 * R) issue_round(rg + 1);
+      }
+      if (rg == R) {
+        output(0, acc, accz);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        run = 0;
+      }
+#pragma unroll 1
+      for (int cl = 0; cl < NKR; ++cl) {
+        const int c = rr * NKR + cl;
+        uint32_t ent[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const int j = g * KG + 8 * c + b;
+          int h = 255;  // padding keys: never kept
+          if (j < n) {
+            const uint4 cc = kb[j];
+            h = __builtin_popcount(q.x ^ cc.x) + __builtin_popcount(q.y ^ cc.y) + __builtin_popcount(q.z ^ cc.z) +
+                __builtin_popcount(q.w ^ cc.w);
+          }
+          const bool kept = h < tau || (h == tau && run < take);
+          run += h == tau ? 1 : 0;
+          ent[b] = kept ? tabg[tau - h] : 0u;
+          if (IDX && pass == 0 && kept && i < n && ipos < keep) idst[ipos++] = j;
+        }
+        bf16x8 Bv[4], A_hi, A_lo;
+        loadB(rg, cl, Bv);
+        make_a(ent, A_hi, A_lo);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, Bv[tt], acc[tt], 0, 0, 0);
+        if (pass == 0) accz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_hi, ones, accz, 0, 0, 0);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, Bv[tt], acc[tt], 0, 0, 0);
+        if (pass == 0) accz = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_lo, ones, accz, 0, 0, 0);
+      }
+    }
+    output(1, acc, accz);
+  };
+  if (exact)
+    run_av_exact();
+  else
+    run_av();
+}
+
+template <int NK, bool PAD, bool IDX>
+hipError_t launch_d128_nk(const MfmaKArgs& ka, dim3 grid, dim3 block, hipStream_t s) {
+  hipLaunchKernelGGL((topn_mfma_d128_kernel<NK, PAD, IDX>), grid, block, 0, s, ka);
+  return hipGetLastError();
+}
+
+template <int NK>
+hipError_t launch_d128_pad(const MfmaKArgs& ka, bool pad, dim3 grid, dim3 block, hipStream_t s) {
+  if (ka.idx != nullptr)
+    return pad ? launch_d128_nk<NK, true, true>(ka, grid, block, s) : launch_d128_nk<NK, false, true>(ka, grid, block, s);
+  return pad ? launch_d128_nk<NK, true, false>(ka, grid, block, s) : launch_d128_nk<NK, false, false>(ka, grid, block, s);
+}
+
 template <int NK, bool PAD, bool IDX, bool FK>
 hipError_t launch_nk(const MfmaKArgs& ka, dim3 grid, dim3 block, hipStream_t s) {
   hipLaunchKernelGGL((topn_mfma_kernel<NK, PAD, IDX, FK>), grid, block, 0, s, ka);
@@ -1043,8 +1553,9 @@ int threshold_guess(int64_t d, int64_t keep, int64_t n) {
 }  // namespace
 
 bool topn_mfma_supported(const AttnParams& p) {
-  const bool base = p.d == kD && p.v_kind == 1 && p.alpha_q == nullptr && p.alpha_k == nullptr &&
-                    p.brow == nullptr && p.n >= 1;
+  const bool base = p.v_kind == 1 && p.alpha_q == nullptr && p.alpha_k == nullptr && p.brow == nullptr && p.n >= 1;
+  if (p.d == kD2) return base && p.bias == nullptr && p.n <= 1024;
+  if (p.d != kD) return false;
   if (p.bias == nullptr) return base && p.n <= 1024;
   return base && p.n <= 256;  // float keys: the heads whose table passes the level test
 }
@@ -1073,6 +1584,15 @@ hipError_t launch_topn_mfma(const AttnParams& p, hipStream_t s) {
   const dim3 grid((unsigned)(BH * ka.split));
   const dim3 block((unsigned)(64 * kWaves));
   const bool pad = p.n != 32 * NK;
+  if (p.d == kD2) {
+    switch (NK) {
+      case 2: return launch_d128_pad<2>(ka, pad, grid, block, s);
+      case 4: return launch_d128_pad<4>(ka, pad, grid, block, s);
+      case 8: return launch_d128_pad<8>(ka, pad, grid, block, s);
+      case 16: return launch_d128_pad<16>(ka, pad, grid, block, s);
+      default: return launch_d128_pad<32>(ka, pad, grid, block, s);
+    }
+  }
   if (p.bias != nullptr) {
     switch (NK) {
       case 2: return launch_pad<2, true>(ka, pad, grid, block, s);

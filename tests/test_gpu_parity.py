@@ -371,8 +371,9 @@ def test_topn_zero_distance_ties():
 
 
 # ------------------------------------------------------------------ head_dim 128
-# The same entry points at d = 128 (codes of four words): the resident kernel up to
-# n = 512 (256 with fp32 V), the long-sequence kernel beyond, and the dense q8 kernel.
+# The same entry points at d = 128 (codes of four words): the matrix-core kernel for
+# plain sign codes with bf16 V and no table up to n = 1024, else the resident kernel up
+# to n = 512 (256 with fp32 V) and the long-sequence kernel beyond; and the dense q8 kernel.
 @pytest.mark.parametrize("n,N,vdtype", [(1, 1, torch.float32), (65, 7, torch.float32), (197, 30, torch.bfloat16),
                                         (256, 120, torch.float32), (300, 30, torch.float32),
                                         (512, 120, torch.bfloat16), (700, 64, torch.bfloat16),

@@ -4,7 +4,7 @@ top-N attention (fp32 A*V) in one launch.
 Bar: the kept index sets equal those of had_pack_qk followed by had_attention_topn on
 the same inputs, and the oracle's (bit-exact, ties to the lower key index); the outputs
 are the same bits as that pair where it runs the resident kernel (fp32 V, mean-centred
-codes, head_dim 128, or a table past 256 tokens), and within 1e-3 relative + 1e-4
+codes, or a table at head_dim 128 or past 256 tokens), and within 1e-3 relative + 1e-4
 absolute of the oracle everywhere.
 """
 import numpy as np
@@ -38,9 +38,9 @@ def _inputs(B, H, n, d, qkdt, vdt, bias, seed):
 
 
 def _pair_runs_resident(mode, vdt, bias, n, d):
-    # had_attention_topn sends plain sign codes with bf16 V at head_dim 64 to the
-    # matrix-core kernel (with a table only up to 256 tokens)
-    return vdt == torch.float32 or mode == MEAN or d == 128 or (bias and n > 256)
+    # had_attention_topn sends plain sign codes with bf16 V to the matrix-core kernel: at
+    # head_dim 64 with a table only up to 256 tokens, at head_dim 128 without one
+    return vdt == torch.float32 or mode == MEAN or (bias and (d == 128 or n > 256))
 
 
 def _check(q, k, v, T, N, mode, what):
