@@ -32,6 +32,30 @@ namespace {
 // head_dim D is 64 or 128 (codes of D / 32 words, D / 16 channel tiles)
 constexpr int kWaves = 4;
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Bit b of a code byte to bit 3 of nibble b, 0x9 (-0.5) to 0x1 (+0.5) for a key (x = -1 at a
+// set bit: -x/2 = +0.5), 0x2 (+1) to 0xA (-1) for a query: the fp4 (e2m1) operands of the
+// distance products.
+HAD_DEVICE uint32_t fp4_spread(uint32_t byte) {
+  uint32_t sp = byte;
+  sp = (sp | (sp << 12)) & 0x000f000fu;
+  sp = (sp | (sp << 6)) & 0x03030303u;
+  sp = (sp | (sp << 3)) & 0x11111111u;
+  return sp << 3;
+}
+
+// Byte offset of the 16-byte half h (dims 32 h .. 32 h + 31) of key kk of a 32-key step
+// among the step's fp4 key operands: the step's four 8-key blocks take 256 bytes each, a
+// key's halves sit at slots 2 (kk % 8) + h, and block q flips slot bits 0 and 3 by q, so that
+// the 16 lanes of one K-block (keys 8 q + e, e < 4, of the four blocks) read 16 different
+// 16-byte slots.
+HAD_DEVICE uint32_t fp4_key_offset(uint32_t kk, uint32_t h) {
+  const uint32_t q = kk >> 3;
+  const uint32_t slot = (2u * (kk & 7u) + h) ^ ((q & 1u) | ((q >> 1) << 3));
+  return q * 256u + slot * 16u;
+}
 
 struct DenseKArgs {
   const uint32_t* qbits;
@@ -110,17 +134,22 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
   constexpr int RPP = 256 / (D / 8);  // rows per pass with eight channels per thread
   __shared__ __align__(16) int8_t vqt[D][NPAD];  // Vq transposed: [channel][key]
   __shared__ __align__(16) Code<D> kcode[NPAD];
+  // head_dim 64: the keys' fp4 operands of the distance products, 1 KB per 32-key step
+  // (fused: in the column-sum partials' space, which is dead by then)
+  __shared__ __align__(256) uint8_t kx_own[D == 64 && !FUSED ? NPAD * 32 : 16];
   __shared__ __align__(16) float akk[NPAD];
   __shared__ int colsum[D];
   __shared__ __align__(16) Code<D> qcode[FP];      // fused: query codes
   __shared__ float aqs[FP];                        // fused: query alphas
   __shared__ float vsc[FD];                        // fused: V scales
   __shared__ float mus[FUSED ? 2 : 1][FD];         // fused: mu of Q and K
-  __shared__ double dred[FUSED ? RPP : 1][FD];     // fused: column-sum partials
+  __shared__ __align__(256) double dred[FUSED ? RPP : 1][FD];  // fused: column-sum partials
   __shared__ float fred[FUSED ? RPP : 1][FD];      // fused: column-max partials
   // BIAS: the 1-D table [2n - 1 + NPAD] (zeros read by padding keys), or the
   // two-dimensional tables followed by the key position codes [NPAD]
   extern __shared__ float biasw[];
+  static_assert(!FUSED || D != 64 || sizeof(dred) >= NPAD * 32, "fp4 key operands fit the partials' space");
+  uint8_t* const kx = FUSED ? reinterpret_cast<uint8_t*>(&dred[0][0]) : kx_own;
 
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;
@@ -336,6 +365,20 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
   }
   }
   __syncthreads();
+  if constexpr (D == 64) {
+    // the keys' fp4 operands (one key per thread)
+    if (tid < NPAD) {
+      const Code<D> c = kcode[tid];
+      const uint32_t ks = (uint32_t)tid >> 5, kk = (uint32_t)tid & 31u;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t w = c.w[h];
+        *reinterpret_cast<uint4*>(kx + ks * 1024u + fp4_key_offset(kk, (uint32_t)h)) =
+            make_uint4(0x99999999u ^ fp4_spread(w & 0xffu), 0x99999999u ^ fp4_spread((w >> 8) & 0xffu),
+                       0x99999999u ^ fp4_spread((w >> 16) & 0xffu), 0x99999999u ^ fp4_spread(w >> 24));
+      }
+    }
+  }
   // column sums of int8 V: four threads per channel, each a quarter of the key
   // blocks summed four keys at a time by v_dot4_i32_i8 against ones
   for (int e = tid; e < 4 * D; e += 256) {
@@ -369,18 +412,55 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
     const float* brow = biasw + (n - 1 - iq);  // 1-D table: bias of key j is brow[j]
     const int2 qb2 = b2 ? bias2d_query(iq, a.gh, a.gw, a.cls) : make_int2(0, 0);
 
-    // ---- logits of this lane's A elements
+    // ---- logits of this lane's A elements.  Head_dim 64: the distances of a 32-key step
+    // from one fp4 product (as in the matrix-core top-N kernel): row 4 g + e of A holds key
+    // 8 g + e in K-blocks 0, 1 and key 8 g + 4 + e in K-blocks 2, 3 (scaled by 2^8), column
+    // r of B query r; from C = 2^22 + 32 + 256 * 32 the result is 2^22 + h0 + 256 h1
+    // exactly, whose float bits hold 2 h0 in byte 0 and 2 h1 in byte 1: lane (g, r) gets
+    // the eight distances of its A elements, d - 2h = 64 - byte.
+    v8i Bq{};
+    int scale_a = 127;
+    if constexpr (D == 64) {
+      const uint32_t qw = (kg & 1) ? qq.w[1] : qq.w[0];  // (a select: no dynamic index into the code)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) Bq[b] = (int)(0x22222222u ^ fp4_spread((qw >> (8 * b)) & 0xffu));
+      scale_a = kg >= 2 ? 127 + 8 : 127;  // E8M0 2^8 for the second key block
+    }
+    const uint32_t koff = fp4_key_offset((uint32_t)(8 * (r16 >> 2) + (r16 & 3) + 4 * (kg >> 1)), (uint32_t)(kg & 1));
     float lg[NK][8];
     float m = -INFINITY;
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
       const int j0 = ks * 32 + kg * 8;
+      float dotf[8];
+      if constexpr (D == 64) {
+        const uint4 av = *reinterpret_cast<const uint4*>(kx + ks * 1024 + koff);
+        v8i A{};
+        A[0] = (int)av.x; A[1] = (int)av.y; A[2] = (int)av.z; A[3] = (int)av.w;
+        constexpr float kC0 = 4194304.0f + 32.0f + 256.0f * 32.0f;
+        f32x4 c = f32x4{kC0, kC0, kC0, kC0};
+        c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bq, c, 4, 4, 0, scale_a, 0, 127);
+        // (elements copied out first: a bit cast of a vector element reads element 0)
+        const float c0 = c[0], c1 = c[1], c2 = c[2], c3 = c[3];
+        auto dots = [&](float ce, float& lo, float& hi) {
+          const uint32_t bits = __builtin_bit_cast(uint32_t, ce);
+          lo = 64.0f - (float)(bits & 0xffu);  // (v_cvt_f32_ubyte0)
+          hi = 64.0f - (float)((bits >> 8) & 0xffu);
+        };
+        dots(c0, dotf[0], dotf[4]);
+        dots(c1, dotf[1], dotf[5]);
+        dots(c2, dotf[2], dotf[6]);
+        dots(c3, dotf[3], dotf[7]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dotf[e] = (float)(D - 2 * hamming<D>(qq, kcode[j0 + e]));
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int j = j0 + e;
-        const int h = hamming<D>(qq, kcode[j]);
         const float b = BIAS ? (b2 ? bias2d_lookup(biasw, qb2, kposs[j]) : brow[j]) : 0.0f;
-        float l = canonical_logit(aqv, akk[j], D - 2 * h, a.isd, b);
+        // the canonical order t = aq ak, u = t dot, v = u / sqrt(d), l = v + B (dot exact in fp32)
+        float l = __fadd_rn(__fmul_rn(__fmul_rn(__fmul_rn(aqv, akk[j]), dotf[e]), a.isd), b);
         if (ks == NK - 1) l = j < n ? l : -INFINITY;  // only the last step holds padding keys
         lg[ks][e] = l;
         m = fmaxf(m, l);
