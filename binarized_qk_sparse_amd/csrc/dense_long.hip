@@ -34,6 +34,29 @@ namespace had {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Bit b of a code byte to bit 3 of nibble b: the key operand of the fp4 distance products
+// is 0x9 (-0.5) xor this, a set bit (x = -1) giving 0x1 (-x/2 = +0.5); the query's is
+// 0x2 (+1) xor this, a set bit giving 0xA (-1).
+HAD_DEVICE uint32_t fp4_spread(uint32_t byte) {
+  uint32_t sp = byte;
+  sp = (sp | (sp << 12)) & 0x000f000fu;
+  sp = (sp | (sp << 6)) & 0x03030303u;
+  sp = (sp | (sp << 3)) & 0x11111111u;
+  return sp << 3;
+}
+
+// Byte offset of the 16-byte half h (dims 32 h .. 32 h + 31) of key kk (0..63) of a tile
+// among its fp4 operands: lane group g's sixteen keys take 512 bytes, a key's halves sit
+// at slots 2 (kk % 16) + h, and group g flips slot bits 0 and 3 by g, so that the 16
+// lanes of one K-block (four groups by four keys) read 16 different 16-byte slots.
+HAD_DEVICE uint32_t fp4_key_offset(uint32_t kk, uint32_t h) {
+  const uint32_t q = kk >> 4;
+  const uint32_t slot = (2u * (kk & 15u) + h) ^ ((q & 1u) | ((q >> 1) << 3));
+  return q * 512u + slot * 16u;
+}
 
 constexpr int kQB = 64;          // queries per workgroup (four waves of 16)
 constexpr int kKT = 64;          // keys per tile
@@ -89,6 +112,8 @@ __global__ __launch_bounds__(256) void dense_long_kernel(const DenseLongArgs a) 
   constexpr int VI = kKT * (D / 4) / 4 / 256;  // 4 x 4 byte blocks of a V tile per thread
   static_assert(VI >= 1 && VI * 256 * 16 == kKT * D, "sixteen bytes per block, every block staged");
   __shared__ __align__(16) Code<D> kc[kKT];
+  // head_dim 64: the tile's keys as fp4 operands of the distance products (2 KB)
+  __shared__ __align__(256) uint8_t kx[D == 64 ? kKT * 32 : 16];
   __shared__ __align__(16) float akk[kKT];
   __shared__ __align__(16) float bwin[kKT + kQB];  // 1-D: bias window; 2-D: key position codes
   __shared__ __align__(16) int8_t vqt[D * kVRow];
@@ -131,8 +156,9 @@ __global__ __launch_bounds__(256) void dense_long_kernel(const DenseLongArgs a) 
   auto tile_j0 = [&](int t) { return (t < ntiles ? t : t - ntiles) * kKT; };
   auto fetch = [&](int t) {
     const int j0 = tile_j0(t);
-    if (tid < kKT) {
-      const int j = j0 + tid;
+    // (head_dim 64: threads 64..127 load the same codes again and expand their second halves)
+    if (tid < (D == 64 ? 2 * kKT : kKT)) {
+      const int j = j0 + (tid & (kKT - 1));
       const int jc = j < n ? j : n - 1;
       pc = load_code<D>(a.kbits, hb + jc);
       pa = (ALPHA && a.ak != nullptr) ? a.ak[hb + jc] : 1.0f;
@@ -166,6 +192,15 @@ __global__ __launch_bounds__(256) void dense_long_kernel(const DenseLongArgs a) 
     if (tid < kKT) {
       kc[tid] = pc;
       akk[tid] = pa;
+    }
+    if constexpr (D == 64) {
+      if (tid < 2 * kKT) {
+        const uint32_t h = (uint32_t)tid >> 6;
+        const uint32_t w = h ? pc.w[1] : pc.w[0];
+        *reinterpret_cast<uint4*>(kx + fp4_key_offset((uint32_t)tid & 63u, h)) =
+            make_uint4(0x99999999u ^ fp4_spread(w & 0xffu), 0x99999999u ^ fp4_spread((w >> 8) & 0xffu),
+                       0x99999999u ^ fp4_spread((w >> 16) & 0xffu), 0x99999999u ^ fp4_spread(w >> 24));
+      }
     }
     if constexpr (BIAS == 1) {
       // + 0 turns a -0 entry into +0 (as the other kernels stage the table)
@@ -206,6 +241,23 @@ __global__ __launch_bounds__(256) void dense_long_kernel(const DenseLongArgs a) 
   for (int nt = 0; nt < NT; ++nt) acc[nt] = v4i{0, 0, 0, 0};
   const uint32_t* kpos = reinterpret_cast<const uint32_t*>(bwin);
   const int wbase = (kQB - 1) - 16 * wave - r16;  // 1-D window index of key column 0
+  // Head_dim 64: a tile's distances from two fp4 products (the encoding of the matrix-core
+  // top-N kernel): in product p, row 4 g + e of A holds key 16 g + 8 p + e in K-blocks 0, 1
+  // and key 16 g + 8 p + 4 + e in K-blocks 2, 3 (scaled by 2^8), column r of B query r;
+  // from C = 2^22 + 32 + 256 * 32 the result is 2^22 + h0 + 256 h1 exactly, so lane (g, r)
+  // finds 2h of its sixteen keys in bytes 0 and 1 of eight results: d - 2h = 64 - byte.
+  v8i Bq{};
+  int scale_a = 127;
+  uint32_t koff[2] = {0u, 0u};
+  if constexpr (D == 64) {
+    const uint32_t qw = (kg & 1) ? qq.w[1] : qq.w[0];  // (a select: no dynamic index into the code)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) Bq[b] = (int)(0x22222222u ^ fp4_spread((qw >> (8 * b)) & 0xffu));
+    scale_a = kg >= 2 ? 127 + 8 : 127;
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      koff[p] = fp4_key_offset((uint32_t)(16 * (r16 >> 2) + 8 * p + (r16 & 3) + 4 * (kg >> 1)), (uint32_t)(kg & 1));
+  }
 
   fetch(0);
   for (int t = 0; t < 2 * ntiles; ++t) {
@@ -224,20 +276,44 @@ __global__ __launch_bounds__(256) void dense_long_kernel(const DenseLongArgs a) 
     }
     // ---- logits of this lane's 16 keys (only the last tile holds padding keys)
     float l[16];
+    float dotf[16];
+    if constexpr (D == 64) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const uint4 av = *reinterpret_cast<const uint4*>(kx + koff[p]);
+        v8i A{};
+        A[0] = (int)av.x; A[1] = (int)av.y; A[2] = (int)av.z; A[3] = (int)av.w;
+        constexpr float kC0 = 4194304.0f + 32.0f + 256.0f * 32.0f;
+        f32x4 c = f32x4{kC0, kC0, kC0, kC0};
+        c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bq, c, 4, 4, 0, scale_a, 0, 127);
+        // (elements copied out first: a bit cast of a vector element reads element 0)
+        const float c0 = c[0], c1 = c[1], c2 = c[2], c3 = c[3];
+        auto dots = [&](float ce, float& lo, float& hi) {
+          const uint32_t bits = __builtin_bit_cast(uint32_t, ce);
+          lo = 64.0f - (float)(bits & 0xffu);  // (v_cvt_f32_ubyte0)
+          hi = 64.0f - (float)((bits >> 8) & 0xffu);
+        };
+        dots(c0, dotf[8 * p + 0], dotf[8 * p + 4]);
+        dots(c1, dotf[8 * p + 1], dotf[8 * p + 5]);
+        dots(c2, dotf[8 * p + 2], dotf[8 * p + 6]);
+        dots(c3, dotf[8 * p + 3], dotf[8 * p + 7]);
+      }
+    }
     auto logits = [&](auto full) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int jj = 16 * kg + e;
-        const int dot = code_dot<D>(qq, kc[jj]);
+        const float dot = D == 64 ? dotf[e] : (float)code_dot<D>(qq, kc[jj]);
         float b = 0.0f;
         if constexpr (BIAS == 1) b = bwin[jj + wbase];
         if constexpr (BIAS == 2) b = bias2d_lookup(tab, qb2, kpos[jj]);
         float lv;
         if constexpr (ALPHA) {
-          lv = canonical_logit(aqv, akk[jj], dot, a.isd, b);
+          // the canonical order t = aq ak, u = t dot, v = u / sqrt(d), l = v + B
+          lv = __fadd_rn(__fmul_rn(__fmul_rn(__fmul_rn(aqv, akk[jj]), dot), a.isd), b);
         } else {
           // alpha = 1: the canonical product 1 * 1 * dot is dot exactly
-          lv = __fadd_rn(__fmul_rn((float)dot, a.isd), b);
+          lv = __fadd_rn(__fmul_rn(dot, a.isd), b);
         }
         if constexpr (decltype(full)::value) {
           l[e] = lv;
