@@ -58,6 +58,31 @@ HAD_DEVICE uint32_t fp4_key_offset(uint32_t kk, uint32_t h) {
   return q * 512u + slot * 16u;
 }
 
+// Word b (0..3) of a code by bitwise selects on masks the compiler cannot see through (a
+// chain of selects on b is otherwise turned into a dynamic index, which puts the code in
+// scratch memory).
+template <int D>
+HAD_DEVICE uint32_t code_word_sel(const Code<D>& c, uint32_t b) {
+  if constexpr (D == 64) {
+    uint32_t m = 0u - (b & 1u);
+    asm volatile("" : "+v"(m));
+    return (c.w[1] & m) | (c.w[0] & ~m);
+  } else {
+    uint32_t m1 = 0u - (b & 1u), m2 = 0u - ((b >> 1) & 1u);
+    asm volatile("" : "+v"(m1), "+v"(m2));
+    const uint32_t w01 = (c.w[1] & m1) | (c.w[0] & ~m1);
+    const uint32_t w23 = (c.w[3] & m1) | (c.w[2] & ~m1);
+    return (w23 & m2) | (w01 & ~m2);
+  }
+}
+
+// Head_dim 128: byte offset of K-block b (dims 32 b .. 32 b + 31) of key kk, 64 bytes a key,
+// the block index flipped by the key's lane group kk / 16 so that the 16 lanes of a K-block
+// (four groups by four keys) read 16 different 16-byte slots.
+HAD_DEVICE uint32_t fp4_key_offset128(uint32_t kk, uint32_t b) {
+  return (kk * 4u + (b ^ ((kk >> 4) & 3u))) * 16u;
+}
+
 constexpr int kQB = 64;          // queries per workgroup (four waves of 16)
 constexpr int kKT = 64;          // keys per tile
 constexpr int kVRow = kKT + 16;  // bytes per channel row of the transposed int8 V tile
@@ -112,8 +137,8 @@ __global__ __launch_bounds__(256) void dense_long_kernel(const DenseLongArgs a) 
   constexpr int VI = kKT * (D / 4) / 4 / 256;  // 4 x 4 byte blocks of a V tile per thread
   static_assert(VI >= 1 && VI * 256 * 16 == kKT * D, "sixteen bytes per block, every block staged");
   __shared__ __align__(16) Code<D> kc[kKT];
-  // head_dim 64: the tile's keys as fp4 operands of the distance products (2 KB)
-  __shared__ __align__(256) uint8_t kx[D == 64 ? kKT * 32 : 16];
+  // the tile's keys as fp4 operands of the distance products (32 bytes a key at head_dim 64, 64 at 128)
+  __shared__ __align__(256) uint8_t kx[kKT * (D / 2)];
   __shared__ __align__(16) float akk[kKT];
   __shared__ __align__(16) float bwin[kKT + kQB];  // 1-D: bias window; 2-D: key position codes
   __shared__ __align__(16) int8_t vqt[D * kVRow];
@@ -156,8 +181,9 @@ __global__ __launch_bounds__(256) void dense_long_kernel(const DenseLongArgs a) 
   auto tile_j0 = [&](int t) { return (t < ntiles ? t : t - ntiles) * kKT; };
   auto fetch = [&](int t) {
     const int j0 = tile_j0(t);
-    // (head_dim 64: threads 64..127 load the same codes again and expand their second halves)
-    if (tid < (D == 64 ? 2 * kKT : kKT)) {
+    // (threads kKT.. load the same codes again and expand their other 16-byte blocks:
+    // two per key at head_dim 64, four at 128)
+    if (tid < (D / 32) * kKT) {
       const int j = j0 + (tid & (kKT - 1));
       const int jc = j < n ? j : n - 1;
       pc = load_code<D>(a.kbits, hb + jc);
@@ -193,14 +219,13 @@ __global__ __launch_bounds__(256) void dense_long_kernel(const DenseLongArgs a) 
       kc[tid] = pc;
       akk[tid] = pa;
     }
-    if constexpr (D == 64) {
-      if (tid < 2 * kKT) {
-        const uint32_t h = (uint32_t)tid >> 6;
-        const uint32_t w = h ? pc.w[1] : pc.w[0];
-        *reinterpret_cast<uint4*>(kx + fp4_key_offset((uint32_t)tid & 63u, h)) =
-            make_uint4(0x99999999u ^ fp4_spread(w & 0xffu), 0x99999999u ^ fp4_spread((w >> 8) & 0xffu),
-                       0x99999999u ^ fp4_spread((w >> 16) & 0xffu), 0x99999999u ^ fp4_spread(w >> 24));
-      }
+    if (tid < (D / 32) * kKT) {
+      const uint32_t h = (uint32_t)tid >> 6;  // the key's block of 32 dims
+      const uint32_t w = code_word_sel<D>(pc, h);
+      const uint32_t off = D == 64 ? fp4_key_offset((uint32_t)tid & 63u, h) : fp4_key_offset128((uint32_t)tid & 63u, h);
+      *reinterpret_cast<uint4*>(kx + off) =
+          make_uint4(0x99999999u ^ fp4_spread(w & 0xffu), 0x99999999u ^ fp4_spread((w >> 8) & 0xffu),
+                     0x99999999u ^ fp4_spread((w >> 16) & 0xffu), 0x99999999u ^ fp4_spread(w >> 24));
     }
     if constexpr (BIAS == 1) {
       // + 0 turns a -0 entry into +0 (as the other kernels stage the table)
@@ -246,17 +271,22 @@ __global__ __launch_bounds__(256) void dense_long_kernel(const DenseLongArgs a) 
   // and key 16 g + 8 p + 4 + e in K-blocks 2, 3 (scaled by 2^8), column r of B query r;
   // from C = 2^22 + 32 + 256 * 32 the result is 2^22 + h0 + 256 h1 exactly, so lane (g, r)
   // finds 2h of its sixteen keys in bytes 0 and 1 of eight results: d - 2h = 64 - byte.
+  // Head_dim 128: K = 128 fills a product with one key block, so four products: in
+  // product p row 4 g + e holds key 16 g + 4 p + e, K-block g' its dims 32 g' ..; from
+  // C = 2^22 + 64 the result is 2^22 + h and d - 2h = 2^23 + 128 - 2C, exact in one fma.
+  constexpr int NPR = D == 64 ? 2 : 4;  // products per tile
   v8i Bq{};
   int scale_a = 127;
-  uint32_t koff[2] = {0u, 0u};
-  if constexpr (D == 64) {
-    const uint32_t qw = (kg & 1) ? qq.w[1] : qq.w[0];  // (a select: no dynamic index into the code)
+  uint32_t koff[NPR];
+  {
+    const uint32_t qw = code_word_sel<D>(qq, (uint32_t)(D == 64 ? (kg & 1) : kg));
 #pragma unroll
     for (int b = 0; b < 4; ++b) Bq[b] = (int)(0x22222222u ^ fp4_spread((qw >> (8 * b)) & 0xffu));
-    scale_a = kg >= 2 ? 127 + 8 : 127;
+    if constexpr (D == 64) scale_a = kg >= 2 ? 127 + 8 : 127;
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-      koff[p] = fp4_key_offset((uint32_t)(16 * (r16 >> 2) + 8 * p + (r16 & 3) + 4 * (kg >> 1)), (uint32_t)(kg & 1));
+    for (int p = 0; p < NPR; ++p)
+      koff[p] = D == 64 ? fp4_key_offset((uint32_t)(16 * (r16 >> 2) + 8 * p + (r16 & 3) + 4 * (kg >> 1)), (uint32_t)(kg & 1))
+                        : fp4_key_offset128((uint32_t)(16 * (r16 >> 2) + 4 * p + (r16 & 3)), (uint32_t)kg);
   }
 
   fetch(0);
@@ -277,6 +307,23 @@ __global__ __launch_bounds__(256) void dense_long_kernel(const DenseLongArgs a) 
     // ---- logits of this lane's 16 keys (only the last tile holds padding keys)
     float l[16];
     float dotf[16];
+    if constexpr (D == 128) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint4 av = *reinterpret_cast<const uint4*>(kx + koff[p]);
+        v8i A{};
+        A[0] = (int)av.x; A[1] = (int)av.y; A[2] = (int)av.z; A[3] = (int)av.w;
+        constexpr float kC0 = 4194304.0f + 64.0f;
+        f32x4 c = f32x4{kC0, kC0, kC0, kC0};
+        c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bq, c, 4, 4, 0, 127, 0, 127);
+        const float c0 = c[0], c1 = c[1], c2 = c[2], c3 = c[3];
+        constexpr float kDot0 = 8388608.0f + 128.0f;  // 2^23 + 128
+        dotf[4 * p + 0] = __builtin_fmaf(c0, -2.0f, kDot0);
+        dotf[4 * p + 1] = __builtin_fmaf(c1, -2.0f, kDot0);
+        dotf[4 * p + 2] = __builtin_fmaf(c2, -2.0f, kDot0);
+        dotf[4 * p + 3] = __builtin_fmaf(c3, -2.0f, kDot0);
+      }
+    }
     if constexpr (D == 64) {
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
@@ -303,7 +350,7 @@ __global__ __launch_bounds__(256) void dense_long_kernel(const DenseLongArgs a) 
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int jj = 16 * kg + e;
-        const float dot = D == 64 ? dotf[e] : (float)code_dot<D>(qq, kc[jj]);
+        const float dot = dotf[e];
         float b = 0.0f;
         if constexpr (BIAS == 1) b = bwin[jj + wbase];
         if constexpr (BIAS == 2) b = bias2d_lookup(tab, qb2, kpos[jj]);

@@ -57,6 +57,46 @@ HAD_DEVICE uint32_t fp4_key_offset(uint32_t kk, uint32_t h) {
   return q * 256u + slot * 16u;
 }
 
+// The fp4 operands of one key (32 bytes at head_dim 64, 64 at 128) into the step's block.
+template <int D>
+HAD_DEVICE void store_fp4_key(uint8_t* kx, const Code<D>& c, uint32_t j);
+
+// Word b (0..3) of a code by bitwise selects on masks the compiler cannot see through (a
+// chain of selects on b is otherwise turned into a dynamic index, which puts the code in
+// scratch memory).
+template <int D>
+HAD_DEVICE uint32_t code_word_sel(const Code<D>& c, uint32_t b) {
+  if constexpr (D == 64) {
+    uint32_t m = 0u - (b & 1u);
+    asm volatile("" : "+v"(m));
+    return (c.w[1] & m) | (c.w[0] & ~m);
+  } else {
+    uint32_t m1 = 0u - (b & 1u), m2 = 0u - ((b >> 1) & 1u);
+    asm volatile("" : "+v"(m1), "+v"(m2));
+    const uint32_t w01 = (c.w[1] & m1) | (c.w[0] & ~m1);
+    const uint32_t w23 = (c.w[3] & m1) | (c.w[2] & ~m1);
+    return (w23 & m2) | (w01 & ~m2);
+  }
+}
+
+// Head_dim 128: byte offset of K-block b (dims 32 b .. 32 b + 31) of key kk of a step, 64
+// bytes a key, the block index flipped by the key's lane group kk / 8 so that the 16 lanes
+// of a K-block (four groups by four keys) read 16 different 16-byte slots.
+HAD_DEVICE uint32_t fp4_key_offset128(uint32_t kk, uint32_t b) { return (kk * 4u + (b ^ ((kk >> 3) & 3u))) * 16u; }
+
+template <int D>
+HAD_DEVICE void store_fp4_key(uint8_t* kx, const Code<D>& c, uint32_t j) {
+  const uint32_t ks = j >> 5, kk = j & 31u;
+#pragma unroll
+  for (int h = 0; h < D / 32; ++h) {
+    const uint32_t w = c.w[h];
+    const uint32_t off = D == 64 ? fp4_key_offset(kk, (uint32_t)h) : fp4_key_offset128(kk, (uint32_t)h);
+    *reinterpret_cast<uint4*>(kx + ks * (32u * (D / 2)) + off) =
+        make_uint4(0x99999999u ^ fp4_spread(w & 0xffu), 0x99999999u ^ fp4_spread((w >> 8) & 0xffu),
+                   0x99999999u ^ fp4_spread((w >> 16) & 0xffu), 0x99999999u ^ fp4_spread(w >> 24));
+  }
+}
+
 struct DenseKArgs {
   const uint32_t* qbits;
   const uint32_t* kbits;
@@ -133,10 +173,10 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
   constexpr int FD = FUSED ? D : 1;
   constexpr int RPP = 256 / (D / 8);  // rows per pass with eight channels per thread
   __shared__ __align__(16) int8_t vqt[D][NPAD];  // Vq transposed: [channel][key]
-  __shared__ __align__(16) Code<D> kcode[NPAD];
-  // head_dim 64: the keys' fp4 operands of the distance products, 1 KB per 32-key step
+  __shared__ __align__(16) Code<D> kcode[FUSED ? NPAD : 1];  // fused: the key codes, expanded after staging
+  // the keys' fp4 operands of the distance products, 32 bytes a key at head_dim 64, 64 at 128
   // (fused: in the column-sum partials' space, which is dead by then)
-  __shared__ __align__(256) uint8_t kx_own[D == 64 && !FUSED ? NPAD * 32 : 16];
+  __shared__ __align__(256) uint8_t kx_own[FUSED ? 16 : NPAD * (D / 2)];
   __shared__ __align__(16) float akk[NPAD];
   __shared__ int colsum[D];
   __shared__ __align__(16) Code<D> qcode[FP];      // fused: query codes
@@ -148,7 +188,7 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
   // BIAS: the 1-D table [2n - 1 + NPAD] (zeros read by padding keys), or the
   // two-dimensional tables followed by the key position codes [NPAD]
   extern __shared__ float biasw[];
-  static_assert(!FUSED || D != 64 || sizeof(dred) >= NPAD * 32, "fp4 key operands fit the partials' space");
+  static_assert(!FUSED || sizeof(dred) >= NPAD * (D / 2), "fp4 key operands fit the partials' space");
   uint8_t* const kx = FUSED ? reinterpret_cast<uint8_t*>(&dred[0][0]) : kx_own;
 
   const int tid = threadIdx.x;
@@ -335,7 +375,7 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
       if (tid >= n)
 #pragma unroll
         for (int w = 0; w < D / 32; ++w) kc_st.w[w] = 0u;
-      kcode[tid] = kc_st;
+      store_fp4_key<D>(kx, kc_st, (uint32_t)tid);
       akk[tid] = ak_st;
     }
   }
@@ -365,19 +405,9 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
   }
   }
   __syncthreads();
-  if constexpr (D == 64) {
-    // the keys' fp4 operands (one key per thread)
-    if (tid < NPAD) {
-      const Code<D> c = kcode[tid];
-      const uint32_t ks = (uint32_t)tid >> 5, kk = (uint32_t)tid & 31u;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t w = c.w[h];
-        *reinterpret_cast<uint4*>(kx + ks * 1024u + fp4_key_offset(kk, (uint32_t)h)) =
-            make_uint4(0x99999999u ^ fp4_spread(w & 0xffu), 0x99999999u ^ fp4_spread((w >> 8) & 0xffu),
-                       0x99999999u ^ fp4_spread((w >> 16) & 0xffu), 0x99999999u ^ fp4_spread(w >> 24));
-      }
-    }
+  if constexpr (FUSED) {
+    // the keys' fp4 operands (one key per thread), now that the partials' space is free
+    if (tid < NPAD) store_fp4_key<D>(kx, kcode[tid], (uint32_t)tid);
   }
   // column sums of int8 V: four threads per channel, each a quarter of the key
   // blocks summed four keys at a time by v_dot4_i32_i8 against ones
@@ -418,23 +448,46 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
     // r of B query r; from C = 2^22 + 32 + 256 * 32 the result is 2^22 + h0 + 256 h1
     // exactly, whose float bits hold 2 h0 in byte 0 and 2 h1 in byte 1: lane (g, r) gets
     // the eight distances of its A elements, d - 2h = 64 - byte.
+    // Head_dim 128: K = 128 fills a product with one key block, so two products per step:
+    // in product p row 4 g + e holds key 8 g + 4 p + e, K-block g' its dims 32 g' ..; from
+    // C = 2^22 + 64 the result is 2^22 + h and d - 2h = 2^23 + 128 - 2C, exact in one fma.
     v8i Bq{};
     int scale_a = 127;
-    if constexpr (D == 64) {
-      const uint32_t qw = (kg & 1) ? qq.w[1] : qq.w[0];  // (a select: no dynamic index into the code)
+    {
+      const uint32_t qw = code_word_sel<D>(qq, (uint32_t)(D == 64 ? (kg & 1) : kg));
 #pragma unroll
       for (int b = 0; b < 4; ++b) Bq[b] = (int)(0x22222222u ^ fp4_spread((qw >> (8 * b)) & 0xffu));
-      scale_a = kg >= 2 ? 127 + 8 : 127;  // E8M0 2^8 for the second key block
+      if constexpr (D == 64) scale_a = kg >= 2 ? 127 + 8 : 127;  // E8M0 2^8 for the second key block
     }
-    const uint32_t koff = fp4_key_offset((uint32_t)(8 * (r16 >> 2) + (r16 & 3) + 4 * (kg >> 1)), (uint32_t)(kg & 1));
+    uint32_t koff[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      koff[p] = D == 64 ? fp4_key_offset((uint32_t)(8 * (r16 >> 2) + (r16 & 3) + 4 * (kg >> 1)), (uint32_t)(kg & 1))
+                        : fp4_key_offset128((uint32_t)(8 * (r16 >> 2) + 4 * p + (r16 & 3)), (uint32_t)kg);
     float lg[NK][8];
     float m = -INFINITY;
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
       const int j0 = ks * 32 + kg * 8;
       float dotf[8];
-      if constexpr (D == 64) {
-        const uint4 av = *reinterpret_cast<const uint4*>(kx + ks * 1024 + koff);
+      if constexpr (D == 128) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const uint4 av = *reinterpret_cast<const uint4*>(kx + ks * 2048 + koff[p]);
+          v8i A{};
+          A[0] = (int)av.x; A[1] = (int)av.y; A[2] = (int)av.z; A[3] = (int)av.w;
+          constexpr float kC0 = 4194304.0f + 64.0f;
+          f32x4 c = f32x4{kC0, kC0, kC0, kC0};
+          c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bq, c, 4, 4, 0, 127, 0, 127);
+          const float c0 = c[0], c1 = c[1], c2 = c[2], c3 = c[3];
+          constexpr float kDot0 = 8388608.0f + 128.0f;  // 2^23 + 128
+          dotf[4 * p + 0] = __builtin_fmaf(c0, -2.0f, kDot0);
+          dotf[4 * p + 1] = __builtin_fmaf(c1, -2.0f, kDot0);
+          dotf[4 * p + 2] = __builtin_fmaf(c2, -2.0f, kDot0);
+          dotf[4 * p + 3] = __builtin_fmaf(c3, -2.0f, kDot0);
+        }
+      } else {
+        const uint4 av = *reinterpret_cast<const uint4*>(kx + ks * 1024 + koff[0]);
         v8i A{};
         A[0] = (int)av.x; A[1] = (int)av.y; A[2] = (int)av.z; A[3] = (int)av.w;
         constexpr float kC0 = 4194304.0f + 32.0f + 256.0f * 32.0f;
@@ -451,9 +504,6 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
         dots(c1, dotf[1], dotf[5]);
         dots(c2, dotf[2], dotf[6]);
         dots(c3, dotf[3], dotf[7]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dotf[e] = (float)(D - 2 * hamming<D>(qq, kcode[j0 + e]));
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {

@@ -29,6 +29,8 @@ on, which are not available here):
 * ``c4@n``: the DeiT-B dense workload at another length (same batch, heads and laws;
   the relative-position table grows to 2n-1 offsets): the sweep of the dense
   kernel over sequence lengths that BinaryAttention's kernel-speed figure runs.
+* ``c4d128`` (and ``c4d128@n``): the dense workload's laws at head_dim 128, the head
+  size of BinaryAttention's kernel-speed figure: batch 8, 12 heads, n=1024.
 * ``c4b2d``, ``c5b2d``: c4 and c5 with the two-dimensional decomposable bias
   (row and column offset tables ~ N(0, 0.02^2) per head, tensor id 7, over
   the 14 x 14 grid after DeiT's class token and the 128 x 128 grid).
@@ -98,6 +100,9 @@ WORKLOADS: Dict[str, Workload] = {
     # the long-context sweep at head_dim 128 (the kernel shape of BinaryAttention's
     # speed-versus-length figure); "c3d128@n" scales N = 15 n / 128 like c3
     "c3d128": Workload("c3d128", 5, 4, 12, 1024, 128, 120, "bf16", SIGN, False, AV_F32, "chan_std"),
+    # the dense forward at head_dim 128 with c4's inputs, 8 x 12 heads of 1024 tokens
+    # ("c4d128@n" for the other lengths of that figure)
+    "c4d128": Workload("c4d128", 6, 8, 12, 1024, 128, None, "bf16", MEAN_SIGN, True, AV_Q8, "chan_mean"),
 }
 
 C3_SWEEP = (128, 256, 512, 1024)
