@@ -233,7 +233,8 @@ static int topn_impl(const uint32_t* qbits, const uint32_t* kbits, const float* 
     return fail(HAD_ERR_INVALID_ARG, fn, "unknown av_mode");
   const int64_t keep = top_n < n ? top_n : n;
   const bool quant = av_mode != HAD_AV_F32;
-  const int v_kind = quant ? 2 : (v_dtype == HAD_BF16 ? 1 : 0);
+  // V kinds: 0 f32, 1 bf16, 2 int8 codes, 3 4-bit codes two per byte
+  const int v_kind = quant ? (av_mode == HAD_AV_Q4 ? 3 : 2) : (v_dtype == HAD_BF16 ? 1 : 0);
   // above the resident limit: the streaming kernel while its candidate buffer holds
   // the kept set, the threshold-first kernel beyond
   const bool streaming = n > topn_max_n(v_kind, d);

@@ -184,6 +184,10 @@ HAD_DEVICE uint32_t quant_i8(float x, float s, float inv) {
   return (uint32_t)((int32_t)r) & 0xffu;
 }
 
+// Channel c (0..7) of a word of eight 4-bit two's-complement codes (nibble c),
+// sign-extended.
+HAD_DEVICE int nibble_s4(uint32_t w, int c) { return (int)(w << (28 - 4 * c)) >> 28; }
+
 // ---- two-dimensional decomposable bias (row + column offset tables, class token)
 // The tables are staged with the class token's values folded in, so that every
 // pair costs two table reads and one addition whatever its kind:

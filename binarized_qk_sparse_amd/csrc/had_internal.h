@@ -32,7 +32,7 @@ struct VQuantParams {
   int64_t BH, n, d;
   float* vmax_partial;  // [BH, chunks, d]
   float* vscale;        // [BH, d]
-  int8_t* vq;           // [BH, n, d]
+  int8_t* vq;           // [BH, n, d] int8, or [BH, n, d/2] bytes of two 4-bit codes (levels 7)
   int levels;           // 127 (int8) or 7 (4-bit values)
 };
 constexpr int kVqChunk = 256;
@@ -46,8 +46,8 @@ struct AttnParams {
   const float* alpha_q;
   const float* alpha_k;
   const float* bias;
-  const void* v;  // f32 / bf16 V (AV_F32) or int8 Vq (AV_Q8)
-  int v_kind;     // 0 f32, 1 bf16, 2 int8 (quantized)
+  const void* v;  // f32 / bf16 V (AV_F32), int8 Vq (AV_Q8) or packed 4-bit Vq (AV_Q4)
+  int v_kind;     // 0 f32, 1 bf16, 2 int8 codes, 3 4-bit codes two per byte (quantized)
   const float* vscale;
   int64_t B, H, n, d;
   int64_t keep;  // min(top_n, n)
@@ -72,7 +72,7 @@ __host__ __device__ inline int64_t bias2d_floats(int64_t gh, int64_t gw, int64_t
   return cls ? (5 * gh - 1) + (5 * gw - 1) : (2 * gh - 1) + (2 * gw - 1);
 }
 hipError_t launch_topn(const AttnParams& p, hipStream_t s);
-// largest n the resident top-N kernel takes for V of kind v_kind (0 f32, 1 bf16, 2 int8)
+// largest n the resident top-N kernel takes for V of kind v_kind (0 f32, 1 bf16, 2 int8, 3 int4)
 int64_t topn_resident_max_n(int v_kind, int64_t d);
 bool topn_mfma_supported(const AttnParams& p);
 hipError_t launch_topn_mfma(const AttnParams& p, hipStream_t s);

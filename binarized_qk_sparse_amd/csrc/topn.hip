@@ -80,7 +80,7 @@ struct TopnKArgs {
 
 template <int VK, int D>
 constexpr int row_bytes() {
-  return VK == 0 ? D * 4 : (VK == 1 ? D * 2 : D);
+  return VK == 0 ? D * 4 : (VK == 1 ? D * 2 : (VK == 2 ? D : D / 2));
 }
 
 
@@ -713,7 +713,7 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
       list[e] = ent;
     }
     const float inv_z = __builtin_amdgcn_rcpf(wave_sum_f32(z));
-    if (VK == 2) {
+    if (VK >= 2) {
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       for (int e = lane; e < keep; e += 64) {
         const float p = __builtin_bit_cast(float, list[e].y) * inv_z;
@@ -727,9 +727,29 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
     const int k = lane >> 3, g = lane & 7;
 #pragma unroll
     for (int cb = 0; cb < D / 64; ++cb) {
-      constexpr int EB = ROWB / D;  // bytes per V element
-      const uint8_t* const vrow0 = smem + cb * 64 * EB;
-      if (VK == 2) {
+      const uint8_t* const vrow0 = smem + cb * 64 * ROWB / D;
+      if (VK == 3) {
+        // 4-bit V: the lane's eight channels are eight two's-complement nibbles of one word
+        int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int t = 0; t < a.lcap; t += 32) {
+          uint2 ent[4];
+          uint32_t raw[4];
+#pragma unroll
+          for (int u4 = 0; u4 < 4; ++u4) ent[u4] = list[t + 8 * u4 + k];
+#pragma unroll
+          for (int u4 = 0; u4 < 4; ++u4) raw[u4] = *reinterpret_cast<const uint32_t*>(vrow0 + ent[u4].x * ROWB + g * 4);
+#pragma unroll
+          for (int u4 = 0; u4 < 4; ++u4) {
+            const int aq8 = (int)ent[u4].y;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[c] += aq8 * nibble_s4(raw[u4], c);
+          }
+        }
+        const int tot = reduce_scatter8<int>(acc, k);
+        const int ch = cb * 64 + 8 * g + k;
+        const float sc = a.vscale[(size_t)bh * D + ch];
+        a.out[row * D + ch] = __fdiv_rn(__fmul_rn((float)tot, sc), 255.0f);
+      } else if (VK == 2) {
         int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         for (int t = 0; t < a.lcap; t += 32) {
           uint2 ent[4], raw[4];
@@ -820,7 +840,7 @@ hipError_t launch_one(const TopnKArgs& ka, dim3 grid, dim3 block, uint32_t lds, 
   if constexpr (FK) {
     if (ka.brow != nullptr) return launch_inst<NS, FK, VK, PAD, D, 1>(ka, grid, block, lds, s);
   }
-  if constexpr (VK != 2) {
+  if constexpr (VK < 2) {
     if (ka.xk != nullptr) return launch_inst<NS, FK, VK, PAD, D, 2>(ka, grid, block, lds, s);
   }
   return launch_inst<NS, FK, VK, PAD, D, 0>(ka, grid, block, lds, s);
@@ -837,7 +857,8 @@ hipError_t launch_vk(const TopnKArgs& ka, int vk, bool pad, dim3 grid, dim3 bloc
   switch (vk) {
     case 0: return launch_pad<NS, FK, 0, D>(ka, pad, grid, block, lds, s);
     case 1: return launch_pad<NS, FK, 1, D>(ka, pad, grid, block, lds, s);
-    default: return launch_pad<NS, FK, 2, D>(ka, pad, grid, block, lds, s);
+    case 2: return launch_pad<NS, FK, 2, D>(ka, pad, grid, block, lds, s);
+    default: return launch_pad<NS, FK, 3, D>(ka, pad, grid, block, lds, s);
   }
 }
 
@@ -879,7 +900,7 @@ hipError_t launch_topn(const AttnParams& p, hipStream_t s) {
                   p.d != 64 || (fused && p.mean);
   if (fused && p.mean && p.n > 256) return hipErrorInvalidValue;
   const int vk = p.v_kind;
-  const int rowb = (int)p.d * (vk == 0 ? 4 : (vk == 1 ? 2 : 1));
+  const int rowb = vk == 3 ? (int)p.d / 2 : (int)p.d * (vk == 0 ? 4 : (vk == 1 ? 2 : 1));
   TopnKArgs ka{};
   ka.qbits = p.qbits;
   ka.kbits = p.kbits;

@@ -69,9 +69,21 @@ struct Lds {
 static_assert(Lds<128, 16>::kTotal <= 160 * 1024, "LDS");
 static_assert(2 * Lds<128, 8>::kTotal <= 160 * 1024, "LDS: two workgroups of eight waves per CU");
 
+// Byte transpose of four words: byte k of out[m] is byte m of in[k].
+HAD_DEVICE void transpose_bytes4(const uint32_t (&in)[4], uint32_t (&out)[4]) {
+  const uint32_t lo01 = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);  // in0.b0 in1.b0 in0.b1 in1.b1
+  const uint32_t hi01 = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);  // in0.b2 in1.b2 in0.b3 in1.b3
+  const uint32_t lo23 = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);
+  const uint32_t hi23 = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);
+  out[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+  out[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+  out[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+}
+
 template <int VK, int D>
 constexpr int row_bytes() {
-  return VK == 0 ? D * 4 : (VK == 1 ? D * 2 : D);
+  return VK == 0 ? D * 4 : (VK == 1 ? D * 2 : (VK == 2 ? D : D / 2));
 }
 
 // Exact top-`keep` of the first `cnt` buffer entries (entry order = key order),
@@ -546,7 +558,7 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
   for (int e = lane; e < a.lcap; e += 64) {
     uint2 ent = e < cnt ? buf[e] : make_uint2(0u, 0u);
     const float p = __builtin_bit_cast(float, ent.x) * inv_z;
-    if (VK == 2) {
+    if (VK >= 2) {
       const float qv = fminf(fmaxf(rintf(255.0f * p), 0.0f), 255.0f);
       ent.x = e < cnt ? (uint32_t)qv : 0u;
       asum += (int)ent.x;
@@ -600,6 +612,65 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
         for (int c = 0; c < 4; ++c) {
           const int ch = cb * 64 + c4 + c;
           const int tot = (int)(acc[c] - 128u * (uint32_t)total_a);
+          a.out[row * D + ch] = __fdiv_rn(__fmul_rn((float)tot, a.vscale[(size_t)bh * D + ch]), 255.0f);
+        }
+      }
+    }
+    return;
+  }
+
+  if constexpr (VK == 3) {
+    // ---- 4-bit V: a row is D / 2 bytes of two's-complement nibbles (byte b: channel 2b
+    // low, 2b + 1 high).  Lane (key slot ks = lane / 8, channels c8 .. c8 + 7, c8 =
+    // 8 (lane % 8)) takes four kept keys per step, 32 keys per step over the wave, with
+    // one 32-bit read per key for its eight channels.  Each nibble xor 8 is V_q + 8 in
+    // [1, 15]; masked into the bytes of the even and of the odd channels and
+    // byte-transposed into one word per channel, it multiplies the packed A_q with
+    // v_dot4_u32_u8: sum A_q V_q + 8 sum A_q, exact in 32 bits (255 * 15 * 704 < 2^32).
+    const int total_a = wave_sum_i32(asum);
+    const int c8 = 8 * (lane & 7), ks = lane >> 3;
+#pragma unroll
+    for (int cb = 0; cb < D / 64; ++cb) {
+      const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + (size_t)bh * n * ROWB + cb * 32 + c8 / 2;
+      uint32_t acc[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+      // (the list holds lcap entries, a multiple of 32, zero past the kept ones; two steps
+      // per iteration put eight row reads of each lane in flight)
+#pragma unroll 2
+      for (int t = 0; t < a.lcap; t += 32) {
+        const uint4 e01 = *reinterpret_cast<const uint4*>(buf + t + 4 * ks);
+        const uint4 e23 = *reinterpret_cast<const uint4*>(buf + t + 4 * ks + 2);
+        uint32_t w[4];
+        w[0] = *reinterpret_cast<const uint32_t*>(vbase + (size_t)e01.y * ROWB) ^ 0x88888888u;
+        w[1] = *reinterpret_cast<const uint32_t*>(vbase + (size_t)e01.w * ROWB) ^ 0x88888888u;
+        w[2] = *reinterpret_cast<const uint32_t*>(vbase + (size_t)e23.y * ROWB) ^ 0x88888888u;
+        w[3] = *reinterpret_cast<const uint32_t*>(vbase + (size_t)e23.w * ROWB) ^ 0x88888888u;
+        const uint32_t a4 = e01.x | (e01.z << 8) | (e23.x << 16) | (e23.z << 24);
+        uint32_t ev[4], od[4];  // byte b: channel c8 + 2b (ev) or c8 + 2b + 1 (od) of key k
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          ev[kk] = w[kk] & 0x0f0f0f0fu;
+          od[kk] = (w[kk] >> 4) & 0x0f0f0f0fu;
+        }
+        uint32_t te[4], to[4];  // word m: the four keys' bytes of channel c8 + 2m (te), c8 + 2m + 1 (to)
+        transpose_bytes4(ev, te);
+        transpose_bytes4(od, to);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          acc[2 * m] = __builtin_amdgcn_udot4(a4, te[m], acc[2 * m], false);
+          acc[2 * m + 1] = __builtin_amdgcn_udot4(a4, to[m], acc[2 * m + 1], false);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        acc[c] += (uint32_t)__shfl_xor((int)acc[c], 8, 64);
+        acc[c] += (uint32_t)__shfl_xor((int)acc[c], 16, 64);
+        acc[c] += (uint32_t)__shfl_xor((int)acc[c], 32, 64);
+      }
+      if (ks == 0) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int ch = cb * 64 + c8 + c;
+          const int tot = (int)(acc[c] - 8u * (uint32_t)total_a);
           a.out[row * D + ch] = __fdiv_rn(__fmul_rn((float)tot, a.vscale[(size_t)bh * D + ch]), 255.0f);
         }
       }
@@ -707,7 +778,8 @@ hipError_t launch_d(const StreamKArgs& ka, int vk, int64_t BH, hipStream_t s) {
   switch (vk) {
     case 0: return launch_w<0, D>(ka, BH, s);
     case 1: return launch_w<1, D>(ka, BH, s);
-    default: return launch_w<2, D>(ka, BH, s);
+    case 2: return launch_w<2, D>(ka, BH, s);
+    default: return launch_w<3, D>(ka, BH, s);
   }
 }
 
@@ -739,7 +811,7 @@ hipError_t launch_topn_stream(const AttnParams& p, hipStream_t s) {
   ka.H = (int)p.H;
   ka.n = (int)p.n;
   ka.keep = (int)p.keep;
-  ka.lcap = (int)((p.keep + 15) / 16 * 16);
+  ka.lcap = (int)((p.keep + 31) / 32 * 32);  // (<= kCap: keep <= kCap - 64)
   ka.isd = (float)(1.0 / sqrt((double)p.d));
   const int64_t BH = p.B * p.H;
   return p.d == 128 ? launch_d<128>(ka, p.v_kind, BH, s) : launch_d<64>(ka, p.v_kind, BH, s);

@@ -70,7 +70,7 @@ static_assert(WLds<128>::kTotal <= 160 * 1024, "LDS");
 
 template <int VK, int D>
 constexpr int row_bytes() {
-  return VK == 0 ? D * 4 : (VK == 1 ? D * 2 : D);
+  return VK == 0 ? D * 4 : (VK == 1 ? D * 2 : (VK == 2 ? D : D / 2));
 }
 
 // The bin holding the need-th largest entry of a wave's histogram of NB bins
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(64 * kW) void topn_wide_kernel(const WideKArgs a) {
     plan[npass++] = kLevel2;
     plan[npass++] = kLevel3;
   }
-  if (VK == 2) plan[npass++] = kNorm;
+  if (VK >= 2) plan[npass++] = kNorm;
   plan[npass++] = kAv;
 
   float lmax = -INFINITY;
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(64 * kW) void topn_wide_kernel(const WideKArgs a) {
   float inv_z = 0.0f;
   // A*V state: eight lanes per kept key (k = lane / 8), eight channels per lane (g)
   const int k8 = lane >> 3, g8 = lane & 7;
-  using Acc = typename std::conditional<VK == 2, int, float>::type;
+  using Acc = typename std::conditional<VK >= 2, int, float>::type;
   Acc acc[D / 64][8];
 #pragma unroll
   for (int cb = 0; cb < D / 64; ++cb)
@@ -248,7 +248,13 @@ __global__ __launch_bounds__(64 * kW) void topn_wide_kernel(const WideKArgs a) {
         const uint8_t* vr = vhead + (size_t)ent.y * ROWB;
 #pragma unroll
         for (int cb = 0; cb < D / 64; ++cb) {
-          if constexpr (VK == 2) {
+          if constexpr (VK == 3) {
+            // 4-bit V: eight two's-complement nibbles of one word
+            const uint32_t raw = *reinterpret_cast<const uint32_t*>(vr + cb * 32 + 4 * g8);
+            const int w = (int)ent.x;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[cb][c] += w * nibble_s4(raw, c);
+          } else if constexpr (VK == 2) {
             const uint2 raw = *reinterpret_cast<const uint2*>(vr + cb * 64 + 8 * g8);
             const int w = (int)ent.x;
 #pragma unroll
@@ -336,7 +342,7 @@ __global__ __launch_bounds__(64 * kW) void topn_wide_kernel(const WideKArgs a) {
             const int slot = (int)mask_rank(km);
             if (kept) {
               uint32_t wbits;
-              if constexpr (VK == 2) {
+              if constexpr (VK >= 2) {
                 wbits = (uint32_t)fminf(fmaxf(rintf(255.0f * (e * inv_z)), 0.0f), 255.0f);
               } else {
                 wbits = __builtin_bit_cast(uint32_t, e);
@@ -344,7 +350,7 @@ __global__ __launch_bounds__(64 * kW) void topn_wide_kernel(const WideKArgs a) {
               buf[cnt + slot] = make_uint2(wbits, (uint32_t)(c0 + t));
               if (a.idx != nullptr && pos + slot < keep) a.idx[row * keep + pos + slot] = c0 + t;
             }
-            if constexpr (VK != 2) zsum += e;
+            if constexpr (VK < 2) zsum += e;
             const int add = __builtin_popcountll(km);
             cnt += add;
             pos += add;
@@ -393,12 +399,12 @@ __global__ __launch_bounds__(64 * kW) void topn_wide_kernel(const WideKArgs a) {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   flush(cnt);
   float scale = 1.0f;
-  if constexpr (VK != 2) scale = 1.0f / wave_sum_f32(zsum);
+  if constexpr (VK < 2) scale = 1.0f / wave_sum_f32(zsum);
 #pragma unroll
   for (int cb = 0; cb < D / 64; ++cb) {
     const int ch = cb * 64 + 8 * g8 + k8;
     const Acc tot = fold8<Acc>(acc[cb], k8);
-    if constexpr (VK == 2) {
+    if constexpr (VK >= 2) {
       a.out[row * D + ch] = __fdiv_rn(__fmul_rn((float)tot, a.vscale[(size_t)bh * D + ch]), 255.0f);
     } else {
       a.out[row * D + ch] = tot * scale;
@@ -429,7 +435,8 @@ hipError_t launch_wide_d(const WideKArgs& ka, int vk, int64_t BH, hipStream_t s)
   switch (vk) {
     case 0: return launch_wide_vk<0, D>(ka, BH, s);
     case 1: return launch_wide_vk<1, D>(ka, BH, s);
-    default: return launch_wide_vk<2, D>(ka, BH, s);
+    case 2: return launch_wide_vk<2, D>(ka, BH, s);
+    default: return launch_wide_vk<3, D>(ka, BH, s);
   }
 }
 

@@ -1,11 +1,13 @@
 // Per-channel integer quantization of V (BinaryAttention, section 2.4: V is
 // quantized per channel to int8 because its channels can hold outliers; the
 // conclusion names 4-bit V as the next step), with L levels each side of zero,
-// L = 127 (int8) or 7 (4-bit values, stored one per byte):
+// L = 127 (int8) or 7 (4-bit values):
 //   scale[c] = max_j |V[j][c]| / L          (float32, correctly rounded)
 //   Vq[j][c] = clamp(rint(V[j][c] / scale[c]), -L, L), 0 if scale is 0
 // A streaming pass bound by HBM bandwidth: a max pass over V, then a quantize
-// pass that reads V again and writes one byte per element.
+// pass that reads V again and writes one byte per element (L = 127), or two
+// 4-bit two's-complement codes per byte (L = 7): byte b of a row holds channel
+// 2b in its low nibble and channel 2b + 1 in its high nibble.
 #include "had_device.hpp"
 #include "had_internal.h"
 #include "../../include/had.h"
@@ -82,6 +84,22 @@ __global__ __launch_bounds__(kThreads) void vscale_kernel(const float* __restric
   }
 }
 
+template <int D, int L>
+HAD_DEVICE void store_codes(int8_t* __restrict__ vq, uint32_t r, int cg, const uint32_t (&b)[8]) {
+  if constexpr (L == 7) {
+    // eight 4-bit codes in one word: nibble c is channel 8 cg + c
+    uint32_t o = 0u;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o |= (b[c] & 0xfu) << (4 * c);
+    *reinterpret_cast<uint32_t*>(vq + (size_t)r * (D / 2) + 4 * cg) = o;
+  } else {
+    uint2 o;
+    o.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    o.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+    *reinterpret_cast<uint2*>(vq + (size_t)r * D + 8 * cg) = o;
+  }
+}
+
 template <typename T, int D, int L>
 __global__ __launch_bounds__(kThreads) void vq_kernel(const T* __restrict__ v, uint32_t rows, uint32_t n,
                                                       const float* __restrict__ scale, int8_t* __restrict__ vq) {
@@ -99,10 +117,7 @@ __global__ __launch_bounds__(kThreads) void vq_kernel(const T* __restrict__ v, u
   uint32_t b[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) b[c] = quant_i8<L>(x[c], s[c], __builtin_amdgcn_rcpf(s[c]));
-  uint2 o;
-  o.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
-  o.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
-  *reinterpret_cast<uint2*>(vq + (size_t)r * D + 8 * cg) = o;
+  store_codes<D, L>(vq, r, cg, b);
 }
 
 // The quantize pass with the scales finished in the same launch: when a
@@ -142,10 +157,7 @@ __global__ __launch_bounds__(kThreads) void vq_fused_kernel(const T* __restrict_
   uint32_t b[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) b[c] = quant_i8<L>(x[c], sp[c], __builtin_amdgcn_rcpf(sp[c]));
-  uint2 o;
-  o.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
-  o.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
-  *reinterpret_cast<uint2*>(vq + (size_t)r * D + 8 * cg) = o;
+  store_codes<D, L>(vq, r, cg, b);
 }
 
 template <typename T, int D, int L>

@@ -293,9 +293,11 @@ def binattn_dense_q8_fused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mo
     return out
 
 
-def workspace_view(ws: torch.Tensor, B: int, H: int, n: int, d: int):
-    """(vq int8 [B,H,n,d], vscale f32 [B,H,d]) views of a workspace after a quantized call,
-    at the offsets the library reports (had_workspace_region)."""
+def workspace_view(ws: torch.Tensor, B: int, H: int, n: int, d: int, av_mode: int = HAD_AV_Q8):
+    """(vq, vscale f32 [B,H,d]) views of a workspace after a quantized call, at the offsets
+    the library reports (had_workspace_region).  vq is int8 [B,H,n,d] after HAD_AV_Q8, and
+    uint8 [B,H,n,d/2] after HAD_AV_Q4: two 4-bit two's-complement codes per byte, channel 2b
+    in the low nibble of byte b and channel 2b + 1 in the high nibble."""
     import ctypes
 
     lib = _lib.load()
@@ -307,6 +309,9 @@ def workspace_view(ws: torch.Tensor, B: int, H: int, n: int, d: int):
         if off.value + nb.value > ws.numel():
             raise ValueError("workspace smaller than the region it should hold")
         views.append(ws[off.value:off.value + nb.value])
-    vq = views[0].view(torch.int8).view(B, H, n, d)
+    if av_mode == HAD_AV_Q4:
+        vq = views[0][:B * H * n * (d // 2)].view(torch.uint8).view(B, H, n, d // 2)
+    else:
+        vq = views[0].view(torch.int8).view(B, H, n, d)
     sc = views[1].view(torch.float32).view(B, H, d)
     return vq, sc

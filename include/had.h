@@ -160,8 +160,11 @@ int had_pack_qk(const void* q, const void* k, int x_dtype, int64_t B, int64_t H,
  *                 each query in ascending order; NULL to skip
  *  workspace      >= had_workspace_bytes(B,H,n,d) bytes (HAD_AV_Q8 and
  *                 HAD_AV_Q4; may be NULL for HAD_AV_F32).  On return (after
- *                 the stream has run) it holds the integer V (one byte per
- *                 element) and its per-channel scales.
+ *                 the stream has run) it holds the integer V and its
+ *                 per-channel scales: HAD_AV_Q8 one int8 per element;
+ *                 HAD_AV_Q4 two 4-bit two's-complement codes per byte
+ *                 (byte b of a row: channel 2b in the low nibble, channel
+ *                 2b + 1 in the high nibble), in the same region.
  *
  *  Logit, in float32 with each operation rounded as written:
  *      t = alpha_q*alpha_k;  u = t*(d-2h);  v = u*float(1/sqrt(d));  l = v + B
@@ -170,8 +173,9 @@ int had_pack_qk(const void* q, const void* k, int x_dtype, int64_t B, int64_t H,
  *  over all n tokens, Vq = clamp(rint(V/scale_c), -127, 127),
  *  A_q = clamp(rint(255 p), 0, 255), O = float(sum A_q*Vq) * scale_c / 255.
  *  HAD_AV_Q4 (the 4-bit V that BinaryAttention's conclusion names as the next
- *  step): the same with 7 in place of 127.  gfx950 has no 4-bit integer matrix
- *  instruction, so the 4-bit codes are kept one per byte and use the int8 path.
+ *  step): the same with 7 in place of 127, the codes stored two per byte; the
+ *  kernels widen them to bytes for the 8-bit dot products (gfx950 has no
+ *  4-bit integer matrix instruction).
  */
 int had_attention_topn(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q,
                        const float* alpha_k, const float* bias_table, const void* v, int v_dtype,

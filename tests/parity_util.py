@@ -70,3 +70,22 @@ def q8_tolerance(vscale: np.ndarray, rows: np.ndarray, n: int) -> np.ndarray:
     """One int8 LSB of V per output element: the scale of its channel."""
     bh = rows // n
     return vscale.reshape(-1, vscale.shape[-1])[bh]
+
+
+def unpack_q4(packed: np.ndarray) -> np.ndarray:
+    """int8 codes [..., 2m] from bytes [..., m] that hold two 4-bit two's-complement codes
+    each (channel 2b in the low nibble of byte b, channel 2b + 1 in the high nibble)."""
+    p = packed.astype(np.uint8)
+    nib = np.stack([p & 0xF, p >> 4], axis=-1).astype(np.int8)
+    nib = np.where(nib >= 8, nib - 16, nib).astype(np.int8)
+    return nib.reshape(packed.shape[:-1] + (2 * packed.shape[-1],))
+
+
+def ws_vq(ws: torch.Tensor, B: int, H: int, n: int, d: int, av: int):
+    """(V codes int8 [B,H,n,d], scales f32 [B,H,d]) as CPU tensors from a workspace after a
+    quantized call, the 4-bit codes unpacked."""
+    vq, sc = ops.workspace_view(ws, B, H, n, d, av_mode=av)
+    vq = vq.cpu()
+    if av == synth.AV_Q4:
+        vq = torch.from_numpy(unpack_q4(vq.numpy()))
+    return vq, sc.cpu()

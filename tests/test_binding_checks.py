@@ -4,6 +4,7 @@ These run on the CPU: the argument checks take the device to compare against as 
 parameter, so CPU tensors stand in for device tensors here; the public functions
 themselves refuse host tensors outright.
 """
+import numpy as np
 import pytest
 import torch
 
@@ -136,3 +137,16 @@ def test_workspace_regions_come_from_the_library():
     vq, sc = ops.workspace_view(ws, B, H, n, d)
     assert vq.shape == (B, H, n, d) and vq.dtype == torch.int8
     assert sc.shape == (B, H, d) and sc.dtype == torch.float32
+    # 4-bit V: two codes per byte in the same region
+    vq4, _ = ops.workspace_view(ws, B, H, n, d, av_mode=ops.HAD_AV_Q4)
+    assert vq4.shape == (B, H, n, d // 2) and vq4.dtype == torch.uint8
+
+
+def test_unpack_q4_reads_two_codes_per_byte():
+    from parity_util import unpack_q4
+
+    codes = np.array([[-7, 7, 0, -1, 3, -4, 1, 2]], np.int8)
+    packed = np.array([[(int(c0) & 0xF) | ((int(c1) & 0xF) << 4) for c0, c1 in zip(codes[0, 0::2], codes[0, 1::2])]],
+                      np.uint8)
+    assert packed.tolist() == [[0x79, 0xF0, 0xC3, 0x21]]
+    assert np.array_equal(unpack_q4(packed), codes)

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from binarized_qk_sparse_amd import ops, synth
-from parity_util import assert_close, f32, q8_tolerance, rows_per_head, sample_rows
+from parity_util import assert_close, f32, q8_tolerance, rows_per_head, sample_rows, ws_vq
 
 pytestmark = pytest.mark.gpu
 
@@ -84,7 +84,7 @@ def test_topn_bias2d_quantized(av, gh, gw, cls):
     ref = oracle.attention(qb, kb, f32(v), alpha_q=aq, alpha_k=ak, bias2d=b2, top_n=256, av_mode=av, rows=rows,
                            want_idx=True)
     assert np.array_equal(idx.cpu().numpy().reshape(-1, 256)[rows], ref["idx"])
-    vq, sc = ops.workspace_view(ws, 1, 2, n, 64)
+    vq, sc = ws_vq(ws, 1, 2, n, 64, av)
     assert np.array_equal(vq.cpu().numpy(), ref["vq"]) and np.array_equal(sc.cpu().numpy(), ref["vscale"])
     diff = np.abs(out.cpu().numpy().reshape(-1, 64)[rows] - ref["out"])
     assert np.all(diff <= q8_tolerance(ref["vscale"], rows, n) + 1e-6)

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from binarized_qk_sparse_amd import ops, synth
-from parity_util import assert_close, f32, packed_inputs, q8_tolerance, rows_per_head, sample_rows, u32
+from parity_util import assert_close, f32, packed_inputs, q8_tolerance, rows_per_head, sample_rows, u32, ws_vq
 
 pytestmark = pytest.mark.gpu
 
@@ -229,7 +229,7 @@ def test_topn_q8_matches_oracle(n, N, av):
     out, idx = ops.had_attention_topn(dt(qb.view(np.int32)), dt(kb.view(np.int32)), v.to(DEV), N, alpha_q=dt(aq),
                                       alpha_k=dt(ak), bias=dt(T), av_mode=av, want_idx=True, ws=ws)
     torch.cuda.synchronize()
-    vq, sc = ops.workspace_view(ws, 2, 2, n, 64)
+    vq, sc = ws_vq(ws, 2, 2, n, 64, av)
     ref = oracle.attention(qb, kb, f32(v), alpha_q=aq, alpha_k=ak, bias=T, top_n=N, av_mode=av, want_idx=True)
     if av == synth.AV_Q4:
         assert np.abs(vq.cpu().numpy()).max() == 7
@@ -305,7 +305,7 @@ def test_topn_long_sequence_matches_oracle(n, N, keys, av):
     if av == synth.AV_F32:
         assert_close(got, ref["out"], f"long n={n} N={N}")
     else:
-        vq, sc = ops.workspace_view(ws, 1, 2, n, 64)
+        vq, sc = ws_vq(ws, 1, 2, n, 64, av)
         _check_q8(got, vq.cpu().numpy(), sc.cpu().numpy(), ref, rows, n, f"long q8 n={n}")
 
 
@@ -350,7 +350,7 @@ def test_topn_c5_full_size_sampled(name):
     ref = oracle.attention(oq, okb, f32(g["v"]), alpha_q=oaq, alpha_k=oak, bias=g["bias"].numpy(), top_n=w.top_n,
                            av_mode=w.av_mode, rows=rows, want_idx=True)
     assert np.array_equal(idx.cpu().numpy().reshape(-1, w.top_n)[rows], ref["idx"])
-    vq, sc = ops.workspace_view(ws, w.B, w.H, w.n, w.d)
+    vq, sc = ws_vq(ws, w.B, w.H, w.n, w.d, w.av_mode)
     _check_q8(out.cpu().numpy().reshape(-1, 64)[rows], vq.cpu().numpy(), sc.cpu().numpy(), ref, rows, w.n, name)
 
 
@@ -391,21 +391,22 @@ def test_topn_d128_matches_oracle(n, N, vdtype, keys):
 
 
 @pytest.mark.parametrize("n,N", [(197, 30), (512, 64), (1300, 120)])
-def test_topn_q8_d128_matches_oracle(n, N):
+@pytest.mark.parametrize("av", [synth.AV_Q8, synth.AV_Q4])
+def test_topn_q8_d128_matches_oracle(n, N, av):
     qb, kb, aq, ak, T, v = _topn_case(1, 2, n, N, torch.bfloat16, synth.MEAN_SIGN, True, seed=6, d=128)
     dt = lambda a: torch.from_numpy(a).to(DEV)
     ws = ops.workspace(1, 2, n, 128)
     out, idx = ops.had_attention_topn(dt(qb.view(np.int32)), dt(kb.view(np.int32)), v.to(DEV), N, alpha_q=dt(aq),
-                                      alpha_k=dt(ak), bias=dt(T), av_mode=ops.HAD_AV_Q8, want_idx=True, ws=ws)
+                                      alpha_k=dt(ak), bias=dt(T), av_mode=av, want_idx=True, ws=ws)
     torch.cuda.synchronize()
-    vq, sc = ops.workspace_view(ws, 1, 2, n, 128)
+    vq, sc = ws_vq(ws, 1, 2, n, 128, av)
     rows = sample_rows(2 * n, 600, n)
-    ref = oracle.attention(qb, kb, f32(v), alpha_q=aq, alpha_k=ak, bias=T, top_n=N, av_mode=oracle.AV_Q8,
+    ref = oracle.attention(qb, kb, f32(v), alpha_q=aq, alpha_k=ak, bias=T, top_n=N, av_mode=av,
                            rows=rows, want_idx=True)
     keep = min(N, n)
     assert np.array_equal(idx.cpu().numpy().reshape(-1, keep)[rows], ref["idx"])
     _check_q8(out.cpu().numpy().reshape(-1, 128)[rows], vq.cpu().numpy(), sc.cpu().numpy(), ref, rows, n,
-              f"q8 d=128 n={n}")
+              f"av={av} d=128 n={n}")
 
 
 @pytest.mark.parametrize("n", [1, 33, 197, 256])

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from binarized_qk_sparse_amd import ops, synth
-from parity_util import assert_close, f32, q8_tolerance
+from parity_util import assert_close, f32, q8_tolerance, ws_vq
 
 pytestmark = pytest.mark.gpu
 
@@ -65,8 +65,8 @@ def _run_and_check(qb, kb, aq, ak, T, v, N, av, rows, what, bias2d=None):
     if av == synth.AV_F32:
         assert_close(got, ref["out"], what)
     else:
-        vq, sc = ops.workspace_view(ws, B, H, n, d)
-        assert np.array_equal(vq.cpu().numpy(), ref["vq"]), f"{what}: int8 V differs"
+        vq, sc = ws_vq(ws, B, H, n, d, av)
+        assert np.array_equal(vq.cpu().numpy(), ref["vq"]), f"{what}: integer V differs"
         assert np.array_equal(sc.cpu().numpy(), ref["vscale"]), f"{what}: V scales differ"
         tol = q8_tolerance(ref["vscale"], rows, n)
         diff = np.abs(got - ref["out"])
@@ -112,10 +112,11 @@ def test_wide_head_dim_128(keys, vdtype):
     _run_and_check(qb, kb, aq, ak, T, v, N, synth.AV_F32, _rows(2, n, 60, 4), f"d=128 N={N} {keys}")
 
 
-def test_wide_head_dim_128_q8():
+@pytest.mark.parametrize("av", [synth.AV_Q8, synth.AV_Q4])
+def test_wide_head_dim_128_q8(av):
     n, N = 1500, 1200
     qb, kb, aq, ak, T, v = _case(1, 2, n, 128, synth.MEAN_SIGN, True, torch.bfloat16, seed=5)
-    _run_and_check(qb, kb, aq, ak, T, v, N, synth.AV_Q8, _rows(2, n, 60, 5), "d=128 q8")
+    _run_and_check(qb, kb, aq, ak, T, v, N, av, _rows(2, n, 60, 5), f"d=128 av={av}")
 
 
 @pytest.mark.parametrize("N", [705, 1500, 2999])
