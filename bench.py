@@ -38,7 +38,7 @@ sys.path.insert(0, ROOT)
 METRIC = "binarized-attention QK pairs/sec at n=1024,12 heads; % of roofline"
 VALU_PEAK = 256 * 64 * 2.4e9  # lane-slots per second: 256 CUs x 64 lanes x 2.4 GHz
 HBM_PEAK = 8.0e12
-STREAM_MAX_KEEP = 704  # most keys the streaming top-N kernel buffers per query (768 entries less one tile)
+STREAM_MAX_KEEP = 1472  # most keys the streaming top-N kernel buffers per query (1536 entries less one tile)
 
 
 def log(*a):

@@ -238,10 +238,10 @@ static int topn_impl(const uint32_t* qbits, const uint32_t* kbits, const float* 
   // above the resident limit: the streaming kernel while its candidate buffer holds
   // the kept set, the threshold-first kernel beyond
   const bool streaming = n > topn_max_n(v_kind, d);
-  const bool wide = streaming && keep > topn_stream_max_keep();
-  if (streaming && b2.row != nullptr &&
-      bias2d_floats(b2.gh, b2.gw, b2.cls != nullptr) > (wide ? topn_wide_bias2d_max() : topn_stream_bias2d_max(n)))
-    return fail(HAD_ERR_UNSUPPORTED, fn, "grid too long for the long-sequence kernel's bias tables");
+  const int64_t tab = b2.row != nullptr ? bias2d_floats(b2.gh, b2.gw, b2.cls != nullptr) : 0;
+  const bool wide = streaming && !topn_stream_takes(n, keep, tab);
+  if (wide && tab > topn_wide_bias2d_max())
+    return fail(HAD_ERR_UNSUPPORTED, fn, "grid too long for the long-sequence kernels' bias tables");
   hipStream_t s = static_cast<hipStream_t>(stream);
   AttnParams p{};
   p.qbits = qbits;

@@ -77,8 +77,9 @@ int64_t topn_resident_max_n(int v_kind, int64_t d);
 bool topn_mfma_supported(const AttnParams& p);
 hipError_t launch_topn_mfma(const AttnParams& p, hipStream_t s);
 hipError_t launch_topn_stream(const AttnParams& p, hipStream_t s);
-int64_t topn_stream_max_keep();
-int64_t topn_stream_bias2d_max(int64_t n);
+// whether the streaming kernel takes n keys, kept sets of `keep` and two-dimensional
+// bias tables of `tab` floats (0: none)
+bool topn_stream_takes(int64_t n, int64_t keep, int64_t tab);
 // top-N above the resident limit with more kept keys than the streaming kernel
 // buffers (topn_wide.hip): threshold by radix selection, then the kept keys
 hipError_t launch_topn_wide(const AttnParams& p, hipStream_t s);

@@ -30,9 +30,11 @@ namespace had {
 namespace {
 
 // head_dim D is 64 or 128 (codes of D / 32 words).  A workgroup of W waves
-// (W = 8 or 16) streams keys in LDS chunks of 128 W.
-constexpr int kCap = 768;     // candidate-buffer entries per wave
-constexpr int kR = kCap / 64;
+// (W = 8 or 16) streams keys in LDS chunks of 128 W.  Each wave's candidate buffer
+// holds CAP entries: 768 (kept sets up to 704), or 1536 for larger kept sets (up to
+// 1472; eight waves, one workgroup per CU).
+constexpr int kCapSmall = 768;
+constexpr int kCapBig = 1536;
 
 struct StreamKArgs {
   const uint32_t* qbits;
@@ -53,21 +55,22 @@ struct StreamKArgs {
   int gh, gw, cls;
 };
 
-// LDS layout (bytes) for head_dim D and W waves
-template <int D, int W>
+// LDS layout (bytes) for head_dim D, W waves and CAP buffer entries per wave
+template <int D, int W, int CAP = kCapSmall>
 struct Lds {
   static constexpr int kChunk = 128 * W;                             // keys per chunk
   static constexpr uint32_t kCodeOff = 0;                           // Code<D>[kChunk]
   static constexpr uint32_t kAkOff = kCodeOff + kChunk * (D / 8);   // float[kChunk]
   static constexpr uint32_t kBiasOff = kAkOff + kChunk * 4;         // float[kChunk + W]
-  static constexpr uint32_t kBufOff = kBiasOff + (kChunk + 64) * 4;  // uint2[W][kCap]
-  static constexpr uint32_t kCandOff = kBufOff + W * kCap * 8;      // uint2[W][64]
+  static constexpr uint32_t kBufOff = kBiasOff + (kChunk + 64) * 4;  // uint2[W][CAP]
+  static constexpr uint32_t kCandOff = kBufOff + W * CAP * 8;       // uint2[W][64]
   static constexpr int kTab = W == 16 ? 1536 : 512;                  // floats of two-dimensional bias tables
   static constexpr uint32_t kTabOff = kCandOff + W * 64 * 8;         // float[kTab]
   static constexpr uint32_t kTotal = kTabOff + kTab * 4;
 };
 static_assert(Lds<128, 16>::kTotal <= 160 * 1024, "LDS");
 static_assert(2 * Lds<128, 8>::kTotal <= 160 * 1024, "LDS: two workgroups of eight waves per CU");
+static_assert(Lds<128, 8, kCapBig>::kTotal <= 160 * 1024, "LDS: one workgroup of eight waves per CU");
 
 // Byte transpose of four words: byte k of out[m] is byte m of in[k].
 HAD_DEVICE void transpose_bytes4(const uint32_t (&in)[4], uint32_t (&out)[4]) {
@@ -90,8 +93,10 @@ constexpr int row_bytes() {
 // ties to the earlier entry.  Rewrites the buffer with the kept entries in
 // order and returns their count (min(cnt, keep)); `vstar` receives the value
 // of the worst kept entry and `lmax` the best.
+template <int CAP>
 HAD_DEVICE int select_compact(uint2* buf, uint2* cand, int cnt, int keep, int lane, float* vstar_out,
                               float* lmax_out) {
+  constexpr int kR = CAP / 64;
   float vals[kR];
 #pragma unroll
   for (int r = 0; r < kR; ++r) {
@@ -256,7 +261,9 @@ HAD_DEVICE float sample_threshold(const float (&v)[R], int m) {
 // later key with l <= t ranks below the keep kept entries at or above t (equal
 // values go to the lower key index).  Returns -1 when no such t turns up within
 // a few steps (heavy ties); the caller then runs the exact selection.
+template <int CAP>
 HAD_DEVICE int compact_approx(uint2* buf, int cnt, int keep, int lane, float* theta) {
+  constexpr int kR = CAP / 64;
   uint2 ent[kR];
   float vals[kR];
 #pragma unroll
@@ -343,14 +350,14 @@ HAD_DEVICE T reduce_scatter8(T (&acc)[8], int k) {
 
 // B2: the two-dimensional bias (a.brow != NULL), a separate instance so that the
 // 1-D path carries none of its code
-template <int VK, int D, int W, bool B2>
+template <int VK, int D, int W, int CAP, bool B2>
 __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a) {
   // 64-key groups per block of the key loop: eight at head_dim 64, two at 128 (whose
   // codes take twice the registers and LDS reads per key)
   constexpr int kG = D == 64 ? 8 : 2;
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int ROWB = row_bytes<VK, D>();
-  using L = Lds<D, W>;
+  using L = Lds<D, W, CAP>;
   constexpr int kWaves = W;
   constexpr int kChunk = L::kChunk;
   Code<D>* codes = reinterpret_cast<Code<D>*>(smem + L::kCodeOff);
@@ -359,7 +366,7 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
   float* tab = reinterpret_cast<float*>(smem + L::kTabOff);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  uint2* buf = reinterpret_cast<uint2*>(smem + L::kBufOff) + wave * kCap;
+  uint2* buf = reinterpret_cast<uint2*>(smem + L::kBufOff) + wave * CAP;
   uint2* cand = reinterpret_cast<uint2*>(smem + L::kCandOff) + wave * 64;
   const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / a.tiles, tile = wg % a.tiles, hh = bh % a.H;
@@ -435,7 +442,7 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
   int cnt = 0;
   // intermediate compactions may leave up to keep + kSlack entries when that
   // still frees room for two more groups
-  const bool approx = keep + kSlack <= kCap - 128;
+  const bool approx = keep + kSlack <= CAP - 128;
   fetch_chunk(0);
   bool sampled = false;  // theta started from the first chunk's logits
   bool redo = false;     // this row streams again from theta = -inf
@@ -448,7 +455,7 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
     __syncthreads();
     if (!live || (pass == 1 && !redo)) continue;
     const int boff = ilast - i;  // bias window index of chunk key t is t + boff
-    // Blocks of kG 64-key groups.  The buffer holds at most kCap - 64 entries
+    // Blocks of kG 64-key groups.  The buffer holds at most CAP - 64 entries
     // between groups, so one more group always fits.  Fast path (a full block
     // whose admitted keys keep that bound): kG logits with fixed LDS offsets,
     // then the kG appends.  Otherwise (a partial block, or a block that fills
@@ -493,7 +500,7 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
           m[u] = ballot(l[u] > theta);
           tot += __builtin_popcountll(m[u]);
         }
-        if (cnt + tot <= kCap - 64) {
+        if (cnt + tot <= CAP - 64) {
 #pragma unroll
           for (int u = 0; u < kG; ++u) {
             if (m[u] != 0) {
@@ -517,12 +524,12 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
         if (m != 0) {
           if (adm) buf[cnt + (int)mask_rank(m)] = make_uint2(__builtin_bit_cast(uint32_t, l), (uint32_t)(c0 + t));
           cnt += __builtin_popcountll(m);
-          if (cnt > kCap - 64) {
+          if (cnt > CAP - 64) {
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            int kept = approx ? compact_approx(buf, cnt, keep, lane, &theta) : -1;
+            int kept = approx ? compact_approx<CAP>(buf, cnt, keep, lane, &theta) : -1;
             if (kept < 0) {
               float lm;
-              kept = select_compact(buf, cand, cnt, keep, lane, &theta, &lm);
+              kept = select_compact<CAP>(buf, cand, cnt, keep, lane, &theta, &lm);
             }
             cnt = kept;
           }
@@ -543,7 +550,7 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   float lmax;
   float vs;
-  cnt = select_compact(buf, cand, cnt, keep, lane, &vs, &lmax);  // cnt == keep now
+  cnt = select_compact<CAP>(buf, cand, cnt, keep, lane, &vs, &lmax);  // cnt == keep now
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
   // ---- softmax over the kept entries (buffer order = ascending key index)
@@ -679,12 +686,13 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
   }
 
   // ---- A*V: eight lanes per kept key, eight channels per lane, rows from global memory,
-  // per block of 64 channels (head_dim 128 takes two).  Four kept keys per lane are
-  // fetched before any is used, so four row loads are in flight at once.
+  // per block of 64 channels (head_dim 128 takes two).  U kept keys per lane are
+  // fetched before any is used, so U row loads are in flight at once (eight with the
+  // larger buffers, whose kept sets are longer and whose two waves per SIMD hide less).
   const int k = lane >> 3, g = lane & 7;
   using Raw = typename std::conditional<VK == 2, uint2, typename std::conditional<VK == 1, uint4, F8>::type>::type;
   using Acc = typename std::conditional<VK == 2, int, float>::type;
-  constexpr int U = 4;
+  constexpr int U = CAP == kCapBig ? 8 : 4;
 #pragma unroll
   for (int cb = 0; cb < D / 64; ++cb) {
     const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + (size_t)bh * n * ROWB + cb * 64 * (ROWB / D);
@@ -747,51 +755,59 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
   }
 }
 
-template <int VK, int D, int W, bool B2>
+template <int VK, int D, int W, int CAP, bool B2>
 hipError_t launch_b2(StreamKArgs ka, int64_t BH, hipStream_t s) {
-  constexpr uint32_t lds = Lds<D, W>::kTotal;
+  constexpr uint32_t lds = Lds<D, W, CAP>::kTotal;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&topn_stream_kernel<VK, D, W, B2>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)lds);
+      reinterpret_cast<const void*>(&topn_stream_kernel<VK, D, W, CAP, B2>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
   ka.tiles = (ka.n + W - 1) / W;
   const dim3 grid((unsigned)(BH * ka.tiles));
-  hipLaunchKernelGGL((topn_stream_kernel<VK, D, W, B2>), grid, dim3(64 * W), lds, s, ka);
+  hipLaunchKernelGGL((topn_stream_kernel<VK, D, W, CAP, B2>), grid, dim3(64 * W), lds, s, ka);
   return hipGetLastError();
 }
 
-template <int VK, int D, int W>
+template <int VK, int D, int W, int CAP>
 hipError_t launch_vk(const StreamKArgs& ka, int64_t BH, hipStream_t s) {
-  return ka.brow != nullptr ? launch_b2<VK, D, W, true>(ka, BH, s) : launch_b2<VK, D, W, false>(ka, BH, s);
+  return ka.brow != nullptr ? launch_b2<VK, D, W, CAP, true>(ka, BH, s) : launch_b2<VK, D, W, CAP, false>(ka, BH, s);
 }
 
-// Sixteen waves per workgroup (one per CU) for the longest sequences, where the
-// larger chunks halve the key traffic into LDS; eight (two workgroups per CU)
-// below, where the two workgroups' selection and A*V tails overlap.
+// Whether the 768-entry buffers take the kept set and the two-dimensional tables
+// (floats; 0 without them).
+bool small_cap_fits(int64_t n, int64_t keep, int64_t tab) {
+  return keep <= kCapSmall - 64 && tab <= (n > 4096 ? Lds<64, 16>::kTab : Lds<64, 8>::kTab);
+}
+
+// 768-entry buffers: sixteen waves per workgroup (one per CU) for the longest
+// sequences, where the larger chunks halve the key traffic into LDS; eight (two
+// workgroups per CU) below, where the two workgroups' selection and A*V tails overlap.
+// Larger kept sets: 1536-entry buffers at eight waves (one workgroup per CU).
 template <int VK, int D>
-hipError_t launch_w(const StreamKArgs& ka, int64_t BH, hipStream_t s) {
-  return ka.n > 4096 ? launch_vk<VK, D, 16>(ka, BH, s) : launch_vk<VK, D, 8>(ka, BH, s);
+hipError_t launch_w(const StreamKArgs& ka, int64_t tab, int64_t BH, hipStream_t s) {
+  if (!small_cap_fits(ka.n, ka.keep, tab)) return launch_vk<VK, D, 8, kCapBig>(ka, BH, s);
+  return ka.n > 4096 ? launch_vk<VK, D, 16, kCapSmall>(ka, BH, s) : launch_vk<VK, D, 8, kCapSmall>(ka, BH, s);
 }
 
 template <int D>
-hipError_t launch_d(const StreamKArgs& ka, int vk, int64_t BH, hipStream_t s) {
+hipError_t launch_d(const StreamKArgs& ka, int vk, int64_t tab, int64_t BH, hipStream_t s) {
   switch (vk) {
-    case 0: return launch_w<0, D>(ka, BH, s);
-    case 1: return launch_w<1, D>(ka, BH, s);
-    case 2: return launch_w<2, D>(ka, BH, s);
-    default: return launch_w<3, D>(ka, BH, s);
+    case 0: return launch_w<0, D>(ka, tab, BH, s);
+    case 1: return launch_w<1, D>(ka, tab, BH, s);
+    case 2: return launch_w<2, D>(ka, tab, BH, s);
+    default: return launch_w<3, D>(ka, tab, BH, s);
   }
 }
 
 }  // namespace
 
-int64_t topn_stream_max_keep() { return kCap - 64; }
-
-// Largest two-dimensional bias tables (floats) the kernel stages for sequences of n keys.
-int64_t topn_stream_bias2d_max(int64_t n) { return n > 4096 ? Lds<64, 16>::kTab : Lds<64, 8>::kTab; }
+bool topn_stream_takes(int64_t n, int64_t keep, int64_t tab) {
+  return small_cap_fits(n, keep, tab) || (keep <= kCapBig - 64 && tab <= Lds<64, 8, kCapBig>::kTab);
+}
 
 hipError_t launch_topn_stream(const AttnParams& p, hipStream_t s) {
-  if ((p.d != 64 && p.d != 128) || p.keep > topn_stream_max_keep()) return hipErrorInvalidValue;
+  const int64_t tab = p.brow != nullptr ? bias2d_floats(p.gh, p.gw, p.cls) : 0;
+  if ((p.d != 64 && p.d != 128) || !topn_stream_takes(p.n, p.keep, tab)) return hipErrorInvalidValue;
   StreamKArgs ka{};
   ka.qbits = p.qbits;
   ka.kbits = p.kbits;
@@ -811,10 +827,10 @@ hipError_t launch_topn_stream(const AttnParams& p, hipStream_t s) {
   ka.H = (int)p.H;
   ka.n = (int)p.n;
   ka.keep = (int)p.keep;
-  ka.lcap = (int)((p.keep + 31) / 32 * 32);  // (<= kCap: keep <= kCap - 64)
+  ka.lcap = (int)((p.keep + 31) / 32 * 32);  // (<= CAP: keep <= CAP - 64)
   ka.isd = (float)(1.0 / sqrt((double)p.d));
   const int64_t BH = p.B * p.H;
-  return p.d == 128 ? launch_d<128>(ka, p.v_kind, BH, s) : launch_d<64>(ka, p.v_kind, BH, s);
+  return p.d == 128 ? launch_d<128>(ka, p.v_kind, tab, BH, s) : launch_d<64>(ka, p.v_kind, tab, BH, s);
 }
 
 }  // namespace had

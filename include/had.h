@@ -219,7 +219,7 @@ int binattn_dense_q8(const uint32_t* qbits, const uint32_t* kbits, const float* 
  * HAD_ERR_UNSUPPORTED: grid_h or grid_w above 13000, or tables of
  * (2*grid_h-1)+(2*grid_w-1) floats (5*(grid_h+grid_w)-2 with a class token) above
  * what the kernel keeps on chip beside its key tiles: 1536 for top-N above the
- * resident limit (512 for n <= 4096), 4096 for the dense entry point above 256
+ * resident limit, 4096 for the dense entry point above 256
  * tokens.
  */
 int had_attention_topn_2d(const uint32_t* qbits, const uint32_t* kbits, const float* alpha_q,

@@ -1,6 +1,7 @@
-"""GPU parity of had_attention_topn for long sequences with large kept sets (the
-threshold-first kernel: more kept keys than the streaming kernel buffers, up to
-every key).
+"""GPU parity of had_attention_topn for long sequences with large kept sets: the
+streaming kernel with its larger candidate buffers (kept sets of 705 to 1472 keys)
+and the threshold-first kernel beyond (up to every key, and two-dimensional tables
+the streaming buffers leave no room for).
 
 Bar: kept index sets bit-exact (ties to the lower key index); fp32 outputs within
 1e-3 relative + 1e-4 absolute; the quantized paths within one int8 LSB of V per
@@ -86,7 +87,7 @@ def test_wide_every_key_kept(N, keys, av):
     assert np.all(idx.cpu().numpy() == np.arange(n))
 
 
-@pytest.mark.parametrize("av", [synth.AV_F32, synth.AV_Q8])
+@pytest.mark.parametrize("av", [synth.AV_F32, synth.AV_Q8, synth.AV_Q4])
 @pytest.mark.parametrize("keys", ["int", "bias", "alpha_bias"])
 def test_wide_hads_linear_schedule_at_8192(keys, av):
     # N = 15 n / 128 = 960 at n = 8192 (the linear schedule carried to long contexts)
@@ -101,6 +102,29 @@ def test_wide_past_the_streaming_buffer(n, N):
     # kept sets just past the streaming kernel's buffer, and up to one short of every key
     qb, kb, aq, ak, T, v = _case(1, 2, n, 64, synth.MEAN_SIGN, True, torch.bfloat16, seed=3)
     _run_and_check(qb, kb, aq, ak, T, v, N, synth.AV_F32, _rows(2, n, 60, 3), f"N={N} n={n}")
+
+
+@pytest.mark.parametrize("n,N", [(3000, 1472), (3000, 1473), (9000, 1472), (9000, 1473)])
+@pytest.mark.parametrize("av", [synth.AV_F32, synth.AV_Q4])
+def test_wide_at_the_larger_buffer(n, N, av):
+    # the largest kept set the streaming kernel's larger buffers take, and one more (the
+    # threshold-first kernel), below and above the sixteen-wave length
+    qb, kb, aq, ak, T, v = _case(1, 2, n, 64, synth.MEAN_SIGN, True, torch.bfloat16, seed=8)
+    _run_and_check(qb, kb, aq, ak, T, v, N, av, _rows(2, n, 40, 8), f"N={N} n={n} av={av}")
+
+
+def test_wide_bias2d_tables_past_the_streaming_limit():
+    # a 60 x 60 grid with a class token (3601 keys): its staged tables (598 floats) exceed
+    # what the streaming kernel keeps beside eight-wave chunks, so the threshold-first
+    # kernel takes the row even with a kept set the streaming buffers would hold
+    gh = gw = 60
+    n, N, H = gh * gw + 1, 500, 2
+    qb, kb, aq, ak, _, v = _case(1, H, n, 64, synth.MEAN_SIGN, False, torch.bfloat16, seed=9)
+    g = np.random.default_rng(66)
+    b2 = {"grid": (gh, gw), "row": (0.02 * g.standard_normal((H, 2 * gh - 1))).astype(np.float32),
+          "col": (0.02 * g.standard_normal((H, 2 * gw - 1))).astype(np.float32),
+          "cls": (0.02 * g.standard_normal((H, 3))).astype(np.float32)}
+    _run_and_check(qb, kb, aq, ak, None, v, N, synth.AV_F32, _rows(H, n, 60, 9), "2-D bias 60x60", bias2d=b2)
 
 
 @pytest.mark.parametrize("vdtype", [torch.float32, torch.bfloat16])
