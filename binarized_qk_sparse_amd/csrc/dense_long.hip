@@ -418,7 +418,7 @@ __global__ __launch_bounds__(256) void dense_long_kernel(const DenseLongArgs a) 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int orow = i0 + 16 * wave + 4 * kg + r;
-      if (orow < n) a.out[(hb + orow) * D + c] = __fdiv_rn(__fmul_rn((float)(acc[nt][r] + cs128), sc), 255.0f);
+      if (orow < n) a.out[(hb + orow) * D + c] = div255_rn(__fmul_rn((float)(acc[nt][r] + cs128), sc));
     }
   }
 }

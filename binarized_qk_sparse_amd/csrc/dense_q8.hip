@@ -524,7 +524,9 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
     for (int ks = 0; ks < NK; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float ex = exp2f(__builtin_fmaf(lg[ks][e], log2e, -mb));
+        // (v_exp_f32 alone: the argument is a logit minus the row maximum, so a result
+        // below 2^-126 that flushes to 0 is negligible beside the maximum's own 1)
+        const float ex = __builtin_amdgcn_exp2f(__builtin_fmaf(lg[ks][e], log2e, -mb));
         lg[ks][e] = ex;
         z += ex;
       }
@@ -561,7 +563,7 @@ __global__ __launch_bounds__(256) void dense_q8_kernel(const DenseKArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int orow = tile * 16 + 4 * kg + r;
         if (orow < n)
-          a.out[((size_t)bh * n + orow) * D + c] = __fdiv_rn(__fmul_rn((float)(acc[nt][r] + cs), sc), 255.0f);
+          a.out[((size_t)bh * n + orow) * D + c] = div255_rn(__fmul_rn((float)(acc[nt][r] + cs), sc));
       }
     }
   }

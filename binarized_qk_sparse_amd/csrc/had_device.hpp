@@ -184,6 +184,18 @@ HAD_DEVICE uint32_t quant_i8(float x, float s, float inv) {
   return (uint32_t)((int32_t)r) & 0xffu;
 }
 
+// x / 255 rounded to nearest even, as __fdiv_rn(x, 255.0f) gives it, in three
+// operations: q0 = fl(x * y) with y = fl(1 / 255), the exact remainder
+// r = fma(-q0, 255, x), and q = fma(r, y, q0).  Checked against IEEE division for
+// every finite float, denormals included (the identity holds for this divisor; it
+// is not a general division).
+HAD_DEVICE float div255_rn(float x) {
+  constexpr float y = 1.0f / 255.0f;
+  const float q0 = __fmul_rn(x, y);
+  const float r = __builtin_fmaf(-q0, 255.0f, x);
+  return __builtin_fmaf(r, y, q0);
+}
+
 // Channel c (0..7) of a word of eight 4-bit two's-complement codes (nibble c),
 // sign-extended.
 HAD_DEVICE int nibble_s4(uint32_t w, int c) { return (int)(w << (28 - 4 * c)) >> 28; }

@@ -748,7 +748,7 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
         const int tot = reduce_scatter8<int>(acc, k);
         const int ch = cb * 64 + 8 * g + k;
         const float sc = a.vscale[(size_t)bh * D + ch];
-        a.out[row * D + ch] = __fdiv_rn(__fmul_rn((float)tot, sc), 255.0f);
+        a.out[row * D + ch] = div255_rn(__fmul_rn((float)tot, sc));
       } else if (VK == 2) {
         int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         for (int t = 0; t < a.lcap; t += 32) {
@@ -770,7 +770,7 @@ __global__ __launch_bounds__(1024) void topn_resident_kernel(const TopnKArgs a) 
         const int tot = reduce_scatter8<int>(acc, k);
         const int ch = cb * 64 + 8 * g + k;
         const float sc = a.vscale[(size_t)bh * D + ch];
-        a.out[row * D + ch] = __fdiv_rn(__fmul_rn((float)tot, sc), 255.0f);
+        a.out[row * D + ch] = div255_rn(__fmul_rn((float)tot, sc));
       } else {
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         // four entries per group in flight: their list reads, then their row reads, then the math

@@ -619,7 +619,7 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
         for (int c = 0; c < 4; ++c) {
           const int ch = cb * 64 + c4 + c;
           const int tot = (int)(acc[c] - 128u * (uint32_t)total_a);
-          a.out[row * D + ch] = __fdiv_rn(__fmul_rn((float)tot, a.vscale[(size_t)bh * D + ch]), 255.0f);
+          a.out[row * D + ch] = div255_rn(__fmul_rn((float)tot, a.vscale[(size_t)bh * D + ch]));
         }
       }
     }
@@ -678,7 +678,7 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
         for (int c = 0; c < 8; ++c) {
           const int ch = cb * 64 + c8 + c;
           const int tot = (int)(acc[c] - 8u * (uint32_t)total_a);
-          a.out[row * D + ch] = __fdiv_rn(__fmul_rn((float)tot, a.vscale[(size_t)bh * D + ch]), 255.0f);
+          a.out[row * D + ch] = div255_rn(__fmul_rn((float)tot, a.vscale[(size_t)bh * D + ch]));
         }
       }
     }
@@ -748,7 +748,7 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
     if constexpr (VK == 2) {
       const int tot = reduce_scatter8<int>(acc, k);
       const int ch = cb * 64 + 8 * g + k;
-      a.out[row * D + ch] = __fdiv_rn(__fmul_rn((float)tot, a.vscale[(size_t)bh * D + ch]), 255.0f);
+      a.out[row * D + ch] = div255_rn(__fmul_rn((float)tot, a.vscale[(size_t)bh * D + ch]));
     } else {
       a.out[row * D + cb * 64 + 8 * g + k] = reduce_scatter8<float>(acc, k);
     }

@@ -405,7 +405,7 @@ __global__ __launch_bounds__(64 * kW) void topn_wide_kernel(const WideKArgs a) {
     const int ch = cb * 64 + 8 * g8 + k8;
     const Acc tot = fold8<Acc>(acc[cb], k8);
     if constexpr (VK >= 2) {
-      a.out[row * D + ch] = __fdiv_rn(__fmul_rn((float)tot, a.vscale[(size_t)bh * D + ch]), 255.0f);
+      a.out[row * D + ch] = div255_rn(__fmul_rn((float)tot, a.vscale[(size_t)bh * D + ch]));
     } else {
       a.out[row * D + ch] = tot * scale;
     }
