@@ -398,11 +398,15 @@ def main():
         if args.fused:
             print("--fused takes the 1-D bias table only", file=sys.stderr)
             sys.exit(2)
+    # plain sign codes: no scales or means to write (the attention call takes alpha = 1)
+    pmq = mq.data_ptr() if w.mode == 1 else None
+    pmk = mk.data_ptr() if w.mode == 1 else None
+
     def pack():
         s = torch.cuda.current_stream().cuda_stream  # the capture stream while a graph records
         ops._lib.check("had_pack_qk", lib.had_pack_qk(q.data_ptr(), k.data_ptr(), dt, w.B, w.H, w.n, w.d, w.mode,
-                                                      qb.data_ptr(), kb.data_ptr(), aq.data_ptr(), ak.data_ptr(),
-                                                      mq.data_ptr(), mk.data_ptr(), ws.data_ptr(), ws.numel(), s))
+                                                      qb.data_ptr(), kb.data_ptr(), pa, pk, pmq, pmk, ws.data_ptr(),
+                                                      ws.numel(), s))
 
     def attend():
         s = torch.cuda.current_stream().cuda_stream
