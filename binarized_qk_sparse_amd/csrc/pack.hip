@@ -173,6 +173,108 @@ __global__ __launch_bounds__(kThreads) void pack_rows_kernel(const Sets S, uint3
   if (part == 0 && S.alpha[set] != nullptr) S.alpha[set][r] = MEAN ? (float)(asum / (double)D) : 1.0f;
 }
 
+// MEAN_SIGN for heads of one column-sum chunk (n <= kPackChunk): one workgroup per
+// (tensor, head) reads the head's rows into LDS once, then takes the column sums in the
+// thread layout and order of colsum_partial_kernel, finishes mu as the row pass does,
+// and runs the row pass of pack_rows_kernel from LDS (same lanes, same order), so the
+// codes, alpha and mu are the same bits as the two-pass route with half the HBM reads.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void pack_head_kernel(const Sets S, uint32_t BH, uint32_t n) {
+  constexpr int TPR = D / 8;           // column pass: threads per token row
+  constexpr int RPP = kThreads / TPR;  // rows per pass
+  constexpr int LPR = D / 32;          // row pass: lanes per token row
+  constexpr int RPW = kThreads / LPR;  // rows per pass
+  extern __shared__ __align__(16) uint8_t smem[];
+  const uint32_t xbytes = (n * D * (uint32_t)sizeof(T) + 15u) & ~15u;
+  T* xs = reinterpret_cast<T*>(smem);                             // [n][D]
+  double* red = reinterpret_cast<double*>(smem + xbytes);         // [RPP][D]
+  float* mus = reinterpret_cast<float*>(red + RPP * D);           // [D]
+  const int set = (int)(blockIdx.x / BH);
+  const size_t bh = blockIdx.x % BH;
+  const int tid = threadIdx.x;
+  {
+    const uint8_t* src = static_cast<const uint8_t*>(S.x[set]) + bh * n * D * sizeof(T);
+    const uint32_t total = n * D * (uint32_t)sizeof(T);  // a multiple of 16 (D * sizeof(T) >= 64)
+    // eight 16-byte loads per thread in flight before their stores
+    constexpr uint32_t kStep = kThreads * 16u;
+    for (uint32_t base = (uint32_t)tid * 16u; base < total; base += 8u * kStep) {
+      uint4 w[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t o = base + k * kStep;
+        w[k] = o < total ? *reinterpret_cast<const uint4*>(src + o) : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t o = base + k * kStep;
+        if (o < total) *reinterpret_cast<uint4*>(smem + o) = w[k];
+      }
+    }
+  }
+  __syncthreads();
+  {
+    const int r_off = tid / TPR, cg = tid % TPR;
+    double sm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int k = 0; k < kPackChunk / RPP; ++k) {
+      const uint32_t r = (uint32_t)(r_off + RPP * k);
+      if (r < n) {
+        float v[8];
+        load8<T>(xs + (size_t)r * D + 8 * cg, v);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) sm[c] += (double)v[c];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) red[r_off * D + 8 * cg + c] = sm[c];
+  }
+  __syncthreads();
+  if (tid < D) {
+    double part = 0.0;  // the chunk's partial, as colsum_partial_kernel forms it
+    for (int rp = 0; rp < RPP; ++rp) part += red[rp * D + tid];
+    double acc = 0.0;  // the sum over the (one) chunk, as the row pass finishes it
+    acc += part;
+    const float m = (float)(acc / (double)n);
+    mus[tid] = m;
+    S.mu[set][bh * D + tid] = m;
+  }
+  __syncthreads();
+  for (uint32_t r0 = 0; r0 < n; r0 += RPW) {
+    const uint32_t r = r0 + (uint32_t)tid / LPR, part = (uint32_t)tid % LPR;
+    const bool live = r < n;
+    const uint32_t rr = live ? r : n - 1;
+    float v[32];
+    const T* src = xs + (size_t)rr * D + 32 * part;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float e[8];
+      load8<T>(src + 8 * k, e);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v[8 * k + c] = e[c];
+    }
+    double asum = 0.0;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) v[c] = __fsub_rn(v[c], mus[32 * part + c]);
+#pragma unroll
+    for (int c = 0; c < 32; ++c) asum += fabs((double)v[c]);
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) asum += __shfl_xor(asum, off, 64);
+    uint32_t w = 0;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) w |= (uint32_t)(v[c] < 0.0f) << c;
+    if (live) {
+      const size_t row = bh * n + r;
+      S.bits[set][row * (D / 32) + part] = w;
+      if (part == 0) S.alpha[set][row] = (float)(asum / (double)D);
+    }
+  }
+}
+
+// LDS bytes of pack_head_kernel for n tokens
+template <typename T, int D>
+uint32_t pack_head_lds(int64_t n) {
+  return (uint32_t)(((n * D * (int64_t)sizeof(T) + 15) & ~(int64_t)15) + (int64_t)(kThreads / (D / 8)) * D * 8 + D * 4);
+}
+
 template <typename T, int D>
 hipError_t launch_typed(const PackParams& p, hipStream_t s) {
   Sets S{};
@@ -186,6 +288,17 @@ hipError_t launch_typed(const PackParams& p, hipStream_t s) {
   const unsigned cnt = (unsigned)p.count;
   const int64_t rows = p.BH * p.n;
   const int64_t threads = rows * (D / 32);
+  if (p.mode == HAD_MEAN_SIGN && p.n <= kPackChunk) {
+    // one chunk per head: one pass over x, from LDS
+    const uint32_t lds = pack_head_lds<T, D>(p.n);
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&pack_head_kernel<T, D>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       (int)pack_head_lds<T, D>(kPackChunk));
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((pack_head_kernel<T, D>), dim3(cnt * (unsigned)p.BH), dim3(kThreads), lds, s, S,
+                       (uint32_t)p.BH, (uint32_t)p.n);
+    return hipGetLastError();
+  }
   if (p.mode == HAD_MEAN_SIGN) {
     const unsigned per = (unsigned)((threads + kThreads - 1) / kThreads);
     const int64_t chunks = pack_chunks(p.n);
