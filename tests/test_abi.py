@@ -80,6 +80,7 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
     (dict(d=48), _lib.HAD_ERR_UNSUPPORTED),
     (dict(d=256), _lib.HAD_ERR_UNSUPPORTED),
     (dict(n=70000), _lib.HAD_ERR_UNSUPPORTED),
+    (dict(n=65537), _lib.HAD_ERR_UNSUPPORTED),
     (dict(mode=1, alpha=None), _lib.HAD_ERR_INVALID_ARG),
     (dict(mode=1, ws=None), _lib.HAD_ERR_WORKSPACE),
     (dict(mode=1, wsz=16), _lib.HAD_ERR_WORKSPACE),
@@ -125,6 +126,7 @@ def test_pack_qk_validation(args, want):
     (dict(d=32), _lib.HAD_ERR_UNSUPPORTED),
     (dict(d=256), _lib.HAD_ERR_UNSUPPORTED),
     (dict(n=1 << 20), _lib.HAD_ERR_UNSUPPORTED),
+    (dict(n=65537), _lib.HAD_ERR_UNSUPPORTED),
     (dict(av=1, ws=None), _lib.HAD_ERR_WORKSPACE),
     (dict(av=1, wsz=100), _lib.HAD_ERR_WORKSPACE),
     (dict(av=1, ws=ctypes.c_void_p(0x1001)), _lib.HAD_ERR_WORKSPACE),
@@ -143,6 +145,7 @@ def test_attention_validation(args, want):
     (dict(k=None), _lib.HAD_ERR_INVALID_ARG),
     (dict(n=0), _lib.HAD_ERR_INVALID_ARG),
     (dict(d=32), _lib.HAD_ERR_UNSUPPORTED),
+    (dict(n=65537), _lib.HAD_ERR_UNSUPPORTED),
     (dict(ws=None), _lib.HAD_ERR_WORKSPACE),
     (dict(wsz=0), _lib.HAD_ERR_WORKSPACE),
 ])

@@ -179,3 +179,13 @@ def test_wide_bias2d():
           "cls": (0.02 * g.standard_normal((H, 3))).astype(np.float32)}
     for av in (synth.AV_F32, synth.AV_Q8):
         _run_and_check(qb, kb, aq, ak, None, v, N, av, _rows(H, n, 60, 7), f"2-D bias av={av}", bias2d=b2)
+
+
+@pytest.mark.parametrize("N,av", [(256, synth.AV_Q8), (256, synth.AV_F32), (1000, synth.AV_Q4), (3000, synth.AV_F32)])
+def test_topn_maximum_length(N, av):
+    # n = 65536, the largest the library takes: the streaming kernel (768- and 1536-entry
+    # buffers) and the threshold-first kernel, one head, the first, middle and last rows
+    n = 65536
+    qb, kb, aq, ak, T, v = _case(1, 1, n, 64, synth.MEAN_SIGN, True, torch.bfloat16, seed=10)
+    rows = np.array([0, 1, 4097, 32768, n - 65, n - 2, n - 1], np.int64)
+    _run_and_check(qb, kb, aq, ak, T, v, N, av, rows, f"n=65536 N={N} av={av}")
