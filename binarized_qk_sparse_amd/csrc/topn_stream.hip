@@ -582,7 +582,7 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
     // c4 = 4 (lane % 16)) takes four kept keys per step, 16 keys per step over the wave.  The
     // four keys' 32-bit reads of their channels are byte-transposed into one word per channel,
     // and V_q + 128 (xor 0x80, unsigned) is multiplied with the packed A_q: the sum is
-    // sum A_q V_q + 128 sum A_q, exact in 32 bits (255 * 255 * 704 < 2^32).
+    // sum A_q V_q + 128 sum A_q, exact in 32 bits (255 * 255 * 1472 < 2^32).
     const int total_a = wave_sum_i32(asum);
     const int c4 = 4 * (lane & 15), ks = lane >> 4;
 #pragma unroll
@@ -633,7 +633,7 @@ __global__ __launch_bounds__(64 * W) void topn_stream_kernel(const StreamKArgs a
     // one 32-bit read per key for its eight channels.  Each nibble xor 8 is V_q + 8 in
     // [1, 15]; masked into the bytes of the even and of the odd channels and
     // byte-transposed into one word per channel, it multiplies the packed A_q with
-    // v_dot4_u32_u8: sum A_q V_q + 8 sum A_q, exact in 32 bits (255 * 15 * 704 < 2^32).
+    // v_dot4_u32_u8: sum A_q V_q + 8 sum A_q, exact in 32 bits (255 * 15 * 1472 < 2^32).
     const int total_a = wave_sum_i32(asum);
     const int c8 = 8 * (lane & 7), ks = lane >> 3;
 #pragma unroll
