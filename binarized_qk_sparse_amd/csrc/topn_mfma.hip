@@ -144,6 +144,42 @@ HAD_DEVICE int quad_rows_excl(int v, int g) {
   return (int)(((g & 1) ? e : 0u) + ((g & 2) ? l : 0u));
 }
 
+// The 16 largest values of two lanes' lists (each sorted in descending order), sorted
+// in descending order, in both lanes: c[k] = max(A[k], B[15 - k]) holds the 16 largest
+// of the union and falls then rises (a bitonic sequence), which four half-cleaner
+// layers sort.  HALF: the lanes 32 apart (quarters g and g ^ 2), else 16 apart (g ^ 1).
+// Equal values may come out as either of two floats that compare equal (+0 and -0),
+// which leaves every count of values above or equal to a bound unchanged.
+template <bool HALF>
+HAD_DEVICE void pair_top16(float (&m)[16]) {
+  float c[16];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    uint32_t a0, b0, a1, b1;  // first and second lane's values at k and at 15 - k
+    if constexpr (HALF) {
+      half_pair(__builtin_bit_cast(uint32_t, m[k]), a0, b0);
+      half_pair(__builtin_bit_cast(uint32_t, m[15 - k]), a1, b1);
+    } else {
+      row_pair(__builtin_bit_cast(uint32_t, m[k]), a0, b0);
+      row_pair(__builtin_bit_cast(uint32_t, m[15 - k]), a1, b1);
+    }
+    c[k] = fmaxf(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, b1));
+    c[15 - k] = fmaxf(__builtin_bit_cast(float, a1), __builtin_bit_cast(float, b0));
+  }
+#pragma unroll
+  for (int j = 8; j >= 1; j >>= 1)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if ((i & j) == 0) {
+        const float hi = fmaxf(c[i], c[i + j]);
+        const float lo = fminf(c[i], c[i + j]);
+        c[i] = hi;
+        c[i + j] = lo;
+      }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) m[k] = c[k];
+}
+
 // A sorting network on 12 inputs (39 comparators in 9 layers; every 0-1 input comes out
 // sorted, which the tests check): comparator (i, j), i < j, leaves the larger value at i.
 constexpr int kSort12[39][2] = {{0, 8}, {1, 7}, {2, 6}, {3, 11}, {4, 10}, {5, 9},  {0, 1}, {2, 5}, {3, 4}, {6, 9},
@@ -674,40 +710,58 @@ __global__ __launch_bounds__(64 * kWaves) void topn_mfma_kernel(const MfmaKArgs 
             sq[0] = fmaxf(sq[0], y);
           }
         }
-        int popped = 0;  // this lane's values at or above L
-        bool short_queue = false;  // this lane's queue ran out before its candidates did
-        const int ncand = __builtin_popcountll(cm);
-        L = quad_rows_max(sq[0]);  // the top value
-        for (int it = 0; it <= 4 * KG && __builtin_amdgcn_ballot_w64(!done) != 0; ++it) {
-          // (-inf fillers are below every L; ties pop together, one per pass.  The shift
-          // is a bitwise select under an opaque mask: as a select between neighbouring
-          // elements it is turned into a dynamically indexed read of the queue, a chain
-          // of compares per element)
-          while (__builtin_amdgcn_ballot_w64(sq[0] >= L) != 0) {
-            const bool pop = sq[0] >= L;
-            uint32_t m = pop ? 0xffffffffu : 0u;
-            asm volatile("" : "+v"(m));
+        if (__builtin_amdgcn_ballot_w64(rs > kCache) == 0) {
+          // Every row's rank lies within its lanes' twelve largest values (a lane's
+          // queue holds its twelve largest, and at most rs - 1 values rank above the
+          // rs-th): the row's sixteen largest come from merging the four queues in two
+          // pair steps, L is the one at rank rs and `above` counts those strictly above.
+          float mq[16];
 #pragma unroll
-            for (int k = 0; k + 1 < kCache; ++k)
-              sq[k] = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, sq[k]) & ~m) |
-                                                    (__builtin_bit_cast(uint32_t, sq[k + 1]) & m));
-            sq[kCache - 1] = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, sq[kCache - 1]) & ~m) |
-                                                           (0xff800000u & m));
-            popped += pop ? 1 : 0;
-          }
-          const int c = quad_rows_sum(popped);
-          const float nb = quad_rows_max(sq[0]);  // every head is below L now
-          short_queue = short_queue || (!done && popped >= kCache && ncand > kCache);
-          if (!done) {
-            if (c >= rs) {
-              done = true;
-            } else {
-              above = c;
-              L = nb;
+          for (int k = 0; k < 16; ++k) mq[k] = k < kCache ? sq[k] : -INFINITY;
+          pair_top16<false>(mq);
+          pair_top16<true>(mq);
+          L = mq[0];
+#pragma unroll
+          for (int k = 1; k < 16; ++k) L = k == rs - 1 ? mq[k] : L;
+#pragma unroll
+          for (int k = 0; k < 16; ++k) above += mq[k] > L ? 1 : 0;
+          queued = true;
+        } else {
+          int popped = 0;  // this lane's values at or above L
+          bool short_queue = false;  // this lane's queue ran out before its candidates did
+          const int ncand = __builtin_popcountll(cm);
+          L = quad_rows_max(sq[0]);  // the top value
+          for (int it = 0; it <= 4 * KG && __builtin_amdgcn_ballot_w64(!done) != 0; ++it) {
+            // (-inf fillers are below every L; ties pop together, one per pass.  The shift
+            // is a bitwise select under an opaque mask: as a select between neighbouring
+            // elements it is turned into a dynamically indexed read of the queue, a chain
+            // of compares per element)
+            while (__builtin_amdgcn_ballot_w64(sq[0] >= L) != 0) {
+              const bool pop = sq[0] >= L;
+              uint32_t m = pop ? 0xffffffffu : 0u;
+              asm volatile("" : "+v"(m));
+#pragma unroll
+              for (int k = 0; k + 1 < kCache; ++k)
+                sq[k] = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, sq[k]) & ~m) |
+                                                      (__builtin_bit_cast(uint32_t, sq[k + 1]) & m));
+              sq[kCache - 1] = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, sq[kCache - 1]) & ~m) |
+                                                             (0xff800000u & m));
+              popped += pop ? 1 : 0;
+            }
+            const int c = quad_rows_sum(popped);
+            const float nb = quad_rows_max(sq[0]);  // every head is below L now
+            short_queue = short_queue || (!done && popped >= kCache && ncand > kCache);
+            if (!done) {
+              if (c >= rs) {
+                done = true;
+              } else {
+                above = c;
+                L = nb;
+              }
             }
           }
+          queued = __builtin_amdgcn_ballot_w64(short_queue) == 0;
         }
-        queued = __builtin_amdgcn_ballot_w64(short_queue) == 0;
       }
       if (!queued) {
         above = 0;
