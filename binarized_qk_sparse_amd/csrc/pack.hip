@@ -51,13 +51,27 @@ struct Sets {
   double* partial[2];
 };
 
+// Column sums of a workgroup's rows, in float64, in one fixed order: each thread runs
+// over its rows (r_off + RPP k, k ascending) for eight columns, a butterfly over the
+// lanes of a wave that hold the same columns adds the runs (every lane ends with the
+// same bits: each step adds the same two values, in either order), and the kWaves
+// wave sums are added in wave order by the caller.  s holds the wave sums afterwards.
+constexpr int kPackWaves = kThreads / 64;
+template <int D>
+HAD_DEVICE void wave_colsum(double (&s)[8]) {
+#pragma unroll
+  for (int off = D / 8; off < 64; off <<= 1)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s[c] += __shfl_xor(s[c], off, 64);
+}
+
 // Column sums over one chunk of tokens, in float64: partial[bh][chunk][c].
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void colsum_partial_kernel(const Sets S, int64_t n, int64_t chunks,
                                                                   int64_t per) {
   constexpr int TPR = D / 8;          // threads per token row
   constexpr int RPP = kThreads / TPR;  // rows per pass
-  __shared__ double red[RPP][D];
+  __shared__ double red[kPackWaves][D];
   const int set = (int)(blockIdx.x / per);
   const int64_t b = blockIdx.x % per;
   const T* __restrict__ x = static_cast<const T*>(S.x[set]);
@@ -76,12 +90,16 @@ __global__ __launch_bounds__(kThreads) void colsum_partial_kernel(const Sets S, 
       for (int c = 0; c < 8; ++c) s[c] += (double)v[c];
     }
   }
+  wave_colsum<D>(s);
+  if (t % 64 < TPR) {
 #pragma unroll
-  for (int c = 0; c < 8; ++c) red[r_off][8 * cg + c] = s[c];
+    for (int c = 0; c < 8; ++c) red[t / 64][8 * cg + c] = s[c];
+  }
   __syncthreads();
   if (t < D) {
     double acc = 0.0;
-    for (int rp = 0; rp < RPP; ++rp) acc += red[rp][t];
+#pragma unroll
+    for (int w = 0; w < kPackWaves; ++w) acc += red[w][t];
     S.partial[set][(bh * chunks + chunk) * D + t] = acc;
   }
 }
@@ -179,7 +197,10 @@ __global__ __launch_bounds__(kThreads) void pack_rows_kernel(const Sets S, uint3
 // and runs the row pass of pack_rows_kernel from LDS (same lanes, same order), so the
 // codes, alpha and mu are the same bits as the two-pass route with half the HBM reads.
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void pack_head_kernel(const Sets S, uint32_t BH, uint32_t n) {
+// (five waves per SIMD: the head and the column sums take 27.5 KB of LDS at d = 64, so
+// five workgroups fit a CU once the registers allow it)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5)))
+void pack_head_kernel(const Sets S, uint32_t BH, uint32_t n) {
   constexpr int TPR = D / 8;           // column pass: threads per token row
   constexpr int RPP = kThreads / TPR;  // rows per pass
   constexpr int LPR = D / 32;          // row pass: lanes per token row
@@ -187,8 +208,8 @@ __global__ __launch_bounds__(kThreads) void pack_head_kernel(const Sets S, uint3
   extern __shared__ __align__(16) uint8_t smem[];
   const uint32_t xbytes = (n * D * (uint32_t)sizeof(T) + 15u) & ~15u;
   T* xs = reinterpret_cast<T*>(smem);                             // [n][D]
-  double* red = reinterpret_cast<double*>(smem + xbytes);         // [RPP][D]
-  float* mus = reinterpret_cast<float*>(red + RPP * D);           // [D]
+  double* red = reinterpret_cast<double*>(smem + xbytes);         // [kPackWaves][D]
+  float* mus = reinterpret_cast<float*>(red + kPackWaves * D);    // [D]
   const int set = (int)(blockIdx.x / BH);
   const size_t bh = blockIdx.x % BH;
   const int tid = threadIdx.x;
@@ -224,13 +245,17 @@ __global__ __launch_bounds__(kThreads) void pack_head_kernel(const Sets S, uint3
         for (int c = 0; c < 8; ++c) sm[c] += (double)v[c];
       }
     }
+    wave_colsum<D>(sm);
+    if (tid % 64 < TPR) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) red[r_off * D + 8 * cg + c] = sm[c];
+      for (int c = 0; c < 8; ++c) red[(tid / 64) * D + 8 * cg + c] = sm[c];
+    }
   }
   __syncthreads();
   if (tid < D) {
     double part = 0.0;  // the chunk's partial, as colsum_partial_kernel forms it
-    for (int rp = 0; rp < RPP; ++rp) part += red[rp * D + tid];
+#pragma unroll
+    for (int w = 0; w < kPackWaves; ++w) part += red[w * D + tid];
     double acc = 0.0;  // the sum over the (one) chunk, as the row pass finishes it
     acc += part;
     const float m = (float)(acc / (double)n);
@@ -272,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void pack_head_kernel(const Sets S, uint3
 // LDS bytes of pack_head_kernel for n tokens
 template <typename T, int D>
 uint32_t pack_head_lds(int64_t n) {
-  return (uint32_t)(((n * D * (int64_t)sizeof(T) + 15) & ~(int64_t)15) + (int64_t)(kThreads / (D / 8)) * D * 8 + D * 4);
+  return (uint32_t)(((n * D * (int64_t)sizeof(T) + 15) & ~(int64_t)15) + (int64_t)kPackWaves * D * 8 + D * 4);
 }
 
 template <typename T, int D>
