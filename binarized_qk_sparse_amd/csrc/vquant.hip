@@ -160,9 +160,102 @@ __global__ __launch_bounds__(kThreads) void vq_fused_kernel(const T* __restrict_
   store_codes<D, L>(vq, r, cg, b);
 }
 
+// Eight elements from the registers one 16-byte load (bf16) or two (fp32) filled.
+template <typename T>
+HAD_DEVICE void unpack8(const uint4 (&w)[sizeof(T) / 2], float (&x)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    x[0] = bf16_lo(w[0].x); x[1] = bf16_hi(w[0].x);
+    x[2] = bf16_lo(w[0].y); x[3] = bf16_hi(w[0].y);
+    x[4] = bf16_lo(w[0].z); x[5] = bf16_hi(w[0].z);
+    x[6] = bf16_lo(w[0].w); x[7] = bf16_hi(w[0].w);
+  } else {
+    const uint32_t u[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) x[c] = __builtin_bit_cast(float, u[c]);
+  }
+}
+
+// Heads of at most kVqChunk rows in one launch: one workgroup per (b, h) loads the
+// head's rows into registers (rows r_off + RPP k, eight channels per thread), takes
+// the channel maxima of |V| (per thread, then a butterfly over the lanes of a wave
+// that hold the same channels, then the waves through LDS), divides them by L as
+// vscale_kernel does, and quantizes the rows it holds.  V is read once instead of
+// twice, with the same bits: a maximum does not depend on the order it is taken in.
+template <typename T, int D, int L>
+__global__ __launch_bounds__(kThreads) void vq_head_kernel(const T* __restrict__ v, uint32_t n,
+                                                           float* __restrict__ scale, int8_t* __restrict__ vq) {
+  constexpr int TPR = D / 8;
+  constexpr int RPP = kThreads / TPR;
+  constexpr int PASSES = kVqChunk / RPP;
+  constexpr int NW = sizeof(T) / 2;  // 16-byte words per eight elements
+  __shared__ float red[kThreads / 64][D];
+  __shared__ float sc[D];
+  const size_t bh = blockIdx.x;
+  const int t = threadIdx.x;
+  const int r_off = t / TPR, cg = t % TPR;
+  const uint4* src = reinterpret_cast<const uint4*>(v + bh * n * D);
+  uint4 raw[PASSES][NW];
+#pragma unroll
+  for (int k = 0; k < PASSES; ++k) {
+    const uint32_t r = (uint32_t)(r_off + RPP * k);
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      raw[k][w] = r < n ? src[((size_t)r * D + 8 * cg) / (8 / NW) + w] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int k = 0; k < PASSES; ++k) {
+    float x[8];
+    unpack8<T>(raw[k], x);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) m[c] = fmaxf(m[c], fabsf(x[c]));  // (rows past n hold zeros)
+  }
+#pragma unroll
+  for (int off = TPR; off < 64; off <<= 1)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) m[c] = fmaxf(m[c], __shfl_xor(m[c], off, 64));
+  if (t % 64 < TPR) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) red[t / 64][8 * cg + c] = m[c];
+  }
+  __syncthreads();
+  if (t < D) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) acc = fmaxf(acc, red[w][t]);
+    const float q = __fdiv_rn(acc, (float)L);
+    sc[t] = q;
+    scale[bh * D + t] = q;
+  }
+  __syncthreads();
+  float sv[8], inv[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    sv[c] = sc[8 * cg + c];
+    inv[c] = __builtin_amdgcn_rcpf(sv[c]);
+  }
+#pragma unroll
+  for (int k = 0; k < PASSES; ++k) {
+    const uint32_t r = (uint32_t)(r_off + RPP * k);
+    if (r < n) {
+      float x[8];
+      unpack8<T>(raw[k], x);
+      uint32_t b[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) b[c] = quant_i8<L>(x[c], sv[c], inv[c]);
+      store_codes<D, L>(vq, (uint32_t)(bh * n) + r, cg, b);
+    }
+  }
+}
+
 template <typename T, int D, int L>
 hipError_t launch_levels(const VQuantParams& p, hipStream_t s) {
   const T* v = static_cast<const T*>(p.v);
+  if (p.n <= kVqChunk) {
+    hipLaunchKernelGGL((vq_head_kernel<T, D, L>), dim3((unsigned)p.BH), dim3(kThreads), 0, s, v, (uint32_t)p.n,
+                       p.vscale, p.vq);
+    return hipGetLastError();
+  }
   const int64_t chunks = vq_chunks(p.n);
   hipLaunchKernelGGL((vmax_partial_kernel<T, D>), dim3((unsigned)(p.BH * chunks)), dim3(kThreads), 0, s, v,
                      p.n, chunks, p.vmax_partial);
