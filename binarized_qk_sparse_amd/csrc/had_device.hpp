@@ -58,6 +58,60 @@ HAD_DEVICE int wave_sum_i32(int v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
+// The values of this lane and of lane l ^ OFF (OFF = 4, 8, 16 or 32), on the VALU
+// where the hardware has the exchange: a DPP rotation by 8 within each 16-lane row
+// (lane l meets l ^ 8), the gfx950 permlane swaps across 16-lane rows and 32-lane
+// halves (which hand both lanes the pair in the same order); a bpermute for 4.  The
+// two values may come in either order, so a commutative combination of them gives
+// both lanes the same bits.
+template <int OFF>
+HAD_DEVICE void xor_pair(uint32_t x, uint32_t& a, uint32_t& b) {
+  static_assert(OFF == 4 || OFF == 8 || OFF == 16 || OFF == 32, "lane distance");
+  if constexpr (OFF == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    a = r[0];
+    b = r[1];
+  } else if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    a = r[0];
+    b = r[1];
+  } else if constexpr (OFF == 8) {
+    a = x;
+    b = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xf, 0xf, true);  // row_ror:8
+  } else {
+    a = x;
+    b = (uint32_t)__shfl_xor((int)x, OFF, 64);
+  }
+}
+
+// Butterfly over the lanes OFF, 2 OFF, .., 32 apart: f(this lane's value, the other's)
+// at each step, f commutative (float64 sum, float max), so every lane ends with the
+// same bits.
+template <int OFF, class F>
+HAD_DEVICE double butterfly_f64(double v, F f) {
+  if constexpr (OFF >= 64) {
+    return v;
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    uint32_t al, bl, ah, bh;
+    xor_pair<OFF>((uint32_t)u, al, bl);
+    xor_pair<OFF>((uint32_t)(u >> 32), ah, bh);
+    const double a = __builtin_bit_cast(double, ((uint64_t)ah << 32) | al);
+    const double b = __builtin_bit_cast(double, ((uint64_t)bh << 32) | bl);
+    return butterfly_f64<2 * OFF>(f(a, b), f);
+  }
+}
+template <int OFF, class F>
+HAD_DEVICE float butterfly_f32(float v, F f) {
+  if constexpr (OFF >= 64) {
+    return v;
+  } else {
+    uint32_t a, b;
+    xor_pair<OFF>(__builtin_bit_cast(uint32_t, v), a, b);
+    return butterfly_f32<2 * OFF>(f(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)), f);
+  }
+}
+
 HAD_DEVICE float as_f(int v) { return __builtin_bit_cast(float, v); }
 HAD_DEVICE int as_i(float v) { return __builtin_bit_cast(int, v); }
 

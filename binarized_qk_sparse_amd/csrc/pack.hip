@@ -60,9 +60,7 @@ constexpr int kPackWaves = kThreads / 64;
 template <int D>
 HAD_DEVICE void wave_colsum(double (&s)[8]) {
 #pragma unroll
-  for (int off = D / 8; off < 64; off <<= 1)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) s[c] += __shfl_xor(s[c], off, 64);
+  for (int c = 0; c < 8; ++c) s[c] = butterfly_f64<D / 8>(s[c], [](double a, double b) { return a + b; });
 }
 
 // Column sums over one chunk of tokens, in float64: partial[bh][chunk][c].

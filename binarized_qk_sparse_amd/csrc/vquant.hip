@@ -211,9 +211,7 @@ __global__ __launch_bounds__(kThreads) void vq_head_kernel(const T* __restrict__
     for (int c = 0; c < 8; ++c) m[c] = fmaxf(m[c], fabsf(x[c]));  // (rows past n hold zeros)
   }
 #pragma unroll
-  for (int off = TPR; off < 64; off <<= 1)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) m[c] = fmaxf(m[c], __shfl_xor(m[c], off, 64));
+  for (int c = 0; c < 8; ++c) m[c] = butterfly_f32<TPR>(m[c], [](float a, float b) { return fmaxf(a, b); });
   if (t % 64 < TPR) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) red[t / 64][8 * cg + c] = m[c];
