@@ -157,3 +157,32 @@ def test_wide_tables(scale):
     T = (scale * g.standard_normal((H, 2 * n - 1))).astype(np.float32)
     for N in (1, 30, 196, 5000):
         _check(qb, kb, T, v, N, f"wide x{scale} N={N}")
+
+
+@pytest.mark.parametrize("N", [6, 17, 18, 23, 24, 35])
+def test_ranks_at_the_merged_queue_limit(N):
+    # Every query is all +1; 5 keys at distance 0, 30 at distance 1 (20 in the first key
+    # quarter, more than a lane's queue of twelve, and 10 in the third), the rest at 5.
+    # The threshold level is 1 and the row keeps N - 5 of the 30 keys at it, so the rank
+    # from the nearer end is 1, 12 (merged queues), 13, 13 (walk), 12 (from the low end,
+    # merged) and 1 (low end).  Head 0 has distinct table values, head 1 a table rounded
+    # to a few values, so that keys at the threshold tie on the logit and split by index.
+    n, H = 256, 2
+    g = np.random.default_rng(74)
+    q = np.ones((1, H, n, 64), np.float32)
+    k = np.ones((1, H, n, 64), np.float32)
+    k[..., :5] = -1.0  # distance 5
+    level0 = [3, 70, 140, 200, 250]
+    level1 = list(range(1, 61, 3)) + list(range(130, 190, 6))
+    assert len(level1) == 30 and not set(level1) & set(level0)
+    k[0, :, level0] = 1.0
+    k[0, :, level1] = 1.0
+    k[0, :, level1, 0] = -1.0
+    qb, _, _ = oracle.pack(q, oracle.SIGN)
+    kb, _, _ = oracle.pack(k, oracle.SIGN)
+    h = oracle.logits(qb, kb)[0][0, 0, 0]
+    assert np.sum(h == 0) == 5 and np.sum(h == 1) == 30 and np.sum(h == 5) == n - 35
+    T = (0.01 * g.standard_normal((H, 2 * n - 1))).astype(np.float32)
+    T[1] = np.round(T[1] / 0.01).astype(np.float32) * np.float32(0.01)
+    v = torch.from_numpy(g.standard_normal((1, H, n, 64)).astype(np.float32)).to(torch.bfloat16)
+    _check(qb, kb, T, v, N, f"merge limit N={N}")
