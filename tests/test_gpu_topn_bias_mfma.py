@@ -159,21 +159,28 @@ def test_wide_tables(scale):
         _check(qb, kb, T, v, N, f"wide x{scale} N={N}")
 
 
-@pytest.mark.parametrize("N", [6, 17, 18, 23, 24, 35])
-def test_ranks_at_the_merged_queue_limit(N):
-    # Every query is all +1; 5 keys at distance 0, 30 at distance 1 (20 in the first key
-    # quarter, more than a lane's queue of twelve, and 10 in the third), the rest at 5.
-    # The threshold level is 1 and the row keeps N - 5 of the 30 keys at it, so the rank
-    # from the nearer end is 1, 12 (merged queues), 13, 13 (walk), 12 (from the low end,
-    # merged) and 1 (low end).  Head 0 has distinct table values, head 1 a table rounded
-    # to a few values, so that keys at the threshold tie on the logit and split by index.
+@pytest.mark.parametrize("layout,N", [("crowded", 6), ("crowded", 17), ("crowded", 18), ("crowded", 23),
+                                      ("crowded", 24), ("crowded", 35), ("spread", 18), ("spread", 20),
+                                      ("spread", 21), ("spread", 22)])
+def test_ranks_at_the_merged_queue_limit(layout, N):
+    # Every query is all +1; 5 keys at distance 0, 30 at distance 1, the rest at 5, so the
+    # threshold level is 1 and a row keeps N - 5 of the 30 keys at it.  "crowded": 20 of
+    # the 30 in the first key quarter (more than a lane's queue of twelve) and 10 in the
+    # third; the rank from the nearer end is then 1, 12 (merged queues), 13, 13 (walk), 12
+    # (from the low end, merged) and 1.  "spread": at most 8 in each quarter, so no queue
+    # drops a candidate, with ranks 13, 15, 16 and 14 (from the low end), past what the
+    # merged queues take.  Head 0 has distinct table values, head 1 a table rounded to a few
+    # values, so that keys at the threshold tie on the logit and split by index.
     n, H = 256, 2
     g = np.random.default_rng(74)
     q = np.ones((1, H, n, 64), np.float32)
     k = np.ones((1, H, n, 64), np.float32)
     k[..., :5] = -1.0  # distance 5
-    level0 = [3, 70, 140, 200, 250]
-    level1 = list(range(1, 61, 3)) + list(range(130, 190, 6))
+    level0 = [3, 71, 141, 201, 250]
+    if layout == "crowded":
+        level1 = list(range(1, 61, 3)) + list(range(130, 190, 6))
+    else:
+        level1 = [4 + 8 * i for i in range(30)]
     assert len(level1) == 30 and not set(level1) & set(level0)
     k[0, :, level0] = 1.0
     k[0, :, level1] = 1.0
@@ -185,4 +192,4 @@ def test_ranks_at_the_merged_queue_limit(N):
     T = (0.01 * g.standard_normal((H, 2 * n - 1))).astype(np.float32)
     T[1] = np.round(T[1] / 0.01).astype(np.float32) * np.float32(0.01)
     v = torch.from_numpy(g.standard_normal((1, H, n, 64)).astype(np.float32)).to(torch.bfloat16)
-    _check(qb, kb, T, v, N, f"merge limit N={N}")
+    _check(qb, kb, T, v, N, f"merge limit {layout} N={N}")
